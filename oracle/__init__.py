@@ -1,0 +1,288 @@
+"""Float64 CPU oracle for the Palimpsa dual-state recurrence.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the bench's
+CPU-baseline leg may import this package; the product path
+(``bayesian_metaplastic_memory_amd``) never does, and the two share no code.
+
+Contents
+--------
+``fwd`` / ``step``
+    Thin ctypes wrappers over ``palimpsa_oracle.c``: the sequential Eq. (5)
+    recurrence of "Learning to Remember, Learn, and Forget in Attention-Based
+    Models" (slides, frame "Palimpsa updates content and importance
+    together") with the posterior-mean readout ``y_t = mu_t q_t``.
+``fwd_numpy``
+    The same definition written with numpy, vectorised over the state entries
+    of one token; a second, independent transcription for small cases.
+``fwd_natural``
+    The natural-parameter affine scans ``M = I . mu``, ``Ibar = I - I_prior``
+    (slides, frame "Natural parameters expose two affine scans", App. A.12).
+``fwd_full_gaussian``
+    The full-precision Gaussian update per value row (slides, backup frame
+    "dropping precision correlations changes the mean", App. A.3-A.5), with
+    an option that keeps only the diagonal of the precision at every token.
+``fwd_mamba2_limit``
+    The frozen-importance recurrence of the Mamba2 limit (slides, frame "The
+    Mamba2 limit enables a gradual model upgrade", Secs. 2.3-2.4).
+
+All arrays use the library's layouts: q, k ``[B, T, H, dk]``; v, beta
+``[B, T, H, dv]``; dt ``[B, T, H]``; A, I_prior ``[H]``; state
+``[B, H, dv, dk]``; y ``[B, T, H, dv]``.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against the
+pages' worked examples, closed forms, limits and a brute-force posterior.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "palimpsa_oracle.c")
+_LIB = os.path.join(_HERE, "libpalimpsa_oracle.so")
+_lock = threading.Lock()
+_handle = None
+
+# -O2 without fast-math and without contraction: every product and sum is a
+# separately rounded IEEE float64 operation.
+GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+             "-shared", "-fPIC", "-std=c11"]
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc (idempotent unless ``force``)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _lib():
+    global _handle
+    with _lock:
+        if _handle is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            dp = ctypes.POINTER(ctypes.c_double)
+            i = ctypes.c_int
+            lib.oracle_fwd.argtypes = [i, i, i, i, i] + [dp] * 10 + [i]
+            lib.oracle_fwd.restype = None
+            lib.oracle_step.argtypes = [i, i, i, i] + [dp] * 10 + [i]
+            lib.oracle_step.restype = None
+            lib.oracle_max_threads.argtypes = []
+            lib.oracle_max_threads.restype = i
+            _handle = lib
+    return _handle
+
+
+def max_threads() -> int:
+    """Threads the OpenMP runtime would use by default."""
+    return int(_lib().oracle_max_threads())
+
+
+def _f64(x) -> np.ndarray:
+    """Exact upcast to contiguous float64 (bf16 and fp32 values are exact)."""
+    if hasattr(x, "detach"):  # a torch tensor; bf16 needs a float32 hop
+        x = x.detach().cpu()
+        if str(x.dtype) == "torch.bfloat16":
+            x = x.float()
+        x = x.numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _init_state(B, H, dv, dk, Ip, mu0, I0):
+    if (mu0 is None) != (I0 is None):
+        raise ValueError("give both mu0 and I0, or neither")
+    if mu0 is None:
+        mu = np.zeros((B, H, dv, dk))
+        I = np.broadcast_to(Ip[None, :, None, None], (B, H, dv, dk)).copy()
+    else:
+        mu, I = _f64(mu0).copy(), _f64(I0).copy()
+        if mu.shape != (B, H, dv, dk) or I.shape != (B, H, dv, dk):
+            raise ValueError("state must be [B, H, dv, dk]")
+    return mu, I
+
+
+def fwd(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None, nthreads: int = 0):
+    """Sequential float64 Eq. (5) over the whole sequence (C oracle).
+
+    Returns ``(y [B,T,H,dv], muT [B,H,dv,dk], IT [B,H,dv,dk])`` as float64.
+    ``mu0 = I0 = None`` means ``mu0 = 0`` and ``I0 = I_prior``.
+    """
+    q, k, v, beta, dt = (_f64(x) for x in (q, k, v, beta, dt))
+    A, Ip = _f64(A), _f64(I_prior)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != v.shape \
+            or dt.shape != (B, T, H) or A.shape != (H,) or Ip.shape != (H,):
+        raise ValueError("inconsistent shapes")
+    mu, I = _init_state(B, H, dv, dk, Ip, mu0, I0)
+    y = np.zeros((B, T, H, dv))
+    _lib().oracle_fwd(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                      _ptr(dt), _ptr(A), _ptr(Ip), _ptr(mu), _ptr(I), _ptr(y),
+                      int(nthreads))
+    return y, mu, I
+
+
+def step(q, k, v, beta, dt, A, I_prior, mu, I, nthreads: int = 0):
+    """One decode token (C oracle).  q, k ``[B,H,dk]``; v, beta ``[B,H,dv]``;
+    dt ``[B,H]``.  Returns ``(y [B,H,dv], mu', I')`` without touching inputs."""
+    q, k, v, beta, dt = (_f64(x) for x in (q, k, v, beta, dt))
+    A, Ip = _f64(A), _f64(I_prior)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    mu, I = _f64(mu).copy(), _f64(I).copy()
+    if mu.shape != (B, H, dv, dk) or I.shape != mu.shape or dt.shape != (B, H):
+        raise ValueError("inconsistent shapes")
+    y = np.zeros((B, H, dv))
+    _lib().oracle_step(B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                       _ptr(dt), _ptr(A), _ptr(Ip), _ptr(mu), _ptr(I), _ptr(y),
+                       int(nthreads))
+    return y, mu, I
+
+
+# ---------------------------------------------------------------------------
+# numpy transcriptions (small cases and pins)
+# ---------------------------------------------------------------------------
+
+def _gate(A_h, dt):
+    """alpha = exp(-A dt) and 1 - alpha = -expm1(-A dt) (Eq. (9) gate)."""
+    return np.exp(-A_h * dt), -np.expm1(-A_h * dt)
+
+
+def fwd_numpy(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None):
+    """Eq. (5) token by token, vectorised over the (i, j) state entries."""
+    q, k, v, beta, dt = (_f64(x) for x in (q, k, v, beta, dt))
+    A, Ip = _f64(A), _f64(I_prior)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    mu, I = _init_state(B, H, dv, dk, Ip, mu0, I0)
+    y = np.zeros((B, T, H, dv))
+    for b in range(B):
+        for h in range(H):
+            m, P = mu[b, h], I[b, h]
+            for t in range(T):
+                a, oma = _gate(A[h], dt[b, t, h])
+                kk = k[b, t, h]
+                P_new = a * P + oma * Ip[h] + np.outer(beta[b, t, h], kk * kk)
+                m = a * (P / P_new) * m + np.outer(beta[b, t, h] * v[b, t, h], kk) / P_new
+                P = P_new
+                y[b, t, h] = m @ q[b, t, h]
+            mu[b, h], I[b, h] = m, P
+    return y, mu, I
+
+
+def fwd_natural(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None):
+    """Natural-parameter form: M_t = alpha M_{t-1} + (beta.v) (x) k,
+    Ibar_t = alpha Ibar_{t-1} + beta (x) k^2, y_t = (M_t / (I_prior + Ibar_t)) q_t.
+    Returns ``(y, muT, IT)`` like ``fwd``."""
+    q, k, v, beta, dt = (_f64(x) for x in (q, k, v, beta, dt))
+    A, Ip = _f64(A), _f64(I_prior)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    mu, I = _init_state(B, H, dv, dk, Ip, mu0, I0)
+    y = np.zeros((B, T, H, dv))
+    for b in range(B):
+        for h in range(H):
+            M = I[b, h] * mu[b, h]
+            Ibar = I[b, h] - Ip[h]
+            for t in range(T):
+                a, _ = _gate(A[h], dt[b, t, h])
+                kk = k[b, t, h]
+                M = a * M + np.outer(beta[b, t, h] * v[b, t, h], kk)
+                Ibar = a * Ibar + np.outer(beta[b, t, h], kk * kk)
+                y[b, t, h] = (M / (Ip[h] + Ibar)) @ q[b, t, h]
+            I[b, h] = Ip[h] + Ibar
+            mu[b, h] = M / I[b, h]
+    return y, mu, I
+
+
+def fwd_full_gaussian(k, v, beta, alpha, P_prior, mu0=None, P0=None,
+                      diagonal: bool = False):
+    """Full-precision Gaussian filter for ONE head, value rows independent.
+
+    For each value row i (App. A.3-A.5):
+        P_t = alpha_t P_{t-1} + (1 - alpha_t) P_prior + beta_{t,i} k_t k_t^T
+        mu_t = P_t^{-1} [alpha_t P_{t-1} mu_{t-1} + beta_{t,i} v_{t,i} k_t]
+    k ``[T, dk]``, v and beta ``[T, dv]``, alpha ``[T]``, P_prior ``[dk, dk]``.
+    With ``diagonal=True`` only the diagonal of every new precision is kept
+    (the off-diagonal precision terms are discarded from the coupled
+    solution, which is how Eq. (5) is obtained).
+    Returns ``(mu [dv, dk], P [dv, dk, dk], mus [T, dv, dk])``.
+    """
+    k, v, beta, alpha = (np.asarray(x, dtype=np.float64) for x in (k, v, beta, alpha))
+    P_prior = np.asarray(P_prior, dtype=np.float64)
+    T, dk = k.shape
+    dv = v.shape[1]
+    mu = np.zeros((dv, dk)) if mu0 is None else np.array(mu0, dtype=np.float64)
+    P = np.broadcast_to(P_prior, (dv, dk, dk)).copy() if P0 is None \
+        else np.array(P0, dtype=np.float64)
+    if diagonal:
+        P = np.stack([np.diag(np.diag(Pi)) for Pi in P])
+    mus = np.zeros((T, dv, dk))
+    for t in range(T):
+        a = alpha[t]
+        for i in range(dv):
+            P_new = a * P[i] + (1.0 - a) * P_prior + beta[t, i] * np.outer(k[t], k[t])
+            if diagonal:
+                P_new = np.diag(np.diag(P_new))
+            rhs = a * P[i] @ mu[i] + beta[t, i] * v[t, i] * k[t]
+            mu[i] = np.linalg.solve(P_new, rhs)
+            P[i] = P_new
+        mus[t] = mu
+    return mu, P, mus
+
+
+def fwd_mamba2_limit(q, k, v, beta, dt, A, I_prior, mu0=None):
+    """Frozen-importance recurrence mu_t = alpha_t mu_{t-1} + ((beta.v)/I_prior) (x) k_t
+    with readout y_t = mu_t q_t (scalar I_prior per head)."""
+    q, k, v, beta, dt = (_f64(x) for x in (q, k, v, beta, dt))
+    A, Ip = _f64(A), _f64(I_prior)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    mu = np.zeros((B, H, dv, dk)) if mu0 is None else _f64(mu0).copy()
+    y = np.zeros((B, T, H, dv))
+    for b in range(B):
+        for h in range(H):
+            m = mu[b, h]
+            for t in range(T):
+                a, _ = _gate(A[h], dt[b, t, h])
+                m = a * m + np.outer(beta[b, t, h] * v[b, t, h] / Ip[h], k[b, t, h])
+                y[b, t, h] = m @ q[b, t, h]
+            mu[b, h] = m
+    return y, mu
+
+
+# ---------------------------------------------------------------------------
+# head sampling for full-size parity checks
+# ---------------------------------------------------------------------------
+
+def select_heads(inputs: dict, heads) -> dict:
+    """Gather the listed (b, h) heads of API-layout inputs into a batch of
+    shape B=1, H=len(heads), so the oracle runs only on those heads.  Heads are
+    independent, so the result equals the corresponding slice of a full run."""
+    bs = np.array([b for b, _ in heads])
+    hs = np.array([h for _, h in heads])
+    out = {}
+    for name in ("q", "k", "v", "beta"):
+        x = _f64(inputs[name])                   # [B, T, H, d]
+        out[name] = np.ascontiguousarray(x[bs, :, hs, :].transpose(1, 0, 2)[None])
+    dt = _f64(inputs["dt"])                      # [B, T, H]
+    out["dt"] = np.ascontiguousarray(dt[bs, :, hs].T[None])
+    out["A"] = _f64(inputs["A"])[hs]
+    out["I_prior"] = _f64(inputs["I_prior"])[hs]
+    for name in ("mu0", "I0"):
+        if inputs.get(name) is not None:
+            out[name] = np.ascontiguousarray(_f64(inputs[name])[bs, hs][None])
+        else:
+            out[name] = None
+    return out
