@@ -1,0 +1,11 @@
+"""Palimpsa dual-state recurrence on MI355X (gfx950).
+
+``fwd_chunked`` (training / prefill) and ``step`` (decode) call the HIP
+kernels of ``libpalimpsa.so`` through its C ABI; see ``include/palimpsa.h``
+for the operation, layouts and error behaviour.
+"""
+from ._binding import (BF16, F32, LIB_PATH, PalimpsaError, fwd_chunked, load_library,
+                       status_string, step, version)
+
+__all__ = ["fwd_chunked", "step", "load_library", "status_string", "version",
+           "PalimpsaError", "LIB_PATH", "F32", "BF16"]

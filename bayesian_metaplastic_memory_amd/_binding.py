@@ -1,0 +1,174 @@
+"""ctypes binding over libpalimpsa.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (``include/palimpsa.h``).  torch supplies device
+memory and the current HIP stream.  There is no fallback: if the library is
+missing or the tensors are not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpalimpsa.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_HIP = range(5)
+F32, BF16 = 0, 1
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class PalimpsaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (what, status_string(status), status))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libpalimpsa.so from the package directory (raises if it is missing)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(
+                    "libpalimpsa.so is not built; run `python -m bayesian_metaplastic_memory_amd.build` "
+                    "(or __graft_entry__.build())")
+            lib = ctypes.CDLL(LIB_PATH)
+            vp, fp, i = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
+            lib.palimpsa_fwd_chunked.argtypes = [vp] * 5 + [fp] * 4 + [vp, fp, fp] + [i] * 8 + [vp]
+            lib.palimpsa_fwd_chunked.restype = i
+            lib.palimpsa_step.argtypes = [vp] * 5 + [fp] * 4 + [vp] + [i] * 6 + [vp]
+            lib.palimpsa_step.restype = i
+            lib.palimpsa_status_string.argtypes = [i]
+            lib.palimpsa_status_string.restype = ctypes.c_char_p
+            lib.palimpsa_version.argtypes = []
+            lib.palimpsa_version.restype = i
+            _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load_library().palimpsa_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(load_library().palimpsa_version())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def fwd_chunked(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None, chunk: int = 0,
+                out_dtype=None, y=None, muT=None, IT=None, write_state: bool = True):
+    """Chunked forward.  Returns ``(y, muT, IT)``; ``muT``/``IT`` are None when
+    ``write_state`` is False.  Outputs are allocated unless passed in (they may
+    alias ``mu0``/``I0`` for an in-place resume)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    in_dtype = q.dtype
+    if in_dtype not in _DTYPES:
+        raise ValueError("unsupported input dtype %s" % in_dtype)
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    if out_dtype not in _DTYPES:
+        raise ValueError("unsupported output dtype %s" % out_dtype)
+    _check(k, "k", (B, T, H, dk), in_dtype, dev)
+    _check(v, "v", (B, T, H, dv), in_dtype, dev)
+    _check(beta, "beta", (B, T, H, dv), in_dtype, dev)
+    _check(dt, "dt", (B, T, H), in_dtype, dev)
+    _check(q, "q", (B, T, H, dk), in_dtype, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(I_prior, "I_prior", (H,), torch.float32, dev)
+    if (mu0 is None) != (I0 is None):
+        raise ValueError("give both mu0 and I0, or neither")
+    if mu0 is not None:
+        _check(mu0, "mu0", (B, H, dv, dk), torch.float32, dev)
+        _check(I0, "I0", (B, H, dv, dk), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _check(y, "y", (B, T, H, dv), out_dtype, dev)
+    if write_state:
+        if muT is None:
+            muT = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        if IT is None:
+            IT = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        _check(muT, "muT", (B, H, dv, dk), torch.float32, dev)
+        _check(IT, "IT", (B, H, dv, dk), torch.float32, dev)
+    else:
+        muT = IT = None
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.palimpsa_fwd_chunked(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(dt), _ptr(A), _ptr(I_prior),
+            _ptr(mu0), _ptr(I0), _ptr(y) if y.numel() else None,
+            _ptr(muT), _ptr(IT), B, T, H, dk, dv, int(chunk),
+            _DTYPES[in_dtype], _DTYPES[out_dtype], _stream_handle(dev))
+    if st != OK:
+        raise PalimpsaError(st, "palimpsa_fwd_chunked")
+    return y, muT, IT
+
+
+def step(q, k, v, beta, dt, A, I_prior, mu, I, out_dtype=None, y=None):
+    """One decode token; updates ``mu`` and ``I`` in place and returns ``y``."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, dk]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    in_dtype = q.dtype
+    if in_dtype not in _DTYPES:
+        raise ValueError("unsupported input dtype %s" % in_dtype)
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    if out_dtype not in _DTYPES:
+        raise ValueError("unsupported output dtype %s" % out_dtype)
+    _check(k, "k", (B, H, dk), in_dtype, dev)
+    _check(v, "v", (B, H, dv), in_dtype, dev)
+    _check(beta, "beta", (B, H, dv), in_dtype, dev)
+    _check(dt, "dt", (B, H), in_dtype, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(I_prior, "I_prior", (H,), torch.float32, dev)
+    _check(mu, "mu", (B, H, dv, dk), torch.float32, dev)
+    _check(I, "I", (B, H, dv, dk), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _check(y, "y", (B, H, dv), out_dtype, dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.palimpsa_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(dt), _ptr(A),
+                               _ptr(I_prior), _ptr(mu), _ptr(I), _ptr(y), B, H, dk, dv,
+                               _DTYPES[in_dtype], _DTYPES[out_dtype], _stream_handle(dev))
+    if st != OK:
+        raise PalimpsaError(st, "palimpsa_step")
+    return y

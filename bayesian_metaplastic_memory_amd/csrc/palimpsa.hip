@@ -1,0 +1,645 @@
+// libpalimpsa: the Palimpsa dual-state recurrence on MI355X (gfx950).
+//
+// Recurrence ("Learning to Remember, Learn, and Forget in Attention-Based
+// Models", slides frames "Palimpsa updates content and importance together"
+// and "Natural parameters expose two affine scans", Eq. (5), App. A.12),
+// per head, value channel i, key channel j, token t:
+//
+//   alpha_t = exp(-A dt_t),  c_t = (1 - alpha_t) I_prior
+//   I_t  = alpha_t I_{t-1} + c_t + beta_t[i] k_t[j]^2
+//   M_t  = alpha_t M_{t-1} + (beta_t[i] v_t[i]) k_t[j]        (M = I . mu)
+//   y_t[i] = sum_j (M_t / I_t)[i, j] q_t[j]                   (read after the write)
+//
+// Chunked forward (palimpsa_fwd_chunked)
+// --------------------------------------
+// The readout divides by a per-token, per-entry precision, so no step is a
+// dense contraction: the kernel is bound by the FP32 vector ALU, not by HBM
+// (a few hundred GB/s) and not by the matrix cores.  Each state entry costs
+// four FMA/MUL pairs' worth of VALU work per token: 6 VALU instructions and
+// one v_rcp_f32.  Everything else is arranged so that those instructions are
+// nearly all the SIMDs issue:
+//
+//  * The state (M, I) never leaves VGPRs between the first and the last
+//    token: one workgroup owns 16 value rows of one head for the whole
+//    sequence, so no inter-chunk state goes to HBM.
+//  * Lane layout: a wave owns 4 value rows; 16 lanes share a row and each
+//    owns DK/16 key columns (8 at d_k = 128).  The row sum of the readout is
+//    a 4-step DPP butterfly inside a 16-lane row; no LDS round trip.
+//  * Per chunk of C tokens the workgroup stages, once, the per-column
+//    operands k, k^2, q (float32), the per-row pair (beta, beta*v) and the
+//    per-token gate (alpha, c) in LDS; bf16 is widened once here, not per
+//    lane.  Staging is double-buffered: the global loads of chunk n+1 are in
+//    flight while chunk n is computed, and one barrier separates chunks.
+//  * Column operands are read from LDS as 128-bit vectors with the 16 lanes
+//    of a row covering 256 contiguous bytes (conflict-free); the 4 rows of a
+//    wave read the same addresses (broadcast).
+//  * blockIdx -> (head, row block) is remapped so the row blocks of one head
+//    run on one XCD and share k/q through that XCD's L2.
+//
+// Decode step (palimpsa_step)
+// ---------------------------
+// One token over a state held as (mu, I): 16 bytes of state are read and
+// written per entry, so the kernel streams HBM with 128-bit non-temporal
+// accesses; the arithmetic is a few percent of the memory time.
+//
+// Precision: all arithmetic is float32; bf16 inputs are widened exactly and
+// bf16 outputs are rounded to nearest even.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "palimpsa.h"
+
+#define PALIMPSA_VERSION 100  // 0.1.0
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16_t;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct io;
+template <> struct io<float> {
+    static constexpr int kBytes = 4;
+    __device__ static inline float to_f32(float x) { return x; }
+    __device__ static inline float from_f32(float x) { return x; }
+};
+template <> struct io<bf16_t> {
+    static constexpr int kBytes = 2;
+    __device__ static inline float to_f32(bf16_t x) { return (float)x; }
+    __device__ static inline bf16_t from_f32(float x) { return (bf16_t)x; }  // RNE
+};
+
+// Widen a 16-byte packet of T to float32 values.
+template <typename T> struct packet;
+template <> struct packet<float> {
+    static constexpr int kN = 4;
+    __device__ static inline void widen(const uint4 &p, float *out) {
+        out[0] = __uint_as_float(p.x); out[1] = __uint_as_float(p.y);
+        out[2] = __uint_as_float(p.z); out[3] = __uint_as_float(p.w);
+    }
+};
+template <> struct packet<bf16_t> {
+    static constexpr int kN = 8;
+    __device__ static inline void widen(const uint4 &p, float *out) {
+        const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(w[i] << 16);
+            out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+
+// Sum over the 16 lanes of a DPP row; every lane receives the total.
+__device__ inline float row16_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));  // row_half_mirror
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));  // row_mirror
+    return x;
+}
+
+// The gate of Eq. (9): alpha = exp(-A dt) and c = (1 - alpha) I_prior, with
+// 1 - alpha taken as -expm1(-A dt) so that it keeps full relative accuracy
+// when A dt is small.
+__device__ inline float2 gate(float A, float dt, float Ip) {
+    const float x = -A * dt;
+    return make_float2(expf(x), -expm1f(x) * Ip);
+}
+
+// ---------------------------------------------------------------------------
+// chunked forward
+// ---------------------------------------------------------------------------
+
+struct FwdArgs {
+    const void *q, *k, *v, *beta, *dt;
+    const float *A, *Ip, *mu0, *I0;
+    void *y;
+    float *muT, *IT;
+    int B, T, H, dv;
+    int nwg;           // launched workgroups
+    int xcd_remap;     // 1: remap so one head's row blocks share an XCD
+};
+
+constexpr int kWaves = 4;                 // waves per workgroup (one per SIMD)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = 4;
+constexpr int kRowsPerWG = kRowsPerWave * kWaves;   // 16 value rows per workgroup
+constexpr int kLanesPerRow = 16;
+
+// LDS floats per staged token: k, k^2, q columns + (beta, beta*v) per row + gate.
+template <int DK> struct Stage {
+    static constexpr int kColFloats = 3 * DK;
+    static constexpr int kRowFloats = 2 * kRowsPerWG;
+    static constexpr int kTokFloats = kColFloats + kRowFloats + 2;
+};
+
+template <int DK, int C>
+constexpr size_t fwd_lds_bytes() { return (size_t)2 * C * Stage<DK>::kTokFloats * sizeof(float); }
+
+// Per-chunk staging: which 16-byte packets each thread loads, and where they go.
+template <int DK, int C, typename TIn>
+struct Stager {
+    static constexpr int kPerPkt = packet<TIn>::kN;            // elements per 16 B
+    static constexpr int kColPkts = DK / kPerPkt;              // packets per k (or q) row
+    static constexpr int kKQ = C * 2 * kColPkts;               // k and q packets per chunk
+    static constexpr int kKQPerThread = (kKQ + kThreads - 1) / kThreads;
+    static constexpr int kRowPkts = kRowsPerWG / kPerPkt;      // packets per v (or beta) row slice
+    static constexpr int kVB = C * kRowPkts;                   // (v, beta) packet pairs per chunk
+    static_assert(kVB <= kThreads, "one (v, beta) pair per thread at most");
+    static_assert(C <= kThreads, "one gate per thread at most");
+
+    uint4 kq[kKQPerThread];
+    uint4 vv, bb;
+    float dtv;
+
+    // Issue the global loads of chunk starting at token t0 (tokens >= T are skipped).
+    __device__ inline void load(const FwdArgs &a, int b, int h, int row0, int t0, int tid) {
+        const size_t H = a.H;
+#pragma unroll
+        for (int u = 0; u < kKQPerThread; ++u) {
+            const int p = tid + u * kThreads;
+            if (kKQ % kThreads == 0 || p < kKQ) {
+                const int tt = p / (2 * kColPkts);
+                const int arr = (p / kColPkts) & 1;
+                const int off = (p % kColPkts) * kPerPkt;
+                const int t = t0 + tt;
+                if (t < a.T) {
+                    const size_t base = (((size_t)b * a.T + t) * H + h) * DK + off;
+                    const TIn *src = (const TIn *)(arr ? a.q : a.k);
+                    kq[u] = *(const uint4 *)(src + base);
+                }
+            }
+        }
+        if (tid < kVB) {
+            const int tt = tid / kRowPkts;
+            const int off = (tid % kRowPkts) * kPerPkt;
+            const int t = t0 + tt;
+            if (t < a.T) {
+                const size_t base = (((size_t)b * a.T + t) * H + h) * a.dv + row0 + off;
+                vv = *(const uint4 *)((const TIn *)a.v + base);
+                bb = *(const uint4 *)((const TIn *)a.beta + base);
+            }
+        }
+        if (tid < C) {
+            const int t = t0 + tid;
+            if (t < a.T)
+                dtv = io<TIn>::to_f32(((const TIn *)a.dt)[((size_t)b * a.T + t) * H + h]);
+        }
+    }
+
+    // Widen and write the loaded chunk to one LDS buffer.
+    __device__ inline void commit(float *buf, float A, float Ip, int tid) const {
+        float *cols = buf;
+        float *rows = buf + C * Stage<DK>::kColFloats;
+        float *gates = rows + C * Stage<DK>::kRowFloats;
+#pragma unroll
+        for (int u = 0; u < kKQPerThread; ++u) {
+            const int p = tid + u * kThreads;
+            if (kKQ % kThreads == 0 || p < kKQ) {
+                const int tt = p / (2 * kColPkts);
+                const int arr = (p / kColPkts) & 1;
+                const int off = (p % kColPkts) * kPerPkt;
+                float x[kPerPkt];
+                packet<TIn>::widen(kq[u], x);
+                float *dst = cols + tt * Stage<DK>::kColFloats + off;
+                if (arr == 0) {   // k and k^2
+#pragma unroll
+                    for (int e = 0; e < kPerPkt; e += 4) {
+                        *(float4 *)(dst + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+                        *(float4 *)(dst + DK + e) = make_float4(x[e] * x[e], x[e + 1] * x[e + 1],
+                                                                x[e + 2] * x[e + 2], x[e + 3] * x[e + 3]);
+                    }
+                } else {          // q
+#pragma unroll
+                    for (int e = 0; e < kPerPkt; e += 4)
+                        *(float4 *)(dst + 2 * DK + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+                }
+            }
+        }
+        if (tid < kVB) {
+            const int tt = tid / kRowPkts;
+            const int off = (tid % kRowPkts) * kPerPkt;
+            float xv[kPerPkt], xb[kPerPkt];
+            packet<TIn>::widen(vv, xv);
+            packet<TIn>::widen(bb, xb);
+            float *dst = rows + tt * Stage<DK>::kRowFloats + 2 * off;
+#pragma unroll
+            for (int e = 0; e < kPerPkt; e += 2)
+                *(float4 *)(dst + 2 * e) = make_float4(xb[e], xb[e] * xv[e], xb[e + 1], xb[e + 1] * xv[e + 1]);
+        }
+        if (tid < C)
+            *(float2 *)(gates + 2 * tid) = gate(A, dtv, Ip);
+    }
+};
+
+template <int DK>
+struct LaneTile {
+    static constexpr int kCols = DK / kLanesPerRow;          // key columns per lane
+    static constexpr int kVec = kCols < 4 ? kCols : 4;       // floats per LDS vector read
+    static constexpr int kNVec = kCols / kVec;
+    // column of entry (m, e) for lane g of its row: vectors interleaved so that
+    // the 16 lanes of a row read one contiguous 16*kVec-float span per m.
+    __device__ static inline int col(int g, int m, int e) { return kVec * g + kLanesPerRow * kVec * m + e; }
+};
+
+template <int V> struct vecf;
+template <> struct vecf<4> {
+    __device__ static inline void ld(const float *p, float *o) {
+        const float4 x = *(const float4 *)p; o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+    }
+    __device__ static inline void st(float *p, const float *o) { *(float4 *)p = make_float4(o[0], o[1], o[2], o[3]); }
+};
+template <> struct vecf<2> {
+    __device__ static inline void ld(const float *p, float *o) {
+        const float2 x = *(const float2 *)p; o[0] = x.x; o[1] = x.y;
+    }
+    __device__ static inline void st(float *p, const float *o) { *(float2 *)p = make_float2(o[0], o[1]); }
+};
+
+// The per-token hot loop over n staged tokens.
+template <int DK, int C, typename TOut>
+__device__ inline void compute_chunk(const float *buf, int n, float *M, float *I,
+                                     int row_local, int g, TOut *yrow, size_t ystride) {
+    using LT = LaneTile<DK>;
+    const float *cols = buf;
+    const float *rows = buf + C * Stage<DK>::kColFloats;
+    const float *gates = rows + C * Stage<DK>::kRowFloats;
+#pragma unroll 2
+    for (int tt = 0; tt < n; ++tt) {
+        const float2 gc = *(const float2 *)(gates + 2 * tt);                          // alpha, c
+        const float2 rb = *(const float2 *)(rows + tt * Stage<DK>::kRowFloats + 2 * row_local);  // beta, beta*v
+        const float *ct = cols + tt * Stage<DK>::kColFloats;
+        float acc[2] = {0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < LT::kNVec; ++m) {
+            float kk[LT::kVec], k2[LT::kVec], qq[LT::kVec];
+            const int c0 = LT::col(g, m, 0);
+            vecf<LT::kVec>::ld(ct + c0, kk);
+            vecf<LT::kVec>::ld(ct + DK + c0, k2);
+            vecf<LT::kVec>::ld(ct + 2 * DK + c0, qq);
+#pragma unroll
+            for (int e = 0; e < LT::kVec; ++e) {
+                const int s = m * LT::kVec + e;
+                const float w = fmaf(rb.x, k2[e], gc.y);
+                I[s] = fmaf(gc.x, I[s], w);
+                M[s] = fmaf(gc.x, M[s], rb.y * kk[e]);
+                const float r = __builtin_amdgcn_rcpf(I[s]);
+                acc[s & 1] = fmaf(M[s] * r, qq[e], acc[s & 1]);
+            }
+        }
+        const float yv = row16_sum(acc[0] + acc[1]);
+        if (g == 0)
+            yrow[(size_t)tt * ystride] = io<TOut>::from_f32(yv);
+    }
+}
+
+template <int DK, int C, typename TIn, typename TOut>
+__global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
+    using LT = LaneTile<DK>;
+    extern __shared__ float lds[];
+    float *buf0 = lds;
+    float *buf1 = lds + C * Stage<DK>::kTokFloats;
+
+    // workgroup -> (head, row block), keeping one head's row blocks on one XCD
+    const int rb_per_head = a.dv / kRowsPerWG;
+    int wg = blockIdx.x;
+    if (a.xcd_remap) {
+        const int per_xcd = a.nwg / 8;
+        wg = (wg % 8) * per_xcd + wg / 8;
+    }
+    const int bh = wg / rb_per_head;
+    const int row0 = (wg % rb_per_head) * kRowsPerWG;
+    const int b = bh / a.H, h = bh % a.H;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane & (kLanesPerRow - 1);
+    const int row_local = wave * kRowsPerWave + (lane >> 4);
+    const int row = row0 + row_local;
+
+    const float A = a.A[h], Ip = a.Ip[h];
+
+    // initial state: M = I0 . mu0, I = I0   (or M = 0, I = I_prior)
+    float M[LT::kCols], I[LT::kCols];
+    const size_t srow = ((size_t)bh * a.dv + row) * DK;
+    if (a.mu0) {
+#pragma unroll
+        for (int m = 0; m < LT::kNVec; ++m) {
+            float mu[LT::kVec], ii[LT::kVec];
+            vecf<LT::kVec>::ld(a.mu0 + srow + LT::col(g, m, 0), mu);
+            vecf<LT::kVec>::ld(a.I0 + srow + LT::col(g, m, 0), ii);
+#pragma unroll
+            for (int e = 0; e < LT::kVec; ++e) {
+                I[m * LT::kVec + e] = ii[e];
+                M[m * LT::kVec + e] = ii[e] * mu[e];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < LT::kCols; ++s) { I[s] = Ip; M[s] = 0.f; }
+    }
+
+    const int nchunks = (a.T + C - 1) / C;
+    const size_t ystride = (size_t)a.H * a.dv;
+    TOut *ybase = (TOut *)a.y + ((size_t)b * a.T * a.H + h) * a.dv + row;
+
+    Stager<DK, C, TIn> st;
+    if (nchunks > 0) {
+        st.load(a, b, h, row0, 0, tid);
+        st.commit(buf0, A, Ip, tid);
+        __syncthreads();
+    }
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * C;
+        const bool more = c + 1 < nchunks;
+        if (more) st.load(a, b, h, row0, t0 + C, tid);
+        const float *cur = (c & 1) ? buf1 : buf0;
+        const int n = min(C, a.T - t0);
+        TOut *yrow = ybase + (size_t)t0 * ystride;
+        if (n == C)
+            compute_chunk<DK, C, TOut>(cur, C, M, I, row_local, g, yrow, ystride);
+        else
+            compute_chunk<DK, C, TOut>(cur, n, M, I, row_local, g, yrow, ystride);
+        if (more) st.commit((c & 1) ? buf0 : buf1, A, Ip, tid);
+        __syncthreads();
+    }
+
+    // final state: mu = M / I (correctly rounded division), I
+    if (a.muT) {
+#pragma unroll
+        for (int m = 0; m < LT::kNVec; ++m) {
+            float mu[LT::kVec], ii[LT::kVec];
+            if (nchunks == 0 && a.mu0) {
+                vecf<LT::kVec>::ld(a.mu0 + srow + LT::col(g, m, 0), mu);   // copy through exactly
+            } else {
+#pragma unroll
+                for (int e = 0; e < LT::kVec; ++e) mu[e] = M[m * LT::kVec + e] / I[m * LT::kVec + e];
+            }
+#pragma unroll
+            for (int e = 0; e < LT::kVec; ++e) ii[e] = I[m * LT::kVec + e];
+            vecf<LT::kVec>::st(a.muT + srow + LT::col(g, m, 0), mu);
+            vecf<LT::kVec>::st(a.IT + srow + LT::col(g, m, 0), ii);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// decode step
+// ---------------------------------------------------------------------------
+
+struct StepArgs {
+    const void *q, *k, *v, *beta, *dt;
+    const float *A, *Ip;
+    float *mu, *I;
+    void *y;
+    int B, H, dv;
+    long long rows;    // B * H * dv
+};
+
+constexpr int kStepThreads = 256;
+
+// Sum over groups of W consecutive lanes (W a power of two <= 32).
+template <int W>
+__device__ inline float group_sum(float x) {
+    if (W >= 16) x = row16_sum(x);
+    else {
+#pragma unroll
+        for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    }
+    if (W == 32) x += __shfl_xor(x, 16, 64);
+    return x;
+}
+
+template <int DK, typename TIn, typename TOut>
+__global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
+    constexpr int kTPR = DK / 4;                    // threads per value row, 4 columns each
+    constexpr int kRowsPerBlock = kStepThreads / kTPR;
+    const int tid = threadIdx.x;
+    const long long row = (long long)blockIdx.x * kRowsPerBlock + tid / kTPR;
+    const int j0 = (tid % kTPR) * 4;
+    // every lane of a row group takes part in the reduction, so rows past the
+    // end are clamped (and not stored) instead of returning early
+    const bool valid = row < a.rows;
+    const long long r = valid ? row : a.rows - 1;
+    const long long bh = r / a.dv;
+    const int i = (int)(r % a.dv);
+    const int h = (int)(bh % a.H);
+
+    const TIn *qp = (const TIn *)a.q + bh * DK + j0;
+    const TIn *kp = (const TIn *)a.k + bh * DK + j0;
+    float qq[4], kk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { qq[e] = io<TIn>::to_f32(qp[e]); kk[e] = io<TIn>::to_f32(kp[e]); }
+    const float bt = io<TIn>::to_f32(((const TIn *)a.beta)[bh * a.dv + i]);
+    const float bv = bt * io<TIn>::to_f32(((const TIn *)a.v)[bh * a.dv + i]);
+    const float2 gc = gate(a.A[h], io<TIn>::to_f32(((const TIn *)a.dt)[bh]), a.Ip[h]);
+
+    f32x4 *mup = (f32x4 *)(a.mu + r * DK + j0);
+    f32x4 *Ipp = (f32x4 *)(a.I + r * DK + j0);
+    const f32x4 mu4 = __builtin_nontemporal_load(mup);
+    const f32x4 I4 = __builtin_nontemporal_load(Ipp);
+    const float mu[4] = {mu4[0], mu4[1], mu4[2], mu4[3]};
+    const float Io[4] = {I4[0], I4[1], I4[2], I4[3]};
+    float mun[4], In[4], acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        In[e] = fmaf(gc.x, Io[e], fmaf(bt, kk[e] * kk[e], gc.y));
+        const float num = fmaf(gc.x * Io[e], mu[e], bv * kk[e]);   // alpha I mu + beta v k
+        mun[e] = num / In[e];
+        acc = fmaf(mun[e], qq[e], acc);
+    }
+    const float yv = group_sum<kTPR>(acc);
+    if (valid) {
+        const f32x4 mo = {mun[0], mun[1], mun[2], mun[3]};
+        const f32x4 io4 = {In[0], In[1], In[2], In[3]};
+        __builtin_nontemporal_store(mo, mup);
+        __builtin_nontemporal_store(io4, Ipp);
+        if (tid % kTPR == 0)
+            ((TOut *)a.y)[r] = io<TOut>::from_f32(yv);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool head_ok(int d) { return d == 32 || d == 64 || d == 128; }
+inline bool dtype_ok(int t) { return t == PALIMPSA_F32 || t == PALIMPSA_BF16; }
+
+template <int DK, int C, typename TIn, typename TOut>
+palimpsa_status launch_fwd_t(const FwdArgs &a0, hipStream_t s) {
+    FwdArgs a = a0;
+    const size_t lds = fwd_lds_bytes<DK, C>();
+    auto kern = fwd_chunked_kernel<DK, C, TIn, TOut>;
+    if (lds > 64 * 1024) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return PALIMPSA_ERR_HIP;
+    }
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(kern, dim3(a.nwg), dim3(kThreads), lds, s, a);
+    return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
+}
+
+template <int DK, typename TIn, typename TOut>
+palimpsa_status launch_fwd_c(const FwdArgs &a, int C, hipStream_t s) {
+    switch (C) {
+    case 8: return launch_fwd_t<DK, 8, TIn, TOut>(a, s);
+    case 16: return launch_fwd_t<DK, 16, TIn, TOut>(a, s);
+    case 32: return launch_fwd_t<DK, 32, TIn, TOut>(a, s);
+    default: return launch_fwd_t<DK, 64, TIn, TOut>(a, s);
+    }
+}
+
+template <typename TIn, typename TOut>
+palimpsa_status launch_fwd_d(const FwdArgs &a, int dk, int C, hipStream_t s) {
+    switch (dk) {
+    case 32: return launch_fwd_c<32, TIn, TOut>(a, C, s);
+    case 64: return launch_fwd_c<64, TIn, TOut>(a, C, s);
+    default: return launch_fwd_c<128, TIn, TOut>(a, C, s);
+    }
+}
+
+size_t lds_bytes_for(int dk, int C) { return (size_t)2 * C * (3 * dk + 2 * kRowsPerWG + 2) * sizeof(float); }
+
+// Chunk actually used: the request if given (shrunk until its buffers fit the
+// device's LDS), else the largest that lets three workgroups share a CU when
+// there are enough workgroups to need it.
+int pick_chunk(int requested, int dk, long long nwg, size_t lds_max) {
+    int C = requested;
+    if (C == 0) {
+        const size_t budget = nwg > 256 ? 54 * 1024 : lds_max;
+        C = 64;
+        while (C > 8 && lds_bytes_for(dk, C) > budget) C /= 2;
+    }
+    while (C > 8 && lds_bytes_for(dk, C) > lds_max) C /= 2;
+    return C;
+}
+
+size_t device_lds_max() {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 64 * 1024;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
+        return 64 * 1024;
+    return (size_t)v;
+}
+
+}  // namespace
+
+extern "C" {
+
+palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v,
+                                     const void *beta, const void *dt,
+                                     const float *A, const float *I_prior,
+                                     const float *mu0, const float *I0,
+                                     void *y, float *muT, float *IT,
+                                     int B, int T, int H, int dk, int dv, int chunk,
+                                     palimpsa_dtype in_dtype, palimpsa_dtype out_dtype,
+                                     void *stream) {
+    if (!q || !k || !v || !beta || !dt || !A || !I_prior || (!y && T > 0))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if ((mu0 == nullptr) != (I0 == nullptr) || (muT == nullptr) != (IT == nullptr))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0)
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (chunk != 0 && chunk != 8 && chunk != 16 && chunk != 32 && chunk != 64)
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (!head_ok(dk) || !head_ok(dv))
+        return PALIMPSA_ERR_UNSUPPORTED;
+    const void *ptrs[] = {q, k, v, beta, dt, A, I_prior, mu0, I0, y, muT, IT};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return PALIMPSA_ERR_ALIGNMENT;
+    const long long nwg = (long long)B * H * (dv / kRowsPerWG);
+    if (nwg > 0x7fffffffLL || (long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 46))
+        return PALIMPSA_ERR_UNSUPPORTED;
+
+    FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.dt = dt;
+    a.A = A; a.Ip = I_prior; a.mu0 = mu0; a.I0 = I0;
+    a.y = y; a.muT = muT; a.IT = IT;
+    a.B = B; a.T = T; a.H = H; a.dv = dv;
+    a.nwg = (int)nwg;
+    a.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
+
+    if (T == 0 && !muT) return PALIMPSA_OK;   // nothing to compute or write
+    const int C = pick_chunk(chunk, dk, nwg, device_lds_max());
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf_in = in_dtype == PALIMPSA_BF16, bf_out = out_dtype == PALIMPSA_BF16;
+    if (bf_in && bf_out) return launch_fwd_d<bf16_t, bf16_t>(a, dk, C, s);
+    if (bf_in) return launch_fwd_d<bf16_t, float>(a, dk, C, s);
+    if (bf_out) return launch_fwd_d<float, bf16_t>(a, dk, C, s);
+    return launch_fwd_d<float, float>(a, dk, C, s);
+}
+
+palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
+                              const void *beta, const void *dt,
+                              const float *A, const float *I_prior,
+                              float *mu, float *I, void *y,
+                              int B, int H, int dk, int dv,
+                              palimpsa_dtype in_dtype, palimpsa_dtype out_dtype,
+                              void *stream) {
+    if (!q || !k || !v || !beta || !dt || !A || !I_prior || !mu || !I || !y)
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (!head_ok(dk) || !head_ok(dv))
+        return PALIMPSA_ERR_UNSUPPORTED;
+    const void *ptrs[] = {q, k, v, beta, dt, A, I_prior, mu, I, y};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return PALIMPSA_ERR_ALIGNMENT;
+    const long long rows = (long long)B * H * dv;
+    if (rows * dk > (1LL << 46))
+        return PALIMPSA_ERR_UNSUPPORTED;
+
+    StepArgs a;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.dt = dt;
+    a.A = A; a.Ip = I_prior; a.mu = mu; a.I = I; a.y = y;
+    a.B = B; a.H = H; a.dv = dv; a.rows = rows;
+    const int rows_per_block = kStepThreads / (dk / 4);
+    const long long blocks = (rows + rows_per_block - 1) / rows_per_block;
+    if (blocks > 0x7fffffffLL) return PALIMPSA_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf_in = in_dtype == PALIMPSA_BF16, bf_out = out_dtype == PALIMPSA_BF16;
+    (void)hipGetLastError();
+#define PALIMPSA_STEP_LAUNCH(DK_, TI, TO) \
+    hipLaunchKernelGGL((step_kernel<DK_, TI, TO>), dim3((unsigned)blocks), dim3(kStepThreads), 0, s, a)
+#define PALIMPSA_STEP_TYPES(DK_)                                              \
+    do {                                                                      \
+        if (bf_in && bf_out) PALIMPSA_STEP_LAUNCH(DK_, bf16_t, bf16_t);       \
+        else if (bf_in) PALIMPSA_STEP_LAUNCH(DK_, bf16_t, float);             \
+        else if (bf_out) PALIMPSA_STEP_LAUNCH(DK_, float, bf16_t);            \
+        else PALIMPSA_STEP_LAUNCH(DK_, float, float);                         \
+    } while (0)
+    switch (dk) {
+    case 32: PALIMPSA_STEP_TYPES(32); break;
+    case 64: PALIMPSA_STEP_TYPES(64); break;
+    default: PALIMPSA_STEP_TYPES(128); break;
+    }
+#undef PALIMPSA_STEP_TYPES
+#undef PALIMPSA_STEP_LAUNCH
+    return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
+}
+
+const char *palimpsa_status_string(int status) {
+    switch (status) {
+    case PALIMPSA_OK: return "ok";
+    case PALIMPSA_ERR_INVALID_ARG: return "invalid argument (null pointer, size or enum)";
+    case PALIMPSA_ERR_UNSUPPORTED: return "unsupported configuration (head size must be 32, 64 or 128)";
+    case PALIMPSA_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
+    case PALIMPSA_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+    }
+}
+
+int palimpsa_version(void) { return PALIMPSA_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Benchmark of the Palimpsa chunked forward on one MI355X.
+
+One step = one palimpsa_fwd_chunked pass over the 760M-model layer workload
+(B=8, H=12, T=4096, d_k=d_v=128, bf16 inputs and output, float32 state),
+inputs resident in HBM.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+The roofline object reports the chunked-forward kernel against the FP32
+vector-ALU issue roof (the binding one: the readout divides by a per-token,
+per-entry precision, so there is no dense contraction for the matrix cores,
+and the kernel needs only a few hundred GB/s of HBM).  Per state-entry update
+the method needs 4 FMA + 2 MUL + 1 reciprocal = 10 flops + 1 rcp.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# Chip constants used by the ALU roof (MI355X: 256 CUs x 4 SIMDs, each SIMD
+# issuing one wave64 FP32 VALU instruction every 4 clocks = 16 lane-ops/clk,
+# at the 2.4 GHz peak engine clock).  Packed FP32 is not used by this build,
+# so one FMA is one lane-op.
+CUS, SIMDS, LANES_PER_CLK, CLOCK_HZ = 256, 4, 16, 2.4e9
+LANE_OPS_PER_S = CUS * SIMDS * LANES_PER_CLK * CLOCK_HZ       # 3.93e13
+VALU_PER_UPDATE = 6          # 4 FMA + 2 MUL
+RCP_SLOTS = 4                # v_rcp_f32 issue cost in FMA slots (quarter rate)
+FLOPS_PER_UPDATE = 10        # FMA = 2 flops, MUL = 1; the reciprocal is not counted
+HBM_PEAK_GBS = 8000.0
+
+
+def alu_peak_tflops():
+    updates_per_s = LANE_OPS_PER_S / (VALU_PER_UPDATE + RCP_SLOTS)
+    return updates_per_s * FLOPS_PER_UPDATE / 1e12
+
+
+def kernel_source_hash():
+    p = os.path.join(ROOT, "bayesian_metaplastic_memory_amd", "csrc", "palimpsa.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(name):
+    """HBM traffic per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", name)
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup, torch):
+    """Run fn() warmup times, then time `steps` calls with one event pair per
+    launch on the current stream (the stream the kernels are enqueued on)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    outer0 = torch.cuda.Event(enable_timing=True)
+    outer1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    outer0.record()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    outer1.record()
+    torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return outer0.elapsed_time(outer1), per
+
+
+def cpu_baseline(inp, w, max_heads):
+    import numpy as np
+    import oracle
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:max_heads]
+    sub = oracle.select_heads(inp, heads)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.fwd(**sub, nthreads=threads)
+    wall = time.perf_counter() - t0
+    layer_seqs = len(heads) / w.H                # sampled heads as a fraction of B sequences
+    return {"value": layer_seqs * w.T / wall, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d heads (b,h) at full T=%d, float64 sequential Eq. (5), "
+                      "OpenMP over heads; %.1f s wall" % (len(heads), w.B * w.H, w.T, wall)}
+
+
+def decode_extra(torch, pm, workloads, steps):
+    """Decode step at B=64, H=32, d=128 (state 268 MB read + written per step)."""
+    w = workloads.WORKLOADS[3]
+    dev = torch.device("cuda:0")
+    A, Ip = (x.to(dev) for x in workloads.head_constants(w))
+    mu0, I0 = workloads.random_state(w.B, w.H, w.dv, w.dk, Ip.cpu(), seed=7)
+    mu, I = mu0.to(dev), I0.to(dev)
+    d = {n: x.to(dev) for n, x in workloads.decode_inputs(w, 0).items()}
+    y = torch.empty(w.B, w.H, w.dv, dtype=w.dtype, device=dev)
+    fn = lambda: pm.step(d["q"], d["k"], d["v"], d["beta"], d["dt"], A, Ip, mu, I, y=y)
+    total_ms, per = time_launches(fn, steps, 5, torch)
+    avg_s = sum(per) / len(per) / 1e3
+    state_bytes = 16 * w.B * w.H * w.dv * w.dk
+    in_bytes = 2 * w.B * w.H * (2 * w.dk + 2 * w.dv + 1) + 2 * w.B * w.H * w.dv
+    return {"workload": "decode B=64 H=32 d_k=d_v=128, bf16 inputs, fp32 state",
+            "tokens_per_s": w.B / avg_s, "us_per_step": avg_s * 1e6,
+            "roofline": {"bound": "hbm", "achieved": (state_bytes + in_bytes) / avg_s / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": (state_bytes + in_bytes) / avg_s / 1e9 / HBM_PEAK_GBS,
+                         "traffic": load_traffic("step_kernel_decode_B64_H32_d128_traffic.json")}}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads in the oracle sample (0: all heads of the workload)")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--chunk", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads shard across GPUs with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bayesian_metaplastic_memory_amd as pm
+    import workloads
+
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[2]
+    inp = workloads.make_inputs(w)
+    g = {n: (x.to(dev) if isinstance(x, torch.Tensor) else x) for n, x in inp.items()}
+    y = torch.empty(w.B, w.T, w.H, w.dv, dtype=w.dtype, device=dev)
+    muT = torch.empty(w.B, w.H, w.dv, w.dk, device=dev)
+    IT = torch.empty_like(muT)
+    args_fwd = (g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"])
+    fn = lambda: pm.fwd_chunked(*args_fwd, chunk=args.chunk, y=y, muT=muT, IT=IT)
+
+    total_ms, per = time_launches(fn, args.steps, args.warmup, torch)
+    avg_launch_s = sum(per) / len(per) / 1e3
+    tokens = w.B * w.T
+    updates = w.B * w.H * w.T * w.dv * w.dk
+    achieved = updates * FLOPS_PER_UPDATE / avg_launch_s / 1e12
+    peak = alu_peak_tflops()
+    traffic = load_traffic("fwd_chunked_layer760m_bf16_traffic.json")
+    hbm_alg = (w.B * w.T * w.H * (2 * w.dk + 2 * w.dv + 1 + w.dv) * 2
+               + 8 * w.B * w.H * w.dv * w.dk)
+    out = {
+        "metric": "tokens/s of Palimpsa chunked forward (B*T/s) and % of HBM/MFMA roofline",
+        "value": tokens * args.steps / (total_ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "760M-model layer, chunked forward", "B": w.B, "H": w.H,
+                   "T": w.T, "d_k": w.dk, "d_v": w.dv, "chunk": args.chunk or "auto",
+                   "inputs": "bf16", "state": "fp32", "global_batch": w.B, "seq_len": w.T},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "kernel": "fwd_chunked_kernel<128, C, bf16, bf16>",
+                     "avg_launch_ms": avg_launch_s * 1e3,
+                     "per_update": "4 FMA + 2 MUL (10 flops) + 1 v_rcp_f32 (4 FMA slots)",
+                     "hbm_algorithmic_GBs": hbm_alg / avg_launch_s / 1e9},
+    }
+    if not args.no_decode:
+        out["decode"] = decode_extra(torch, pm, workloads, max(10, args.steps))
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads or w.B * w.H)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

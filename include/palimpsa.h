@@ -1,0 +1,123 @@
+/*
+ * palimpsa.h - C ABI of libpalimpsa.so, the MI355X (gfx950) implementation
+ * of the Palimpsa dual-state recurrence.
+ *
+ * The operation ("Learning to Remember, Learn, and Forget in Attention-Based
+ * Models", slides frames "The attention state is an online regression
+ * model", "Forgetting discounts evidence and restores the prior" and
+ * "Palimpsa updates content and importance together", Eqs. (1)-(2), (5), (9)):
+ * for every sequence b and head h, with value channel i < dv and key
+ * channel j < dk,
+ *
+ *     alpha_t    = exp(-A[h] * dt[b,t,h])                       (gate, in (0, 1])
+ *     I_t[i,j]   = alpha_t I_{t-1}[i,j] + (1 - alpha_t) I_prior[h]
+ *                  + beta[b,t,h,i] * k[b,t,h,j]^2                (importance)
+ *     mu_t[i,j]  = alpha_t (I_{t-1}[i,j] / I_t[i,j]) mu_{t-1}[i,j]
+ *                  + beta[b,t,h,i] v[b,t,h,i] k[b,t,h,j] / I_t[i,j]   (content)
+ *     y[b,t,h,i] = sum_j mu_t[i,j] q[b,t,h,j]                   (readout, after the write)
+ *
+ * The chunked forward evaluates it in the natural parameters M = I . mu and
+ * I (slides frame "Natural parameters expose two affine scans", App. A.12),
+ * which is the same function up to float32 rounding.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor pointers are DEVICE pointers, owned by the caller, contiguous and
+ *    row-major in the layouts stated per argument.  Every tensor pointer must
+ *    be 16-byte aligned.
+ *  - in_dtype applies to q, k, v, beta and dt; out_dtype to y.  A, I_prior and
+ *    every state array are float32.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL means the default
+ *    stream) and runs asynchronously; the caller synchronises.
+ *  - The library allocates no device memory and keeps no per-call state.
+ *  - Every argument is checked on the host before anything is launched; an
+ *    invalid call returns an error code and launches nothing.  No C++
+ *    exception crosses this interface.
+ *  - Data preconditions that are NOT checked (they live in device memory):
+ *    A >= 0 and finite, I_prior > 0, beta >= 0, dt >= 0, I0 > 0, all inputs
+ *    finite.  Violations give unspecified values, never a fault.
+ *  - Supported head sizes: dk, dv in {32, 64, 128}.
+ */
+#ifndef PALIMPSA_H
+#define PALIMPSA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PALIMPSA_OK = 0,
+    PALIMPSA_ERR_INVALID_ARG = 1,  /* null pointer, negative or zero size, bad enum */
+    PALIMPSA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head size, dtype pair) */
+    PALIMPSA_ERR_ALIGNMENT = 3,    /* a tensor pointer is not 16-byte aligned */
+    PALIMPSA_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
+} palimpsa_status;
+
+typedef enum {
+    PALIMPSA_F32 = 0,
+    PALIMPSA_BF16 = 1
+} palimpsa_dtype;
+
+/*
+ * Chunked forward over a whole sequence (training / prefill).
+ *
+ *   q, k      [B, T, H, dk]  in_dtype
+ *   v, beta   [B, T, H, dv]  in_dtype
+ *   dt        [B, T, H]      in_dtype
+ *   A         [H]            float32, per-head decay rate
+ *   I_prior   [H]            float32, per-head prior precision
+ *   mu0, I0   [B, H, dv, dk] float32 initial state; both NULL means
+ *                            mu0 = 0 and I0 = I_prior (one NULL alone is an error)
+ *   y         [B, T, H, dv]  out_dtype, every token's readout
+ *   muT, IT   [B, H, dv, dk] float32 final state; both NULL skips writing it
+ *                            (one NULL alone is an error).  muT may alias mu0
+ *                            and IT may alias I0 (in-place resume).
+ *   chunk     tokens staged per step through on-chip memory, one of
+ *             {8, 16, 32, 64}, or 0 for the library's choice.  Results do not
+ *             depend on it beyond float32 rounding.
+ *
+ * T == 0 is valid: y is empty and the state is copied through (or, with both
+ * mu0 and I0 NULL, set to mu = 0, I = I_prior).  B, H >= 1.
+ * bf16 inputs are read exactly; bf16 outputs are rounded to nearest even.
+ */
+palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v,
+                                     const void *beta, const void *dt,
+                                     const float *A, const float *I_prior,
+                                     const float *mu0, const float *I0,
+                                     void *y, float *muT, float *IT,
+                                     int B, int T, int H, int dk, int dv, int chunk,
+                                     palimpsa_dtype in_dtype, palimpsa_dtype out_dtype,
+                                     void *stream);
+
+/*
+ * One decode token (recurrent inference): the recurrence above for a single
+ * t, applied in place to a state held as (mu, I).
+ *
+ *   q, k      [B, H, dk]     in_dtype
+ *   v, beta   [B, H, dv]     in_dtype
+ *   dt        [B, H]         in_dtype
+ *   A, I_prior [H]           float32
+ *   mu, I     [B, H, dv, dk] float32, read and overwritten with the new state
+ *   y         [B, H, dv]     out_dtype
+ */
+palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
+                              const void *beta, const void *dt,
+                              const float *A, const float *I_prior,
+                              float *mu, float *I, void *y,
+                              int B, int H, int dk, int dv,
+                              palimpsa_dtype in_dtype, palimpsa_dtype out_dtype,
+                              void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *palimpsa_status_string(int status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int palimpsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PALIMPSA_H */

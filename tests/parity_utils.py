@@ -1,0 +1,49 @@
+"""Shared helpers for the GPU parity tests (test infrastructure)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+# Parity bars against the float64 oracle: normwise max relative error per
+# output tensor, max|x - ref| / max|ref|.
+TOL_F32 = 1e-4
+TOL_BF16 = 2e-2
+
+
+def tol_for(dtype) -> float:
+    return TOL_BF16 if dtype == torch.bfloat16 else TOL_F32
+
+
+def to_np(x) -> np.ndarray:
+    if isinstance(x, torch.Tensor):
+        x = x.detach()
+        if x.dtype == torch.bfloat16:
+            x = x.float()
+        return x.cpu().numpy().astype(np.float64)
+    return np.asarray(x, dtype=np.float64)
+
+
+def rel_err(x, ref) -> float:
+    x, ref = to_np(x), to_np(ref)
+    assert x.shape == ref.shape, (x.shape, ref.shape)
+    if x.size == 0:
+        return 0.0
+    den = np.abs(ref).max()
+    return float(np.abs(x - ref).max() / (den if den > 0 else 1.0))
+
+
+def assert_close(name, x, ref, tol, log=None):
+    e = rel_err(x, ref)
+    if log is not None:
+        log[name] = e
+    print("  %-22s max normwise rel err %.3e (bar %.0e)" % (name, e, tol), flush=True)
+    assert np.isfinite(to_np(x)).all(), "%s has non-finite values" % name
+    assert e <= tol, "%s: rel err %.3e > %.1e" % (name, e, tol)
+
+
+def to_device(inp: dict, dev) -> dict:
+    return {n: (x.to(dev) if isinstance(x, torch.Tensor) else x) for n, x in inp.items()}
+
+
+def gpu_args(inp: dict):
+    return (inp["q"], inp["k"], inp["v"], inp["beta"], inp["dt"], inp["A"], inp["I_prior"])

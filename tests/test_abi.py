@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects invalid calls with the documented status codes before
+launching anything (no GPU needed: every call here fails validation)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "palimpsa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import bayesian_metaplastic_memory_amd as pm
+    if not os.path.exists(pm.LIB_PATH):
+        from bayesian_metaplastic_memory_amd import build
+        build.build()
+    return pm.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(palimpsa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("palimpsa_fwd_chunked", "palimpsa_step", "palimpsa_status_string", "palimpsa_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import bayesian_metaplastic_memory_amd as pm
+    out = subprocess.run(["nm", "-D", "--defined-only", pm.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    import bayesian_metaplastic_memory_amd as pm
+    for s in range(5):
+        assert pm.status_string(s)
+    assert pm.status_string(99) == "unknown status"
+    assert pm.version() >= 100
+
+
+FAKE = 0x10000       # 16-byte aligned host address, never dereferenced
+
+
+def _fwd_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dt=FAKE, A=FAKE, Ip=FAKE, mu0=None, I0=None,
+             y=FAKE, muT=FAKE, IT=FAKE, B=2, T=8, H=3, dk=64, dv=64, chunk=0, ind=1, outd=1,
+             stream=None)
+    a.update(over)
+    return [a[n] for n in ("q", "k", "v", "beta", "dt", "A", "Ip", "mu0", "I0", "y", "muT", "IT",
+                           "B", "T", "H", "dk", "dv", "chunk", "ind", "outd", "stream")]
+
+
+FWD_CASES = [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(dt=None), 1), (dict(A=None), 1),
+    (dict(Ip=None), 1), (dict(y=None), 1), (dict(mu0=FAKE), 1), (dict(I0=FAKE), 1),
+    (dict(muT=None), 1), (dict(IT=None), 1), (dict(B=0), 1), (dict(H=0), 1), (dict(T=-1), 1),
+    (dict(dk=0), 1), (dict(ind=2), 1), (dict(outd=-1), 1), (dict(chunk=12), 1),
+    (dict(chunk=128), 1), (dict(dk=48), 2), (dict(dv=256), 2), (dict(dk=16), 2),
+    (dict(q=FAKE + 4), 3), (dict(v=FAKE + 8), 3), (dict(y=FAKE + 2), 3),
+    (dict(mu0=FAKE + 4, I0=FAKE), 3), (dict(IT=FAKE + 12), 3),
+]
+
+
+@pytest.mark.parametrize("over,status", FWD_CASES)
+def test_fwd_rejects_invalid_calls(lib, over, status):
+    assert lib.palimpsa_fwd_chunked(*_fwd_args(**over)) == status
+
+
+def _step_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dt=FAKE, A=FAKE, Ip=FAKE, mu=FAKE, I=FAKE, y=FAKE,
+             B=2, H=3, dk=128, dv=128, ind=1, outd=1, stream=None)
+    a.update(over)
+    return [a[n] for n in ("q", "k", "v", "beta", "dt", "A", "Ip", "mu", "I", "y",
+                           "B", "H", "dk", "dv", "ind", "outd", "stream")]
+
+
+STEP_CASES = [
+    (dict(q=None), 1), (dict(mu=None), 1), (dict(I=None), 1), (dict(y=None), 1),
+    (dict(B=0), 1), (dict(H=-2), 1), (dict(ind=5), 1), (dict(dk=100), 2), (dict(dv=8), 2),
+    (dict(mu=FAKE + 4), 3), (dict(k=FAKE + 2), 3),
+]
+
+
+@pytest.mark.parametrize("over,status", STEP_CASES)
+def test_step_rejects_invalid_calls(lib, over, status):
+    assert lib.palimpsa_step(*_step_args(**over)) == status
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The package and its library never import, load or link the oracle."""
+    pkg = os.path.join(ROOT, "bayesian_metaplastic_memory_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
+                assert "palimpsa_oracle" not in text, f
+    import bayesian_metaplastic_memory_amd as pm
+    if os.path.exists(pm.LIB_PATH):
+        needed = subprocess.run(["readelf", "-d", pm.LIB_PATH], capture_output=True,
+                                text=True).stdout
+        assert "oracle" not in needed
+
+
+def test_binding_fails_loudly_without_a_gpu_tensor():
+    import torch
+    import bayesian_metaplastic_memory_amd as pm
+    x = torch.zeros(1, 4, 1, 32)
+    with pytest.raises(ValueError):
+        pm.fwd_chunked(x, x, x, x, torch.zeros(1, 4, 1), torch.ones(1), torch.ones(1))

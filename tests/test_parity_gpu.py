@@ -1,0 +1,331 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Small cases compare every output element; full-size workloads run the GPU on
+the whole batch and the oracle on sampled heads (heads are independent, so a
+sampled head's outputs are exactly that head's slice of the full run).
+Every case prints its name and shape before it touches the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity_utils import assert_close, gpu_args, rel_err, to_device, to_np, tol_for
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _pm():
+    import bayesian_metaplastic_memory_amd as pm
+    return pm
+
+
+def _announce(what, **shape):
+    print("\n[case] %s %s" % (what, " ".join("%s=%s" % kv for kv in shape.items())), flush=True)
+
+
+def _run_fwd(inp, chunk=0, out_dtype=None):
+    g = to_device(inp, DEV)
+    y, muT, IT = _pm().fwd_chunked(*gpu_args(g), mu0=g.get("mu0"), I0=g.get("I0"),
+                                   chunk=chunk, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return y, muT, IT
+
+
+def _compare_full(inp, y, muT, IT, tol, log=None):
+    y_ref, mu_ref, I_ref = oracle.fwd(**inp)
+    assert_close("y", y, y_ref, tol, log)
+    assert_close("muT", muT, mu_ref, tol, log)
+    assert_close("IT", IT, I_ref, tol, log)
+
+
+def _compare_sampled(inp, heads, y, muT, IT, tol):
+    sub = oracle.select_heads(inp, heads)
+    y_ref, mu_ref, I_ref = oracle.fwd(**sub, nthreads=len(heads))
+    bs = [b for b, _ in heads]
+    hs = [h for _, h in heads]
+    y_s = to_np(y)[bs, :, hs, :].transpose(1, 0, 2)[None]       # [1, T, S, dv]
+    assert_close("y (sampled heads)", y_s, y_ref, tol)
+    assert_close("muT (sampled heads)", to_np(muT)[bs, hs][None], mu_ref, tol)
+    assert_close("IT (sampled heads)", to_np(IT)[bs, hs][None], I_ref, tol)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------
+
+def test_tiny_fp32_full():
+    w = workloads.WORKLOADS[0]
+    _announce("fwd tiny fp32", B=w.B, H=w.H, T=w.T, d=w.dk, chunk=w.chunk)
+    inp = workloads.make_inputs(w)
+    y, muT, IT = _run_fwd(inp, chunk=w.chunk)
+    _compare_full(inp, y, muT, IT, tol_for(w.dtype))
+
+
+def test_tiny_fp32_step_sequence():
+    w = workloads.WORKLOADS[0]
+    _announce("step x T tiny fp32", B=w.B, H=w.H, T=w.T, d=w.dk)
+    inp = workloads.make_inputs(w)
+    g = to_device(inp, DEV)
+    mu = torch.zeros(w.B, w.H, w.dv, w.dk, device=DEV)
+    I = g["I_prior"].view(1, -1, 1, 1).expand(w.B, w.H, w.dv, w.dk).contiguous()
+    ys = []
+    for t in range(w.T):
+        ys.append(_pm().step(g["q"][:, t].contiguous(), g["k"][:, t].contiguous(),
+                             g["v"][:, t].contiguous(), g["beta"][:, t].contiguous(),
+                             g["dt"][:, t].contiguous(), g["A"], g["I_prior"], mu, I))
+    torch.cuda.synchronize()
+    y = torch.stack(ys, dim=1)
+    _compare_full(inp, y, mu, I, tol_for(w.dtype))
+
+
+def test_mqar_fp32_full():
+    w = workloads.WORKLOADS[1]
+    _announce("fwd mqar fp32", B=w.B, H=w.H, T=w.T, d=w.dk, chunk=w.chunk)
+    inp = workloads.make_inputs(w)
+    y, muT, IT = _run_fwd(inp, chunk=w.chunk)
+    _compare_full(inp, y, muT, IT, tol_for(w.dtype))
+
+
+LAYER_HEADS = [(0, 0), (3, 5), (7, 11), (5, 2)]
+
+
+def test_layer760m_bf16_sampled():
+    w = workloads.WORKLOADS[2]
+    _announce("fwd 760M-layer bf16", B=w.B, H=w.H, T=w.T, d=w.dk, chunk=w.chunk)
+    inp = workloads.make_inputs(w)
+    y, muT, IT = _run_fwd(inp, chunk=w.chunk)
+    _compare_sampled(inp, LAYER_HEADS, y, muT, IT, tol_for(w.dtype))
+
+
+def test_layer760m_bf16_default_chunk_bitwise_equal():
+    """The launch the bench times (library-chosen chunk) gives the same bits."""
+    w = workloads.WORKLOADS[2]
+    _announce("fwd 760M-layer bf16 chunk invariance", B=w.B, H=w.H, T=w.T)
+    inp = workloads.make_inputs(w)
+    a = _run_fwd(inp, chunk=w.chunk)
+    b = _run_fwd(inp, chunk=0)
+    for x, z in zip(a, b):
+        assert torch.equal(x, z)
+
+
+@pytest.mark.parametrize("variant", [4, "4b"])
+def test_long_context_bf16_sampled(variant):
+    w = workloads.WORKLOADS[variant]
+    _announce("fwd long-context bf16 " + str(variant), B=w.B, H=w.H, T=w.T, d=w.dk)
+    inp = workloads.make_inputs(w)
+    y, muT, IT = _run_fwd(inp, chunk=w.chunk)
+    heads = [(0, 0), (0, 31)]
+    _compare_sampled(inp, heads, y, muT, IT, tol_for(w.dtype))
+    if variant == "4b":
+        # importance stays at I_prior: the Mamba2-form recurrence gives the same readout
+        sub = oracle.select_heads(inp, heads)
+        y_lim, _ = oracle.fwd_mamba2_limit(**{n: sub[n] for n in
+                                              ("q", "k", "v", "beta", "dt", "A", "I_prior")})
+        y_s = to_np(y)[[0, 0], :, [0, 31], :].transpose(1, 0, 2)[None]
+        e = rel_err(y_s, y_lim)
+        print("  y vs Mamba2-limit recurrence: %.3e" % e, flush=True)
+        assert e <= 1e-2
+        Ibar = (to_np(IT) - 1.0).max()
+        print("  max excess importance: %.3e" % Ibar, flush=True)
+        assert Ibar < 1e-3
+
+
+def test_decode_bf16_after_prefill():
+    w = workloads.WORKLOADS[3]
+    steps = workloads.DECODE_STEPS
+    _announce("prefill + decode bf16", B=w.B, H=w.H, T=w.T, steps=steps, d=w.dk)
+    inp = workloads.make_inputs(w, device=DEV)          # drawn on the GPU (2.1 GB per array)
+    y_pre, mu, I = _pm().fwd_chunked(*gpu_args(inp), chunk=w.chunk)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (17, 9), (63, 31)]
+    bs = [b for b, _ in heads]
+    hs = [h for _, h in heads]
+    sub_in = {}
+    for n in ("q", "k", "v", "beta"):
+        sub_in[n] = inp[n][bs, :, hs, :].transpose(0, 1).unsqueeze(0).cpu()   # [1, T, S, d]
+    sub_in["dt"] = inp["dt"][bs, :, hs].transpose(0, 1).unsqueeze(0).cpu()
+    sub_in["A"] = inp["A"][hs].cpu()
+    sub_in["I_prior"] = inp["I_prior"][hs].cpu()
+    y_ref, m_ref, P_ref = oracle.fwd(**sub_in, nthreads=len(heads))
+    tol = tol_for(w.dtype)
+    y_s = to_np(y_pre[bs, :, hs, :].transpose(0, 1).unsqueeze(0))
+    assert_close("prefill y (sampled)", y_s, y_ref, tol)
+    assert_close("prefill mu (sampled)", to_np(mu[bs, hs]).reshape(m_ref.shape), m_ref, tol)
+    assert_close("prefill I (sampled)", to_np(I[bs, hs]).reshape(P_ref.shape), P_ref, tol)
+    del inp, y_pre
+    worst = 0.0
+    A_s, Ip_s = sub_in["A"], sub_in["I_prior"]
+    for s in range(steps):
+        d = workloads.decode_inputs(w, s, device=DEV)
+        y = _pm().step(d["q"], d["k"], d["v"], d["beta"], d["dt"], w_A(w, DEV), w_Ip(w, DEV), mu, I)
+        ds = {n: d[n][bs, hs].unsqueeze(0).cpu() for n in ("q", "k", "v", "beta", "dt")}
+        yr, m_ref, P_ref = oracle.step(ds["q"], ds["k"], ds["v"], ds["beta"], ds["dt"],
+                                       A_s, Ip_s, m_ref, P_ref)
+        e = rel_err(to_np(y[bs, hs]).reshape(yr.shape), yr)
+        worst = max(worst, e)
+        if s % 256 == 0:
+            print("  step %4d y rel err %.3e" % (s, e), flush=True)
+        assert e <= tol, "step %d: %.3e" % (s, e)
+    torch.cuda.synchronize()
+    print("  worst step y rel err %.3e" % worst, flush=True)
+    assert_close("final mu (sampled)", to_np(mu[bs, hs]).reshape(m_ref.shape), m_ref, tol)
+    assert_close("final I (sampled)", to_np(I[bs, hs]).reshape(P_ref.shape), P_ref, tol)
+
+
+def w_A(w, dev):
+    return workloads.head_constants(w)[0].to(dev)
+
+
+def w_Ip(w, dev):
+    return workloads.head_constants(w)[1].to(dev)
+
+
+# ---------------------------------------------------------------------------
+# invariances and cross-entry consistency
+# ---------------------------------------------------------------------------
+
+def test_chunk_size_is_bitwise_invariant():
+    w = workloads.WORKLOADS[1].with_(B=2, H=3)
+    _announce("chunk invariance", B=w.B, H=w.H, T=300, d=w.dk)
+    inp = workloads.make_inputs(w, T=300)
+    mu0, I0 = workloads.random_state(w.B, w.H, w.dv, w.dk, inp["I_prior"], seed=5)
+    inp["mu0"], inp["I0"] = mu0, I0
+    outs = [_run_fwd(inp, chunk=c) for c in (8, 16, 32, 64, 0)]
+    for o in outs[1:]:
+        for x, z in zip(outs[0], o):
+            assert torch.equal(x, z)
+    _compare_full(inp, *outs[0], tol=1e-4)
+
+
+def test_split_and_resume_matches_one_pass():
+    w = workloads.WORKLOADS[1].with_(B=2, H=2)
+    T, T1 = 257, 100
+    _announce("split/resume", B=w.B, H=w.H, T=T, T1=T1, d=w.dk)
+    inp = workloads.make_inputs(w, T=T)
+    g = to_device(inp, DEV)
+    pm = _pm()
+    y, muT, IT = pm.fwd_chunked(*gpu_args(g))
+    first = {n: (x[:, :T1].contiguous() if n in ("q", "k", "v", "beta", "dt") else x) for n, x in g.items()}
+    second = {n: (x[:, T1:].contiguous() if n in ("q", "k", "v", "beta", "dt") else x) for n, x in g.items()}
+    y1, mu1, I1 = pm.fwd_chunked(*gpu_args(first))
+    # resume in place: the final state overwrites the initial state
+    y2, mu2, I2 = pm.fwd_chunked(*gpu_args(second), mu0=mu1, I0=I1, muT=mu1, IT=I1)
+    torch.cuda.synchronize()
+    assert mu2.data_ptr() == mu1.data_ptr()
+    assert rel_err(torch.cat([y1, y2], dim=1), y) <= 1e-5
+    assert rel_err(mu2, muT) <= 1e-5 and rel_err(I2, IT) <= 1e-6
+    _compare_full(inp, torch.cat([y1, y2], dim=1), mu2, I2, tol=1e-4)
+
+
+def test_step_sequence_matches_chunked():
+    w = workloads.WORKLOADS[2].with_(B=2, H=3)
+    T = 40
+    _announce("step^T vs fwd bf16", B=w.B, H=w.H, T=T, d=w.dk)
+    inp = workloads.make_inputs(w, T=T)
+    g = to_device(inp, DEV)
+    pm = _pm()
+    y, muT, IT = pm.fwd_chunked(*gpu_args(g), out_dtype=torch.float32)
+    mu = torch.zeros_like(muT)
+    I = g["I_prior"].view(1, -1, 1, 1).expand_as(IT).contiguous()
+    ys = [pm.step(g["q"][:, t].contiguous(), g["k"][:, t].contiguous(), g["v"][:, t].contiguous(),
+                  g["beta"][:, t].contiguous(), g["dt"][:, t].contiguous(), g["A"], g["I_prior"],
+                  mu, I, out_dtype=torch.float32) for t in range(T)]
+    torch.cuda.synchronize()
+    assert rel_err(torch.stack(ys, 1), y) <= 1e-5
+    assert rel_err(mu, muT) <= 1e-5 and rel_err(I, IT) <= 1e-6
+
+
+HEAD_SHAPES = [(32, 32), (32, 64), (64, 32), (64, 128), (128, 64), (32, 128), (128, 32)]
+
+
+@pytest.mark.parametrize("dk,dv", HEAD_SHAPES)
+@pytest.mark.parametrize("T", [1, 37])
+def test_head_shapes_ragged_lengths(dk, dv, T):
+    w = workloads.WORKLOADS[0].with_(B=2, H=3, dk=dk, dv=dv, A_mode="logspace16")
+    _announce("fwd shapes fp32", B=w.B, H=w.H, T=T, dk=dk, dv=dv)
+    inp = workloads.make_inputs(w, T=T)
+    mu0, I0 = workloads.random_state(w.B, w.H, dv, dk, inp["I_prior"], seed=T + dk + dv)
+    inp["mu0"], inp["I0"] = mu0, I0
+    y, muT, IT = _run_fwd(inp, chunk=16)
+    _compare_full(inp, y, muT, IT, tol=1e-4)
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 64), (128, 128), (64, 32)])
+def test_step_head_shapes(dk, dv):
+    w = workloads.WORKLOADS[0].with_(B=3, H=5, dk=dk, dv=dv, A_mode="logspace16")
+    _announce("step shapes fp32", B=w.B, H=w.H, dk=dk, dv=dv)
+    A, Ip = workloads.head_constants(w)
+    mu0, I0 = workloads.random_state(w.B, w.H, dv, dk, Ip, seed=dk * dv)
+    mu, I = mu0.to(DEV), I0.to(DEV)
+    m, P = mu0, I0
+    for s in range(3):
+        d = workloads.decode_inputs(w, s)
+        gd = to_device(d, DEV)
+        y = _pm().step(gd["q"], gd["k"], gd["v"], gd["beta"], gd["dt"], A.to(DEV), Ip.to(DEV), mu, I)
+        yr, m, P = oracle.step(d["q"], d["k"], d["v"], d["beta"], d["dt"], A, Ip, m, P)
+        torch.cuda.synchronize()
+        assert_close("step y", y, yr, 1e-4)
+    assert_close("step mu", mu, m, 1e-4)
+    assert_close("step I", I, P, 1e-4)
+
+
+def test_bf16_inputs_fp32_outputs_and_fp32_inputs_bf16_outputs():
+    w = workloads.WORKLOADS[2].with_(B=1, H=8)
+    _announce("dtype pairs", B=w.B, H=w.H, T=70)
+    inp = workloads.make_inputs(w, T=70)
+    y, muT, IT = _run_fwd(inp, out_dtype=torch.float32)
+    assert y.dtype == torch.float32
+    _compare_full(inp, y, muT, IT, tol=1e-4)      # inputs exact in bf16, arithmetic fp32
+    inp32 = {n: (x.float() if isinstance(x, torch.Tensor) else x) for n, x in inp.items()}
+    y2, _, _ = _run_fwd(inp32, out_dtype=torch.bfloat16)
+    assert y2.dtype == torch.bfloat16
+    assert rel_err(y2, y) <= 4e-3
+
+
+def test_empty_sequence_copies_state_through():
+    w = workloads.WORKLOADS[0].with_(B=2, H=2)
+    _announce("T=0", B=w.B, H=w.H)
+    inp = workloads.make_inputs(w, T=0)
+    mu0, I0 = workloads.random_state(2, 2, 32, 32, inp["I_prior"], seed=3)
+    inp["mu0"], inp["I0"] = mu0, I0
+    y, muT, IT = _run_fwd(inp)
+    assert y.shape == (2, 0, 2, 32)
+    assert torch.equal(muT.cpu(), mu0) and torch.equal(IT.cpu(), I0)
+    inp["mu0"] = inp["I0"] = None
+    y, muT, IT = _run_fwd(inp)
+    assert torch.equal(muT.cpu(), torch.zeros_like(mu0))
+    assert torch.equal(IT.cpu(), torch.ones_like(I0))
+
+
+def test_no_forgetting_long_accumulation():
+    """dt = 0 for 4096 tokens: importance grows to thousands; fp32 stays accurate."""
+    w = workloads.WORKLOADS[0].with_(B=1, H=2, dk=64, dv=64)
+    T = 4096
+    _announce("alpha=1 accumulation", B=1, H=2, T=T, d=64)
+    inp = workloads.make_inputs(w, T=T)
+    inp["dt"] = torch.zeros_like(inp["dt"])
+    y, muT, IT = _run_fwd(inp)
+    _compare_full(inp, y, muT, IT, tol=1e-4)
+
+
+def test_binding_reports_library_errors():
+    pm = _pm()
+    _announce("error paths")
+    x = torch.zeros(1, 4, 1, 33, device=DEV)[..., 1:]      # offset view: not contiguous
+    with pytest.raises(ValueError):
+        pm.fwd_chunked(x, x, x, x, torch.zeros(1, 4, 1, device=DEV),
+                       torch.ones(1, device=DEV), torch.ones(1, device=DEV))
+    base = torch.zeros(1 * 4 * 1 * 32 + 1, device=DEV)
+    xm = base[1:].view(1, 4, 1, 32)                          # contiguous but 4-byte offset
+    dt = torch.zeros(1, 4, 1, device=DEV)
+    with pytest.raises(pm.PalimpsaError) as e:
+        pm.fwd_chunked(xm, xm, xm, xm, dt, torch.ones(1, device=DEV), torch.ones(1, device=DEV))
+    assert e.value.status == 3
+    x48 = torch.zeros(1, 4, 1, 48, device=DEV)
+    with pytest.raises(pm.PalimpsaError) as e:
+        pm.fwd_chunked(x48, x48, x48, x48, dt, torch.ones(1, device=DEV), torch.ones(1, device=DEV))
+    assert e.value.status == 2

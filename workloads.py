@@ -84,38 +84,46 @@ def _unit(x: torch.Tensor) -> torch.Tensor:
     return x / x.norm(dim=-1, keepdim=True)
 
 
-def make_inputs(w: Workload, T: int | None = None, seed: int | None = None) -> dict:
-    """Draw one sequence batch for workload ``w`` (``T`` overrides its length)."""
+def make_inputs(w: Workload, T: int | None = None, seed: int | None = None,
+                device: str | torch.device = "cpu") -> dict:
+    """Draw one sequence batch for workload ``w`` (``T`` overrides its length).
+
+    With ``device`` a GPU the numbers come from that device's generator (a
+    different stream than the CPU's, used for inputs too large to draw on
+    the host quickly); both sides of a comparison then read the same tensors.
+    """
     T = w.T if T is None else T
-    g = torch.Generator().manual_seed(w.seed if seed is None else seed)
+    g = torch.Generator(device=device).manual_seed(w.seed if seed is None else seed)
     B, H, dk, dv = w.B, w.H, w.dk, w.dv
-    q = _unit(torch.randn(B, T, H, dk, generator=g))
-    k = _unit(torch.randn(B, T, H, dk, generator=g))
-    v = torch.randn(B, T, H, dv, generator=g)
-    beta = torch.sigmoid(torch.randn(B, T, H, dv, generator=g))
-    dt = torch.nn.functional.softplus(torch.randn(B, T, H, generator=g) + w.dt_mean)
+    kw = dict(generator=g, device=device)
+    q = _unit(torch.randn(B, T, H, dk, **kw))
+    k = _unit(torch.randn(B, T, H, dk, **kw))
+    v = torch.randn(B, T, H, dv, **kw)
+    beta = torch.sigmoid(torch.randn(B, T, H, dv, **kw))
+    dt = torch.nn.functional.softplus(torch.randn(B, T, H, **kw) + w.dt_mean)
     if w.key_pool:
-        pool = _unit(torch.randn(w.key_pool, dk, generator=g))
-        idx = torch.randint(0, w.key_pool, (B, T, H), generator=g)
+        pool = _unit(torch.randn(w.key_pool, dk, **kw))
+        idx = torch.randint(0, w.key_pool, (B, T, H), **kw)
         k = pool[idx]
     if w.beta_const is not None:
         beta = torch.full_like(beta, w.beta_const)
     A, Ip = head_constants(w)
     cast = (lambda x: x.to(w.dtype).contiguous())
     return {"q": cast(q), "k": cast(k), "v": cast(v), "beta": cast(beta), "dt": cast(dt),
-            "A": A, "I_prior": Ip, "mu0": None, "I0": None}
+            "A": A.to(device), "I_prior": Ip.to(device), "mu0": None, "I0": None}
 
 
-def decode_inputs(w: Workload, step: int) -> dict:
+def decode_inputs(w: Workload, step: int, device: str | torch.device = "cpu") -> dict:
     """Fresh single-token inputs for decode step ``step`` (0-based); each step
     has its own seed, so any step can be regenerated on its own."""
-    g = torch.Generator().manual_seed(1_000_000 * (w.seed + 1) + step)
+    g = torch.Generator(device=device).manual_seed(1_000_000 * (w.seed + 1) + step)
     B, H, dk, dv = w.B, w.H, w.dk, w.dv
-    q = _unit(torch.randn(B, H, dk, generator=g))
-    k = _unit(torch.randn(B, H, dk, generator=g))
-    v = torch.randn(B, H, dv, generator=g)
-    beta = torch.sigmoid(torch.randn(B, H, dv, generator=g))
-    dt = torch.nn.functional.softplus(torch.randn(B, H, generator=g) + w.dt_mean)
+    kw = dict(generator=g, device=device)
+    q = _unit(torch.randn(B, H, dk, **kw))
+    k = _unit(torch.randn(B, H, dk, **kw))
+    v = torch.randn(B, H, dv, **kw)
+    beta = torch.sigmoid(torch.randn(B, H, dv, **kw))
+    dt = torch.nn.functional.softplus(torch.randn(B, H, **kw) + w.dt_mean)
     cast = (lambda x: x.to(w.dtype).contiguous())
     return {"q": cast(q), "k": cast(k), "v": cast(v), "beta": cast(beta), "dt": cast(dt)}
 
