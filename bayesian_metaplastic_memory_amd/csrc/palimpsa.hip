@@ -23,8 +23,11 @@
 //    token: one workgroup owns 16 value rows of one head for the whole
 //    sequence, so no inter-chunk state goes to HBM.
 //  * Lane layout: a wave owns 4 value rows; 16 lanes share a row and each
-//    owns DK/16 key columns (8 at d_k = 128).  The row sum of the readout is
-//    a 4-step DPP butterfly inside a 16-lane row; no LDS round trip.
+//    owns DK/16 key columns (8 at d_k = 128).  Each lane keeps its partial
+//    readout of 16 consecutive tokens in registers; one transposing DPP
+//    reduction then leaves token g's row sum in lane g (2.8 VALU ops per
+//    token instead of a 4-step all-reduce per token), and each lane stores
+//    one y value per 16 tokens.
 //  * Per chunk of C tokens the workgroup stages, once, the per-column
 //    operands k, k^2, q (float32), the per-row pair (beta, beta*v) and the
 //    per-token gate (alpha, c) in LDS; bf16 is widened once here, not per
@@ -130,6 +133,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 4;
 constexpr int kRowsPerWG = kRowsPerWave * kWaves;   // 16 value rows per workgroup
 constexpr int kLanesPerRow = 16;
+constexpr int kGroup = 16;                // tokens per transposing reduction (= lanes per row)
 
 // LDS floats per staged token: k, k^2, q columns + (beta, beta*v) per row + gate.
 template <int DK> struct Stage {
@@ -141,13 +145,23 @@ template <int DK> struct Stage {
 template <int DK, int C>
 constexpr size_t fwd_lds_bytes() { return (size_t)2 * C * Stage<DK>::kTokFloats * sizeof(float); }
 
-// Per-chunk staging: which 16-byte packets each thread loads, and where they go.
+// Staging of one chunk of C tokens into an LDS buffer.
+//
+// Every thread loads and widens k/q packets (16 bytes each); the (v, beta)
+// packet pairs start at wave 1 and the per-token gates at wave 2, so no wave
+// carries all the extras into the barrier.  Addresses are a per-chunk base
+// (uniform) plus a per-thread 32-bit element offset.  Tokens past the end of
+// the sequence are staged as neutral updates (k = q = 0, beta = 0, dt = 0, so
+// alpha = 1 and c = 0): they leave (M, I) bit-identical and their y is not
+// stored, so the last chunk runs the same code as the others.
 template <int DK, int C, typename TIn>
 struct Stager {
     static constexpr int kPerPkt = packet<TIn>::kN;            // elements per 16 B
     static constexpr int kColPkts = DK / kPerPkt;              // packets per k (or q) row
-    static constexpr int kKQ = C * 2 * kColPkts;               // k and q packets per chunk
+    static constexpr int kHalf = C * kColPkts;                 // k packets per chunk (= q packets)
+    static constexpr int kKQ = 2 * kHalf;
     static constexpr int kKQPerThread = (kKQ + kThreads - 1) / kThreads;
+    static constexpr bool kSplit = kHalf % kThreads == 0;      // packet u is all-k or all-q
     static constexpr int kRowPkts = kRowsPerWG / kPerPkt;      // packets per v (or beta) row slice
     static constexpr int kVB = C * kRowPkts;                   // (v, beta) packet pairs per chunk
     static_assert(kVB <= kThreads, "one (v, beta) pair per thread at most");
@@ -157,38 +171,41 @@ struct Stager {
     uint4 vv, bb;
     float dtv;
 
-    // Issue the global loads of chunk starting at token t0 (tokens >= T are skipped).
-    __device__ inline void load(const FwdArgs &a, int b, int h, int row0, int t0, int tid) {
-        const size_t H = a.H;
+    __device__ static inline int vb_slot(int tid) { return (tid + kThreads - 64) % kThreads; }
+    __device__ static inline int gate_slot(int tid) { return (tid + kThreads - 128) % kThreads; }
+    __device__ static inline bool is_q(int u, int p) { return kSplit ? (u >= kHalf / kThreads) : (p >= kHalf); }
+
+    // Chunk bases point at token t0 of this (b, h): k/q at [.., DK], v/beta at
+    // the workgroup's first row, dt at the token.  `left` = T - t0 tokens remain.
+    __device__ inline void load(const TIn *kb, const TIn *qb, const TIn *vb, const TIn *bb_,
+                                const TIn *db, int left, int H, int dv, int tid) {
 #pragma unroll
         for (int u = 0; u < kKQPerThread; ++u) {
             const int p = tid + u * kThreads;
             if (kKQ % kThreads == 0 || p < kKQ) {
-                const int tt = p / (2 * kColPkts);
-                const int arr = (p / kColPkts) & 1;
-                const int off = (p % kColPkts) * kPerPkt;
-                const int t = t0 + tt;
-                if (t < a.T) {
-                    const size_t base = (((size_t)b * a.T + t) * H + h) * DK + off;
-                    const TIn *src = (const TIn *)(arr ? a.q : a.k);
-                    kq[u] = *(const uint4 *)(src + base);
-                }
+                const bool q = is_q(u, p);
+                const int pp = q ? p - kHalf : p;
+                const int tt = pp / kColPkts;
+                const uint32_t off = (uint32_t)tt * (uint32_t)(H * DK) + (pp % kColPkts) * kPerPkt;
+                kq[u] = make_uint4(0, 0, 0, 0);
+                if (tt < left) kq[u] = *(const uint4 *)((q ? qb : kb) + off);
             }
         }
-        if (tid < kVB) {
-            const int tt = tid / kRowPkts;
-            const int off = (tid % kRowPkts) * kPerPkt;
-            const int t = t0 + tt;
-            if (t < a.T) {
-                const size_t base = (((size_t)b * a.T + t) * H + h) * a.dv + row0 + off;
-                vv = *(const uint4 *)((const TIn *)a.v + base);
-                bb = *(const uint4 *)((const TIn *)a.beta + base);
+        const int pv = vb_slot(tid);
+        if (pv < kVB) {
+            const int tt = pv / kRowPkts;
+            const uint32_t off = (uint32_t)tt * (uint32_t)(H * dv) + (pv % kRowPkts) * kPerPkt;
+            vv = make_uint4(0, 0, 0, 0);
+            bb = make_uint4(0, 0, 0, 0);
+            if (tt < left) {
+                vv = *(const uint4 *)(vb + off);
+                bb = *(const uint4 *)(bb_ + off);
             }
         }
-        if (tid < C) {
-            const int t = t0 + tid;
-            if (t < a.T)
-                dtv = io<TIn>::to_f32(((const TIn *)a.dt)[((size_t)b * a.T + t) * H + h]);
+        const int pg = gate_slot(tid);
+        if (pg < C) {
+            dtv = 0.f;
+            if (pg < left) dtv = io<TIn>::to_f32(db[(uint32_t)pg * (uint32_t)H]);
         }
     }
 
@@ -201,29 +218,31 @@ struct Stager {
         for (int u = 0; u < kKQPerThread; ++u) {
             const int p = tid + u * kThreads;
             if (kKQ % kThreads == 0 || p < kKQ) {
-                const int tt = p / (2 * kColPkts);
-                const int arr = (p / kColPkts) & 1;
-                const int off = (p % kColPkts) * kPerPkt;
+                const bool q = is_q(u, p);
+                const int pp = q ? p - kHalf : p;
+                const int tt = pp / kColPkts;
+                const int off = (pp % kColPkts) * kPerPkt;
                 float x[kPerPkt];
                 packet<TIn>::widen(kq[u], x);
                 float *dst = cols + tt * Stage<DK>::kColFloats + off;
-                if (arr == 0) {   // k and k^2
+                if (!q) {   // k and k^2
 #pragma unroll
                     for (int e = 0; e < kPerPkt; e += 4) {
                         *(float4 *)(dst + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
                         *(float4 *)(dst + DK + e) = make_float4(x[e] * x[e], x[e + 1] * x[e + 1],
                                                                 x[e + 2] * x[e + 2], x[e + 3] * x[e + 3]);
                     }
-                } else {          // q
+                } else {    // q
 #pragma unroll
                     for (int e = 0; e < kPerPkt; e += 4)
                         *(float4 *)(dst + 2 * DK + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
                 }
             }
         }
-        if (tid < kVB) {
-            const int tt = tid / kRowPkts;
-            const int off = (tid % kRowPkts) * kPerPkt;
+        const int pv = vb_slot(tid);
+        if (pv < kVB) {
+            const int tt = pv / kRowPkts;
+            const int off = (pv % kRowPkts) * kPerPkt;
             float xv[kPerPkt], xb[kPerPkt];
             packet<TIn>::widen(vv, xv);
             packet<TIn>::widen(bb, xb);
@@ -232,8 +251,9 @@ struct Stager {
             for (int e = 0; e < kPerPkt; e += 2)
                 *(float4 *)(dst + 2 * e) = make_float4(xb[e], xb[e] * xv[e], xb[e + 1], xb[e + 1] * xv[e + 1]);
         }
-        if (tid < C)
-            *(float2 *)(gates + 2 * tid) = gate(A, dtv, Ip);
+        const int pg = gate_slot(tid);
+        if (pg < C)
+            *(float2 *)(gates + 2 * pg) = gate(A, dtv, Ip);
     }
 };
 
@@ -261,39 +281,80 @@ template <> struct vecf<2> {
     __device__ static inline void st(float *p, const float *o) { *(float2 *)p = make_float2(o[0], o[1]); }
 };
 
-// The per-token hot loop over n staged tokens.
+// Transposing reduction over the 16 lanes g of a DPP row: lane g holds 16
+// partial sums x[0..15] (one per token of a group) and returns the row-wide
+// sum of x[g].  Four exchange stages; in each, a lane keeps half of its
+// values, sends the other half to its partner, and adds what it receives.
+// Partners: l^15 (row_mirror), l^7 within each half-row (row_half_mirror),
+// l^2 and l^1 (quad permutations).  The four XOR masks span all 16 lanes, and
+// the half a lane keeps is chosen by lane bits 3, 2, 1, 0, so lane g ends
+// with token 8 b3 + 4 b2 + 2 b1 + b0 = g.  45 VALU ops for 16 tokens.
+template <int CTRL>
+__device__ inline float dpp_from(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+__device__ inline float row16_transpose_sum(const float (&x)[16], int g) {
+    const bool b3 = g & 8, b2 = g & 4, b1 = g & 2, b0 = g & 1;
+    float s1[8], s2[4], s3[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        s1[i] = (b3 ? x[i + 8] : x[i]) + dpp_from<0x140>(b3 ? x[i] : x[i + 8]);       // row_mirror
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        s2[i] = (b2 ? s1[i + 4] : s1[i]) + dpp_from<0x141>(b2 ? s1[i] : s1[i + 4]);   // row_half_mirror
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        s3[i] = (b1 ? s2[i + 2] : s2[i]) + dpp_from<0x4E>(b1 ? s2[i] : s2[i + 2]);    // quad_perm [2,3,0,1]
+    return (b0 ? s3[1] : s3[0]) + dpp_from<0xB1>(b0 ? s3[0] : s3[1]);                 // quad_perm [1,0,3,2]
+}
+
+// The per-token hot loop over one staged chunk.  Per token and lane: for each
+// of the lane's DK/16 state entries 6 VALU ops and one v_rcp_f32; the lane's
+// partial of y_t goes to a register.  Every 16 tokens one transposing
+// reduction leaves y for token g in lane g, which stores it if the token is
+// inside the sequence (`left` = tokens remaining from the chunk start).
 template <int DK, int C, typename TOut>
-__device__ inline void compute_chunk(const float *buf, int n, float *M, float *I,
+__device__ inline void compute_chunk(const float *buf, int left, float *M, float *I,
                                      int row_local, int g, TOut *yrow, size_t ystride) {
     using LT = LaneTile<DK>;
-    const float *cols = buf;
-    const float *rows = buf + C * Stage<DK>::kColFloats;
-    const float *gates = rows + C * Stage<DK>::kRowFloats;
-#pragma unroll 2
-    for (int tt = 0; tt < n; ++tt) {
-        const float2 gc = *(const float2 *)(gates + 2 * tt);                          // alpha, c
-        const float2 rb = *(const float2 *)(rows + tt * Stage<DK>::kRowFloats + 2 * row_local);  // beta, beta*v
-        const float *ct = cols + tt * Stage<DK>::kColFloats;
-        float acc[2] = {0.f, 0.f};
+    static_assert(C % kGroup == 0, "chunk must be a multiple of 16 tokens");
+    const float *cbase = buf + LT::col(g, 0, 0);
+    const float *rbase = buf + C * Stage<DK>::kColFloats + 2 * row_local;
+    const float *gbase = buf + C * (Stage<DK>::kColFloats + Stage<DK>::kRowFloats);
+#pragma unroll 1
+    for (int grp = 0; grp < C / kGroup; ++grp) {
+        const float *cg = cbase + grp * kGroup * Stage<DK>::kColFloats;
+        const float *rg = rbase + grp * kGroup * Stage<DK>::kRowFloats;
+        const float *gg = gbase + grp * kGroup * 2;
+        float part[kGroup];
 #pragma unroll
-        for (int m = 0; m < LT::kNVec; ++m) {
-            float kk[LT::kVec], k2[LT::kVec], qq[LT::kVec];
-            const int c0 = LT::col(g, m, 0);
-            vecf<LT::kVec>::ld(ct + c0, kk);
-            vecf<LT::kVec>::ld(ct + DK + c0, k2);
-            vecf<LT::kVec>::ld(ct + 2 * DK + c0, qq);
+        for (int u = 0; u < kGroup; ++u) {
+            const float2 gc = *(const float2 *)(gg + 2 * u);                          // alpha, c
+            const float2 rb = *(const float2 *)(rg + u * Stage<DK>::kRowFloats);      // beta, beta*v
+            const float *ct = cg + u * Stage<DK>::kColFloats;
+            float acc = 0.f;
 #pragma unroll
-            for (int e = 0; e < LT::kVec; ++e) {
-                const int s = m * LT::kVec + e;
-                const float w = fmaf(rb.x, k2[e], gc.y);
-                I[s] = fmaf(gc.x, I[s], w);
-                M[s] = fmaf(gc.x, M[s], rb.y * kk[e]);
-                const float r = __builtin_amdgcn_rcpf(I[s]);
-                acc[s & 1] = fmaf(M[s] * r, qq[e], acc[s & 1]);
+            for (int m = 0; m < LT::kNVec; ++m) {
+                float kk[LT::kVec], k2[LT::kVec], qq[LT::kVec];
+                const int c0 = kLanesPerRow * LT::kVec * m;
+                vecf<LT::kVec>::ld(ct + c0, kk);
+                vecf<LT::kVec>::ld(ct + DK + c0, k2);
+                vecf<LT::kVec>::ld(ct + 2 * DK + c0, qq);
+#pragma unroll
+                for (int e = 0; e < LT::kVec; ++e) {
+                    const int s = m * LT::kVec + e;
+                    const float w = fmaf(rb.x, k2[e], gc.y);        // c + beta_i k_j^2
+                    I[s] = fmaf(gc.x, I[s], w);                     // importance
+                    M[s] = fmaf(gc.x, M[s], rb.y * kk[e]);          // natural content
+                    const float r = __builtin_amdgcn_rcpf(I[s]);
+                    acc = fmaf(M[s] * r, qq[e], acc);               // mu_ij q_j
+                }
             }
+            part[u] = acc;
         }
-        const float yv = row16_sum(acc[0] + acc[1]);
-        if (g == 0)
+        const float yv = row16_transpose_sum(part, g);
+        const int tt = grp * kGroup + g;
+        if (tt < left)
             yrow[(size_t)tt * ystride] = io<TOut>::from_f32(yv);
     }
 }
@@ -344,27 +405,34 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
         for (int s = 0; s < LT::kCols; ++s) { I[s] = Ip; M[s] = 0.f; }
     }
 
-    const int nchunks = (a.T + C - 1) / C;
+    // per-sequence bases (token 0 of this (b, h)) and per-token strides
+    const size_t seq = (size_t)b * a.T * a.H + h;             // row index of (b, 0, h) in [B, T, H]
+    const TIn *kseq = (const TIn *)a.k + seq * DK;
+    const TIn *qseq = (const TIn *)a.q + seq * DK;
+    const TIn *vseq = (const TIn *)a.v + seq * a.dv + row0;
+    const TIn *bseq = (const TIn *)a.beta + seq * a.dv + row0;
+    const TIn *dseq = (const TIn *)a.dt + seq;
+    const size_t kq_tok = (size_t)a.H * DK, vb_tok = (size_t)a.H * a.dv;
     const size_t ystride = (size_t)a.H * a.dv;
-    TOut *ybase = (TOut *)a.y + ((size_t)b * a.T * a.H + h) * a.dv + row;
+    TOut *ybase = (TOut *)a.y + seq * a.dv + row;
 
+    const int nchunks = (a.T + C - 1) / C;
     Stager<DK, C, TIn> st;
     if (nchunks > 0) {
-        st.load(a, b, h, row0, 0, tid);
+        st.load(kseq, qseq, vseq, bseq, dseq, a.T, a.H, a.dv, tid);
         st.commit(buf0, A, Ip, tid);
         __syncthreads();
     }
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * C;
         const bool more = c + 1 < nchunks;
-        if (more) st.load(a, b, h, row0, t0 + C, tid);
+        if (more) {
+            const size_t tn = (size_t)(t0 + C);
+            st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
+                    dseq + tn * a.H, a.T - (t0 + C), a.H, a.dv, tid);
+        }
         const float *cur = (c & 1) ? buf1 : buf0;
-        const int n = min(C, a.T - t0);
-        TOut *yrow = ybase + (size_t)t0 * ystride;
-        if (n == C)
-            compute_chunk<DK, C, TOut>(cur, C, M, I, row_local, g, yrow, ystride);
-        else
-            compute_chunk<DK, C, TOut>(cur, n, M, I, row_local, g, yrow, ystride);
+        compute_chunk<DK, C, TOut>(cur, a.T - t0, M, I, row_local, g, ybase + (size_t)t0 * ystride, ystride);
         if (more) st.commit((c & 1) ? buf0 : buf1, A, Ip, tid);
         __syncthreads();
     }
@@ -468,7 +536,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
 // host side
 // ---------------------------------------------------------------------------
 
-inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool aligned_to(const void *p, size_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
 inline bool head_ok(int d) { return d == 32 || d == 64 || d == 128; }
 inline bool dtype_ok(int t) { return t == PALIMPSA_F32 || t == PALIMPSA_BF16; }
 
@@ -489,7 +557,6 @@ palimpsa_status launch_fwd_t(const FwdArgs &a0, hipStream_t s) {
 template <int DK, typename TIn, typename TOut>
 palimpsa_status launch_fwd_c(const FwdArgs &a, int C, hipStream_t s) {
     switch (C) {
-    case 8: return launch_fwd_t<DK, 8, TIn, TOut>(a, s);
     case 16: return launch_fwd_t<DK, 16, TIn, TOut>(a, s);
     case 32: return launch_fwd_t<DK, 32, TIn, TOut>(a, s);
     default: return launch_fwd_t<DK, 64, TIn, TOut>(a, s);
@@ -507,17 +574,18 @@ palimpsa_status launch_fwd_d(const FwdArgs &a, int dk, int C, hipStream_t s) {
 
 size_t lds_bytes_for(int dk, int C) { return (size_t)2 * C * (3 * dk + 2 * kRowsPerWG + 2) * sizeof(float); }
 
-// Chunk actually used: the request if given (shrunk until its buffers fit the
-// device's LDS), else the largest that lets three workgroups share a CU when
-// there are enough workgroups to need it.
+// Chunk actually used: the request if given (8 is raised to 16, the
+// reduction group; larger requests shrink until the buffers fit the device's
+// LDS), else the largest that lets three workgroups share a CU when there are
+// enough workgroups to need it.
 int pick_chunk(int requested, int dk, long long nwg, size_t lds_max) {
-    int C = requested;
+    int C = requested < 16 ? (requested == 0 ? 0 : 16) : requested;
     if (C == 0) {
         const size_t budget = nwg > 256 ? 54 * 1024 : lds_max;
         C = 64;
-        while (C > 8 && lds_bytes_for(dk, C) > budget) C /= 2;
+        while (C > 16 && lds_bytes_for(dk, C) > budget) C /= 2;
     }
-    while (C > 8 && lds_bytes_for(dk, C) > lds_max) C /= 2;
+    while (C > 16 && lds_bytes_for(dk, C) > lds_max) C /= 2;
     return C;
 }
 
@@ -541,7 +609,7 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
                                      int B, int T, int H, int dk, int dv, int chunk,
                                      palimpsa_dtype in_dtype, palimpsa_dtype out_dtype,
                                      void *stream) {
-    if (!q || !k || !v || !beta || !dt || !A || !I_prior || (!y && T > 0))
+    if (!A || !I_prior || (T > 0 && (!q || !k || !v || !beta || !dt || !y)))
         return PALIMPSA_ERR_INVALID_ARG;
     if ((mu0 == nullptr) != (I0 == nullptr) || (muT == nullptr) != (IT == nullptr))
         return PALIMPSA_ERR_INVALID_ARG;
@@ -553,11 +621,17 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
         return PALIMPSA_ERR_INVALID_ARG;
     if (!head_ok(dk) || !head_ok(dv))
         return PALIMPSA_ERR_UNSUPPORTED;
-    const void *ptrs[] = {q, k, v, beta, dt, A, I_prior, mu0, I0, y, muT, IT};
-    for (const void *p : ptrs)
-        if (p && !aligned16(p)) return PALIMPSA_ERR_ALIGNMENT;
+    // 128-bit accesses: q, k, v, beta and the state arrays; element-wise: the rest
+    const void *vec_ptrs[] = {q, k, v, beta, mu0, I0, muT, IT};
+    for (const void *p : vec_ptrs)
+        if (p && !aligned_to(p, 16)) return PALIMPSA_ERR_ALIGNMENT;
+    const size_t in_sz = in_dtype == PALIMPSA_BF16 ? 2 : 4, out_sz = out_dtype == PALIMPSA_BF16 ? 2 : 4;
+    if (!aligned_to(dt, in_sz) || !aligned_to(A, 4) || !aligned_to(I_prior, 4) || (y && !aligned_to(y, out_sz)))
+        return PALIMPSA_ERR_ALIGNMENT;
     const long long nwg = (long long)B * H * (dv / kRowsPerWG);
-    if (nwg > 0x7fffffffLL || (long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 46))
+    // per-chunk staging offsets are 32-bit: 64 tokens x H x d must stay below 2^31
+    if (nwg > 0x7fffffffLL || (long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 46) ||
+        64LL * H * (dk > dv ? dk : dv) >= (1LL << 31))
         return PALIMPSA_ERR_UNSUPPORTED;
 
     FwdArgs a;
@@ -593,9 +667,13 @@ palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
         return PALIMPSA_ERR_INVALID_ARG;
     if (!head_ok(dk) || !head_ok(dv))
         return PALIMPSA_ERR_UNSUPPORTED;
-    const void *ptrs[] = {q, k, v, beta, dt, A, I_prior, mu, I, y};
-    for (const void *p : ptrs)
-        if (!aligned16(p)) return PALIMPSA_ERR_ALIGNMENT;
+    // 128-bit accesses: the state; element-wise: the rest
+    if (!aligned_to(mu, 16) || !aligned_to(I, 16)) return PALIMPSA_ERR_ALIGNMENT;
+    const size_t in_sz = in_dtype == PALIMPSA_BF16 ? 2 : 4, out_sz = out_dtype == PALIMPSA_BF16 ? 2 : 4;
+    const void *in_ptrs[] = {q, k, v, beta, dt};
+    for (const void *p : in_ptrs)
+        if (!aligned_to(p, in_sz)) return PALIMPSA_ERR_ALIGNMENT;
+    if (!aligned_to(A, 4) || !aligned_to(I_prior, 4) || !aligned_to(y, out_sz)) return PALIMPSA_ERR_ALIGNMENT;
     const long long rows = (long long)B * H * dv;
     if (rows * dk > (1LL << 46))
         return PALIMPSA_ERR_UNSUPPORTED;
@@ -634,7 +712,7 @@ const char *palimpsa_status_string(int status) {
     case PALIMPSA_OK: return "ok";
     case PALIMPSA_ERR_INVALID_ARG: return "invalid argument (null pointer, size or enum)";
     case PALIMPSA_ERR_UNSUPPORTED: return "unsupported configuration (head size must be 32, 64 or 128)";
-    case PALIMPSA_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
+    case PALIMPSA_ERR_ALIGNMENT: return "tensor pointer misaligned (see palimpsa.h)";
     case PALIMPSA_ERR_HIP: return "HIP runtime error at launch";
     default: return "unknown status";
     }

@@ -33,7 +33,7 @@ if ROOT not in sys.path:
 CUS, SIMDS, LANES_PER_CLK, CLOCK_HZ = 256, 4, 16, 2.4e9
 LANE_OPS_PER_S = CUS * SIMDS * LANES_PER_CLK * CLOCK_HZ       # 3.93e13
 VALU_PER_UPDATE = 6          # 4 FMA + 2 MUL
-RCP_SLOTS = 4                # v_rcp_f32 issue cost in FMA slots (quarter rate)
+RCP_SLOTS = 2                # v_rcp_f32 issue cost in FMA slots: half rate on gfx950
 FLOPS_PER_UPDATE = 10        # FMA = 2 flops, MUL = 1; the reciprocal is not counted
 HBM_PEAK_GBS = 8000.0
 
@@ -182,7 +182,7 @@ def main():
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": "fwd_chunked_kernel<128, C, bf16, bf16>",
                      "avg_launch_ms": avg_launch_s * 1e3,
-                     "per_update": "4 FMA + 2 MUL (10 flops) + 1 v_rcp_f32 (4 FMA slots)",
+                     "per_update": "4 FMA + 2 MUL (10 flops) + 1 v_rcp_f32 (2 FMA slots)",
                      "hbm_algorithmic_GBs": hbm_alg / avg_launch_s / 1e9},
     }
     if not args.no_decode:

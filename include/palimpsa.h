@@ -23,8 +23,10 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Tensor pointers are DEVICE pointers, owned by the caller, contiguous and
- *    row-major in the layouts stated per argument.  Every tensor pointer must
- *    be 16-byte aligned.
+ *    row-major in the layouts stated per argument.  Pointers the kernels read
+ *    or write with 128-bit accesses must be 16-byte aligned: q, k, v, beta and
+ *    the state arrays of palimpsa_fwd_chunked, and mu, I of palimpsa_step.
+ *    Every other pointer needs the natural alignment of its element type.
  *  - in_dtype applies to q, k, v, beta and dt; out_dtype to y.  A, I_prior and
  *    every state array are float32.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL means the default
@@ -51,7 +53,7 @@ typedef enum {
     PALIMPSA_OK = 0,
     PALIMPSA_ERR_INVALID_ARG = 1,  /* null pointer, negative or zero size, bad enum */
     PALIMPSA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head size, dtype pair) */
-    PALIMPSA_ERR_ALIGNMENT = 3,    /* a tensor pointer is not 16-byte aligned */
+    PALIMPSA_ERR_ALIGNMENT = 3,    /* a tensor pointer breaks the alignment rule above */
     PALIMPSA_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
 } palimpsa_status;
 
@@ -75,11 +77,14 @@ typedef enum {
  *                            (one NULL alone is an error).  muT may alias mu0
  *                            and IT may alias I0 (in-place resume).
  *   chunk     tokens staged per step through on-chip memory, one of
- *             {8, 16, 32, 64}, or 0 for the library's choice.  Results do not
- *             depend on it beyond float32 rounding.
+ *             {8, 16, 32, 64}, or 0 for the library's choice (8 is run as 16;
+ *             a chunk whose staging buffers exceed the device's LDS is
+ *             halved until they fit).  A performance hint only: the results
+ *             are bit-identical for every chunk.
  *
  * T == 0 is valid: y is empty and the state is copied through (or, with both
- * mu0 and I0 NULL, set to mu = 0, I = I_prior).  B, H >= 1.
+ * mu0 and I0 NULL, set to mu = 0, I = I_prior); the per-token pointers q, k,
+ * v, beta, dt and y are then not read and may be NULL.  B, H >= 1.
  * bf16 inputs are read exactly; bf16 outputs are rounded to nearest even.
  */
 palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v,

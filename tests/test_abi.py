@@ -65,12 +65,14 @@ def _fwd_args(**over):
 
 FWD_CASES = [
     (dict(q=None), 1), (dict(k=None), 1), (dict(dt=None), 1), (dict(A=None), 1),
+    (dict(A=None, T=0), 1), (dict(Ip=None, T=0, q=None), 1),
     (dict(Ip=None), 1), (dict(y=None), 1), (dict(mu0=FAKE), 1), (dict(I0=FAKE), 1),
     (dict(muT=None), 1), (dict(IT=None), 1), (dict(B=0), 1), (dict(H=0), 1), (dict(T=-1), 1),
     (dict(dk=0), 1), (dict(ind=2), 1), (dict(outd=-1), 1), (dict(chunk=12), 1),
     (dict(chunk=128), 1), (dict(dk=48), 2), (dict(dv=256), 2), (dict(dk=16), 2),
-    (dict(q=FAKE + 4), 3), (dict(v=FAKE + 8), 3), (dict(y=FAKE + 2), 3),
-    (dict(mu0=FAKE + 4, I0=FAKE), 3), (dict(IT=FAKE + 12), 3),
+    (dict(q=FAKE + 4), 3), (dict(v=FAKE + 8), 3),
+    (dict(mu0=FAKE + 4, I0=FAKE), 3), (dict(IT=FAKE + 12), 3), (dict(dt=FAKE + 1), 3),
+    (dict(y=FAKE + 1), 3), (dict(A=FAKE + 2), 3), (dict(beta=FAKE + 2), 3),
 ]
 
 
@@ -90,7 +92,8 @@ def _step_args(**over):
 STEP_CASES = [
     (dict(q=None), 1), (dict(mu=None), 1), (dict(I=None), 1), (dict(y=None), 1),
     (dict(B=0), 1), (dict(H=-2), 1), (dict(ind=5), 1), (dict(dk=100), 2), (dict(dv=8), 2),
-    (dict(mu=FAKE + 4), 3), (dict(k=FAKE + 2), 3),
+    (dict(mu=FAKE + 4), 3), (dict(I=FAKE + 8), 3), (dict(k=FAKE + 1), 3), (dict(dt=FAKE + 1), 3),
+    (dict(y=FAKE + 3), 3), (dict(Ip=FAKE + 2), 3),
 ]
 
 
