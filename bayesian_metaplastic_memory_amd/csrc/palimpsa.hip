@@ -148,8 +148,8 @@ constexpr size_t fwd_lds_bytes() { return (size_t)2 * C * Stage<DK>::kTokFloats 
 // Staging of one chunk of C tokens into an LDS buffer.
 //
 // Every thread loads and widens k/q packets (16 bytes each); the (v, beta)
-// packet pairs start at wave 1 and the per-token gates at wave 2, so no wave
-// carries all the extras into the barrier.  Addresses are a per-chunk base
+// packet pairs start at wave 1, the gate's alpha at wave 2 and its c at wave
+// 3, so no wave carries all the extras into the barrier.  Addresses are a per-chunk base
 // (uniform) plus a per-thread 32-bit element offset.  Tokens past the end of
 // the sequence are staged as neutral updates (k = q = 0, beta = 0, dt = 0, so
 // alpha = 1 and c = 0): they leave (M, I) bit-identical and their y is not
@@ -169,10 +169,11 @@ struct Stager {
 
     uint4 kq[kKQPerThread];
     uint4 vv, bb;
-    float dtv;
+    float dtv, dtc;
 
     __device__ static inline int vb_slot(int tid) { return (tid + kThreads - 64) % kThreads; }
     __device__ static inline int gate_slot(int tid) { return (tid + kThreads - 128) % kThreads; }
+    __device__ static inline int c_slot(int tid) { return (tid + kThreads - 192) % kThreads; }
     __device__ static inline bool is_q(int u, int p) { return kSplit ? (u >= kHalf / kThreads) : (p >= kHalf); }
 
     // Chunk bases point at token t0 of this (b, h): k/q at [.., DK], v/beta at
@@ -206,6 +207,11 @@ struct Stager {
         if (pg < C) {
             dtv = 0.f;
             if (pg < left) dtv = io<TIn>::to_f32(db[(uint32_t)pg * (uint32_t)H]);
+        }
+        const int pc = c_slot(tid);
+        if (pc < C) {
+            dtc = 0.f;
+            if (pc < left) dtc = io<TIn>::to_f32(db[(uint32_t)pc * (uint32_t)H]);
         }
     }
 
@@ -251,9 +257,13 @@ struct Stager {
             for (int e = 0; e < kPerPkt; e += 2)
                 *(float4 *)(dst + 2 * e) = make_float4(xb[e], xb[e] * xv[e], xb[e + 1], xb[e + 1] * xv[e + 1]);
         }
+        // alpha on wave 2 and c = (1 - alpha) I_prior on wave 3 (the gate of Eq. (9))
         const int pg = gate_slot(tid);
         if (pg < C)
-            *(float2 *)(gates + 2 * pg) = gate(A, dtv, Ip);
+            gates[2 * pg] = expf(-A * dtv);
+        const int pc = c_slot(tid);
+        if (pc < C)
+            gates[2 * pc + 1] = -expm1f(-A * dtc) * Ip;
     }
 };
 
@@ -320,7 +330,12 @@ __device__ inline void compute_chunk(const float *buf, int left, float *M, float
     static_assert(C % kGroup == 0, "chunk must be a multiple of 16 tokens");
     const float *cbase = buf + LT::col(g, 0, 0);
     const float *rbase = buf + C * Stage<DK>::kColFloats + 2 * row_local;
-    const float *gbase = buf + C * (Stage<DK>::kColFloats + Stage<DK>::kRowFloats);
+    // The gate address is the same in every lane; holding it in a VGPR (the
+    // empty asm hides its uniformity) lets every gate read be one ds_read_b64
+    // with an immediate offset instead of a per-token SGPR-to-VGPR move.
+    int goff = C * (Stage<DK>::kColFloats + Stage<DK>::kRowFloats);
+    asm volatile("" : "+v"(goff));
+    const float *gbase = buf + goff;
 #pragma unroll 1
     for (int grp = 0; grp < C / kGroup; ++grp) {
         const float *cg = cbase + grp * kGroup * Stage<DK>::kColFloats;

@@ -124,13 +124,16 @@ def decode_extra(torch, pm, workloads, steps):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads in the oracle sample (0: all heads of the workload)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times "
+                         "(calibrates the HBM byte counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -144,6 +147,15 @@ def main():
     import workloads
 
     dev = torch.device("cuda:0")
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_each_way": 4 * n, "launches": 3}))
+        return
     w = workloads.WORKLOADS[2]
     inp = workloads.make_inputs(w)
     g = {n: (x.to(dev) if isinstance(x, torch.Tensor) else x) for n, x in inp.items()}
