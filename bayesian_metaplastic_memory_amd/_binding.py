@@ -41,8 +41,12 @@ def load_library() -> ctypes.CDLL:
                     "(or __graft_entry__.build())")
             lib = ctypes.CDLL(LIB_PATH)
             vp, fp, i = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
-            lib.palimpsa_fwd_chunked.argtypes = [vp] * 5 + [fp] * 4 + [vp, fp, fp] + [i] * 8 + [vp]
+            sz = ctypes.c_size_t
+            lib.palimpsa_fwd_chunked.argtypes = ([vp] * 5 + [fp] * 4 + [vp, fp, fp] + [i] * 9 +
+                                                 [vp, sz, vp])
             lib.palimpsa_fwd_chunked.restype = i
+            lib.palimpsa_fwd_workspace_size.argtypes = [i] * 6
+            lib.palimpsa_fwd_workspace_size.restype = sz
             lib.palimpsa_step.argtypes = [vp] * 5 + [fp] * 4 + [vp] + [i] * 6 + [vp]
             lib.palimpsa_step.restype = i
             lib.palimpsa_status_string.argtypes = [i]
@@ -82,11 +86,19 @@ def _check(t, name, shape, dtype, device):
         raise ValueError("%s must be contiguous" % name)
 
 
+def workspace_size(B, T, H, dk, dv, segments: int = 0) -> int:
+    """Bytes of workspace the chunked forward uses for these sizes (0: none)."""
+    return int(load_library().palimpsa_fwd_workspace_size(B, T, H, dk, dv, int(segments)))
+
+
 def fwd_chunked(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None, chunk: int = 0,
-                out_dtype=None, y=None, muT=None, IT=None, write_state: bool = True):
+                out_dtype=None, y=None, muT=None, IT=None, write_state: bool = True,
+                segments: int = 0, workspace=None):
     """Chunked forward.  Returns ``(y, muT, IT)``; ``muT``/``IT`` are None when
     ``write_state`` is False.  Outputs are allocated unless passed in (they may
-    alias ``mu0``/``I0`` for an in-place resume)."""
+    alias ``mu0``/``I0`` for an in-place resume).  ``segments`` (0 = library's
+    choice) selects the time split; its workspace is allocated here unless a
+    uint8 device tensor is passed as ``workspace``."""
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
     B, T, H, dk = q.shape
@@ -126,12 +138,19 @@ def fwd_chunked(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None, chunk: int = 0
     else:
         muT = IT = None
     lib = load_library()
+    if workspace is None:
+        nbytes = workspace_size(B, T, H, dk, dv, segments)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
     with torch.cuda.device(dev):
         st = lib.palimpsa_fwd_chunked(
             _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(dt), _ptr(A), _ptr(I_prior),
             _ptr(mu0), _ptr(I0), _ptr(y) if y.numel() else None,
-            _ptr(muT), _ptr(IT), B, T, H, dk, dv, int(chunk),
-            _DTYPES[in_dtype], _DTYPES[out_dtype], _stream_handle(dev))
+            _ptr(muT), _ptr(IT), B, T, H, dk, dv, int(chunk), int(segments),
+            _DTYPES[in_dtype], _DTYPES[out_dtype],
+            _ptr(workspace) if workspace is not None and workspace.numel() else None,
+            workspace.numel() if workspace is not None else 0, _stream_handle(dev))
     if st != OK:
         raise PalimpsaError(st, "palimpsa_fwd_chunked")
     return y, muT, IT

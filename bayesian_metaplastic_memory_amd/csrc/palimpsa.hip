@@ -126,6 +126,24 @@ struct FwdArgs {
     int B, T, H, dv;
     int nwg;           // launched workgroups
     int xcd_remap;     // 1: remap so one head's row blocks share an XCD
+    int nwg_seg;       // workgroups per time segment: B * H * dv / 16
+    int seg_len;       // tokens per time segment (a multiple of the chunk)
+    int nseg;          // time segments (1: no split)
+    float *ws;         // segment summaries, see SegWs
+};
+
+// Workspace of a time-split forward: for each of the first nseg-1 segments,
+// its affine summary from a zero state, laid out as M_loc [nseg-1][B*H][dv][dk],
+// then Ibar_loc (same shape), then the decay product P [nseg-1][B*H].
+struct SegWs {
+    float *M, *Ib, *P;
+    size_t per_seg;    // B * H * dv * dk
+    __device__ SegWs(float *ws, int nseg, size_t bh, int dv, int dk)
+        : per_seg(bh * dv * dk) {
+        M = ws;
+        Ib = ws + (size_t)(nseg - 1) * per_seg;
+        P = Ib + (size_t)(nseg - 1) * per_seg;
+    }
 };
 
 constexpr int kWaves = 4;                 // waves per workgroup (one per SIMD)
@@ -153,13 +171,14 @@ constexpr size_t fwd_lds_bytes() { return (size_t)2 * C * Stage<DK>::kTokFloats 
 // (uniform) plus a per-thread 32-bit element offset.  Tokens past the end of
 // the sequence are staged as neutral updates (k = q = 0, beta = 0, dt = 0, so
 // alpha = 1 and c = 0): they leave (M, I) bit-identical and their y is not
-// stored, so the last chunk runs the same code as the others.
-template <int DK, int C, typename TIn>
+// stored, so the last chunk runs the same code as the others.  Without q
+// (WITHQ false, for the time-split summary pass) only k is staged.
+template <int DK, int C, typename TIn, bool WITHQ>
 struct Stager {
     static constexpr int kPerPkt = packet<TIn>::kN;            // elements per 16 B
     static constexpr int kColPkts = DK / kPerPkt;              // packets per k (or q) row
     static constexpr int kHalf = C * kColPkts;                 // k packets per chunk (= q packets)
-    static constexpr int kKQ = 2 * kHalf;
+    static constexpr int kKQ = (WITHQ ? 2 : 1) * kHalf;        // the summary pass needs no q
     static constexpr int kKQPerThread = (kKQ + kThreads - 1) / kThreads;
     static constexpr bool kSplit = kHalf % kThreads == 0;      // packet u is all-k or all-q
     static constexpr int kRowPkts = kRowsPerWG / kPerPkt;      // packets per v (or beta) row slice
@@ -374,20 +393,70 @@ __device__ inline void compute_chunk(const float *buf, int left, float *M, float
     }
 }
 
-template <int DK, int C, typename TIn, typename TOut>
+// Summary pass of a time-split forward over one staged chunk: the affine map
+// of the chunk applied to a zero start, Ibar = alpha Ibar + beta k^2 and
+// M = alpha M + (beta v) k (natural parameters, App. A.12), plus the running
+// decay product P.  4 VALU ops per entry and token, no reciprocal, no readout.
+template <int DK, int C>
+__device__ inline void summary_chunk(const float *buf, float *M, float *Ib, float &P,
+                                     int row_local, int g) {
+    using LT = LaneTile<DK>;
+    const float *cbase = buf + LT::col(g, 0, 0);
+    const float *rbase = buf + C * Stage<DK>::kColFloats + 2 * row_local;
+    int goff = C * (Stage<DK>::kColFloats + Stage<DK>::kRowFloats);
+    asm volatile("" : "+v"(goff));
+    const float *gbase = buf + goff;
+#pragma unroll 4
+    for (int u = 0; u < C; ++u) {
+        const float alpha = gbase[2 * u];
+        const float2 rb = *(const float2 *)(rbase + u * Stage<DK>::kRowFloats);     // beta, beta*v
+        const float *ct = cbase + u * Stage<DK>::kColFloats;
+        P *= alpha;
+#pragma unroll
+        for (int m = 0; m < LT::kNVec; ++m) {
+            float kk[LT::kVec], k2[LT::kVec];
+            const int c0 = kLanesPerRow * LT::kVec * m;
+            vecf<LT::kVec>::ld(ct + c0, kk);
+            vecf<LT::kVec>::ld(ct + DK + c0, k2);
+#pragma unroll
+            for (int e = 0; e < LT::kVec; ++e) {
+                const int s = m * LT::kVec + e;
+                Ib[s] = fmaf(alpha, Ib[s], rb.x * k2[e]);
+                M[s] = fmaf(alpha, M[s], rb.y * kk[e]);
+            }
+        }
+    }
+}
+
+enum FwdMode { kReplay = 0, kSummary = 1 };
+
+// One launch of the chunked forward.
+//
+// kReplay: every (head, row block, segment) runs its tokens with the readout.
+// Segment 0 starts from (mu0, I0); segment s > 0 starts from the fold of the
+// summaries of segments 0..s-1 (M = P M + M_loc, Ibar = P Ibar + Ibar_loc, the
+// composition of the affine scans).  The last segment writes (muT, IT).
+// Without a split (nseg = 1) this is the whole sequence in one pass.
+//
+// kSummary: segment s < nseg-1 runs from a zero state without readout and
+// writes its (M_loc, Ibar_loc, P) to the workspace.
+template <int DK, int C, typename TIn, typename TOut, int MODE>
 __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
     using LT = LaneTile<DK>;
     extern __shared__ float lds[];
     float *buf0 = lds;
     float *buf1 = lds + C * Stage<DK>::kTokFloats;
 
-    // workgroup -> (head, row block), keeping one head's row blocks on one XCD
+    // workgroup -> (segment, head, row block), keeping one head's row blocks
+    // of a segment on one XCD
     const int rb_per_head = a.dv / kRowsPerWG;
     int wg = blockIdx.x;
     if (a.xcd_remap) {
         const int per_xcd = a.nwg / 8;
         wg = (wg % 8) * per_xcd + wg / 8;
     }
+    const int seg = wg / a.nwg_seg;
+    wg -= seg * a.nwg_seg;
     const int bh = wg / rb_per_head;
     const int row0 = (wg % rb_per_head) * kRowsPerWG;
     const int b = bh / a.H, h = bh % a.H;
@@ -399,29 +468,58 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
     const int row = row0 + row_local;
 
     const float A = a.A[h], Ip = a.Ip[h];
+    const int t_begin = seg * a.seg_len;
+    const int t_end = min(a.T, t_begin + a.seg_len);
 
-    // initial state: M = I0 . mu0, I = I0   (or M = 0, I = I_prior)
+    // start state.  Replay: M = I0 . mu0, I = I0 (or M = 0, I = I_prior), then
+    // the earlier segments' summaries folded in.  Summary: M = Ibar = 0.
     float M[LT::kCols], I[LT::kCols];
     const size_t srow = ((size_t)bh * a.dv + row) * DK;
-    if (a.mu0) {
+    if (MODE == kSummary) {
 #pragma unroll
-        for (int m = 0; m < LT::kNVec; ++m) {
-            float mu[LT::kVec], ii[LT::kVec];
-            vecf<LT::kVec>::ld(a.mu0 + srow + LT::col(g, m, 0), mu);
-            vecf<LT::kVec>::ld(a.I0 + srow + LT::col(g, m, 0), ii);
-#pragma unroll
-            for (int e = 0; e < LT::kVec; ++e) {
-                I[m * LT::kVec + e] = ii[e];
-                M[m * LT::kVec + e] = ii[e] * mu[e];
-            }
-        }
+        for (int s = 0; s < LT::kCols; ++s) { I[s] = 0.f; M[s] = 0.f; }   // I holds Ibar here
     } else {
+        if (a.mu0) {
 #pragma unroll
-        for (int s = 0; s < LT::kCols; ++s) { I[s] = Ip; M[s] = 0.f; }
+            for (int m = 0; m < LT::kNVec; ++m) {
+                float mu[LT::kVec], ii[LT::kVec];
+                vecf<LT::kVec>::ld(a.mu0 + srow + LT::col(g, m, 0), mu);
+                vecf<LT::kVec>::ld(a.I0 + srow + LT::col(g, m, 0), ii);
+#pragma unroll
+                for (int e = 0; e < LT::kVec; ++e) {
+                    I[m * LT::kVec + e] = ii[e];
+                    M[m * LT::kVec + e] = ii[e] * mu[e];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < LT::kCols; ++s) { I[s] = Ip; M[s] = 0.f; }
+        }
+        if (seg > 0) {
+            const SegWs w(a.ws, a.nseg, (size_t)a.B * a.H, a.dv, DK);
+#pragma unroll
+            for (int s = 0; s < LT::kCols; ++s) I[s] -= Ip;              // Ibar
+            for (int sp = 0; sp < seg; ++sp) {
+                const float P = w.P[(size_t)sp * a.B * a.H + bh];
+#pragma unroll
+                for (int m = 0; m < LT::kNVec; ++m) {
+                    float ml[LT::kVec], il[LT::kVec];
+                    vecf<LT::kVec>::ld(w.M + sp * w.per_seg + srow + LT::col(g, m, 0), ml);
+                    vecf<LT::kVec>::ld(w.Ib + sp * w.per_seg + srow + LT::col(g, m, 0), il);
+#pragma unroll
+                    for (int e = 0; e < LT::kVec; ++e) {
+                        M[m * LT::kVec + e] = fmaf(P, M[m * LT::kVec + e], ml[e]);
+                        I[m * LT::kVec + e] = fmaf(P, I[m * LT::kVec + e], il[e]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < LT::kCols; ++s) I[s] += Ip;
+        }
     }
 
-    // per-sequence bases (token 0 of this (b, h)) and per-token strides
-    const size_t seq = (size_t)b * a.T * a.H + h;             // row index of (b, 0, h) in [B, T, H]
+    // per-sequence bases (token t_begin of this (b, h)) and per-token strides
+    const size_t seq = ((size_t)b * a.T + t_begin) * a.H + h;   // row of (b, t_begin, h) in [B, T, H]
     const TIn *kseq = (const TIn *)a.k + seq * DK;
     const TIn *qseq = (const TIn *)a.q + seq * DK;
     const TIn *vseq = (const TIn *)a.v + seq * a.dv + row0;
@@ -429,12 +527,14 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
     const TIn *dseq = (const TIn *)a.dt + seq;
     const size_t kq_tok = (size_t)a.H * DK, vb_tok = (size_t)a.H * a.dv;
     const size_t ystride = (size_t)a.H * a.dv;
-    TOut *ybase = (TOut *)a.y + seq * a.dv + row;
+    TOut *ybase = MODE == kReplay ? (TOut *)a.y + seq * a.dv + row : nullptr;
 
-    const int nchunks = (a.T + C - 1) / C;
-    Stager<DK, C, TIn> st;
+    const int ntok = t_end - t_begin;
+    const int nchunks = (ntok + C - 1) / C;
+    float P = 1.f;
+    Stager<DK, C, TIn, MODE == kReplay> st;
     if (nchunks > 0) {
-        st.load(kseq, qseq, vseq, bseq, dseq, a.T, a.H, a.dv, tid);
+        st.load(kseq, qseq, vseq, bseq, dseq, ntok, a.H, a.dv, tid);
         st.commit(buf0, A, Ip, tid);
         __syncthreads();
     }
@@ -444,20 +544,35 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
         if (more) {
             const size_t tn = (size_t)(t0 + C);
             st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
-                    dseq + tn * a.H, a.T - (t0 + C), a.H, a.dv, tid);
+                    dseq + tn * a.H, ntok - (t0 + C), a.H, a.dv, tid);
         }
         const float *cur = (c & 1) ? buf1 : buf0;
-        compute_chunk<DK, C, TOut>(cur, a.T - t0, M, I, row_local, g, ybase + (size_t)t0 * ystride, ystride);
+        if (MODE == kReplay)
+            compute_chunk<DK, C, TOut>(cur, ntok - t0, M, I, row_local, g, ybase + (size_t)t0 * ystride, ystride);
+        else
+            summary_chunk<DK, C>(cur, M, I, P, row_local, g);
         if (more) st.commit((c & 1) ? buf0 : buf1, A, Ip, tid);
         __syncthreads();
     }
 
-    // final state: mu = M / I (correctly rounded division), I
-    if (a.muT) {
+    if (MODE == kSummary) {
+        const SegWs w(a.ws, a.nseg, (size_t)a.B * a.H, a.dv, DK);
+#pragma unroll
+        for (int m = 0; m < LT::kNVec; ++m) {
+            vecf<LT::kVec>::st(w.M + seg * w.per_seg + srow + LT::col(g, m, 0), M + m * LT::kVec);
+            vecf<LT::kVec>::st(w.Ib + seg * w.per_seg + srow + LT::col(g, m, 0), I + m * LT::kVec);
+        }
+        if (row0 == 0 && tid == 0)
+            w.P[(size_t)seg * a.B * a.H + bh] = P;
+        return;
+    }
+
+    // final state (last segment only): mu = M / I (correctly rounded division), I
+    if (a.muT && seg == a.nseg - 1) {
 #pragma unroll
         for (int m = 0; m < LT::kNVec; ++m) {
             float mu[LT::kVec], ii[LT::kVec];
-            if (nchunks == 0 && a.mu0) {
+            if (a.T == 0 && a.mu0) {
                 vecf<LT::kVec>::ld(a.mu0 + srow + LT::col(g, m, 0), mu);   // copy through exactly
             } else {
 #pragma unroll
@@ -555,11 +670,12 @@ inline bool aligned_to(const void *p, size_t n) { return ((uintptr_t)p & (n - 1)
 inline bool head_ok(int d) { return d == 32 || d == 64 || d == 128; }
 inline bool dtype_ok(int t) { return t == PALIMPSA_F32 || t == PALIMPSA_BF16; }
 
-template <int DK, int C, typename TIn, typename TOut>
-palimpsa_status launch_fwd_t(const FwdArgs &a0, hipStream_t s) {
-    FwdArgs a = a0;
+template <int DK, int C, typename TIn, typename TOut, int MODE>
+palimpsa_status launch_pass(FwdArgs a, int nseg_launched, hipStream_t s) {
+    a.nwg = a.nwg_seg * nseg_launched;
+    a.xcd_remap = (a.nwg % 8 == 0) ? 1 : 0;
     const size_t lds = fwd_lds_bytes<DK, C>();
-    auto kern = fwd_chunked_kernel<DK, C, TIn, TOut>;
+    auto kern = fwd_chunked_kernel<DK, C, TIn, TOut, MODE>;
     if (lds > 64 * 1024) {
         if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
             return PALIMPSA_ERR_HIP;
@@ -567,6 +683,16 @@ palimpsa_status launch_fwd_t(const FwdArgs &a0, hipStream_t s) {
     (void)hipGetLastError();
     hipLaunchKernelGGL(kern, dim3(a.nwg), dim3(kThreads), lds, s, a);
     return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
+}
+
+// Summary pass (segments 0..nseg-2) then the replay pass (all segments).
+template <int DK, int C, typename TIn, typename TOut>
+palimpsa_status launch_fwd_t(const FwdArgs &a, hipStream_t s) {
+    if (a.nseg > 1) {
+        const palimpsa_status st = launch_pass<DK, C, TIn, TOut, kSummary>(a, a.nseg - 1, s);
+        if (st != PALIMPSA_OK) return st;
+    }
+    return launch_pass<DK, C, TIn, TOut, kReplay>(a, a.nseg, s);
 }
 
 template <int DK, typename TIn, typename TOut>
@@ -604,6 +730,47 @@ int pick_chunk(int requested, int dk, long long nwg, size_t lds_max) {
     return C;
 }
 
+int device_cus() {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+        return 256;
+    return v;
+}
+
+// Time segments of the forward.  With few (head, row block) workgroups the
+// GPU is under-filled, so the sequence is cut into segments that run side by
+// side (a summary pass, then a replay pass).  Auto: aim at three workgroups
+// per CU when fewer than two would run, at most 8 segments and at least 256
+// tokens per segment.  Segment lengths are multiples of 64 tokens, so the
+// chunk choice never moves a segment boundary.
+struct SegPlan {
+    int nseg, seg_len;
+    size_t ws_bytes;
+};
+SegPlan plan_segments(int B, int T, int H, int dk, int dv, int segments, int cus) {
+    const long long nwg_seg = (long long)B * H * (dv / kRowsPerWG);
+    long long S = 1;
+    if (T > 0 && segments >= 2) {
+        S = segments;
+    } else if (T > 0 && segments == 0 && nwg_seg < 2LL * cus) {
+        S = (3LL * cus) / nwg_seg;
+        S = S > 8 ? 8 : S;
+        S = S > T / 256 ? T / 256 : S;
+    }
+    const long long units = (T + 63) / 64;
+    if (S > units) S = units;
+    if (S < 1) S = 1;
+    SegPlan p;
+    p.seg_len = (int)(((T + S - 1) / S + 63) / 64 * 64);
+    if (p.seg_len == 0) p.seg_len = 64;
+    p.nseg = (int)((T + p.seg_len - 1) / p.seg_len);
+    if (p.nseg < 1) p.nseg = 1;
+    p.ws_bytes = p.nseg > 1 ? ((size_t)(p.nseg - 1) * ((size_t)2 * B * H * dv * dk + (size_t)B * H) * sizeof(float))
+                            : 0;
+    return p;
+}
+
 size_t device_lds_max() {
     int dev = 0, v = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 64 * 1024;
@@ -616,14 +783,19 @@ size_t device_lds_max() {
 
 extern "C" {
 
+size_t palimpsa_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segments) {
+    if (B <= 0 || H <= 0 || T < 0 || !head_ok(dk) || !head_ok(dv) || segments < 0) return 0;
+    return plan_segments(B, T, H, dk, dv, segments, device_cus()).ws_bytes;
+}
+
 palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v,
                                      const void *beta, const void *dt,
                                      const float *A, const float *I_prior,
                                      const float *mu0, const float *I0,
                                      void *y, float *muT, float *IT,
-                                     int B, int T, int H, int dk, int dv, int chunk,
+                                     int B, int T, int H, int dk, int dv, int chunk, int segments,
                                      palimpsa_dtype in_dtype, palimpsa_dtype out_dtype,
-                                     void *stream) {
+                                     void *workspace, size_t workspace_bytes, void *stream) {
     if (!A || !I_prior || (T > 0 && (!q || !k || !v || !beta || !dt || !y)))
         return PALIMPSA_ERR_INVALID_ARG;
     if ((mu0 == nullptr) != (I0 == nullptr) || (muT == nullptr) != (IT == nullptr))
@@ -634,10 +806,12 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
         return PALIMPSA_ERR_INVALID_ARG;
     if (chunk != 0 && chunk != 8 && chunk != 16 && chunk != 32 && chunk != 64)
         return PALIMPSA_ERR_INVALID_ARG;
+    if (segments < 0 || segments > 64 || (workspace_bytes > 0 && !workspace))
+        return PALIMPSA_ERR_INVALID_ARG;
     if (!head_ok(dk) || !head_ok(dv))
         return PALIMPSA_ERR_UNSUPPORTED;
-    // 128-bit accesses: q, k, v, beta and the state arrays; element-wise: the rest
-    const void *vec_ptrs[] = {q, k, v, beta, mu0, I0, muT, IT};
+    // 128-bit accesses: q, k, v, beta, the state arrays and the workspace; element-wise: the rest
+    const void *vec_ptrs[] = {q, k, v, beta, mu0, I0, muT, IT, workspace};
     for (const void *p : vec_ptrs)
         if (p && !aligned_to(p, 16)) return PALIMPSA_ERR_ALIGNMENT;
     const size_t in_sz = in_dtype == PALIMPSA_BF16 ? 2 : 4, out_sz = out_dtype == PALIMPSA_BF16 ? 2 : 4;
@@ -656,9 +830,19 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
     a.B = B; a.T = T; a.H = H; a.dv = dv;
     a.nwg = (int)nwg;
     a.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
+    a.nwg_seg = (int)nwg;
 
     if (T == 0 && !muT) return PALIMPSA_OK;   // nothing to compute or write
-    const int C = pick_chunk(chunk, dk, nwg, device_lds_max());
+    SegPlan plan = plan_segments(B, T, H, dk, dv, segments, device_cus());
+    if (plan.nseg > 1 && (!workspace || workspace_bytes < plan.ws_bytes)) {
+        if (segments >= 2) return PALIMPSA_ERR_INVALID_ARG;     // a split was asked for explicitly
+        plan = plan_segments(B, T, H, dk, dv, 1, 256);          // auto: run unsplit
+    }
+    if (nwg * plan.nseg > 0x7fffffffLL) return PALIMPSA_ERR_UNSUPPORTED;
+    a.nseg = plan.nseg;
+    a.seg_len = plan.seg_len;
+    a.ws = (float *)workspace;
+    const int C = pick_chunk(chunk, dk, nwg * plan.nseg, device_lds_max());
     hipStream_t s = (hipStream_t)stream;
     const bool bf_in = in_dtype == PALIMPSA_BF16, bf_out = out_dtype == PALIMPSA_BF16;
     if (bf_in && bf_out) return launch_fwd_d<bf16_t, bf16_t>(a, dk, C, s);

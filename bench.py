@@ -131,6 +131,8 @@ def main():
                     help="heads in the oracle sample (0: all heads of the workload)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--workload", default="2",
+                    help="forward workload to time: 2 (760M layer, default), 0, 1, 4 or 4b")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times "
                          "(calibrates the HBM byte counters) and exit")
@@ -156,7 +158,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_each_way": 4 * n, "launches": 3}))
         return
-    w = workloads.WORKLOADS[2]
+    w = workloads.WORKLOADS[int(args.workload) if args.workload.isdigit() else args.workload]
     inp = workloads.make_inputs(w)
     g = {n: (x.to(dev) if isinstance(x, torch.Tensor) else x) for n, x in inp.items()}
     y = torch.empty(w.B, w.T, w.H, w.dv, dtype=w.dtype, device=dev)
@@ -171,8 +173,9 @@ def main():
     updates = w.B * w.H * w.T * w.dv * w.dk
     achieved = updates * FLOPS_PER_UPDATE / avg_launch_s / 1e12
     peak = alu_peak_tflops()
-    traffic = load_traffic("fwd_chunked_layer760m_bf16_traffic.json")
-    hbm_alg = (w.B * w.T * w.H * (2 * w.dk + 2 * w.dv + 1 + w.dv) * 2
+    traffic = load_traffic("fwd_chunked_layer760m_bf16_traffic.json") if args.workload == "2" else None
+    esz = 2 if w.dtype == torch.bfloat16 else 4
+    hbm_alg = (w.B * w.T * w.H * (2 * w.dk + 2 * w.dv + 1 + w.dv) * esz
                + 8 * w.B * w.H * w.dv * w.dk)
     out = {
         "metric": "tokens/s of Palimpsa chunked forward (B*T/s) and % of HBM/MFMA roofline",
@@ -187,12 +190,13 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "760M-model layer, chunked forward", "B": w.B, "H": w.H,
+        "config": {"workload": w.name + ", chunked forward", "B": w.B, "H": w.H,
                    "T": w.T, "d_k": w.dk, "d_v": w.dv, "chunk": args.chunk or "auto",
-                   "inputs": "bf16", "state": "fp32", "global_batch": w.B, "seq_len": w.T},
+                   "inputs": str(w.dtype).replace("torch.", ""), "state": "fp32",
+                   "global_batch": w.B, "seq_len": w.T},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
-                     "kernel": "fwd_chunked_kernel<128, C, bf16, bf16>",
+                     "kernel": "fwd_chunked_kernel<%d, C, %s, %s>" % (w.dk, *(2 * [str(w.dtype)[6:]])),
                      "avg_launch_ms": avg_launch_s * 1e3,
                      "per_update": "4 FMA + 2 MUL (10 flops) + 1 v_rcp_f32 (2 FMA slots)",
                      "hbm_algorithmic_GBs": hbm_alg / avg_launch_s / 1e9},

@@ -31,7 +31,8 @@
  *    every state array are float32.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL means the default
  *    stream) and runs asynchronously; the caller synchronises.
- *  - The library allocates no device memory and keeps no per-call state.
+ *  - The library allocates no device memory and keeps no per-call state;
+ *    scratch, where a call uses any, is a caller-owned workspace argument.
  *  - Every argument is checked on the host before anything is launched; an
  *    invalid call returns an error code and launches nothing.  No C++
  *    exception crosses this interface.
@@ -81,6 +82,24 @@ typedef enum {
  *             a chunk whose staging buffers exceed the device's LDS is
  *             halved until they fit).  A performance hint only: the results
  *             are bit-identical for every chunk.
+ *   segments  time segments (0..64).  1: one pass over the sequence.  >= 2:
+ *             cut T into that many segments (lengths rounded up to multiples
+ *             of 64 tokens, so fewer may result) that run side by side: a
+ *             summary pass computes each segment's affine map from a zero
+ *             state (M_loc, Ibar_loc and the decay product, the composable
+ *             form of the natural-parameter scans, slides frame "Natural
+ *             parameters expose two affine scans"), then a replay pass starts
+ *             every segment from the composition of the earlier maps and reads
+ *             out.  0: the library decides (it splits only when B*H*dv/16
+ *             workgroups would leave the GPU under-filled).  Results of a split
+ *             match the single pass up to float32 rounding.
+ *   workspace, workspace_bytes
+ *             device scratch for the segment summaries, owned by the caller,
+ *             16-byte aligned; palimpsa_fwd_workspace_size() gives the size.
+ *             NULL / 0 is valid: with segments == 0 the forward then runs in
+ *             one pass; an explicit segments >= 2 without enough workspace is
+ *             PALIMPSA_ERR_INVALID_ARG.  Contents are overwritten; calls that
+ *             share a workspace must not overlap.
  *
  * T == 0 is valid: y is empty and the state is copied through (or, with both
  * mu0 and I0 NULL, set to mu = 0, I = I_prior); the per-token pointers q, k,
@@ -93,8 +112,16 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
                                      const float *mu0, const float *I0,
                                      void *y, float *muT, float *IT,
                                      int B, int T, int H, int dk, int dv, int chunk,
-                                     palimpsa_dtype in_dtype, palimpsa_dtype out_dtype,
-                                     void *stream);
+                                     int segments, palimpsa_dtype in_dtype,
+                                     palimpsa_dtype out_dtype, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace palimpsa_fwd_chunked needs for the split it would choose
+ * for these sizes and `segments` on the current device (0: no split, no
+ * workspace).  Returns 0 for sizes the forward would reject.
+ */
+size_t palimpsa_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segments);
 
 /*
  * One decode token (recurrent inference): the recurrence above for a single

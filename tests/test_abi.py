@@ -56,11 +56,12 @@ FAKE = 0x10000       # 16-byte aligned host address, never dereferenced
 
 def _fwd_args(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dt=FAKE, A=FAKE, Ip=FAKE, mu0=None, I0=None,
-             y=FAKE, muT=FAKE, IT=FAKE, B=2, T=8, H=3, dk=64, dv=64, chunk=0, ind=1, outd=1,
-             stream=None)
+             y=FAKE, muT=FAKE, IT=FAKE, B=2, T=8, H=3, dk=64, dv=64, chunk=0, segments=0,
+             ind=1, outd=1, ws=None, wsb=0, stream=None)
     a.update(over)
     return [a[n] for n in ("q", "k", "v", "beta", "dt", "A", "Ip", "mu0", "I0", "y", "muT", "IT",
-                           "B", "T", "H", "dk", "dv", "chunk", "ind", "outd", "stream")]
+                           "B", "T", "H", "dk", "dv", "chunk", "segments", "ind", "outd",
+                           "ws", "wsb", "stream")]
 
 
 FWD_CASES = [
@@ -73,7 +74,25 @@ FWD_CASES = [
     (dict(q=FAKE + 4), 3), (dict(v=FAKE + 8), 3),
     (dict(mu0=FAKE + 4, I0=FAKE), 3), (dict(IT=FAKE + 12), 3), (dict(dt=FAKE + 1), 3),
     (dict(y=FAKE + 1), 3), (dict(A=FAKE + 2), 3), (dict(beta=FAKE + 2), 3),
+    (dict(segments=-1), 1), (dict(segments=65), 1), (dict(wsb=64), 1),
+    (dict(ws=FAKE + 8, wsb=64), 3),
 ]
+
+
+def test_workspace_size_host_logic(lib):
+    """Segment planning is host logic: auto splits only under-filled grids."""
+    import bayesian_metaplastic_memory_amd as pm
+    # 760M layer (768 workgroups): no split
+    assert pm.workspace_size(8, 4096, 12, 128, 128, 0) == 0
+    # long context, 32 heads (256 workgroups): 3 segments -> 2 summaries
+    assert pm.workspace_size(1, 32768, 32, 128, 128, 0) == 2 * (2 * 32 * 128 * 128 + 32) * 4
+    # explicit requests; rounding to 64-token segments caps the count
+    assert pm.workspace_size(1, 1000, 2, 64, 64, 4) == 3 * (2 * 2 * 64 * 64 + 2) * 4
+    assert pm.workspace_size(1, 100, 2, 64, 64, 8) == 1 * (2 * 2 * 64 * 64 + 2) * 4
+    assert pm.workspace_size(1, 64, 2, 64, 64, 8) == 0
+    assert pm.workspace_size(1, 4096, 2, 64, 64, 1) == 0
+    assert pm.workspace_size(1, 0, 2, 64, 64, 4) == 0
+    assert pm.workspace_size(1, 64, 2, 48, 64, 0) == 0
 
 
 @pytest.mark.parametrize("over,status", FWD_CASES)

@@ -329,3 +329,65 @@ def test_binding_reports_library_errors():
     with pytest.raises(pm.PalimpsaError) as e:
         pm.fwd_chunked(x48, x48, x48, x48, dt, torch.ones(1, device=DEV), torch.ones(1, device=DEV))
     assert e.value.status == 2
+
+
+# ---------------------------------------------------------------------------
+# time-split forward (summary pass + replay pass)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("segments", [2, 3, 5, 64])
+@pytest.mark.parametrize("dk,dv,T", [(64, 64, 1000), (128, 32, 333), (32, 128, 700)])
+def test_time_split_matches_oracle_and_single_pass(segments, dk, dv, T):
+    w = workloads.WORKLOADS[1].with_(B=2, H=2, dk=dk, dv=dv, key_pool=0, A_mode="logspace16")
+    _announce("time split", segments=segments, T=T, dk=dk, dv=dv)
+    inp = workloads.make_inputs(w, T=T)
+    mu0, I0 = workloads.random_state(2, 2, dv, dk, inp["I_prior"], seed=segments + T)
+    inp["mu0"], inp["I0"] = mu0, I0
+    g = to_device(inp, DEV)
+    pm = _pm()
+    assert pm.workspace_size(2, T, 2, dk, dv, segments) > 0
+    y1, mu1, I1 = pm.fwd_chunked(*gpu_args(g), mu0=g["mu0"], I0=g["I0"], segments=1)
+    ys, mus, Is = pm.fwd_chunked(*gpu_args(g), mu0=g["mu0"], I0=g["I0"], segments=segments)
+    torch.cuda.synchronize()
+    assert rel_err(ys, y1) <= 1e-5 and rel_err(mus, mu1) <= 1e-5 and rel_err(Is, I1) <= 1e-5
+    _compare_full(inp, ys, mus, Is, tol=1e-4)
+
+
+def test_time_split_chunk_invariance_and_bf16():
+    w = workloads.WORKLOADS[4].with_(H=4, T=3000)
+    _announce("time split bf16 chunk invariance", B=1, H=4, T=3000)
+    inp = workloads.make_inputs(w)
+    outs = [_pm().fwd_chunked(*gpu_args(to_device(inp, DEV)), segments=4, chunk=c) for c in (16, 32, 64)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        for x, z in zip(outs[0], o):
+            assert torch.equal(x, z)
+    _compare_full(inp, *outs[0], tol=tol_for(w.dtype))
+
+
+def test_time_split_requires_workspace():
+    pm = _pm()
+    w = workloads.WORKLOADS[0]
+    _announce("time split without workspace")
+    g = to_device(workloads.make_inputs(w), DEV)
+    with pytest.raises(pm.PalimpsaError) as e:
+        pm.fwd_chunked(*gpu_args(g), segments=3, workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+    assert e.value.status == 1
+    # auto with no workspace runs in one pass
+    y, muT, IT = pm.fwd_chunked(*gpu_args(g), segments=0,
+                                workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    _compare_full(workloads.make_inputs(w), y, muT, IT, tol=1e-4)
+
+
+def test_long_context_auto_split_matches_single_pass():
+    w = workloads.WORKLOADS[4]
+    pm = _pm()
+    assert pm.workspace_size(w.B, w.T, w.H, w.dk, w.dv, 0) > 0      # the auto path splits here
+    _announce("long context auto split vs one pass", B=w.B, H=w.H, T=w.T)
+    g = to_device(workloads.make_inputs(w), DEV)
+    a = pm.fwd_chunked(*gpu_args(g), segments=0, out_dtype=torch.float32)
+    b = pm.fwd_chunked(*gpu_args(g), segments=1, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for x, z in zip(a, b):
+        assert rel_err(x, z) <= 1e-5
