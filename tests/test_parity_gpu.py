@@ -391,3 +391,35 @@ def test_long_context_auto_split_matches_single_pass():
     torch.cuda.synchronize()
     for x, z in zip(a, b):
         assert rel_err(x, z) <= 1e-5
+
+
+def test_decode_steps_replay_in_a_hip_graph():
+    """Captured decode launches replay to the same results as eager ones, every
+    replay, with eager work and synchronisations in between."""
+    pm = _pm()
+    w = workloads.WORKLOADS[3].with_(B=4, H=4)
+    _announce("decode graph replay", B=w.B, H=w.H, steps_per_graph=3, replays=4)
+    A, Ip = (x.to(DEV) for x in workloads.head_constants(w))
+    mu0, I0 = workloads.random_state(w.B, w.H, w.dv, w.dk, Ip.cpu(), seed=11)
+    d = [to_device(workloads.decode_inputs(w, s), DEV) for s in range(3)]
+    mu_g, I_g = mu0.to(DEV), I0.to(DEV)
+    ys = [torch.empty(w.B, w.H, w.dv, dtype=w.dtype, device=DEV) for _ in range(3)]
+    run = lambda mu, I, out: [pm.step(x["q"], x["k"], x["v"], x["beta"], x["dt"], A, Ip, mu, I, y=o)
+                              for x, o in zip(d, out)]
+    run(mu_g.clone(), I_g.clone(), [torch.empty_like(y) for y in ys])    # warm the binding
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(mu_g, I_g, ys)
+    mu_e, I_e = mu0.to(DEV), I0.to(DEV)
+    for r in range(4):
+        mu_g.copy_(mu_e)
+        I_g.copy_(I_e)
+        torch.cuda.synchronize()
+        graph.replay()
+        ye = [torch.empty_like(y) for y in ys]
+        run(mu_e, I_e, ye)                      # eager reference advances from the same state
+        torch.cuda.synchronize()
+        for a, b in zip(ys, ye):
+            assert torch.equal(a, b), "replay %d" % r
+        assert torch.equal(mu_g, mu_e) and torch.equal(I_g, I_e)
