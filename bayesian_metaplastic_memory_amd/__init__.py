@@ -4,8 +4,8 @@
 kernels of ``libpalimpsa.so`` through its C ABI; see ``include/palimpsa.h``
 for the operation, layouts and error behaviour.
 """
-from ._binding import (BF16, F32, LIB_PATH, PalimpsaError, fwd_chunked, load_library,
+from ._binding import (BF16, F32, LIB_PATH, PalimpsaError, fwd_chunked, fwd_frozen, load_library,
                        status_string, step, version, workspace_size)
 
-__all__ = ["fwd_chunked", "step", "workspace_size", "load_library", "status_string", "version",
+__all__ = ["fwd_chunked", "fwd_frozen", "step", "workspace_size", "load_library", "status_string", "version",
            "PalimpsaError", "LIB_PATH", "F32", "BF16"]

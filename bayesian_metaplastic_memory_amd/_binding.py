@@ -47,6 +47,8 @@ def load_library() -> ctypes.CDLL:
             lib.palimpsa_fwd_chunked.restype = i
             lib.palimpsa_fwd_workspace_size.argtypes = [i] * 6
             lib.palimpsa_fwd_workspace_size.restype = sz
+            lib.palimpsa_fwd_frozen.argtypes = [vp] * 5 + [fp] * 3 + [vp, fp] + [i] * 7 + [vp]
+            lib.palimpsa_fwd_frozen.restype = i
             lib.palimpsa_step.argtypes = [vp] * 5 + [fp] * 4 + [vp] + [i] * 6 + [vp]
             lib.palimpsa_step.restype = i
             lib.palimpsa_status_string.argtypes = [i]
@@ -191,3 +193,50 @@ def step(q, k, v, beta, dt, A, I_prior, mu, I, out_dtype=None, y=None):
     if st != OK:
         raise PalimpsaError(st, "palimpsa_step")
     return y
+
+
+def fwd_frozen(q, k, v, beta, dt, A, I_prior, mu0=None, out_dtype=None, y=None, muT=None,
+               write_state: bool = True):
+    """Frozen-importance (Mamba2-limit) forward on the matrix cores.  ``beta``
+    may be None when ``v`` already holds beta * v.  Returns ``(y, muT)``."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    in_dtype = q.dtype
+    if in_dtype not in _DTYPES:
+        raise ValueError("unsupported input dtype %s" % in_dtype)
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    if out_dtype not in _DTYPES:
+        raise ValueError("unsupported output dtype %s" % out_dtype)
+    _check(k, "k", (B, T, H, dk), in_dtype, dev)
+    _check(v, "v", (B, T, H, dv), in_dtype, dev)
+    if beta is not None:
+        _check(beta, "beta", (B, T, H, dv), in_dtype, dev)
+    _check(dt, "dt", (B, T, H), in_dtype, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(I_prior, "I_prior", (H,), torch.float32, dev)
+    if mu0 is not None:
+        _check(mu0, "mu0", (B, H, dv, dk), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _check(y, "y", (B, T, H, dv), out_dtype, dev)
+    if write_state:
+        if muT is None:
+            muT = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        _check(muT, "muT", (B, H, dv, dk), torch.float32, dev)
+    else:
+        muT = None
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.palimpsa_fwd_frozen(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(dt), _ptr(A), _ptr(I_prior), _ptr(mu0),
+            _ptr(y) if y.numel() else None, _ptr(muT), B, T, H, dk, dv,
+            _DTYPES[in_dtype], _DTYPES[out_dtype], _stream_handle(dev))
+    if st != OK:
+        raise PalimpsaError(st, "palimpsa_fwd_frozen")
+    return y, muT

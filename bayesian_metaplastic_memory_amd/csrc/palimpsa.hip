@@ -587,6 +587,355 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// frozen-importance forward (the Mamba2 limit) on the matrix cores
+// ---------------------------------------------------------------------------
+//
+// With the importance held at I_prior (slides frame "The Mamba2 limit enables
+// a gradual model upgrade", Secs. 2.3-2.4) the recurrence is
+//     mu_t = alpha_t mu_{t-1} + w_t (x) k_t,   w_t = beta_t . v_t / I_prior,
+//     y_t  = mu_t q_t,
+// a scalar-decay linear attention whose chunked form is dense: per chunk of
+// 64 tokens with Lam_t = sum_{r<=t} (-A dt_r),
+//     Y     = diag(e^Lam) Q S^T + (L . Q K^T) W,   L_ts = e^(Lam_t - Lam_s) [s <= t]
+//     S_end = e^Lam_end S + W^T diag(e^(Lam_end - Lam)) K.
+// All four products run on v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32
+// accumulation); the state S stays in fp32 accumulators for the whole sequence.
+//
+// One workgroup owns 64 value rows of one head (see frozen_fwd_kernel for the
+// split of its 8 waves into staging and compute).
+// MFMA fragments (16x16x32): A lane l = row l%16, k = 8(l/16)+j; B lane l =
+// column l%16, k = 8(l/16)+j; D lane l = rows 4(l/16)+r of column l%16.  The
+// state is kept as S^T tiles in D layout, which are fed back as A operands of
+// S Q^T with the k index permuted (4 consecutive j from each of two tiles);
+// the matching B operand reads Q with the same permutation.
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kFzC = 64;       // tokens per chunk
+constexpr int kFzRows = 64;    // value rows per workgroup
+
+struct FrozenArgs {
+    const bf16_t *q, *k, *v, *beta, *dt;      // beta NULL: v already holds beta . v
+    const float *A, *Ip, *mu0;
+    void *y;
+    float *muT;
+    int B, T, H, dv;
+    int y_bf16;
+};
+
+template <int DK>
+struct FzLds {
+    // One staging buffer (bf16 unless noted); two are used alternately.  Rows
+    // are padded by 8 elements (16 bytes) so that the 16 rows a fragment read
+    // touches fall in distinct LDS banks.
+    static constexpr int kQS = DK + 8;                   // row stride of Q and K
+    static constexpr int kTS = kFzC + 8;                 // row stride of the token-minor arrays
+    static constexpr int kQ = 0;                         // Q  [C][DK]
+    static constexpr int kK = kQ + kFzC * kQS;           // K  [C][DK]
+    static constexpr int kKt = kK + kFzC * kQS;          // K^T [DK][C]
+    static constexpr int kWt = kKt + DK * kTS;           // W^T [64][C]
+    static constexpr int kWdt = kWt + kFzRows * kTS;     // (diag(d) W)^T [64][C]
+    static constexpr int kBufHalves = kWdt + kFzRows * kTS;
+    static constexpr int kLamBytes = kFzC * 4;           // Lam [C] float, after the halves
+    static constexpr int kBufBytes = kBufHalves * 2 + kLamBytes;
+    static constexpr int kTotal = 2 * kBufBytes;
+};
+
+// Dword i of a 16-byte packet, and the bf16 in its low / high half as float.
+// (Indexing a register packet through a pointer would push it to scratch.)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline uint32_t u4get(const u32x4 &p, int i) { return p[i]; }
+__device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (bf16_t)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (bf16_t)hi) << 16);
+}
+
+__device__ inline bf16x8_t lds_b128(const bf16_t *p) { return *(const bf16x8_t *)p; }
+__device__ inline bf16x4_t lds_b64(const bf16_t *p) { return *(const bf16x4_t *)p; }
+__device__ inline bf16x8_t cat8(bf16x4_t x, bf16x4_t y) {
+    return bf16x8_t{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+}
+// index of the lower-triangle score tile (s block sb <= query block tb)
+__device__ constexpr int tri(int sb, int tb) { return tb * (tb + 1) / 2 + sb; }
+
+// Warp-specialised: waves 0-3 compute chunk c while waves 4-7 widen and
+// stage chunk c+1 into the other LDS buffer and load chunk c+2 from HBM; one
+// barrier per chunk.  Compute wave w owns value rows [16w, 16w+16) of the
+// workgroup: it forms all 10 lower-triangle score tiles of the chunk (so the
+// decay-masked scores never leave its registers), then Y for its rows and
+// its part of the state.
+template <int DK>
+__global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
+    using L = FzLds<DK>;
+    extern __shared__ float lds_f[];
+    char *lds = (char *)lds_f;
+    const int rb_per_head = a.dv / kFzRows;
+    const int bh = blockIdx.x / rb_per_head;
+    const int ib0 = (blockIdx.x % rb_per_head) * kFzRows;      // first value row of the workgroup
+    const int b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const bool stager = wv >= 4;
+    const int w = wv & 3;
+    const int lr = lane & 15, lg = lane >> 4;                 // fragment row/col and lane group
+    const float Ah = a.A[h], inv_ip = 1.f / a.Ip[h];
+    const size_t seq = (size_t)b * a.T * a.H + h;            // [B, T, H] row of (b, 0, h)
+    const int nchunks = (a.T + kFzC - 1) / kFzC;
+
+    // ---- staging waves (threads 256..511, index u = tid - 256).  Roles:
+    //   u in [0, DK):        one 8x8 block of K (tokens 8 (u / (DK/8)).., columns
+    //                        8 (u % (DK/8))..), written as K rows and, transposed in
+    //                        registers, as K^T rows
+    //   u in [DK, DK+64):    8 tokens x DK/8 columns of Q
+    //   u in [DK+64, DK+128): one 8x8 block of W = beta . v / I_prior (tokens
+    //                        8 (x/8).., value rows 8 (x%8).., x = u - DK - 64),
+    //                        written transposed as W^T and (diag(d) W)^T; this
+    //                        wave (exactly one) also scans the gate
+    //   u >= DK+128:         idle (d_k = 64)
+    // Loads read a valid row (clamped to T-1); tokens past the end are zeroed
+    // when written (q = k = w = 0, dt = 0: no effect on y or the state).
+    const int u = tid - 256;
+    u32x4 pr[16];                 // 16-byte packets of this thread's role
+    float pdt = 0.f;
+    auto load = [&](int t0) __attribute__((always_inline)) {
+        if (u < DK) {
+            const int tok0 = 8 * (u / (DK / 8)), col = 8 * (u % (DK / 8));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const size_t row = seq + (size_t)min(t0 + tok0 + e, a.T - 1) * a.H;
+                pr[e] = *(const u32x4 *)(a.k + row * DK + col);
+            }
+        } else if (u < DK + 64) {
+            const int tok0 = 8 * ((u - DK) / 8), col0 = (DK / 8) * ((u - DK) % 8);
+            // 8 tokens x DK/8 columns = DK/8 packets (<= 16)
+#pragma unroll
+            for (int e = 0; e < DK / 8; ++e) {
+                const int tt = e / (DK / 64), cc = col0 + 8 * (e % (DK / 64));
+                const size_t row = seq + (size_t)min(t0 + tok0 + tt, a.T - 1) * a.H;
+                pr[e] = *(const u32x4 *)(a.q + row * DK + cc);
+            }
+        } else if (u < DK + 128) {
+            const int x = u - DK - 64, tok0 = 8 * (x / 8), i0 = ib0 + 8 * (x % 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const size_t row = seq + (size_t)min(t0 + tok0 + e, a.T - 1) * a.H;
+                pr[e] = *(const u32x4 *)(a.v + row * a.dv + i0);
+                pr[8 + e] = a.beta ? *(const u32x4 *)(a.beta + row * a.dv + i0)
+                                   : u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0
+            }
+            pdt = (float)a.dt[seq + (size_t)min(t0 + lane, a.T - 1) * a.H];
+        }
+    };
+    // 8x8 transpose of bf16: out[c] holds element c of in[0..7]
+    auto transpose8 = [](const u32x4 (&in)[8], u32x4 (&out)[8]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int wd = c / 2;
+            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+            out[c] = u32x4{__builtin_amdgcn_perm(u4get(in[1], wd), u4get(in[0], wd), sel),
+                                __builtin_amdgcn_perm(u4get(in[3], wd), u4get(in[2], wd), sel),
+                                __builtin_amdgcn_perm(u4get(in[5], wd), u4get(in[4], wd), sel),
+                                __builtin_amdgcn_perm(u4get(in[7], wd), u4get(in[6], wd), sel)};
+        }
+    };
+    auto commit = [&](char *buf, int t0) __attribute__((always_inline)) {
+        bf16_t *hb = (bf16_t *)buf;
+        float *lam = (float *)(buf + L::kBufHalves * 2);
+        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+        if (u < DK) {
+            const int tok0 = 8 * (u / (DK / 8)), col = 8 * (u % (DK / 8));
+            u32x4 kin[8], kt[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kin[e] = (t0 + tok0 + e < a.T) ? pr[e] : z;
+                *(u32x4 *)(hb + L::kK + (tok0 + e) * L::kQS + col) = kin[e];
+            }
+            transpose8(kin, kt);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) *(u32x4 *)(hb + L::kKt + (col + c) * L::kTS + tok0) = kt[c];
+        } else if (u < DK + 64) {
+            const int tok0 = 8 * ((u - DK) / 8), col0 = (DK / 8) * ((u - DK) % 8);
+#pragma unroll
+            for (int e = 0; e < DK / 8; ++e) {
+                const int tt = e / (DK / 64), cc = col0 + 8 * (e % (DK / 64));
+                *(u32x4 *)(hb + L::kQ + (tok0 + tt) * L::kQS + cc) = (t0 + tok0 + tt < a.T) ? pr[e] : z;
+            }
+        } else if (u < DK + 128) {
+            // gate: inclusive prefix sum of -A dt over the chunk, one token per lane
+            float x = (t0 + lane < a.T) ? -Ah * pdt : 0.f;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const float y = __shfl_up(x, o, 64);
+                if (lane >= o) x += y;
+            }
+            const float dl = __expf(__shfl(x, 63, 64) - x);   // e^(Lam_end - Lam_s)
+            lam[lane] = x;
+            const int xb = u - DK - 64, tok0 = 8 * (xb / 8), il0 = 8 * (xb % 8);
+            u32x4 win[8], wdn[8], wt[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float de = __shfl(dl, tok0 + e, 64);
+                const bool ok = t0 + tok0 + e < a.T;
+                uint32_t ww[4], wd[4];
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) {
+                    const uint32_t vw = u4get(pr[e], pp), bw = u4get(pr[8 + e], pp);
+                    const float w0 = ok ? bf_lo(bw) * bf_lo(vw) * inv_ip : 0.f;
+                    const float w1 = ok ? bf_hi(bw) * bf_hi(vw) * inv_ip : 0.f;
+                    ww[pp] = pack_bf16(w0, w1);
+                    wd[pp] = pack_bf16(w0 * de, w1 * de);
+                }
+                win[e] = u32x4{ww[0], ww[1], ww[2], ww[3]};
+                wdn[e] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+            }
+            transpose8(win, wt);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) *(u32x4 *)(hb + L::kWt + (il0 + c) * L::kTS + tok0) = wt[c];
+            transpose8(wdn, wt);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) *(u32x4 *)(hb + L::kWdt + (il0 + c) * L::kTS + tok0) = wt[c];
+        }
+    };
+
+    // ---- compute waves: state S^T tiles (jb, rows of wave w); lane holds
+    // S^T[16 jb + 4 lg + r][16 w + lr] = S[i][j]
+    f32x4 St[DK / 16];
+    const int irow = ib0 + 16 * w + lr;
+    const size_t srow = ((size_t)bh * a.dv + irow) * DK;
+    if (!stager) {
+        if (a.mu0) {
+#pragma unroll
+            for (int jb = 0; jb < DK / 16; ++jb) St[jb] = *(const f32x4 *)(a.mu0 + srow + 16 * jb + 4 * lg);
+        } else {
+#pragma unroll
+            for (int jb = 0; jb < DK / 16; ++jb) St[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    } else if (nchunks > 0) {
+        load(0);
+        commit(lds, 0);
+        if (nchunks > 1) load(kFzC);
+    }
+    __syncthreads();
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * kFzC;
+        if (stager) {
+            if (c + 1 < nchunks) {
+                commit(lds + ((c + 1) & 1) * L::kBufBytes, t0 + kFzC);
+                if (c + 2 < nchunks) load(t0 + 2 * kFzC);
+            }
+        } else {
+            const char *buf = lds + (c & 1) * L::kBufBytes;
+            const bf16_t *hb = (const bf16_t *)buf;
+            const float *lam = (const float *)(buf + L::kBufHalves * 2);
+
+            // (a) scores G^T[s][t] = k_s . q_t for the 10 tiles with s block <= t block
+            f32x4 g[10];
+#pragma unroll
+            for (int i = 0; i < 10; ++i) g[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                bf16x8_t qf[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    qf[x] = lds_b128(hb + L::kQ + (16 * x + lr) * L::kQS + 32 * kk + 8 * lg);
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) {
+                    const bf16x8_t kf = lds_b128(hb + L::kK + (16 * sb + lr) * L::kQS + 32 * kk + 8 * lg);
+#pragma unroll
+                    for (int tb = sb; tb < 4; ++tb)
+                        g[tri(sb, tb)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[tb], g[tri(sb, tb)], 0, 0, 0);
+                }
+            }
+            // decay and causal mask: P^T[s][t] = G^T[s][t] e^(Lam_t - Lam_s) for s <= t, as bf16
+            bf16x4_t pt[10];
+            float lam_t[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) lam_t[tb] = lam[16 * tb + lr];
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                const f32x4 ls = *(const f32x4 *)(lam + 16 * sb + 4 * lg);
+#pragma unroll
+                for (int tb = sb; tb < 4; ++tb) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const bool keep = sb < tb || 4 * lg + r <= lr;
+                        pt[tri(sb, tb)][r] = (bf16_t)(keep ? g[tri(sb, tb)][r] * __expf(lam_t[tb] - ls[r]) : 0.f);
+                    }
+                }
+            }
+
+            // (c) Y^T for value rows of wave w: intra-chunk W^T P^T + inter-chunk S Q^T e^Lam_t.
+            // The k index (token s) of the intra product follows the P^T
+            // fragments: slots 0-3 = s 4lg..4lg+3 of s block 2ks, slots 4-7 of block 2ks+1.
+            bf16x8_t sa[DK / 32];
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    sa[kk][r] = (bf16_t)St[2 * kk][r];
+                    sa[kk][4 + r] = (bf16_t)St[2 * kk + 1][r];
+                }
+            }
+            const bf16_t *wrow = hb + L::kWt + (16 * w + lr) * L::kTS + 4 * lg;
+            const bf16x4_t zero4 = {(bf16_t)0.f, (bf16_t)0.f, (bf16_t)0.f, (bf16_t)0.f};
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                f32x4 yi = {0.f, 0.f, 0.f, 0.f}, ye = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks <= tb / 2; ++ks) {
+                    const bf16x8_t av = cat8(lds_b64(wrow + 32 * ks), lds_b64(wrow + 32 * ks + 16));
+                    const bf16x8_t bv = cat8(pt[tri(2 * ks, tb)], 2 * ks + 1 <= tb ? pt[tri(2 * ks + 1 <= tb ? 2 * ks + 1 : 0, tb)] : zero4);
+                    yi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, yi, 0, 0, 0);
+                }
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) {
+                    const bf16_t *qrow = hb + L::kQ + (16 * tb + lr) * L::kQS + 32 * kk + 4 * lg;
+                    ye = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[kk], cat8(lds_b64(qrow), lds_b64(qrow + 16)), ye, 0, 0, 0);
+                }
+                const int t = 16 * tb + lr;
+                const float et = __expf(lam_t[tb]);
+                if (t0 + t < a.T) {
+                    const size_t yo = (seq + (size_t)(t0 + t) * a.H) * a.dv + ib0 + 16 * w + 4 * lg;
+                    float o[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = fmaf(et, ye[r], yi[r]);
+                    if (a.y_bf16) {
+                        const bf16x4_t ob = {(bf16_t)o[0], (bf16_t)o[1], (bf16_t)o[2], (bf16_t)o[3]};
+                        *(bf16x4_t *)((bf16_t *)a.y + yo) = ob;
+                    } else {
+                        *(f32x4 *)((float *)a.y + yo) = f32x4{o[0], o[1], o[2], o[3]};
+                    }
+                }
+            }
+
+            // (e) state: S^T = e^Lam_end S^T + K^T diag(d) W
+            const float e_end = __expf(lam[kFzC - 1]);
+            bf16x8_t wd[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) wd[ks] = lds_b128(hb + L::kWdt + (16 * w + lr) * L::kTS + 32 * ks + 8 * lg);
+#pragma unroll
+            for (int jb = 0; jb < DK / 16; ++jb) {
+                f32x4 acc = St[jb] * e_end;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        lds_b128(hb + L::kKt + (16 * jb + lr) * L::kTS + 32 * ks + 8 * lg), wd[ks], acc, 0, 0, 0);
+                St[jb] = acc;
+            }
+        }
+        __syncthreads();
+    }
+    if (!stager && a.muT) {
+#pragma unroll
+        for (int jb = 0; jb < DK / 16; ++jb)
+            *(f32x4 *)(a.muT + srow + 16 * jb + 4 * lg) = St[jb];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // decode step
 // ---------------------------------------------------------------------------
 
@@ -779,9 +1128,54 @@ size_t device_lds_max() {
     return (size_t)v;
 }
 
+template <int DK>
+palimpsa_status launch_frozen(const FrozenArgs &a, hipStream_t s) {
+    constexpr size_t lds = FzLds<DK>::kTotal;
+    auto kern = frozen_fwd_kernel<DK>;
+    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return PALIMPSA_ERR_HIP;
+    const long long grid = (long long)a.B * a.H * (a.dv / kFzRows);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, s, a);
+    return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+palimpsa_status palimpsa_fwd_frozen(const void *q, const void *k, const void *v,
+                                    const void *beta, const void *dt,
+                                    const float *A, const float *I_prior, const float *mu0,
+                                    void *y, float *muT, int B, int T, int H, int dk, int dv,
+                                    palimpsa_dtype in_dtype, palimpsa_dtype out_dtype,
+                                    void *stream) {
+    if (!A || !I_prior || (T > 0 && (!q || !k || !v || !dt || !y)))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0)
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (in_dtype != PALIMPSA_BF16 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+        return PALIMPSA_ERR_UNSUPPORTED;
+    const void *vec_ptrs[] = {q, k, v, beta, mu0, muT, y};
+    for (const void *p : vec_ptrs)
+        if (p && !aligned_to(p, 16)) return PALIMPSA_ERR_ALIGNMENT;
+    if (!aligned_to(dt, 2) || !aligned_to(A, 4) || !aligned_to(I_prior, 4))
+        return PALIMPSA_ERR_ALIGNMENT;
+    if ((long long)B * H * (dv / kFzRows) > 0x7fffffffLL || (long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 46))
+        return PALIMPSA_ERR_UNSUPPORTED;
+    FrozenArgs a;
+    a.q = (const bf16_t *)q; a.k = (const bf16_t *)k; a.v = (const bf16_t *)v;
+    a.beta = (const bf16_t *)beta; a.dt = (const bf16_t *)dt;
+    a.A = A; a.Ip = I_prior; a.mu0 = mu0; a.y = y; a.muT = muT;
+    a.B = B; a.T = T; a.H = H; a.dv = dv;
+    a.y_bf16 = out_dtype == PALIMPSA_BF16;
+    if (T == 0 && !muT) return PALIMPSA_OK;
+    hipStream_t s = (hipStream_t)stream;
+    return dk == 64 ? launch_frozen<64>(a, s) : launch_frozen<128>(a, s);
+}
+
 
 size_t palimpsa_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segments) {
     if (B <= 0 || H <= 0 || T < 0 || !head_ok(dk) || !head_ok(dv) || segments < 0) return 0;

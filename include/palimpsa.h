@@ -124,6 +124,38 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
 size_t palimpsa_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segments);
 
 /*
+ * Frozen-importance forward: the Mamba2 limit of the recurrence, in which the
+ * importance stays at I_prior (slides frame "The Mamba2 limit enables a
+ * gradual model upgrade"; reading notes section 2.8):
+ *
+ *     mu_t = alpha_t mu_{t-1} + (beta_t . v_t / I_prior[h]) (x) k_t,   y_t = mu_t q_t
+ *
+ * It is the recurrence of the "without metaplasticity" model that a Palimpsa
+ * layer upgrades, and the exact form's limit for small excess importance.
+ * Its chunked form is dense, so it runs on the matrix cores (bf16 operands,
+ * fp32 accumulation, fp32 state).
+ *
+ *   q, k      [B, T, H, dk]  bf16 (in_dtype must be PALIMPSA_BF16)
+ *   v, beta   [B, T, H, dv]  bf16; beta NULL means v already holds beta . v
+ *             (the reparameterised write v* of the same frame)
+ *   dt        [B, T, H]      bf16
+ *   A, I_prior [H]           float32
+ *   mu0       [B, H, dv, dk] float32 initial mean, or NULL for 0
+ *   y         [B, T, H, dv]  out_dtype
+ *   muT       [B, H, dv, dk] float32 final mean, or NULL to skip
+ *
+ * dk, dv in {64, 128}; other sizes or fp32 inputs return PALIMPSA_ERR_UNSUPPORTED.
+ * q, k, v, beta, mu0, muT and y must be 16-byte aligned.  Rounding: operands
+ * of the products are bf16, so y carries about 2^-8 relative error.
+ */
+palimpsa_status palimpsa_fwd_frozen(const void *q, const void *k, const void *v,
+                                    const void *beta, const void *dt,
+                                    const float *A, const float *I_prior, const float *mu0,
+                                    void *y, float *muT, int B, int T, int H, int dk, int dv,
+                                    palimpsa_dtype in_dtype, palimpsa_dtype out_dtype,
+                                    void *stream);
+
+/*
  * One decode token (recurrent inference): the recurrence above for a single
  * t, applied in place to a state held as (mu, I).
  *

@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("palimpsa_fwd_chunked", "palimpsa_step", "palimpsa_status_string", "palimpsa_version"):
+    for n in ("palimpsa_fwd_chunked", "palimpsa_fwd_workspace_size", "palimpsa_fwd_frozen",
+              "palimpsa_step", "palimpsa_status_string", "palimpsa_version"):
         assert n in names
 
 
@@ -143,3 +144,24 @@ def test_binding_fails_loudly_without_a_gpu_tensor():
     x = torch.zeros(1, 4, 1, 32)
     with pytest.raises(ValueError):
         pm.fwd_chunked(x, x, x, x, torch.zeros(1, 4, 1), torch.ones(1), torch.ones(1))
+
+
+def _frozen_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dt=FAKE, A=FAKE, Ip=FAKE, mu0=None, y=FAKE,
+             muT=FAKE, B=2, T=8, H=3, dk=128, dv=64, ind=1, outd=1, stream=None)
+    a.update(over)
+    return [a[n] for n in ("q", "k", "v", "beta", "dt", "A", "Ip", "mu0", "y", "muT",
+                           "B", "T", "H", "dk", "dv", "ind", "outd", "stream")]
+
+
+FROZEN_CASES = [
+    (dict(q=None), 1), (dict(dt=None), 1), (dict(y=None), 1), (dict(A=None), 1), (dict(B=0), 1),
+    (dict(T=-2), 1), (dict(ind=3), 1), (dict(ind=0), 2), (dict(dk=32), 2), (dict(dv=32), 2),
+    (dict(dk=48), 2), (dict(q=FAKE + 8), 3), (dict(y=FAKE + 8), 3), (dict(beta=FAKE + 4), 3),
+    (dict(mu0=FAKE + 4), 3), (dict(dt=FAKE + 1), 3),
+]
+
+
+@pytest.mark.parametrize("over,status", FROZEN_CASES)
+def test_frozen_rejects_invalid_calls(lib, over, status):
+    assert lib.palimpsa_fwd_frozen(*_frozen_args(**over)) == status

@@ -423,3 +423,79 @@ def test_decode_steps_replay_in_a_hip_graph():
         for a, b in zip(ys, ye):
             assert torch.equal(a, b), "replay %d" % r
         assert torch.equal(mu_g, mu_e) and torch.equal(I_g, I_e)
+
+
+# ---------------------------------------------------------------------------
+# frozen-importance (Mamba2-limit) forward on the matrix cores
+# ---------------------------------------------------------------------------
+
+def _frozen_ref(inp, mu0=None, vstar=False):
+    import numpy as np
+    args = {n: inp[n] for n in ("q", "k", "v", "beta", "dt", "A", "I_prior")}
+    if vstar:
+        args["beta"] = np.ones(tuple(inp["v"].shape))
+    return oracle.fwd_mamba2_limit(**args, mu0=mu0)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("T", [200, 64, 1])
+def test_frozen_matches_mamba2_limit_oracle(dk, dv, T):
+    w = workloads.WORKLOADS[2].with_(B=2, H=3, dk=dk, dv=dv)
+    _announce("frozen fwd", T=T, dk=dk, dv=dv)
+    inp = workloads.make_inputs(w, T=T)
+    mu0, _ = workloads.random_state(2, 3, dv, dk, inp["I_prior"], seed=T + dk)
+    g = to_device(inp, DEV)
+    y, muT = _pm().fwd_frozen(*gpu_args(g), mu0=mu0.to(DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    y_ref, mu_ref = _frozen_ref(inp, mu0=mu0)
+    assert_close("frozen y", y, y_ref, 2e-2)
+    assert_close("frozen muT", muT, mu_ref, 2e-2)
+
+
+def test_frozen_vstar_input_and_bf16_output():
+    w = workloads.WORKLOADS[2].with_(B=1, H=4)
+    T = 300
+    _announce("frozen fwd v*", T=T)
+    inp = workloads.make_inputs(w, T=T)
+    g = to_device(inp, DEV)
+    y, muT = _pm().fwd_frozen(g["q"], g["k"], g["v"], None, g["dt"], g["A"], g["I_prior"])
+    torch.cuda.synchronize()
+    assert y.dtype == torch.bfloat16
+    y_ref, mu_ref = _frozen_ref(inp, vstar=True)
+    assert_close("frozen y (v*)", y, y_ref, 2e-2)
+    assert_close("frozen muT (v*)", muT, mu_ref, 2e-2)
+
+
+def test_frozen_layer760m_sampled():
+    w = workloads.WORKLOADS[2]
+    _announce("frozen fwd 760M layer", B=w.B, H=w.H, T=w.T)
+    inp = workloads.make_inputs(w)
+    g = to_device(inp, DEV)
+    y, muT = _pm().fwd_frozen(*gpu_args(g))
+    torch.cuda.synchronize()
+    heads = [(0, 0), (7, 11)]
+    sub = oracle.select_heads(inp, heads)
+    y_ref, mu_ref = _frozen_ref(sub)
+    bs = [b for b, _ in heads]
+    hs = [h for _, h in heads]
+    assert_close("frozen y (sampled)", to_np(y)[bs, :, hs, :].transpose(1, 0, 2)[None], y_ref, 2e-2)
+    assert_close("frozen muT (sampled)", to_np(muT)[bs, hs][None], mu_ref, 2e-2)
+
+
+def test_frozen_agrees_with_exact_path_when_importance_stays_at_prior():
+    """beta = 1e-6 with v* = beta . v fixed: the exact recurrence reaches the same readout."""
+    w = workloads.WORKLOADS[2].with_(B=1, H=4)
+    T = 256
+    _announce("frozen vs exact at tiny beta", T=T)
+    inp = workloads.make_inputs(w, T=T)
+    g = to_device(inp, DEV)
+    vstar = (g["beta"].float() * g["v"].float())
+    beta = torch.full_like(g["beta"], 1e-6)
+    v_big = (vstar / beta.float()).to(torch.bfloat16)
+    vstar_eff = (beta.float() * v_big.float()).to(torch.bfloat16)      # what the exact path writes
+    y_ex, _, _ = _pm().fwd_chunked(g["q"], g["k"], v_big, beta, g["dt"], g["A"], g["I_prior"],
+                                   out_dtype=torch.float32)
+    y_fz, _ = _pm().fwd_frozen(g["q"], g["k"], vstar_eff, None, g["dt"], g["A"], g["I_prior"],
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert rel_err(y_fz, y_ex) <= 2e-2
