@@ -646,6 +646,30 @@ struct FzLds {
 // (Indexing a register packet through a pointer would push it to scratch.)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ inline uint32_t u4get(const u32x4 &p, int i) { return p[i]; }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Value of x in lane `src` (wave-uniform source lane).
+__device__ inline float wave_read(float x, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
+}
+// x of the lane CTRL's row shift names, or 0 where that lane is outside the row.
+template <int CTRL>
+__device__ inline float dpp_or_zero(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active):
+// Hillis-Steele within each 16-lane row (row_shr 1, 2, 4, 8), then each row
+// adds the totals of the rows before it, read from lanes 15, 31, 47.
+__device__ inline float wave_incl_scan(float x, int lane) {
+    x += dpp_or_zero<0x111>(x);
+    x += dpp_or_zero<0x112>(x);
+    x += dpp_or_zero<0x114>(x);
+    x += dpp_or_zero<0x118>(x);
+    const float r0 = wave_read(x, 15), r1 = wave_read(x, 31), r2 = wave_read(x, 47);
+    const int row = lane >> 4;
+    const float before = row == 0 ? 0.f : row == 1 ? r0 : row == 2 ? r0 + r1 : (r0 + r1) + r2;
+    return x + before;
+}
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
@@ -688,44 +712,51 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
     //   u in [0, DK):        one 8x8 block of K (tokens 8 (u / (DK/8)).., columns
     //                        8 (u % (DK/8))..), written as K rows and, transposed in
     //                        registers, as K^T rows
-    //   u in [DK, DK+64):    8 tokens x DK/8 columns of Q
-    //   u in [DK+64, DK+128): one 8x8 block of W = beta . v / I_prior (tokens
-    //                        8 (x/8).., value rows 8 (x%8).., x = u - DK - 64),
-    //                        written transposed as W^T and (diag(d) W)^T; this
-    //                        wave (exactly one) also scans the gate
+    //   u in [DK, DK+128):   x = u - DK; two whole waves.  Each thread stages
+    //                        DK/16 packets of Q (consecutive threads cover a token
+    //                        row) and one 4-token x 8-row block of
+    //                        W = beta . v / I_prior (tokens 4 (x/8).., rows 8 (x%8)..),
+    //                        written transposed as W^T and (diag(d) W)^T; both waves
+    //                        scan the gate (one token per lane) and the first
+    //                        writes Lam
     //   u >= DK+128:         idle (d_k = 64)
     // Loads read a valid row (clamped to T-1); tokens past the end are zeroed
     // when written (q = k = w = 0, dt = 0: no effect on y or the state).
     const int u = tid - 256;
+    constexpr int kQPk = DK / 8;            // 16-byte packets per Q row
+    constexpr int kQTok = 128 / kQPk;       // Q rows covered by one packet index
     u32x4 pr[16];                 // 16-byte packets of this thread's role
     float pdt = 0.f;
+    // Token t of a [B, T, H, n] tensor starts at element (seq + t H) n.  Full
+    // chunks step a per-thread pointer by a uniform token stride; the last,
+    // partial chunk clamps each token to T-1 instead.
     auto load = [&](int t0) __attribute__((always_inline)) {
+        const bool full = t0 + kFzC <= a.T;
+        auto tok = [&](int t) { return seq + (size_t)(full ? t : min(t, a.T - 1)) * a.H; };
         if (u < DK) {
             const int tok0 = 8 * (u / (DK / 8)), col = 8 * (u % (DK / 8));
+            const bf16_t *p = a.k + tok(t0 + tok0) * DK + col;
+            const size_t st = (size_t)a.H * DK;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const size_t row = seq + (size_t)min(t0 + tok0 + e, a.T - 1) * a.H;
-                pr[e] = *(const u32x4 *)(a.k + row * DK + col);
-            }
-        } else if (u < DK + 64) {
-            const int tok0 = 8 * ((u - DK) / 8), col0 = (DK / 8) * ((u - DK) % 8);
-            // 8 tokens x DK/8 columns = DK/8 packets (<= 16)
-#pragma unroll
-            for (int e = 0; e < DK / 8; ++e) {
-                const int tt = e / (DK / 64), cc = col0 + 8 * (e % (DK / 64));
-                const size_t row = seq + (size_t)min(t0 + tok0 + tt, a.T - 1) * a.H;
-                pr[e] = *(const u32x4 *)(a.q + row * DK + cc);
-            }
+            for (int e = 0; e < 8; ++e)
+                pr[e] = *(const u32x4 *)(full ? p + e * st : a.k + tok(t0 + tok0 + e) * DK + col);
         } else if (u < DK + 128) {
-            const int x = u - DK - 64, tok0 = 8 * (x / 8), i0 = ib0 + 8 * (x % 8);
+            const int x = u - DK, tok0 = 4 * (x / 8), i0 = ib0 + 8 * (x % 8);
+            const size_t vo = tok(t0 + tok0) * a.dv + i0, vst = (size_t)a.H * a.dv;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const size_t row = seq + (size_t)min(t0 + tok0 + e, a.T - 1) * a.H;
-                pr[e] = *(const u32x4 *)(a.v + row * a.dv + i0);
-                pr[8 + e] = a.beta ? *(const u32x4 *)(a.beta + row * a.dv + i0)
+            for (int e = 0; e < 4; ++e) {
+                const size_t o = full ? vo + e * vst : tok(t0 + tok0 + e) * a.dv + i0;
+                pr[e] = *(const u32x4 *)(a.v + o);
+                pr[4 + e] = a.beta ? *(const u32x4 *)(a.beta + o)
                                    : u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0
             }
-            pdt = (float)a.dt[seq + (size_t)min(t0 + lane, a.T - 1) * a.H];
+            const int tq0 = x / kQPk, col = 8 * (x % kQPk);
+            const bf16_t *pq = a.q + tok(t0 + tq0) * DK + col;
+            const size_t qst = (size_t)kQTok * a.H * DK;
+#pragma unroll
+            for (int e = 0; e < DK / 16; ++e)
+                pr[8 + e] = *(const u32x4 *)(full ? pq + e * qst : a.q + tok(t0 + e * kQTok + tq0) * DK + col);
+            pdt = (float)a.dt[tok(t0 + lane)];
         }
     };
     // 8x8 transpose of bf16: out[c] holds element c of in[0..7]
@@ -738,6 +769,16 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
                                 __builtin_amdgcn_perm(u4get(in[3], wd), u4get(in[2], wd), sel),
                                 __builtin_amdgcn_perm(u4get(in[5], wd), u4get(in[4], wd), sel),
                                 __builtin_amdgcn_perm(u4get(in[7], wd), u4get(in[6], wd), sel)};
+        }
+    };
+    // 4x8 -> 8x4 transpose of bf16: out[c] (two dwords) holds element c of in[0..3]
+    auto transpose4x8 = [](const u32x4 (&in)[4], u32x2 (&out)[8]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int wd = c / 2;
+            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+            out[c] = u32x2{__builtin_amdgcn_perm(u4get(in[1], wd), u4get(in[0], wd), sel),
+                           __builtin_amdgcn_perm(u4get(in[3], wd), u4get(in[2], wd), sel)};
         }
     };
     auto commit = [&](char *buf, int t0) __attribute__((always_inline)) {
@@ -755,33 +796,27 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
             transpose8(kin, kt);
 #pragma unroll
             for (int c = 0; c < 8; ++c) *(u32x4 *)(hb + L::kKt + (col + c) * L::kTS + tok0) = kt[c];
-        } else if (u < DK + 64) {
-            const int tok0 = 8 * ((u - DK) / 8), col0 = (DK / 8) * ((u - DK) % 8);
-#pragma unroll
-            for (int e = 0; e < DK / 8; ++e) {
-                const int tt = e / (DK / 64), cc = col0 + 8 * (e % (DK / 64));
-                *(u32x4 *)(hb + L::kQ + (tok0 + tt) * L::kQS + cc) = (t0 + tok0 + tt < a.T) ? pr[e] : z;
-            }
         } else if (u < DK + 128) {
-            // gate: inclusive prefix sum of -A dt over the chunk, one token per lane
-            float x = (t0 + lane < a.T) ? -Ah * pdt : 0.f;
+            const int x = u - DK;
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const float y = __shfl_up(x, o, 64);
-                if (lane >= o) x += y;
+            for (int e = 0; e < DK / 16; ++e) {
+                const int tq = e * kQTok + x / kQPk, col = 8 * (x % kQPk);
+                *(u32x4 *)(hb + L::kQ + tq * L::kQS + col) = (t0 + tq < a.T) ? pr[8 + e] : z;
             }
-            const float dl = __expf(__shfl(x, 63, 64) - x);   // e^(Lam_end - Lam_s)
-            lam[lane] = x;
-            const int xb = u - DK - 64, tok0 = 8 * (xb / 8), il0 = 8 * (xb % 8);
-            u32x4 win[8], wdn[8], wt[8];
+            // gate: Lam = inclusive prefix sum of -A dt over the chunk, lane = token
+            const float lam_l = wave_incl_scan((t0 + lane < a.T) ? -Ah * pdt : 0.f, lane);
+            if (x < 64) lam[lane] = lam_l;
+            const float dl = __expf(wave_read(lam_l, 63) - lam_l);   // e^(Lam_end - Lam_s)
+            const int tok0 = 4 * (x / 8), il0 = 8 * (x % 8);
+            u32x4 win[4], wdn[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < 4; ++e) {
                 const float de = __shfl(dl, tok0 + e, 64);
                 const bool ok = t0 + tok0 + e < a.T;
                 uint32_t ww[4], wd[4];
 #pragma unroll
                 for (int pp = 0; pp < 4; ++pp) {
-                    const uint32_t vw = u4get(pr[e], pp), bw = u4get(pr[8 + e], pp);
+                    const uint32_t vw = u4get(pr[e], pp), bw = u4get(pr[4 + e], pp);
                     const float w0 = ok ? bf_lo(bw) * bf_lo(vw) * inv_ip : 0.f;
                     const float w1 = ok ? bf_hi(bw) * bf_hi(vw) * inv_ip : 0.f;
                     ww[pp] = pack_bf16(w0, w1);
@@ -790,12 +825,13 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
                 win[e] = u32x4{ww[0], ww[1], ww[2], ww[3]};
                 wdn[e] = u32x4{wd[0], wd[1], wd[2], wd[3]};
             }
-            transpose8(win, wt);
+            u32x2 wt[8];
+            transpose4x8(win, wt);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) *(u32x4 *)(hb + L::kWt + (il0 + c) * L::kTS + tok0) = wt[c];
-            transpose8(wdn, wt);
+            for (int c = 0; c < 8; ++c) *(u32x2 *)(hb + L::kWt + (il0 + c) * L::kTS + tok0) = wt[c];
+            transpose4x8(wdn, wt);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) *(u32x4 *)(hb + L::kWdt + (il0 + c) * L::kTS + tok0) = wt[c];
+            for (int c = 0; c < 8; ++c) *(u32x2 *)(hb + L::kWdt + (il0 + c) * L::kTS + tok0) = wt[c];
         }
     };
 
