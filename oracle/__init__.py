@@ -21,6 +21,8 @@ Contents
     The full-precision Gaussian update per value row (slides, backup frame
     "dropping precision correlations changes the mean", App. A.3-A.5), with
     an option that keeps only the diagonal of the precision at every token.
+``bwd``
+    The reverse-mode derivative of ``fwd`` (C oracle), for the training path.
 ``fwd_mamba2_limit``
     The frozen-importance recurrence of the Mamba2 limit (slides, frame "The
     Mamba2 limit enables a gradual model upgrade", Secs. 2.3-2.4).
@@ -74,6 +76,8 @@ def _lib():
             lib.oracle_fwd.restype = None
             lib.oracle_step.argtypes = [i, i, i, i] + [dp] * 10 + [i]
             lib.oracle_step.restype = None
+            lib.oracle_bwd.argtypes = [i, i, i, i, i] + [dp] * 21 + [i]
+            lib.oracle_bwd.restype = None
             lib.oracle_max_threads.argtypes = []
             lib.oracle_max_threads.restype = i
             _handle = lib
@@ -148,6 +152,50 @@ def step(q, k, v, beta, dt, A, I_prior, mu, I, nthreads: int = 0):
                        _ptr(dt), _ptr(A), _ptr(Ip), _ptr(mu), _ptr(I), _ptr(y),
                        int(nthreads))
     return y, mu, I
+
+
+def bwd(q, k, v, beta, dt, A, I_prior, gy, mu0=None, I0=None, gmuT=None, gIT=None,
+        nthreads: int = 0) -> dict:
+    """Reverse-mode derivative of ``fwd`` (C oracle) for the scalar
+    ``L = sum(gy * y) + sum(gmuT * muT) + sum(gIT * IT)``.
+
+    Returns a dict of float64 arrays: ``gq, gk [B,T,H,dk]``, ``gv, gbeta
+    [B,T,H,dv]``, ``gdt [B,T,H]``, ``gA, gIp [H]`` (summed over the batch),
+    ``gmu0, gI0 [B,H,dv,dk]``.  With ``mu0 = I0 = None`` the start state is
+    ``mu0 = 0, I0 = I_prior``; it then depends on ``I_prior``, so ``gIp``
+    also collects the sum of ``gI0`` over the head's entries.
+    """
+    q, k, v, beta, dt, gy = (_f64(x) for x in (q, k, v, beta, dt, gy))
+    A, Ip = _f64(A), _f64(I_prior)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != v.shape \
+            or dt.shape != (B, T, H) or gy.shape != v.shape or A.shape != (H,) or Ip.shape != (H,):
+        raise ValueError("inconsistent shapes")
+    default_state = mu0 is None
+    mu, I = _init_state(B, H, dv, dk, Ip, mu0, I0)
+    gmuT = None if gmuT is None else _f64(gmuT)
+    gIT = None if gIT is None else _f64(gIT)
+    for x in (gmuT, gIT):
+        if x is not None and x.shape != (B, H, dv, dk):
+            raise ValueError("final-state gradients must be [B, H, dv, dk]")
+    out = {"gq": np.zeros((B, T, H, dk)), "gk": np.zeros((B, T, H, dk)),
+           "gv": np.zeros((B, T, H, dv)), "gbeta": np.zeros((B, T, H, dv)),
+           "gdt": np.zeros((B, T, H)), "gmu0": np.zeros((B, H, dv, dk)),
+           "gI0": np.zeros((B, H, dv, dk))}
+    gA_bh, gIp_bh = np.zeros((B, H)), np.zeros((B, H))
+    null = ctypes.POINTER(ctypes.c_double)()
+    _lib().oracle_bwd(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(dt),
+                      _ptr(A), _ptr(Ip), _ptr(mu), _ptr(I), _ptr(gy),
+                      null if gmuT is None else _ptr(gmuT), null if gIT is None else _ptr(gIT),
+                      _ptr(out["gq"]), _ptr(out["gk"]), _ptr(out["gv"]), _ptr(out["gbeta"]),
+                      _ptr(out["gdt"]), _ptr(gA_bh), _ptr(gIp_bh), _ptr(out["gmu0"]),
+                      _ptr(out["gI0"]), int(nthreads))
+    out["gA"] = gA_bh.sum(axis=0)
+    out["gIp"] = gIp_bh.sum(axis=0)
+    if default_state:
+        out["gIp"] = out["gIp"] + out["gI0"].sum(axis=(0, 2, 3))
+    return out
 
 
 # ---------------------------------------------------------------------------
