@@ -51,6 +51,10 @@ def load_library() -> ctypes.CDLL:
             lib.palimpsa_fwd_frozen.restype = i
             lib.palimpsa_step.argtypes = [vp] * 5 + [fp] * 4 + [vp] + [i] * 6 + [vp]
             lib.palimpsa_step.restype = i
+            lib.palimpsa_bwd.argtypes = [vp] * 5 + [fp] * 4 + [vp, fp, fp] + [fp] * 9 + [i] * 7 + [vp, sz, vp]
+            lib.palimpsa_bwd.restype = i
+            lib.palimpsa_bwd_workspace_size.argtypes = [i] * 5
+            lib.palimpsa_bwd_workspace_size.restype = sz
             lib.palimpsa_status_string.argtypes = [i]
             lib.palimpsa_status_string.restype = ctypes.c_char_p
             lib.palimpsa_version.argtypes = []
@@ -240,3 +244,70 @@ def fwd_frozen(q, k, v, beta, dt, A, I_prior, mu0=None, out_dtype=None, y=None, 
     if st != OK:
         raise PalimpsaError(st, "palimpsa_fwd_frozen")
     return y, muT
+
+
+def bwd_workspace_size(B, T, H, dk, dv) -> int:
+    """Bytes of workspace ``palimpsa_bwd`` needs (checkpoints and partials)."""
+    return int(load_library().palimpsa_bwd_workspace_size(B, T, H, dk, dv))
+
+
+def bwd(q, k, v, beta, dt, A, I_prior, gy, mu0=None, I0=None, gmuT=None, gIT=None,
+        want_state_grads: bool = True, workspace=None, out=None):
+    """Backward of ``fwd_chunked`` for ``L = <gy, y> + <gmuT, muT> + <gIT, IT>``.
+
+    Takes the forward's inputs (the library recomputes the states) and returns
+    a dict of float32 gradients ``gq, gk, gv, gbeta, gdt, gA, gIp`` and, if
+    ``want_state_grads``, ``gmu0, gI0``.  ``gmuT``/``gIT`` may be None (zero).
+    ``out`` may supply preallocated output tensors by the same names;
+    ``workspace`` a contiguous uint8 device tensor of at least
+    ``bwd_workspace_size`` bytes (allocated here otherwise)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    in_dtype = q.dtype
+    if in_dtype not in _DTYPES or gy.dtype not in _DTYPES:
+        raise ValueError("unsupported dtype")
+    for t, name, shape in ((k, "k", (B, T, H, dk)), (v, "v", (B, T, H, dv)), (beta, "beta", (B, T, H, dv)),
+                           (dt, "dt", (B, T, H))):
+        _check(t, name, shape, in_dtype, dev)
+    _check(gy, "gy", (B, T, H, dv), gy.dtype, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(I_prior, "I_prior", (H,), torch.float32, dev)
+    if (mu0 is None) != (I0 is None):
+        raise ValueError("give both mu0 and I0, or neither")
+    for t, name in ((mu0, "mu0"), (I0, "I0"), (gmuT, "gmuT"), (gIT, "gIT")):
+        if t is not None:
+            _check(t, name, (B, H, dv, dk), torch.float32, dev)
+    shapes = {"gq": (B, T, H, dk), "gk": (B, T, H, dk), "gv": (B, T, H, dv), "gbeta": (B, T, H, dv),
+              "gdt": (B, T, H), "gA": (H,), "gIp": (H,)}
+    if want_state_grads:
+        shapes.update(gmu0=(B, H, dv, dk), gI0=(B, H, dv, dk))
+    res = {}
+    for name, shape in shapes.items():
+        t = (out or {}).get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=torch.float32, device=dev)
+        _check(t, name, shape, torch.float32, dev)
+        res[name] = t
+    lib = load_library()
+    nbytes = bwd_workspace_size(B, T, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
+    nz = lambda t: _ptr(t) if t is not None and t.numel() else None
+    with torch.cuda.device(dev):
+        st = lib.palimpsa_bwd(
+            nz(q), nz(k), nz(v), nz(beta), nz(dt), _ptr(A), _ptr(I_prior), _ptr(mu0), _ptr(I0),
+            nz(gy), _ptr(gmuT), _ptr(gIT),
+            nz(res["gq"]), nz(res["gk"]), nz(res["gv"]), nz(res["gbeta"]), nz(res["gdt"]),
+            _ptr(res["gA"]), _ptr(res["gIp"]), _ptr(res.get("gmu0")), _ptr(res.get("gI0")),
+            B, T, H, dk, dv, _DTYPES[in_dtype], _DTYPES[gy.dtype],
+            _ptr(workspace), workspace.numel(), _stream_handle(dev))
+    if st != OK:
+        raise PalimpsaError(st, "palimpsa_bwd")
+    return res

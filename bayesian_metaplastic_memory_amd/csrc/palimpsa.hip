@@ -130,6 +130,8 @@ struct FwdArgs {
     int seg_len;       // tokens per time segment (a multiple of the chunk)
     int nseg;          // time segments (1: no split)
     float *ws;         // segment summaries, see SegWs
+    float *ck;         // backward checkpoints (kCheckpoint mode), see bwd_kernel
+    int nsb;           // checkpoints per sequence: ceil(T / kSB)
 };
 
 // Workspace of a time-split forward: for each of the first nseg-1 segments,
@@ -152,6 +154,7 @@ constexpr int kRowsPerWave = 4;
 constexpr int kRowsPerWG = kRowsPerWave * kWaves;   // 16 value rows per workgroup
 constexpr int kLanesPerRow = 16;
 constexpr int kGroup = 16;                // tokens per transposing reduction (= lanes per row)
+constexpr int kSB = 8;                    // tokens between backward checkpoints
 
 // LDS floats per staged token: k, k^2, q columns + (beta, beta*v) per row + gate.
 template <int DK> struct Stage {
@@ -428,7 +431,74 @@ __device__ inline void summary_chunk(const float *buf, float *M, float *Ib, floa
     }
 }
 
-enum FwdMode { kReplay = 0, kSummary = 1 };
+// A lane's checkpoint: dst[0, N) = M, dst[N, 2N) = I, as 128-bit accesses
+// (N = DK / 16 in {2, 4, 8}; dst is 16-byte aligned).
+template <int N>
+__device__ inline void store_pair(float *dst, const float *M, const float *I) {
+    float v[2 * N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) { v[i] = M[i]; v[N + i] = I[i]; }
+#pragma unroll
+    for (int i = 0; i < 2 * N; i += 4) *(float4 *)(dst + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+}
+template <int N>
+__device__ inline void load_pair(const float *src, float *M, float *I) {
+    float v[2 * N];
+#pragma unroll
+    for (int i = 0; i < 2 * N; i += 4) {
+        const float4 x = *(const float4 *)(src + i);
+        v[i] = x.x; v[i + 1] = x.y; v[i + 2] = x.z; v[i + 3] = x.w;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) { M[i] = v[i]; I[i] = v[N + i]; }
+}
+
+// Checkpoint pass of the backward over one staged chunk: the forward update
+// without readout (the same 4 VALU ops per entry and token as the replay,
+// so the states are bit-identical to the forward's), storing (M, I) before
+// every kSB-th token of the sequence.  The lane's 2 DK/16 floats of a
+// checkpoint are contiguous: ckp + s * ck_stride for the checkpoint before
+// token kSB s.
+template <int DK, int C>
+__device__ inline void ckpt_chunk(const float *buf, float *M, float *I, int row_local, int g,
+                                  float *ckp, size_t ck_stride, int t0, int ntok) {
+    using LT = LaneTile<DK>;
+    static_assert(C % kSB == 0, "chunk must hold whole checkpoint intervals");
+    const float *cbase = buf + LT::col(g, 0, 0);
+    const float *rbase = buf + C * Stage<DK>::kColFloats + 2 * row_local;
+    int goff = C * (Stage<DK>::kColFloats + Stage<DK>::kRowFloats);
+    asm volatile("" : "+v"(goff));
+    const float *gbase = buf + goff;
+#pragma unroll 1
+    for (int sb = 0; sb < C / kSB; ++sb) {
+        if (t0 + sb * kSB < ntok) {
+            store_pair<LT::kCols>(ckp + (size_t)((t0 / kSB) + sb) * ck_stride, M, I);
+        }
+#pragma unroll
+        for (int u0 = 0; u0 < kSB; ++u0) {
+            const int u = sb * kSB + u0;
+            const float2 gc = *(const float2 *)(gbase + 2 * u);
+            const float2 rb = *(const float2 *)(rbase + u * Stage<DK>::kRowFloats);
+            const float *ct = cbase + u * Stage<DK>::kColFloats;
+#pragma unroll
+            for (int m = 0; m < LT::kNVec; ++m) {
+                float kk[LT::kVec], k2[LT::kVec];
+                const int c0 = kLanesPerRow * LT::kVec * m;
+                vecf<LT::kVec>::ld(ct + c0, kk);
+                vecf<LT::kVec>::ld(ct + DK + c0, k2);
+#pragma unroll
+                for (int e = 0; e < LT::kVec; ++e) {
+                    const int s = m * LT::kVec + e;
+                    const float w = fmaf(rb.x, k2[e], gc.y);
+                    I[s] = fmaf(gc.x, I[s], w);
+                    M[s] = fmaf(gc.x, M[s], rb.y * kk[e]);
+                }
+            }
+        }
+    }
+}
+
+enum FwdMode { kReplay = 0, kSummary = 1, kCheckpoint = 2 };
 
 // One launch of the chunked forward.
 //
@@ -437,6 +507,9 @@ enum FwdMode { kReplay = 0, kSummary = 1 };
 // summaries of segments 0..s-1 (M = P M + M_loc, Ibar = P Ibar + Ibar_loc, the
 // composition of the affine scans).  The last segment writes (muT, IT).
 // Without a split (nseg = 1) this is the whole sequence in one pass.
+//
+// kCheckpoint (the backward's first pass; nseg = 1): the sequence from
+// (mu0, I0) without readout, storing (M, I) before every kSB-th token.
 //
 // kSummary: segment s < nseg-1 runs from a zero state without readout and
 // writes its (M_loc, Ibar_loc, P) to the workspace.
@@ -532,6 +605,12 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
     const int ntok = t_end - t_begin;
     const int nchunks = (ntok + C - 1) / C;
     float P = 1.f;
+    // checkpoints: [B*H][nsb][row block][thread][2 DK/16] floats
+    const size_t ck_stride = (size_t)rb_per_head * kThreads * 2 * LT::kCols;
+    float *ckp = MODE == kCheckpoint
+                     ? a.ck + ((size_t)bh * a.nsb * rb_per_head + row0 / kRowsPerWG) * (kThreads * 2 * LT::kCols) +
+                           tid * 2 * LT::kCols
+                     : nullptr;
     Stager<DK, C, TIn, MODE == kReplay> st;
     if (nchunks > 0) {
         st.load(kseq, qseq, vseq, bseq, dseq, ntok, a.H, a.dv, tid);
@@ -549,12 +628,15 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
         const float *cur = (c & 1) ? buf1 : buf0;
         if (MODE == kReplay)
             compute_chunk<DK, C, TOut>(cur, ntok - t0, M, I, row_local, g, ybase + (size_t)t0 * ystride, ystride);
-        else
+        else if (MODE == kSummary)
             summary_chunk<DK, C>(cur, M, I, P, row_local, g);
+        else
+            ckpt_chunk<DK, C>(cur, M, I, row_local, g, ckp, ck_stride, t0, ntok);
         if (more) st.commit((c & 1) ? buf0 : buf1, A, Ip, tid);
         __syncthreads();
     }
 
+    if (MODE == kCheckpoint) return;
     if (MODE == kSummary) {
         const SegWs w(a.ws, a.nseg, (size_t)a.B * a.H, a.dv, DK);
 #pragma unroll
@@ -584,6 +666,552 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
             vecf<LT::kVec>::st(a.IT + srow + LT::col(g, m, 0), ii);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// backward (training): reverse mode of the chunked forward
+// ---------------------------------------------------------------------------
+//
+// The pages train through the recurrence but print no backward; this is the
+// adjoint of the natural-parameter scans (slides, frame "Natural parameters
+// expose two affine scans", App. A.12) per state entry (i, j):
+//     M_t = a_t M_{t-1} + bv_i k_j,   I_t = a_t I_{t-1} + c_t + b_i k_j^2,
+//     y_t[i] = sum_j (M_t / I_t) q_j,   a = e^{-A dt},  c = (1 - a) I_prior.
+// With GM, GI the adjoints of (M_t, I_t), r = 1 / I_t and mu = M_t r, walking
+// t from T-1 down to 0:
+//     GM += gy_i q_j r,         GI -= gy_i q_j r mu           (readout)
+//     gq_j += gy_i mu,          gk_j += GM bv_i + 2 GI b_i k_j
+//     gbv_i += GM k_j,          gb_i += GI k_j^2
+//     da_t += GM M_{t-1} + GI I_{t-1},     dc_t += GI
+//     GM *= a_t,  GI *= a_t                                    (to t-1)
+// and then gv = gbv b, gbeta = gbv v + gb, gdt = A a (I_prior dc - da),
+// gA = sum dt a (I_prior dc - da), gI_prior = sum (1 - a) dc.  The adjoint
+// of the final state (mu_T = M_T / I_T, I_T) starts the walk:
+// GM = gmuT / I_T, GI = gIT - GM mu_T; at the start M_0 = I_0 mu_0 gives
+// gmu0 = GM I_0 and gI0 = GI + GM mu_0.
+//
+// Passes (one stream):
+//  1. checkpoint: the forward kernel in kCheckpoint mode stores (M, I)
+//     before every 8th token (4 VALU ops per entry and token, no readout).
+//  2. bwd_kernel: one workgroup per (head, 16 value rows), the forward's
+//     lane layout.  Sub-blocks of 8 tokens are taken newest first; each half
+//     of 4 tokens is replayed from the checkpoint into registers and walked
+//     in reverse.  Row sums (gbv, gb, da, dc) use the forward's transposing
+//     DPP reduction; column sums (gq, gk) are reduce-scattered across the
+//     4 rows of a wave, summed over the 4 waves in LDS and written as this
+//     row block's partial.
+//  3. bwd_qk_kernel sums the row-block partials into gq, gk;
+//     bwd_gate_kernel forms gdt and per-sequence sums of the gate gradients;
+//     bwd_head_kernel sums those over the batch into gA, gI_prior.
+
+template <int DK> struct BwdStage {
+    static constexpr int kColFloats = 3 * DK;                 // k, k^2, q
+    static constexpr int kRowFloats = 4 * kRowsPerWG;         // (beta, beta v, v, gy) per row
+    static constexpr int kRows = kSB * kColFloats;
+    static constexpr int kGate = kRows + kSB * kRowFloats;    // (alpha, c) per token
+    static constexpr int kFloats = kGate + 2 * kSB;
+    static constexpr int kRed = 2 * kFloats;                  // gq | gk per token and wave
+    static constexpr int kRs = kRed + kSB * kWaves * 2 * DK;   // row sums [token][4][16 rows]
+    static constexpr int kTotal = kRs + kSB * 4 * kRowsPerWG;
+};
+
+struct BwdArgs {
+    const void *q, *k, *v, *beta, *dt, *gy;
+    const float *A, *Ip, *mu0, *I0, *gmuT, *gIT;
+    float *gv, *gbeta, *gmu0, *gI0;
+    const float *ck;
+    float *pqk;        // [row block][B*T*H][2 DK]: gq | gk partials
+    float *ps;         // [row block][B*T*H][2]: (da, dc) partials
+    float *pI0;        // [B*H][row block]: sum of gI0 (default start state)
+    int B, T, H, dv, nsb, nwg, xcd_remap;
+};
+
+// Staging of one sub-block of kSB tokens (newest-first order of use; the
+// layout is that of the forward with q always present and per-row gy, v).
+template <int DK, typename TIn, typename TG>
+struct BwdStager {
+    static constexpr int kPer = packet<TIn>::kN;
+    static constexpr int kColPkts = DK / kPer;
+    static constexpr int kHalf = kSB * kColPkts;              // k packets (= q packets)
+    static constexpr int kKQPer = (2 * kHalf + kThreads - 1) / kThreads;
+    static constexpr int kRowPkts = kRowsPerWG / kPer;
+    static constexpr int kVB = kSB * kRowPkts;
+    static constexpr int kPerG = packet<TG>::kN;
+    static constexpr int kRowPktsG = kRowsPerWG / kPerG;
+    static constexpr int kGY = kSB * kRowPktsG;
+    static_assert(kVB <= kThreads && kGY <= kThreads, "one packet per thread");
+
+    uint4 kq[kKQPer];
+    uint4 vv, bb, gg;
+    float dtv;
+
+    __device__ static inline int vb_slot(int tid) { return (tid + kThreads - 64) % kThreads; }
+    __device__ static inline int gy_slot(int tid) { return (tid + kThreads - 128) % kThreads; }
+    __device__ static inline int dt_slot(int tid) { return (tid + kThreads - 192) % kThreads; }
+
+    // Bases point at token t0 of this (b, h) (v, beta, gy at the workgroup's
+    // first row); `left` = T - t0.  Token tt is at offset tt H d.
+    __device__ inline void load(const TIn *kb, const TIn *qb, const TIn *vb, const TIn *bb_, const TG *gb,
+                                const TIn *db, int left, int H, int dv, int tid) {
+#pragma unroll
+        for (int u = 0; u < kKQPer; ++u) {
+            const int p = tid + u * kThreads;
+            if ((2 * kHalf) % kThreads == 0 || p < 2 * kHalf) {
+                const bool isq = p >= kHalf;
+                const int pp = isq ? p - kHalf : p;
+                const int tt = pp / kColPkts;
+                const uint32_t off = (uint32_t)tt * (uint32_t)(H * DK) + (pp % kColPkts) * kPer;
+                kq[u] = make_uint4(0, 0, 0, 0);
+                if (tt < left) kq[u] = *(const uint4 *)((isq ? qb : kb) + off);
+            }
+        }
+        const int pv = vb_slot(tid);
+        if (pv < kVB) {
+            const int tt = pv / kRowPkts;
+            const uint32_t off = (uint32_t)tt * (uint32_t)(H * dv) + (pv % kRowPkts) * kPer;
+            vv = make_uint4(0, 0, 0, 0);
+            bb = make_uint4(0, 0, 0, 0);
+            if (tt < left) {
+                vv = *(const uint4 *)(vb + off);
+                bb = *(const uint4 *)(bb_ + off);
+            }
+        }
+        const int pg = gy_slot(tid);
+        if (pg < kGY) {
+            const int tt = pg / kRowPktsG;
+            const uint32_t off = (uint32_t)tt * (uint32_t)(H * dv) + (pg % kRowPktsG) * kPerG;
+            gg = make_uint4(0, 0, 0, 0);
+            if (tt < left) gg = *(const uint4 *)(gb + off);
+        }
+        const int pd = dt_slot(tid);
+        if (pd < kSB) {
+            dtv = 0.f;
+            if (pd < left) dtv = io<TIn>::to_f32(db[(uint32_t)pd * (uint32_t)H]);
+        }
+    }
+
+    __device__ inline void commit(float *buf, float A, float Ip, int tid) const {
+        using S = BwdStage<DK>;
+        float *rows = buf + S::kRows;
+#pragma unroll
+        for (int u = 0; u < kKQPer; ++u) {
+            const int p = tid + u * kThreads;
+            if ((2 * kHalf) % kThreads == 0 || p < 2 * kHalf) {
+                const bool isq = p >= kHalf;
+                const int pp = isq ? p - kHalf : p;
+                const int tt = pp / kColPkts;
+                const int off = (pp % kColPkts) * kPer;
+                float x[kPer];
+                packet<TIn>::widen(kq[u], x);
+                float *dst = buf + tt * S::kColFloats + off;
+#pragma unroll
+                for (int e = 0; e < kPer; e += 4) {
+                    if (!isq) {
+                        *(float4 *)(dst + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+                        *(float4 *)(dst + DK + e) = make_float4(x[e] * x[e], x[e + 1] * x[e + 1],
+                                                                x[e + 2] * x[e + 2], x[e + 3] * x[e + 3]);
+                    } else {
+                        *(float4 *)(dst + 2 * DK + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+                    }
+                }
+            }
+        }
+        const int pv = vb_slot(tid);
+        if (pv < kVB) {
+            const int tt = pv / kRowPkts;
+            const int r0 = (pv % kRowPkts) * kPer;
+            float xv[kPer], xb[kPer];
+            packet<TIn>::widen(vv, xv);
+            packet<TIn>::widen(bb, xb);
+            float *dst = rows + tt * S::kRowFloats + 4 * r0;
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) {
+                *(float2 *)(dst + 4 * e) = make_float2(xb[e], xb[e] * xv[e]);
+                dst[4 * e + 2] = xv[e];
+            }
+        }
+        const int pg = gy_slot(tid);
+        if (pg < kGY) {
+            const int tt = pg / kRowPktsG;
+            const int r0 = (pg % kRowPktsG) * kPerG;
+            float xg[kPerG];
+            packet<TG>::widen(gg, xg);
+            float *dst = rows + tt * S::kRowFloats + 4 * r0 + 3;
+#pragma unroll
+            for (int e = 0; e < kPerG; ++e) dst[4 * e] = xg[e];
+        }
+        const int pd = dt_slot(tid);
+        if (pd < kSB) {
+            const float2 gc = gate(A, dtv, Ip);
+            *(float2 *)(buf + S::kGate + 2 * pd) = gc;
+        }
+    }
+};
+
+// One token of the replay: the forward update of the lane's entries (the
+// same operations as compute_chunk, so the states are bit-identical).
+template <int DK>
+__device__ inline void bwd_replay_token(const float *buf, int e, float *M, float *I, int row_local, int g) {
+    using LT = LaneTile<DK>;
+    using S = BwdStage<DK>;
+    const float2 gc = *(const float2 *)(buf + S::kGate + 2 * e);
+    const float2 rb = *(const float2 *)(buf + S::kRows + e * S::kRowFloats + 4 * row_local);
+    const float *ct = buf + e * S::kColFloats + LT::col(g, 0, 0);
+#pragma unroll
+    for (int m = 0; m < LT::kNVec; ++m) {
+        float kk[LT::kVec], k2[LT::kVec];
+        const int c0 = kLanesPerRow * LT::kVec * m;
+        vecf<LT::kVec>::ld(ct + c0, kk);
+        vecf<LT::kVec>::ld(ct + DK + c0, k2);
+#pragma unroll
+        for (int x = 0; x < LT::kVec; ++x) {
+            const int s = m * LT::kVec + x;
+            const float w = fmaf(rb.x, k2[x], gc.y);
+            I[s] = fmaf(gc.x, I[s], w);
+            M[s] = fmaf(gc.x, M[s], rb.y * kk[x]);
+        }
+    }
+}
+
+// One token of the reverse walk for the lane's entries: (Mt, It) the state
+// after the token, (Mp, Ipv) before it.  Updates the adjoints, returns the
+// lane's row partials of (gbv, gb, da, dc), and writes the wave's column sums
+// of (gq, gk) for the token to red (2 DK floats), reduce-scattered over the
+// wave's 4 rows: after exchanges with lanes l^32 and l^16, lane (rg, g) holds
+// DK/32 consecutive columns of gq (rg < 2) or gk (rg >= 2).
+template <int DK>
+__device__ inline void bwd_reverse_token(const float *buf, int e, const float *Mt, const float *It,
+                                         const float *Mp, const float *Ipv, float *GM, float *GI,
+                                         int row_local, int g, int lane, float *red,
+                                         float &cbv, float &cb, float &s1, float &s2) {
+    using LT = LaneTile<DK>;
+    using S = BwdStage<DK>;
+    constexpr int KC = LT::kCols;
+    const float alpha = buf[S::kGate + 2 * e];
+    const float4 rw = *(const float4 *)(buf + S::kRows + e * S::kRowFloats + 4 * row_local);
+    const float b2 = 2.f * rw.x, bv = rw.y, gy = rw.w;
+    const float *ct = buf + e * S::kColFloats + LT::col(g, 0, 0);
+    float dq[KC], dk[KC];
+    cbv = 0.f; cb = 0.f; s1 = 0.f; s2 = 0.f;
+#pragma unroll
+    for (int m = 0; m < LT::kNVec; ++m) {
+        float kk[LT::kVec], k2[LT::kVec], qq[LT::kVec];
+        const int c0 = kLanesPerRow * LT::kVec * m;
+        vecf<LT::kVec>::ld(ct + c0, kk);
+        vecf<LT::kVec>::ld(ct + DK + c0, k2);
+        vecf<LT::kVec>::ld(ct + 2 * DK + c0, qq);
+#pragma unroll
+        for (int x = 0; x < LT::kVec; ++x) {
+            const int s = m * LT::kVec + x;
+            const float r = __builtin_amdgcn_rcpf(It[s]);
+            const float mu = Mt[s] * r;
+            const float gr = gy * qq[x] * r;
+            GM[s] += gr;
+            GI[s] = fmaf(-gr, mu, GI[s]);
+            dq[s] = gy * mu;
+            dk[s] = fmaf(GM[s], bv, GI[s] * (b2 * kk[x]));
+            cbv = fmaf(GM[s], kk[x], cbv);
+            cb = fmaf(GI[s], k2[x], cb);
+            s1 = fmaf(GM[s], Mp[s], s1);
+            s1 = fmaf(GI[s], Ipv[s], s1);
+            s2 += GI[s];
+            GM[s] *= alpha;
+            GI[s] *= alpha;
+        }
+    }
+    // reduce-scatter of (gq, gk) over the wave's 4 rows
+    const bool up32 = lane & 32, up16 = lane & 16;
+    float h8[KC];
+#pragma unroll
+    for (int s = 0; s < KC; ++s)
+        h8[s] = (up32 ? dk[s] : dq[s]) + __shfl_xor(up32 ? dq[s] : dk[s], 32, 64);
+    constexpr int KH = KC / 2;
+    float h4[KH];
+#pragma unroll
+    for (int s = 0; s < KH; ++s)
+        h4[s] = (up16 ? h8[KH + s] : h8[s]) + __shfl_xor(up16 ? h8[s] : h8[KH + s], 16, 64);
+    const int s0 = up16 ? KH : 0;
+    float *dst = red + (up32 ? DK : 0) + LT::col(g, s0 / LT::kVec, s0 % LT::kVec);
+    if (KH == 4) *(float4 *)dst = make_float4(h4[0], h4[KH > 1 ? 1 : 0], h4[KH > 2 ? 2 : 0], h4[KH > 3 ? 3 : 0]);
+    else if (KH == 2) *(float2 *)dst = make_float2(h4[0], h4[KH > 1 ? 1 : 0]);
+    else dst[0] = h4[0];
+}
+
+// Row sums of one half-block: acc holds the lane's partials of (gbv, gb, da,
+// dc) for 4 tokens, quantity-major.  After the transposing reduction lane g
+// holds quantity g / 4 of token g % 4 summed over its row; it is written to
+// dst[(token * 4 + quantity) * 16] (dst at this half's first token and the
+// lane's row).
+__device__ inline void bwd_row_sums(const float (&acc)[16], int g, float *dst) {
+    const float r = row16_transpose_sum(acc, g);
+    dst[((g % 4) * 4 + g / 4) * kRowsPerWG] = r;
+}
+
+template <int DK, typename TIn, typename TG>
+__global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
+    using LT = LaneTile<DK>;
+    using S = BwdStage<DK>;
+    constexpr int KC = LT::kCols;
+    extern __shared__ float lds[];
+    float *red = lds + S::kRed;
+    float *rs = lds + S::kRs;
+
+    const int rb_per_head = a.dv / kRowsPerWG;
+    int wg = blockIdx.x;
+    if (a.xcd_remap) {
+        const int per_xcd = a.nwg / 8;
+        wg = (wg % 8) * per_xcd + wg / 8;
+    }
+    const int bh = wg / rb_per_head;
+    const int rb = wg % rb_per_head;
+    const int row0 = rb * kRowsPerWG;
+    const int b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane & (kLanesPerRow - 1);
+    const int rg = lane >> 4;
+    const int row_local = wave * kRowsPerWave + rg;
+    const int row = row0 + row_local;
+    const float A = a.A[h], Ip = a.Ip[h];
+    const size_t srow = ((size_t)bh * a.dv + row) * DK;
+
+    float GM[KC], GI[KC];
+    const size_t seq0 = (size_t)b * a.T * a.H + h;           // row of (b, 0, h) in [B, T, H]
+    const size_t bth = (size_t)a.B * a.T * a.H;
+    const size_t kq_tok = (size_t)a.H * DK, vb_tok = (size_t)a.H * a.dv;
+
+    if (a.nsb == 0) {
+        // T = 0: the final state is the initial state, copied through exactly
+#pragma unroll
+        for (int m = 0; m < LT::kNVec; ++m)
+#pragma unroll
+            for (int x = 0; x < LT::kVec; ++x) {
+                const int s = m * LT::kVec + x;
+                const size_t o = srow + LT::col(g, m, x);
+                const float gmu = a.gmuT ? a.gmuT[o] : 0.f, gI = a.gIT ? a.gIT[o] : 0.f;
+                if (a.gmu0) a.gmu0[o] = gmu;
+                if (a.gI0) a.gI0[o] = gI;
+                GI[s] = gI;
+            }
+    } else {
+        const size_t ck_stride = (size_t)rb_per_head * kThreads * 2 * KC;
+        const float *ckb = a.ck + ((size_t)bh * a.nsb * rb_per_head + rb) * (kThreads * 2 * KC) + tid * 2 * KC;
+        const TIn *kseq = (const TIn *)a.k + seq0 * DK;
+        const TIn *qseq = (const TIn *)a.q + seq0 * DK;
+        const TIn *vseq = (const TIn *)a.v + seq0 * a.dv + row0;
+        const TIn *bseq = (const TIn *)a.beta + seq0 * a.dv + row0;
+        const TG *gseq = (const TG *)a.gy + seq0 * a.dv + row0;
+        const TIn *dseq = (const TIn *)a.dt + seq0;
+        BwdStager<DK, TIn, TG> st;
+        {
+            const size_t tn = (size_t)(a.nsb - 1) * kSB;
+            st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
+                    gseq + tn * vb_tok, dseq + tn * a.H, a.T - (int)tn, a.H, a.dv, tid);
+            st.commit(lds + ((a.nsb - 1) & 1) * S::kFloats, A, Ip, tid);
+        }
+        float ckM[KC], ckI[KC];
+        load_pair<KC>(ckb + (size_t)(a.nsb - 1) * ck_stride, ckM, ckI);
+        __syncthreads();
+
+        for (int sb = a.nsb - 1; sb >= 0; --sb) {
+            const float *cur = lds + (sb & 1) * S::kFloats;
+            const int t0 = sb * kSB;
+            if (sb > 0) {
+                const size_t tn = (size_t)(t0 - kSB);
+                st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
+                        gseq + tn * vb_tok, dseq + tn * a.H, a.T - (int)tn, a.H, a.dv, tid);
+            }
+            float xM[4][KC], xI[4][KC];
+            float acc[16];      // this half's row partials: gbv, gb, da, dc of its 4 tokens
+            // upper half: tokens 4..7, replayed from the checkpoint
+            float mM[KC], mI[KC];
+#pragma unroll
+            for (int s = 0; s < KC; ++s) { mM[s] = ckM[s]; mI[s] = ckI[s]; }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bwd_replay_token<DK>(cur, e, mM, mI, row_local, g);
+#pragma unroll
+            for (int e = 4; e < 8; ++e) {
+                const float *pm = e == 4 ? mM : xM[e > 4 ? e - 5 : 0];
+                const float *pi = e == 4 ? mI : xI[e > 4 ? e - 5 : 0];
+#pragma unroll
+                for (int s = 0; s < KC; ++s) { xM[e - 4][s] = pm[s]; xI[e - 4][s] = pi[s]; }
+                bwd_replay_token<DK>(cur, e, xM[e - 4], xI[e - 4], row_local, g);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (sb == a.nsb - 1) {
+                // adjoint of the final state (tokens past T are neutral: xM[3] is the state after T-1)
+#pragma unroll
+                for (int m = 0; m < LT::kNVec; ++m)
+#pragma unroll
+                    for (int x = 0; x < LT::kVec; ++x) {
+                        const int s = m * LT::kVec + x;
+                        const size_t o = srow + LT::col(g, m, x);
+                        const float gmu = a.gmuT ? a.gmuT[o] : 0.f, gI = a.gIT ? a.gIT[o] : 0.f;
+                        const float muT = xM[3][s] / xI[3][s];
+                        GM[s] = gmu / xI[3][s];
+                        GI[s] = gI - GM[s] * muT;
+                    }
+            }
+#pragma unroll
+            for (int e = 7; e >= 4; --e)
+                bwd_reverse_token<DK>(cur, e, xM[e - 4], xI[e - 4], e == 4 ? mM : xM[e > 4 ? e - 5 : 0],
+                                      e == 4 ? mI : xI[e > 4 ? e - 5 : 0],
+                                      GM, GI, row_local, g, lane, red + (e * kWaves + wave) * 2 * DK,
+                                      acc[e - 4], acc[e], acc[e + 4], acc[e + 8]);
+                __builtin_amdgcn_sched_barrier(0);
+            bwd_row_sums(acc, g, rs + 4 * 4 * kRowsPerWG + row_local);
+            // lower half: tokens 0..3
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float *pm = e == 0 ? ckM : xM[e > 0 ? e - 1 : 0];
+                const float *pi = e == 0 ? ckI : xI[e > 0 ? e - 1 : 0];
+#pragma unroll
+                for (int s = 0; s < KC; ++s) { xM[e][s] = pm[s]; xI[e][s] = pi[s]; }
+                bwd_replay_token<DK>(cur, e, xM[e], xI[e], row_local, g);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            float nM[KC], nI[KC];
+            if (sb > 0) load_pair<KC>(ckb + (size_t)(sb - 1) * ck_stride, nM, nI);
+#pragma unroll
+            for (int e = 3; e >= 0; --e)
+                bwd_reverse_token<DK>(cur, e, xM[e], xI[e], e == 0 ? ckM : xM[e > 0 ? e - 1 : 0],
+                                      e == 0 ? ckI : xI[e > 0 ? e - 1 : 0],
+                                      GM, GI, row_local, g, lane, red + (e * kWaves + wave) * 2 * DK,
+                                      acc[e], acc[e + 4], acc[e + 8], acc[e + 12]);
+                __builtin_amdgcn_sched_barrier(0);
+            bwd_row_sums(acc, g, rs + row_local);
+            if (sb > 0) st.commit(lds + ((sb - 1) & 1) * S::kFloats, A, Ip, tid);
+            __syncthreads();
+            // sums over the 4 waves: this row block's partials of (gq, gk) and (da, dc)
+            for (int n = tid; n < kSB * 2 * DK; n += kThreads) {
+                const int e = n / (2 * DK), c = n % (2 * DK);
+                const float v = (red[(e * kWaves + 0) * 2 * DK + c] + red[(e * kWaves + 1) * 2 * DK + c]) +
+                                (red[(e * kWaves + 2) * 2 * DK + c] + red[(e * kWaves + 3) * 2 * DK + c]);
+                if (t0 + e < a.T)
+                    a.pqk[((size_t)rb * bth + seq0 + (size_t)(t0 + e) * a.H) * 2 * DK + c] = v;
+            }
+            // per (token, row): gv = gbv beta, gbeta = gbv v + gb; per token: the
+            // row block's sums of (da, dc)
+            if (tid < kSB * kRowsPerWG) {
+                const int e = tid / kRowsPerWG, r = tid % kRowsPerWG;
+                const float gbv = rs[(e * 4 + 0) * kRowsPerWG + r], gb = rs[(e * 4 + 1) * kRowsPerWG + r];
+                const float4 rw = *(const float4 *)(cur + S::kRows + e * S::kRowFloats + 4 * r);
+                if (t0 + e < a.T) {
+                    const size_t o = (seq0 + (size_t)(t0 + e) * a.H) * a.dv + row0 + r;
+                    a.gv[o] = gbv * rw.x;
+                    a.gbeta[o] = fmaf(gbv, rw.z, gb);
+                }
+            } else if (tid < kSB * kRowsPerWG + 2 * kSB) {
+                const int u = tid - kSB * kRowsPerWG, e = u % kSB, qd = u / kSB;
+                const float *src = rs + (e * 4 + 2 + qd) * kRowsPerWG;
+                float v = 0.f;
+#pragma unroll
+                for (int r = 0; r < kRowsPerWG; ++r) v += src[r];
+                if (t0 + e < a.T) a.ps[((size_t)rb * bth + seq0 + (size_t)(t0 + e) * a.H) * 2 + qd] = v;
+            }
+            __syncthreads();
+            if (sb > 0) {
+#pragma unroll
+                for (int s = 0; s < KC; ++s) { ckM[s] = nM[s]; ckI[s] = nI[s]; }
+            }
+        }
+        // gradients of the start state: M_0 = I_0 mu_0
+        float gi_sum = 0.f;
+#pragma unroll
+        for (int m = 0; m < LT::kNVec; ++m)
+#pragma unroll
+            for (int x = 0; x < LT::kVec; ++x) {
+                const int s = m * LT::kVec + x;
+                const size_t o = srow + LT::col(g, m, x);
+                const float i0 = a.mu0 ? a.I0[o] : Ip, m0 = a.mu0 ? a.mu0[o] : 0.f;
+                const float gI0 = fmaf(GM[s], m0, GI[s]);
+                if (a.gmu0) a.gmu0[o] = GM[s] * i0;
+                if (a.gI0) a.gI0[o] = gI0;
+                GI[s] = gI0;
+            }
+    }
+    // this row block's sum of gI0 (the default start state I0 = I_prior feeds gI_prior)
+    float gs = 0.f;
+#pragma unroll
+    for (int s = 0; s < KC; ++s) gs += GI[s];
+    gs = row16_sum(gs);
+    gs += __shfl_xor(gs, 16, 64);
+    gs += __shfl_xor(gs, 32, 64);
+    __syncthreads();
+    if (lane == 0) rs[wave] = gs;
+    __syncthreads();
+    if (tid == 0) a.pI0[(size_t)bh * rb_per_head + rb] = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+}
+
+// gq, gk: sums of the row-block partials (4 floats per thread).
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_qk_kernel(const float *pqk, float *gq, float *gk, size_t bth, int nrb) {
+    const size_t n4 = (size_t)blockIdx.x * 256 + threadIdx.x;          // float4 index
+    if (n4 >= bth * (2 * DK / 4)) return;
+    float4 acc = *(const float4 *)(pqk + 4 * n4);
+    for (int r = 1; r < nrb; ++r) {
+        const float4 x = *(const float4 *)(pqk + (size_t)r * bth * 2 * DK + 4 * n4);
+        acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+    }
+    const size_t tok = (4 * n4) / (2 * DK);
+    const int c = (int)((4 * n4) % (2 * DK));
+    float *dst = c < DK ? gq + tok * DK + c : gk + tok * DK + (c - DK);
+    *(float4 *)dst = acc;
+}
+
+// gdt per token and per-sequence sums of the gate gradients: one block per
+// (b, h), tokens strided over its threads.
+__global__ __launch_bounds__(256) void bwd_gate_kernel(const float *ps, const void *dt, int dt_bf16,
+                                                        const float *A, const float *Ip, float *gdt,
+                                                        float *gabh, float *gibh, int B, int T, int H, int nrb) {
+    __shared__ float sh[2][4];
+    const int bh = blockIdx.x, b = bh / H, h = bh % H;
+    const size_t bth = (size_t)B * T * H;
+    const float Ah = A[h], Iph = Ip[h];
+    float accA = 0.f, accI = 0.f;
+    for (int t = threadIdx.x; t < T; t += 256) {
+        const size_t row = ((size_t)b * T + t) * H + h;
+        float da = 0.f, dc = 0.f;
+        for (int r = 0; r < nrb; ++r) {
+            const float2 x = *(const float2 *)(ps + ((size_t)r * bth + row) * 2);
+            da += x.x;
+            dc += x.y;
+        }
+        const float d = dt_bf16 ? (float)((const bf16_t *)dt)[row] : ((const float *)dt)[row];
+        const float x = -Ah * d;
+        const float al = expf(x), oma = -expm1f(x);
+        const float u = fmaf(Iph, dc, -da);
+        gdt[row] = Ah * al * u;
+        accA = fmaf(d * al, u, accA);
+        accI = fmaf(oma, dc, accI);
+    }
+    accA = row16_sum(accA);
+    accI = row16_sum(accI);
+    accA += __shfl_xor(accA, 16, 64); accA += __shfl_xor(accA, 32, 64);
+    accI += __shfl_xor(accI, 16, 64); accI += __shfl_xor(accI, 32, 64);
+    if ((threadIdx.x & 63) == 0) { sh[0][threadIdx.x >> 6] = accA; sh[1][threadIdx.x >> 6] = accI; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        gabh[bh] = (sh[0][0] + sh[0][1]) + (sh[0][2] + sh[0][3]);
+        gibh[bh] = (sh[1][0] + sh[1][1]) + (sh[1][2] + sh[1][3]);
+    }
+}
+
+// gA, gI_prior per head: sums over the batch (plus the start state's share
+// when it defaults to I_prior).
+__global__ __launch_bounds__(64) void bwd_head_kernel(const float *gabh, const float *gibh, const float *pI0,
+                                                       float *gA, float *gIp, int B, int H, int nrb, int dflt) {
+    const int h = blockIdx.x * 64 + threadIdx.x;
+    if (h >= H) return;
+    float sa = 0.f, si = 0.f;
+    for (int b = 0; b < B; ++b) {
+        sa += gabh[(size_t)b * H + h];
+        si += gibh[(size_t)b * H + h];
+        if (dflt)
+            for (int r = 0; r < nrb; ++r) si += pI0[((size_t)b * H + h) * nrb + r];
+    }
+    gA[h] = sa;
+    gIp[h] = si;
 }
 
 // ---------------------------------------------------------------------------
@@ -1176,9 +1804,139 @@ palimpsa_status launch_frozen(const FrozenArgs &a, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
 }
 
+// Workspace of the backward, in 256-byte aligned sections (float counts):
+//   ck    [B*H][nsb][dv/16][256][2 dk/16]   checkpoints, nsb = ceil(T / 8)
+//   pqk   [dv/16][B*T*H][2 dk]              row-block partials of gq | gk
+//   ps    [dv/16][B*T*H][2]                 row-block partials of (da, dc)
+//   gabh, gibh [B*H]                        per-sequence gate gradient sums
+//   pI0   [B*H][dv/16]                      row-block sums of gI0
+struct BwdWs {
+    float *ck, *pqk, *ps, *gabh, *gibh, *pI0;
+    size_t bytes;
+};
+BwdWs plan_bwd_ws(void *base, int B, int T, int H, int dk, int dv) {
+    const size_t nsb = (size_t)(T + kSB - 1) / kSB, nrb = (size_t)dv / kRowsPerWG;
+    const size_t bh = (size_t)B * H, bth = bh * T;
+    size_t off = 0;
+    auto take = [&](size_t floats) {
+        const size_t o = off;
+        off = (off + floats * sizeof(float) + 255) / 256 * 256;
+        return o;
+    };
+    const size_t o_ck = take(bh * nsb * 2 * dv * dk), o_pqk = take(nrb * bth * 2 * dk), o_ps = take(nrb * bth * 2);
+    const size_t o_ga = take(bh), o_gi = take(bh), o_pi = take(bh * nrb);
+    BwdWs w;
+    char *c = (char *)base;
+    w.ck = (float *)(c + o_ck); w.pqk = (float *)(c + o_pqk); w.ps = (float *)(c + o_ps);
+    w.gabh = (float *)(c + o_ga); w.gibh = (float *)(c + o_gi); w.pI0 = (float *)(c + o_pi);
+    w.bytes = off;
+    return w;
+}
+
+template <int DK, typename TIn, typename TG>
+palimpsa_status launch_bwd_t(const FwdArgs &fa, const BwdArgs &ba, const BwdWs &w, float *gq, float *gk,
+                             float *gdt, float *gA, float *gIp, int dt_bf16, hipStream_t s) {
+    if (ba.T > 0) {
+        const palimpsa_status st = launch_pass<DK, 16, TIn, float, kCheckpoint>(fa, 1, s);
+        if (st != PALIMPSA_OK) return st;
+    }
+    const size_t lds = (size_t)BwdStage<DK>::kTotal * sizeof(float);
+    auto kern = bwd_kernel<DK, TIn, TG>;
+    if (lds > 64 * 1024 &&
+        hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return PALIMPSA_ERR_HIP;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(kern, dim3(ba.nwg), dim3(kThreads), lds, s, ba);
+    const size_t bth = (size_t)ba.B * ba.T * ba.H;
+    const int nrb = ba.dv / kRowsPerWG;
+    if (bth > 0) {
+        const size_t n4 = bth * (2 * DK / 4);
+        hipLaunchKernelGGL(bwd_qk_kernel<DK>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                           (const float *)w.pqk, gq, gk, bth, nrb);
+    }
+    hipLaunchKernelGGL(bwd_gate_kernel, dim3(ba.B * ba.H), dim3(256), 0, s, (const float *)w.ps, ba.dt, dt_bf16,
+                       ba.A, ba.Ip, gdt, w.gabh, w.gibh, ba.B, ba.T, ba.H, nrb);
+    hipLaunchKernelGGL(bwd_head_kernel, dim3((ba.H + 63) / 64), dim3(64), 0, s, (const float *)w.gabh,
+                       (const float *)w.gibh, (const float *)w.pI0, gA, gIp, ba.B, ba.H, nrb, ba.mu0 ? 0 : 1);
+    return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
+}
+
+template <typename TIn, typename TG>
+palimpsa_status launch_bwd_d(int dk, const FwdArgs &fa, const BwdArgs &ba, const BwdWs &w, float *gq, float *gk,
+                             float *gdt, float *gA, float *gIp, int dt_bf16, hipStream_t s) {
+    switch (dk) {
+    case 32: return launch_bwd_t<32, TIn, TG>(fa, ba, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    case 64: return launch_bwd_t<64, TIn, TG>(fa, ba, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    default: return launch_bwd_t<128, TIn, TG>(fa, ba, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv) {
+    if (B <= 0 || H <= 0 || T < 0 || !head_ok(dk) || !head_ok(dv)) return 0;
+    return plan_bwd_ws(nullptr, B, T, H, dk, dv).bytes;
+}
+
+palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const void *beta, const void *dt,
+                             const float *A, const float *I_prior, const float *mu0, const float *I0,
+                             const void *gy, const float *gmuT, const float *gIT,
+                             float *gq, float *gk, float *gv, float *gbeta, float *gdt,
+                             float *gA, float *gIp, float *gmu0, float *gI0,
+                             int B, int T, int H, int dk, int dv,
+                             palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    if (!A || !I_prior || !gA || !gIp || !workspace)
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (T > 0 && (!q || !k || !v || !beta || !dt || !gy || !gq || !gk || !gv || !gbeta || !gdt))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if ((mu0 == nullptr) != (I0 == nullptr))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || !dtype_ok(in_dtype) || !dtype_ok(gy_dtype))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (!head_ok(dk) || !head_ok(dv))
+        return PALIMPSA_ERR_UNSUPPORTED;
+    const void *vec_ptrs[] = {q, k, v, beta, gy, mu0, I0, gmuT, gIT, gq, gk, gmu0, gI0, workspace};
+    for (const void *p : vec_ptrs)
+        if (p && !aligned_to(p, 16)) return PALIMPSA_ERR_ALIGNMENT;
+    const size_t in_sz = in_dtype == PALIMPSA_BF16 ? 2 : 4;
+    const void *f32_ptrs[] = {A, I_prior, gA, gIp, gv, gbeta, gdt};
+    for (const void *p : f32_ptrs)
+        if (p && !aligned_to(p, 4)) return PALIMPSA_ERR_ALIGNMENT;
+    if (dt && !aligned_to(dt, in_sz)) return PALIMPSA_ERR_ALIGNMENT;
+    const long long nwg = (long long)B * H * (dv / kRowsPerWG);
+    if (nwg > 0x7fffffffLL || (long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 46) ||
+        64LL * H * (dk > dv ? dk : dv) >= (1LL << 31) || (long long)B * H * 2 > 0x7fffffffLL)
+        return PALIMPSA_ERR_UNSUPPORTED;
+    const BwdWs w = plan_bwd_ws(workspace, B, T, H, dk, dv);
+    if (workspace_bytes < w.bytes) return PALIMPSA_ERR_INVALID_ARG;
+
+    FwdArgs fa = {};
+    fa.q = q; fa.k = k; fa.v = v; fa.beta = beta; fa.dt = dt;
+    fa.A = A; fa.Ip = I_prior; fa.mu0 = mu0; fa.I0 = I0;
+    fa.B = B; fa.T = T; fa.H = H; fa.dv = dv;
+    fa.nwg = (int)nwg; fa.xcd_remap = (nwg % 8 == 0) ? 1 : 0; fa.nwg_seg = (int)nwg;
+    fa.seg_len = T > 0 ? T : 1; fa.nseg = 1;
+    fa.ck = w.ck; fa.nsb = (T + kSB - 1) / kSB;
+
+    BwdArgs ba = {};
+    ba.q = q; ba.k = k; ba.v = v; ba.beta = beta; ba.dt = dt; ba.gy = gy;
+    ba.A = A; ba.Ip = I_prior; ba.mu0 = mu0; ba.I0 = I0; ba.gmuT = gmuT; ba.gIT = gIT;
+    ba.gv = gv; ba.gbeta = gbeta; ba.gmu0 = gmu0; ba.gI0 = gI0;
+    ba.ck = w.ck; ba.pqk = w.pqk; ba.ps = w.ps; ba.pI0 = w.pI0;
+    ba.B = B; ba.T = T; ba.H = H; ba.dv = dv; ba.nsb = fa.nsb;
+    ba.nwg = (int)nwg; ba.xcd_remap = fa.xcd_remap;
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf_in = in_dtype == PALIMPSA_BF16, bf_gy = gy_dtype == PALIMPSA_BF16;
+    const int dtb = bf_in ? 1 : 0;
+    if (bf_in && bf_gy) return launch_bwd_d<bf16_t, bf16_t>(dk, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
+    if (bf_in) return launch_bwd_d<bf16_t, float>(dk, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
+    if (bf_gy) return launch_bwd_d<float, bf16_t>(dk, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
+    return launch_bwd_d<float, float>(dk, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
+}
 
 palimpsa_status palimpsa_fwd_frozen(const void *q, const void *k, const void *v,
                                     const void *beta, const void *dt,

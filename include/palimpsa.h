@@ -174,6 +174,58 @@ palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
                               palimpsa_dtype in_dtype, palimpsa_dtype out_dtype,
                               void *stream);
 
+/*
+ * Backward of palimpsa_fwd_chunked (training).  The pages train through the
+ * recurrence but print no backward; this is the exact reverse-mode
+ * derivative (vector-Jacobian product) of the forward above for the scalar
+ *
+ *     L = sum(gy . y) + sum(gmuT . muT) + sum(gIT . IT),
+ *
+ * taken through the natural-parameter scans of the slides' frame "Natural
+ * parameters expose two affine scans" (App. A.12) and the gate of Eq. (9)
+ * (alpha = exp(-A dt), c = (1 - alpha) I_prior).  It recomputes the forward
+ * states itself (checkpoints every 8 tokens in the workspace), so it takes
+ * the forward's inputs, not its outputs.
+ *
+ * Inputs (device pointers, layouts and dtypes as palimpsa_fwd_chunked):
+ *   q, k, v, beta, dt, A, I_prior, mu0, I0   the forward's inputs (mu0 and I0
+ *             both NULL: the default start state mu0 = 0, I0 = I_prior)
+ *   gy        [B, T, H, dv]  gy_dtype   dL/dy
+ *   gmuT, gIT [B, H, dv, dk] float32    dL/dmuT, dL/dIT; each may be NULL (zero)
+ * Outputs (float32, overwritten):
+ *   gq, gk    [B, T, H, dk]     gv, gbeta [B, T, H, dv]     gdt [B, T, H]
+ *   gA, gIp   [H]   summed over the batch; with the default start state gIp
+ *             includes the share of I0 = I_prior
+ *   gmu0, gI0 [B, H, dv, dk]  gradient of the start state, or NULL to skip
+ *             (with the default start state: the gradient at mu0 = 0, I0 = I_prior)
+ *   workspace at least palimpsa_bwd_workspace_size(B, T, H, dk, dv) bytes,
+ *             16-byte aligned, caller-owned; contents on entry are ignored
+ *
+ * dk, dv in {32, 64, 128} (else PALIMPSA_ERR_UNSUPPORTED).  q, k, v, beta,
+ * gy, the state arrays, gq, gk and the workspace must be 16-byte aligned;
+ * the other pointers naturally aligned.  At T = 0 the per-token pointers may
+ * be NULL.  Launches are asynchronous on `stream`; calls that share a
+ * workspace must not overlap.  Arithmetic is float32; results are
+ * deterministic (no atomics).
+ */
+palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const void *beta,
+                             const void *dt, const float *A, const float *I_prior,
+                             const float *mu0, const float *I0,
+                             const void *gy, const float *gmuT, const float *gIT,
+                             float *gq, float *gk, float *gv, float *gbeta, float *gdt,
+                             float *gA, float *gIp, float *gmu0, float *gI0,
+                             int B, int T, int H, int dk, int dv,
+                             palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace palimpsa_bwd needs: the checkpoints (8 B per state
+ * entry every 8 tokens: B H ceil(T/8) dv dk 8 bytes) plus the per-row-block
+ * partials of gq, gk (dv/16 x B T H x 2 dk x 4 bytes) and small sums.
+ * Returns 0 for sizes palimpsa_bwd would reject.
+ */
+size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *palimpsa_status_string(int status);
 

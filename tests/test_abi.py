@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("palimpsa_fwd_chunked", "palimpsa_fwd_workspace_size", "palimpsa_fwd_frozen",
-              "palimpsa_step", "palimpsa_status_string", "palimpsa_version"):
+              "palimpsa_step", "palimpsa_bwd", "palimpsa_bwd_workspace_size",
+              "palimpsa_status_string", "palimpsa_version"):
         assert n in names
 
 
@@ -165,3 +166,48 @@ FROZEN_CASES = [
 @pytest.mark.parametrize("over,status", FROZEN_CASES)
 def test_frozen_rejects_invalid_calls(lib, over, status):
     assert lib.palimpsa_fwd_frozen(*_frozen_args(**over)) == status
+
+
+def _bwd_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dt=FAKE, A=FAKE, Ip=FAKE, mu0=None, I0=None,
+             gy=FAKE, gmuT=None, gIT=None, gq=FAKE, gk=FAKE, gv=FAKE, gbeta=FAKE, gdt=FAKE,
+             gA=FAKE, gIp=FAKE, gmu0=None, gI0=None, B=2, T=8, H=3, dk=64, dv=64, ind=1, gyd=1,
+             ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(over)
+    return [a[n] for n in ("q", "k", "v", "beta", "dt", "A", "Ip", "mu0", "I0", "gy", "gmuT", "gIT",
+                           "gq", "gk", "gv", "gbeta", "gdt", "gA", "gIp", "gmu0", "gI0",
+                           "B", "T", "H", "dk", "dv", "ind", "gyd", "ws", "wsb", "stream")]
+
+
+BWD_CASES = [
+    (dict(q=None), 1), (dict(gy=None), 1), (dict(gq=None), 1), (dict(gdt=None), 1),
+    (dict(gA=None), 1), (dict(gIp=None), 1), (dict(A=None), 1), (dict(ws=None), 1),
+    (dict(mu0=FAKE), 1), (dict(I0=FAKE), 1), (dict(B=0), 1), (dict(T=-1), 1), (dict(H=0), 1),
+    (dict(ind=2), 1), (dict(gyd=5), 1), (dict(wsb=64), 1), (dict(q=None, T=0, A=None), 1),
+    (dict(dk=48), 2), (dict(dv=256), 2), (dict(dk=16), 2),
+    (dict(q=FAKE + 4), 3), (dict(gy=FAKE + 8), 3), (dict(gq=FAKE + 4), 3), (dict(gk=FAKE + 8), 3),
+    (dict(gdt=FAKE + 2), 3), (dict(dt=FAKE + 1), 3), (dict(ws=FAKE + 8), 3),
+    (dict(gmuT=FAKE + 4), 3), (dict(gmu0=FAKE + 12), 3), (dict(gA=FAKE + 1), 3),
+    (dict(mu0=FAKE + 4, I0=FAKE), 3),
+]
+
+
+@pytest.mark.parametrize("over,status", BWD_CASES)
+def test_bwd_rejects_invalid_calls(lib, over, status):
+    assert lib.palimpsa_bwd(*_bwd_args(**over)) == status
+
+
+def test_bwd_workspace_size_host_logic(lib):
+    """Checkpoints every 8 tokens plus the row-block partials, each section
+    padded to 256 bytes."""
+    import bayesian_metaplastic_memory_amd as pm
+    pad = lambda n: (4 * n + 255) // 256 * 256
+
+    def expect(B, T, H, dk, dv):
+        nsb, nrb, bh = (T + 7) // 8, dv // 16, B * H
+        return (pad(bh * nsb * 2 * dv * dk) + pad(nrb * bh * T * 2 * dk) + pad(nrb * bh * T * 2)
+                + 2 * pad(bh) + pad(bh * nrb))
+    for shape in [(1, 10, 2, 32, 32), (8, 4096, 12, 128, 128), (1, 0, 3, 64, 128), (2, 9, 1, 128, 64)]:
+        assert pm.bwd_workspace_size(*shape) == expect(*shape), shape
+    assert pm.bwd_workspace_size(1, 8, 2, 48, 64) == 0
+    assert pm.bwd_workspace_size(0, 8, 2, 64, 64) == 0

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import workloads
-from parity_utils import assert_close, gpu_args, rel_err, to_device, to_np, tol_for
+from parity_utils import TOL_BWD, assert_close, gpu_args, rel_err, to_device, to_np, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -499,3 +499,121 @@ def test_frozen_agrees_with_exact_path_when_importance_stays_at_prior():
                                out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert rel_err(y_fz, y_ex) <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# backward (training)
+# ---------------------------------------------------------------------------
+
+BWD_NAMES = ("gq", "gk", "gv", "gbeta", "gdt", "gA", "gIp", "gmu0", "gI0")
+
+
+def _run_bwd(inp, gr, want_state=True):
+    g = to_device(inp, DEV)
+    gg = to_device(gr, DEV)
+    out = _pm().bwd(*gpu_args(g), gg["gy"], mu0=g.get("mu0"), I0=g.get("I0"),
+                    gmuT=gg.get("gmuT"), gIT=gg.get("gIT"), want_state_grads=want_state)
+    torch.cuda.synchronize()
+    return out
+
+
+def _bwd_ref(inp, gr, nthreads=0):
+    return oracle.bwd(**inp, gy=gr["gy"], gmuT=gr.get("gmuT"), gIT=gr.get("gIT"), nthreads=nthreads)
+
+
+def _compare_bwd(got, ref, tol, names=BWD_NAMES, log=None):
+    for n in names:
+        if n in got:
+            assert_close(n, got[n], ref[n], tol, log)
+
+
+BWD_CASES = [
+    # B, T, H, dk, dv, dtype, start state given, final-state gradients
+    (1, 37, 2, 32, 32, torch.float32, True, True),
+    (2, 64, 3, 64, 64, torch.float32, False, False),
+    (1, 100, 2, 128, 128, torch.bfloat16, True, True),
+    (2, 17, 2, 64, 128, torch.float32, True, False),
+    (1, 9, 3, 128, 64, torch.bfloat16, False, True),
+    (1, 1, 2, 32, 64, torch.float32, True, True),
+    (2, 8, 1, 128, 32, torch.float32, False, True),
+    (1, 200, 1, 32, 128, torch.bfloat16, False, False),
+]
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,dtype,state,final", BWD_CASES)
+def test_bwd_matches_oracle(B, T, H, dk, dv, dtype, state, final):
+    w = workloads.WORKLOADS[0].with_(B=B, H=H, dk=dk, dv=dv, dtype=dtype, A_mode="logspace16")
+    _announce("bwd", B=B, T=T, H=H, dk=dk, dv=dv, dtype=dtype, state=state, final=final)
+    inp = workloads.make_inputs(w, T=T, seed=T + dk + 3 * dv)
+    if state:
+        inp["mu0"], inp["I0"] = workloads.random_state(B, H, dv, dk, inp["I_prior"], seed=T + 1)
+    gr = workloads.upstream_grads(B, T, H, dv, dk, dtype, seed=T + dk, final=final)
+    got = _run_bwd(inp, gr)
+    _compare_bwd(got, _bwd_ref(inp, gr), TOL_BWD)
+
+
+def test_bwd_empty_sequence():
+    w = workloads.WORKLOADS[0].with_(B=2, H=3, dk=64, dv=32)
+    _announce("bwd T=0", B=2, H=3, dk=64, dv=32)
+    inp = workloads.make_inputs(w, T=0)
+    inp["mu0"], inp["I0"] = workloads.random_state(2, 3, 32, 64, inp["I_prior"], seed=4)
+    gr = workloads.upstream_grads(2, 0, 3, 32, 64, torch.float32, seed=4)
+    got = _run_bwd(inp, gr)
+    assert torch.equal(got["gmu0"].cpu(), gr["gmuT"]) and torch.equal(got["gI0"].cpu(), gr["gIT"])
+    assert float(got["gA"].abs().max()) == 0.0 and float(got["gIp"].abs().max()) == 0.0
+
+
+def test_bwd_tiny_workload_full():
+    w = workloads.WORKLOADS[0]
+    _announce("bwd tiny fp32", B=w.B, H=w.H, T=w.T, d=w.dk)
+    inp = workloads.make_inputs(w)
+    gr = workloads.upstream_grads(w.B, w.T, w.H, w.dv, w.dk, w.dtype, seed=0)
+    _compare_bwd(_run_bwd(inp, gr), _bwd_ref(inp, gr), TOL_BWD)
+
+
+def test_bwd_mqar_workload_full():
+    w = workloads.WORKLOADS[1]
+    _announce("bwd mqar fp32", B=w.B, H=w.H, T=w.T, d=w.dk)
+    inp = workloads.make_inputs(w)
+    gr = workloads.upstream_grads(w.B, w.T, w.H, w.dv, w.dk, w.dtype, seed=1)
+    _compare_bwd(_run_bwd(inp, gr), _bwd_ref(inp, gr), TOL_BWD)
+
+
+def test_bwd_layer760m_sampled_head():
+    """Full 760M-layer backward on the GPU; the oracle runs one head index h
+    for every sequence b, so gA[h] and gIp[h] (sums over b) compare exactly."""
+    w = workloads.WORKLOADS[2]
+    h = 7
+    _announce("bwd 760M layer bf16", B=w.B, H=w.H, T=w.T, d=w.dk, sampled_head=h)
+    inp = workloads.make_inputs(w)
+    gr = workloads.upstream_grads(w.B, w.T, w.H, w.dv, w.dk, w.dtype, seed=2)
+    got = _run_bwd(inp, gr)
+    heads = [(b, h) for b in range(w.B)]
+    sub = oracle.select_heads(inp, heads)
+    gy_s = to_np(gr["gy"])[:, :, h, :].transpose(1, 0, 2)[None]
+    gm_s = to_np(gr["gmuT"])[:, h][None]
+    gi_s = to_np(gr["gIT"])[:, h][None]
+    ref = oracle.bwd(**sub, gy=gy_s, gmuT=gm_s, gIT=gi_s, nthreads=len(heads))
+    bs = list(range(w.B))
+    for n in ("gq", "gk", "gv", "gbeta"):
+        assert_close(n + " (head %d)" % h, to_np(got[n])[bs, :, h, :].transpose(1, 0, 2)[None], ref[n], TOL_BWD)
+    assert_close("gdt (head %d)" % h, to_np(got["gdt"])[:, :, h].T[None], ref["gdt"], TOL_BWD)
+    assert_close("gA[h]", to_np(got["gA"])[h:h + 1], ref["gA"].sum(keepdims=True), TOL_BWD)
+    assert_close("gIp[h]", to_np(got["gIp"])[h:h + 1], ref["gIp"].sum(keepdims=True), TOL_BWD)
+    assert_close("gmu0 (head %d)" % h, to_np(got["gmu0"])[:, h][None], ref["gmu0"], TOL_BWD)
+    assert_close("gI0 (head %d)" % h, to_np(got["gI0"])[:, h][None], ref["gI0"], TOL_BWD)
+
+
+def test_bwd_is_deterministic_and_ignores_stale_workspace():
+    w = workloads.WORKLOADS[0].with_(B=2, H=2, dk=64, dv=64)
+    _announce("bwd determinism", B=2, H=2, T=77, dk=64, dv=64)
+    inp = workloads.make_inputs(w, T=77)
+    gr = workloads.upstream_grads(2, 77, 2, 64, 64, torch.float32, seed=5)
+    g = to_device(inp, DEV)
+    gg = to_device(gr, DEV)
+    ws = torch.full((_pm().bwd_workspace_size(2, 77, 2, 64, 64),), 0x7F, dtype=torch.uint8, device=DEV)
+    a = _pm().bwd(*gpu_args(g), gg["gy"], gmuT=gg["gmuT"], gIT=gg["gIT"], workspace=ws)
+    b = _pm().bwd(*gpu_args(g), gg["gy"], gmuT=gg["gmuT"], gIT=gg["gIT"])
+    torch.cuda.synchronize()
+    for n in BWD_NAMES:
+        assert torch.equal(a[n], b[n]), n

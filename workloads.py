@@ -135,3 +135,15 @@ def random_state(B: int, H: int, dv: int, dk: int, I_prior: torch.Tensor, seed: 
     excess = torch.empty(B, H, dv, dk).exponential_(1.0, generator=g)
     I0 = I_prior.view(1, H, 1, 1) * (1.0 + excess)
     return mu0.float().contiguous(), I0.float().contiguous()
+
+
+def upstream_grads(B: int, T: int, H: int, dv: int, dk: int, dtype: torch.dtype, seed: int,
+                   final: bool = True) -> dict:
+    """Seeded upstream gradients for the backward: gy ~ N(0, 1) in the
+    output dtype, and (if ``final``) gmuT, gIT ~ 0.1 N(0, 1) in float32."""
+    g = torch.Generator().manual_seed(10_000 + seed)
+    out = {"gy": torch.randn(B, T, H, dv, generator=g).to(dtype).contiguous(), "gmuT": None, "gIT": None}
+    if final:
+        out["gmuT"] = (0.1 * torch.randn(B, H, dv, dk, generator=g)).contiguous()
+        out["gIT"] = (0.1 * torch.randn(B, H, dv, dk, generator=g)).contiguous()
+    return out
