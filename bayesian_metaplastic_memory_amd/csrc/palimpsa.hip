@@ -431,23 +431,27 @@ __device__ inline void summary_chunk(const float *buf, float *M, float *Ib, floa
     }
 }
 
-// A lane's checkpoint: dst[0, N) = M, dst[N, 2N) = I, as 128-bit accesses
-// (N = DK / 16 in {2, 4, 8}; dst is 16-byte aligned).
+// A workgroup's checkpoint block: the lane's values (M[0, N), I[0, N)),
+// N = DK / 16 in {2, 4, 8}, as 2N/4 float4s, float4 i of thread tid at
+// blk + 4 (i * kThreads + tid), so each access instruction covers 1 KiB of
+// contiguous memory.  Written once and read once much later: non-temporal.
 template <int N>
-__device__ inline void store_pair(float *dst, const float *M, const float *I) {
+__device__ inline void store_pair(float *blk, int tid, const float *M, const float *I) {
     float v[2 * N];
 #pragma unroll
     for (int i = 0; i < N; ++i) { v[i] = M[i]; v[N + i] = I[i]; }
 #pragma unroll
-    for (int i = 0; i < 2 * N; i += 4) *(float4 *)(dst + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+    for (int i = 0; i < 2 * N; i += 4)
+        __builtin_nontemporal_store(f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]},
+                                    (f32x4 *)(blk + 4 * ((i / 4) * kThreads + tid)));
 }
 template <int N>
-__device__ inline void load_pair(const float *src, float *M, float *I) {
+__device__ inline void load_pair(const float *blk, int tid, float *M, float *I) {
     float v[2 * N];
 #pragma unroll
     for (int i = 0; i < 2 * N; i += 4) {
-        const float4 x = *(const float4 *)(src + i);
-        v[i] = x.x; v[i + 1] = x.y; v[i + 2] = x.z; v[i + 3] = x.w;
+        const f32x4 x = __builtin_nontemporal_load((const f32x4 *)(blk + 4 * ((i / 4) * kThreads + tid)));
+        v[i] = x[0]; v[i + 1] = x[1]; v[i + 2] = x[2]; v[i + 3] = x[3];
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) { M[i] = v[i]; I[i] = v[N + i]; }
@@ -456,9 +460,8 @@ __device__ inline void load_pair(const float *src, float *M, float *I) {
 // Checkpoint pass of the backward over one staged chunk: the forward update
 // without readout (the same 4 VALU ops per entry and token as the replay,
 // so the states are bit-identical to the forward's), storing (M, I) before
-// every kSB-th token of the sequence.  The lane's 2 DK/16 floats of a
-// checkpoint are contiguous: ckp + s * ck_stride for the checkpoint before
-// token kSB s.
+// every kSB-th token of the sequence: the workgroup's block for the
+// checkpoint before token kSB s is at ckp + s * ck_stride.
 template <int DK, int C>
 __device__ inline void ckpt_chunk(const float *buf, float *M, float *I, int row_local, int g,
                                   float *ckp, size_t ck_stride, int t0, int ntok) {
@@ -472,7 +475,7 @@ __device__ inline void ckpt_chunk(const float *buf, float *M, float *I, int row_
 #pragma unroll 1
     for (int sb = 0; sb < C / kSB; ++sb) {
         if (t0 + sb * kSB < ntok) {
-            store_pair<LT::kCols>(ckp + (size_t)((t0 / kSB) + sb) * ck_stride, M, I);
+            store_pair<LT::kCols>(ckp + (size_t)((t0 / kSB) + sb) * ck_stride, threadIdx.x, M, I);
         }
 #pragma unroll
         for (int u0 = 0; u0 < kSB; ++u0) {
@@ -608,8 +611,7 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
     // checkpoints: [B*H][nsb][row block][thread][2 DK/16] floats
     const size_t ck_stride = (size_t)rb_per_head * kThreads * 2 * LT::kCols;
     float *ckp = MODE == kCheckpoint
-                     ? a.ck + ((size_t)bh * a.nsb * rb_per_head + row0 / kRowsPerWG) * (kThreads * 2 * LT::kCols) +
-                           tid * 2 * LT::kCols
+                     ? a.ck + ((size_t)bh * a.nsb * rb_per_head + row0 / kRowsPerWG) * (kThreads * 2 * LT::kCols)
                      : nullptr;
     Stager<DK, C, TIn, MODE == kReplay> st;
     if (nchunks > 0) {
@@ -721,7 +723,7 @@ struct BwdArgs {
     float *gv, *gbeta, *gmu0, *gI0;
     const float *ck;
     float *pqk;        // [row block][B*T*H][2 DK]: gq | gk partials
-    float *ps;         // [row block][B*T*H][2]: (da, dc) partials
+    float *ps;         // [row block][B*H][T][2]: (da, dc) partials
     float *pI0;        // [B*H][row block]: sum of gI0 (default start state)
     int B, T, H, dv, nsb, nwg, xcd_remap;
 };
@@ -919,17 +921,26 @@ __device__ inline void bwd_reverse_token(const float *buf, int e, const float *M
             GI[s] *= alpha;
         }
     }
-    // reduce-scatter of (gq, gk) over the wave's 4 rows
+    // reduce-scatter of (gq, gk) over the wave's 4 rows.  v_permlane32_swap
+    // of (x, y) leaves lanes < 32 with x of lanes l and l+32 and the others
+    // with y of lanes l-32 and l, so one add pairs rows (0, 2) and (1, 3) and
+    // keeps gq in the low half-wave, gk in the high; v_permlane16_swap then
+    // pairs rows (0, 1) and (2, 3), even rows keeping the first half of the
+    // lane's columns.
     const bool up32 = lane & 32, up16 = lane & 16;
     float h8[KC];
 #pragma unroll
-    for (int s = 0; s < KC; ++s)
-        h8[s] = (up32 ? dk[s] : dq[s]) + __shfl_xor(up32 ? dq[s] : dk[s], 32, 64);
+    for (int s = 0; s < KC; ++s) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(dq[s]), __float_as_uint(dk[s]), false, false);
+        h8[s] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
     constexpr int KH = KC / 2;
     float h4[KH];
 #pragma unroll
-    for (int s = 0; s < KH; ++s)
-        h4[s] = (up16 ? h8[KH + s] : h8[s]) + __shfl_xor(up16 ? h8[s] : h8[KH + s], 16, 64);
+    for (int s = 0; s < KH; ++s) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(h8[s]), __float_as_uint(h8[KH + s]), false, false);
+        h4[s] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
     const int s0 = up16 ? KH : 0;
     float *dst = red + (up32 ? DK : 0) + LT::col(g, s0 / LT::kVec, s0 % LT::kVec);
     if (KH == 4) *(float4 *)dst = make_float4(h4[0], h4[KH > 1 ? 1 : 0], h4[KH > 2 ? 2 : 0], h4[KH > 3 ? 3 : 0]);
@@ -995,7 +1006,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             }
     } else {
         const size_t ck_stride = (size_t)rb_per_head * kThreads * 2 * KC;
-        const float *ckb = a.ck + ((size_t)bh * a.nsb * rb_per_head + rb) * (kThreads * 2 * KC) + tid * 2 * KC;
+        const float *ckb = a.ck + ((size_t)bh * a.nsb * rb_per_head + rb) * (kThreads * 2 * KC);
         const TIn *kseq = (const TIn *)a.k + seq0 * DK;
         const TIn *qseq = (const TIn *)a.q + seq0 * DK;
         const TIn *vseq = (const TIn *)a.v + seq0 * a.dv + row0;
@@ -1010,7 +1021,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             st.commit(lds + ((a.nsb - 1) & 1) * S::kFloats, A, Ip, tid);
         }
         float ckM[KC], ckI[KC];
-        load_pair<KC>(ckb + (size_t)(a.nsb - 1) * ck_stride, ckM, ckI);
+        load_pair<KC>(ckb + (size_t)(a.nsb - 1) * ck_stride, tid, ckM, ckI);
         __syncthreads();
 
         for (int sb = a.nsb - 1; sb >= 0; --sb) {
@@ -1071,7 +1082,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             float nM[KC], nI[KC];
-            if (sb > 0) load_pair<KC>(ckb + (size_t)(sb - 1) * ck_stride, nM, nI);
+            if (sb > 0) load_pair<KC>(ckb + (size_t)(sb - 1) * ck_stride, tid, nM, nI);
 #pragma unroll
             for (int e = 3; e >= 0; --e)
                 bwd_reverse_token<DK>(cur, e, xM[e], xI[e], e == 0 ? ckM : xM[e > 0 ? e - 1 : 0],
@@ -1107,7 +1118,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                 float v = 0.f;
 #pragma unroll
                 for (int r = 0; r < kRowsPerWG; ++r) v += src[r];
-                if (t0 + e < a.T) a.ps[((size_t)rb * bth + seq0 + (size_t)(t0 + e) * a.H) * 2 + qd] = v;
+                if (t0 + e < a.T) a.ps[((size_t)rb * bth + (size_t)bh * a.T + t0 + e) * 2 + qd] = v;
             }
             __syncthreads();
             if (sb > 0) {
@@ -1173,7 +1184,7 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const float *ps, const vo
         const size_t row = ((size_t)b * T + t) * H + h;
         float da = 0.f, dc = 0.f;
         for (int r = 0; r < nrb; ++r) {
-            const float2 x = *(const float2 *)(ps + ((size_t)r * bth + row) * 2);
+            const float2 x = *(const float2 *)(ps + ((size_t)r * bth + (size_t)bh * T + t) * 2);
             da += x.x;
             dc += x.y;
         }
@@ -1805,9 +1816,9 @@ palimpsa_status launch_frozen(const FrozenArgs &a, hipStream_t s) {
 }
 
 // Workspace of the backward, in 256-byte aligned sections (float counts):
-//   ck    [B*H][nsb][dv/16][256][2 dk/16]   checkpoints, nsb = ceil(T / 8)
+//   ck    [B*H][nsb][dv/16][dk/32][256][4]  checkpoints, nsb = ceil(T / 8)
 //   pqk   [dv/16][B*T*H][2 dk]              row-block partials of gq | gk
-//   ps    [dv/16][B*T*H][2]                 row-block partials of (da, dc)
+//   ps    [dv/16][B*H][T][2]                row-block partials of (da, dc)
 //   gabh, gibh [B*H]                        per-sequence gate gradient sums
 //   pI0   [B*H][dv/16]                      row-block sums of gI0
 struct BwdWs {

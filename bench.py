@@ -36,6 +36,11 @@ VALU_PER_UPDATE = 6          # 4 FMA + 2 MUL
 RCP_SLOTS = 2                # v_rcp_f32 issue cost in FMA slots: half rate on gfx950
 FLOPS_PER_UPDATE = 10        # FMA = 2 flops, MUL = 1; the reciprocal is not counted
 HBM_PEAK_GBS = 8000.0
+# Backward per state entry and token: replay of the update (2 FMA + MUL + FMA
+# = 4 VALU, 7 flops) and the reverse step (17 VALU = 22 flops, plus one
+# v_rcp_f32 = 2 slots): 23 issue slots, 29 flops.
+BWD_SLOTS_PER_UPDATE = 23
+BWD_FLOPS_PER_UPDATE = 29
 
 
 def alu_peak_tflops():
@@ -59,6 +64,10 @@ def load_traffic(name):
     if d.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def bwd_peak_tflops():
+    return LANE_OPS_PER_S / BWD_SLOTS_PER_UPDATE * BWD_FLOPS_PER_UPDATE / 1e12
 
 
 def time_launches(fn, steps, warmup, torch):
@@ -132,6 +141,47 @@ def decode_extra(torch, pm, workloads, steps):
                          "traffic": load_traffic("step_kernel_decode_B64_H32_d128_traffic.json")}}
 
 
+def backward_extra(torch, pm, workloads, w, g, steps):
+    """palimpsa_bwd on the same workload: checkpoint pass, backward kernel and
+    the three finishing kernels, timed as one call."""
+    dev = g["q"].device
+    gr = {n: (x.to(dev) if x is not None else None)
+          for n, x in workloads.upstream_grads(w.B, w.T, w.H, w.dv, w.dk, w.dtype, seed=2).items()}
+    ws = torch.empty(pm.bwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device=dev)
+    args = (g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], gr["gy"])
+    out = pm.bwd(*args, gmuT=gr["gmuT"], gIT=gr["gIT"], workspace=ws)
+    fn = lambda: pm.bwd(*args, gmuT=gr["gmuT"], gIT=gr["gIT"], workspace=ws, out=out)
+    _, per = time_launches(fn, steps, 3, torch)
+    avg_s = sum(per) / len(per) / 1e3
+    updates = w.B * w.H * w.T * w.dv * w.dk
+    achieved = updates * BWD_FLOPS_PER_UPDATE / avg_s / 1e12
+    return {"workload": w.name + ", backward (gq, gk, gv, gbeta, gdt, gA, gIp, gmu0, gI0)",
+            "tokens_per_s": w.B * w.T / avg_s, "ms_per_call": avg_s * 1e3,
+            "workspace_GB": ws.numel() / 1e9,
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": bwd_peak_tflops(), "unit": "TFLOP/s",
+                         "frac": achieved / bwd_peak_tflops(),
+                         "traffic": load_traffic("bwd_layer760m_bf16_traffic.json") if w.name.startswith("layer760m") else None,
+                         "scope": "whole call (5 kernels); per-kernel split in the committed trace",
+                         "per_update": "replay 4 VALU + reverse 17 VALU + 1 v_rcp_f32 = 23 slots, 29 flops"}}
+
+
+def frozen_extra(torch, pm, w, g, steps):
+    """palimpsa_fwd_frozen (importance held at I_prior) on the same workload."""
+    y = torch.empty(w.B, w.T, w.H, w.dv, dtype=w.dtype, device=g["q"].device)
+    muT = torch.empty(w.B, w.H, w.dv, w.dk, device=g["q"].device)
+    fn = lambda: pm.fwd_frozen(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], y=y, muT=muT)
+    _, per = time_launches(fn, steps, 10, torch)
+    avg_s = sum(per) / len(per) / 1e3
+    esz = 2 if w.dtype == torch.bfloat16 else 4
+    hbm = w.B * w.T * w.H * (2 * w.dk + 2 * w.dv + 1 + w.dv) * esz + 4 * w.B * w.H * w.dv * w.dk
+    return {"workload": w.name + ", frozen importance (Mamba2 limit) on MFMA",
+            "tokens_per_s": w.B * w.T / avg_s, "ms_per_launch": avg_s * 1e3,
+            "roofline": {"bound": "hbm", "achieved": hbm / avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": hbm / avg_s / 1e9 / HBM_PEAK_GBS,
+                         "traffic": load_traffic("frozen_fwd_layer760m_bf16_traffic.json") if w.name.startswith("layer760m") else None,
+                         "algorithmic_bytes": hbm}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +191,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads in the oracle sample (0: all heads of the workload)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the backward and frozen-path timings")
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--workload", default="2",
                     help="forward workload to time: 2 (760M layer, default), 0, 1, 4 or 4b")
@@ -214,6 +265,9 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = decode_extra(torch, pm, workloads, max(64, args.steps))
+    if not args.no_extras and w.dtype == torch.bfloat16:
+        out["backward"] = backward_extra(torch, pm, workloads, w, g, max(5, args.steps // 5))
+        out["frozen"] = frozen_extra(torch, pm, w, g, max(20, args.steps))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads or w.B * w.H)
     print(json.dumps(out), flush=True)
