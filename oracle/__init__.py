@@ -72,11 +72,11 @@ def _lib():
             lib = ctypes.CDLL(_LIB)
             dp = ctypes.POINTER(ctypes.c_double)
             i = ctypes.c_int
-            lib.oracle_fwd.argtypes = [i, i, i, i, i] + [dp] * 10 + [i]
+            lib.oracle_fwd.argtypes = [i, i, i, i, i] + [dp] * 10 + [i, i]
             lib.oracle_fwd.restype = None
-            lib.oracle_step.argtypes = [i, i, i, i] + [dp] * 10 + [i]
+            lib.oracle_step.argtypes = [i, i, i, i] + [dp] * 10 + [i, i]
             lib.oracle_step.restype = None
-            lib.oracle_bwd.argtypes = [i, i, i, i, i] + [dp] * 21 + [i]
+            lib.oracle_bwd.argtypes = [i, i, i, i, i] + [dp] * 21 + [i, i]
             lib.oracle_bwd.restype = None
             lib.oracle_max_threads.argtypes = []
             lib.oracle_max_threads.restype = i
@@ -103,12 +103,32 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
+VSTAR, PRIOR_PER_ENTRY = 1, 2
+
+
+def _opts(Ip, H, dv, dk, vstar):
+    """Option bits of the C oracle: the prior is per head ``[H]`` or per
+    state entry ``[H, dv, dk]``; ``vstar`` means v holds beta . v."""
+    if Ip.shape == (H,):
+        o = 0
+    elif Ip.shape == (H, dv, dk):
+        o = PRIOR_PER_ENTRY
+    else:
+        raise ValueError("I_prior must be [H] or [H, dv, dk]")
+    return o | (VSTAR if vstar else 0)
+
+
+def _prior_full(Ip, H, dv, dk):
+    """The prior as [H, dv, dk] (a per-head prior broadcast to every entry)."""
+    return Ip if Ip.shape == (H, dv, dk) else np.broadcast_to(Ip[:, None, None], (H, dv, dk))
+
+
 def _init_state(B, H, dv, dk, Ip, mu0, I0):
     if (mu0 is None) != (I0 is None):
         raise ValueError("give both mu0 and I0, or neither")
     if mu0 is None:
         mu = np.zeros((B, H, dv, dk))
-        I = np.broadcast_to(Ip[None, :, None, None], (B, H, dv, dk)).copy()
+        I = np.broadcast_to(_prior_full(Ip, H, dv, dk)[None], (B, H, dv, dk)).copy()
     else:
         mu, I = _f64(mu0).copy(), _f64(I0).copy()
         if mu.shape != (B, H, dv, dk) or I.shape != (B, H, dv, dk):
@@ -116,28 +136,31 @@ def _init_state(B, H, dv, dk, Ip, mu0, I0):
     return mu, I
 
 
-def fwd(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None, nthreads: int = 0):
+def fwd(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None, nthreads: int = 0, vstar: bool = False):
     """Sequential float64 Eq. (5) over the whole sequence (C oracle).
 
     Returns ``(y [B,T,H,dv], muT [B,H,dv,dk], IT [B,H,dv,dk])`` as float64.
-    ``mu0 = I0 = None`` means ``mu0 = 0`` and ``I0 = I_prior``.
+    ``mu0 = I0 = None`` means ``mu0 = 0`` and ``I0 = I_prior``.  ``I_prior``
+    is ``[H]`` or ``[H, dv, dk]`` (one prior per state entry); with ``vstar``
+    the ``v`` argument holds ``v* = beta . v``.
     """
     q, k, v, beta, dt = (_f64(x) for x in (q, k, v, beta, dt))
     A, Ip = _f64(A), _f64(I_prior)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != v.shape \
-            or dt.shape != (B, T, H) or A.shape != (H,) or Ip.shape != (H,):
+            or dt.shape != (B, T, H) or A.shape != (H,):
         raise ValueError("inconsistent shapes")
+    opts = _opts(Ip, H, dv, dk, vstar)
     mu, I = _init_state(B, H, dv, dk, Ip, mu0, I0)
     y = np.zeros((B, T, H, dv))
     _lib().oracle_fwd(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                       _ptr(dt), _ptr(A), _ptr(Ip), _ptr(mu), _ptr(I), _ptr(y),
-                      int(nthreads))
+                      opts, int(nthreads))
     return y, mu, I
 
 
-def step(q, k, v, beta, dt, A, I_prior, mu, I, nthreads: int = 0):
+def step(q, k, v, beta, dt, A, I_prior, mu, I, nthreads: int = 0, vstar: bool = False):
     """One decode token (C oracle).  q, k ``[B,H,dk]``; v, beta ``[B,H,dv]``;
     dt ``[B,H]``.  Returns ``(y [B,H,dv], mu', I')`` without touching inputs."""
     q, k, v, beta, dt = (_f64(x) for x in (q, k, v, beta, dt))
@@ -147,15 +170,16 @@ def step(q, k, v, beta, dt, A, I_prior, mu, I, nthreads: int = 0):
     mu, I = _f64(mu).copy(), _f64(I).copy()
     if mu.shape != (B, H, dv, dk) or I.shape != mu.shape or dt.shape != (B, H):
         raise ValueError("inconsistent shapes")
+    opts = _opts(Ip, H, dv, dk, vstar)
     y = np.zeros((B, H, dv))
     _lib().oracle_step(B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                        _ptr(dt), _ptr(A), _ptr(Ip), _ptr(mu), _ptr(I), _ptr(y),
-                       int(nthreads))
+                       opts, int(nthreads))
     return y, mu, I
 
 
 def bwd(q, k, v, beta, dt, A, I_prior, gy, mu0=None, I0=None, gmuT=None, gIT=None,
-        nthreads: int = 0) -> dict:
+        nthreads: int = 0, vstar: bool = False) -> dict:
     """Reverse-mode derivative of ``fwd`` (C oracle) for the scalar
     ``L = sum(gy * y) + sum(gmuT * muT) + sum(gIT * IT)``.
 
@@ -163,15 +187,20 @@ def bwd(q, k, v, beta, dt, A, I_prior, gy, mu0=None, I0=None, gmuT=None, gIT=Non
     [B,T,H,dv]``, ``gdt [B,T,H]``, ``gA, gIp [H]`` (summed over the batch),
     ``gmu0, gI0 [B,H,dv,dk]``.  With ``mu0 = I0 = None`` the start state is
     ``mu0 = 0, I0 = I_prior``; it then depends on ``I_prior``, so ``gIp``
-    also collects the sum of ``gI0`` over the head's entries.
+    also collects the sum of ``gI0`` over the head's entries.  With a
+    per-entry prior ``[H, dv, dk]``, ``gIp`` has that shape (and collects
+    ``gI0`` entry by entry); with ``vstar``, ``gv`` is the gradient with
+    respect to ``v* = beta . v`` and ``gbeta`` only has the importance term.
     """
     q, k, v, beta, dt, gy = (_f64(x) for x in (q, k, v, beta, dt, gy))
     A, Ip = _f64(A), _f64(I_prior)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != v.shape \
-            or dt.shape != (B, T, H) or gy.shape != v.shape or A.shape != (H,) or Ip.shape != (H,):
+            or dt.shape != (B, T, H) or gy.shape != v.shape or A.shape != (H,):
         raise ValueError("inconsistent shapes")
+    opts = _opts(Ip, H, dv, dk, vstar)
+    per_entry = bool(opts & PRIOR_PER_ENTRY)
     default_state = mu0 is None
     mu, I = _init_state(B, H, dv, dk, Ip, mu0, I0)
     gmuT = None if gmuT is None else _f64(gmuT)
@@ -183,18 +212,19 @@ def bwd(q, k, v, beta, dt, A, I_prior, gy, mu0=None, I0=None, gmuT=None, gIT=Non
            "gv": np.zeros((B, T, H, dv)), "gbeta": np.zeros((B, T, H, dv)),
            "gdt": np.zeros((B, T, H)), "gmu0": np.zeros((B, H, dv, dk)),
            "gI0": np.zeros((B, H, dv, dk))}
-    gA_bh, gIp_bh = np.zeros((B, H)), np.zeros((B, H))
+    gA_bh = np.zeros((B, H))
+    gIp_bh = np.zeros((B, H, dv, dk)) if per_entry else np.zeros((B, H))
     null = ctypes.POINTER(ctypes.c_double)()
     _lib().oracle_bwd(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(dt),
                       _ptr(A), _ptr(Ip), _ptr(mu), _ptr(I), _ptr(gy),
                       null if gmuT is None else _ptr(gmuT), null if gIT is None else _ptr(gIT),
                       _ptr(out["gq"]), _ptr(out["gk"]), _ptr(out["gv"]), _ptr(out["gbeta"]),
                       _ptr(out["gdt"]), _ptr(gA_bh), _ptr(gIp_bh), _ptr(out["gmu0"]),
-                      _ptr(out["gI0"]), int(nthreads))
+                      _ptr(out["gI0"]), opts, int(nthreads))
     out["gA"] = gA_bh.sum(axis=0)
     out["gIp"] = gIp_bh.sum(axis=0)
     if default_state:
-        out["gIp"] = out["gIp"] + out["gI0"].sum(axis=(0, 2, 3))
+        out["gIp"] = out["gIp"] + (out["gI0"].sum(axis=0) if per_entry else out["gI0"].sum(axis=(0, 2, 3)))
     return out
 
 
@@ -207,13 +237,15 @@ def _gate(A_h, dt):
     return np.exp(-A_h * dt), -np.expm1(-A_h * dt)
 
 
-def fwd_numpy(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None):
-    """Eq. (5) token by token, vectorised over the (i, j) state entries."""
+def fwd_numpy(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None, vstar: bool = False):
+    """Eq. (5) token by token, vectorised over the (i, j) state entries.
+    ``I_prior`` is ``[H]`` or ``[H, dv, dk]``; ``vstar`` as in ``fwd``."""
     q, k, v, beta, dt = (_f64(x) for x in (q, k, v, beta, dt))
     A, Ip = _f64(A), _f64(I_prior)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     mu, I = _init_state(B, H, dv, dk, Ip, mu0, I0)
+    prior = _prior_full(Ip, H, dv, dk)
     y = np.zeros((B, T, H, dv))
     for b in range(B):
         for h in range(H):
@@ -221,8 +253,9 @@ def fwd_numpy(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None):
             for t in range(T):
                 a, oma = _gate(A[h], dt[b, t, h])
                 kk = k[b, t, h]
-                P_new = a * P + oma * Ip[h] + np.outer(beta[b, t, h], kk * kk)
-                m = a * (P / P_new) * m + np.outer(beta[b, t, h] * v[b, t, h], kk) / P_new
+                P_new = a * P + oma * prior[h] + np.outer(beta[b, t, h], kk * kk)
+                wv = v[b, t, h] if vstar else beta[b, t, h] * v[b, t, h]
+                m = a * (P / P_new) * m + np.outer(wv, kk) / P_new
                 P = P_new
                 y[b, t, h] = m @ q[b, t, h]
             mu[b, h], I[b, h] = m, P

@@ -29,6 +29,15 @@
  *   q, k   [B, T, H, dk]     v, beta  [B, T, H, dv]     dt  [B, T, H]
  *   A, Ip  [H]               mu, I    [B, H, dv, dk]    y   [B, T, H, dv]
  *
+ * Options (the `opts` bit mask of every entry point):
+ *   ORACLE_PRIOR_PER_ENTRY (2): Ip is [H, dv, dk], one prior precision per
+ *       state entry instead of one per head (the reading notes' table of
+ *       symbols allows a prior of the state's shape, broadcast from a scalar);
+ *       the prior term is (1 - alpha) Ip[h, i, j].
+ *   ORACLE_VSTAR (1): v holds v* = beta . v, the write itself (the slides'
+ *       frame on the Mamba2 limit makes v* the kernel input); beta still
+ *       scales k^2 in the importance.
+ *
  *   backward  oracle_bwd: the reverse-mode derivative of all of the above
  *             for L = sum(gy . y) + sum(gmuT . mu_T) + sum(gIT . I_T), taken
  *             term by term of the same expressions (the pages print no
@@ -46,20 +55,27 @@
 #include <omp.h>
 #endif
 
-/* One token for one head: Eq. (5) applied in place, then the readout. */
+#define ORACLE_VSTAR 1
+#define ORACLE_PRIOR_PER_ENTRY 2
+
+/* One token for one head: Eq. (5) applied in place, then the readout.
+ * Ip points at the head's prior: one value, or dv * dk values. */
 static void oracle_token(int dk, int dv,
                          const double *q, const double *k, const double *v,
-                         const double *beta, double dt, double A, double Ip,
-                         double *mu, double *I, double *y)
+                         const double *beta, double dt, double A, const double *Ip,
+                         double *mu, double *I, double *y, int opts)
 {
     const double a = exp(-A * dt);
     const double oma = -expm1(-A * dt);
+    const int per_entry = (opts & ORACLE_PRIOR_PER_ENTRY) != 0;
     for (int i = 0; i < dv; ++i) {
         for (int j = 0; j < dk; ++j) {
             const size_t e = (size_t)i * dk + j;
             const double I_old = I[e];
-            const double I_new = a * I_old + oma * Ip + beta[i] * (k[j] * k[j]);
-            const double write = (beta[i] * v[i]) * k[j];
+            const double prior = per_entry ? Ip[e] : Ip[0];
+            const double I_new = a * I_old + oma * prior + beta[i] * (k[j] * k[j]);
+            const double wv = (opts & ORACLE_VSTAR) ? v[i] : beta[i] * v[i];
+            const double write = wv * k[j];
             mu[e] = a * (I_old / I_new) * mu[e] + write / I_new;
             I[e] = I_new;
         }
@@ -100,7 +116,7 @@ void oracle_fwd(int B, int T, int H, int dk, int dv,
                 const double *q, const double *k, const double *v,
                 const double *beta, const double *dt,
                 const double *A, const double *Ip,
-                double *mu, double *I, double *y, int nthreads)
+                double *mu, double *I, double *y, int opts, int nthreads)
 {
     set_threads(nthreads);
     const long nheads = (long)B * H;
@@ -112,8 +128,9 @@ void oracle_fwd(int B, int T, int H, int dk, int dv,
         for (int t = 0; t < T; ++t) {
             const size_t row = ((size_t)b * T + t) * H + h;
             oracle_token(dk, dv, q + row * dk, k + row * dk, v + row * dv,
-                         beta + row * dv, dt[row], A[h], Ip[h],
-                         mu_h, I_h, y + row * dv);
+                         beta + row * dv, dt[row], A[h],
+                         Ip + ((opts & ORACLE_PRIOR_PER_ENTRY) ? (size_t)h * dv * dk : (size_t)h),
+                         mu_h, I_h, y + row * dv, opts);
         }
     }
 }
@@ -126,7 +143,7 @@ void oracle_step(int B, int H, int dk, int dv,
                  const double *q, const double *k, const double *v,
                  const double *beta, const double *dt,
                  const double *A, const double *Ip,
-                 double *mu, double *I, double *y, int nthreads)
+                 double *mu, double *I, double *y, int opts, int nthreads)
 {
     set_threads(nthreads);
     const long nheads = (long)B * H;
@@ -134,9 +151,9 @@ void oracle_step(int B, int H, int dk, int dv,
     for (long bh = 0; bh < nheads; ++bh) {
         const int h = (int)(bh % H);
         oracle_token(dk, dv, q + (size_t)bh * dk, k + (size_t)bh * dk,
-                     v + (size_t)bh * dv, beta + (size_t)bh * dv, dt[bh],
-                     A[h], Ip[h], mu + (size_t)bh * dv * dk,
-                     I + (size_t)bh * dv * dk, y + (size_t)bh * dv);
+                     v + (size_t)bh * dv, beta + (size_t)bh * dv, dt[bh], A[h],
+                     Ip + ((opts & ORACLE_PRIOR_PER_ENTRY) ? (size_t)h * dv * dk : (size_t)h),
+                     mu + (size_t)bh * dv * dk, I + (size_t)bh * dv * dk, y + (size_t)bh * dv, opts);
     }
 }
 
@@ -166,19 +183,21 @@ void oracle_step(int B, int H, int dk, int dv,
  */
 static void oracle_token_bwd(int dk, int dv,
                              const double *q, const double *k, const double *v,
-                             const double *beta, double dt, double A, double Ip,
+                             const double *beta, double dt, double A, const double *Ip,
                              const double *mo, const double *Io,
                              const double *mn, const double *In,
                              const double *gy, double *gm, double *gI,
                              double *gq, double *gk, double *gv, double *gbeta,
-                             double *gdt, double *gA, double *gIp)
+                             double *gdt, double *gA, double *gIp, int opts)
 {
     const double a = exp(-A * dt);
     const double oma = -expm1(-A * dt);
+    const int per_entry = (opts & ORACLE_PRIOR_PER_ENTRY) != 0;
+    const int vstar = (opts & ORACLE_VSTAR) != 0;
     double ga = 0.0, goma = 0.0, gip = 0.0;
     for (int j = 0; j < dk; ++j) { gq[j] = 0.0; gk[j] = 0.0; }
     for (int i = 0; i < dv; ++i) {
-        const double bv = beta[i] * v[i];
+        const double bv = vstar ? v[i] : beta[i] * v[i];
         double g_w_sum = 0.0;     /* sum_j dL/dw_ij k_j  -> d(beta_i v_i) */
         double g_b_sum = 0.0;     /* sum_j dL/dI_new_ij k_j^2 -> beta_i via k^2 term */
         for (int j = 0; j < dk; ++j) {
@@ -195,21 +214,27 @@ static void oracle_token_bwd(int dk, int dv,
             g_w_sum += g_w * k[j];
             gk[j] += g_w * bv;
             /* I_new = a I_old + oma Ip + beta_i k_j^2 */
+            const double prior = per_entry ? Ip[e] : Ip[0];
             g_Io += g_In * a;
             ga += g_In * Io[e];
-            goma += g_In * Ip;
-            gip += g_In * oma;
+            goma += g_In * prior;
+            if (per_entry)
+                gIp[e] += g_In * oma;
+            else
+                gip += g_In * oma;
             g_b_sum += g_In * (k[j] * k[j]);
             gk[j] += g_In * 2.0 * beta[i] * k[j];
             gm[e] = g_mo;
             gI[e] = g_Io;
         }
-        gv[i] = g_w_sum * beta[i];
-        gbeta[i] = g_w_sum * v[i] + g_b_sum;
+        /* the write is (beta_i v_i) k_j, or v*_i k_j */
+        gv[i] = vstar ? g_w_sum : g_w_sum * beta[i];
+        gbeta[i] = vstar ? g_b_sum : g_w_sum * v[i] + g_b_sum;
     }
     *gdt = A * a * (goma - ga);
     *gA += dt * a * (goma - ga);
-    *gIp += gip;
+    if (!per_entry)
+        *gIp += gip;
 }
 
 /*
@@ -217,7 +242,8 @@ static void oracle_token_bwd(int dk, int dv,
  *   inputs as oracle_fwd; mu0, I0 [B, H, dv, dk] hold the initial state;
  *   gy [B, T, H, dv]; gmuT, gIT [B, H, dv, dk] (NULL: zero).
  * Outputs: gq, gk [B, T, H, dk]; gv, gbeta [B, T, H, dv]; gdt [B, T, H];
- *   gA_bh, gIp_bh [B, H] (per sequence; the caller sums over b);
+ *   gA_bh [B, H] and gIp_bh [B, H] or, with a per-entry prior,
+ *   [B, H, dv, dk] (per sequence; the caller sums over b);
  *   gmu0, gI0 [B, H, dv, dk].
  * States are needed newest first.  The forward pass keeps the state at the
  * start of every segment of `seg` tokens; each segment is then replayed with
@@ -232,7 +258,7 @@ void oracle_bwd(int B, int T, int H, int dk, int dv,
                 const double *gy, const double *gmuT, const double *gIT,
                 double *gq, double *gk, double *gv, double *gbeta, double *gdt,
                 double *gA_bh, double *gIp_bh, double *gmu0, double *gI0,
-                int nthreads)
+                int opts, int nthreads)
 {
     set_threads(nthreads);
     const long nheads = (long)B * H;
@@ -250,6 +276,10 @@ void oracle_bwd(int B, int T, int H, int dk, int dv,
         double *mu = malloc(sizeof(double) * S), *I = malloc(sizeof(double) * S);
         double *ysc = malloc(sizeof(double) * (size_t)dv);
         double *gm = gmu0 + (size_t)bh * S, *gI = gI0 + (size_t)bh * S;
+        const int per_entry = (opts & ORACLE_PRIOR_PER_ENTRY) != 0;
+        const double *Ip_h = Ip + (per_entry ? (size_t)h * S : (size_t)h);
+        if (per_entry)
+            for (size_t e = 0; e < S; ++e) gIp_bh[(size_t)bh * S + e] = 0.0;
         for (size_t e = 0; e < S; ++e) {
             mu[e] = mu0[(size_t)bh * S + e];
             I[e] = I0[(size_t)bh * S + e];
@@ -264,7 +294,7 @@ void oracle_bwd(int B, int T, int H, int dk, int dv,
             }
             const size_t row = ((size_t)b * T + t) * H + h;
             oracle_token(dk, dv, q + row * dk, k + row * dk, v + row * dv,
-                         beta + row * dv, dt[row], A[h], Ip[h], mu, I, ysc);
+                         beta + row * dv, dt[row], A[h], Ip_h, mu, I, ysc, opts);
         }
         /* adjoint of the final state */
         for (size_t e = 0; e < S; ++e) {
@@ -284,21 +314,23 @@ void oracle_bwd(int B, int T, int H, int dk, int dv,
                 double *nm = st_mu + (size_t)(u + 1) * S, *nI = st_I + (size_t)(u + 1) * S;
                 for (size_t e = 0; e < S; ++e) { nm[e] = st_mu[(size_t)u * S + e]; nI[e] = st_I[(size_t)u * S + e]; }
                 oracle_token(dk, dv, q + row * dk, k + row * dk, v + row * dv,
-                             beta + row * dv, dt[row], A[h], Ip[h], nm, nI, ysc);
+                             beta + row * dv, dt[row], A[h], Ip_h, nm, nI, ysc, opts);
             }
             for (int u = len - 1; u >= 0; --u) {
                 const size_t row = ((size_t)b * T + t0 + u) * H + h;
                 oracle_token_bwd(dk, dv, q + row * dk, k + row * dk, v + row * dv,
-                                 beta + row * dv, dt[row], A[h], Ip[h],
+                                 beta + row * dv, dt[row], A[h], Ip_h,
                                  st_mu + (size_t)u * S, st_I + (size_t)u * S,
                                  st_mu + (size_t)(u + 1) * S, st_I + (size_t)(u + 1) * S,
                                  gy + row * dv, gm, gI,
                                  gq + row * dk, gk + row * dk, gv + row * dv,
-                                 gbeta + row * dv, gdt + row, &gA_acc, &gIp_acc);
+                                 gbeta + row * dv, gdt + row, &gA_acc,
+                                 per_entry ? gIp_bh + (size_t)bh * S : &gIp_acc, opts);
             }
         }
         gA_bh[bh] = gA_acc;
-        gIp_bh[bh] = gIp_acc;
+        if (!per_entry)
+            gIp_bh[bh] = gIp_acc;
         free(ck_mu); free(ck_I); free(st_mu); free(st_I); free(mu); free(I); free(ysc);
     }
 }

@@ -42,8 +42,8 @@ def _inputs(rng, B, T, H, dk, dv, state=True):
     return d
 
 
-def _loss(fwd, inp, gy, gmuT, gIT):
-    y, mu, I = fwd(**inp)
+def _loss(fwd, inp, gy, gmuT, gIT, **kw):
+    y, mu, I = fwd(**inp, **kw)
     L = float((y * gy).sum())
     if gmuT is not None:
         L += float((mu * gmuT).sum())
@@ -56,7 +56,7 @@ GRAD_OF = {"q": "gq", "k": "gk", "v": "gv", "beta": "gbeta", "dt": "gdt", "A": "
            "I_prior": "gIp", "mu0": "gmu0", "I0": "gI0"}
 
 
-def _finite_differences(fwd, inp, gy, gmuT, gIT, h=1e-6):
+def _finite_differences(fwd, inp, gy, gmuT, gIT, h=1e-6, **kw):
     """Central differences of L for every element of every input."""
     fd = {}
     for name, g in GRAD_OF.items():
@@ -68,9 +68,9 @@ def _finite_differences(fwd, inp, gy, gmuT, gIT, h=1e-6):
             x = base.copy()
             step = h * max(1.0, abs(base[idx]))
             x[idx] = base[idx] + step
-            lp = _loss(fwd, dict(inp, **{name: x}), gy, gmuT, gIT)
+            lp = _loss(fwd, dict(inp, **{name: x}), gy, gmuT, gIT, **kw)
             x[idx] = base[idx] - step
-            lm = _loss(fwd, dict(inp, **{name: x}), gy, gmuT, gIT)
+            lm = _loss(fwd, dict(inp, **{name: x}), gy, gmuT, gIT, **kw)
             out[idx] = (lp - lm) / (2 * step)
         fd[g] = out
     return fd
@@ -81,15 +81,18 @@ def _normwise(a, b):
     return np.abs(a - b).max() / scale
 
 
-def _fd_pin_errors(bwd, seed, state, final_grads, T=7):
+def _fd_pin_errors(bwd, seed, state, final_grads, T=7, per_entry=False, vstar=False):
     rng = np.random.default_rng(seed)
     B, H, dk, dv = 2, 2, 3, 2
     inp = _inputs(rng, B, T, H, dk, dv, state=state)
+    if per_entry:
+        inp["I_prior"] = rng.uniform(0.5, 1.5, size=(H, dv, dk))
     gy = rng.normal(size=(B, T, H, dv))
     gmuT = rng.normal(size=(B, H, dv, dk)) if final_grads else None
     gIT = rng.normal(size=(B, H, dv, dk)) if final_grads else None
-    got = bwd(**inp, gy=gy, gmuT=gmuT, gIT=gIT)
-    fd = _finite_differences(oracle.fwd, inp, gy, gmuT, gIT)
+    kw = {"vstar": True} if vstar else {}
+    got = bwd(**inp, gy=gy, gmuT=gmuT, gIT=gIT, **kw)
+    fd = _finite_differences(oracle.fwd, inp, gy, gmuT, gIT, **kw)
     return {g: _normwise(got[g], ref) for g, ref in fd.items()}
 
 
@@ -102,6 +105,17 @@ FD_TOL = 1e-6
 def test_oracle_bwd_matches_finite_differences(state, final_grads):
     err = _fd_pin_errors(oracle.bwd, seed=3 + 2 * state + final_grads, state=state,
                          final_grads=final_grads)
+    bad = {g: e for g, e in err.items() if not e < FD_TOL}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("per_entry,vstar,state", [(True, False, False), (True, False, True),
+                                                  (False, True, True), (True, True, False)])
+def test_oracle_bwd_options_match_finite_differences(per_entry, vstar, state):
+    """A prior per state entry (gIp then has the state's shape) and the v*
+    input (gv is then the gradient with respect to v* itself)."""
+    err = _fd_pin_errors(oracle.bwd, seed=60 + per_entry + 2 * vstar + 4 * state, state=state,
+                         final_grads=True, per_entry=per_entry, vstar=vstar)
     bad = {g: e for g, e in err.items() if not e < FD_TOL}
     assert not bad, bad
 

@@ -461,3 +461,63 @@ def test_unmutated_copy_passes_pins():
 @pytest.mark.parametrize("kind", MUTANTS)
 def test_pins_catch_planted_mistake(kind):
     assert not _pins_pass(_mutant_fwd(kind))
+
+
+# ---------------------------------------------------------------------------
+# options: a prior per state entry, and v* = beta . v as the write input
+# ---------------------------------------------------------------------------
+
+def _per_entry_prior(rng, H, dv, dk):
+    return rng.uniform(0.3, 2.0, size=(H, dv, dk))
+
+
+def test_per_entry_prior_c_and_numpy_agree():
+    rng = np.random.default_rng(31)
+    inp = _rand_inputs(rng, B=2, T=9, H=2, dk=3, dv=4)
+    inp["I_prior"] = _per_entry_prior(rng, 2, 4, 3)
+    for state in (False, True):
+        if state:
+            inp["mu0"] = rng.normal(size=(2, 2, 4, 3))
+            inp["I0"] = rng.uniform(0.5, 2.0, size=(2, 2, 4, 3))
+        a = oracle.fwd(**inp)
+        b = oracle.fwd_numpy(**inp)
+        for x, y in zip(a, b):
+            np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-14)
+
+
+def test_per_entry_prior_equal_to_the_head_prior_is_the_scalar_case():
+    rng = np.random.default_rng(32)
+    inp = _rand_inputs(rng, B=1, T=6, H=3, dk=4, dv=2)
+    full = dict(inp, I_prior=np.broadcast_to(np.asarray(inp["I_prior"])[:, None, None], (3, 2, 4)).copy())
+    for x, y in zip(oracle.fwd(**inp), oracle.fwd(**full)):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_per_entry_prior_no_evidence_closed_form():
+    """beta = 0: each entry relaxes to its own prior, I_T - Ip = (prod alpha)(I_0 - Ip),
+    and the mean only decays, M_T = (prod alpha) M_0, so mu_T = (prod alpha) I_0 mu_0 / I_T."""
+    rng = np.random.default_rng(33)
+    B, T, H, dk, dv = 2, 7, 2, 3, 2
+    inp = _rand_inputs(rng, B=B, T=T, H=H, dk=dk, dv=dv)
+    inp["beta"] = np.zeros_like(inp["beta"])
+    Ip = _per_entry_prior(rng, H, dv, dk)
+    mu0 = rng.normal(size=(B, H, dv, dk))
+    I0 = rng.uniform(0.5, 3.0, size=(B, H, dv, dk))
+    _, mu, I = oracle.fwd(**dict(inp, I_prior=Ip, mu0=mu0, I0=I0))
+    P = np.exp(-np.asarray(inp["A"])[None, :] * np.asarray(inp["dt"]).sum(axis=1))   # [B, H]
+    I_ref = Ip[None] + P[:, :, None, None] * (I0 - Ip[None])
+    np.testing.assert_allclose(I, I_ref, rtol=1e-12)
+    np.testing.assert_allclose(mu, P[:, :, None, None] * I0 * mu0 / I_ref, rtol=1e-11)
+
+
+def test_vstar_input_is_the_product_it_replaces():
+    rng = np.random.default_rng(34)
+    inp = _rand_inputs(rng, B=2, T=8, H=2, dk=3, dv=3)
+    vstar = np.asarray(inp["beta"]) * np.asarray(inp["v"])
+    a = oracle.fwd(**inp)
+    b = oracle.fwd(**dict(inp, v=vstar), vstar=True)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    c = oracle.fwd_numpy(**dict(inp, v=vstar), vstar=True)
+    for x, y in zip(a, c):
+        np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-14)
