@@ -42,18 +42,18 @@ def load_library() -> ctypes.CDLL:
             lib = ctypes.CDLL(LIB_PATH)
             vp, fp, i = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
             sz = ctypes.c_size_t
-            lib.palimpsa_fwd_chunked.argtypes = ([vp] * 5 + [fp] * 4 + [vp, fp, fp] + [i] * 9 +
+            lib.palimpsa_fwd_chunked.argtypes = ([vp] * 5 + [fp] * 4 + [vp, fp, fp] + [i] * 10 +
                                                  [vp, sz, vp])
             lib.palimpsa_fwd_chunked.restype = i
             lib.palimpsa_fwd_workspace_size.argtypes = [i] * 6
             lib.palimpsa_fwd_workspace_size.restype = sz
             lib.palimpsa_fwd_frozen.argtypes = [vp] * 5 + [fp] * 3 + [vp, fp] + [i] * 7 + [vp]
             lib.palimpsa_fwd_frozen.restype = i
-            lib.palimpsa_step.argtypes = [vp] * 5 + [fp] * 4 + [vp] + [i] * 6 + [vp]
+            lib.palimpsa_step.argtypes = [vp] * 5 + [fp] * 4 + [vp] + [i] * 7 + [vp]
             lib.palimpsa_step.restype = i
-            lib.palimpsa_bwd.argtypes = [vp] * 5 + [fp] * 4 + [vp, fp, fp] + [fp] * 9 + [i] * 7 + [vp, sz, vp]
+            lib.palimpsa_bwd.argtypes = [vp] * 5 + [fp] * 4 + [vp, fp, fp] + [fp] * 9 + [i] * 8 + [vp, sz, vp]
             lib.palimpsa_bwd.restype = i
-            lib.palimpsa_bwd_workspace_size.argtypes = [i] * 5
+            lib.palimpsa_bwd_workspace_size.argtypes = [i] * 6
             lib.palimpsa_bwd_workspace_size.restype = sz
             lib.palimpsa_status_string.argtypes = [i]
             lib.palimpsa_status_string.restype = ctypes.c_char_p
@@ -92,6 +92,21 @@ def _check(t, name, shape, dtype, device):
         raise ValueError("%s must be contiguous" % name)
 
 
+VSTAR, PRIOR_PER_ENTRY = 1, 2
+
+
+def _prior_flags(I_prior, H, dv, dk, dev, vstar):
+    """Option bits from the prior's shape ([H] or [H, dv, dk]) and ``vstar``."""
+    if tuple(I_prior.shape) == (H,):
+        f = 0
+    elif tuple(I_prior.shape) == (H, dv, dk):
+        f = PRIOR_PER_ENTRY
+    else:
+        raise ValueError("I_prior must be [H] or [H, dv, dk]")
+    _check(I_prior, "I_prior", tuple(I_prior.shape), torch.float32, dev)
+    return f | (VSTAR if vstar else 0)
+
+
 def workspace_size(B, T, H, dk, dv, segments: int = 0) -> int:
     """Bytes of workspace the chunked forward uses for these sizes (0: none)."""
     return int(load_library().palimpsa_fwd_workspace_size(B, T, H, dk, dv, int(segments)))
@@ -99,12 +114,14 @@ def workspace_size(B, T, H, dk, dv, segments: int = 0) -> int:
 
 def fwd_chunked(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None, chunk: int = 0,
                 out_dtype=None, y=None, muT=None, IT=None, write_state: bool = True,
-                segments: int = 0, workspace=None):
+                segments: int = 0, workspace=None, vstar: bool = False):
     """Chunked forward.  Returns ``(y, muT, IT)``; ``muT``/``IT`` are None when
     ``write_state`` is False.  Outputs are allocated unless passed in (they may
     alias ``mu0``/``I0`` for an in-place resume).  ``segments`` (0 = library's
     choice) selects the time split; its workspace is allocated here unless a
-    uint8 device tensor is passed as ``workspace``."""
+    uint8 device tensor is passed as ``workspace``.  ``I_prior`` is ``[H]`` or
+    ``[H, dv, dk]`` (a prior per state entry); ``vstar`` means ``v`` holds
+    ``beta * v``."""
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
     B, T, H, dk = q.shape
@@ -124,7 +141,7 @@ def fwd_chunked(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None, chunk: int = 0
     _check(dt, "dt", (B, T, H), in_dtype, dev)
     _check(q, "q", (B, T, H, dk), in_dtype, dev)
     _check(A, "A", (H,), torch.float32, dev)
-    _check(I_prior, "I_prior", (H,), torch.float32, dev)
+    flags = _prior_flags(I_prior, H, dv, dk, dev, vstar)
     if (mu0 is None) != (I0 is None):
         raise ValueError("give both mu0 and I0, or neither")
     if mu0 is not None:
@@ -154,7 +171,7 @@ def fwd_chunked(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None, chunk: int = 0
             _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(dt), _ptr(A), _ptr(I_prior),
             _ptr(mu0), _ptr(I0), _ptr(y) if y.numel() else None,
             _ptr(muT), _ptr(IT), B, T, H, dk, dv, int(chunk), int(segments),
-            _DTYPES[in_dtype], _DTYPES[out_dtype],
+            _DTYPES[in_dtype], _DTYPES[out_dtype], flags,
             _ptr(workspace) if workspace is not None and workspace.numel() else None,
             workspace.numel() if workspace is not None else 0, _stream_handle(dev))
     if st != OK:
@@ -162,8 +179,9 @@ def fwd_chunked(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None, chunk: int = 0
     return y, muT, IT
 
 
-def step(q, k, v, beta, dt, A, I_prior, mu, I, out_dtype=None, y=None):
-    """One decode token; updates ``mu`` and ``I`` in place and returns ``y``."""
+def step(q, k, v, beta, dt, A, I_prior, mu, I, out_dtype=None, y=None, vstar: bool = False):
+    """One decode token; updates ``mu`` and ``I`` in place and returns ``y``.
+    ``I_prior`` is ``[H]`` or ``[H, dv, dk]``; ``vstar`` as in ``fwd_chunked``."""
     if q.dim() != 3:
         raise ValueError("q must be [B, H, dk]")
     B, H, dk = q.shape
@@ -182,7 +200,7 @@ def step(q, k, v, beta, dt, A, I_prior, mu, I, out_dtype=None, y=None):
     _check(beta, "beta", (B, H, dv), in_dtype, dev)
     _check(dt, "dt", (B, H), in_dtype, dev)
     _check(A, "A", (H,), torch.float32, dev)
-    _check(I_prior, "I_prior", (H,), torch.float32, dev)
+    flags = _prior_flags(I_prior, H, dv, dk, dev, vstar)
     _check(mu, "mu", (B, H, dv, dk), torch.float32, dev)
     _check(I, "I", (B, H, dv, dk), torch.float32, dev)
     if y is None:
@@ -193,7 +211,7 @@ def step(q, k, v, beta, dt, A, I_prior, mu, I, out_dtype=None, y=None):
     with torch.cuda.device(dev):
         st = lib.palimpsa_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(dt), _ptr(A),
                                _ptr(I_prior), _ptr(mu), _ptr(I), _ptr(y), B, H, dk, dv,
-                               _DTYPES[in_dtype], _DTYPES[out_dtype], _stream_handle(dev))
+                               _DTYPES[in_dtype], _DTYPES[out_dtype], flags, _stream_handle(dev))
     if st != OK:
         raise PalimpsaError(st, "palimpsa_step")
     return y
@@ -246,13 +264,13 @@ def fwd_frozen(q, k, v, beta, dt, A, I_prior, mu0=None, out_dtype=None, y=None, 
     return y, muT
 
 
-def bwd_workspace_size(B, T, H, dk, dv) -> int:
+def bwd_workspace_size(B, T, H, dk, dv, flags: int = 0) -> int:
     """Bytes of workspace ``palimpsa_bwd`` needs (checkpoints and partials)."""
-    return int(load_library().palimpsa_bwd_workspace_size(B, T, H, dk, dv))
+    return int(load_library().palimpsa_bwd_workspace_size(B, T, H, dk, dv, int(flags)))
 
 
 def bwd(q, k, v, beta, dt, A, I_prior, gy, mu0=None, I0=None, gmuT=None, gIT=None,
-        want_state_grads: bool = True, workspace=None, out=None):
+        want_state_grads: bool = True, workspace=None, out=None, vstar: bool = False):
     """Backward of ``fwd_chunked`` for ``L = <gy, y> + <gmuT, muT> + <gIT, IT>``.
 
     Takes the forward's inputs (the library recomputes the states) and returns
@@ -260,7 +278,9 @@ def bwd(q, k, v, beta, dt, A, I_prior, gy, mu0=None, I0=None, gmuT=None, gIT=Non
     ``want_state_grads``, ``gmu0, gI0``.  ``gmuT``/``gIT`` may be None (zero).
     ``out`` may supply preallocated output tensors by the same names;
     ``workspace`` a contiguous uint8 device tensor of at least
-    ``bwd_workspace_size`` bytes (allocated here otherwise)."""
+    ``bwd_workspace_size`` bytes (allocated here otherwise).  With a prior per
+    state entry (``I_prior`` ``[H, dv, dk]``) ``gIp`` has that shape; with
+    ``vstar`` (``v`` holds ``beta * v``) ``gv`` is the gradient w.r.t. it."""
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
     B, T, H, dk = q.shape
@@ -276,14 +296,14 @@ def bwd(q, k, v, beta, dt, A, I_prior, gy, mu0=None, I0=None, gmuT=None, gIT=Non
         _check(t, name, shape, in_dtype, dev)
     _check(gy, "gy", (B, T, H, dv), gy.dtype, dev)
     _check(A, "A", (H,), torch.float32, dev)
-    _check(I_prior, "I_prior", (H,), torch.float32, dev)
+    flags = _prior_flags(I_prior, H, dv, dk, dev, vstar)
     if (mu0 is None) != (I0 is None):
         raise ValueError("give both mu0 and I0, or neither")
     for t, name in ((mu0, "mu0"), (I0, "I0"), (gmuT, "gmuT"), (gIT, "gIT")):
         if t is not None:
             _check(t, name, (B, H, dv, dk), torch.float32, dev)
     shapes = {"gq": (B, T, H, dk), "gk": (B, T, H, dk), "gv": (B, T, H, dv), "gbeta": (B, T, H, dv),
-              "gdt": (B, T, H), "gA": (H,), "gIp": (H,)}
+              "gdt": (B, T, H), "gA": (H,), "gIp": tuple(I_prior.shape)}
     if want_state_grads:
         shapes.update(gmu0=(B, H, dv, dk), gI0=(B, H, dv, dk))
     res = {}
@@ -294,7 +314,7 @@ def bwd(q, k, v, beta, dt, A, I_prior, gy, mu0=None, I0=None, gmuT=None, gIT=Non
         _check(t, name, shape, torch.float32, dev)
         res[name] = t
     lib = load_library()
-    nbytes = bwd_workspace_size(B, T, H, dk, dv)
+    nbytes = bwd_workspace_size(B, T, H, dk, dv, flags)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
@@ -306,7 +326,7 @@ def bwd(q, k, v, beta, dt, A, I_prior, gy, mu0=None, I0=None, gmuT=None, gIT=Non
             nz(gy), _ptr(gmuT), _ptr(gIT),
             nz(res["gq"]), nz(res["gk"]), nz(res["gv"]), nz(res["gbeta"]), nz(res["gdt"]),
             _ptr(res["gA"]), _ptr(res["gIp"]), _ptr(res.get("gmu0")), _ptr(res.get("gI0")),
-            B, T, H, dk, dv, _DTYPES[in_dtype], _DTYPES[gy.dtype],
+            B, T, H, dk, dv, _DTYPES[in_dtype], _DTYPES[gy.dtype], flags,
             _ptr(workspace), workspace.numel(), _stream_handle(dev))
     if st != OK:
         raise PalimpsaError(st, "palimpsa_bwd")

@@ -132,6 +132,7 @@ struct FwdArgs {
     float *ws;         // segment summaries, see SegWs
     float *ck;         // backward checkpoints (kCheckpoint mode), see bwd_kernel
     int nsb;           // checkpoints per sequence: ceil(T / kSB)
+    int vstar;         // 1: v holds beta . v (the write itself)
 };
 
 // Workspace of a time-split forward: for each of the first nseg-1 segments,
@@ -237,8 +238,9 @@ struct Stager {
         }
     }
 
-    // Widen and write the loaded chunk to one LDS buffer.
-    __device__ inline void commit(float *buf, float A, float Ip, int tid) const {
+    // Widen and write the loaded chunk to one LDS buffer.  With vstar the v
+    // packets already hold beta . v.
+    __device__ inline void commit(float *buf, float A, float Ip, int tid, bool vstar) const {
         float *cols = buf;
         float *rows = buf + C * Stage<DK>::kColFloats;
         float *gates = rows + C * Stage<DK>::kRowFloats;
@@ -277,7 +279,8 @@ struct Stager {
             float *dst = rows + tt * Stage<DK>::kRowFloats + 2 * off;
 #pragma unroll
             for (int e = 0; e < kPerPkt; e += 2)
-                *(float4 *)(dst + 2 * e) = make_float4(xb[e], xb[e] * xv[e], xb[e + 1], xb[e + 1] * xv[e + 1]);
+                *(float4 *)(dst + 2 * e) = make_float4(xb[e], vstar ? xv[e] : xb[e] * xv[e], xb[e + 1],
+                                                       vstar ? xv[e + 1] : xb[e + 1] * xv[e + 1]);
         }
         // alpha on wave 2 and c = (1 - alpha) I_prior on wave 3 (the gate of Eq. (9))
         const int pg = gate_slot(tid);
@@ -345,9 +348,12 @@ __device__ inline float row16_transpose_sum(const float (&x)[16], int g) {
 // partial of y_t goes to a register.  Every 16 tokens one transposing
 // reduction leaves y for token g in lane g, which stores it if the token is
 // inside the sequence (`left` = tokens remaining from the chunk start).
-template <int DK, int C, typename TOut>
+//
+// With a prior per state entry (IPE) the gate's c is staged as 1 - alpha and
+// scaled by the lane's prior ipe[s]: one more VALU op per entry and token.
+template <int DK, int C, typename TOut, bool IPE>
 __device__ inline void compute_chunk(const float *buf, int left, float *M, float *I,
-                                     int row_local, int g, TOut *yrow, size_t ystride) {
+                                     int row_local, int g, TOut *yrow, size_t ystride, const float *ipe) {
     using LT = LaneTile<DK>;
     static_assert(C % kGroup == 0, "chunk must be a multiple of 16 tokens");
     const float *cbase = buf + LT::col(g, 0, 0);
@@ -380,7 +386,7 @@ __device__ inline void compute_chunk(const float *buf, int left, float *M, float
 #pragma unroll
                 for (int e = 0; e < LT::kVec; ++e) {
                     const int s = m * LT::kVec + e;
-                    const float w = fmaf(rb.x, k2[e], gc.y);        // c + beta_i k_j^2
+                    const float w = fmaf(rb.x, k2[e], IPE ? gc.y * ipe[s] : gc.y);   // c + beta_i k_j^2
                     I[s] = fmaf(gc.x, I[s], w);                     // importance
                     M[s] = fmaf(gc.x, M[s], rb.y * kk[e]);          // natural content
                     const float r = __builtin_amdgcn_rcpf(I[s]);
@@ -462,9 +468,9 @@ __device__ inline void load_pair(const float *blk, int tid, float *M, float *I) 
 // so the states are bit-identical to the forward's), storing (M, I) before
 // every kSB-th token of the sequence: the workgroup's block for the
 // checkpoint before token kSB s is at ckp + s * ck_stride.
-template <int DK, int C>
+template <int DK, int C, bool IPE>
 __device__ inline void ckpt_chunk(const float *buf, float *M, float *I, int row_local, int g,
-                                  float *ckp, size_t ck_stride, int t0, int ntok) {
+                                  float *ckp, size_t ck_stride, int t0, int ntok, const float *ipe) {
     using LT = LaneTile<DK>;
     static_assert(C % kSB == 0, "chunk must hold whole checkpoint intervals");
     const float *cbase = buf + LT::col(g, 0, 0);
@@ -492,7 +498,7 @@ __device__ inline void ckpt_chunk(const float *buf, float *M, float *I, int row_
 #pragma unroll
                 for (int e = 0; e < LT::kVec; ++e) {
                     const int s = m * LT::kVec + e;
-                    const float w = fmaf(rb.x, k2[e], gc.y);
+                    const float w = fmaf(rb.x, k2[e], IPE ? gc.y * ipe[s] : gc.y);
                     I[s] = fmaf(gc.x, I[s], w);
                     M[s] = fmaf(gc.x, M[s], rb.y * kk[e]);
                 }
@@ -516,7 +522,7 @@ enum FwdMode { kReplay = 0, kSummary = 1, kCheckpoint = 2 };
 //
 // kSummary: segment s < nseg-1 runs from a zero state without readout and
 // writes its (M_loc, Ibar_loc, P) to the workspace.
-template <int DK, int C, typename TIn, typename TOut, int MODE>
+template <int DK, int C, typename TIn, typename TOut, int MODE, bool IPE>
 __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
     using LT = LaneTile<DK>;
     extern __shared__ float lds[];
@@ -543,7 +549,9 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
     const int row_local = wave * kRowsPerWave + (lane >> 4);
     const int row = row0 + row_local;
 
-    const float A = a.A[h], Ip = a.Ip[h];
+    // prior: one per head, or (IPE) one per state entry [H, dv, dk]; with IPE
+    // the staged c is 1 - alpha and Ip is 1
+    const float A = a.A[h], Ip = IPE ? 1.f : a.Ip[h];
     const int t_begin = seg * a.seg_len;
     const int t_end = min(a.T, t_begin + a.seg_len);
 
@@ -551,6 +559,12 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
     // the earlier segments' summaries folded in.  Summary: M = Ibar = 0.
     float M[LT::kCols], I[LT::kCols];
     const size_t srow = ((size_t)bh * a.dv + row) * DK;
+    float ipe[IPE ? LT::kCols : 1];
+    if (IPE) {
+        const float *ip = a.Ip + ((size_t)h * a.dv + row) * DK;
+#pragma unroll
+        for (int m = 0; m < LT::kNVec; ++m) vecf<LT::kVec>::ld(ip + LT::col(g, m, 0), ipe + m * LT::kVec);
+    }
     if (MODE == kSummary) {
 #pragma unroll
         for (int s = 0; s < LT::kCols; ++s) { I[s] = 0.f; M[s] = 0.f; }   // I holds Ibar here
@@ -569,12 +583,12 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
             }
         } else {
 #pragma unroll
-            for (int s = 0; s < LT::kCols; ++s) { I[s] = Ip; M[s] = 0.f; }
+            for (int s = 0; s < LT::kCols; ++s) { I[s] = IPE ? ipe[s] : Ip; M[s] = 0.f; }
         }
         if (seg > 0) {
             const SegWs w(a.ws, a.nseg, (size_t)a.B * a.H, a.dv, DK);
 #pragma unroll
-            for (int s = 0; s < LT::kCols; ++s) I[s] -= Ip;              // Ibar
+            for (int s = 0; s < LT::kCols; ++s) I[s] -= IPE ? ipe[s] : Ip;   // Ibar
             for (int sp = 0; sp < seg; ++sp) {
                 const float P = w.P[(size_t)sp * a.B * a.H + bh];
 #pragma unroll
@@ -590,7 +604,7 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
                 }
             }
 #pragma unroll
-            for (int s = 0; s < LT::kCols; ++s) I[s] += Ip;
+            for (int s = 0; s < LT::kCols; ++s) I[s] += IPE ? ipe[s] : Ip;
         }
     }
 
@@ -616,7 +630,7 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
     Stager<DK, C, TIn, MODE == kReplay> st;
     if (nchunks > 0) {
         st.load(kseq, qseq, vseq, bseq, dseq, ntok, a.H, a.dv, tid);
-        st.commit(buf0, A, Ip, tid);
+        st.commit(buf0, A, Ip, tid, a.vstar);
         __syncthreads();
     }
     for (int c = 0; c < nchunks; ++c) {
@@ -629,12 +643,13 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
         }
         const float *cur = (c & 1) ? buf1 : buf0;
         if (MODE == kReplay)
-            compute_chunk<DK, C, TOut>(cur, ntok - t0, M, I, row_local, g, ybase + (size_t)t0 * ystride, ystride);
+            compute_chunk<DK, C, TOut, IPE>(cur, ntok - t0, M, I, row_local, g, ybase + (size_t)t0 * ystride,
+                                            ystride, ipe);
         else if (MODE == kSummary)
             summary_chunk<DK, C>(cur, M, I, P, row_local, g);
         else
-            ckpt_chunk<DK, C>(cur, M, I, row_local, g, ckp, ck_stride, t0, ntok);
-        if (more) st.commit((c & 1) ? buf0 : buf1, A, Ip, tid);
+            ckpt_chunk<DK, C, IPE>(cur, M, I, row_local, g, ckp, ck_stride, t0, ntok, ipe);
+        if (more) st.commit((c & 1) ? buf0 : buf1, A, Ip, tid, a.vstar);
         __syncthreads();
     }
 
@@ -725,7 +740,9 @@ struct BwdArgs {
     float *pqk;        // [row block][B*T*H][2 DK]: gq | gk partials
     float *ps;         // [row block][B*H][T][2]: (da, dc) partials
     float *pI0;        // [B*H][row block]: sum of gI0 (default start state)
+    float *pip;        // per-entry prior: [B*H][dv][dk] per-sequence gradient of I_prior
     int B, T, H, dv, nsb, nwg, xcd_remap;
+    int vstar;         // 1: v holds beta . v
 };
 
 // Staging of one sub-block of kSB tokens (newest-first order of use; the
@@ -792,7 +809,7 @@ struct BwdStager {
         }
     }
 
-    __device__ inline void commit(float *buf, float A, float Ip, int tid) const {
+    __device__ inline void commit(float *buf, float A, float Ip, int tid, bool vstar) const {
         using S = BwdStage<DK>;
         float *rows = buf + S::kRows;
 #pragma unroll
@@ -828,7 +845,7 @@ struct BwdStager {
             float *dst = rows + tt * S::kRowFloats + 4 * r0;
 #pragma unroll
             for (int e = 0; e < kPer; ++e) {
-                *(float2 *)(dst + 4 * e) = make_float2(xb[e], xb[e] * xv[e]);
+                *(float2 *)(dst + 4 * e) = make_float2(xb[e], vstar ? xv[e] : xb[e] * xv[e]);
                 dst[4 * e + 2] = xv[e];
             }
         }
@@ -852,8 +869,9 @@ struct BwdStager {
 
 // One token of the replay: the forward update of the lane's entries (the
 // same operations as compute_chunk, so the states are bit-identical).
-template <int DK>
-__device__ inline void bwd_replay_token(const float *buf, int e, float *M, float *I, int row_local, int g) {
+template <int DK, bool IPE>
+__device__ inline void bwd_replay_token(const float *buf, int e, float *M, float *I, int row_local, int g,
+                                        const float *ipe) {
     using LT = LaneTile<DK>;
     using S = BwdStage<DK>;
     const float2 gc = *(const float2 *)(buf + S::kGate + 2 * e);
@@ -868,7 +886,7 @@ __device__ inline void bwd_replay_token(const float *buf, int e, float *M, float
 #pragma unroll
         for (int x = 0; x < LT::kVec; ++x) {
             const int s = m * LT::kVec + x;
-            const float w = fmaf(rb.x, k2[x], gc.y);
+            const float w = fmaf(rb.x, k2[x], IPE ? gc.y * ipe[s] : gc.y);
             I[s] = fmaf(gc.x, I[s], w);
             M[s] = fmaf(gc.x, M[s], rb.y * kk[x]);
         }
@@ -880,16 +898,20 @@ __device__ inline void bwd_replay_token(const float *buf, int e, float *M, float
 // lane's row partials of (gbv, gb, da, dc), and writes the wave's column sums
 // of (gq, gk) for the token to red (2 DK floats), reduce-scattered over the
 // wave's 4 rows: after exchanges with lanes l^32 and l^16, lane (rg, g) holds
-// DK/32 consecutive columns of gq (rg < 2) or gk (rg >= 2).
-template <int DK>
+// DK/32 consecutive columns of gq (rg < 2) or gk (rg >= 2).  With a prior per
+// entry (IPE) dc is sum Ip_ij GI_ij (the staged c is 1 - alpha) and accIp
+// collects the entry's own gradient, sum_t (1 - alpha_t) GI_ij.
+template <int DK, bool IPE>
 __device__ inline void bwd_reverse_token(const float *buf, int e, const float *Mt, const float *It,
                                          const float *Mp, const float *Ipv, float *GM, float *GI,
                                          int row_local, int g, int lane, float *red,
-                                         float &cbv, float &cb, float &s1, float &s2) {
+                                         float &cbv, float &cb, float &s1, float &s2,
+                                         const float *ipe, float *accIp) {
     using LT = LaneTile<DK>;
     using S = BwdStage<DK>;
     constexpr int KC = LT::kCols;
-    const float alpha = buf[S::kGate + 2 * e];
+    const float2 gate_e = *(const float2 *)(buf + S::kGate + 2 * e);
+    const float alpha = gate_e.x;
     const float4 rw = *(const float4 *)(buf + S::kRows + e * S::kRowFloats + 4 * row_local);
     const float b2 = 2.f * rw.x, bv = rw.y, gy = rw.w;
     const float *ct = buf + e * S::kColFloats + LT::col(g, 0, 0);
@@ -916,7 +938,12 @@ __device__ inline void bwd_reverse_token(const float *buf, int e, const float *M
             cb = fmaf(GI[s], k2[x], cb);
             s1 = fmaf(GM[s], Mp[s], s1);
             s1 = fmaf(GI[s], Ipv[s], s1);
-            s2 += GI[s];
+            if (IPE) {
+                s2 = fmaf(ipe[s], GI[s], s2);
+                accIp[s] = fmaf(gate_e.y, GI[s], accIp[s]);
+            } else {
+                s2 += GI[s];
+            }
             GM[s] *= alpha;
             GI[s] *= alpha;
         }
@@ -958,7 +985,7 @@ __device__ inline void bwd_row_sums(const float (&acc)[16], int g, float *dst) {
     dst[((g % 4) * 4 + g / 4) * kRowsPerWG] = r;
 }
 
-template <int DK, typename TIn, typename TG>
+template <int DK, typename TIn, typename TG, bool IPE>
 __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     using LT = LaneTile<DK>;
     using S = BwdStage<DK>;
@@ -983,8 +1010,16 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     const int rg = lane >> 4;
     const int row_local = wave * kRowsPerWave + rg;
     const int row = row0 + row_local;
-    const float A = a.A[h], Ip = a.Ip[h];
+    const float A = a.A[h], Ip = IPE ? 1.f : a.Ip[h];
     const size_t srow = ((size_t)bh * a.dv + row) * DK;
+    float ipe[IPE ? KC : 1], accIp[IPE ? KC : 1];
+    if (IPE) {
+        const float *ip = a.Ip + ((size_t)h * a.dv + row) * DK;
+#pragma unroll
+        for (int m = 0; m < LT::kNVec; ++m) vecf<LT::kVec>::ld(ip + LT::col(g, m, 0), ipe + m * LT::kVec);
+#pragma unroll
+        for (int s = 0; s < KC; ++s) accIp[s] = 0.f;
+    }
 
     float GM[KC], GI[KC];
     const size_t seq0 = (size_t)b * a.T * a.H + h;           // row of (b, 0, h) in [B, T, H]
@@ -1018,7 +1053,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             const size_t tn = (size_t)(a.nsb - 1) * kSB;
             st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
                     gseq + tn * vb_tok, dseq + tn * a.H, a.T - (int)tn, a.H, a.dv, tid);
-            st.commit(lds + ((a.nsb - 1) & 1) * S::kFloats, A, Ip, tid);
+            st.commit(lds + ((a.nsb - 1) & 1) * S::kFloats, A, Ip, tid, a.vstar);
         }
         float ckM[KC], ckI[KC];
         load_pair<KC>(ckb + (size_t)(a.nsb - 1) * ck_stride, tid, ckM, ckI);
@@ -1039,14 +1074,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
 #pragma unroll
             for (int s = 0; s < KC; ++s) { mM[s] = ckM[s]; mI[s] = ckI[s]; }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) bwd_replay_token<DK>(cur, e, mM, mI, row_local, g);
+            for (int e = 0; e < 4; ++e) bwd_replay_token<DK, IPE>(cur, e, mM, mI, row_local, g, ipe);
 #pragma unroll
             for (int e = 4; e < 8; ++e) {
                 const float *pm = e == 4 ? mM : xM[e > 4 ? e - 5 : 0];
                 const float *pi = e == 4 ? mI : xI[e > 4 ? e - 5 : 0];
 #pragma unroll
                 for (int s = 0; s < KC; ++s) { xM[e - 4][s] = pm[s]; xI[e - 4][s] = pi[s]; }
-                bwd_replay_token<DK>(cur, e, xM[e - 4], xI[e - 4], row_local, g);
+                bwd_replay_token<DK, IPE>(cur, e, xM[e - 4], xI[e - 4], row_local, g, ipe);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (sb == a.nsb - 1) {
@@ -1065,10 +1100,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             }
 #pragma unroll
             for (int e = 7; e >= 4; --e)
-                bwd_reverse_token<DK>(cur, e, xM[e - 4], xI[e - 4], e == 4 ? mM : xM[e > 4 ? e - 5 : 0],
+                bwd_reverse_token<DK, IPE>(cur, e, xM[e - 4], xI[e - 4], e == 4 ? mM : xM[e > 4 ? e - 5 : 0],
                                       e == 4 ? mI : xI[e > 4 ? e - 5 : 0],
                                       GM, GI, row_local, g, lane, red + (e * kWaves + wave) * 2 * DK,
-                                      acc[e - 4], acc[e], acc[e + 4], acc[e + 8]);
+                                      acc[e - 4], acc[e], acc[e + 4], acc[e + 8], ipe, accIp);
                 __builtin_amdgcn_sched_barrier(0);
             bwd_row_sums(acc, g, rs + 4 * 4 * kRowsPerWG + row_local);
             // lower half: tokens 0..3
@@ -1078,20 +1113,20 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                 const float *pi = e == 0 ? ckI : xI[e > 0 ? e - 1 : 0];
 #pragma unroll
                 for (int s = 0; s < KC; ++s) { xM[e][s] = pm[s]; xI[e][s] = pi[s]; }
-                bwd_replay_token<DK>(cur, e, xM[e], xI[e], row_local, g);
+                bwd_replay_token<DK, IPE>(cur, e, xM[e], xI[e], row_local, g, ipe);
                 __builtin_amdgcn_sched_barrier(0);
             }
             float nM[KC], nI[KC];
             if (sb > 0) load_pair<KC>(ckb + (size_t)(sb - 1) * ck_stride, tid, nM, nI);
 #pragma unroll
             for (int e = 3; e >= 0; --e)
-                bwd_reverse_token<DK>(cur, e, xM[e], xI[e], e == 0 ? ckM : xM[e > 0 ? e - 1 : 0],
+                bwd_reverse_token<DK, IPE>(cur, e, xM[e], xI[e], e == 0 ? ckM : xM[e > 0 ? e - 1 : 0],
                                       e == 0 ? ckI : xI[e > 0 ? e - 1 : 0],
                                       GM, GI, row_local, g, lane, red + (e * kWaves + wave) * 2 * DK,
-                                      acc[e], acc[e + 4], acc[e + 8], acc[e + 12]);
+                                      acc[e], acc[e + 4], acc[e + 8], acc[e + 12], ipe, accIp);
                 __builtin_amdgcn_sched_barrier(0);
             bwd_row_sums(acc, g, rs + row_local);
-            if (sb > 0) st.commit(lds + ((sb - 1) & 1) * S::kFloats, A, Ip, tid);
+            if (sb > 0) st.commit(lds + ((sb - 1) & 1) * S::kFloats, A, Ip, tid, a.vstar);
             __syncthreads();
             // sums over the 4 waves: this row block's partials of (gq, gk) and (da, dc)
             for (int n = tid; n < kSB * 2 * DK; n += kThreads) {
@@ -1108,9 +1143,11 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                 const float gbv = rs[(e * 4 + 0) * kRowsPerWG + r], gb = rs[(e * 4 + 1) * kRowsPerWG + r];
                 const float4 rw = *(const float4 *)(cur + S::kRows + e * S::kRowFloats + 4 * r);
                 if (t0 + e < a.T) {
+                    // the write is (beta v) k, or v* k: gv is then dL/dv* and beta
+                    // enters only through the importance
                     const size_t o = (seq0 + (size_t)(t0 + e) * a.H) * a.dv + row0 + r;
-                    a.gv[o] = gbv * rw.x;
-                    a.gbeta[o] = fmaf(gbv, rw.z, gb);
+                    a.gv[o] = a.vstar ? gbv : gbv * rw.x;
+                    a.gbeta[o] = a.vstar ? gb : fmaf(gbv, rw.z, gb);
                 }
             } else if (tid < kSB * kRowsPerWG + 2 * kSB) {
                 const int u = tid - kSB * kRowsPerWG, e = u % kSB, qd = u / kSB;
@@ -1134,11 +1171,22 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             for (int x = 0; x < LT::kVec; ++x) {
                 const int s = m * LT::kVec + x;
                 const size_t o = srow + LT::col(g, m, x);
-                const float i0 = a.mu0 ? a.I0[o] : Ip, m0 = a.mu0 ? a.mu0[o] : 0.f;
+                const float i0 = a.mu0 ? a.I0[o] : (IPE ? ipe[s] : Ip), m0 = a.mu0 ? a.mu0[o] : 0.f;
                 const float gI0 = fmaf(GM[s], m0, GI[s]);
                 if (a.gmu0) a.gmu0[o] = GM[s] * i0;
                 if (a.gI0) a.gI0[o] = gI0;
                 GI[s] = gI0;
+            }
+    }
+    if (IPE) {
+        // this sequence's gradient of the per-entry prior (the default start
+        // state I0 = I_prior adds gI0 entry by entry)
+#pragma unroll
+        for (int m = 0; m < LT::kNVec; ++m)
+#pragma unroll
+            for (int x = 0; x < LT::kVec; ++x) {
+                const int s = m * LT::kVec + x;
+                a.pip[srow + LT::col(g, m, x)] = a.mu0 ? accIp[s] : accIp[s] + GI[s];
             }
     }
     // this row block's sum of gI0 (the default start state I0 = I_prior feeds gI_prior)
@@ -1172,13 +1220,14 @@ __global__ __launch_bounds__(256) void bwd_qk_kernel(const float *pqk, float *gq
 
 // gdt per token and per-sequence sums of the gate gradients: one block per
 // (b, h), tokens strided over its threads.
+// (with a prior per entry dc already carries the prior: Ip enters as 1)
 __global__ __launch_bounds__(256) void bwd_gate_kernel(const float *ps, const void *dt, int dt_bf16,
-                                                        const float *A, const float *Ip, float *gdt,
+                                                        const float *A, const float *Ip, int ipe, float *gdt,
                                                         float *gabh, float *gibh, int B, int T, int H, int nrb) {
     __shared__ float sh[2][4];
     const int bh = blockIdx.x, b = bh / H, h = bh % H;
     const size_t bth = (size_t)B * T * H;
-    const float Ah = A[h], Iph = Ip[h];
+    const float Ah = A[h], Iph = ipe ? 1.f : Ip[h];
     float accA = 0.f, accI = 0.f;
     for (int t = threadIdx.x; t < T; t += 256) {
         const size_t row = ((size_t)b * T + t) * H + h;
@@ -1209,9 +1258,11 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const float *ps, const vo
 }
 
 // gA, gI_prior per head: sums over the batch (plus the start state's share
-// when it defaults to I_prior).
+// when it defaults to I_prior).  With a prior per entry only gA is written
+// here (gI_prior comes from bwd_prior_kernel).
 __global__ __launch_bounds__(64) void bwd_head_kernel(const float *gabh, const float *gibh, const float *pI0,
-                                                       float *gA, float *gIp, int B, int H, int nrb, int dflt) {
+                                                       float *gA, float *gIp, int B, int H, int nrb, int dflt,
+                                                       int ipe) {
     const int h = blockIdx.x * 64 + threadIdx.x;
     if (h >= H) return;
     float sa = 0.f, si = 0.f;
@@ -1222,7 +1273,20 @@ __global__ __launch_bounds__(64) void bwd_head_kernel(const float *gabh, const f
             for (int r = 0; r < nrb; ++r) si += pI0[((size_t)b * H + h) * nrb + r];
     }
     gA[h] = sa;
-    gIp[h] = si;
+    if (!ipe) gIp[h] = si;
+}
+
+// Per-entry prior: gI_prior[h, i, j] = sum over the batch of the sequences'
+// gradients (4 entries per thread).
+__global__ __launch_bounds__(256) void bwd_prior_kernel(const float *pip, float *gIp, int B, size_t per_b) {
+    const size_t n4 = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (4 * n4 >= per_b) return;
+    float4 acc = *(const float4 *)(pip + 4 * n4);
+    for (int b = 1; b < B; ++b) {
+        const float4 x = *(const float4 *)(pip + (size_t)b * per_b + 4 * n4);
+        acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+    }
+    *(float4 *)(gIp + 4 * n4) = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -1621,6 +1685,8 @@ struct StepArgs {
     void *y;
     int B, H, dv;
     long long rows;    // B * H * dv
+    int vstar;         // 1: v holds beta . v
+    int ipe;           // 1: I_prior is [H, dv, dk]
 };
 
 constexpr int kStepThreads = 256;
@@ -1658,8 +1724,16 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) { qq[e] = io<TIn>::to_f32(qp[e]); kk[e] = io<TIn>::to_f32(kp[e]); }
     const float bt = io<TIn>::to_f32(((const TIn *)a.beta)[bh * a.dv + i]);
-    const float bv = bt * io<TIn>::to_f32(((const TIn *)a.v)[bh * a.dv + i]);
-    const float2 gc = gate(a.A[h], io<TIn>::to_f32(((const TIn *)a.dt)[bh]), a.Ip[h]);
+    const float vv = io<TIn>::to_f32(((const TIn *)a.v)[bh * a.dv + i]);
+    const float bv = a.vstar ? vv : bt * vv;
+    const float2 gc = gate(a.A[h], io<TIn>::to_f32(((const TIn *)a.dt)[bh]), a.ipe ? 1.f : a.Ip[h]);
+    // c per entry: (1 - alpha) I_prior[h] or (1 - alpha) I_prior[h, i, j]
+    float cc[4] = {gc.y, gc.y, gc.y, gc.y};
+    if (a.ipe) {
+        const f32x4 ip4 = *(const f32x4 *)(a.Ip + ((size_t)h * a.dv + i) * DK + j0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cc[e] = gc.y * ip4[e];
+    }
 
     f32x4 *mup = (f32x4 *)(a.mu + r * DK + j0);
     f32x4 *Ipp = (f32x4 *)(a.I + r * DK + j0);
@@ -1670,7 +1744,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
     float mun[4], In[4], acc = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        In[e] = fmaf(gc.x, Io[e], fmaf(bt, kk[e] * kk[e], gc.y));
+        In[e] = fmaf(gc.x, Io[e], fmaf(bt, kk[e] * kk[e], cc[e]));
         const float num = fmaf(gc.x * Io[e], mu[e], bv * kk[e]);   // alpha I mu + beta v k
         mun[e] = num / In[e];
         acc = fmaf(mun[e], qq[e], acc);
@@ -1692,14 +1766,18 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
 
 inline bool aligned_to(const void *p, size_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
 inline bool head_ok(int d) { return d == 32 || d == 64 || d == 128; }
+// value rows run in blocks of 16 (64 on the frozen path), so d_v may be any
+// such multiple up to 1024 (d_v = 2 d_k, the pages' value expansion, included)
+inline bool dv_ok(int d) { return d >= 16 && d <= 1024 && d % 16 == 0; }
+constexpr int kFlagsKnown = PALIMPSA_VSTAR | PALIMPSA_PRIOR_PER_ENTRY;
 inline bool dtype_ok(int t) { return t == PALIMPSA_F32 || t == PALIMPSA_BF16; }
 
-template <int DK, int C, typename TIn, typename TOut, int MODE>
+template <int DK, int C, typename TIn, typename TOut, int MODE, bool IPE>
 palimpsa_status launch_pass(FwdArgs a, int nseg_launched, hipStream_t s) {
     a.nwg = a.nwg_seg * nseg_launched;
     a.xcd_remap = (a.nwg % 8 == 0) ? 1 : 0;
     const size_t lds = fwd_lds_bytes<DK, C>();
-    auto kern = fwd_chunked_kernel<DK, C, TIn, TOut, MODE>;
+    auto kern = fwd_chunked_kernel<DK, C, TIn, TOut, MODE, IPE>;
     if (lds > 64 * 1024) {
         if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
             return PALIMPSA_ERR_HIP;
@@ -1710,30 +1788,34 @@ palimpsa_status launch_pass(FwdArgs a, int nseg_launched, hipStream_t s) {
 }
 
 // Summary pass (segments 0..nseg-2) then the replay pass (all segments).
-template <int DK, int C, typename TIn, typename TOut>
+// (the summary pass does not read the prior, so it has no IPE variant)
+template <int DK, int C, typename TIn, typename TOut, bool IPE>
 palimpsa_status launch_fwd_t(const FwdArgs &a, hipStream_t s) {
     if (a.nseg > 1) {
-        const palimpsa_status st = launch_pass<DK, C, TIn, TOut, kSummary>(a, a.nseg - 1, s);
+        const palimpsa_status st = launch_pass<DK, C, TIn, TOut, kSummary, false>(a, a.nseg - 1, s);
         if (st != PALIMPSA_OK) return st;
     }
-    return launch_pass<DK, C, TIn, TOut, kReplay>(a, a.nseg, s);
+    return launch_pass<DK, C, TIn, TOut, kReplay, IPE>(a, a.nseg, s);
 }
 
-template <int DK, typename TIn, typename TOut>
+template <int DK, typename TIn, typename TOut, bool IPE>
 palimpsa_status launch_fwd_c(const FwdArgs &a, int C, hipStream_t s) {
     switch (C) {
-    case 16: return launch_fwd_t<DK, 16, TIn, TOut>(a, s);
-    case 32: return launch_fwd_t<DK, 32, TIn, TOut>(a, s);
-    default: return launch_fwd_t<DK, 64, TIn, TOut>(a, s);
+    case 16: return launch_fwd_t<DK, 16, TIn, TOut, IPE>(a, s);
+    case 32: return launch_fwd_t<DK, 32, TIn, TOut, IPE>(a, s);
+    default: return launch_fwd_t<DK, 64, TIn, TOut, IPE>(a, s);
     }
 }
 
 template <typename TIn, typename TOut>
-palimpsa_status launch_fwd_d(const FwdArgs &a, int dk, int C, hipStream_t s) {
-    switch (dk) {
-    case 32: return launch_fwd_c<32, TIn, TOut>(a, C, s);
-    case 64: return launch_fwd_c<64, TIn, TOut>(a, C, s);
-    default: return launch_fwd_c<128, TIn, TOut>(a, C, s);
+palimpsa_status launch_fwd_d(const FwdArgs &a, int dk, int C, bool ipe, hipStream_t s) {
+    switch (dk * 2 + (ipe ? 1 : 0)) {
+    case 64: return launch_fwd_c<32, TIn, TOut, false>(a, C, s);
+    case 65: return launch_fwd_c<32, TIn, TOut, true>(a, C, s);
+    case 128: return launch_fwd_c<64, TIn, TOut, false>(a, C, s);
+    case 129: return launch_fwd_c<64, TIn, TOut, true>(a, C, s);
+    case 257: return launch_fwd_c<128, TIn, TOut, true>(a, C, s);
+    default: return launch_fwd_c<128, TIn, TOut, false>(a, C, s);
     }
 }
 
@@ -1821,11 +1903,12 @@ palimpsa_status launch_frozen(const FrozenArgs &a, hipStream_t s) {
 //   ps    [dv/16][B*H][T][2]                row-block partials of (da, dc)
 //   gabh, gibh [B*H]                        per-sequence gate gradient sums
 //   pI0   [B*H][dv/16]                      row-block sums of gI0
+//   pip   [B*H][dv][dk]                     per-entry prior only: per-sequence gI_prior
 struct BwdWs {
-    float *ck, *pqk, *ps, *gabh, *gibh, *pI0;
+    float *ck, *pqk, *ps, *gabh, *gibh, *pI0, *pip;
     size_t bytes;
 };
-BwdWs plan_bwd_ws(void *base, int B, int T, int H, int dk, int dv) {
+BwdWs plan_bwd_ws(void *base, int B, int T, int H, int dk, int dv, bool ipe) {
     const size_t nsb = (size_t)(T + kSB - 1) / kSB, nrb = (size_t)dv / kRowsPerWG;
     const size_t bh = (size_t)B * H, bth = bh * T;
     size_t off = 0;
@@ -1836,23 +1919,25 @@ BwdWs plan_bwd_ws(void *base, int B, int T, int H, int dk, int dv) {
     };
     const size_t o_ck = take(bh * nsb * 2 * dv * dk), o_pqk = take(nrb * bth * 2 * dk), o_ps = take(nrb * bth * 2);
     const size_t o_ga = take(bh), o_gi = take(bh), o_pi = take(bh * nrb);
+    const size_t o_pip = ipe ? take(bh * dv * dk) : off;
     BwdWs w;
     char *c = (char *)base;
     w.ck = (float *)(c + o_ck); w.pqk = (float *)(c + o_pqk); w.ps = (float *)(c + o_ps);
     w.gabh = (float *)(c + o_ga); w.gibh = (float *)(c + o_gi); w.pI0 = (float *)(c + o_pi);
+    w.pip = ipe ? (float *)(c + o_pip) : nullptr;
     w.bytes = off;
     return w;
 }
 
-template <int DK, typename TIn, typename TG>
+template <int DK, typename TIn, typename TG, bool IPE>
 palimpsa_status launch_bwd_t(const FwdArgs &fa, const BwdArgs &ba, const BwdWs &w, float *gq, float *gk,
                              float *gdt, float *gA, float *gIp, int dt_bf16, hipStream_t s) {
     if (ba.T > 0) {
-        const palimpsa_status st = launch_pass<DK, 16, TIn, float, kCheckpoint>(fa, 1, s);
+        const palimpsa_status st = launch_pass<DK, 16, TIn, float, kCheckpoint, IPE>(fa, 1, s);
         if (st != PALIMPSA_OK) return st;
     }
     const size_t lds = (size_t)BwdStage<DK>::kTotal * sizeof(float);
-    auto kern = bwd_kernel<DK, TIn, TG>;
+    auto kern = bwd_kernel<DK, TIn, TG, IPE>;
     if (lds > 64 * 1024 &&
         hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return PALIMPSA_ERR_HIP;
@@ -1866,19 +1951,28 @@ palimpsa_status launch_bwd_t(const FwdArgs &fa, const BwdArgs &ba, const BwdWs &
                            (const float *)w.pqk, gq, gk, bth, nrb);
     }
     hipLaunchKernelGGL(bwd_gate_kernel, dim3(ba.B * ba.H), dim3(256), 0, s, (const float *)w.ps, ba.dt, dt_bf16,
-                       ba.A, ba.Ip, gdt, w.gabh, w.gibh, ba.B, ba.T, ba.H, nrb);
+                       ba.A, ba.Ip, IPE ? 1 : 0, gdt, w.gabh, w.gibh, ba.B, ba.T, ba.H, nrb);
     hipLaunchKernelGGL(bwd_head_kernel, dim3((ba.H + 63) / 64), dim3(64), 0, s, (const float *)w.gabh,
-                       (const float *)w.gibh, (const float *)w.pI0, gA, gIp, ba.B, ba.H, nrb, ba.mu0 ? 0 : 1);
+                       (const float *)w.gibh, (const float *)w.pI0, gA, gIp, ba.B, ba.H, nrb, ba.mu0 ? 0 : 1,
+                       IPE ? 1 : 0);
+    if (IPE) {
+        const size_t per_b = (size_t)ba.H * ba.dv * DK;
+        hipLaunchKernelGGL(bwd_prior_kernel, dim3((unsigned)((per_b / 4 + 255) / 256)), dim3(256), 0, s,
+                           (const float *)w.pip, gIp, ba.B, per_b);
+    }
     return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
 }
 
 template <typename TIn, typename TG>
-palimpsa_status launch_bwd_d(int dk, const FwdArgs &fa, const BwdArgs &ba, const BwdWs &w, float *gq, float *gk,
-                             float *gdt, float *gA, float *gIp, int dt_bf16, hipStream_t s) {
-    switch (dk) {
-    case 32: return launch_bwd_t<32, TIn, TG>(fa, ba, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
-    case 64: return launch_bwd_t<64, TIn, TG>(fa, ba, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
-    default: return launch_bwd_t<128, TIn, TG>(fa, ba, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+palimpsa_status launch_bwd_d(int dk, bool ipe, const FwdArgs &fa, const BwdArgs &ba, const BwdWs &w, float *gq,
+                             float *gk, float *gdt, float *gA, float *gIp, int dt_bf16, hipStream_t s) {
+    switch (dk * 2 + (ipe ? 1 : 0)) {
+    case 64: return launch_bwd_t<32, TIn, TG, false>(fa, ba, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    case 65: return launch_bwd_t<32, TIn, TG, true>(fa, ba, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    case 128: return launch_bwd_t<64, TIn, TG, false>(fa, ba, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    case 129: return launch_bwd_t<64, TIn, TG, true>(fa, ba, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    case 257: return launch_bwd_t<128, TIn, TG, true>(fa, ba, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    default: return launch_bwd_t<128, TIn, TG, false>(fa, ba, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
     }
 }
 
@@ -1886,9 +1980,9 @@ palimpsa_status launch_bwd_d(int dk, const FwdArgs &fa, const BwdArgs &ba, const
 
 extern "C" {
 
-size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv) {
-    if (B <= 0 || H <= 0 || T < 0 || !head_ok(dk) || !head_ok(dv)) return 0;
-    return plan_bwd_ws(nullptr, B, T, H, dk, dv).bytes;
+size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv, int flags) {
+    if (B <= 0 || H <= 0 || T < 0 || !head_ok(dk) || !dv_ok(dv) || (flags & ~kFlagsKnown)) return 0;
+    return plan_bwd_ws(nullptr, B, T, H, dk, dv, (flags & PALIMPSA_PRIOR_PER_ENTRY) != 0).bytes;
 }
 
 palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const void *beta, const void *dt,
@@ -1897,9 +1991,9 @@ palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const 
                              float *gq, float *gk, float *gv, float *gbeta, float *gdt,
                              float *gA, float *gIp, float *gmu0, float *gI0,
                              int B, int T, int H, int dk, int dv,
-                             palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype,
+                             palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype, int flags,
                              void *workspace, size_t workspace_bytes, void *stream) {
-    if (!A || !I_prior || !gA || !gIp || !workspace)
+    if (!A || !I_prior || !gA || !gIp || !workspace || (flags & ~kFlagsKnown))
         return PALIMPSA_ERR_INVALID_ARG;
     if (T > 0 && (!q || !k || !v || !beta || !dt || !gy || !gq || !gk || !gv || !gbeta || !gdt))
         return PALIMPSA_ERR_INVALID_ARG;
@@ -1907,9 +2001,11 @@ palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const 
         return PALIMPSA_ERR_INVALID_ARG;
     if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || !dtype_ok(in_dtype) || !dtype_ok(gy_dtype))
         return PALIMPSA_ERR_INVALID_ARG;
-    if (!head_ok(dk) || !head_ok(dv))
+    if (!head_ok(dk) || !dv_ok(dv))
         return PALIMPSA_ERR_UNSUPPORTED;
-    const void *vec_ptrs[] = {q, k, v, beta, gy, mu0, I0, gmuT, gIT, gq, gk, gmu0, gI0, workspace};
+    const bool ipe = (flags & PALIMPSA_PRIOR_PER_ENTRY) != 0;
+    const void *vec_ptrs[] = {q, k, v, beta, gy, mu0, I0, gmuT, gIT, gq, gk, gmu0, gI0, workspace,
+                              ipe ? (const void *)I_prior : nullptr, ipe ? (const void *)gIp : nullptr};
     for (const void *p : vec_ptrs)
         if (p && !aligned_to(p, 16)) return PALIMPSA_ERR_ALIGNMENT;
     const size_t in_sz = in_dtype == PALIMPSA_BF16 ? 2 : 4;
@@ -1921,7 +2017,7 @@ palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const 
     if (nwg > 0x7fffffffLL || (long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 46) ||
         64LL * H * (dk > dv ? dk : dv) >= (1LL << 31) || (long long)B * H * 2 > 0x7fffffffLL)
         return PALIMPSA_ERR_UNSUPPORTED;
-    const BwdWs w = plan_bwd_ws(workspace, B, T, H, dk, dv);
+    const BwdWs w = plan_bwd_ws(workspace, B, T, H, dk, dv, ipe);
     if (workspace_bytes < w.bytes) return PALIMPSA_ERR_INVALID_ARG;
 
     FwdArgs fa = {};
@@ -1931,22 +2027,24 @@ palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const 
     fa.nwg = (int)nwg; fa.xcd_remap = (nwg % 8 == 0) ? 1 : 0; fa.nwg_seg = (int)nwg;
     fa.seg_len = T > 0 ? T : 1; fa.nseg = 1;
     fa.ck = w.ck; fa.nsb = (T + kSB - 1) / kSB;
+    fa.vstar = (flags & PALIMPSA_VSTAR) ? 1 : 0;
 
     BwdArgs ba = {};
     ba.q = q; ba.k = k; ba.v = v; ba.beta = beta; ba.dt = dt; ba.gy = gy;
     ba.A = A; ba.Ip = I_prior; ba.mu0 = mu0; ba.I0 = I0; ba.gmuT = gmuT; ba.gIT = gIT;
     ba.gv = gv; ba.gbeta = gbeta; ba.gmu0 = gmu0; ba.gI0 = gI0;
-    ba.ck = w.ck; ba.pqk = w.pqk; ba.ps = w.ps; ba.pI0 = w.pI0;
+    ba.ck = w.ck; ba.pqk = w.pqk; ba.ps = w.ps; ba.pI0 = w.pI0; ba.pip = w.pip;
+    ba.vstar = fa.vstar;
     ba.B = B; ba.T = T; ba.H = H; ba.dv = dv; ba.nsb = fa.nsb;
     ba.nwg = (int)nwg; ba.xcd_remap = fa.xcd_remap;
 
     hipStream_t s = (hipStream_t)stream;
     const bool bf_in = in_dtype == PALIMPSA_BF16, bf_gy = gy_dtype == PALIMPSA_BF16;
     const int dtb = bf_in ? 1 : 0;
-    if (bf_in && bf_gy) return launch_bwd_d<bf16_t, bf16_t>(dk, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
-    if (bf_in) return launch_bwd_d<bf16_t, float>(dk, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
-    if (bf_gy) return launch_bwd_d<float, bf16_t>(dk, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
-    return launch_bwd_d<float, float>(dk, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
+    if (bf_in && bf_gy) return launch_bwd_d<bf16_t, bf16_t>(dk, ipe, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
+    if (bf_in) return launch_bwd_d<bf16_t, float>(dk, ipe, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
+    if (bf_gy) return launch_bwd_d<float, bf16_t>(dk, ipe, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
+    return launch_bwd_d<float, float>(dk, ipe, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
 }
 
 palimpsa_status palimpsa_fwd_frozen(const void *q, const void *k, const void *v,
@@ -1961,7 +2059,7 @@ palimpsa_status palimpsa_fwd_frozen(const void *q, const void *k, const void *v,
         return PALIMPSA_ERR_INVALID_ARG;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
         return PALIMPSA_ERR_INVALID_ARG;
-    if (in_dtype != PALIMPSA_BF16 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+    if (in_dtype != PALIMPSA_BF16 || (dk != 64 && dk != 128) || !dv_ok(dv) || dv % kFzRows != 0)
         return PALIMPSA_ERR_UNSUPPORTED;
     const void *vec_ptrs[] = {q, k, v, beta, mu0, muT, y};
     for (const void *p : vec_ptrs)
@@ -1983,7 +2081,7 @@ palimpsa_status palimpsa_fwd_frozen(const void *q, const void *k, const void *v,
 
 
 size_t palimpsa_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segments) {
-    if (B <= 0 || H <= 0 || T < 0 || !head_ok(dk) || !head_ok(dv) || segments < 0) return 0;
+    if (B <= 0 || H <= 0 || T < 0 || !head_ok(dk) || !dv_ok(dv) || segments < 0) return 0;
     return plan_segments(B, T, H, dk, dv, segments, device_cus()).ws_bytes;
 }
 
@@ -1993,9 +2091,9 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
                                      const float *mu0, const float *I0,
                                      void *y, float *muT, float *IT,
                                      int B, int T, int H, int dk, int dv, int chunk, int segments,
-                                     palimpsa_dtype in_dtype, palimpsa_dtype out_dtype,
+                                     palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
                                      void *workspace, size_t workspace_bytes, void *stream) {
-    if (!A || !I_prior || (T > 0 && (!q || !k || !v || !beta || !dt || !y)))
+    if (!A || !I_prior || (T > 0 && (!q || !k || !v || !beta || !dt || !y)) || (flags & ~kFlagsKnown))
         return PALIMPSA_ERR_INVALID_ARG;
     if ((mu0 == nullptr) != (I0 == nullptr) || (muT == nullptr) != (IT == nullptr))
         return PALIMPSA_ERR_INVALID_ARG;
@@ -2007,10 +2105,12 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
         return PALIMPSA_ERR_INVALID_ARG;
     if (segments < 0 || segments > 64 || (workspace_bytes > 0 && !workspace))
         return PALIMPSA_ERR_INVALID_ARG;
-    if (!head_ok(dk) || !head_ok(dv))
+    if (!head_ok(dk) || !dv_ok(dv))
         return PALIMPSA_ERR_UNSUPPORTED;
-    // 128-bit accesses: q, k, v, beta, the state arrays and the workspace; element-wise: the rest
-    const void *vec_ptrs[] = {q, k, v, beta, mu0, I0, muT, IT, workspace};
+    const bool ipe = (flags & PALIMPSA_PRIOR_PER_ENTRY) != 0;
+    // 128-bit accesses: q, k, v, beta, the state arrays (and a per-entry prior) and
+    // the workspace; element-wise: the rest
+    const void *vec_ptrs[] = {q, k, v, beta, mu0, I0, muT, IT, workspace, ipe ? (const void *)I_prior : nullptr};
     for (const void *p : vec_ptrs)
         if (p && !aligned_to(p, 16)) return PALIMPSA_ERR_ALIGNMENT;
     const size_t in_sz = in_dtype == PALIMPSA_BF16 ? 2 : 4, out_sz = out_dtype == PALIMPSA_BF16 ? 2 : 4;
@@ -2030,6 +2130,8 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
     a.nwg = (int)nwg;
     a.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
     a.nwg_seg = (int)nwg;
+    a.vstar = (flags & PALIMPSA_VSTAR) ? 1 : 0;
+    a.ck = nullptr; a.nsb = 0;
 
     if (T == 0 && !muT) return PALIMPSA_OK;   // nothing to compute or write
     SegPlan plan = plan_segments(B, T, H, dk, dv, segments, device_cus());
@@ -2044,10 +2146,10 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
     const int C = pick_chunk(chunk, dk, nwg * plan.nseg, device_lds_max());
     hipStream_t s = (hipStream_t)stream;
     const bool bf_in = in_dtype == PALIMPSA_BF16, bf_out = out_dtype == PALIMPSA_BF16;
-    if (bf_in && bf_out) return launch_fwd_d<bf16_t, bf16_t>(a, dk, C, s);
-    if (bf_in) return launch_fwd_d<bf16_t, float>(a, dk, C, s);
-    if (bf_out) return launch_fwd_d<float, bf16_t>(a, dk, C, s);
-    return launch_fwd_d<float, float>(a, dk, C, s);
+    if (bf_in && bf_out) return launch_fwd_d<bf16_t, bf16_t>(a, dk, C, ipe, s);
+    if (bf_in) return launch_fwd_d<bf16_t, float>(a, dk, C, ipe, s);
+    if (bf_out) return launch_fwd_d<float, bf16_t>(a, dk, C, ipe, s);
+    return launch_fwd_d<float, float>(a, dk, C, ipe, s);
 }
 
 palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
@@ -2055,18 +2157,20 @@ palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
                               const float *A, const float *I_prior,
                               float *mu, float *I, void *y,
                               int B, int H, int dk, int dv,
-                              palimpsa_dtype in_dtype, palimpsa_dtype out_dtype,
+                              palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
                               void *stream) {
-    if (!q || !k || !v || !beta || !dt || !A || !I_prior || !mu || !I || !y)
+    if (!q || !k || !v || !beta || !dt || !A || !I_prior || !mu || !I || !y || (flags & ~kFlagsKnown))
         return PALIMPSA_ERR_INVALID_ARG;
     if (B <= 0 || H <= 0 || dk <= 0 || dv <= 0)
         return PALIMPSA_ERR_INVALID_ARG;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
         return PALIMPSA_ERR_INVALID_ARG;
-    if (!head_ok(dk) || !head_ok(dv))
+    if (!head_ok(dk) || !dv_ok(dv))
         return PALIMPSA_ERR_UNSUPPORTED;
-    // 128-bit accesses: the state; element-wise: the rest
-    if (!aligned_to(mu, 16) || !aligned_to(I, 16)) return PALIMPSA_ERR_ALIGNMENT;
+    const bool ipe = (flags & PALIMPSA_PRIOR_PER_ENTRY) != 0;
+    // 128-bit accesses: the state (and a per-entry prior); element-wise: the rest
+    if (!aligned_to(mu, 16) || !aligned_to(I, 16) || (ipe && !aligned_to(I_prior, 16)))
+        return PALIMPSA_ERR_ALIGNMENT;
     const size_t in_sz = in_dtype == PALIMPSA_BF16 ? 2 : 4, out_sz = out_dtype == PALIMPSA_BF16 ? 2 : 4;
     const void *in_ptrs[] = {q, k, v, beta, dt};
     for (const void *p : in_ptrs)
@@ -2080,6 +2184,8 @@ palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.dt = dt;
     a.A = A; a.Ip = I_prior; a.mu = mu; a.I = I; a.y = y;
     a.B = B; a.H = H; a.dv = dv; a.rows = rows;
+    a.vstar = (flags & PALIMPSA_VSTAR) ? 1 : 0;
+    a.ipe = ipe ? 1 : 0;
     const int rows_per_block = kStepThreads / (dk / 4);
     const long long blocks = (rows + rows_per_block - 1) / rows_per_block;
     if (blocks > 0x7fffffffLL) return PALIMPSA_ERR_UNSUPPORTED;

@@ -39,7 +39,24 @@
  *  - Data preconditions that are NOT checked (they live in device memory):
  *    A >= 0 and finite, I_prior > 0, beta >= 0, dt >= 0, I0 > 0, all inputs
  *    finite.  Violations give unspecified values, never a fault.
- *  - Supported head sizes: dk, dv in {32, 64, 128}.
+ *  - Supported head sizes: dk in {32, 64, 128}; dv any multiple of 16 from
+ *    16 to 1024 (so the value expansion dv = 2 dk of the pages' model is
+ *    covered).  The frozen path's limits are stated at its declaration.
+ *  - Options (`flags`, a bit mask of palimpsa_flags) of the exact forward,
+ *    the decode step and the backward:
+ *      PALIMPSA_VSTAR            v holds v* = beta . v, the write itself (the
+ *                                slides' frame on the Mamba2 limit makes v*
+ *                                the layer's input); beta still scales k^2 in
+ *                                the importance.  The backward's gv is then
+ *                                dL/dv*, and gbeta has only the importance term.
+ *      PALIMPSA_PRIOR_PER_ENTRY  I_prior is [H, dv, dk] float32, one prior
+ *                                precision per state entry (the reading notes'
+ *                                symbol table allows a prior of the state's
+ *                                shape); 16-byte aligned.  The prior term is
+ *                                (1 - alpha_t) I_prior[h, i, j]; the default
+ *                                start state is I0 = I_prior entry by entry;
+ *                                the backward's gIp is [H, dv, dk].
+ *    Unknown bits are PALIMPSA_ERR_INVALID_ARG.
  */
 #ifndef PALIMPSA_H
 #define PALIMPSA_H
@@ -63,6 +80,11 @@ typedef enum {
     PALIMPSA_BF16 = 1
 } palimpsa_dtype;
 
+typedef enum {
+    PALIMPSA_VSTAR = 1,
+    PALIMPSA_PRIOR_PER_ENTRY = 2
+} palimpsa_flags;
+
 /*
  * Chunked forward over a whole sequence (training / prefill).
  *
@@ -71,6 +93,7 @@ typedef enum {
  *   dt        [B, T, H]      in_dtype
  *   A         [H]            float32, per-head decay rate
  *   I_prior   [H]            float32, per-head prior precision
+ *             ([H, dv, dk] with PALIMPSA_PRIOR_PER_ENTRY)
  *   mu0, I0   [B, H, dv, dk] float32 initial state; both NULL means
  *                            mu0 = 0 and I0 = I_prior (one NULL alone is an error)
  *   y         [B, T, H, dv]  out_dtype, every token's readout
@@ -100,6 +123,7 @@ typedef enum {
  *             one pass; an explicit segments >= 2 without enough workspace is
  *             PALIMPSA_ERR_INVALID_ARG.  Contents are overwritten; calls that
  *             share a workspace must not overlap.
+ *   flags     palimpsa_flags bits (see above), or 0.
  *
  * T == 0 is valid: y is empty and the state is copied through (or, with both
  * mu0 and I0 NULL, set to mu = 0, I = I_prior); the per-token pointers q, k,
@@ -113,7 +137,7 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
                                      void *y, float *muT, float *IT,
                                      int B, int T, int H, int dk, int dv, int chunk,
                                      int segments, palimpsa_dtype in_dtype,
-                                     palimpsa_dtype out_dtype, void *workspace,
+                                     palimpsa_dtype out_dtype, int flags, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
 /*
@@ -144,7 +168,10 @@ size_t palimpsa_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segm
  *   y         [B, T, H, dv]  out_dtype
  *   muT       [B, H, dv, dk] float32 final mean, or NULL to skip
  *
- * dk, dv in {64, 128}; other sizes or fp32 inputs return PALIMPSA_ERR_UNSUPPORTED.
+ * dk in {64, 128}, dv a multiple of 64 up to 1024; other sizes or fp32
+ * inputs return PALIMPSA_ERR_UNSUPPORTED.  (A prior per state entry would
+ * make the write per entry instead of an outer product, so this path takes
+ * the per-head prior only.)
  * q, k, v, beta, mu0, muT and y must be 16-byte aligned.  Rounding: operands
  * of the products are bf16, so y carries about 2^-8 relative error.
  */
@@ -162,16 +189,17 @@ palimpsa_status palimpsa_fwd_frozen(const void *q, const void *k, const void *v,
  *   q, k      [B, H, dk]     in_dtype
  *   v, beta   [B, H, dv]     in_dtype
  *   dt        [B, H]         in_dtype
- *   A, I_prior [H]           float32
+ *   A, I_prior [H]           float32 (I_prior [H, dv, dk] with PALIMPSA_PRIOR_PER_ENTRY)
  *   mu, I     [B, H, dv, dk] float32, read and overwritten with the new state
  *   y         [B, H, dv]     out_dtype
+ *   flags     palimpsa_flags bits, or 0
  */
 palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
                               const void *beta, const void *dt,
                               const float *A, const float *I_prior,
                               float *mu, float *I, void *y,
                               int B, int H, int dk, int dv,
-                              palimpsa_dtype in_dtype, palimpsa_dtype out_dtype,
+                              palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
                               void *stream);
 
 /*
@@ -201,7 +229,11 @@ palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
  *   workspace at least palimpsa_bwd_workspace_size(B, T, H, dk, dv) bytes,
  *             16-byte aligned, caller-owned; contents on entry are ignored
  *
- * dk, dv in {32, 64, 128} (else PALIMPSA_ERR_UNSUPPORTED).  q, k, v, beta,
+ * flags: palimpsa_flags bits (the options change gv, gbeta and the shape of
+ * gIp as stated above); the workspace size depends on them.
+ *
+ * dk in {32, 64, 128}, dv a multiple of 16 up to 1024 (else
+ * PALIMPSA_ERR_UNSUPPORTED).  q, k, v, beta,
  * gy, the state arrays, gq, gk and the workspace must be 16-byte aligned;
  * the other pointers naturally aligned.  At T = 0 the per-token pointers may
  * be NULL.  Launches are asynchronous on `stream`; calls that share a
@@ -215,16 +247,17 @@ palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const 
                              float *gq, float *gk, float *gv, float *gbeta, float *gdt,
                              float *gA, float *gIp, float *gmu0, float *gI0,
                              int B, int T, int H, int dk, int dv,
-                             palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype,
+                             palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype, int flags,
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Bytes of workspace palimpsa_bwd needs: the checkpoints (8 B per state
  * entry every 8 tokens: B H ceil(T/8) dv dk 8 bytes) plus the per-row-block
- * partials of gq, gk (dv/16 x B T H x 2 dk x 4 bytes) and small sums.
- * Returns 0 for sizes palimpsa_bwd would reject.
+ * partials of gq, gk (dv/16 x B T H x 2 dk x 4 bytes) and small sums; with
+ * PALIMPSA_PRIOR_PER_ENTRY also each sequence's gIp (B H dv dk x 4 bytes).
+ * Returns 0 for sizes or flags palimpsa_bwd would reject.
  */
-size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv);
+size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv, int flags);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *palimpsa_status_string(int status);

@@ -59,10 +59,10 @@ FAKE = 0x10000       # 16-byte aligned host address, never dereferenced
 def _fwd_args(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dt=FAKE, A=FAKE, Ip=FAKE, mu0=None, I0=None,
              y=FAKE, muT=FAKE, IT=FAKE, B=2, T=8, H=3, dk=64, dv=64, chunk=0, segments=0,
-             ind=1, outd=1, ws=None, wsb=0, stream=None)
+             ind=1, outd=1, flags=0, ws=None, wsb=0, stream=None)
     a.update(over)
     return [a[n] for n in ("q", "k", "v", "beta", "dt", "A", "Ip", "mu0", "I0", "y", "muT", "IT",
-                           "B", "T", "H", "dk", "dv", "chunk", "segments", "ind", "outd",
+                           "B", "T", "H", "dk", "dv", "chunk", "segments", "ind", "outd", "flags",
                            "ws", "wsb", "stream")]
 
 
@@ -72,7 +72,8 @@ FWD_CASES = [
     (dict(Ip=None), 1), (dict(y=None), 1), (dict(mu0=FAKE), 1), (dict(I0=FAKE), 1),
     (dict(muT=None), 1), (dict(IT=None), 1), (dict(B=0), 1), (dict(H=0), 1), (dict(T=-1), 1),
     (dict(dk=0), 1), (dict(ind=2), 1), (dict(outd=-1), 1), (dict(chunk=12), 1),
-    (dict(chunk=128), 1), (dict(dk=48), 2), (dict(dv=256), 2), (dict(dk=16), 2),
+    (dict(chunk=128), 1), (dict(dk=48), 2), (dict(dv=1040), 2), (dict(dv=24), 2), (dict(dk=16), 2),
+    (dict(flags=4), 1), (dict(flags=-1), 1), (dict(flags=2, Ip=FAKE + 4), 3),
     (dict(q=FAKE + 4), 3), (dict(v=FAKE + 8), 3),
     (dict(mu0=FAKE + 4, I0=FAKE), 3), (dict(IT=FAKE + 12), 3), (dict(dt=FAKE + 1), 3),
     (dict(y=FAKE + 1), 3), (dict(A=FAKE + 2), 3), (dict(beta=FAKE + 2), 3),
@@ -104,17 +105,18 @@ def test_fwd_rejects_invalid_calls(lib, over, status):
 
 def _step_args(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dt=FAKE, A=FAKE, Ip=FAKE, mu=FAKE, I=FAKE, y=FAKE,
-             B=2, H=3, dk=128, dv=128, ind=1, outd=1, stream=None)
+             B=2, H=3, dk=128, dv=128, ind=1, outd=1, flags=0, stream=None)
     a.update(over)
     return [a[n] for n in ("q", "k", "v", "beta", "dt", "A", "Ip", "mu", "I", "y",
-                           "B", "H", "dk", "dv", "ind", "outd", "stream")]
+                           "B", "H", "dk", "dv", "ind", "outd", "flags", "stream")]
 
 
 STEP_CASES = [
     (dict(q=None), 1), (dict(mu=None), 1), (dict(I=None), 1), (dict(y=None), 1),
     (dict(B=0), 1), (dict(H=-2), 1), (dict(ind=5), 1), (dict(dk=100), 2), (dict(dv=8), 2),
     (dict(mu=FAKE + 4), 3), (dict(I=FAKE + 8), 3), (dict(k=FAKE + 1), 3), (dict(dt=FAKE + 1), 3),
-    (dict(y=FAKE + 3), 3), (dict(Ip=FAKE + 2), 3),
+    (dict(y=FAKE + 3), 3), (dict(Ip=FAKE + 2), 3), (dict(flags=4), 1), (dict(dv=40), 2),
+    (dict(flags=2, Ip=FAKE + 8), 3),
 ]
 
 
@@ -159,7 +161,7 @@ FROZEN_CASES = [
     (dict(q=None), 1), (dict(dt=None), 1), (dict(y=None), 1), (dict(A=None), 1), (dict(B=0), 1),
     (dict(T=-2), 1), (dict(ind=3), 1), (dict(ind=0), 2), (dict(dk=32), 2), (dict(dv=32), 2),
     (dict(dk=48), 2), (dict(q=FAKE + 8), 3), (dict(y=FAKE + 8), 3), (dict(beta=FAKE + 4), 3),
-    (dict(mu0=FAKE + 4), 3), (dict(dt=FAKE + 1), 3),
+    (dict(mu0=FAKE + 4), 3), (dict(dt=FAKE + 1), 3), (dict(dv=96), 2), (dict(dv=1088), 2),
 ]
 
 
@@ -172,11 +174,11 @@ def _bwd_args(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dt=FAKE, A=FAKE, Ip=FAKE, mu0=None, I0=None,
              gy=FAKE, gmuT=None, gIT=None, gq=FAKE, gk=FAKE, gv=FAKE, gbeta=FAKE, gdt=FAKE,
              gA=FAKE, gIp=FAKE, gmu0=None, gI0=None, B=2, T=8, H=3, dk=64, dv=64, ind=1, gyd=1,
-             ws=FAKE, wsb=1 << 40, stream=None)
+             flags=0, ws=FAKE, wsb=1 << 40, stream=None)
     a.update(over)
     return [a[n] for n in ("q", "k", "v", "beta", "dt", "A", "Ip", "mu0", "I0", "gy", "gmuT", "gIT",
                            "gq", "gk", "gv", "gbeta", "gdt", "gA", "gIp", "gmu0", "gI0",
-                           "B", "T", "H", "dk", "dv", "ind", "gyd", "ws", "wsb", "stream")]
+                           "B", "T", "H", "dk", "dv", "ind", "gyd", "flags", "ws", "wsb", "stream")]
 
 
 BWD_CASES = [
@@ -184,7 +186,8 @@ BWD_CASES = [
     (dict(gA=None), 1), (dict(gIp=None), 1), (dict(A=None), 1), (dict(ws=None), 1),
     (dict(mu0=FAKE), 1), (dict(I0=FAKE), 1), (dict(B=0), 1), (dict(T=-1), 1), (dict(H=0), 1),
     (dict(ind=2), 1), (dict(gyd=5), 1), (dict(wsb=64), 1), (dict(q=None, T=0, A=None), 1),
-    (dict(dk=48), 2), (dict(dv=256), 2), (dict(dk=16), 2),
+    (dict(dk=48), 2), (dict(dv=1040), 2), (dict(dv=8), 2), (dict(dk=16), 2),
+    (dict(flags=8), 1), (dict(flags=2, Ip=FAKE + 4), 3), (dict(flags=2, gIp=FAKE + 4), 3),
     (dict(q=FAKE + 4), 3), (dict(gy=FAKE + 8), 3), (dict(gq=FAKE + 4), 3), (dict(gk=FAKE + 8), 3),
     (dict(gdt=FAKE + 2), 3), (dict(dt=FAKE + 1), 3), (dict(ws=FAKE + 8), 3),
     (dict(gmuT=FAKE + 4), 3), (dict(gmu0=FAKE + 12), 3), (dict(gA=FAKE + 1), 3),
@@ -203,11 +206,16 @@ def test_bwd_workspace_size_host_logic(lib):
     import bayesian_metaplastic_memory_amd as pm
     pad = lambda n: (4 * n + 255) // 256 * 256
 
-    def expect(B, T, H, dk, dv):
+    def expect(B, T, H, dk, dv, per_entry=False):
         nsb, nrb, bh = (T + 7) // 8, dv // 16, B * H
         return (pad(bh * nsb * 2 * dv * dk) + pad(nrb * bh * T * 2 * dk) + pad(nrb * bh * T * 2)
-                + 2 * pad(bh) + pad(bh * nrb))
-    for shape in [(1, 10, 2, 32, 32), (8, 4096, 12, 128, 128), (1, 0, 3, 64, 128), (2, 9, 1, 128, 64)]:
+                + 2 * pad(bh) + pad(bh * nrb) + (pad(bh * dv * dk) if per_entry else 0))
+    for shape in [(1, 10, 2, 32, 32), (8, 4096, 12, 128, 128), (1, 0, 3, 64, 128), (2, 9, 1, 128, 64),
+                  (1, 33, 2, 128, 256), (2, 5, 3, 64, 48)]:
         assert pm.bwd_workspace_size(*shape) == expect(*shape), shape
+        assert pm.bwd_workspace_size(*shape, flags=2) == expect(*shape, per_entry=True), shape
+        assert pm.bwd_workspace_size(*shape, flags=1) == expect(*shape), shape
     assert pm.bwd_workspace_size(1, 8, 2, 48, 64) == 0
     assert pm.bwd_workspace_size(0, 8, 2, 64, 64) == 0
+    assert pm.bwd_workspace_size(1, 8, 2, 64, 24) == 0
+    assert pm.bwd_workspace_size(1, 8, 2, 64, 64, flags=4) == 0

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import workloads
-from parity_utils import TOL_BWD, assert_close, gpu_args, rel_err, to_device, to_np, tol_for
+from parity_utils import TOL_BWD, TOL_F32, assert_close, gpu_args, rel_err, to_device, to_np, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -617,3 +617,107 @@ def test_bwd_is_deterministic_and_ignores_stale_workspace():
     torch.cuda.synchronize()
     for n in BWD_NAMES:
         assert torch.equal(a[n], b[n]), n
+
+
+# ---------------------------------------------------------------------------
+# generalised boundary: value expansion / any dv multiple of 16, v* input,
+# a prior per state entry
+# ---------------------------------------------------------------------------
+
+DV_SHAPES = [(128, 256, torch.float32), (128, 256, torch.bfloat16), (64, 48, torch.float32),
+             (32, 16, torch.float32), (128, 512, torch.bfloat16), (64, 176, torch.float32)]
+
+
+@pytest.mark.parametrize("dk,dv,dtype", DV_SHAPES)
+def test_value_expansion_forward_step_backward(dk, dv, dtype):
+    w = workloads.WORKLOADS[0].with_(B=2, H=2, dk=dk, dv=dv, dtype=dtype, A_mode="logspace16")
+    T = 45
+    _announce("dv shapes fwd+step+bwd", B=w.B, H=w.H, T=T, dk=dk, dv=dv, dtype=dtype)
+    inp = workloads.make_inputs(w, T=T, seed=dk + dv)
+    inp["mu0"], inp["I0"] = workloads.random_state(w.B, w.H, dv, dk, inp["I_prior"], seed=dv)
+    y, muT, IT = _run_fwd(inp)
+    _compare_full(inp, y, muT, IT, tol_for(dtype))
+    # one decode step from the final state
+    d = {n: x.to(DEV) for n, x in workloads.decode_inputs(w, 0).items()}
+    ref_y, ref_mu, ref_I = oracle.step(**{n: workloads_cpu(d[n]) for n in d}, A=inp["A"], I_prior=inp["I_prior"],
+                                       mu=to_np(muT), I=to_np(IT))
+    mu, I = muT.clone(), IT.clone()
+    ys = _pm().step(d["q"], d["k"], d["v"], d["beta"], d["dt"], inp["A"].to(DEV), inp["I_prior"].to(DEV), mu, I)
+    torch.cuda.synchronize()
+    assert_close("step y", ys, ref_y, tol_for(dtype))
+    assert_close("step mu", mu, ref_mu, TOL_F32)
+    gr = workloads.upstream_grads(w.B, T, w.H, dv, dk, dtype, seed=dv)
+    _compare_bwd(_run_bwd(inp, gr), _bwd_ref(inp, gr), TOL_BWD)
+
+
+def workloads_cpu(x):
+    return x.cpu() if isinstance(x, torch.Tensor) else x
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_vstar_input_forward_step_backward(dtype):
+    """With PALIMPSA_VSTAR the v tensor is the write v* itself."""
+    w = workloads.WORKLOADS[0].with_(B=2, H=3, dk=64, dv=64, dtype=dtype, A_mode="logspace16")
+    T = 70
+    _announce("v* fwd+step+bwd", B=w.B, H=w.H, T=T, d=64, dtype=dtype)
+    inp = workloads.make_inputs(w, T=T, seed=77)
+    g = to_device(inp, DEV)
+    y, muT, IT = _pm().fwd_chunked(*gpu_args(g), vstar=True)
+    torch.cuda.synchronize()
+    y_ref, mu_ref, I_ref = oracle.fwd(**inp, vstar=True)
+    assert_close("y (v*)", y, y_ref, tol_for(dtype))
+    assert_close("muT (v*)", muT, mu_ref, TOL_F32)
+    assert_close("IT (v*)", IT, I_ref, TOL_F32)
+    d = {n: x.to(DEV) for n, x in workloads.decode_inputs(w, 1).items()}
+    ref = oracle.step(**{n: d[n].cpu() for n in d}, A=inp["A"], I_prior=inp["I_prior"], mu=to_np(muT),
+                      I=to_np(IT), vstar=True)
+    ys = _pm().step(d["q"], d["k"], d["v"], d["beta"], d["dt"], g["A"], g["I_prior"], muT, IT, vstar=True)
+    torch.cuda.synchronize()
+    assert_close("step y (v*)", ys, ref[0], tol_for(dtype))
+    assert_close("step mu (v*)", muT, ref[1], TOL_F32)
+    gr = workloads.upstream_grads(w.B, T, w.H, 64, 64, dtype, seed=78)
+    gg = to_device(gr, DEV)
+    got = _pm().bwd(*gpu_args(g), gg["gy"], gmuT=gg["gmuT"], gIT=gg["gIT"], vstar=True)
+    torch.cuda.synchronize()
+    ref = oracle.bwd(**inp, gy=gr["gy"], gmuT=gr["gmuT"], gIT=gr["gIT"], vstar=True)
+    _compare_bwd(got, ref, TOL_BWD)
+
+
+@pytest.mark.parametrize("dk,dv,state", [(128, 128, False), (64, 32, True), (32, 64, False), (128, 256, True)])
+def test_per_entry_prior_forward_step_backward(dk, dv, state):
+    w = workloads.WORKLOADS[0].with_(B=2, H=2, dk=dk, dv=dv, A_mode="logspace16")
+    T = 200    # long enough for the 3-segment split below (segments are multiples of 64 tokens)
+    _announce("per-entry prior fwd+split+step+bwd", B=w.B, H=w.H, T=T, dk=dk, dv=dv, state=state)
+    inp = workloads.make_inputs(w, T=T, seed=dk * 3 + dv)
+    inp["I_prior"] = workloads.per_entry_prior(w.H, dv, dk, seed=dk + dv)
+    if state:
+        inp["mu0"], inp["I0"] = workloads.random_state(w.B, w.H, dv, dk, torch.ones(w.H), seed=5)
+    y, muT, IT = _run_fwd(inp)
+    _compare_full(inp, y, muT, IT, TOL_F32)
+    g = to_device(inp, DEV)
+    ys, mus, Is = _pm().fwd_chunked(*gpu_args(g), mu0=g.get("mu0"), I0=g.get("I0"), segments=3)
+    torch.cuda.synchronize()
+    assert rel_err(ys, y) <= 1e-5 and rel_err(mus, muT) <= 1e-5 and rel_err(Is, IT) <= 1e-6
+    d = {n: x.to(DEV) for n, x in workloads.decode_inputs(w, 2).items()}
+    ref = oracle.step(**{n: d[n].cpu() for n in d}, A=inp["A"], I_prior=inp["I_prior"], mu=to_np(muT), I=to_np(IT))
+    ys1 = _pm().step(d["q"], d["k"], d["v"], d["beta"], d["dt"], g["A"], g["I_prior"], muT, IT)
+    torch.cuda.synchronize()
+    assert_close("step y (per-entry prior)", ys1, ref[0], TOL_F32)
+    assert_close("step I (per-entry prior)", IT, ref[2], TOL_F32)
+    gr = workloads.upstream_grads(w.B, T, w.H, dv, dk, w.dtype, seed=dk)
+    got = _run_bwd(inp, gr)
+    assert tuple(got["gIp"].shape) == (w.H, dv, dk)
+    _compare_bwd(got, _bwd_ref(inp, gr), TOL_BWD)
+
+
+@pytest.mark.parametrize("dv", [256, 192])
+def test_frozen_value_expansion(dv):
+    w = workloads.WORKLOADS[0].with_(B=1, H=3, dk=128, dv=dv, dtype=torch.bfloat16, A_mode="logspace16")
+    _announce("frozen dv", B=1, H=3, T=130, dk=128, dv=dv)
+    inp = workloads.make_inputs(w, T=130, seed=dv)
+    g = to_device(inp, DEV)
+    y, muT = _pm().fwd_frozen(*gpu_args(g))
+    torch.cuda.synchronize()
+    y_ref, mu_ref = _frozen_ref(inp)
+    assert_close("frozen y (dv=%d)" % dv, y, y_ref, 2e-2)
+    assert_close("frozen muT (dv=%d)" % dv, muT, mu_ref, 2e-2)

@@ -147,3 +147,9 @@ def upstream_grads(B: int, T: int, H: int, dv: int, dk: int, dtype: torch.dtype,
         out["gmuT"] = (0.1 * torch.randn(B, H, dv, dk, generator=g)).contiguous()
         out["gIT"] = (0.1 * torch.randn(B, H, dv, dk, generator=g)).contiguous()
     return out
+
+
+def per_entry_prior(H: int, dv: int, dk: int, seed: int) -> torch.Tensor:
+    """A seeded prior precision per state entry, I_prior[h, i, j] ~ U[0.5, 2]."""
+    g = torch.Generator().manual_seed(20_000 + seed)
+    return (0.5 + 1.5 * torch.rand(H, dv, dk, generator=g)).contiguous()
