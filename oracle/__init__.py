@@ -23,6 +23,10 @@ Contents
     an option that keeps only the diagonal of the precision at every token.
 ``bwd``
     The reverse-mode derivative of ``fwd`` (C oracle), for the training path.
+``fwd_blockdiag``
+    The Gaussian update with the precision kept block-diagonal along the key
+    axis (limited cross-key correlations); block 1 is Eq. (5), block dk the
+    full update.
 ``fwd_mamba2_limit``
     The frozen-importance recurrence of the Mamba2 limit (slides, frame "The
     Mamba2 limit enables a gradual model upgrade", Secs. 2.3-2.4).
@@ -341,6 +345,59 @@ def fwd_mamba2_limit(q, k, v, beta, dt, A, I_prior, mu0=None):
                 y[b, t, h] = m @ q[b, t, h]
             mu[b, h] = m
     return y, mu
+
+
+def fwd_blockdiag(q, k, v, beta, dt, A, I_prior, block: int, mu0=None, P0=None):
+    """Palimpsa with limited cross-key precision: the full-precision Gaussian
+    update of each value row (slides, backup frame "dropping precision
+    correlations changes the mean", App. A.3-A.5)
+
+        P_t = alpha_t P_{t-1} + (1 - alpha_t) I_prior Id + beta_{t,i} k_t k_t^T
+        mu_t = P_t^{-1} [alpha_t P_{t-1} mu_{t-1} + beta_{t,i} v_{t,i} k_t]
+
+    with P_t projected, at every token, onto the block-diagonal matrices of
+    ``block`` x ``block`` blocks along the key axis (the slides' closing
+    question on limited cross-key correlations).  ``block = 1`` is Eq. (5);
+    ``block = dk`` is the full update.  The prior is one scalar per head.
+
+    Layouts as ``fwd``; the precision state is ``[B, H, dv, dk/block, block,
+    block]`` (full blocks).  Defaults: ``mu0 = 0``, ``P0 = I_prior Id``.
+    Returns ``(y, muT, PT)`` as float64.
+    """
+    q, k, v, beta, dt = (_f64(x) for x in (q, k, v, beta, dt))
+    A, Ip = _f64(A), _f64(I_prior)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    bs = int(block)
+    if bs < 1 or dk % bs:
+        raise ValueError("block must divide dk")
+    nb = dk // bs
+    eye = np.eye(bs)
+    mu = np.zeros((B, H, dv, dk)) if mu0 is None else _f64(mu0).copy()
+    if P0 is None:
+        P = np.broadcast_to(Ip[None, :, None, None, None, None] * eye, (B, H, dv, nb, bs, bs)).copy()
+    else:
+        P = _f64(P0).copy()
+        if P.shape != (B, H, dv, nb, bs, bs):
+            raise ValueError("P0 must be [B, H, dv, dk/block, block, block]")
+    y = np.zeros((B, T, H, dv))
+    for b in range(B):
+        for h in range(H):
+            m = mu[b, h].reshape(dv, nb, bs)
+            Pb = P[b, h]
+            for t in range(T):
+                a, oma = _gate(A[h], dt[b, t, h])
+                kb = k[b, t, h].reshape(nb, bs)
+                outer = kb[:, :, None] * kb[:, None, :]                       # [nb, bs, bs]
+                P_new = a * Pb + oma * Ip[h] * eye + beta[b, t, h][:, None, None, None] * outer[None]
+                rhs = a * np.einsum("rnij,rnj->rni", Pb, m) + \
+                    (beta[b, t, h] * v[b, t, h])[:, None, None] * kb[None]
+                m = np.linalg.solve(P_new, rhs[..., None])[..., 0]
+                Pb = P_new
+                y[b, t, h] = m.reshape(dv, dk) @ q[b, t, h]
+            mu[b, h] = m.reshape(dv, dk)
+            P[b, h] = Pb
+    return y, mu, P
 
 
 # ---------------------------------------------------------------------------

@@ -521,3 +521,81 @@ def test_vstar_input_is_the_product_it_replaces():
     c = oracle.fwd_numpy(**dict(inp, v=vstar), vstar=True)
     for x, y in zip(a, c):
         np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# block-diagonal precision (limited cross-key correlations)
+# ---------------------------------------------------------------------------
+
+def test_blockdiag_block_one_is_the_recurrence():
+    rng = np.random.default_rng(41)
+    inp = _rand_inputs(rng, B=2, T=9, H=2, dk=4, dv=3)
+    y, mu, P = oracle.fwd_blockdiag(**inp, block=1)
+    y2, mu2, I2 = oracle.fwd(**inp)
+    np.testing.assert_allclose(y, y2, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(mu, mu2, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(P[..., 0, 0], I2, rtol=1e-12)
+
+
+def test_blockdiag_full_block_is_the_full_gaussian():
+    rng = np.random.default_rng(42)
+    inp = _rand_inputs(rng, B=1, T=7, H=1, dk=4, dv=2)
+    y, mu, P = oracle.fwd_blockdiag(**inp, block=4)
+    alpha = np.exp(-inp["A"][0] * inp["dt"][0, :, 0])
+    mu_f, P_f, mus = oracle.fwd_full_gaussian(inp["k"][0, :, 0], inp["v"][0, :, 0], inp["beta"][0, :, 0],
+                                              alpha, inp["I_prior"][0] * np.eye(4))
+    np.testing.assert_allclose(mu[0, 0], mu_f, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(P[0, 0, :, 0], P_f, rtol=1e-12)
+    np.testing.assert_allclose(y[0, :, 0], np.einsum("tij,tj->ti", mus, inp["q"][0, :, 0]), rtol=1e-10, atol=1e-13)
+
+
+def test_blockdiag_is_exact_when_every_key_lives_in_one_block():
+    """Keys supported on one 2-block per token keep the full precision block-
+    diagonal, so the block model equals the full update exactly."""
+    rng = np.random.default_rng(43)
+    inp = _rand_inputs(rng, B=1, T=10, H=1, dk=4, dv=2)
+    kk = np.zeros_like(inp["k"])
+    for t in range(10):
+        blk = t % 2
+        kk[0, t, 0, 2 * blk:2 * blk + 2] = rng.standard_normal(2)
+    inp["k"] = kk
+    _, mu, _ = oracle.fwd_blockdiag(**inp, block=2)
+    alpha = np.exp(-inp["A"][0] * inp["dt"][0, :, 0])
+    mu_f, _, _ = oracle.fwd_full_gaussian(kk[0, :, 0], inp["v"][0, :, 0], inp["beta"][0, :, 0], alpha,
+                                          inp["I_prior"][0] * np.eye(4))
+    np.testing.assert_allclose(mu[0, 0], mu_f, rtol=1e-10, atol=1e-13)
+    _, mu_d, _ = oracle.fwd_blockdiag(**inp, block=1)
+    assert np.abs(mu_d[0, 0] - mu_f).max() > 1e-3       # the diagonal model is not exact here
+
+
+def test_blockdiag_axis_aligned_keys_agree_for_every_block_size():
+    rng = np.random.default_rng(44)
+    inp = _rand_inputs(rng, B=1, T=8, H=2, dk=4, dv=2)
+    kk = np.zeros_like(inp["k"])
+    idx = rng.integers(0, 4, size=(8, 2))
+    for t in range(8):
+        for h in range(2):
+            kk[0, t, h, idx[t, h]] = rng.standard_normal()
+    inp["k"] = kk
+    ref = oracle.fwd(**inp)
+    for bs in (1, 2, 4):
+        y, mu, _ = oracle.fwd_blockdiag(**inp, block=bs)
+        np.testing.assert_allclose(y, ref[0], rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(mu, ref[1], rtol=1e-11, atol=1e-13)
+
+
+def test_blockdiag_teaching_example_two_by_two():
+    """The backup frame's 2-D example: one key (1, 1), v = beta = 1, prior mean 0,
+    identity prior precision (alpha = 1): the 2-block keeps the correlation and
+    gives the full mean (1/3, 1/3); the diagonal model gives (1/2, 1/2)."""
+    g = _golden("full_vs_diagonal_2d.json")
+    x = g["inputs"]
+    B = T = H = 1
+    inp = dict(q=np.zeros((1, 1, 1, 2)), k=np.array(x["k"], float).reshape(1, 1, 1, 2),
+               v=np.array([[[[x["v"]]]]], float), beta=np.array([[[[x["beta"]]]]], float),
+               dt=np.zeros((1, 1, 1)), A=np.ones(1), I_prior=np.ones(1))
+    _, mu2, P2 = oracle.fwd_blockdiag(**inp, block=2)
+    _, mu1, _ = oracle.fwd_blockdiag(**inp, block=1)
+    np.testing.assert_allclose(mu2[0, 0, 0], g["mu_full"], rtol=1e-12)
+    np.testing.assert_allclose(mu1[0, 0, 0], g["mu_diag"], rtol=1e-12)
+    np.testing.assert_allclose(P2[0, 0, 0, 0], g["P_new"], rtol=1e-12)
