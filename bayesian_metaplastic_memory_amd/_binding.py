@@ -55,6 +55,8 @@ def load_library() -> ctypes.CDLL:
             lib.palimpsa_bwd.restype = i
             lib.palimpsa_bwd_workspace_size.argtypes = [i] * 6
             lib.palimpsa_bwd_workspace_size.restype = sz
+            lib.palimpsa_fwd_blockdiag.argtypes = [vp] * 5 + [fp] * 4 + [vp, fp, fp] + [i] * 8 + [vp]
+            lib.palimpsa_fwd_blockdiag.restype = i
             lib.palimpsa_status_string.argtypes = [i]
             lib.palimpsa_status_string.restype = ctypes.c_char_p
             lib.palimpsa_version.argtypes = []
@@ -331,3 +333,51 @@ def bwd(q, k, v, beta, dt, A, I_prior, gy, mu0=None, I0=None, gmuT=None, gIT=Non
     if st != OK:
         raise PalimpsaError(st, "palimpsa_bwd")
     return res
+
+
+def fwd_blockdiag(q, k, v, beta, dt, A, I_prior, block: int = 2, mu0=None, P0=None, out_dtype=None,
+                  y=None, muT=None, PT=None, write_state: bool = True):
+    """Forward with the precision kept block-diagonal along the key axis
+    (``block`` = 2).  Returns ``(y, muT, PT)`` with ``PT`` ``[B, H, dv, dk/2,
+    2, 2]``; ``mu0``/``P0`` likewise (both or neither)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    in_dtype = q.dtype
+    if in_dtype not in _DTYPES:
+        raise ValueError("unsupported input dtype %s" % in_dtype)
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    for t, name, shape in ((k, "k", (B, T, H, dk)), (v, "v", (B, T, H, dv)), (beta, "beta", (B, T, H, dv)),
+                           (dt, "dt", (B, T, H))):
+        _check(t, name, shape, in_dtype, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(I_prior, "I_prior", (H,), torch.float32, dev)
+    nb = dk // block if block > 0 else 0
+    if (mu0 is None) != (P0 is None):
+        raise ValueError("give both mu0 and P0, or neither")
+    if mu0 is not None:
+        _check(mu0, "mu0", (B, H, dv, dk), torch.float32, dev)
+        _check(P0, "P0", (B, H, dv, nb, block, block), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    _check(y, "y", (B, T, H, dv), out_dtype, dev)
+    if write_state:
+        muT = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if muT is None else muT
+        PT = torch.empty((B, H, dv, nb, block, block), dtype=torch.float32, device=dev) if PT is None else PT
+        _check(muT, "muT", (B, H, dv, dk), torch.float32, dev)
+        _check(PT, "PT", (B, H, dv, nb, block, block), torch.float32, dev)
+    else:
+        muT = PT = None
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.palimpsa_fwd_blockdiag(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(dt), _ptr(A), _ptr(I_prior), _ptr(mu0), _ptr(P0),
+            _ptr(y) if y.numel() else None, _ptr(muT), _ptr(PT), B, T, H, dk, dv, int(block),
+            _DTYPES[in_dtype], _DTYPES[out_dtype], _stream_handle(dev))
+    if st != OK:
+        raise PalimpsaError(st, "palimpsa_fwd_blockdiag")
+    return y, muT, PT

@@ -1290,6 +1290,177 @@ __global__ __launch_bounds__(256) void bwd_prior_kernel(const float *pip, float 
 }
 
 // ---------------------------------------------------------------------------
+// block-diagonal precision (limited cross-key correlations), 2x2 blocks
+// ---------------------------------------------------------------------------
+//
+// The Gaussian update of a value row (slides, backup frame "dropping
+// precision correlations changes the mean", App. A.3-A.5) with the precision
+// kept block-diagonal along the key axis, 2x2 blocks (the slides' closing
+// question on limited cross-key correlations; a block of 1 is Eq. (5)).  In
+// natural parameters h = P mu both stay affine:
+//     P_t = alpha P_{t-1} + (1 - alpha) I_prior Id + beta_i blocks(k k^T)
+//     h_t = alpha h_{t-1} + (beta_i v_i) k
+// and the readout solves each 2x2 block: mu = P^{-1} h, y_i = sum_j mu_j q_j.
+// The lane layout is the forward's (one row, DK/16 columns, which come in
+// aligned 4-wide vectors, so a lane owns whole blocks).  Per block and token:
+// 21 VALU + 1 v_rcp_f32 (10.5 VALU + 0.5 rcp per entry, against 6 + 1).
+struct BdArgs {
+    const void *q, *k, *v, *beta, *dt;
+    const float *A, *Ip, *mu0, *P0;   // P0 / PT: [B, H, dv, dk/2, 2, 2]
+    void *y;
+    float *muT, *PT;
+    int B, T, H, dv, nwg, xcd_remap;
+};
+
+template <int DK, int C, typename TOut>
+__device__ inline void bd2_chunk(const float *buf, int left, float *h, float *p00, float *p01, float *p11,
+                                 int row_local, int g, TOut *yrow, size_t ystride) {
+    using LT = LaneTile<DK>;
+    const float *cbase = buf + LT::col(g, 0, 0);
+    const float *rbase = buf + C * Stage<DK>::kColFloats + 2 * row_local;
+    int goff = C * (Stage<DK>::kColFloats + Stage<DK>::kRowFloats);
+    asm volatile("" : "+v"(goff));
+    const float *gbase = buf + goff;
+#pragma unroll 1
+    for (int grp = 0; grp < C / kGroup; ++grp) {
+        const float *cg = cbase + grp * kGroup * Stage<DK>::kColFloats;
+        const float *rg = rbase + grp * kGroup * Stage<DK>::kRowFloats;
+        const float *gg = gbase + grp * kGroup * 2;
+        float part[kGroup];
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            const float2 gc = *(const float2 *)(gg + 2 * u);                          // alpha, c
+            const float2 rb = *(const float2 *)(rg + u * Stage<DK>::kRowFloats);      // beta, beta*v
+            const float *ct = cg + u * Stage<DK>::kColFloats;
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < LT::kNVec; ++m) {
+                float kk[LT::kVec], k2[LT::kVec], qq[LT::kVec];
+                const int c0 = kLanesPerRow * LT::kVec * m;
+                vecf<LT::kVec>::ld(ct + c0, kk);
+                vecf<LT::kVec>::ld(ct + DK + c0, k2);
+                vecf<LT::kVec>::ld(ct + 2 * DK + c0, qq);
+#pragma unroll
+                for (int e = 0; e < LT::kVec; e += 2) {
+                    const int s = m * LT::kVec + e, pb = s / 2;
+                    p00[pb] = fmaf(gc.x, p00[pb], fmaf(rb.x, k2[e], gc.y));
+                    p11[pb] = fmaf(gc.x, p11[pb], fmaf(rb.x, k2[e + 1], gc.y));
+                    p01[pb] = fmaf(gc.x, p01[pb], rb.x * (kk[e] * kk[e + 1]));
+                    h[s] = fmaf(gc.x, h[s], rb.y * kk[e]);
+                    h[s + 1] = fmaf(gc.x, h[s + 1], rb.y * kk[e + 1]);
+                    const float r = __builtin_amdgcn_rcpf(fmaf(p00[pb], p11[pb], -(p01[pb] * p01[pb])));
+                    const float m0 = fmaf(p11[pb], h[s], -(p01[pb] * h[s + 1])) * r;
+                    const float m1 = fmaf(p00[pb], h[s + 1], -(p01[pb] * h[s])) * r;
+                    acc = fmaf(m0, qq[e], acc);
+                    acc = fmaf(m1, qq[e + 1], acc);
+                }
+            }
+            part[u] = acc;
+        }
+        const float yv = row16_transpose_sum(part, g);
+        const int tt = grp * kGroup + g;
+        if (tt < left)
+            yrow[(size_t)tt * ystride] = io<TOut>::from_f32(yv);
+    }
+}
+
+template <int DK, int C, typename TIn, typename TOut>
+__global__ __launch_bounds__(kThreads) void bd2_fwd_kernel(BdArgs a) {
+    using LT = LaneTile<DK>;
+    static_assert(LT::kVec % 2 == 0, "a lane's columns must hold whole 2-blocks");
+    constexpr int KC = LT::kCols, KB = KC / 2;
+    extern __shared__ float lds[];
+    float *buf0 = lds;
+    float *buf1 = lds + C * Stage<DK>::kTokFloats;
+    const int rb_per_head = a.dv / kRowsPerWG;
+    int wg = blockIdx.x;
+    if (a.xcd_remap) {
+        const int per_xcd = a.nwg / 8;
+        wg = (wg % 8) * per_xcd + wg / 8;
+    }
+    const int bh = wg / rb_per_head;
+    const int row0 = (wg % rb_per_head) * kRowsPerWG;
+    const int b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane & (kLanesPerRow - 1);
+    const int row_local = wave * kRowsPerWave + (lane >> 4);
+    const int row = row0 + row_local;
+    const float A = a.A[h], Ip = a.Ip[h];
+
+    // state: h = P mu per entry, (p00, p01, p11) per 2-block
+    float hv[KC], p00[KB], p01[KB], p11[KB];
+    const size_t srow = ((size_t)bh * a.dv + row) * DK;      // entry (b, h, row, 0)
+#pragma unroll
+    for (int m = 0; m < LT::kNVec; ++m)
+#pragma unroll
+        for (int e = 0; e < LT::kVec; e += 2) {
+            const int s = m * LT::kVec + e, pb = s / 2;
+            const int col = LT::col(g, m, e);                 // even: the block's first column
+            if (a.mu0) {
+                const float4 P = *(const float4 *)(a.P0 + (srow + col) * 2);   // block (col / 2): 2x2
+                const float m0 = a.mu0[srow + col], m1 = a.mu0[srow + col + 1];
+                p00[pb] = P.x; p01[pb] = P.y; p11[pb] = P.w;
+                hv[s] = fmaf(P.x, m0, P.y * m1);
+                hv[s + 1] = fmaf(P.y, m0, P.w * m1);
+            } else {
+                p00[pb] = Ip; p01[pb] = 0.f; p11[pb] = Ip;
+                hv[s] = 0.f; hv[s + 1] = 0.f;
+            }
+        }
+
+    const size_t seq = (size_t)b * a.T * a.H + h;
+    const TIn *kseq = (const TIn *)a.k + seq * DK;
+    const TIn *qseq = (const TIn *)a.q + seq * DK;
+    const TIn *vseq = (const TIn *)a.v + seq * a.dv + row0;
+    const TIn *bseq = (const TIn *)a.beta + seq * a.dv + row0;
+    const TIn *dseq = (const TIn *)a.dt + seq;
+    const size_t kq_tok = (size_t)a.H * DK, vb_tok = (size_t)a.H * a.dv;
+    const size_t ystride = (size_t)a.H * a.dv;
+    TOut *ybase = (TOut *)a.y + seq * a.dv + row;
+    const int nchunks = (a.T + C - 1) / C;
+    Stager<DK, C, TIn, true> st;
+    if (nchunks > 0) {
+        st.load(kseq, qseq, vseq, bseq, dseq, a.T, a.H, a.dv, tid);
+        st.commit(buf0, A, Ip, tid, false);
+        __syncthreads();
+    }
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * C;
+        const bool more = c + 1 < nchunks;
+        if (more) {
+            const size_t tn = (size_t)(t0 + C);
+            st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
+                    dseq + tn * a.H, a.T - (t0 + C), a.H, a.dv, tid);
+        }
+        bd2_chunk<DK, C, TOut>((c & 1) ? buf1 : buf0, a.T - t0, hv, p00, p01, p11, row_local, g,
+                               ybase + (size_t)t0 * ystride, ystride);
+        if (more) st.commit((c & 1) ? buf0 : buf1, A, Ip, tid, false);
+        __syncthreads();
+    }
+    if (a.muT) {
+#pragma unroll
+        for (int m = 0; m < LT::kNVec; ++m)
+#pragma unroll
+            for (int e = 0; e < LT::kVec; e += 2) {
+                const int s = m * LT::kVec + e, pb = s / 2;
+                const int col = LT::col(g, m, e);
+                float m0, m1;
+                if (a.T == 0 && a.mu0) {
+                    m0 = a.mu0[srow + col]; m1 = a.mu0[srow + col + 1];   // copied through exactly
+                } else {
+                    const float det = fmaf(p00[pb], p11[pb], -(p01[pb] * p01[pb]));
+                    m0 = fmaf(p11[pb], hv[s], -(p01[pb] * hv[s + 1])) / det;
+                    m1 = fmaf(p00[pb], hv[s + 1], -(p01[pb] * hv[s])) / det;
+                }
+                a.muT[srow + col] = m0;
+                a.muT[srow + col + 1] = m1;
+                *(float4 *)(a.PT + (srow + col) * 2) = make_float4(p00[pb], p01[pb], p01[pb], p11[pb]);
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // frozen-importance forward (the Mamba2 limit) on the matrix cores
 // ---------------------------------------------------------------------------
 //
@@ -1976,9 +2147,65 @@ palimpsa_status launch_bwd_d(int dk, bool ipe, const FwdArgs &fa, const BwdArgs 
     }
 }
 
+template <int DK, typename TIn, typename TOut>
+palimpsa_status launch_bd2(const BdArgs &a, hipStream_t s) {
+    constexpr int C = 16;
+    const size_t lds = fwd_lds_bytes<DK, C>();
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((bd2_fwd_kernel<DK, C, TIn, TOut>), dim3(a.nwg), dim3(kThreads), lds, s, a);
+    return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
+}
+
+template <typename TIn, typename TOut>
+palimpsa_status launch_bd2_d(const BdArgs &a, int dk, hipStream_t s) {
+    switch (dk) {
+    case 32: return launch_bd2<32, TIn, TOut>(a, s);
+    case 64: return launch_bd2<64, TIn, TOut>(a, s);
+    default: return launch_bd2<128, TIn, TOut>(a, s);
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void *v, const void *beta,
+                                       const void *dt, const float *A, const float *I_prior,
+                                       const float *mu0, const float *P0, void *y, float *muT, float *PT,
+                                       int B, int T, int H, int dk, int dv, int block,
+                                       palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, void *stream) {
+    if (!A || !I_prior || (T > 0 && (!q || !k || !v || !beta || !dt || !y)))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if ((mu0 == nullptr) != (P0 == nullptr) || (muT == nullptr) != (PT == nullptr))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || block <= 0 || !dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (block != 2 || !head_ok(dk) || !dv_ok(dv))
+        return PALIMPSA_ERR_UNSUPPORTED;
+    const void *vec_ptrs[] = {q, k, v, beta, P0, PT};
+    for (const void *p : vec_ptrs)
+        if (p && !aligned_to(p, 16)) return PALIMPSA_ERR_ALIGNMENT;
+    const size_t in_sz = in_dtype == PALIMPSA_BF16 ? 2 : 4, out_sz = out_dtype == PALIMPSA_BF16 ? 2 : 4;
+    if (!aligned_to(dt, in_sz) || !aligned_to(A, 4) || !aligned_to(I_prior, 4) || (y && !aligned_to(y, out_sz)) ||
+        (mu0 && !aligned_to(mu0, 4)) || (muT && !aligned_to(muT, 4)))
+        return PALIMPSA_ERR_ALIGNMENT;
+    const long long nwg = (long long)B * H * (dv / kRowsPerWG);
+    if (nwg > 0x7fffffffLL || (long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 46) ||
+        64LL * H * (dk > dv ? dk : dv) >= (1LL << 31))
+        return PALIMPSA_ERR_UNSUPPORTED;
+    if (T == 0 && !muT) return PALIMPSA_OK;
+    BdArgs a;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.dt = dt;
+    a.A = A; a.Ip = I_prior; a.mu0 = mu0; a.P0 = P0; a.y = y; a.muT = muT; a.PT = PT;
+    a.B = B; a.T = T; a.H = H; a.dv = dv;
+    a.nwg = (int)nwg; a.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf_in = in_dtype == PALIMPSA_BF16, bf_out = out_dtype == PALIMPSA_BF16;
+    if (bf_in && bf_out) return launch_bd2_d<bf16_t, bf16_t>(a, dk, s);
+    if (bf_in) return launch_bd2_d<bf16_t, float>(a, dk, s);
+    if (bf_out) return launch_bd2_d<float, bf16_t>(a, dk, s);
+    return launch_bd2_d<float, float>(a, dk, s);
+}
 
 size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv, int flags) {
     if (B <= 0 || H <= 0 || T < 0 || !head_ok(dk) || !dv_ok(dv) || (flags & ~kFlagsKnown)) return 0;

@@ -41,6 +41,11 @@ HBM_PEAK_GBS = 8000.0
 # v_rcp_f32 = 2 slots): 23 issue slots, 29 flops.
 BWD_SLOTS_PER_UPDATE = 23
 BWD_FLOPS_PER_UPDATE = 29
+# 2x2 block-diagonal precision, per block of two entries and token: precision
+# 2 + 2 + 3 VALU, content 4, determinant 2, solve 6, readout 2 = 21 VALU
+# (33 flops) plus one v_rcp_f32 (2 slots): 11.5 slots and 16.5 flops per entry.
+BD2_SLOTS_PER_ENTRY = 11.5
+BD2_FLOPS_PER_ENTRY = 16.5
 
 
 def alu_peak_tflops():
@@ -68,6 +73,10 @@ def load_traffic(name):
 
 def bwd_peak_tflops():
     return LANE_OPS_PER_S / BWD_SLOTS_PER_UPDATE * BWD_FLOPS_PER_UPDATE / 1e12
+
+
+def bd2_peak_tflops():
+    return LANE_OPS_PER_S / BD2_SLOTS_PER_ENTRY * BD2_FLOPS_PER_ENTRY / 1e12
 
 
 def time_launches(fn, steps, warmup, torch):
@@ -182,6 +191,22 @@ def frozen_extra(torch, pm, w, g, steps):
                          "algorithmic_bytes": hbm}}
 
 
+def blockdiag_extra(torch, pm, w, g, steps):
+    """palimpsa_fwd_blockdiag (2x2 precision blocks along the key axis) on the same workload."""
+    y, muT, PT = pm.fwd_blockdiag(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], block=2)
+    fn = lambda: pm.fwd_blockdiag(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], block=2,
+                                  y=y, muT=muT, PT=PT)
+    _, per = time_launches(fn, steps, 10, torch)
+    avg_s = sum(per) / len(per) / 1e3
+    entries = w.B * w.H * w.T * w.dv * w.dk
+    achieved = entries * BD2_FLOPS_PER_ENTRY / avg_s / 1e12
+    return {"workload": w.name + ", 2x2 block-diagonal precision",
+            "tokens_per_s": w.B * w.T / avg_s, "ms_per_launch": avg_s * 1e3,
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": bd2_peak_tflops(), "unit": "TFLOP/s",
+                         "frac": achieved / bd2_peak_tflops(), "traffic": None,
+                         "per_entry": "10.5 VALU + 0.5 v_rcp_f32 = 11.5 slots, 16.5 flops"}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -268,6 +293,7 @@ def main():
     if not args.no_extras and w.dtype == torch.bfloat16:
         out["backward"] = backward_extra(torch, pm, workloads, w, g, max(5, args.steps // 5))
         out["frozen"] = frozen_extra(torch, pm, w, g, max(20, args.steps))
+        out["blockdiag"] = blockdiag_extra(torch, pm, w, g, max(20, args.steps // 2))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads or w.B * w.H)
     print(json.dumps(out), flush=True)

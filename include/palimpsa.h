@@ -259,6 +259,37 @@ palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const 
  */
 size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv, int flags);
 
+/*
+ * Forward with limited cross-key precision: block-diagonal P (the slides'
+ * closing question on limited cross-key correlations).  Each value row runs
+ * the full Gaussian update of the slides' backup frame "dropping precision
+ * correlations changes the mean" (App. A.3-A.5),
+ *
+ *     P_t  = alpha_t P_{t-1} + (1 - alpha_t) I_prior[h] Id + beta_t[i] k_t k_t^T
+ *     mu_t = P_t^{-1} [alpha_t P_{t-1} mu_{t-1} + beta_t[i] v_t[i] k_t],   y_t[i] = mu_t q_t
+ *
+ * with P kept block-diagonal along the key axis (blocks of `block` adjacent
+ * key channels; the entries between blocks are dropped at every token, as
+ * Eq. (5) drops every off-diagonal entry).  block == 1 is palimpsa_fwd_chunked;
+ * this entry point implements block == 2.
+ *
+ *   q, k, v, beta, dt, A, I_prior, y   as palimpsa_fwd_chunked (per-head prior)
+ *   mu0       [B, H, dv, dk] float32 initial mean, and
+ *   P0        [B, H, dv, dk/2, 2, 2] float32 initial precision blocks (symmetric;
+ *             entry [1][0] is not read); both NULL: mu0 = 0, P0 = I_prior Id
+ *   muT, PT   the final state in the same layouts, or both NULL to skip
+ *
+ * dk in {32, 64, 128}, dv a multiple of 16 up to 1024, block == 2 (else
+ * PALIMPSA_ERR_UNSUPPORTED).  q, k, v, beta, P0 and PT must be 16-byte
+ * aligned.  Arithmetic float32 (each 2x2 block solved with a reciprocal of its
+ * determinant); T == 0 copies the state through.
+ */
+palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void *v, const void *beta,
+                                       const void *dt, const float *A, const float *I_prior,
+                                       const float *mu0, const float *P0, void *y, float *muT, float *PT,
+                                       int B, int T, int H, int dk, int dv, int block,
+                                       palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *palimpsa_status_string(int status);
 

@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("palimpsa_fwd_chunked", "palimpsa_fwd_workspace_size", "palimpsa_fwd_frozen",
-              "palimpsa_step", "palimpsa_bwd", "palimpsa_bwd_workspace_size",
+              "palimpsa_step", "palimpsa_bwd", "palimpsa_bwd_workspace_size", "palimpsa_fwd_blockdiag",
               "palimpsa_status_string", "palimpsa_version"):
         assert n in names
 
@@ -219,3 +219,24 @@ def test_bwd_workspace_size_host_logic(lib):
     assert pm.bwd_workspace_size(0, 8, 2, 64, 64) == 0
     assert pm.bwd_workspace_size(1, 8, 2, 64, 24) == 0
     assert pm.bwd_workspace_size(1, 8, 2, 64, 64, flags=4) == 0
+
+
+def _bd_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dt=FAKE, A=FAKE, Ip=FAKE, mu0=None, P0=None, y=FAKE,
+             muT=FAKE, PT=FAKE, B=2, T=8, H=3, dk=64, dv=64, block=2, ind=1, outd=1, stream=None)
+    a.update(over)
+    return [a[n] for n in ("q", "k", "v", "beta", "dt", "A", "Ip", "mu0", "P0", "y", "muT", "PT",
+                           "B", "T", "H", "dk", "dv", "block", "ind", "outd", "stream")]
+
+
+BD_CASES = [
+    (dict(q=None), 1), (dict(y=None), 1), (dict(A=None), 1), (dict(mu0=FAKE), 1), (dict(PT=None), 1),
+    (dict(B=0), 1), (dict(T=-1), 1), (dict(block=0), 1), (dict(ind=4), 1),
+    (dict(block=1), 2), (dict(block=4), 2), (dict(dk=48), 2), (dict(dv=24), 2),
+    (dict(q=FAKE + 4), 3), (dict(PT=FAKE + 8), 3), (dict(mu0=FAKE + 2, P0=FAKE), 3), (dict(dt=FAKE + 1), 3),
+]
+
+
+@pytest.mark.parametrize("over,status", BD_CASES)
+def test_blockdiag_rejects_invalid_calls(lib, over, status):
+    assert lib.palimpsa_fwd_blockdiag(*_bd_args(**over)) == status

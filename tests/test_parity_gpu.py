@@ -721,3 +721,58 @@ def test_frozen_value_expansion(dv):
     y_ref, mu_ref = _frozen_ref(inp)
     assert_close("frozen y (dv=%d)" % dv, y, y_ref, 2e-2)
     assert_close("frozen muT (dv=%d)" % dv, muT, mu_ref, 2e-2)
+
+
+# ---------------------------------------------------------------------------
+# block-diagonal precision (2x2 blocks along the key axis)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dk,dv,dtype,state,T", [(32, 32, torch.float32, False, 37), (64, 48, torch.float32, True, 100),
+                                                 (128, 128, torch.bfloat16, True, 70), (128, 64, torch.float32, False, 1),
+                                                 (64, 128, torch.bfloat16, False, 160)])
+def test_blockdiag_matches_oracle(dk, dv, dtype, state, T):
+    w = workloads.WORKLOADS[0].with_(B=2, H=2, dk=dk, dv=dv, dtype=dtype, A_mode="logspace16")
+    _announce("blockdiag fwd", B=w.B, H=w.H, T=T, dk=dk, dv=dv, dtype=dtype, state=state)
+    inp = workloads.make_inputs(w, T=T, seed=dk + dv + T)
+    mu0 = P0 = None
+    if state:
+        mu0, P0 = workloads.random_block_state(w.B, w.H, dv, dk, 2, inp["I_prior"], seed=T)
+    g = to_device(inp, DEV)
+    y, muT, PT = _pm().fwd_blockdiag(*gpu_args(g), block=2, mu0=None if mu0 is None else mu0.to(DEV),
+                                     P0=None if P0 is None else P0.to(DEV))
+    torch.cuda.synchronize()
+    y_ref, mu_ref, P_ref = oracle.fwd_blockdiag(**{n: inp[n] for n in ("q", "k", "v", "beta", "dt", "A", "I_prior")},
+                                                block=2, mu0=mu0, P0=P0)
+    assert_close("blockdiag y", y, y_ref, tol_for(dtype))
+    assert_close("blockdiag muT", muT, mu_ref, TOL_F32)
+    assert_close("blockdiag PT", PT, P_ref, TOL_F32)
+
+
+def test_blockdiag_empty_sequence_copies_state():
+    w = workloads.WORKLOADS[0].with_(B=1, H=2, dk=32, dv=32)
+    _announce("blockdiag T=0", B=1, H=2, dk=32, dv=32)
+    inp = workloads.make_inputs(w, T=0)
+    mu0, P0 = workloads.random_block_state(1, 2, 32, 32, 2, inp["I_prior"], seed=3)
+    g = to_device(inp, DEV)
+    _, muT, PT = _pm().fwd_blockdiag(*gpu_args(g), block=2, mu0=mu0.to(DEV), P0=P0.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(muT.cpu(), mu0)
+    assert torch.equal(PT.cpu()[..., 0, 0], P0[..., 0, 0]) and torch.equal(PT.cpu()[..., 0, 1], P0[..., 0, 1])
+
+
+def test_blockdiag_layer760m_sampled():
+    w = workloads.WORKLOADS[2]
+    heads = [(0, 0), (7, 11)]
+    _announce("blockdiag 760M layer", B=w.B, H=w.H, T=w.T, d=w.dk, sampled=heads)
+    inp = workloads.make_inputs(w)
+    g = to_device(inp, DEV)
+    y, muT, PT = _pm().fwd_blockdiag(*gpu_args(g), block=2)
+    torch.cuda.synchronize()
+    sub = oracle.select_heads(inp, heads)
+    y_ref, mu_ref, P_ref = oracle.fwd_blockdiag(**{n: sub[n] for n in ("q", "k", "v", "beta", "dt", "A", "I_prior")},
+                                                block=2)
+    bs = [b for b, _ in heads]
+    hs = [h for _, h in heads]
+    assert_close("blockdiag y (sampled)", to_np(y)[bs, :, hs, :].transpose(1, 0, 2)[None], y_ref, tol_for(w.dtype))
+    assert_close("blockdiag muT (sampled)", to_np(muT)[bs, hs][None], mu_ref, TOL_F32)
+    assert_close("blockdiag PT (sampled)", to_np(PT)[bs, hs][None], P_ref, TOL_F32)

@@ -153,3 +153,14 @@ def per_entry_prior(H: int, dv: int, dk: int, seed: int) -> torch.Tensor:
     """A seeded prior precision per state entry, I_prior[h, i, j] ~ U[0.5, 2]."""
     g = torch.Generator().manual_seed(20_000 + seed)
     return (0.5 + 1.5 * torch.rand(H, dv, dk, generator=g)).contiguous()
+
+
+def random_block_state(B: int, H: int, dv: int, dk: int, block: int, I_prior: torch.Tensor, seed: int):
+    """A non-trivial start state for the block-diagonal forward: mu0 ~ 0.5 N(0, 1)
+    and each precision block I_prior Id + L L^T with L ~ 0.5 N(0, 1) (symmetric
+    positive definite), layout [B, H, dv, dk/block, block, block]."""
+    g = torch.Generator().manual_seed(30_000 + seed)
+    mu0 = 0.5 * torch.randn(B, H, dv, dk, generator=g)
+    L = 0.5 * torch.randn(B, H, dv, dk // block, block, block, generator=g)
+    P0 = I_prior.view(1, H, 1, 1, 1, 1) * torch.eye(block) + L @ L.transpose(-1, -2)
+    return mu0.float().contiguous(), P0.float().contiguous()
