@@ -1461,6 +1461,242 @@ __global__ __launch_bounds__(kThreads) void bd2_fwd_kernel(BdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// wide heads (d_k >= 512): one value row per wave
+// ---------------------------------------------------------------------------
+//
+// For a head as wide as the model (the pages' recurrent-kernel measurement
+// runs one head of width up to 2048, slides frame 22 / Fig. 7) a lane tile of
+// one row and d_k/16 columns would not fit in registers.  Here each wave
+// owns one value row and its 64 lanes split the columns (d_k/64 each, as
+// 4-wide vectors spaced 256 apart, so a wave reads 1 KiB of contiguous LDS
+// per vector); a workgroup of 4 waves owns 4 rows.  The per-column operands
+// k, k^2, q of a chunk of kChunk tokens are staged once per workgroup as in
+// the forward.  Each token's row sum is a whole-wave reduction (a DPP row sum,
+// then the wave's 4 rows added with two permlane swaps: 8 VALU per token and
+// lane, against 8 d_k/64 slots of updates).  Tokens are a rolled loop so that
+// a lane holds one token's operands at a time.  The update is the forward's:
+// 6 VALU + 1 v_rcp_f32 per entry.
+template <int D> struct WideCfg {
+    static constexpr int kCols = D / 64;                 // columns per lane
+    static constexpr int kVecs = kCols / 4;              // 4-wide vectors per lane
+    // tokens per staged chunk: 4 at 512 and 2 above, with k^2 staged up to
+    // 1024 and computed in the lane at 2048, so that the double buffer takes
+    // 49-66 KB (two or three workgroups per CU) and each chunk's global loads
+    // have at least two tokens of compute to arrive
+    static constexpr int kChunk = D == 512 ? 4 : 2;
+    static constexpr bool kStageK2 = D < 2048;
+    static constexpr int kRows = 4;                      // value rows per workgroup
+    static constexpr int kColFloats = (kStageK2 ? 3 : 2) * D;   // k, (k^2), q per token
+    static constexpr int kQ = (kStageK2 ? 2 : 1) * D;    // offset of q in a token
+    static constexpr int kTokFloats = kColFloats + 2 * kRows + 2;
+    static constexpr int kBufFloats = kChunk * kTokFloats;
+    static_assert(kChunk >= 1, "at least one token per chunk");
+    __device__ static inline int col(int lane, int m, int e) { return 256 * m + 4 * lane + e; }
+};
+
+template <int D, typename TIn>
+struct WideStager {
+    using W = WideCfg<D>;
+    static constexpr int C = W::kChunk;
+    static constexpr int kPer = packet<TIn>::kN;
+    static constexpr int kColPkts = D / kPer;
+    static constexpr int kHalf = C * kColPkts;
+    static constexpr int kKQPer = (2 * kHalf + kThreads - 1) / kThreads;
+    uint4 kq[kKQPer];
+    float vv, bb, dtv;
+    // thread slots: (token, row) pairs of (v, beta) on wave 1, dt on wave 2
+    __device__ static inline int vb_slot(int tid) { return (tid + kThreads - 64) % kThreads; }
+    __device__ static inline int dt_slot(int tid) { return (tid + kThreads - 128) % kThreads; }
+
+    __device__ inline void load(const TIn *kb, const TIn *qb, const TIn *vb, const TIn *bb_, const TIn *db,
+                                int left, int H, int dv, int tid) {
+#pragma unroll
+        for (int u = 0; u < kKQPer; ++u) {
+            const int p = tid + u * kThreads;
+            if ((2 * kHalf) % kThreads == 0 || p < 2 * kHalf) {
+                const bool isq = p >= kHalf;
+                const int pp = isq ? p - kHalf : p;
+                const int tt = pp / kColPkts;
+                const size_t off = (size_t)tt * H * D + (pp % kColPkts) * kPer;
+                kq[u] = make_uint4(0, 0, 0, 0);
+                if (tt < left) kq[u] = *(const uint4 *)((isq ? qb : kb) + off);
+            }
+        }
+        const int pv = vb_slot(tid);
+        if (pv < C * W::kRows) {
+            const int tt = pv / W::kRows, r = pv % W::kRows;
+            vv = 0.f; bb = 0.f;
+            if (tt < left) {
+                const size_t off = (size_t)tt * H * dv + r;
+                vv = io<TIn>::to_f32(vb[off]);
+                bb = io<TIn>::to_f32(bb_[off]);
+            }
+        }
+        const int pd = dt_slot(tid);
+        if (pd < C) {
+            dtv = 0.f;
+            if (pd < left) dtv = io<TIn>::to_f32(db[(size_t)pd * H]);
+        }
+    }
+    __device__ inline void commit(float *buf, float A, float Ip, int tid) const {
+        float *rows = buf + C * W::kColFloats;
+        float *gates = rows + C * 2 * W::kRows;
+#pragma unroll
+        for (int u = 0; u < kKQPer; ++u) {
+            const int p = tid + u * kThreads;
+            if ((2 * kHalf) % kThreads == 0 || p < 2 * kHalf) {
+                const bool isq = p >= kHalf;
+                const int pp = isq ? p - kHalf : p;
+                const int tt = pp / kColPkts;
+                const int off = (pp % kColPkts) * kPer;
+                float x[kPer];
+                packet<TIn>::widen(kq[u], x);
+                float *dst = buf + tt * W::kColFloats + off;
+#pragma unroll
+                for (int e = 0; e < kPer; e += 4) {
+                    if (!isq) {
+                        *(float4 *)(dst + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+                        if (W::kStageK2)
+                            *(float4 *)(dst + D + e) = make_float4(x[e] * x[e], x[e + 1] * x[e + 1],
+                                                                   x[e + 2] * x[e + 2], x[e + 3] * x[e + 3]);
+                    } else {
+                        *(float4 *)(dst + W::kQ + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+                    }
+                }
+            }
+        }
+        const int pv = vb_slot(tid);
+        if (pv < C * W::kRows)
+            *(float2 *)(rows + 2 * pv) = make_float2(bb, bb * vv);
+        const int pd = dt_slot(tid);
+        if (pd < C)
+            *(float2 *)(gates + 2 * pd) = gate(A, dtv, Ip);
+    }
+};
+
+// Sum of x over the four 16-lane rows of a wave (every lane receives it).
+__device__ inline float sum_rows4(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, typename TIn, typename TOut>
+__global__ __launch_bounds__(kThreads) void wide_fwd_kernel(FwdArgs a) {
+    using W = WideCfg<D>;
+    constexpr int C = W::kChunk, KC = W::kCols;
+    extern __shared__ float lds[];
+    const int rb_per_head = a.dv / W::kRows;
+    int wg = blockIdx.x;
+    if (a.xcd_remap) {
+        const int per_xcd = a.nwg / 8;
+        wg = (wg % 8) * per_xcd + wg / 8;
+    }
+    const int bh = wg / rb_per_head;
+    const int row0 = (wg % rb_per_head) * W::kRows;
+    const int b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane & 15;
+    const int row = row0 + wave;
+    const float A = a.A[h], Ip = a.Ip[h];
+
+    float M[KC], I[KC];
+    const size_t srow = ((size_t)bh * a.dv + row) * D;
+#pragma unroll
+    for (int m = 0; m < W::kVecs; ++m) {
+        float mu[4], ii[4];
+        if (a.mu0) {
+            vecf<4>::ld(a.mu0 + srow + W::col(lane, m, 0), mu);
+            vecf<4>::ld(a.I0 + srow + W::col(lane, m, 0), ii);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { mu[e] = 0.f; ii[e] = Ip; }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { I[4 * m + e] = ii[e]; M[4 * m + e] = ii[e] * mu[e]; }
+    }
+
+    const size_t seq = (size_t)b * a.T * a.H + h;
+    const TIn *kseq = (const TIn *)a.k + seq * D;
+    const TIn *qseq = (const TIn *)a.q + seq * D;
+    const TIn *vseq = (const TIn *)a.v + seq * a.dv + row0;
+    const TIn *bseq = (const TIn *)a.beta + seq * a.dv + row0;
+    const TIn *dseq = (const TIn *)a.dt + seq;
+    const size_t kq_tok = (size_t)a.H * D, vb_tok = (size_t)a.H * a.dv;
+    const size_t ystride = (size_t)a.H * a.dv;
+    TOut *ybase = (TOut *)a.y + seq * a.dv + row;
+    const int nchunks = (a.T + C - 1) / C;
+    WideStager<D, TIn> st;
+    if (nchunks > 0) {
+        st.load(kseq, qseq, vseq, bseq, dseq, a.T, a.H, a.dv, tid);
+        st.commit(lds, A, Ip, tid);
+        __syncthreads();
+    }
+#pragma unroll 1
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * C;
+        const bool more = c + 1 < nchunks;
+        if (more) {
+            const size_t tn = (size_t)(t0 + C);
+            st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
+                    dseq + tn * a.H, a.T - (t0 + C), a.H, a.dv, tid);
+        }
+        const float *cur = lds + (c & 1) * W::kBufFloats;
+        const float *rows = cur + C * W::kColFloats + 2 * wave;
+        int goff = C * (W::kColFloats + 2 * W::kRows);
+        asm volatile("" : "+v"(goff));
+        const float *gates = cur + goff;
+#pragma unroll 1
+        for (int u = 0; u < C; ++u) {
+            const float2 gc = *(const float2 *)(gates + 2 * u);
+            const float2 rb = *(const float2 *)(rows + u * 2 * W::kRows);
+            const float *ct = cur + u * W::kColFloats + 4 * lane;
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < W::kVecs; ++m) {
+                float kk[4], k2[4], qq[4];
+                vecf<4>::ld(ct + 256 * m, kk);
+                if (W::kStageK2) vecf<4>::ld(ct + D + 256 * m, k2);
+                vecf<4>::ld(ct + W::kQ + 256 * m, qq);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = 4 * m + e;
+                    if (!W::kStageK2) k2[e] = kk[e] * kk[e];
+                    const float w = fmaf(rb.x, k2[e], gc.y);
+                    I[s] = fmaf(gc.x, I[s], w);
+                    M[s] = fmaf(gc.x, M[s], rb.y * kk[e]);
+                    const float r = __builtin_amdgcn_rcpf(I[s]);
+                    acc = fmaf(M[s] * r, qq[e], acc);
+                }
+            }
+            const float yv = sum_rows4(row16_sum(acc));
+            if (lane == 0 && t0 + u < a.T)
+                ybase[(size_t)(t0 + u) * ystride] = io<TOut>::from_f32(yv);
+        }
+        if (more) st.commit(lds + ((c + 1) & 1) * W::kBufFloats, A, Ip, tid);
+        __syncthreads();
+    }
+    if (a.muT) {
+#pragma unroll
+        for (int m = 0; m < W::kVecs; ++m) {
+            float mu[4], ii[4];
+            if (a.T == 0 && a.mu0) {
+                vecf<4>::ld(a.mu0 + srow + W::col(lane, m, 0), mu);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mu[e] = M[4 * m + e] / I[4 * m + e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ii[e] = I[4 * m + e];
+            vecf<4>::st(a.muT + srow + W::col(lane, m, 0), mu);
+            vecf<4>::st(a.IT + srow + W::col(lane, m, 0), ii);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // frozen-importance forward (the Mamba2 limit) on the matrix cores
 // ---------------------------------------------------------------------------
 //
@@ -1876,7 +2112,11 @@ __device__ inline float group_sum(float x) {
 
 template <int DK, typename TIn, typename TOut>
 __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
-    constexpr int kTPR = DK / 4;                    // threads per value row, 4 columns each
+    // threads per value row (4 columns each, or for wide heads 32 threads
+    // walking the row in 4-wide vectors 128 columns apart: coalesced 512-byte
+    // spans per vector, few registers)
+    constexpr int kTPR = DK / 4 < 32 ? DK / 4 : 32;
+    constexpr int kVecs = DK / (4 * kTPR);
     constexpr int kRowsPerBlock = kStepThreads / kTPR;
     const int tid = threadIdx.x;
     const long long row = (long long)blockIdx.x * kRowsPerBlock + tid / kTPR;
@@ -1891,44 +2131,44 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
 
     const TIn *qp = (const TIn *)a.q + bh * DK + j0;
     const TIn *kp = (const TIn *)a.k + bh * DK + j0;
-    float qq[4], kk[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { qq[e] = io<TIn>::to_f32(qp[e]); kk[e] = io<TIn>::to_f32(kp[e]); }
     const float bt = io<TIn>::to_f32(((const TIn *)a.beta)[bh * a.dv + i]);
     const float vv = io<TIn>::to_f32(((const TIn *)a.v)[bh * a.dv + i]);
     const float bv = a.vstar ? vv : bt * vv;
     const float2 gc = gate(a.A[h], io<TIn>::to_f32(((const TIn *)a.dt)[bh]), a.ipe ? 1.f : a.Ip[h]);
-    // c per entry: (1 - alpha) I_prior[h] or (1 - alpha) I_prior[h, i, j]
-    float cc[4] = {gc.y, gc.y, gc.y, gc.y};
-    if (a.ipe) {
-        const f32x4 ip4 = *(const f32x4 *)(a.Ip + ((size_t)h * a.dv + i) * DK + j0);
+    float acc = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) cc[e] = gc.y * ip4[e];
-    }
-
-    f32x4 *mup = (f32x4 *)(a.mu + r * DK + j0);
-    f32x4 *Ipp = (f32x4 *)(a.I + r * DK + j0);
-    const f32x4 mu4 = __builtin_nontemporal_load(mup);
-    const f32x4 I4 = __builtin_nontemporal_load(Ipp);
-    const float mu[4] = {mu4[0], mu4[1], mu4[2], mu4[3]};
-    const float Io[4] = {I4[0], I4[1], I4[2], I4[3]};
-    float mun[4], In[4], acc = 0.f;
+    for (int m = 0; m < kVecs; ++m) {
+        const int jm = 4 * kTPR * m;                       // column offset of this vector
+        float qq[4], kk[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        In[e] = fmaf(gc.x, Io[e], fmaf(bt, kk[e] * kk[e], cc[e]));
-        const float num = fmaf(gc.x * Io[e], mu[e], bv * kk[e]);   // alpha I mu + beta v k
-        mun[e] = num / In[e];
-        acc = fmaf(mun[e], qq[e], acc);
+        for (int e = 0; e < 4; ++e) { qq[e] = io<TIn>::to_f32(qp[jm + e]); kk[e] = io<TIn>::to_f32(kp[jm + e]); }
+        // c per entry: (1 - alpha) I_prior[h] or (1 - alpha) I_prior[h, i, j]
+        float cc[4] = {gc.y, gc.y, gc.y, gc.y};
+        if (a.ipe) {
+            const f32x4 ip4 = *(const f32x4 *)(a.Ip + ((size_t)h * a.dv + i) * DK + j0 + jm);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cc[e] = gc.y * ip4[e];
+        }
+        f32x4 *mup = (f32x4 *)(a.mu + r * DK + j0 + jm);
+        f32x4 *Ipp = (f32x4 *)(a.I + r * DK + j0 + jm);
+        const f32x4 mu4 = __builtin_nontemporal_load(mup);
+        const f32x4 I4 = __builtin_nontemporal_load(Ipp);
+        float mun[4], In[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            In[e] = fmaf(gc.x, I4[e], fmaf(bt, kk[e] * kk[e], cc[e]));
+            const float num = fmaf(gc.x * I4[e], mu4[e], bv * kk[e]);   // alpha I mu + beta v k
+            mun[e] = num / In[e];
+            acc = fmaf(mun[e], qq[e], acc);
+        }
+        if (valid) {
+            __builtin_nontemporal_store(f32x4{mun[0], mun[1], mun[2], mun[3]}, mup);
+            __builtin_nontemporal_store(f32x4{In[0], In[1], In[2], In[3]}, Ipp);
+        }
     }
     const float yv = group_sum<kTPR>(acc);
-    if (valid) {
-        const f32x4 mo = {mun[0], mun[1], mun[2], mun[3]};
-        const f32x4 io4 = {In[0], In[1], In[2], In[3]};
-        __builtin_nontemporal_store(mo, mup);
-        __builtin_nontemporal_store(io4, Ipp);
-        if (tid % kTPR == 0)
-            ((TOut *)a.y)[r] = io<TOut>::from_f32(yv);
-    }
+    if (valid && tid % kTPR == 0)
+        ((TOut *)a.y)[r] = io<TOut>::from_f32(yv);
 }
 
 // ---------------------------------------------------------------------------
@@ -1937,9 +2177,13 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
 
 inline bool aligned_to(const void *p, size_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
 inline bool head_ok(int d) { return d == 32 || d == 64 || d == 128; }
+// key widths of the exact forward and the decode step: up to a head as wide as
+// the model (the pages' recurrent-kernel measurement goes to 2048)
+inline bool fwd_dk_ok(int d) { return head_ok(d) || d == 256 || d == 512 || d == 1024 || d == 2048; }
 // value rows run in blocks of 16 (64 on the frozen path), so d_v may be any
 // such multiple up to 1024 (d_v = 2 d_k, the pages' value expansion, included)
 inline bool dv_ok(int d) { return d >= 16 && d <= 1024 && d % 16 == 0; }
+inline bool fwd_dv_ok(int d) { return d >= 16 && d <= 4096 && d % 16 == 0; }
 constexpr int kFlagsKnown = PALIMPSA_VSTAR | PALIMPSA_PRIOR_PER_ENTRY;
 inline bool dtype_ok(int t) { return t == PALIMPSA_F32 || t == PALIMPSA_BF16; }
 
@@ -1978,8 +2222,30 @@ palimpsa_status launch_fwd_c(const FwdArgs &a, int C, hipStream_t s) {
     }
 }
 
+template <int D, typename TIn, typename TOut>
+palimpsa_status launch_wide(FwdArgs a, hipStream_t s) {
+    const size_t lds = (size_t)2 * WideCfg<D>::kBufFloats * sizeof(float);
+    auto kern = wide_fwd_kernel<D, TIn, TOut>;
+    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return PALIMPSA_ERR_HIP;
+    const long long nwg = (long long)a.B * a.H * (a.dv / WideCfg<D>::kRows);
+    if (nwg > 0x7fffffffLL) return PALIMPSA_ERR_UNSUPPORTED;
+    a.nwg = (int)nwg;
+    a.xcd_remap = (a.nwg % 8 == 0) ? 1 : 0;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(kern, dim3(a.nwg), dim3(kThreads), lds, s, a);
+    return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
+}
+
 template <typename TIn, typename TOut>
 palimpsa_status launch_fwd_d(const FwdArgs &a, int dk, int C, bool ipe, hipStream_t s) {
+    switch (dk) {
+    case 256: return launch_fwd_t<256, 16, TIn, TOut, false>(a, s);   // 102.6 KB of LDS at C = 16
+    case 512: return launch_wide<512, TIn, TOut>(a, s);
+    case 1024: return launch_wide<1024, TIn, TOut>(a, s);
+    case 2048: return launch_wide<2048, TIn, TOut>(a, s);
+    default: break;
+    }
     switch (dk * 2 + (ipe ? 1 : 0)) {
     case 64: return launch_fwd_c<32, TIn, TOut, false>(a, C, s);
     case 65: return launch_fwd_c<32, TIn, TOut, true>(a, C, s);
@@ -2308,7 +2574,7 @@ palimpsa_status palimpsa_fwd_frozen(const void *q, const void *k, const void *v,
 
 
 size_t palimpsa_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segments) {
-    if (B <= 0 || H <= 0 || T < 0 || !head_ok(dk) || !dv_ok(dv) || segments < 0) return 0;
+    if (B <= 0 || H <= 0 || T < 0 || !fwd_dk_ok(dk) || !fwd_dv_ok(dv) || segments < 0 || dk > 256) return 0;
     return plan_segments(B, T, H, dk, dv, segments, device_cus()).ws_bytes;
 }
 
@@ -2332,8 +2598,13 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
         return PALIMPSA_ERR_INVALID_ARG;
     if (segments < 0 || segments > 64 || (workspace_bytes > 0 && !workspace))
         return PALIMPSA_ERR_INVALID_ARG;
-    if (!head_ok(dk) || !dv_ok(dv))
+    if (!fwd_dk_ok(dk) || !fwd_dv_ok(dv))
         return PALIMPSA_ERR_UNSUPPORTED;
+    // heads wider than 128 keys: per-head prior, v as given, one pass (no time split)
+    if (dk > 128 && (flags != 0 || (dv % 16) != 0 || (dk == 256 && dv > 1024)))
+        return PALIMPSA_ERR_UNSUPPORTED;
+    if (dk > 256) segments = segments >= 2 ? -1 : 1;
+    if (segments < 0) return PALIMPSA_ERR_UNSUPPORTED;
     const bool ipe = (flags & PALIMPSA_PRIOR_PER_ENTRY) != 0;
     // 128-bit accesses: q, k, v, beta, the state arrays (and a per-entry prior) and
     // the workspace; element-wise: the rest
@@ -2392,7 +2663,7 @@ palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
         return PALIMPSA_ERR_INVALID_ARG;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
         return PALIMPSA_ERR_INVALID_ARG;
-    if (!head_ok(dk) || !dv_ok(dv))
+    if (!fwd_dk_ok(dk) || !fwd_dv_ok(dv))
         return PALIMPSA_ERR_UNSUPPORTED;
     const bool ipe = (flags & PALIMPSA_PRIOR_PER_ENTRY) != 0;
     // 128-bit accesses: the state (and a per-entry prior); element-wise: the rest
@@ -2413,7 +2684,7 @@ palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
     a.B = B; a.H = H; a.dv = dv; a.rows = rows;
     a.vstar = (flags & PALIMPSA_VSTAR) ? 1 : 0;
     a.ipe = ipe ? 1 : 0;
-    const int rows_per_block = kStepThreads / (dk / 4);
+    const int rows_per_block = kStepThreads / (dk / 4 < 32 ? dk / 4 : 32);
     const long long blocks = (rows + rows_per_block - 1) / rows_per_block;
     if (blocks > 0x7fffffffLL) return PALIMPSA_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
@@ -2431,6 +2702,10 @@ palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
     switch (dk) {
     case 32: PALIMPSA_STEP_TYPES(32); break;
     case 64: PALIMPSA_STEP_TYPES(64); break;
+    case 256: PALIMPSA_STEP_TYPES(256); break;
+    case 512: PALIMPSA_STEP_TYPES(512); break;
+    case 1024: PALIMPSA_STEP_TYPES(1024); break;
+    case 2048: PALIMPSA_STEP_TYPES(2048); break;
     default: PALIMPSA_STEP_TYPES(128); break;
     }
 #undef PALIMPSA_STEP_TYPES

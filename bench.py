@@ -207,6 +207,28 @@ def blockdiag_extra(torch, pm, w, g, steps):
                          "per_entry": "10.5 VALU + 0.5 v_rcp_f32 = 11.5 slots, 16.5 flops"}}
 
 
+def fig7_extra(torch, pm, workloads, dev, D, steps):
+    """One head as wide as the model, the shape of the pages' recurrent-kernel
+    measurement (B=16, L=2048, H=1, d_k = d_v = D; bf16 inputs, fp32 state),
+    through the chunked forward (the state stays on chip for the whole
+    sequence, as in a recurrent kernel)."""
+    w = workloads.WORKLOADS[2].with_(name="recurrent-shape B16 L2048 H1 D%d" % D, B=16, T=2048, H=1, dk=D, dv=D)
+    inp = workloads.make_inputs(w, seed=70 + D // 512)
+    g = {n: (x.to(dev) if isinstance(x, torch.Tensor) else x) for n, x in inp.items()}
+    y = torch.empty(w.B, w.T, w.H, w.dv, dtype=w.dtype, device=dev)
+    muT = torch.empty(w.B, w.H, w.dv, w.dk, device=dev)
+    IT = torch.empty_like(muT)
+    fn = lambda: pm.fwd_chunked(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], y=y, muT=muT, IT=IT)
+    _, per = time_launches(fn, steps, 2, torch)
+    avg_s = sum(per) / len(per) / 1e3
+    updates = w.B * w.H * w.T * w.dv * w.dk
+    achieved = updates * FLOPS_PER_UPDATE / avg_s / 1e12
+    return {"workload": w.name, "tokens_per_s": w.B * w.T / avg_s, "ms_per_launch": avg_s * 1e3,
+            "state_updates_per_s": updates / avg_s,
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": alu_peak_tflops(), "unit": "TFLOP/s",
+                         "frac": achieved / alu_peak_tflops(), "traffic": None}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,6 +316,7 @@ def main():
         out["backward"] = backward_extra(torch, pm, workloads, w, g, max(5, args.steps // 5))
         out["frozen"] = frozen_extra(torch, pm, w, g, max(20, args.steps))
         out["blockdiag"] = blockdiag_extra(torch, pm, w, g, max(20, args.steps // 2))
+        out["recurrent_shape"] = [fig7_extra(torch, pm, workloads, dev, D, 5) for D in (512, 2048)]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads or w.B * w.H)
     print(json.dumps(out), flush=True)

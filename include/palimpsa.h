@@ -41,7 +41,12 @@
  *    finite.  Violations give unspecified values, never a fault.
  *  - Supported head sizes: dk in {32, 64, 128}; dv any multiple of 16 from
  *    16 to 1024 (so the value expansion dv = 2 dk of the pages' model is
- *    covered).  The frozen path's limits are stated at its declaration.
+ *    covered).  The chunked forward and the decode step also take heads as
+ *    wide as the model (the pages' recurrent-kernel measurement, slides
+ *    frame 22 / Fig. 7): dk in {256, 512, 1024, 2048} with dv a multiple of 16
+ *    up to 4096 (up to 1024 at dk = 256), per-head prior, flags 0, and no
+ *    time split for dk >= 512.  The other paths' limits are stated at their
+ *    declarations.
  *  - Options (`flags`, a bit mask of palimpsa_flags) of the exact forward,
  *    the decode step and the backward:
  *      PALIMPSA_VSTAR            v holds v* = beta . v, the write itself (the

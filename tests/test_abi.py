@@ -56,6 +56,17 @@ def test_status_strings(lib):
 FAKE = 0x10000       # 16-byte aligned host address, never dereferenced
 
 
+def _no_gpu_here():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+# The invalid-call tables pass fake pointers: a case that validation let
+# through would launch a kernel on them.  They run on a host without a GPU
+# (there any such launch fails with PALIMPSA_ERR_HIP and the test catches it).
+invalid_calls = pytest.mark.skipif(not _no_gpu_here(), reason="invalid-call tables run on a host without a GPU")
+
+
 def _fwd_args(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dt=FAKE, A=FAKE, Ip=FAKE, mu0=None, I0=None,
              y=FAKE, muT=FAKE, IT=FAKE, B=2, T=8, H=3, dk=64, dv=64, chunk=0, segments=0,
@@ -72,8 +83,10 @@ FWD_CASES = [
     (dict(Ip=None), 1), (dict(y=None), 1), (dict(mu0=FAKE), 1), (dict(I0=FAKE), 1),
     (dict(muT=None), 1), (dict(IT=None), 1), (dict(B=0), 1), (dict(H=0), 1), (dict(T=-1), 1),
     (dict(dk=0), 1), (dict(ind=2), 1), (dict(outd=-1), 1), (dict(chunk=12), 1),
-    (dict(chunk=128), 1), (dict(dk=48), 2), (dict(dv=1040), 2), (dict(dv=24), 2), (dict(dk=16), 2),
+    (dict(chunk=128), 1), (dict(dk=48), 2), (dict(dv=4104), 2), (dict(dv=24), 2), (dict(dk=16), 2),
     (dict(flags=4), 1), (dict(flags=-1), 1), (dict(flags=2, Ip=FAKE + 4), 3),
+    (dict(dk=4096), 2), (dict(dk=384), 2), (dict(dk=512, flags=1), 2), (dict(dk=2048, flags=2), 2),
+    (dict(dk=512, segments=2), 2), (dict(dv=4112), 2), (dict(dk=256, dv=2048), 2), (dict(dk=1024, dv=24), 2),
     (dict(q=FAKE + 4), 3), (dict(v=FAKE + 8), 3),
     (dict(mu0=FAKE + 4, I0=FAKE), 3), (dict(IT=FAKE + 12), 3), (dict(dt=FAKE + 1), 3),
     (dict(y=FAKE + 1), 3), (dict(A=FAKE + 2), 3), (dict(beta=FAKE + 2), 3),
@@ -98,6 +111,7 @@ def test_workspace_size_host_logic(lib):
     assert pm.workspace_size(1, 64, 2, 48, 64, 0) == 0
 
 
+@invalid_calls
 @pytest.mark.parametrize("over,status", FWD_CASES)
 def test_fwd_rejects_invalid_calls(lib, over, status):
     assert lib.palimpsa_fwd_chunked(*_fwd_args(**over)) == status
@@ -116,10 +130,11 @@ STEP_CASES = [
     (dict(B=0), 1), (dict(H=-2), 1), (dict(ind=5), 1), (dict(dk=100), 2), (dict(dv=8), 2),
     (dict(mu=FAKE + 4), 3), (dict(I=FAKE + 8), 3), (dict(k=FAKE + 1), 3), (dict(dt=FAKE + 1), 3),
     (dict(y=FAKE + 3), 3), (dict(Ip=FAKE + 2), 3), (dict(flags=4), 1), (dict(dv=40), 2),
-    (dict(flags=2, Ip=FAKE + 8), 3),
+    (dict(flags=2, Ip=FAKE + 8), 3), (dict(dk=4096), 2), (dict(dk=768), 2),
 ]
 
 
+@invalid_calls
 @pytest.mark.parametrize("over,status", STEP_CASES)
 def test_step_rejects_invalid_calls(lib, over, status):
     assert lib.palimpsa_step(*_step_args(**over)) == status
@@ -165,6 +180,7 @@ FROZEN_CASES = [
 ]
 
 
+@invalid_calls
 @pytest.mark.parametrize("over,status", FROZEN_CASES)
 def test_frozen_rejects_invalid_calls(lib, over, status):
     assert lib.palimpsa_fwd_frozen(*_frozen_args(**over)) == status
@@ -195,6 +211,7 @@ BWD_CASES = [
 ]
 
 
+@invalid_calls
 @pytest.mark.parametrize("over,status", BWD_CASES)
 def test_bwd_rejects_invalid_calls(lib, over, status):
     assert lib.palimpsa_bwd(*_bwd_args(**over)) == status
@@ -237,6 +254,7 @@ BD_CASES = [
 ]
 
 
+@invalid_calls
 @pytest.mark.parametrize("over,status", BD_CASES)
 def test_blockdiag_rejects_invalid_calls(lib, over, status):
     assert lib.palimpsa_fwd_blockdiag(*_bd_args(**over)) == status

@@ -776,3 +776,49 @@ def test_blockdiag_layer760m_sampled():
     assert_close("blockdiag y (sampled)", to_np(y)[bs, :, hs, :].transpose(1, 0, 2)[None], y_ref, tol_for(w.dtype))
     assert_close("blockdiag muT (sampled)", to_np(muT)[bs, hs][None], mu_ref, TOL_F32)
     assert_close("blockdiag PT (sampled)", to_np(PT)[bs, hs][None], P_ref, TOL_F32)
+
+
+# ---------------------------------------------------------------------------
+# heads as wide as the model (the pages' recurrent-kernel measurement, Fig. 7):
+# dk in {256, 512, 1024, 2048}
+# ---------------------------------------------------------------------------
+
+WIDE_CASES = [
+    # B, H, T, dk, dv, dtype, start state
+    (2, 1, 45, 256, 256, torch.float32, True),
+    (1, 2, 37, 512, 512, torch.float32, False),
+    (2, 1, 21, 512, 48, torch.bfloat16, True),
+    (1, 1, 30, 1024, 64, torch.float32, True),
+    (1, 1, 19, 2048, 32, torch.float32, False),
+    (1, 1, 9, 2048, 2048, torch.bfloat16, True),
+]
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv,dtype,state", WIDE_CASES)
+def test_wide_heads_forward_and_step(B, H, T, dk, dv, dtype, state):
+    w = workloads.WORKLOADS[0].with_(B=B, H=H, dk=dk, dv=dv, dtype=dtype, A_mode="logspace16")
+    _announce("wide head fwd+step", B=B, H=H, T=T, dk=dk, dv=dv, dtype=dtype, state=state)
+    inp = workloads.make_inputs(w, T=T, seed=dk + dv + T)
+    if state:
+        inp["mu0"], inp["I0"] = workloads.random_state(B, H, dv, dk, inp["I_prior"], seed=dk)
+    y, muT, IT = _run_fwd(inp)
+    _compare_full(inp, y, muT, IT, tol_for(dtype))
+    d = {n: x.to(DEV) for n, x in workloads.decode_inputs(w, 3).items()}
+    ref = oracle.step(**{n: d[n].cpu() for n in d}, A=inp["A"], I_prior=inp["I_prior"], mu=to_np(muT), I=to_np(IT))
+    ys = _pm().step(d["q"], d["k"], d["v"], d["beta"], d["dt"], inp["A"].to(DEV), inp["I_prior"].to(DEV), muT, IT)
+    torch.cuda.synchronize()
+    assert_close("wide step y", ys, ref[0], tol_for(dtype))
+    assert_close("wide step mu", muT, ref[1], TOL_F32)
+    assert_close("wide step I", IT, ref[2], TOL_F32)
+
+
+def test_wide_head_256_time_split_matches_single_pass():
+    w = workloads.WORKLOADS[0].with_(B=1, H=1, dk=256, dv=64, A_mode="logspace16")
+    _announce("dk=256 time split", T=700, dk=256, dv=64)
+    inp = workloads.make_inputs(w, T=700, seed=256)
+    g = to_device(inp, DEV)
+    y1, mu1, I1 = _pm().fwd_chunked(*gpu_args(g), segments=1)
+    y3, mu3, I3 = _pm().fwd_chunked(*gpu_args(g), segments=3)
+    torch.cuda.synchronize()
+    assert rel_err(y3, y1) <= 1e-5 and rel_err(mu3, mu1) <= 1e-5 and rel_err(I3, I1) <= 1e-6
+    _compare_full(inp, y1, mu1, I1, TOL_F32)
