@@ -94,7 +94,7 @@ def _check(t, name, shape, dtype, device):
         raise ValueError("%s must be contiguous" % name)
 
 
-VSTAR, PRIOR_PER_ENTRY = 1, 2
+VSTAR, PRIOR_PER_ENTRY, SAVE_CHECKPOINTS, CHECKPOINTS_SAVED = 1, 2, 4, 8
 
 
 def _prior_flags(I_prior, H, dv, dk, dev, vstar):
@@ -116,14 +116,20 @@ def workspace_size(B, T, H, dk, dv, segments: int = 0) -> int:
 
 def fwd_chunked(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None, chunk: int = 0,
                 out_dtype=None, y=None, muT=None, IT=None, write_state: bool = True,
-                segments: int = 0, workspace=None, vstar: bool = False):
+                segments: int = 0, workspace=None, vstar: bool = False,
+                save_checkpoints: bool = False):
     """Chunked forward.  Returns ``(y, muT, IT)``; ``muT``/``IT`` are None when
     ``write_state`` is False.  Outputs are allocated unless passed in (they may
     alias ``mu0``/``I0`` for an in-place resume).  ``segments`` (0 = library's
     choice) selects the time split; its workspace is allocated here unless a
     uint8 device tensor is passed as ``workspace``.  ``I_prior`` is ``[H]`` or
     ``[H, dv, dk]`` (a prior per state entry); ``vstar`` means ``v`` holds
-    ``beta * v``."""
+    ``beta * v``.
+
+    ``save_checkpoints`` (the training forward): ``workspace`` must then be a
+    backward workspace (``bwd_workspace_size`` bytes), into which the forward
+    also stores the states the backward needs; pass it to ``bwd`` with
+    ``checkpoints_saved=True`` to skip their recomputation."""
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
     B, T, H, dk = q.shape
@@ -144,6 +150,10 @@ def fwd_chunked(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None, chunk: int = 0
     _check(q, "q", (B, T, H, dk), in_dtype, dev)
     _check(A, "A", (H,), torch.float32, dev)
     flags = _prior_flags(I_prior, H, dv, dk, dev, vstar)
+    if save_checkpoints:
+        if workspace is None:
+            raise ValueError("save_checkpoints needs a backward workspace (bwd_workspace_size bytes)")
+        flags |= SAVE_CHECKPOINTS
     if (mu0 is None) != (I0 is None):
         raise ValueError("give both mu0 and I0, or neither")
     if mu0 is not None:
@@ -272,7 +282,8 @@ def bwd_workspace_size(B, T, H, dk, dv, flags: int = 0) -> int:
 
 
 def bwd(q, k, v, beta, dt, A, I_prior, gy, mu0=None, I0=None, gmuT=None, gIT=None,
-        want_state_grads: bool = True, workspace=None, out=None, vstar: bool = False):
+        want_state_grads: bool = True, workspace=None, out=None, vstar: bool = False,
+        checkpoints_saved: bool = False):
     """Backward of ``fwd_chunked`` for ``L = <gy, y> + <gmuT, muT> + <gIT, IT>``.
 
     Takes the forward's inputs (the library recomputes the states) and returns
@@ -282,7 +293,10 @@ def bwd(q, k, v, beta, dt, A, I_prior, gy, mu0=None, I0=None, gmuT=None, gIT=Non
     ``workspace`` a contiguous uint8 device tensor of at least
     ``bwd_workspace_size`` bytes (allocated here otherwise).  With a prior per
     state entry (``I_prior`` ``[H, dv, dk]``) ``gIp`` has that shape; with
-    ``vstar`` (``v`` holds ``beta * v``) ``gv`` is the gradient w.r.t. it."""
+    ``vstar`` (``v`` holds ``beta * v``) ``gv`` is the gradient w.r.t. it.
+    ``checkpoints_saved``: ``workspace`` holds the checkpoints a
+    ``fwd_chunked(..., save_checkpoints=True)`` call on the same inputs stored,
+    and the backward skips recomputing them."""
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
     B, T, H, dk = q.shape
@@ -299,6 +313,10 @@ def bwd(q, k, v, beta, dt, A, I_prior, gy, mu0=None, I0=None, gmuT=None, gIT=Non
     _check(gy, "gy", (B, T, H, dv), gy.dtype, dev)
     _check(A, "A", (H,), torch.float32, dev)
     flags = _prior_flags(I_prior, H, dv, dk, dev, vstar)
+    if checkpoints_saved:
+        if workspace is None:
+            raise ValueError("checkpoints_saved needs the workspace the training forward filled")
+        flags |= CHECKPOINTS_SAVED
     if (mu0 is None) != (I0 is None):
         raise ValueError("give both mu0 and I0, or neither")
     for t, name in ((mu0, "mu0"), (I0, "I0"), (gmuT, "gmuT"), (gIT, "gIT")):

@@ -130,7 +130,8 @@ struct FwdArgs {
     int seg_len;       // tokens per time segment (a multiple of the chunk)
     int nseg;          // time segments (1: no split)
     float *ws;         // segment summaries, see SegWs
-    float *ck;         // backward checkpoints (kCheckpoint mode), see bwd_kernel
+    float *ck;         // backward checkpoints (kCheckpoint mode, training forward), see bwd_kernel
+    float *ck_sink;    // training forward: one block's worth of discarded stores
     int nsb;           // checkpoints per sequence: ceil(T / kSB)
     int vstar;         // 1: v holds beta . v (the write itself)
 };
@@ -343,6 +344,32 @@ __device__ inline float row16_transpose_sum(const float (&x)[16], int g) {
     return (b0 ? s3[1] : s3[0]) + dpp_from<0xB1>(b0 ? s3[0] : s3[1]);                 // quad_perm [1,0,3,2]
 }
 
+// A workgroup's checkpoint block: the lane's values (M[0, N), I[0, N)),
+// N = DK / 16 in {2, 4, 8}, as 2N/4 float4s, float4 i of thread tid at
+// blk + 4 (i * kThreads + tid), so each access instruction covers 1 KiB of
+// contiguous memory.  Written once and read once much later: non-temporal.
+template <int N>
+__device__ inline void store_pair(float *blk, int tid, const float *M, const float *I) {
+    float v[2 * N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) { v[i] = M[i]; v[N + i] = I[i]; }
+#pragma unroll
+    for (int i = 0; i < 2 * N; i += 4)
+        __builtin_nontemporal_store(f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]},
+                                    (f32x4 *)(blk + 4 * ((i / 4) * kThreads + tid)));
+}
+template <int N>
+__device__ inline void load_pair(const float *blk, int tid, float *M, float *I) {
+    float v[2 * N];
+#pragma unroll
+    for (int i = 0; i < 2 * N; i += 4) {
+        const f32x4 x = __builtin_nontemporal_load((const f32x4 *)(blk + 4 * ((i / 4) * kThreads + tid)));
+        v[i] = x[0]; v[i + 1] = x[1]; v[i + 2] = x[2]; v[i + 3] = x[3];
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) { M[i] = v[i]; I[i] = v[N + i]; }
+}
+
 // The per-token hot loop over one staged chunk.  Per token and lane: for each
 // of the lane's DK/16 state entries 6 VALU ops and one v_rcp_f32; the lane's
 // partial of y_t goes to a register.  Every 16 tokens one transposing
@@ -351,11 +378,19 @@ __device__ inline float row16_transpose_sum(const float (&x)[16], int g) {
 //
 // With a prior per state entry (IPE) the gate's c is staged as 1 - alpha and
 // scaled by the lane's prior ipe[s]: one more VALU op per entry and token.
-template <int DK, int C, typename TOut, bool IPE>
+//
+// With CKPT (the training forward, C = 16) the states before the chunk's
+// tokens 0 and kSB are also stored, as the backward's checkpoint pass would
+// store them, at the blocks ck_a and ck_b.  The caller points ck_b at a sink
+// when the sequence ends within the chunk's first kSB tokens: a data-dependent
+// branch or select in here costs the loop twice its registers.
+template <int DK, int C, typename TOut, bool IPE, bool CKPT>
 __device__ inline void compute_chunk(const float *buf, int left, float *M, float *I,
-                                     int row_local, int g, TOut *yrow, size_t ystride, const float *ipe) {
+                                     int row_local, int g, TOut *yrow, size_t ystride, const float *ipe,
+                                     float *ck_a = nullptr, float *ck_b = nullptr) {
     using LT = LaneTile<DK>;
     static_assert(C % kGroup == 0, "chunk must be a multiple of 16 tokens");
+    static_assert(!CKPT || (C == 16 && kGroup == 2 * kSB), "checkpointing forward runs chunk 16");
     const float *cbase = buf + LT::col(g, 0, 0);
     const float *rbase = buf + C * Stage<DK>::kColFloats + 2 * row_local;
     // The gate address is the same in every lane; holding it in a VGPR (the
@@ -372,6 +407,8 @@ __device__ inline void compute_chunk(const float *buf, int left, float *M, float
         float part[kGroup];
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) {
+            if (CKPT && u == 0) store_pair<LT::kCols>(ck_a, threadIdx.x, M, I);
+            if (CKPT && u == kSB) store_pair<LT::kCols>(ck_b, threadIdx.x, M, I);
             const float2 gc = *(const float2 *)(gg + 2 * u);                          // alpha, c
             const float2 rb = *(const float2 *)(rg + u * Stage<DK>::kRowFloats);      // beta, beta*v
             const float *ct = cg + u * Stage<DK>::kColFloats;
@@ -437,32 +474,6 @@ __device__ inline void summary_chunk(const float *buf, float *M, float *Ib, floa
     }
 }
 
-// A workgroup's checkpoint block: the lane's values (M[0, N), I[0, N)),
-// N = DK / 16 in {2, 4, 8}, as 2N/4 float4s, float4 i of thread tid at
-// blk + 4 (i * kThreads + tid), so each access instruction covers 1 KiB of
-// contiguous memory.  Written once and read once much later: non-temporal.
-template <int N>
-__device__ inline void store_pair(float *blk, int tid, const float *M, const float *I) {
-    float v[2 * N];
-#pragma unroll
-    for (int i = 0; i < N; ++i) { v[i] = M[i]; v[N + i] = I[i]; }
-#pragma unroll
-    for (int i = 0; i < 2 * N; i += 4)
-        __builtin_nontemporal_store(f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]},
-                                    (f32x4 *)(blk + 4 * ((i / 4) * kThreads + tid)));
-}
-template <int N>
-__device__ inline void load_pair(const float *blk, int tid, float *M, float *I) {
-    float v[2 * N];
-#pragma unroll
-    for (int i = 0; i < 2 * N; i += 4) {
-        const f32x4 x = __builtin_nontemporal_load((const f32x4 *)(blk + 4 * ((i / 4) * kThreads + tid)));
-        v[i] = x[0]; v[i + 1] = x[1]; v[i + 2] = x[2]; v[i + 3] = x[3];
-    }
-#pragma unroll
-    for (int i = 0; i < N; ++i) { M[i] = v[i]; I[i] = v[N + i]; }
-}
-
 // Checkpoint pass of the backward over one staged chunk: the forward update
 // without readout (the same 4 VALU ops per entry and token as the replay,
 // so the states are bit-identical to the forward's), storing (M, I) before
@@ -522,7 +533,7 @@ enum FwdMode { kReplay = 0, kSummary = 1, kCheckpoint = 2 };
 //
 // kSummary: segment s < nseg-1 runs from a zero state without readout and
 // writes its (M_loc, Ibar_loc, P) to the workspace.
-template <int DK, int C, typename TIn, typename TOut, int MODE, bool IPE>
+template <int DK, int C, typename TIn, typename TOut, int MODE, bool IPE, bool CKPT = false>
 __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
     using LT = LaneTile<DK>;
     extern __shared__ float lds[];
@@ -624,7 +635,7 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
     float P = 1.f;
     // checkpoints: [B*H][nsb][row block][thread][2 DK/16] floats
     const size_t ck_stride = (size_t)rb_per_head * kThreads * 2 * LT::kCols;
-    float *ckp = MODE == kCheckpoint
+    float *ckp = (MODE == kCheckpoint || CKPT)
                      ? a.ck + ((size_t)bh * a.nsb * rb_per_head + row0 / kRowsPerWG) * (kThreads * 2 * LT::kCols)
                      : nullptr;
     Stager<DK, C, TIn, MODE == kReplay> st;
@@ -643,8 +654,10 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
         }
         const float *cur = (c & 1) ? buf1 : buf0;
         if (MODE == kReplay)
-            compute_chunk<DK, C, TOut, IPE>(cur, ntok - t0, M, I, row_local, g, ybase + (size_t)t0 * ystride,
-                                            ystride, ipe);
+            compute_chunk<DK, C, TOut, IPE, CKPT>(
+                cur, ntok - t0, M, I, row_local, g, ybase + (size_t)t0 * ystride, ystride, ipe,
+                CKPT ? ckp + (size_t)(t0 / kSB) * ck_stride : nullptr,
+                CKPT ? (ntok - t0 > kSB ? ckp + (size_t)(t0 / kSB + 1) * ck_stride : a.ck_sink) : nullptr);
         else if (MODE == kSummary)
             summary_chunk<DK, C>(cur, M, I, P, row_local, g);
         else
@@ -2184,15 +2197,18 @@ inline bool fwd_dk_ok(int d) { return head_ok(d) || d == 256 || d == 512 || d ==
 // such multiple up to 1024 (d_v = 2 d_k, the pages' value expansion, included)
 inline bool dv_ok(int d) { return d >= 16 && d <= 1024 && d % 16 == 0; }
 inline bool fwd_dv_ok(int d) { return d >= 16 && d <= 4096 && d % 16 == 0; }
-constexpr int kFlagsKnown = PALIMPSA_VSTAR | PALIMPSA_PRIOR_PER_ENTRY;
+// option bits each entry point accepts
+constexpr int kFlagsOptions = PALIMPSA_VSTAR | PALIMPSA_PRIOR_PER_ENTRY;
+constexpr int kFlagsFwd = kFlagsOptions | PALIMPSA_SAVE_CHECKPOINTS;
+constexpr int kFlagsBwd = kFlagsOptions | PALIMPSA_CHECKPOINTS_SAVED;
 inline bool dtype_ok(int t) { return t == PALIMPSA_F32 || t == PALIMPSA_BF16; }
 
-template <int DK, int C, typename TIn, typename TOut, int MODE, bool IPE>
+template <int DK, int C, typename TIn, typename TOut, int MODE, bool IPE, bool CKPT = false>
 palimpsa_status launch_pass(FwdArgs a, int nseg_launched, hipStream_t s) {
     a.nwg = a.nwg_seg * nseg_launched;
     a.xcd_remap = (a.nwg % 8 == 0) ? 1 : 0;
     const size_t lds = fwd_lds_bytes<DK, C>();
-    auto kern = fwd_chunked_kernel<DK, C, TIn, TOut, MODE, IPE>;
+    auto kern = fwd_chunked_kernel<DK, C, TIn, TOut, MODE, IPE, CKPT>;
     if (lds > 64 * 1024) {
         if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
             return PALIMPSA_ERR_HIP;
@@ -2235,6 +2251,20 @@ palimpsa_status launch_wide(FwdArgs a, hipStream_t s) {
     (void)hipGetLastError();
     hipLaunchKernelGGL(kern, dim3(a.nwg), dim3(kThreads), lds, s, a);
     return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
+}
+
+// Training forward: the forward that also stores the backward's checkpoints
+// (one pass, chunk 16 as the checkpoint pass, so the states are the same bits).
+template <typename TIn, typename TOut>
+palimpsa_status launch_fwd_ckpt(const FwdArgs &a, int dk, bool ipe, hipStream_t s) {
+    switch (dk * 2 + (ipe ? 1 : 0)) {
+    case 64: return launch_pass<32, 16, TIn, TOut, kReplay, false, true>(a, 1, s);
+    case 65: return launch_pass<32, 16, TIn, TOut, kReplay, true, true>(a, 1, s);
+    case 128: return launch_pass<64, 16, TIn, TOut, kReplay, false, true>(a, 1, s);
+    case 129: return launch_pass<64, 16, TIn, TOut, kReplay, true, true>(a, 1, s);
+    case 257: return launch_pass<128, 16, TIn, TOut, kReplay, true, true>(a, 1, s);
+    default: return launch_pass<128, 16, TIn, TOut, kReplay, false, true>(a, 1, s);
+    }
 }
 
 template <typename TIn, typename TOut>
@@ -2342,7 +2372,7 @@ palimpsa_status launch_frozen(const FrozenArgs &a, hipStream_t s) {
 //   pI0   [B*H][dv/16]                      row-block sums of gI0
 //   pip   [B*H][dv][dk]                     per-entry prior only: per-sequence gI_prior
 struct BwdWs {
-    float *ck, *pqk, *ps, *gabh, *gibh, *pI0, *pip;
+    float *ck, *pqk, *ps, *gabh, *gibh, *pI0, *pip, *sink;
     size_t bytes;
 };
 BwdWs plan_bwd_ws(void *base, int B, int T, int H, int dk, int dv, bool ipe) {
@@ -2357,11 +2387,14 @@ BwdWs plan_bwd_ws(void *base, int B, int T, int H, int dk, int dv, bool ipe) {
     const size_t o_ck = take(bh * nsb * 2 * dv * dk), o_pqk = take(nrb * bth * 2 * dk), o_ps = take(nrb * bth * 2);
     const size_t o_ga = take(bh), o_gi = take(bh), o_pi = take(bh * nrb);
     const size_t o_pip = ipe ? take(bh * dv * dk) : off;
+    // the training forward's discarded checkpoint stores (one workgroup block)
+    const size_t o_sink = take((size_t)kThreads * 2 * (dk / kLanesPerRow));
     BwdWs w;
     char *c = (char *)base;
     w.ck = (float *)(c + o_ck); w.pqk = (float *)(c + o_pqk); w.ps = (float *)(c + o_ps);
     w.gabh = (float *)(c + o_ga); w.gibh = (float *)(c + o_gi); w.pI0 = (float *)(c + o_pi);
     w.pip = ipe ? (float *)(c + o_pip) : nullptr;
+    w.sink = (float *)(c + o_sink);
     w.bytes = off;
     return w;
 }
@@ -2369,7 +2402,7 @@ BwdWs plan_bwd_ws(void *base, int B, int T, int H, int dk, int dv, bool ipe) {
 template <int DK, typename TIn, typename TG, bool IPE>
 palimpsa_status launch_bwd_t(const FwdArgs &fa, const BwdArgs &ba, const BwdWs &w, float *gq, float *gk,
                              float *gdt, float *gA, float *gIp, int dt_bf16, hipStream_t s) {
-    if (ba.T > 0) {
+    if (ba.T > 0 && fa.ck) {   // ck NULL: the training forward stored the checkpoints already
         const palimpsa_status st = launch_pass<DK, 16, TIn, float, kCheckpoint, IPE>(fa, 1, s);
         if (st != PALIMPSA_OK) return st;
     }
@@ -2474,7 +2507,7 @@ palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void 
 }
 
 size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv, int flags) {
-    if (B <= 0 || H <= 0 || T < 0 || !head_ok(dk) || !dv_ok(dv) || (flags & ~kFlagsKnown)) return 0;
+    if (B <= 0 || H <= 0 || T < 0 || !head_ok(dk) || !dv_ok(dv) || (flags & ~(kFlagsFwd | kFlagsBwd))) return 0;
     return plan_bwd_ws(nullptr, B, T, H, dk, dv, (flags & PALIMPSA_PRIOR_PER_ENTRY) != 0).bytes;
 }
 
@@ -2486,7 +2519,7 @@ palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const 
                              int B, int T, int H, int dk, int dv,
                              palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype, int flags,
                              void *workspace, size_t workspace_bytes, void *stream) {
-    if (!A || !I_prior || !gA || !gIp || !workspace || (flags & ~kFlagsKnown))
+    if (!A || !I_prior || !gA || !gIp || !workspace || (flags & ~kFlagsBwd))
         return PALIMPSA_ERR_INVALID_ARG;
     if (T > 0 && (!q || !k || !v || !beta || !dt || !gy || !gq || !gk || !gv || !gbeta || !gdt))
         return PALIMPSA_ERR_INVALID_ARG;
@@ -2519,7 +2552,8 @@ palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const 
     fa.B = B; fa.T = T; fa.H = H; fa.dv = dv;
     fa.nwg = (int)nwg; fa.xcd_remap = (nwg % 8 == 0) ? 1 : 0; fa.nwg_seg = (int)nwg;
     fa.seg_len = T > 0 ? T : 1; fa.nseg = 1;
-    fa.ck = w.ck; fa.nsb = (T + kSB - 1) / kSB;
+    fa.ck = (flags & PALIMPSA_CHECKPOINTS_SAVED) ? nullptr : w.ck;
+    fa.nsb = (T + kSB - 1) / kSB;
     fa.vstar = (flags & PALIMPSA_VSTAR) ? 1 : 0;
 
     BwdArgs ba = {};
@@ -2586,7 +2620,7 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
                                      int B, int T, int H, int dk, int dv, int chunk, int segments,
                                      palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
                                      void *workspace, size_t workspace_bytes, void *stream) {
-    if (!A || !I_prior || (T > 0 && (!q || !k || !v || !beta || !dt || !y)) || (flags & ~kFlagsKnown))
+    if (!A || !I_prior || (T > 0 && (!q || !k || !v || !beta || !dt || !y)) || (flags & ~kFlagsFwd))
         return PALIMPSA_ERR_INVALID_ARG;
     if ((mu0 == nullptr) != (I0 == nullptr) || (muT == nullptr) != (IT == nullptr))
         return PALIMPSA_ERR_INVALID_ARG;
@@ -2603,6 +2637,13 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
     // heads wider than 128 keys: per-head prior, v as given, one pass (no time split)
     if (dk > 128 && (flags != 0 || (dv % 16) != 0 || (dk == 256 && dv > 1024)))
         return PALIMPSA_ERR_UNSUPPORTED;
+    // training forward: one pass at chunk 16 within the backward's sizes
+    const bool save_ck = (flags & PALIMPSA_SAVE_CHECKPOINTS) != 0;
+    if (save_ck) {
+        if (!head_ok(dk) || !dv_ok(dv) || segments > 1 || (chunk != 0 && chunk != 16))
+            return PALIMPSA_ERR_UNSUPPORTED;
+        if (!workspace) return PALIMPSA_ERR_INVALID_ARG;
+    }
     if (dk > 256) segments = segments >= 2 ? -1 : 1;
     if (segments < 0) return PALIMPSA_ERR_UNSUPPORTED;
     const bool ipe = (flags & PALIMPSA_PRIOR_PER_ENTRY) != 0;
@@ -2629,7 +2670,21 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
     a.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
     a.nwg_seg = (int)nwg;
     a.vstar = (flags & PALIMPSA_VSTAR) ? 1 : 0;
-    a.ck = nullptr; a.nsb = 0;
+    a.ck = nullptr; a.ck_sink = nullptr; a.nsb = 0;
+    if (save_ck) {
+        if ((long long)B * H * 2 > 0x7fffffffLL) return PALIMPSA_ERR_UNSUPPORTED;
+        const BwdWs w = plan_bwd_ws(workspace, B, T, H, dk, dv, ipe);
+        if (workspace_bytes < w.bytes) return PALIMPSA_ERR_INVALID_ARG;
+        if (T == 0 && !muT) return PALIMPSA_OK;
+        a.ck = w.ck; a.ck_sink = w.sink; a.nsb = (T + kSB - 1) / kSB;
+        a.nseg = 1; a.seg_len = T > 0 ? T : 1; a.ws = nullptr;
+        hipStream_t s = (hipStream_t)stream;
+        const bool bf_in = in_dtype == PALIMPSA_BF16, bf_out = out_dtype == PALIMPSA_BF16;
+        if (bf_in && bf_out) return launch_fwd_ckpt<bf16_t, bf16_t>(a, dk, ipe, s);
+        if (bf_in) return launch_fwd_ckpt<bf16_t, float>(a, dk, ipe, s);
+        if (bf_out) return launch_fwd_ckpt<float, bf16_t>(a, dk, ipe, s);
+        return launch_fwd_ckpt<float, float>(a, dk, ipe, s);
+    }
 
     if (T == 0 && !muT) return PALIMPSA_OK;   // nothing to compute or write
     SegPlan plan = plan_segments(B, T, H, dk, dv, segments, device_cus());
@@ -2657,7 +2712,7 @@ palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
                               int B, int H, int dk, int dv,
                               palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
                               void *stream) {
-    if (!q || !k || !v || !beta || !dt || !A || !I_prior || !mu || !I || !y || (flags & ~kFlagsKnown))
+    if (!q || !k || !v || !beta || !dt || !A || !I_prior || !mu || !I || !y || (flags & ~kFlagsOptions))
         return PALIMPSA_ERR_INVALID_ARG;
     if (B <= 0 || H <= 0 || dk <= 0 || dv <= 0)
         return PALIMPSA_ERR_INVALID_ARG;

@@ -174,6 +174,38 @@ def backward_extra(torch, pm, workloads, w, g, steps):
                          "per_update": "replay 4 VALU + reverse 17 VALU + 1 v_rcp_f32 = 23 slots, 29 flops"}}
 
 
+def training_extra(torch, pm, workloads, w, g, steps):
+    """One training step of the layer: the forward that stores the backward's
+    checkpoints, then the backward that reuses them; beside it the same step
+    with the plain forward and a backward that recomputes its checkpoints."""
+    dev = g["q"].device
+    gr = {n: (x.to(dev) if x is not None else None)
+          for n, x in workloads.upstream_grads(w.B, w.T, w.H, w.dv, w.dk, w.dtype, seed=2).items()}
+    ws = torch.empty(pm.bwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device=dev)
+    args = (g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"])
+    y = torch.empty(w.B, w.T, w.H, w.dv, dtype=w.dtype, device=dev)
+    muT = torch.empty(w.B, w.H, w.dv, w.dk, device=dev)
+    IT = torch.empty_like(muT)
+    out = pm.bwd(*args, gr["gy"], gmuT=gr["gmuT"], gIT=gr["gIT"], workspace=ws)
+
+    def fused():
+        pm.fwd_chunked(*args, y=y, muT=muT, IT=IT, workspace=ws, save_checkpoints=True)
+        pm.bwd(*args, gr["gy"], gmuT=gr["gmuT"], gIT=gr["gIT"], workspace=ws, out=out, checkpoints_saved=True)
+
+    def recompute():
+        pm.fwd_chunked(*args, y=y, muT=muT, IT=IT)
+        pm.bwd(*args, gr["gy"], gmuT=gr["gmuT"], gIT=gr["gIT"], workspace=ws, out=out)
+
+    _, per_f = time_launches(fused, steps, 3, torch)
+    _, per_r = time_launches(recompute, steps, 3, torch)
+    f_s, r_s = sum(per_f) / len(per_f) / 1e3, sum(per_r) / len(per_r) / 1e3
+    return {"workload": w.name + ", training step (forward with y and final state, then the full backward)",
+            "tokens_per_s": w.B * w.T / f_s, "ms_per_step": f_s * 1e3,
+            "recompute_ms_per_step": r_s * 1e3,
+            "note": "checkpointing forward + backward reusing its checkpoints; "
+                    "recompute_ms_per_step is plain forward + backward with its own checkpoint pass"}
+
+
 def frozen_extra(torch, pm, w, g, steps):
     """palimpsa_fwd_frozen (importance held at I_prior) on the same workload."""
     y = torch.empty(w.B, w.T, w.H, w.dv, dtype=w.dtype, device=g["q"].device)
@@ -314,6 +346,7 @@ def main():
         out["decode"] = decode_extra(torch, pm, workloads, max(64, args.steps))
     if not args.no_extras and w.dtype == torch.bfloat16:
         out["backward"] = backward_extra(torch, pm, workloads, w, g, max(5, args.steps // 5))
+        out["training_step"] = training_extra(torch, pm, workloads, w, g, max(5, args.steps // 5))
         out["frozen"] = frozen_extra(torch, pm, w, g, max(20, args.steps))
         out["blockdiag"] = blockdiag_extra(torch, pm, w, g, max(20, args.steps // 2))
         out["recurrent_shape"] = [fig7_extra(torch, pm, workloads, dev, D, 5) for D in (512, 2048)]

@@ -61,7 +61,15 @@
  *                                (1 - alpha_t) I_prior[h, i, j]; the default
  *                                start state is I0 = I_prior entry by entry;
  *                                the backward's gIp is [H, dv, dk].
- *    Unknown bits are PALIMPSA_ERR_INVALID_ARG.
+ *    Two more bits pair one training forward with its backward, so that the
+ *    backward need not recompute the states (see palimpsa_bwd):
+ *      PALIMPSA_SAVE_CHECKPOINTS  (forward only) also store the backward's
+ *                                state checkpoints into `workspace`, which is
+ *                                then a backward workspace.
+ *      PALIMPSA_CHECKPOINTS_SAVED (backward only) the workspace already holds
+ *                                them; the backward skips its first pass.
+ *    Unknown bits, and a bit on an entry point it does not apply to, are
+ *    PALIMPSA_ERR_INVALID_ARG.
  */
 #ifndef PALIMPSA_H
 #define PALIMPSA_H
@@ -87,7 +95,9 @@ typedef enum {
 
 typedef enum {
     PALIMPSA_VSTAR = 1,
-    PALIMPSA_PRIOR_PER_ENTRY = 2
+    PALIMPSA_PRIOR_PER_ENTRY = 2,
+    PALIMPSA_SAVE_CHECKPOINTS = 4,
+    PALIMPSA_CHECKPOINTS_SAVED = 8
 } palimpsa_flags;
 
 /*
@@ -129,6 +139,15 @@ typedef enum {
  *             PALIMPSA_ERR_INVALID_ARG.  Contents are overwritten; calls that
  *             share a workspace must not overlap.
  *   flags     palimpsa_flags bits (see above), or 0.
+ *
+ * With PALIMPSA_SAVE_CHECKPOINTS (the training forward) the workspace is a
+ * backward workspace of at least palimpsa_bwd_workspace_size(B, T, H, dk, dv,
+ * flags) bytes (else PALIMPSA_ERR_INVALID_ARG); the forward runs in one pass
+ * (segments must be 0 or 1, chunk 0 or 16, dk <= 128, dv <= 1024, else
+ * PALIMPSA_ERR_UNSUPPORTED) and also stores the state before every 8th token
+ * there, bit-identical to what palimpsa_bwd would recompute.  A backward called
+ * on the same inputs, flags (PALIMPSA_CHECKPOINTS_SAVED in place of
+ * PALIMPSA_SAVE_CHECKPOINTS) and workspace then reuses them.
  *
  * T == 0 is valid: y is empty and the state is copied through (or, with both
  * mu0 and I0 NULL, set to mu = 0, I = I_prior); the per-token pointers q, k,
@@ -235,7 +254,14 @@ palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
  *             16-byte aligned, caller-owned; contents on entry are ignored
  *
  * flags: palimpsa_flags bits (the options change gv, gbeta and the shape of
- * gIp as stated above); the workspace size depends on them.
+ * gIp as stated above); the workspace size depends on them.  With
+ * PALIMPSA_CHECKPOINTS_SAVED the workspace must hold the checkpoints that a
+ * palimpsa_fwd_chunked call with PALIMPSA_SAVE_CHECKPOINTS stored for the same
+ * q, k, v, beta, dt, A, I_prior, mu0, I0, sizes and option bits, and nothing
+ * may have written to it since; the backward then skips recomputing them
+ * (results are bit-identical to the backward without the bit).  The library
+ * cannot check this pairing: a workspace that does not hold them gives wrong
+ * gradients, not an error.  The backward leaves the checkpoints in place.
  *
  * dk in {32, 64, 128}, dv a multiple of 16 up to 1024 (else
  * PALIMPSA_ERR_UNSUPPORTED).  q, k, v, beta,
@@ -260,7 +286,8 @@ palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const 
  * entry every 8 tokens: B H ceil(T/8) dv dk 8 bytes) plus the per-row-block
  * partials of gq, gk (dv/16 x B T H x 2 dk x 4 bytes) and small sums; with
  * PALIMPSA_PRIOR_PER_ENTRY also each sequence's gIp (B H dv dk x 4 bytes).
- * Returns 0 for sizes or flags palimpsa_bwd would reject.
+ * Returns 0 for sizes or flags palimpsa_bwd would reject.  flags may carry
+ * either checkpoint bit; only PALIMPSA_PRIOR_PER_ENTRY changes the size.
  */
 size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv, int flags);
 

@@ -84,7 +84,12 @@ FWD_CASES = [
     (dict(muT=None), 1), (dict(IT=None), 1), (dict(B=0), 1), (dict(H=0), 1), (dict(T=-1), 1),
     (dict(dk=0), 1), (dict(ind=2), 1), (dict(outd=-1), 1), (dict(chunk=12), 1),
     (dict(chunk=128), 1), (dict(dk=48), 2), (dict(dv=4104), 2), (dict(dv=24), 2), (dict(dk=16), 2),
-    (dict(flags=4), 1), (dict(flags=-1), 1), (dict(flags=2, Ip=FAKE + 4), 3),
+    (dict(flags=16), 1), (dict(flags=-1), 1), (dict(flags=2, Ip=FAKE + 4), 3),
+    # the training forward: a backward workspace, one pass at chunk 16, dk <= 128
+    (dict(flags=8), 1), (dict(flags=4), 1), (dict(flags=4, ws=FAKE, wsb=64), 1),
+    (dict(flags=4, ws=FAKE, wsb=1 << 40, segments=2), 2), (dict(flags=4, ws=FAKE, wsb=1 << 40, chunk=32), 2),
+    (dict(flags=4, ws=FAKE, wsb=1 << 40, dv=2048), 2), (dict(flags=4, ws=FAKE, wsb=1 << 40, dk=256), 2),
+    (dict(flags=4, ws=FAKE + 8, wsb=1 << 40), 3), (dict(flags=6, ws=FAKE, wsb=1 << 40, Ip=FAKE + 4), 3),
     (dict(dk=4096), 2), (dict(dk=384), 2), (dict(dk=512, flags=1), 2), (dict(dk=2048, flags=2), 2),
     (dict(dk=512, segments=2), 2), (dict(dv=4112), 2), (dict(dk=256, dv=2048), 2), (dict(dk=1024, dv=24), 2),
     (dict(q=FAKE + 4), 3), (dict(v=FAKE + 8), 3),
@@ -129,7 +134,7 @@ STEP_CASES = [
     (dict(q=None), 1), (dict(mu=None), 1), (dict(I=None), 1), (dict(y=None), 1),
     (dict(B=0), 1), (dict(H=-2), 1), (dict(ind=5), 1), (dict(dk=100), 2), (dict(dv=8), 2),
     (dict(mu=FAKE + 4), 3), (dict(I=FAKE + 8), 3), (dict(k=FAKE + 1), 3), (dict(dt=FAKE + 1), 3),
-    (dict(y=FAKE + 3), 3), (dict(Ip=FAKE + 2), 3), (dict(flags=4), 1), (dict(dv=40), 2),
+    (dict(y=FAKE + 3), 3), (dict(Ip=FAKE + 2), 3), (dict(flags=4), 1), (dict(flags=8), 1), (dict(dv=40), 2),
     (dict(flags=2, Ip=FAKE + 8), 3), (dict(dk=4096), 2), (dict(dk=768), 2),
 ]
 
@@ -203,7 +208,9 @@ BWD_CASES = [
     (dict(mu0=FAKE), 1), (dict(I0=FAKE), 1), (dict(B=0), 1), (dict(T=-1), 1), (dict(H=0), 1),
     (dict(ind=2), 1), (dict(gyd=5), 1), (dict(wsb=64), 1), (dict(q=None, T=0, A=None), 1),
     (dict(dk=48), 2), (dict(dv=1040), 2), (dict(dv=8), 2), (dict(dk=16), 2),
-    (dict(flags=8), 1), (dict(flags=2, Ip=FAKE + 4), 3), (dict(flags=2, gIp=FAKE + 4), 3),
+    (dict(flags=4), 1), (dict(flags=16), 1), (dict(flags=12), 1),
+    (dict(flags=8, ws=None), 1), (dict(flags=8, wsb=64), 1),
+    (dict(flags=2, Ip=FAKE + 4), 3), (dict(flags=2, gIp=FAKE + 4), 3),
     (dict(q=FAKE + 4), 3), (dict(gy=FAKE + 8), 3), (dict(gq=FAKE + 4), 3), (dict(gk=FAKE + 8), 3),
     (dict(gdt=FAKE + 2), 3), (dict(dt=FAKE + 1), 3), (dict(ws=FAKE + 8), 3),
     (dict(gmuT=FAKE + 4), 3), (dict(gmu0=FAKE + 12), 3), (dict(gA=FAKE + 1), 3),
@@ -226,16 +233,20 @@ def test_bwd_workspace_size_host_logic(lib):
     def expect(B, T, H, dk, dv, per_entry=False):
         nsb, nrb, bh = (T + 7) // 8, dv // 16, B * H
         return (pad(bh * nsb * 2 * dv * dk) + pad(nrb * bh * T * 2 * dk) + pad(nrb * bh * T * 2)
-                + 2 * pad(bh) + pad(bh * nrb) + (pad(bh * dv * dk) if per_entry else 0))
+                + 2 * pad(bh) + pad(bh * nrb) + (pad(bh * dv * dk) if per_entry else 0)
+                + pad(256 * 2 * dk // 16))    # the training forward's sink block
     for shape in [(1, 10, 2, 32, 32), (8, 4096, 12, 128, 128), (1, 0, 3, 64, 128), (2, 9, 1, 128, 64),
                   (1, 33, 2, 128, 256), (2, 5, 3, 64, 48)]:
         assert pm.bwd_workspace_size(*shape) == expect(*shape), shape
         assert pm.bwd_workspace_size(*shape, flags=2) == expect(*shape, per_entry=True), shape
         assert pm.bwd_workspace_size(*shape, flags=1) == expect(*shape), shape
+        # either checkpoint bit leaves the size as it is
+        assert pm.bwd_workspace_size(*shape, flags=4) == expect(*shape), shape
+        assert pm.bwd_workspace_size(*shape, flags=10) == expect(*shape, per_entry=True), shape
     assert pm.bwd_workspace_size(1, 8, 2, 48, 64) == 0
     assert pm.bwd_workspace_size(0, 8, 2, 64, 64) == 0
     assert pm.bwd_workspace_size(1, 8, 2, 64, 24) == 0
-    assert pm.bwd_workspace_size(1, 8, 2, 64, 64, flags=4) == 0
+    assert pm.bwd_workspace_size(1, 8, 2, 64, 64, flags=16) == 0
 
 
 def _bd_args(**over):

@@ -620,6 +620,87 @@ def test_bwd_is_deterministic_and_ignores_stale_workspace():
 
 
 # ---------------------------------------------------------------------------
+# training forward: the forward also stores the backward's checkpoints
+# ---------------------------------------------------------------------------
+
+TRAIN_CASES = [
+    # B, T, H, dk, dv, dtype, start state given, prior per entry, v*
+    (1, 37, 2, 32, 32, torch.float32, True, False, False),
+    (2, 64, 3, 64, 64, torch.float32, False, False, False),
+    (1, 100, 2, 128, 128, torch.bfloat16, True, False, False),
+    (2, 8, 1, 128, 32, torch.float32, False, False, False),
+    (1, 9, 2, 64, 48, torch.bfloat16, False, True, False),
+    (1, 1, 2, 32, 64, torch.float32, True, False, True),
+    (1, 24, 2, 128, 256, torch.bfloat16, True, True, True),
+    (2, 17, 2, 128, 128, torch.float32, False, True, False),
+    (2, 0, 2, 64, 64, torch.float32, True, False, False),
+]
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,dtype,state,per_entry,vstar", TRAIN_CASES)
+def test_training_forward_checkpoints_feed_the_backward(B, T, H, dk, dv, dtype, state, per_entry, vstar):
+    """The checkpointing forward gives the plain forward's outputs bit for bit,
+    stores the same checkpoint bytes the backward's own first pass would, and
+    a backward that reuses them gives the plain backward's gradients bit for
+    bit (and the oracle's within the backward tolerance)."""
+    w = workloads.WORKLOADS[0].with_(B=B, H=H, dk=dk, dv=dv, dtype=dtype, A_mode="logspace16")
+    _announce("training fwd + bwd(saved)", B=B, T=T, H=H, dk=dk, dv=dv, dtype=dtype, state=state,
+              per_entry=per_entry, vstar=vstar)
+    inp = workloads.make_inputs(w, T=T, seed=11 * T + dk + dv)
+    if per_entry:
+        inp["I_prior"] = workloads.per_entry_prior(H, dv, dk, seed=dk + 2 * dv)
+    if state:
+        ip = torch.ones(H) if per_entry else inp["I_prior"]
+        inp["mu0"], inp["I0"] = workloads.random_state(B, H, dv, dk, ip, seed=T + 3)
+    gr = workloads.upstream_grads(B, T, H, dv, dk, dtype, seed=T + 5)
+    g = to_device(inp, DEV)
+    gg = to_device(gr, DEV)
+    flags = (2 if per_entry else 0) | (1 if vstar else 0)
+    nbytes = _pm().bwd_workspace_size(B, T, H, dk, dv, flags)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=DEV)      # stale contents
+    kw = dict(mu0=g.get("mu0"), I0=g.get("I0"), vstar=vstar)
+    y0, mu0T, I0T = _pm().fwd_chunked(*gpu_args(g), **kw)
+    y1, mu1T, I1T = _pm().fwd_chunked(*gpu_args(g), **kw, workspace=ws, save_checkpoints=True)
+    bk = dict(mu0=g.get("mu0"), I0=g.get("I0"), gmuT=gg["gmuT"], gIT=gg["gIT"], vstar=vstar)
+    ws_own = torch.empty_like(ws)
+    a = _pm().bwd(*gpu_args(g), gg["gy"], **bk, workspace=ws_own)
+    b = _pm().bwd(*gpu_args(g), gg["gy"], **bk, workspace=ws, checkpoints_saved=True)
+    c = _pm().bwd(*gpu_args(g), gg["gy"], **bk, workspace=ws, checkpoints_saved=True)   # left in place
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y0) and torch.equal(mu1T, mu0T) and torch.equal(I1T, I0T)
+    ck_bytes = B * H * ((T + 7) // 8) * 2 * dv * dk * 4
+    assert torch.equal(ws[:ck_bytes], ws_own[:ck_bytes]), "checkpoint bytes differ"
+    for n in BWD_NAMES:
+        assert torch.equal(b[n], a[n]), n
+        assert torch.equal(c[n], a[n]), n
+    ref = oracle.bwd(**inp, gy=gr["gy"], gmuT=gr["gmuT"], gIT=gr["gIT"], vstar=vstar)
+    _compare_bwd(b, ref, TOL_BWD)
+
+
+def test_training_forward_layer760m_matches_plain_forward_and_backward():
+    """At the 760M layer's full size: the checkpointing forward and the backward
+    that reuses its checkpoints equal the plain forward and backward bit for bit."""
+    w = workloads.WORKLOADS[2]
+    _announce("training fwd 760M layer bf16", B=w.B, H=w.H, T=w.T, d=w.dk)
+    inp = workloads.make_inputs(w)
+    gr = workloads.upstream_grads(w.B, w.T, w.H, w.dv, w.dk, w.dtype, seed=2)
+    g = to_device(inp, DEV)
+    gg = to_device(gr, DEV)
+    ws = torch.empty(_pm().bwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device=DEV)
+    y0, mu0T, I0T = _pm().fwd_chunked(*gpu_args(g))
+    y1, mu1T, I1T = _pm().fwd_chunked(*gpu_args(g), workspace=ws, save_checkpoints=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y0) and torch.equal(mu1T, mu0T) and torch.equal(I1T, I0T)
+    del y0, mu0T, I0T
+    b = _pm().bwd(*gpu_args(g), gg["gy"], gmuT=gg["gmuT"], gIT=gg["gIT"], workspace=ws, checkpoints_saved=True)
+    b = {n: b[n].clone() for n in ("gq", "gk", "gv", "gdt", "gA", "gIp")}
+    a = _pm().bwd(*gpu_args(g), gg["gy"], gmuT=gg["gmuT"], gIT=gg["gIT"], workspace=ws)
+    torch.cuda.synchronize()
+    for n in b:
+        assert torch.equal(b[n], a[n]), n
+
+
+# ---------------------------------------------------------------------------
 # generalised boundary: value expansion / any dv multiple of 16, v* input,
 # a prior per state entry
 # ---------------------------------------------------------------------------
