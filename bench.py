@@ -188,20 +188,30 @@ def training_extra(torch, pm, workloads, w, g, steps):
     IT = torch.empty_like(muT)
     out = pm.bwd(*args, gr["gy"], gmuT=gr["gmuT"], gIT=gr["gIT"], workspace=ws)
 
+    fwd_save = lambda: pm.fwd_chunked(*args, y=y, muT=muT, IT=IT, workspace=ws, save_checkpoints=True)
+
     def fused():
-        pm.fwd_chunked(*args, y=y, muT=muT, IT=IT, workspace=ws, save_checkpoints=True)
+        fwd_save()
         pm.bwd(*args, gr["gy"], gmuT=gr["gmuT"], gIT=gr["gIT"], workspace=ws, out=out, checkpoints_saved=True)
 
     def recompute():
         pm.fwd_chunked(*args, y=y, muT=muT, IT=IT)
         pm.bwd(*args, gr["gy"], gmuT=gr["gmuT"], gIT=gr["gIT"], workspace=ws, out=out)
 
+    _, per_s = time_launches(fwd_save, steps, 3, torch)
     _, per_f = time_launches(fused, steps, 3, torch)
     _, per_r = time_launches(recompute, steps, 3, torch)
-    f_s, r_s = sum(per_f) / len(per_f) / 1e3, sum(per_r) / len(per_r) / 1e3
+    mean_s = lambda per: sum(per) / len(per) / 1e3
+    s_s, f_s, r_s = mean_s(per_s), mean_s(per_f), mean_s(per_r)
+    ck_bytes = w.B * w.H * ((w.T + 7) // 8) * 2 * w.dv * w.dk * 4
     return {"workload": w.name + ", training step (forward with y and final state, then the full backward)",
             "tokens_per_s": w.B * w.T / f_s, "ms_per_step": f_s * 1e3,
             "recompute_ms_per_step": r_s * 1e3,
+            "checkpointing_forward": {
+                "ms_per_launch": s_s * 1e3, "checkpoint_GB": ck_bytes / 1e9,
+                "checkpoint_write_GBs": ck_bytes / s_s / 1e9,
+                "traffic": load_traffic("fwd_ckpt_layer760m_bf16_traffic.json")
+                if w.name.startswith("layer760m") else None},
             "note": "checkpointing forward + backward reusing its checkpoints; "
                     "recompute_ms_per_step is plain forward + backward with its own checkpoint pass"}
 
@@ -235,7 +245,9 @@ def blockdiag_extra(torch, pm, w, g, steps):
     return {"workload": w.name + ", 2x2 block-diagonal precision",
             "tokens_per_s": w.B * w.T / avg_s, "ms_per_launch": avg_s * 1e3,
             "roofline": {"bound": "alu", "achieved": achieved, "peak": bd2_peak_tflops(), "unit": "TFLOP/s",
-                         "frac": achieved / bd2_peak_tflops(), "traffic": None,
+                         "frac": achieved / bd2_peak_tflops(),
+                         "traffic": load_traffic("bd2_fwd_layer760m_bf16_traffic.json")
+                         if w.name.startswith("layer760m") else None,
                          "per_entry": "10.5 VALU + 0.5 v_rcp_f32 = 11.5 slots, 16.5 flops"}}
 
 
