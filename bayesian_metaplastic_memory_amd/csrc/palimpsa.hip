@@ -1751,7 +1751,9 @@ template <int DK>
 struct FzLds {
     // One staging buffer (bf16 unless noted); two are used alternately.  Rows
     // are padded by 8 elements (16 bytes) so that the 16 rows a fragment read
-    // touches fall in distinct LDS banks.
+    // touches fall in distinct LDS banks.  K is also swizzled: the 16-byte
+    // column block cb of row r sits at block cb ^ ((r / 8) % 8), which keeps
+    // the stagers' row writes (8 tokens apart) in distinct banks too.
     static constexpr int kQS = DK + 8;                   // row stride of Q and K
     static constexpr int kTS = kFzC + 8;                 // row stride of the token-minor arrays
     static constexpr int kQ = 0;                         // Q  [C][DK]
@@ -1759,7 +1761,8 @@ struct FzLds {
     static constexpr int kKt = kK + kFzC * kQS;          // K^T [DK][C]
     static constexpr int kWt = kKt + DK * kTS;           // W^T [64][C]
     static constexpr int kWdt = kWt + kFzRows * kTS;     // (diag(d) W)^T [64][C]
-    static constexpr int kBufHalves = kWdt + kFzRows * kTS;
+    static constexpr int kP = kWdt + kFzRows * kTS;      // P^T tiles [10][64 lanes][4], D-fragment order
+    static constexpr int kBufHalves = kP + 10 * 256;
     static constexpr int kLamBytes = kFzC * 4;           // Lam [C] float, after the halves
     static constexpr int kBufBytes = kBufHalves * 2 + kLamBytes;
     static constexpr int kTotal = 2 * kBufBytes;
@@ -1809,19 +1812,23 @@ __device__ inline bf16x8_t cat8(bf16x4_t x, bf16x4_t y) {
 __device__ constexpr int tri(int sb, int tb) { return tb * (tb + 1) / 2 + sb; }
 
 // Warp-specialised: waves 0-3 compute chunk c while waves 4-7 widen and
-// stage chunk c+1 into the other LDS buffer and load chunk c+2 from HBM; one
-// barrier per chunk.  Compute wave w owns value rows [16w, 16w+16) of the
-// workgroup: it forms all 10 lower-triangle score tiles of the chunk (so the
-// decay-masked scores never leave its registers), then Y for its rows and
-// its part of the state.
+// stage chunk c+1 into the other LDS buffer and load chunk c+2 from HBM; two
+// barriers per chunk.  The compute waves first form the 10 lower-triangle
+// score tiles of the chunk between them and share them through LDS; then
+// compute wave w, which owns value rows [16w, 16w+16) of the workgroup, forms
+// Y for its rows and its part of the state.
 template <int DK>
 __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
     using L = FzLds<DK>;
     extern __shared__ float lds_f[];
     char *lds = (char *)lds_f;
     const int rb_per_head = a.dv / kFzRows;
-    const int bh = blockIdx.x / rb_per_head;
-    const int ib0 = (blockIdx.x % rb_per_head) * kFzRows;      // first value row of the workgroup
+    // consecutive workgroup ids go round-robin over the 8 XCDs; remap so that
+    // the row blocks of one head, which read the same q and k, share an XCD's L2
+    int wg = blockIdx.x;
+    if (gridDim.x % 8 == 0) wg = (wg % 8) * (gridDim.x / 8) + wg / 8;
+    const int bh = wg / rb_per_head;
+    const int ib0 = (wg % rb_per_head) * kFzRows;      // first value row of the workgroup
     const int b = bh / a.H, h = bh % a.H;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const bool stager = wv >= 4;
@@ -1832,54 +1839,55 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
     const int nchunks = (a.T + kFzC - 1) / kFzC;
 
     // ---- staging waves (threads 256..511, index u = tid - 256).  Roles:
-    //   u in [0, DK):        one 8x8 block of K (tokens 8 (u / (DK/8)).., columns
-    //                        8 (u % (DK/8))..), written as K rows and, transposed in
-    //                        registers, as K^T rows
-    //   u in [DK, DK+128):   x = u - DK; two whole waves.  Each thread stages
-    //                        DK/16 packets of Q (consecutive threads cover a token
-    //                        row) and one 4-token x 8-row block of
-    //                        W = beta . v / I_prior (tokens 4 (x/8).., rows 8 (x%8)..),
-    //                        written transposed as W^T and (diag(d) W)^T; both waves
+    //   u in [0, DK):        one 8x8 block of K (tokens 8 (u % 8).., columns
+    //                        8 (u / 8)..), written as K rows and, transposed in
+    //                        registers, as K^T rows; and 8 packets of Q (packet
+    //                        e DK + u in row-major order: consecutive threads
+    //                        cover a token row)
+    //   u in [DK, DK+128):   x = u - DK; two whole waves.  Each thread stages one
+    //                        4-token x 8-row block of W = beta . v / I_prior
+    //                        (tokens 4 (x%16).., rows 8 (x/16)..), written
+    //                        transposed as W^T and (diag(d) W)^T; both waves
     //                        scan the gate (one token per lane) and the first
     //                        writes Lam
+    // The block assignments put the 16 lanes of one LDS write pass on rows or
+    // tokens that fall in distinct banks.
     //   u >= DK+128:         idle (d_k = 64)
     // Loads read a valid row (clamped to T-1); tokens past the end are zeroed
     // when written (q = k = w = 0, dt = 0: no effect on y or the state).
     const int u = tid - 256;
     constexpr int kQPk = DK / 8;            // 16-byte packets per Q row
-    constexpr int kQTok = 128 / kQPk;       // Q rows covered by one packet index
-    u32x4 pr[16];                 // 16-byte packets of this thread's role
-    float pdt = 0.f;
-    // Token t of a [B, T, H, n] tensor starts at element (seq + t H) n.  Full
-    // chunks step a per-thread pointer by a uniform token stride; the last,
-    // partial chunk clamps each token to T-1 instead.
-    auto load = [&](int t0) __attribute__((always_inline)) {
-        const bool full = t0 + kFzC <= a.T;
-        auto tok = [&](int t) { return seq + (size_t)(full ? t : min(t, a.T - 1)) * a.H; };
+    // 16-byte packets of this thread's role: the K role stages one chunk
+    // from pr; the W role alternates between pr and pr2, two chunks ahead
+    // dt stays in its bf16 bits until the commit: widening it at the load
+    // would make the wave wait for the load there
+    u32x4 pr[16], pr2[16];
+    uint32_t pdt = 0, pdt2 = 0;
+    // Token t of a [B, T, H, n] tensor starts at element (seq + t H) n; tokens
+    // past the end are clamped to T-1.  Every load takes the same branch-free
+    // address form: per-load branches would split the loads into blocks whose
+    // register reuse makes the wave wait for earlier loads.
+    auto load = [&](int t0, u32x4 *pr, uint32_t &pdt) __attribute__((always_inline)) {
+        const int tl = a.T - 1;
+        auto row = [&](int t) { return seq + (size_t)min(t, tl) * a.H; };
         if (u < DK) {
-            const int tok0 = 8 * (u / (DK / 8)), col = 8 * (u % (DK / 8));
-            const bf16_t *p = a.k + tok(t0 + tok0) * DK + col;
-            const size_t st = (size_t)a.H * DK;
+            const int tok0 = 8 * (u % 8), col = 8 * (u / 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pr[e] = *(const u32x4 *)(a.k + row(t0 + tok0 + e) * DK + col);
+            const int tq0 = u / kQPk, qcol = 8 * (u % kQPk);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                pr[e] = *(const u32x4 *)(full ? p + e * st : a.k + tok(t0 + tok0 + e) * DK + col);
+                pr[8 + e] = *(const u32x4 *)(a.q + row(t0 + e * (DK / kQPk) + tq0) * DK + qcol);
         } else if (u < DK + 128) {
-            const int x = u - DK, tok0 = 4 * (x / 8), i0 = ib0 + 8 * (x % 8);
-            const size_t vo = tok(t0 + tok0) * a.dv + i0, vst = (size_t)a.H * a.dv;
+            const int x = u - DK, tok0 = 4 * (x % 16), i0 = ib0 + 8 * (x / 16);
+            const bf16_t *bsrc = a.beta ? a.beta : a.v;    // no beta: replaced by 1.0 at the commit
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const size_t o = full ? vo + e * vst : tok(t0 + tok0 + e) * a.dv + i0;
+                const size_t o = row(t0 + tok0 + e) * a.dv + i0;
                 pr[e] = *(const u32x4 *)(a.v + o);
-                pr[4 + e] = a.beta ? *(const u32x4 *)(a.beta + o)
-                                   : u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0
+                pr[4 + e] = *(const u32x4 *)(bsrc + o);
             }
-            const int tq0 = x / kQPk, col = 8 * (x % kQPk);
-            const bf16_t *pq = a.q + tok(t0 + tq0) * DK + col;
-            const size_t qst = (size_t)kQTok * a.H * DK;
-#pragma unroll
-            for (int e = 0; e < DK / 16; ++e)
-                pr[8 + e] = *(const u32x4 *)(full ? pq + e * qst : a.q + tok(t0 + e * kQTok + tq0) * DK + col);
-            pdt = (float)a.dt[tok(t0 + lane)];
+            pdt = __builtin_bit_cast(uint16_t, a.dt[row(t0 + lane)]);
         }
     };
     // 8x8 transpose of bf16: out[c] holds element c of in[0..7]
@@ -1904,33 +1912,35 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
                            __builtin_amdgcn_perm(u4get(in[3], wd), u4get(in[2], wd), sel)};
         }
     };
-    auto commit = [&](char *buf, int t0) __attribute__((always_inline)) {
+    auto commit = [&](char *buf, int t0, const u32x4 *pr, uint32_t pdt) __attribute__((always_inline)) {
         bf16_t *hb = (bf16_t *)buf;
         float *lam = (float *)(buf + L::kBufHalves * 2);
         const u32x4 z = u32x4{0u, 0u, 0u, 0u};
         if (u < DK) {
-            const int tok0 = 8 * (u / (DK / 8)), col = 8 * (u % (DK / 8));
+            const int tok0 = 8 * (u % 8), col = 8 * (u / 8);
+            const int pcol = 8 * ((u / 8) ^ (u % 8));     // swizzled column block (rows tok0.. share r / 8)
             u32x4 kin[8], kt[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 kin[e] = (t0 + tok0 + e < a.T) ? pr[e] : z;
-                *(u32x4 *)(hb + L::kK + (tok0 + e) * L::kQS + col) = kin[e];
+                *(u32x4 *)(hb + L::kK + (tok0 + e) * L::kQS + pcol) = kin[e];
             }
             transpose8(kin, kt);
 #pragma unroll
             for (int c = 0; c < 8; ++c) *(u32x4 *)(hb + L::kKt + (col + c) * L::kTS + tok0) = kt[c];
+            const int tq0 = u / kQPk, qcol = 8 * (u % kQPk);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int tq = e * (DK / kQPk) + tq0;
+                *(u32x4 *)(hb + L::kQ + tq * L::kQS + qcol) = (t0 + tq < a.T) ? pr[8 + e] : z;
+            }
         } else if (u < DK + 128) {
             const int x = u - DK;
-#pragma unroll
-            for (int e = 0; e < DK / 16; ++e) {
-                const int tq = e * kQTok + x / kQPk, col = 8 * (x % kQPk);
-                *(u32x4 *)(hb + L::kQ + tq * L::kQS + col) = (t0 + tq < a.T) ? pr[8 + e] : z;
-            }
             // gate: Lam = inclusive prefix sum of -A dt over the chunk, lane = token
-            const float lam_l = wave_incl_scan((t0 + lane < a.T) ? -Ah * pdt : 0.f, lane);
+            const float lam_l = wave_incl_scan((t0 + lane < a.T) ? -Ah * __uint_as_float(pdt << 16) : 0.f, lane);
             if (x < 64) lam[lane] = lam_l;
             const float dl = __expf(wave_read(lam_l, 63) - lam_l);   // e^(Lam_end - Lam_s)
-            const int tok0 = 4 * (x / 8), il0 = 8 * (x % 8);
+            const int tok0 = 4 * (x % 16), il0 = 8 * (x / 16);
             u32x4 win[4], wdn[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1939,7 +1949,7 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
                 uint32_t ww[4], wd[4];
 #pragma unroll
                 for (int pp = 0; pp < 4; ++pp) {
-                    const uint32_t vw = u4get(pr[e], pp), bw = u4get(pr[4 + e], pp);
+                    const uint32_t vw = u4get(pr[e], pp), bw = a.beta ? u4get(pr[4 + e], pp) : 0x3f803f80u;
                     const float w0 = ok ? bf_lo(bw) * bf_lo(vw) * inv_ip : 0.f;
                     const float w1 = ok ? bf_hi(bw) * bf_hi(vw) * inv_ip : 0.f;
                     ww[pp] = pack_bf16(w0, w1);
@@ -1958,78 +1968,118 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
         }
     };
 
+    // Two phases per chunk, each closed by a barrier.  Phase A: the compute
+    // waves form the chunk's 10 decay-masked score tiles, 2-3 per wave, and
+    // share them through LDS, while the stagers stage chunk c+1 into buffer
+    // (c+1)&1 (not read during chunk c) and issue the loads of chunk c+2, which
+    // then have a whole chunk to arrive; the compute waves also update the
+    // state, keeping the previous one in bf16 for phase B.  Phase B: the
+    // compute waves form Y.  The two roles run separate loops with the same
+    // barriers, so that neither's registers stay reserved in the other's code.
+    // The K role loads chunk c+2 in phase A, right after staging c+1.  The
+    // W role stages chunk c+1 in phase A and loads chunk c+3 in phase B (its
+    // loads would otherwise queue behind the K role's and hold phase A up),
+    // alternating between two register sets.
+    auto buf_of = [&](int c) { return lds + (c & 1) * L::kBufBytes; };
+    if (stager && u < DK) {
+        if (nchunks > 0) {
+            load(0, pr, pdt);
+            commit(lds, 0, pr, pdt);
+            if (nchunks > 1) load(kFzC, pr, pdt);
+        }
+        __syncthreads();
+        for (int c = 0; c < nchunks; ++c) {
+            if (c + 1 < nchunks) {
+                commit(buf_of(c + 1), (c + 1) * kFzC, pr, pdt);
+                if (c + 2 < nchunks) load((c + 2) * kFzC, pr, pdt);
+            }
+            __syncthreads();
+            __syncthreads();
+        }
+        return;
+    }
+    if (stager) {
+        if (nchunks > 0) {
+            load(0, pr, pdt);
+            commit(lds, 0, pr, pdt);
+            if (nchunks > 1) load(kFzC, pr2, pdt2);
+            if (nchunks > 2) load(2 * kFzC, pr, pdt);
+        }
+        __syncthreads();
+        for (int c = 0; c < nchunks; c += 2) {
+            if (c + 1 < nchunks) commit(buf_of(c + 1), (c + 1) * kFzC, pr2, pdt2);
+            __syncthreads();
+            if (c + 3 < nchunks) load((c + 3) * kFzC, pr2, pdt2);
+            __syncthreads();
+            if (c + 1 >= nchunks) break;
+            if (c + 2 < nchunks) commit(buf_of(c + 2), (c + 2) * kFzC, pr, pdt);
+            __syncthreads();
+            if (c + 4 < nchunks) load((c + 4) * kFzC, pr, pdt);
+            __syncthreads();
+        }
+        return;
+    }
+
     // ---- compute waves: state S^T tiles (jb, rows of wave w); lane holds
     // S^T[16 jb + 4 lg + r][16 w + lr] = S[i][j]
     f32x4 St[DK / 16];
     const int irow = ib0 + 16 * w + lr;
     const size_t srow = ((size_t)bh * a.dv + irow) * DK;
-    if (!stager) {
-        if (a.mu0) {
+    if (a.mu0) {
 #pragma unroll
-            for (int jb = 0; jb < DK / 16; ++jb) St[jb] = *(const f32x4 *)(a.mu0 + srow + 16 * jb + 4 * lg);
-        } else {
+        for (int jb = 0; jb < DK / 16; ++jb) St[jb] = *(const f32x4 *)(a.mu0 + srow + 16 * jb + 4 * lg);
+    } else {
 #pragma unroll
-            for (int jb = 0; jb < DK / 16; ++jb) St[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    } else if (nchunks > 0) {
-        load(0);
-        commit(lds, 0);
-        if (nchunks > 1) load(kFzC);
+        for (int jb = 0; jb < DK / 16; ++jb) St[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     __syncthreads();
-
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * kFzC;
-        if (stager) {
-            if (c + 1 < nchunks) {
-                commit(lds + ((c + 1) & 1) * L::kBufBytes, t0 + kFzC);
-                if (c + 2 < nchunks) load(t0 + 2 * kFzC);
-            }
-        } else {
-            const char *buf = lds + (c & 1) * L::kBufBytes;
-            const bf16_t *hb = (const bf16_t *)buf;
-            const float *lam = (const float *)(buf + L::kBufHalves * 2);
-
-            // (a) scores G^T[s][t] = k_s . q_t for the 10 tiles with s block <= t block
-            f32x4 g[10];
+        bf16x8_t sa[DK / 32];
+        char *bufw = lds + (c & 1) * L::kBufBytes;
+        const char *buf = bufw;
+        const bf16_t *hb = (const bf16_t *)buf;
+        const float *lam = (const float *)(buf + L::kBufHalves * 2);
+        {
+            // (a) scores G^T[s][t] = k_s . q_t of this wave's tiles (tri index
+            // 0-2, 3-5, 6-7, 8-9 for waves 0-3; waves 2 and 3 form their last
+            // tile twice so that all four run the same straight-line code)
+            const int i0 = w < 2 ? 3 * w : 2 * w + 2;
+            int ti[3], tsb[3], ttb[3];
 #pragma unroll
-            for (int i = 0; i < 10; ++i) g[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int n = 0; n < 3; ++n) {
+                ti[n] = i0 + (n < 2 || w < 2 ? n : 1);
+                ttb[n] = ti[n] >= 6 ? 3 : ti[n] >= 3 ? 2 : ti[n] >= 1 ? 1 : 0;
+                tsb[n] = ti[n] - ttb[n] * (ttb[n] + 1) / 2;
+            }
+            f32x4 g3[3];
+#pragma unroll
+            for (int n = 0; n < 3; ++n) g3[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < DK / 32; ++kk) {
-                bf16x8_t qf[4];
 #pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    qf[x] = lds_b128(hb + L::kQ + (16 * x + lr) * L::kQS + 32 * kk + 8 * lg);
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb) {
-                    const bf16x8_t kf = lds_b128(hb + L::kK + (16 * sb + lr) * L::kQS + 32 * kk + 8 * lg);
-#pragma unroll
-                    for (int tb = sb; tb < 4; ++tb)
-                        g[tri(sb, tb)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[tb], g[tri(sb, tb)], 0, 0, 0);
+                for (int n = 0; n < 3; ++n) {
+                    const int kr = 16 * tsb[n] + lr;
+                    const bf16x8_t qf = lds_b128(hb + L::kQ + (16 * ttb[n] + lr) * L::kQS + 32 * kk + 8 * lg);
+                    const bf16x8_t kf = lds_b128(hb + L::kK + kr * L::kQS + 8 * ((4 * kk + lg) ^ ((kr >> 3) & 7)));
+                    g3[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf, g3[n], 0, 0, 0);
                 }
             }
             // decay and causal mask: P^T[s][t] = G^T[s][t] e^(Lam_t - Lam_s) for s <= t, as bf16
-            bf16x4_t pt[10];
-            float lam_t[4];
+            bf16_t *pw = (bf16_t *)bufw + L::kP + 4 * lane;
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) lam_t[tb] = lam[16 * tb + lr];
+            for (int n = 0; n < 3; ++n) {
+                const float lt = lam[16 * ttb[n] + lr];
+                const f32x4 ls = *(const f32x4 *)(lam + 16 * tsb[n] + 4 * lg);
+                bf16x4_t pt;
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                const f32x4 ls = *(const f32x4 *)(lam + 16 * sb + 4 * lg);
-#pragma unroll
-                for (int tb = sb; tb < 4; ++tb) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const bool keep = sb < tb || 4 * lg + r <= lr;
-                        pt[tri(sb, tb)][r] = (bf16_t)(keep ? g[tri(sb, tb)][r] * __expf(lam_t[tb] - ls[r]) : 0.f);
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    const bool keep = tsb[n] < ttb[n] || 4 * lg + r <= lr;
+                    pt[r] = (bf16_t)(keep ? g3[n][r] * __expf(lt - ls[r]) : 0.f);
                 }
+                *(bf16x4_t *)(pw + 256 * ti[n]) = pt;
             }
-
-            // (c) Y^T for value rows of wave w: intra-chunk W^T P^T + inter-chunk S Q^T e^Lam_t.
-            // The k index (token s) of the intra product follows the P^T
-            // fragments: slots 0-3 = s 4lg..4lg+3 of s block 2ks, slots 4-7 of block 2ks+1.
-            bf16x8_t sa[DK / 32];
+            // the state before this chunk, as the bf16 A operand of S Q^T in phase B
 #pragma unroll
             for (int kk = 0; kk < DK / 32; ++kk) {
 #pragma unroll
@@ -2038,6 +2088,32 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
                     sa[kk][4 + r] = (bf16_t)St[2 * kk + 1][r];
                 }
             }
+            // (e) state: S^T = e^Lam_end S^T + K^T diag(d) W
+            const float e_end = __expf(lam[kFzC - 1]);
+            bf16x8_t wd[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) wd[ks] = lds_b128(hb + L::kWdt + (16 * w + lr) * L::kTS + 32 * ks + 8 * lg);
+#pragma unroll
+            for (int jb = 0; jb < DK / 16; ++jb) {
+                f32x4 acc = St[jb] * e_end;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        lds_b128(hb + L::kKt + (16 * jb + lr) * L::kTS + 32 * ks + 8 * lg), wd[ks], acc, 0, 0, 0);
+                St[jb] = acc;
+            }
+        }
+        __syncthreads();
+        {
+            float lam_t[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) lam_t[tb] = lam[16 * tb + lr];
+            const bf16_t *pr_t = hb + L::kP + 4 * lane;   // this lane's fragment of each P^T tile
+            auto ptile = [&](int i) __attribute__((always_inline)) { return lds_b64(pr_t + 256 * i); };
+
+            // (c) Y^T for value rows of wave w: intra-chunk W^T P^T + inter-chunk S Q^T e^Lam_t.
+            // The k index (token s) of the intra product follows the P^T
+            // fragments: slots 0-3 = s 4lg..4lg+3 of s block 2ks, slots 4-7 of block 2ks+1.
             const bf16_t *wrow = hb + L::kWt + (16 * w + lr) * L::kTS + 4 * lg;
             const bf16x4_t zero4 = {(bf16_t)0.f, (bf16_t)0.f, (bf16_t)0.f, (bf16_t)0.f};
 #pragma unroll
@@ -2046,7 +2122,7 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
 #pragma unroll
                 for (int ks = 0; ks <= tb / 2; ++ks) {
                     const bf16x8_t av = cat8(lds_b64(wrow + 32 * ks), lds_b64(wrow + 32 * ks + 16));
-                    const bf16x8_t bv = cat8(pt[tri(2 * ks, tb)], 2 * ks + 1 <= tb ? pt[tri(2 * ks + 1 <= tb ? 2 * ks + 1 : 0, tb)] : zero4);
+                    const bf16x8_t bv = cat8(ptile(tri(2 * ks, tb)), 2 * ks + 1 <= tb ? ptile(tri(2 * ks + 1 <= tb ? 2 * ks + 1 : 0, tb)) : zero4);
                     yi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, yi, 0, 0, 0);
                 }
 #pragma unroll
@@ -2069,25 +2145,10 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
                     }
                 }
             }
-
-            // (e) state: S^T = e^Lam_end S^T + K^T diag(d) W
-            const float e_end = __expf(lam[kFzC - 1]);
-            bf16x8_t wd[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) wd[ks] = lds_b128(hb + L::kWdt + (16 * w + lr) * L::kTS + 32 * ks + 8 * lg);
-#pragma unroll
-            for (int jb = 0; jb < DK / 16; ++jb) {
-                f32x4 acc = St[jb] * e_end;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        lds_b128(hb + L::kKt + (16 * jb + lr) * L::kTS + 32 * ks + 8 * lg), wd[ks], acc, 0, 0, 0);
-                St[jb] = acc;
-            }
         }
         __syncthreads();
     }
-    if (!stager && a.muT) {
+    if (a.muT) {
 #pragma unroll
         for (int jb = 0; jb < DK / 16; ++jb)
             *(f32x4 *)(a.muT + srow + 16 * jb + 4 * lg) = St[jb];
@@ -2355,6 +2416,7 @@ size_t device_lds_max() {
 template <int DK>
 palimpsa_status launch_frozen(const FrozenArgs &a, hipStream_t s) {
     constexpr size_t lds = FzLds<DK>::kTotal;
+    static_assert(lds <= 160 * 1024, "frozen staging exceeds the CU's LDS");
     auto kern = frozen_fwd_kernel<DK>;
     if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return PALIMPSA_ERR_HIP;
