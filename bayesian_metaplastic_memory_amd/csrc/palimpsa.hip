@@ -65,15 +65,22 @@ typedef __bf16 bf16_t;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T> struct io;
+// bits()/from_bits(): a scalar kept in its raw bits between a prefetch and its
+// use, so that the widening (and the wait for the load) happens at the use
+// and not where the load is issued; bits 0 is 0.0 in both types.
 template <> struct io<float> {
     static constexpr int kBytes = 4;
     __device__ static inline float to_f32(float x) { return x; }
     __device__ static inline float from_f32(float x) { return x; }
+    __device__ static inline uint32_t bits(float x) { return __float_as_uint(x); }
+    __device__ static inline float from_bits(uint32_t b) { return __uint_as_float(b); }
 };
 template <> struct io<bf16_t> {
     static constexpr int kBytes = 2;
     __device__ static inline float to_f32(bf16_t x) { return (float)x; }
     __device__ static inline bf16_t from_f32(float x) { return (bf16_t)x; }  // RNE
+    __device__ static inline uint32_t bits(bf16_t x) { return __builtin_bit_cast(uint16_t, x); }
+    __device__ static inline float from_bits(uint32_t b) { return __uint_as_float(b << 16); }
 };
 
 // Widen a 16-byte packet of T to float32 values.
@@ -193,7 +200,7 @@ struct Stager {
 
     uint4 kq[kKQPerThread];
     uint4 vv, bb;
-    float dtv, dtc;
+    uint32_t dtv, dtc;     // raw bits (io<TIn>::bits) until the commit
 
     __device__ static inline int vb_slot(int tid) { return (tid + kThreads - 64) % kThreads; }
     __device__ static inline int gate_slot(int tid) { return (tid + kThreads - 128) % kThreads; }
@@ -229,13 +236,13 @@ struct Stager {
         }
         const int pg = gate_slot(tid);
         if (pg < C) {
-            dtv = 0.f;
-            if (pg < left) dtv = io<TIn>::to_f32(db[(uint32_t)pg * (uint32_t)H]);
+            dtv = 0;
+            if (pg < left) dtv = io<TIn>::bits(db[(uint32_t)pg * (uint32_t)H]);
         }
         const int pc = c_slot(tid);
         if (pc < C) {
-            dtc = 0.f;
-            if (pc < left) dtc = io<TIn>::to_f32(db[(uint32_t)pc * (uint32_t)H]);
+            dtc = 0;
+            if (pc < left) dtc = io<TIn>::bits(db[(uint32_t)pc * (uint32_t)H]);
         }
     }
 
@@ -286,10 +293,10 @@ struct Stager {
         // alpha on wave 2 and c = (1 - alpha) I_prior on wave 3 (the gate of Eq. (9))
         const int pg = gate_slot(tid);
         if (pg < C)
-            gates[2 * pg] = expf(-A * dtv);
+            gates[2 * pg] = expf(-A * io<TIn>::from_bits(dtv));
         const int pc = c_slot(tid);
         if (pc < C)
-            gates[2 * pc + 1] = -expm1f(-A * dtc) * Ip;
+            gates[2 * pc + 1] = -expm1f(-A * io<TIn>::from_bits(dtc)) * Ip;
     }
 };
 
@@ -775,7 +782,7 @@ struct BwdStager {
 
     uint4 kq[kKQPer];
     uint4 vv, bb, gg;
-    float dtv;
+    uint32_t dtv;          // raw bits (io<TIn>::bits) until the commit
 
     __device__ static inline int vb_slot(int tid) { return (tid + kThreads - 64) % kThreads; }
     __device__ static inline int gy_slot(int tid) { return (tid + kThreads - 128) % kThreads; }
@@ -817,8 +824,8 @@ struct BwdStager {
         }
         const int pd = dt_slot(tid);
         if (pd < kSB) {
-            dtv = 0.f;
-            if (pd < left) dtv = io<TIn>::to_f32(db[(uint32_t)pd * (uint32_t)H]);
+            dtv = 0;
+            if (pd < left) dtv = io<TIn>::bits(db[(uint32_t)pd * (uint32_t)H]);
         }
     }
 
@@ -874,7 +881,7 @@ struct BwdStager {
         }
         const int pd = dt_slot(tid);
         if (pd < kSB) {
-            const float2 gc = gate(A, dtv, Ip);
+            const float2 gc = gate(A, io<TIn>::from_bits(dtv), Ip);
             *(float2 *)(buf + S::kGate + 2 * pd) = gc;
         }
     }
@@ -1516,7 +1523,7 @@ struct WideStager {
     static constexpr int kHalf = C * kColPkts;
     static constexpr int kKQPer = (2 * kHalf + kThreads - 1) / kThreads;
     uint4 kq[kKQPer];
-    float vv, bb, dtv;
+    uint32_t vv, bb, dtv;  // raw bits (io<TIn>::bits) until the commit
     // thread slots: (token, row) pairs of (v, beta) on wave 1, dt on wave 2
     __device__ static inline int vb_slot(int tid) { return (tid + kThreads - 64) % kThreads; }
     __device__ static inline int dt_slot(int tid) { return (tid + kThreads - 128) % kThreads; }
@@ -1538,17 +1545,17 @@ struct WideStager {
         const int pv = vb_slot(tid);
         if (pv < C * W::kRows) {
             const int tt = pv / W::kRows, r = pv % W::kRows;
-            vv = 0.f; bb = 0.f;
+            vv = 0; bb = 0;
             if (tt < left) {
                 const size_t off = (size_t)tt * H * dv + r;
-                vv = io<TIn>::to_f32(vb[off]);
-                bb = io<TIn>::to_f32(bb_[off]);
+                vv = io<TIn>::bits(vb[off]);
+                bb = io<TIn>::bits(bb_[off]);
             }
         }
         const int pd = dt_slot(tid);
         if (pd < C) {
-            dtv = 0.f;
-            if (pd < left) dtv = io<TIn>::to_f32(db[(size_t)pd * H]);
+            dtv = 0;
+            if (pd < left) dtv = io<TIn>::bits(db[(size_t)pd * H]);
         }
     }
     __device__ inline void commit(float *buf, float A, float Ip, int tid) const {
@@ -1579,11 +1586,13 @@ struct WideStager {
             }
         }
         const int pv = vb_slot(tid);
-        if (pv < C * W::kRows)
-            *(float2 *)(rows + 2 * pv) = make_float2(bb, bb * vv);
+        if (pv < C * W::kRows) {
+            const float b = io<TIn>::from_bits(bb), v = io<TIn>::from_bits(vv);
+            *(float2 *)(rows + 2 * pv) = make_float2(b, b * v);
+        }
         const int pd = dt_slot(tid);
         if (pd < C)
-            *(float2 *)(gates + 2 * pd) = gate(A, dtv, Ip);
+            *(float2 *)(gates + 2 * pd) = gate(A, io<TIn>::from_bits(dtv), Ip);
     }
 };
 
