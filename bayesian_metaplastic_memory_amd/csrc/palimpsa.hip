@@ -1149,12 +1149,15 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             if (sb > 0) st.commit(lds + ((sb - 1) & 1) * S::kFloats, A, Ip, tid, a.vstar);
             __syncthreads();
             // sums over the 4 waves: this row block's partials of (gq, gk) and (da, dc)
-            for (int n = tid; n < kSB * 2 * DK; n += kThreads) {
+            for (int n = 4 * tid; n < kSB * 2 * DK; n += 4 * kThreads) {
                 const int e = n / (2 * DK), c = n % (2 * DK);
-                const float v = (red[(e * kWaves + 0) * 2 * DK + c] + red[(e * kWaves + 1) * 2 * DK + c]) +
-                                (red[(e * kWaves + 2) * 2 * DK + c] + red[(e * kWaves + 3) * 2 * DK + c]);
+                const float *r0 = red + e * kWaves * 2 * DK + c;
+                const float4 v0 = *(const float4 *)r0, v1 = *(const float4 *)(r0 + 2 * DK);
+                const float4 v2 = *(const float4 *)(r0 + 4 * DK), v3 = *(const float4 *)(r0 + 6 * DK);
                 if (t0 + e < a.T)
-                    a.pqk[((size_t)rb * bth + seq0 + (size_t)(t0 + e) * a.H) * 2 * DK + c] = v;
+                    *(float4 *)(a.pqk + ((size_t)rb * bth + seq0 + (size_t)(t0 + e) * a.H) * 2 * DK + c) =
+                        make_float4((v0.x + v1.x) + (v2.x + v3.x), (v0.y + v1.y) + (v2.y + v3.y),
+                                    (v0.z + v1.z) + (v2.z + v3.z), (v0.w + v1.w) + (v2.w + v3.w));
             }
             // per (token, row): gv = gbv beta, gbeta = gbv v + gb; per token: the
             // row block's sums of (da, dc)
