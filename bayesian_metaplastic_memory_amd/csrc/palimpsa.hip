@@ -947,12 +947,13 @@ __device__ inline void bwd_reverse_token(const float *buf, int e, const float *M
 #pragma unroll
         for (int x = 0; x < LT::kVec; ++x) {
             const int s = m * LT::kVec + x;
+            // readout adjoint: with u = q r, GM += gy u and GI -= gy q r mu = dq u
             const float r = __builtin_amdgcn_rcpf(It[s]);
+            const float u = qq[x] * r;
             const float mu = Mt[s] * r;
-            const float gr = gy * qq[x] * r;
-            GM[s] += gr;
-            GI[s] = fmaf(-gr, mu, GI[s]);
+            GM[s] = fmaf(gy, u, GM[s]);
             dq[s] = gy * mu;
+            GI[s] = fmaf(-dq[s], u, GI[s]);
             dk[s] = fmaf(GM[s], bv, GI[s] * (b2 * kk[x]));
             cbv = fmaf(GM[s], kk[x], cbv);
             cb = fmaf(GI[s], k2[x], cb);

@@ -37,9 +37,9 @@ RCP_SLOTS = 2                # v_rcp_f32 issue cost in FMA slots: half rate on g
 FLOPS_PER_UPDATE = 10        # FMA = 2 flops, MUL = 1; the reciprocal is not counted
 HBM_PEAK_GBS = 8000.0
 # Backward per state entry and token: replay of the update (2 FMA + MUL + FMA
-# = 4 VALU, 7 flops) and the reverse step (17 VALU = 22 flops, plus one
-# v_rcp_f32 = 2 slots): 23 issue slots, 29 flops.
-BWD_SLOTS_PER_UPDATE = 23
+# = 4 VALU, 7 flops) and the reverse step (16 VALU = 22 flops, plus one
+# v_rcp_f32 = 2 slots): 22 issue slots, 29 flops.
+BWD_SLOTS_PER_UPDATE = 22
 BWD_FLOPS_PER_UPDATE = 29
 # 2x2 block-diagonal precision, per block of two entries and token: precision
 # 2 + 2 + 3 VALU, content 4, determinant 2, solve 6, readout 2 = 21 VALU
@@ -171,7 +171,7 @@ def backward_extra(torch, pm, workloads, w, g, steps):
                          "frac": achieved / bwd_peak_tflops(),
                          "traffic": load_traffic("bwd_layer760m_bf16_traffic.json") if w.name.startswith("layer760m") else None,
                          "scope": "whole call (5 kernels); per-kernel split in the committed trace",
-                         "per_update": "replay 4 VALU + reverse 17 VALU + 1 v_rcp_f32 = 23 slots, 29 flops"}}
+                         "per_update": "replay 4 VALU + reverse 16 VALU + 1 v_rcp_f32 = 22 slots, 29 flops"}}
 
 
 def training_extra(torch, pm, workloads, w, g, steps):
