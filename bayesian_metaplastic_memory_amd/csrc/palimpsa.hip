@@ -1509,7 +1509,8 @@ template <int D> struct WideCfg {
     // have at least two tokens of compute to arrive
     static constexpr int kChunk = D == 512 ? 4 : 2;
     static constexpr bool kStageK2 = D < 2048;
-    static constexpr int kRows = 4;                      // value rows per workgroup
+    static constexpr int kRowsPerWave = D >= 2048 ? 1 : 2;   // rows per wave: a lane holds each one's entries of its columns
+    static constexpr int kRows = 4 * kRowsPerWave;       // value rows per workgroup
     static constexpr int kColFloats = (kStageK2 ? 3 : 2) * D;   // k, (k^2), q per token
     static constexpr int kQ = (kStageK2 ? 2 : 1) * D;    // offset of q in a token
     static constexpr int kTokFloats = kColFloats + 2 * kRows + 2;
@@ -1611,7 +1612,7 @@ __device__ inline float sum_rows4(float x) {
 template <int D, typename TIn, typename TOut>
 __global__ __launch_bounds__(kThreads) void wide_fwd_kernel(FwdArgs a) {
     using W = WideCfg<D>;
-    constexpr int C = W::kChunk, KC = W::kCols;
+    constexpr int C = W::kChunk, KC = W::kCols, R = W::kRowsPerWave;
     extern __shared__ float lds[];
     const int rb_per_head = a.dv / W::kRows;
     int wg = blockIdx.x;
@@ -1624,25 +1625,27 @@ __global__ __launch_bounds__(kThreads) void wide_fwd_kernel(FwdArgs a) {
     const int b = bh / a.H, h = bh % a.H;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int g = lane & 15;
-    const int row = row0 + wave;
+    const int rw = wave * R;                          // the wave's first row in the workgroup
     const float A = a.A[h], Ip = a.Ip[h];
 
-    float M[KC], I[KC];
-    const size_t srow = ((size_t)bh * a.dv + row) * D;
+    // state of the wave's R rows: the lane's KC columns of each
+    float M[R][KC], I[R][KC];
+    const size_t srow = ((size_t)bh * a.dv + row0 + rw) * D;
 #pragma unroll
-    for (int m = 0; m < W::kVecs; ++m) {
-        float mu[4], ii[4];
-        if (a.mu0) {
-            vecf<4>::ld(a.mu0 + srow + W::col(lane, m, 0), mu);
-            vecf<4>::ld(a.I0 + srow + W::col(lane, m, 0), ii);
-        } else {
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { mu[e] = 0.f; ii[e] = Ip; }
+        for (int m = 0; m < W::kVecs; ++m) {
+            float mu[4], ii[4];
+            if (a.mu0) {
+                vecf<4>::ld(a.mu0 + srow + (size_t)r * D + W::col(lane, m, 0), mu);
+                vecf<4>::ld(a.I0 + srow + (size_t)r * D + W::col(lane, m, 0), ii);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { mu[e] = 0.f; ii[e] = Ip; }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { I[r][4 * m + e] = ii[e]; M[r][4 * m + e] = ii[e] * mu[e]; }
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { I[4 * m + e] = ii[e]; M[4 * m + e] = ii[e] * mu[e]; }
-    }
 
     const size_t seq = (size_t)b * a.T * a.H + h;
     const TIn *kseq = (const TIn *)a.k + seq * D;
@@ -1652,7 +1655,7 @@ __global__ __launch_bounds__(kThreads) void wide_fwd_kernel(FwdArgs a) {
     const TIn *dseq = (const TIn *)a.dt + seq;
     const size_t kq_tok = (size_t)a.H * D, vb_tok = (size_t)a.H * a.dv;
     const size_t ystride = (size_t)a.H * a.dv;
-    TOut *ybase = (TOut *)a.y + seq * a.dv + row;
+    TOut *ybase = (TOut *)a.y + seq * a.dv + row0 + rw;
     const int nchunks = (a.T + C - 1) / C;
     WideStager<D, TIn> st;
     if (nchunks > 0) {
@@ -1670,16 +1673,22 @@ __global__ __launch_bounds__(kThreads) void wide_fwd_kernel(FwdArgs a) {
                     dseq + tn * a.H, a.T - (t0 + C), a.H, a.dv, tid);
         }
         const float *cur = lds + (c & 1) * W::kBufFloats;
-        const float *rows = cur + C * W::kColFloats + 2 * wave;
+        const float *rows = cur + C * W::kColFloats + 2 * rw;
         int goff = C * (W::kColFloats + 2 * W::kRows);
         asm volatile("" : "+v"(goff));
         const float *gates = cur + goff;
-#pragma unroll 1
+        // the chunk's 2-4 tokens unrolled: the next token's LDS reads are
+        // issued under the current token's arithmetic
+#pragma unroll
         for (int u = 0; u < C; ++u) {
             const float2 gc = *(const float2 *)(gates + 2 * u);
-            const float2 rb = *(const float2 *)(rows + u * 2 * W::kRows);
+            float2 rb[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) rb[r] = *(const float2 *)(rows + u * 2 * W::kRows + 2 * r);
             const float *ct = cur + u * W::kColFloats + 4 * lane;
-            float acc = 0.f;
+            float acc[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = 0.f;
 #pragma unroll
             for (int m = 0; m < W::kVecs; ++m) {
                 float kk[4], k2[4], qq[4];
@@ -1690,35 +1699,44 @@ __global__ __launch_bounds__(kThreads) void wide_fwd_kernel(FwdArgs a) {
                 for (int e = 0; e < 4; ++e) {
                     const int s = 4 * m + e;
                     if (!W::kStageK2) k2[e] = kk[e] * kk[e];
-                    const float w = fmaf(rb.x, k2[e], gc.y);
-                    I[s] = fmaf(gc.x, I[s], w);
-                    M[s] = fmaf(gc.x, M[s], rb.y * kk[e]);
-                    const float r = __builtin_amdgcn_rcpf(I[s]);
-                    acc = fmaf(M[s] * r, qq[e], acc);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const float w = fmaf(rb[r].x, k2[e], gc.y);
+                        I[r][s] = fmaf(gc.x, I[r][s], w);
+                        M[r][s] = fmaf(gc.x, M[r][s], rb[r].y * kk[e]);
+                        const float rc = __builtin_amdgcn_rcpf(I[r][s]);
+                        acc[r] = fmaf(M[r][s] * rc, qq[e], acc[r]);
+                    }
                 }
             }
-            const float yv = sum_rows4(row16_sum(acc));
-            if (lane == 0 && t0 + u < a.T)
-                ybase[(size_t)(t0 + u) * ystride] = io<TOut>::from_f32(yv);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float yv = sum_rows4(row16_sum(acc[r]));
+                if (lane == 0 && t0 + u < a.T)
+                    ybase[(size_t)(t0 + u) * ystride + r] = io<TOut>::from_f32(yv);
+            }
         }
         if (more) st.commit(lds + ((c + 1) & 1) * W::kBufFloats, A, Ip, tid);
         __syncthreads();
     }
     if (a.muT) {
 #pragma unroll
-        for (int m = 0; m < W::kVecs; ++m) {
-            float mu[4], ii[4];
-            if (a.T == 0 && a.mu0) {
-                vecf<4>::ld(a.mu0 + srow + W::col(lane, m, 0), mu);
-            } else {
+        for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) mu[e] = M[4 * m + e] / I[4 * m + e];
+            for (int m = 0; m < W::kVecs; ++m) {
+                float mu[4], ii[4];
+                const size_t o = srow + (size_t)r * D + W::col(lane, m, 0);
+                if (a.T == 0 && a.mu0) {
+                    vecf<4>::ld(a.mu0 + o, mu);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) mu[e] = M[r][4 * m + e] / I[r][4 * m + e];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ii[e] = I[r][4 * m + e];
+                vecf<4>::st(a.muT + o, mu);
+                vecf<4>::st(a.IT + o, ii);
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ii[e] = I[4 * m + e];
-            vecf<4>::st(a.muT + srow + W::col(lane, m, 0), mu);
-            vecf<4>::st(a.IT + srow + W::col(lane, m, 0), ii);
-        }
     }
 }
 
