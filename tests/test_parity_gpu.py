@@ -872,6 +872,10 @@ WIDE_CASES = [
     (1, 1, 30, 1024, 64, torch.float32, True),
     (1, 1, 19, 2048, 32, torch.float32, False),
     (1, 1, 9, 2048, 2048, torch.bfloat16, True),
+    (2, 3, 11, 512, 16, torch.float32, True),      # two 8-row workgroups per head
+    (1, 2, 66, 1024, 80, torch.bfloat16, False),   # ten 8-row workgroups, 33 chunks
+    (1, 1, 0, 512, 16, torch.float32, True),       # empty sequence: the state is copied through
+    (2, 1, 0, 2048, 32, torch.float32, False),     # empty sequence from the default state
 ]
 
 
