@@ -27,9 +27,10 @@ Contents
     The Gaussian update with the precision kept block-diagonal along the key
     axis (limited cross-key correlations); block 1 is Eq. (5), block dk the
     full update.
-``fwd_mamba2_limit``
+``fwd_mamba2_limit`` / ``bwd_mamba2_limit``
     The frozen-importance recurrence of the Mamba2 limit (slides, frame "The
-    Mamba2 limit enables a gradual model upgrade", Secs. 2.3-2.4).
+    Mamba2 limit enables a gradual model upgrade", Secs. 2.3-2.4), and its
+    reverse-mode derivative.
 
 All arrays use the library's layouts: q, k ``[B, T, H, dk]``; v, beta
 ``[B, T, H, dv]``; dt ``[B, T, H]``; A, I_prior ``[H]``; state
@@ -345,6 +346,65 @@ def fwd_mamba2_limit(q, k, v, beta, dt, A, I_prior, mu0=None):
                 y[b, t, h] = m @ q[b, t, h]
             mu[b, h] = m
     return y, mu
+
+
+def bwd_mamba2_limit(q, k, v, beta, dt, A, I_prior, gy, mu0=None, gmuT=None):
+    """Reverse-mode derivative of ``fwd_mamba2_limit`` for
+    ``L = <gy, y> + <gmuT, muT>``; ``beta`` None means ``v`` holds beta . v.
+
+    The frozen recurrence m_t = a_t m_{t-1} + w_t k_t^T, w_t = beta_t v_t / I_prior,
+    y_t = m_t q_t, walked from t = T-1 down with G the adjoint of m_t:
+    G += gy_t q_t^T (readout), then gq_t = m_t^T gy_t, gk_t = G^T w_t,
+    gw_t = G k_t, ga_t = <G, m_{t-1}>, and G = a_t G for m_{t-1}.  States
+    are recomputed from checkpoints every ceil(sqrt(T)) tokens.  Returns a
+    dict of float64 arrays gq, gk, gv, gbeta (None without beta), gdt, gA,
+    gIp, gmu0."""
+    q, k, v, dt, gy = (_f64(x) for x in (q, k, v, dt, gy))
+    vstar = beta is None
+    beta = np.ones(v.shape) if vstar else _f64(beta)
+    A, Ip = _f64(A), _f64(I_prior)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    m0 = np.zeros((B, H, dv, dk)) if mu0 is None else _f64(mu0)
+    gT = np.zeros((B, H, dv, dk)) if gmuT is None else _f64(gmuT)
+    out = {n: np.zeros(x.shape) for n, x in (("gq", q), ("gk", k), ("gv", v), ("gbeta", v), ("gdt", dt))}
+    out["gA"], out["gIp"], out["gmu0"] = np.zeros(H), np.zeros(H), np.zeros((B, H, dv, dk))
+    seg = max(1, int(np.ceil(np.sqrt(max(T, 1)))))
+    for b in range(B):
+        for h in range(H):
+            w = beta[b, :, h] * v[b, :, h] / Ip[h]                    # [T, dv]
+            gates = [_gate(A[h], dt[b, t, h])[0] for t in range(T)]
+            # checkpoints: the state before tokens 0, seg, 2 seg, ...
+            cks, m = [], m0[b, h].copy()
+            for t in range(T):
+                if t % seg == 0:
+                    cks.append(m.copy())
+                m = gates[t] * m + np.outer(w[t], k[b, t, h])
+            G = gT[b, h].copy()
+            for s0 in (range(((T - 1) // seg) * seg, -1, -seg) if T else ()):
+                # states before each token of the segment [s0, s1)
+                s1 = min(T, s0 + seg)
+                states = [cks[s0 // seg]]
+                for t in range(s0, s1):
+                    states.append(gates[t] * states[-1] + np.outer(w[t], k[b, t, h]))
+                for t in range(s1 - 1, s0 - 1, -1):
+                    m_t, m_p = states[t - s0 + 1], states[t - s0]
+                    G = G + np.outer(gy[b, t, h], q[b, t, h])
+                    out["gq"][b, t, h] = m_t.T @ gy[b, t, h]
+                    out["gk"][b, t, h] = G.T @ w[t]
+                    gw = G @ k[b, t, h]
+                    ga = float(np.sum(G * m_p))
+                    out["gv"][b, t, h] = gw * beta[b, t, h] / Ip[h]
+                    out["gbeta"][b, t, h] = gw * v[b, t, h] / Ip[h]
+                    out["gIp"][h] -= float(gw @ w[t]) / Ip[h]
+                    a = gates[t]
+                    out["gdt"][b, t, h] = -A[h] * a * ga
+                    out["gA"][h] -= dt[b, t, h] * a * ga
+                    G = a * G
+            out["gmu0"][b, h] = G
+    if vstar:
+        out["gbeta"] = None
+    return out
 
 
 def fwd_blockdiag(q, k, v, beta, dt, A, I_prior, block: int, mu0=None, P0=None):
