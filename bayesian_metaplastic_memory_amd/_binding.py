@@ -54,6 +54,8 @@ def load_library() -> ctypes.CDLL:
             lib.palimpsa_bwd.argtypes = [vp] * 5 + [fp] * 4 + [vp, fp, fp] + [fp] * 9 + [i] * 8 + [vp, sz, vp]
             lib.palimpsa_bwd.restype = i
             lib.palimpsa_bwd_workspace_size.argtypes = [i] * 6
+            lib.palimpsa_bwd_frozen.argtypes = [vp] * 5 + [fp] * 3 + [vp, fp] + [fp] * 8 + [i] * 7 + [vp, sz, vp]
+            lib.palimpsa_bwd_frozen.restype = i
             lib.palimpsa_bwd_workspace_size.restype = sz
             lib.palimpsa_fwd_blockdiag.argtypes = [vp] * 5 + [fp] * 4 + [vp, fp, fp] + [i] * 8 + [vp]
             lib.palimpsa_fwd_blockdiag.restype = i
@@ -350,6 +352,68 @@ def bwd(q, k, v, beta, dt, A, I_prior, gy, mu0=None, I0=None, gmuT=None, gIT=Non
             _ptr(workspace), workspace.numel(), _stream_handle(dev))
     if st != OK:
         raise PalimpsaError(st, "palimpsa_bwd")
+    return res
+
+
+def bwd_frozen(q, k, v, beta, dt, A, I_prior, gy, mu0=None, gmuT=None, want_state_grads: bool = True,
+               workspace=None, out=None):
+    """Backward of ``fwd_frozen`` (frozen importance) for ``L = <gy, y> + <gmuT, muT>``.
+
+    Takes the forward's inputs and returns a dict of float32 gradients ``gq,
+    gk, gv, gbeta, gdt, gA, gIp`` and, if ``want_state_grads``, ``gmu0``.
+    ``beta`` None means ``v`` holds the write ``beta * v``; ``gv`` is then the
+    gradient w.r.t. it and ``gbeta`` is None.  ``out`` and ``workspace`` as in
+    ``bwd`` (workspace: ``bwd_workspace_size(B, T, H, dk, dv)`` bytes)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    in_dtype = q.dtype
+    if in_dtype not in _DTYPES or gy.dtype not in _DTYPES:
+        raise ValueError("unsupported dtype")
+    for t, name, shape in ((k, "k", (B, T, H, dk)), (v, "v", (B, T, H, dv)), (dt, "dt", (B, T, H))):
+        _check(t, name, shape, in_dtype, dev)
+    if beta is not None:
+        _check(beta, "beta", (B, T, H, dv), in_dtype, dev)
+    _check(gy, "gy", (B, T, H, dv), gy.dtype, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(I_prior, "I_prior", (H,), torch.float32, dev)
+    for t, name in ((mu0, "mu0"), (gmuT, "gmuT")):
+        if t is not None:
+            _check(t, name, (B, H, dv, dk), torch.float32, dev)
+    shapes = {"gq": (B, T, H, dk), "gk": (B, T, H, dk), "gv": (B, T, H, dv), "gdt": (B, T, H), "gA": (H,),
+              "gIp": (H,)}
+    if beta is not None:
+        shapes["gbeta"] = (B, T, H, dv)
+    if want_state_grads:
+        shapes["gmu0"] = (B, H, dv, dk)
+    res = {}
+    for name, shape in shapes.items():
+        t = (out or {}).get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=torch.float32, device=dev)
+        _check(t, name, shape, torch.float32, dev)
+        res[name] = t
+    lib = load_library()
+    nbytes = bwd_workspace_size(B, T, H, dk, dv, 0)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
+    nz = lambda t: _ptr(t) if t is not None and t.numel() else None
+    with torch.cuda.device(dev):
+        st = lib.palimpsa_bwd_frozen(
+            nz(q), nz(k), nz(v), nz(beta), nz(dt), _ptr(A), _ptr(I_prior), _ptr(mu0), nz(gy), _ptr(gmuT),
+            nz(res["gq"]), nz(res["gk"]), nz(res["gv"]), nz(res.get("gbeta")), nz(res["gdt"]),
+            _ptr(res["gA"]), _ptr(res["gIp"]), _ptr(res.get("gmu0")),
+            B, T, H, dk, dv, _DTYPES[in_dtype], _DTYPES[gy.dtype],
+            _ptr(workspace), workspace.numel(), _stream_handle(dev))
+    if st != OK:
+        raise PalimpsaError(st, "palimpsa_bwd_frozen")
+    res.setdefault("gbeta", None)
     return res
 
 

@@ -141,6 +141,7 @@ struct FwdArgs {
     float *ck_sink;    // training forward: one block's worth of discarded stores
     int nsb;           // checkpoints per sequence: ceil(T / kSB)
     int vstar;         // 1: v holds beta . v (the write itself)
+    int frozen;        // checkpoint pass of the frozen-importance backward: M_0 = I_prior mu0
 };
 
 // Workspace of a time-split forward: for each of the first nseg-1 segments,
@@ -592,7 +593,12 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
             for (int m = 0; m < LT::kNVec; ++m) {
                 float mu[LT::kVec], ii[LT::kVec];
                 vecf<LT::kVec>::ld(a.mu0 + srow + LT::col(g, m, 0), mu);
-                vecf<LT::kVec>::ld(a.I0 + srow + LT::col(g, m, 0), ii);
+                if (a.frozen) {
+#pragma unroll
+                    for (int e = 0; e < LT::kVec; ++e) ii[e] = Ip;
+                } else {
+                    vecf<LT::kVec>::ld(a.I0 + srow + LT::col(g, m, 0), ii);
+                }
 #pragma unroll
                 for (int e = 0; e < LT::kVec; ++e) {
                     I[m * LT::kVec + e] = ii[e];
@@ -888,8 +894,9 @@ struct BwdStager {
 };
 
 // One token of the replay: the forward update of the lane's entries (the
-// same operations as compute_chunk, so the states are bit-identical).
-template <int DK, bool IPE>
+// same operations as compute_chunk, so the states are bit-identical).  FZ
+// (frozen importance) replays the content scan only.
+template <int DK, bool IPE, bool FZ = false>
 __device__ inline void bwd_replay_token(const float *buf, int e, float *M, float *I, int row_local, int g,
                                         const float *ipe) {
     using LT = LaneTile<DK>;
@@ -906,11 +913,44 @@ __device__ inline void bwd_replay_token(const float *buf, int e, float *M, float
 #pragma unroll
         for (int x = 0; x < LT::kVec; ++x) {
             const int s = m * LT::kVec + x;
-            const float w = fmaf(rb.x, k2[x], IPE ? gc.y * ipe[s] : gc.y);
-            I[s] = fmaf(gc.x, I[s], w);
+            if (!FZ) {
+                const float w = fmaf(rb.x, k2[x], IPE ? gc.y * ipe[s] : gc.y);
+                I[s] = fmaf(gc.x, I[s], w);
+            }
             M[s] = fmaf(gc.x, M[s], rb.y * kk[x]);
         }
     }
+}
+
+// Reduce-scatter of a token's (gq, gk) lane partials over the wave's 4 rows.
+// v_permlane32_swap of (x, y) leaves lanes < 32 with x of lanes l and l+32
+// and the others with y of lanes l-32 and l, so one add pairs rows (0, 2) and
+// (1, 3) and keeps gq in the low half-wave, gk in the high; v_permlane16_swap
+// then pairs rows (0, 1) and (2, 3), even rows keeping the first half of the
+// lane's columns.  The wave's column sums land in red (2 DK floats).
+template <int DK>
+__device__ inline void bwd_scatter_qk(const float *dq, const float *dk, int lane, int g, float *red) {
+    using LT = LaneTile<DK>;
+    constexpr int KC = LT::kCols;
+    const bool up32 = lane & 32, up16 = lane & 16;
+    float h8[KC];
+#pragma unroll
+    for (int s = 0; s < KC; ++s) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(dq[s]), __float_as_uint(dk[s]), false, false);
+        h8[s] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    constexpr int KH = KC / 2;
+    float h4[KH];
+#pragma unroll
+    for (int s = 0; s < KH; ++s) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(h8[s]), __float_as_uint(h8[KH + s]), false, false);
+        h4[s] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    const int s0 = up16 ? KH : 0;
+    float *dst = red + (up32 ? DK : 0) + LT::col(g, s0 / LT::kVec, s0 % LT::kVec);
+    if (KH == 4) *(float4 *)dst = make_float4(h4[0], h4[KH > 1 ? 1 : 0], h4[KH > 2 ? 2 : 0], h4[KH > 3 ? 3 : 0]);
+    else if (KH == 2) *(float2 *)dst = make_float2(h4[0], h4[KH > 1 ? 1 : 0]);
+    else dst[0] = h4[0];
 }
 
 // One token of the reverse walk for the lane's entries: (Mt, It) the state
@@ -969,31 +1009,45 @@ __device__ inline void bwd_reverse_token(const float *buf, int e, const float *M
             GI[s] *= alpha;
         }
     }
-    // reduce-scatter of (gq, gk) over the wave's 4 rows.  v_permlane32_swap
-    // of (x, y) leaves lanes < 32 with x of lanes l and l+32 and the others
-    // with y of lanes l-32 and l, so one add pairs rows (0, 2) and (1, 3) and
-    // keeps gq in the low half-wave, gk in the high; v_permlane16_swap then
-    // pairs rows (0, 1) and (2, 3), even rows keeping the first half of the
-    // lane's columns.
-    const bool up32 = lane & 32, up16 = lane & 16;
-    float h8[KC];
+    bwd_scatter_qk<DK>(dq, dk, lane, g, red);
+}
+
+// One token of the frozen-importance reverse walk (the importance held at
+// I_prior, the Mamba2 limit): the content scan M_t = a_t M_{t-1} + bv_i k_j is
+// the exact path's, the readout is y_t = M_t q_t / I_prior.  With GM the
+// adjoint of M_t: GM += gy_i q_j / I_prior, gq_j += gy_i M_ij / I_prior,
+// gk_j += GM bv_i, gbv_i += GM k_j, da_t += GM M_{t-1}, GM *= a_t.
+template <int DK>
+__device__ inline void bwd_reverse_token_fz(const float *buf, int e, const float *Mt, const float *Mp, float *GM,
+                                            int row_local, int g, int lane, float *red, float &cbv, float &s1,
+                                            float rIp) {
+    using LT = LaneTile<DK>;
+    using S = BwdStage<DK>;
+    constexpr int KC = LT::kCols;
+    const float alpha = buf[S::kGate + 2 * e];
+    const float4 rw = *(const float4 *)(buf + S::kRows + e * S::kRowFloats + 4 * row_local);
+    const float bv = rw.y, gyr = rw.w * rIp;
+    const float *ct = buf + e * S::kColFloats + LT::col(g, 0, 0);
+    float dq[KC], dk[KC];
+    cbv = 0.f; s1 = 0.f;
 #pragma unroll
-    for (int s = 0; s < KC; ++s) {
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(dq[s]), __float_as_uint(dk[s]), false, false);
-        h8[s] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-    constexpr int KH = KC / 2;
-    float h4[KH];
+    for (int m = 0; m < LT::kNVec; ++m) {
+        float kk[LT::kVec], qq[LT::kVec];
+        const int c0 = kLanesPerRow * LT::kVec * m;
+        vecf<LT::kVec>::ld(ct + c0, kk);
+        vecf<LT::kVec>::ld(ct + 2 * DK + c0, qq);
 #pragma unroll
-    for (int s = 0; s < KH; ++s) {
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(h8[s]), __float_as_uint(h8[KH + s]), false, false);
-        h4[s] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        for (int x = 0; x < LT::kVec; ++x) {
+            const int s = m * LT::kVec + x;
+            GM[s] = fmaf(gyr, qq[x], GM[s]);
+            dq[s] = gyr * Mt[s];
+            dk[s] = GM[s] * bv;
+            cbv = fmaf(GM[s], kk[x], cbv);
+            s1 = fmaf(GM[s], Mp[s], s1);
+            GM[s] *= alpha;
+        }
     }
-    const int s0 = up16 ? KH : 0;
-    float *dst = red + (up32 ? DK : 0) + LT::col(g, s0 / LT::kVec, s0 % LT::kVec);
-    if (KH == 4) *(float4 *)dst = make_float4(h4[0], h4[KH > 1 ? 1 : 0], h4[KH > 2 ? 2 : 0], h4[KH > 3 ? 3 : 0]);
-    else if (KH == 2) *(float2 *)dst = make_float2(h4[0], h4[KH > 1 ? 1 : 0]);
-    else dst[0] = h4[0];
+    bwd_scatter_qk<DK>(dq, dk, lane, g, red);
 }
 
 // Row sums of one half-block: acc holds the lane's partials of (gbv, gb, da,
@@ -1006,7 +1060,10 @@ __device__ inline void bwd_row_sums(const float (&acc)[16], int g, float *dst) {
     dst[((g % 4) * 4 + g / 4) * kRowsPerWG] = r;
 }
 
-template <int DK, typename TIn, typename TG, bool IPE>
+// FZ: the backward of the frozen-importance forward (the importance held at
+// I_prior): the same content scan, checkpoints and sums, with the importance
+// terms dropped (see bwd_reverse_token_fz).
+template <int DK, typename TIn, typename TG, bool IPE, bool FZ = false>
 __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     using LT = LaneTile<DK>;
     using S = BwdStage<DK>;
@@ -1043,6 +1100,11 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     }
 
     float GM[KC], GI[KC];
+    if (FZ) {
+#pragma unroll
+        for (int s = 0; s < KC; ++s) GI[s] = 0.f;
+    }
+    const float rIp = 1.f / Ip;    // frozen importance: the readout divides by I_prior
     const size_t seq0 = (size_t)b * a.T * a.H + h;           // row of (b, 0, h) in [B, T, H]
     const size_t bth = (size_t)a.B * a.T * a.H;
     const size_t kq_tok = (size_t)a.H * DK, vb_tok = (size_t)a.H * a.dv;
@@ -1058,7 +1120,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                 const float gmu = a.gmuT ? a.gmuT[o] : 0.f, gI = a.gIT ? a.gIT[o] : 0.f;
                 if (a.gmu0) a.gmu0[o] = gmu;
                 if (a.gI0) a.gI0[o] = gI;
-                GI[s] = gI;
+                GI[s] = FZ ? 0.f : gI;
             }
     } else {
         const size_t ck_stride = (size_t)rb_per_head * kThreads * 2 * KC;
@@ -1095,14 +1157,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
 #pragma unroll
             for (int s = 0; s < KC; ++s) { mM[s] = ckM[s]; mI[s] = ckI[s]; }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) bwd_replay_token<DK, IPE>(cur, e, mM, mI, row_local, g, ipe);
+            for (int e = 0; e < 4; ++e) bwd_replay_token<DK, IPE, FZ>(cur, e, mM, mI, row_local, g, ipe);
 #pragma unroll
             for (int e = 4; e < 8; ++e) {
                 const float *pm = e == 4 ? mM : xM[e > 4 ? e - 5 : 0];
                 const float *pi = e == 4 ? mI : xI[e > 4 ? e - 5 : 0];
 #pragma unroll
                 for (int s = 0; s < KC; ++s) { xM[e - 4][s] = pm[s]; xI[e - 4][s] = pi[s]; }
-                bwd_replay_token<DK, IPE>(cur, e, xM[e - 4], xI[e - 4], row_local, g, ipe);
+                bwd_replay_token<DK, IPE, FZ>(cur, e, xM[e - 4], xI[e - 4], row_local, g, ipe);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (sb == a.nsb - 1) {
@@ -1114,18 +1176,30 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                         const int s = m * LT::kVec + x;
                         const size_t o = srow + LT::col(g, m, x);
                         const float gmu = a.gmuT ? a.gmuT[o] : 0.f, gI = a.gIT ? a.gIT[o] : 0.f;
-                        const float muT = xM[3][s] / xI[3][s];
-                        GM[s] = gmu / xI[3][s];
-                        GI[s] = gI - GM[s] * muT;
+                        if (FZ) {
+                            GM[s] = gmu * rIp;                  // mu_T = M_T / I_prior
+                        } else {
+                            const float muT = xM[3][s] / xI[3][s];
+                            GM[s] = gmu / xI[3][s];
+                            GI[s] = gI - GM[s] * muT;
+                        }
                     }
             }
 #pragma unroll
-            for (int e = 7; e >= 4; --e)
-                bwd_reverse_token<DK, IPE>(cur, e, xM[e - 4], xI[e - 4], e == 4 ? mM : xM[e > 4 ? e - 5 : 0],
-                                      e == 4 ? mI : xI[e > 4 ? e - 5 : 0],
-                                      GM, GI, row_local, g, lane, red + (e * kWaves + wave) * 2 * DK,
-                                      acc[e - 4], acc[e], acc[e + 4], acc[e + 8], ipe, accIp);
+            for (int e = 7; e >= 4; --e) {
+                if (FZ) {
+                    bwd_reverse_token_fz<DK>(cur, e, xM[e - 4], e == 4 ? mM : xM[e > 4 ? e - 5 : 0], GM, row_local, g,
+                                             lane, red + (e * kWaves + wave) * 2 * DK, acc[e - 4], acc[e + 4], rIp);
+                    acc[e] = 0.f;
+                    acc[e + 8] = 0.f;
+                } else {
+                    bwd_reverse_token<DK, IPE>(cur, e, xM[e - 4], xI[e - 4], e == 4 ? mM : xM[e > 4 ? e - 5 : 0],
+                                               e == 4 ? mI : xI[e > 4 ? e - 5 : 0],
+                                               GM, GI, row_local, g, lane, red + (e * kWaves + wave) * 2 * DK,
+                                               acc[e - 4], acc[e], acc[e + 4], acc[e + 8], ipe, accIp);
+                }
                 __builtin_amdgcn_sched_barrier(0);
+            }
             bwd_row_sums(acc, g, rs + 4 * 4 * kRowsPerWG + row_local);
             // lower half: tokens 0..3
 #pragma unroll
@@ -1134,18 +1208,26 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                 const float *pi = e == 0 ? ckI : xI[e > 0 ? e - 1 : 0];
 #pragma unroll
                 for (int s = 0; s < KC; ++s) { xM[e][s] = pm[s]; xI[e][s] = pi[s]; }
-                bwd_replay_token<DK, IPE>(cur, e, xM[e], xI[e], row_local, g, ipe);
+                bwd_replay_token<DK, IPE, FZ>(cur, e, xM[e], xI[e], row_local, g, ipe);
                 __builtin_amdgcn_sched_barrier(0);
             }
             float nM[KC], nI[KC];
             if (sb > 0) load_pair<KC>(ckb + (size_t)(sb - 1) * ck_stride, tid, nM, nI);
 #pragma unroll
-            for (int e = 3; e >= 0; --e)
-                bwd_reverse_token<DK, IPE>(cur, e, xM[e], xI[e], e == 0 ? ckM : xM[e > 0 ? e - 1 : 0],
-                                      e == 0 ? ckI : xI[e > 0 ? e - 1 : 0],
-                                      GM, GI, row_local, g, lane, red + (e * kWaves + wave) * 2 * DK,
-                                      acc[e], acc[e + 4], acc[e + 8], acc[e + 12], ipe, accIp);
+            for (int e = 3; e >= 0; --e) {
+                if (FZ) {
+                    bwd_reverse_token_fz<DK>(cur, e, xM[e], e == 0 ? ckM : xM[e > 0 ? e - 1 : 0], GM, row_local, g,
+                                             lane, red + (e * kWaves + wave) * 2 * DK, acc[e], acc[e + 8], rIp);
+                    acc[e + 4] = 0.f;
+                    acc[e + 12] = 0.f;
+                } else {
+                    bwd_reverse_token<DK, IPE>(cur, e, xM[e], xI[e], e == 0 ? ckM : xM[e > 0 ? e - 1 : 0],
+                                               e == 0 ? ckI : xI[e > 0 ? e - 1 : 0],
+                                               GM, GI, row_local, g, lane, red + (e * kWaves + wave) * 2 * DK,
+                                               acc[e], acc[e + 4], acc[e + 8], acc[e + 12], ipe, accIp);
+                }
                 __builtin_amdgcn_sched_barrier(0);
+            }
             bwd_row_sums(acc, g, rs + row_local);
             if (sb > 0) st.commit(lds + ((sb - 1) & 1) * S::kFloats, A, Ip, tid, a.vstar);
             __syncthreads();
@@ -1171,14 +1253,23 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
                     // enters only through the importance
                     const size_t o = (seq0 + (size_t)(t0 + e) * a.H) * a.dv + row0 + r;
                     a.gv[o] = a.vstar ? gbv : gbv * rw.x;
-                    a.gbeta[o] = a.vstar ? gb : fmaf(gbv, rw.z, gb);
+                    if (!FZ || a.gbeta) a.gbeta[o] = a.vstar ? gb : fmaf(gbv, rw.z, gb);
                 }
             } else if (tid < kSB * kRowsPerWG + 2 * kSB) {
                 const int u = tid - kSB * kRowsPerWG, e = u % kSB, qd = u / kSB;
                 const float *src = rs + (e * 4 + 2 + qd) * kRowsPerWG;
                 float v = 0.f;
+                if (FZ && qd == 1) {
+                    // frozen importance: sum_i gbv_i (beta v)_i, the prior's gradient
+                    // through the readout's 1 / I_prior
 #pragma unroll
-                for (int r = 0; r < kRowsPerWG; ++r) v += src[r];
+                    for (int r = 0; r < kRowsPerWG; ++r)
+                        v = fmaf(rs[e * 4 * kRowsPerWG + r],
+                                 (cur + S::kRows + e * S::kRowFloats + 4 * r)[1], v);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < kRowsPerWG; ++r) v += src[r];
+                }
                 if (t0 + e < a.T) a.ps[((size_t)rb * bth + (size_t)bh * a.T + t0 + e) * 2 + qd] = v;
             }
             __syncthreads();
@@ -1195,6 +1286,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
             for (int x = 0; x < LT::kVec; ++x) {
                 const int s = m * LT::kVec + x;
                 const size_t o = srow + LT::col(g, m, x);
+                if (FZ) {
+                    if (a.gmu0) a.gmu0[o] = GM[s] * Ip;       // M_0 = I_prior mu_0
+                    continue;
+                }
                 const float i0 = a.mu0 ? a.I0[o] : (IPE ? ipe[s] : Ip), m0 = a.mu0 ? a.mu0[o] : 0.f;
                 const float gI0 = fmaf(GM[s], m0, GI[s]);
                 if (a.gmu0) a.gmu0[o] = GM[s] * i0;
@@ -1245,8 +1340,10 @@ __global__ __launch_bounds__(256) void bwd_qk_kernel(const float *pqk, float *gq
 // gdt per token and per-sequence sums of the gate gradients: one block per
 // (b, h), tokens strided over its threads.
 // (with a prior per entry dc already carries the prior: Ip enters as 1)
+// fz (frozen importance): ps holds (da, sum_i gbv_i (beta v)_i) and the gate
+// has no prior term.
 __global__ __launch_bounds__(256) void bwd_gate_kernel(const float *ps, const void *dt, int dt_bf16,
-                                                        const float *A, const float *Ip, int ipe, float *gdt,
+                                                        const float *A, const float *Ip, int ipe, int fz, float *gdt,
                                                         float *gabh, float *gibh, int B, int T, int H, int nrb) {
     __shared__ float sh[2][4];
     const int bh = blockIdx.x, b = bh / H, h = bh % H;
@@ -1264,10 +1361,10 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const float *ps, const vo
         const float d = dt_bf16 ? (float)((const bf16_t *)dt)[row] : ((const float *)dt)[row];
         const float x = -Ah * d;
         const float al = expf(x), oma = -expm1f(x);
-        const float u = fmaf(Iph, dc, -da);
+        const float u = fz ? -da : fmaf(Iph, dc, -da);
         gdt[row] = Ah * al * u;
         accA = fmaf(d * al, u, accA);
-        accI = fmaf(oma, dc, accI);
+        accI = fz ? accI + dc : fmaf(oma, dc, accI);
     }
     accA = row16_sum(accA);
     accI = row16_sum(accI);
@@ -1284,9 +1381,10 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const float *ps, const vo
 // gA, gI_prior per head: sums over the batch (plus the start state's share
 // when it defaults to I_prior).  With a prior per entry only gA is written
 // here (gI_prior comes from bwd_prior_kernel).
+// fz: the frozen-importance prior gradient, -(1 / I_prior) sum gbv . (beta v).
 __global__ __launch_bounds__(64) void bwd_head_kernel(const float *gabh, const float *gibh, const float *pI0,
-                                                       float *gA, float *gIp, int B, int H, int nrb, int dflt,
-                                                       int ipe) {
+                                                       const float *Ip, float *gA, float *gIp, int B, int H, int nrb,
+                                                       int dflt, int ipe, int fz) {
     const int h = blockIdx.x * 64 + threadIdx.x;
     if (h >= H) return;
     float sa = 0.f, si = 0.f;
@@ -1297,7 +1395,8 @@ __global__ __launch_bounds__(64) void bwd_head_kernel(const float *gabh, const f
             for (int r = 0; r < nrb; ++r) si += pI0[((size_t)b * H + h) * nrb + r];
     }
     gA[h] = sa;
-    if (!ipe) gIp[h] = si;
+    if (fz) gIp[h] = -si / Ip[h];
+    else if (!ipe) gIp[h] = si;
 }
 
 // Per-entry prior: gI_prior[h, i, j] = sum over the batch of the sequences'
@@ -2492,7 +2591,7 @@ BwdWs plan_bwd_ws(void *base, int B, int T, int H, int dk, int dv, bool ipe) {
     return w;
 }
 
-template <int DK, typename TIn, typename TG, bool IPE>
+template <int DK, typename TIn, typename TG, bool IPE, bool FZ = false>
 palimpsa_status launch_bwd_t(const FwdArgs &fa, const BwdArgs &ba, const BwdWs &w, float *gq, float *gk,
                              float *gdt, float *gA, float *gIp, int dt_bf16, hipStream_t s) {
     if (ba.T > 0 && fa.ck) {   // ck NULL: the training forward stored the checkpoints already
@@ -2500,7 +2599,7 @@ palimpsa_status launch_bwd_t(const FwdArgs &fa, const BwdArgs &ba, const BwdWs &
         if (st != PALIMPSA_OK) return st;
     }
     const size_t lds = (size_t)BwdStage<DK>::kTotal * sizeof(float);
-    auto kern = bwd_kernel<DK, TIn, TG, IPE>;
+    auto kern = bwd_kernel<DK, TIn, TG, IPE, FZ>;
     if (lds > 64 * 1024 &&
         hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return PALIMPSA_ERR_HIP;
@@ -2514,16 +2613,26 @@ palimpsa_status launch_bwd_t(const FwdArgs &fa, const BwdArgs &ba, const BwdWs &
                            (const float *)w.pqk, gq, gk, bth, nrb);
     }
     hipLaunchKernelGGL(bwd_gate_kernel, dim3(ba.B * ba.H), dim3(256), 0, s, (const float *)w.ps, ba.dt, dt_bf16,
-                       ba.A, ba.Ip, IPE ? 1 : 0, gdt, w.gabh, w.gibh, ba.B, ba.T, ba.H, nrb);
+                       ba.A, ba.Ip, IPE ? 1 : 0, FZ ? 1 : 0, gdt, w.gabh, w.gibh, ba.B, ba.T, ba.H, nrb);
     hipLaunchKernelGGL(bwd_head_kernel, dim3((ba.H + 63) / 64), dim3(64), 0, s, (const float *)w.gabh,
-                       (const float *)w.gibh, (const float *)w.pI0, gA, gIp, ba.B, ba.H, nrb, ba.mu0 ? 0 : 1,
-                       IPE ? 1 : 0);
+                       (const float *)w.gibh, (const float *)w.pI0, ba.Ip, gA, gIp, ba.B, ba.H, nrb,
+                       (ba.mu0 || FZ) ? 0 : 1, IPE ? 1 : 0, FZ ? 1 : 0);
     if (IPE) {
         const size_t per_b = (size_t)ba.H * ba.dv * DK;
         hipLaunchKernelGGL(bwd_prior_kernel, dim3((unsigned)((per_b / 4 + 255) / 256)), dim3(256), 0, s,
                            (const float *)w.pip, gIp, ba.B, per_b);
     }
     return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
+}
+
+template <typename TIn, typename TG>
+palimpsa_status launch_bwd_fz_d(int dk, const FwdArgs &fa, const BwdArgs &ba, const BwdWs &w, float *gq, float *gk,
+                                float *gdt, float *gA, float *gIp, int dt_bf16, hipStream_t s) {
+    switch (dk) {
+    case 32: return launch_bwd_t<32, TIn, TG, false, true>(fa, ba, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    case 64: return launch_bwd_t<64, TIn, TG, false, true>(fa, ba, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    default: return launch_bwd_t<128, TIn, TG, false, true>(fa, ba, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    }
 }
 
 template <typename TIn, typename TG>
@@ -2667,6 +2776,69 @@ palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const 
     return launch_bwd_d<float, float>(dk, ipe, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
 }
 
+palimpsa_status palimpsa_bwd_frozen(const void *q, const void *k, const void *v, const void *beta,
+                                    const void *dt, const float *A, const float *I_prior, const float *mu0,
+                                    const void *gy, const float *gmuT,
+                                    float *gq, float *gk, float *gv, float *gbeta, float *gdt,
+                                    float *gA, float *gIp, float *gmu0,
+                                    int B, int T, int H, int dk, int dv,
+                                    palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+    if (!A || !I_prior || !gA || !gIp || !workspace)
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (T > 0 && (!q || !k || !v || !dt || !gy || !gq || !gk || !gv || !gdt || (beta && !gbeta)))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || !dtype_ok(in_dtype) || !dtype_ok(gy_dtype))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (!head_ok(dk) || !dv_ok(dv))
+        return PALIMPSA_ERR_UNSUPPORTED;
+    const void *vec_ptrs[] = {q, k, v, beta, gy, mu0, gmuT, gq, gk, gmu0, workspace};
+    for (const void *p : vec_ptrs)
+        if (p && !aligned_to(p, 16)) return PALIMPSA_ERR_ALIGNMENT;
+    const size_t in_sz = in_dtype == PALIMPSA_BF16 ? 2 : 4;
+    const void *f32_ptrs[] = {A, I_prior, gA, gIp, gv, gbeta, gdt};
+    for (const void *p : f32_ptrs)
+        if (p && !aligned_to(p, 4)) return PALIMPSA_ERR_ALIGNMENT;
+    if (dt && !aligned_to(dt, in_sz)) return PALIMPSA_ERR_ALIGNMENT;
+    const long long nwg = (long long)B * H * (dv / kRowsPerWG);
+    if (nwg > 0x7fffffffLL || (long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 46) ||
+        64LL * H * (dk > dv ? dk : dv) >= (1LL << 31) || (long long)B * H * 2 > 0x7fffffffLL)
+        return PALIMPSA_ERR_UNSUPPORTED;
+    const BwdWs w = plan_bwd_ws(workspace, B, T, H, dk, dv, false);
+    if (workspace_bytes < w.bytes) return PALIMPSA_ERR_INVALID_ARG;
+    // without beta the v tensor is the write itself; the beta pointer is then
+    // pointed at v so that every staged load stays valid (the frozen walk
+    // never reads it)
+    const void *bsrc = beta ? beta : v;
+
+    FwdArgs fa = {};
+    fa.q = q; fa.k = k; fa.v = v; fa.beta = bsrc; fa.dt = dt;
+    fa.A = A; fa.Ip = I_prior; fa.mu0 = mu0; fa.I0 = nullptr;
+    fa.B = B; fa.T = T; fa.H = H; fa.dv = dv;
+    fa.nwg = (int)nwg; fa.xcd_remap = (nwg % 8 == 0) ? 1 : 0; fa.nwg_seg = (int)nwg;
+    fa.seg_len = T > 0 ? T : 1; fa.nseg = 1;
+    fa.ck = w.ck; fa.nsb = (T + kSB - 1) / kSB;
+    fa.vstar = beta ? 0 : 1;
+    fa.frozen = 1;
+
+    BwdArgs ba = {};
+    ba.q = q; ba.k = k; ba.v = v; ba.beta = bsrc; ba.dt = dt; ba.gy = gy;
+    ba.A = A; ba.Ip = I_prior; ba.mu0 = mu0; ba.I0 = nullptr; ba.gmuT = gmuT; ba.gIT = nullptr;
+    ba.gv = gv; ba.gbeta = beta ? gbeta : nullptr; ba.gmu0 = gmu0; ba.gI0 = nullptr;
+    ba.ck = w.ck; ba.pqk = w.pqk; ba.ps = w.ps; ba.pI0 = w.pI0; ba.pip = nullptr;
+    ba.vstar = fa.vstar;
+    ba.B = B; ba.T = T; ba.H = H; ba.dv = dv; ba.nsb = fa.nsb;
+    ba.nwg = (int)nwg; ba.xcd_remap = fa.xcd_remap;
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf_in = in_dtype == PALIMPSA_BF16, bf_gy = gy_dtype == PALIMPSA_BF16;
+    const int dtb = bf_in ? 1 : 0;
+    if (bf_in && bf_gy) return launch_bwd_fz_d<bf16_t, bf16_t>(dk, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
+    if (bf_in) return launch_bwd_fz_d<bf16_t, float>(dk, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
+    if (bf_gy) return launch_bwd_fz_d<float, bf16_t>(dk, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
+    return launch_bwd_fz_d<float, float>(dk, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
+}
+
 palimpsa_status palimpsa_fwd_frozen(const void *q, const void *k, const void *v,
                                     const void *beta, const void *dt,
                                     const float *A, const float *I_prior, const float *mu0,
@@ -2763,7 +2935,7 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
     a.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
     a.nwg_seg = (int)nwg;
     a.vstar = (flags & PALIMPSA_VSTAR) ? 1 : 0;
-    a.ck = nullptr; a.ck_sink = nullptr; a.nsb = 0;
+    a.ck = nullptr; a.ck_sink = nullptr; a.nsb = 0; a.frozen = 0;
     if (save_ck) {
         if ((long long)B * H * 2 > 0x7fffffffLL) return PALIMPSA_ERR_UNSUPPORTED;
         const BwdWs w = plan_bwd_ws(workspace, B, T, H, dk, dv, ipe);

@@ -292,6 +292,50 @@ palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const 
 size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv, int flags);
 
 /*
+ * Backward of palimpsa_fwd_frozen (training the frozen-importance model that a
+ * Palimpsa layer upgrades, slides frame "The Mamba2 limit enables a gradual
+ * model upgrade").  The exact reverse-mode derivative of
+ *
+ *     mu_t = alpha_t mu_{t-1} + (w_t / I_prior[h]) (x) k_t,   y_t = mu_t q_t,
+ *     w_t = beta_t . v_t (or v*_t when beta is NULL),  alpha_t = exp(-A dt_t),
+ *
+ * for L = sum(gy . y) + sum(gmuT . muT), computed in float32 from the forward's
+ * inputs (it recomputes the states, checkpoints every 8 tokens in the
+ * workspace).  It differentiates the recurrence above, not the bf16 products
+ * of palimpsa_fwd_frozen: it also takes float32 inputs and any dk the exact
+ * backward takes.
+ *
+ * Inputs (device pointers, layouts as palimpsa_fwd_chunked):
+ *   q, k      [B, T, H, dk]  in_dtype
+ *   v, beta   [B, T, H, dv]  in_dtype; beta NULL: v holds the write v*
+ *   dt        [B, T, H]      in_dtype
+ *   A, I_prior [H]           float32 (per-head prior only)
+ *   mu0       [B, H, dv, dk] float32 start mean, or NULL for 0
+ *   gy        [B, T, H, dv]  gy_dtype   dL/dy
+ *   gmuT      [B, H, dv, dk] float32    dL/dmuT, or NULL (zero)
+ * Outputs (float32, overwritten):
+ *   gq, gk    [B, T, H, dk]     gv [B, T, H, dv] (dL/dv*, with beta NULL)
+ *   gbeta     [B, T, H, dv]     required with beta, not written without it
+ *   gdt       [B, T, H]
+ *   gA, gIp   [H]   summed over the batch
+ *   gmu0      [B, H, dv, dk]    dL/dmu0 (at mu0 = 0 when mu0 is NULL), or NULL
+ *   workspace at least palimpsa_bwd_workspace_size(B, T, H, dk, dv, 0) bytes,
+ *             16-byte aligned, caller-owned; contents on entry are ignored
+ *
+ * dk in {32, 64, 128}, dv a multiple of 16 up to 1024 (else
+ * PALIMPSA_ERR_UNSUPPORTED).  Alignment, T = 0, streams and determinism as
+ * palimpsa_bwd.
+ */
+palimpsa_status palimpsa_bwd_frozen(const void *q, const void *k, const void *v, const void *beta,
+                                    const void *dt, const float *A, const float *I_prior, const float *mu0,
+                                    const void *gy, const float *gmuT,
+                                    float *gq, float *gk, float *gv, float *gbeta, float *gdt,
+                                    float *gA, float *gIp, float *gmu0,
+                                    int B, int T, int H, int dk, int dv,
+                                    palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Forward with limited cross-key precision: block-diagonal P (the slides'
  * closing question on limited cross-key correlations).  Each value row runs
  * the full Gaussian update of the slides' backup frame "dropping precision

@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("palimpsa_fwd_chunked", "palimpsa_fwd_workspace_size", "palimpsa_fwd_frozen",
-              "palimpsa_step", "palimpsa_bwd", "palimpsa_bwd_workspace_size", "palimpsa_fwd_blockdiag",
+              "palimpsa_step", "palimpsa_bwd", "palimpsa_bwd_workspace_size", "palimpsa_bwd_frozen",
+              "palimpsa_fwd_blockdiag",
               "palimpsa_status_string", "palimpsa_version"):
         assert n in names
 
@@ -222,6 +223,38 @@ BWD_CASES = [
 @pytest.mark.parametrize("over,status", BWD_CASES)
 def test_bwd_rejects_invalid_calls(lib, over, status):
     assert lib.palimpsa_bwd(*_bwd_args(**over)) == status
+
+
+def _bwd_fz_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dt=FAKE, A=FAKE, Ip=FAKE, mu0=None, gy=FAKE, gmuT=None,
+             gq=FAKE, gk=FAKE, gv=FAKE, gbeta=FAKE, gdt=FAKE, gA=FAKE, gIp=FAKE, gmu0=None,
+             B=2, T=8, H=3, dk=64, dv=64, ind=1, gyd=1, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(over)
+    return [a[n] for n in ("q", "k", "v", "beta", "dt", "A", "Ip", "mu0", "gy", "gmuT",
+                           "gq", "gk", "gv", "gbeta", "gdt", "gA", "gIp", "gmu0",
+                           "B", "T", "H", "dk", "dv", "ind", "gyd", "ws", "wsb", "stream")]
+
+
+# every case fails validation (a NULL beta alone would be a valid call)
+BWD_FZ_CASES = [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(dt=None), 1), (dict(gy=None), 1),
+    (dict(gq=None), 1), (dict(gk=None), 1), (dict(gv=None), 1), (dict(gdt=None), 1),
+    (dict(gbeta=None), 1), (dict(beta=None, gq=None), 1),
+    (dict(gA=None), 1), (dict(gIp=None), 1), (dict(A=None), 1), (dict(Ip=None), 1), (dict(ws=None), 1),
+    (dict(B=0), 1), (dict(T=-1), 1), (dict(H=0), 1), (dict(dk=0), 1), (dict(ind=2), 1), (dict(gyd=5), 1),
+    (dict(wsb=64), 1), (dict(beta=None, gbeta=None, wsb=64), 1), (dict(q=None, T=0, A=None), 1),
+    (dict(dk=48), 2), (dict(dk=16), 2), (dict(dv=1040), 2), (dict(dv=8), 2),
+    (dict(q=FAKE + 4), 3), (dict(beta=FAKE + 8), 3), (dict(gy=FAKE + 8), 3), (dict(gq=FAKE + 4), 3),
+    (dict(gk=FAKE + 8), 3), (dict(mu0=FAKE + 4), 3), (dict(gmuT=FAKE + 4), 3), (dict(gmu0=FAKE + 12), 3),
+    (dict(gdt=FAKE + 2), 3), (dict(dt=FAKE + 1), 3), (dict(gA=FAKE + 1), 3), (dict(gIp=FAKE + 2), 3),
+    (dict(ws=FAKE + 8), 3),
+]
+
+
+@invalid_calls
+@pytest.mark.parametrize("over,status", BWD_FZ_CASES)
+def test_bwd_frozen_rejects_invalid_calls(lib, over, status):
+    assert lib.palimpsa_bwd_frozen(*_bwd_fz_args(**over)) == status
 
 
 def test_bwd_workspace_size_host_logic(lib):

@@ -620,6 +620,115 @@ def test_bwd_is_deterministic_and_ignores_stale_workspace():
 
 
 # ---------------------------------------------------------------------------
+# backward of the frozen-importance (Mamba2-limit) recurrence
+# ---------------------------------------------------------------------------
+
+FZ_BWD_NAMES = ("gq", "gk", "gv", "gbeta", "gdt", "gA", "gIp", "gmu0")
+
+
+def _run_bwd_frozen(inp, gr, mu0=None, vstar=False, workspace=None):
+    g = to_device(inp, DEV)
+    gg = to_device(gr, DEV)
+    out = _pm().bwd_frozen(g["q"], g["k"], g["v"], None if vstar else g["beta"], g["dt"], g["A"],
+                           g["I_prior"], gg["gy"], mu0=None if mu0 is None else mu0.to(DEV),
+                           gmuT=gg.get("gmuT"), workspace=workspace)
+    torch.cuda.synchronize()
+    return out
+
+
+def _bwd_frozen_ref(inp, gr, mu0=None, vstar=False):
+    return oracle.bwd_mamba2_limit(inp["q"], inp["k"], inp["v"], None if vstar else inp["beta"], inp["dt"],
+                                   inp["A"], inp["I_prior"], gr["gy"], mu0=mu0, gmuT=gr.get("gmuT"))
+
+
+def _compare_bwd_frozen(got, ref, vstar):
+    for n in FZ_BWD_NAMES:
+        if n == "gbeta" and vstar:
+            assert got[n] is None and ref[n] is None
+            continue
+        if n in got:
+            assert_close("frozen " + n, got[n], ref[n], TOL_BWD)
+
+
+FZ_BWD_CASES = [
+    # B, T, H, dk, dv, dtype, start state given, final-state gradient, v* input
+    (1, 37, 2, 32, 32, torch.float32, True, True, False),
+    (2, 64, 3, 64, 64, torch.float32, False, False, False),
+    (1, 100, 2, 128, 128, torch.bfloat16, True, True, False),
+    (2, 17, 2, 64, 128, torch.float32, True, False, True),
+    (1, 9, 3, 128, 64, torch.bfloat16, False, True, True),
+    (1, 1, 2, 32, 64, torch.float32, True, True, False),
+    (2, 8, 1, 128, 32, torch.float32, False, True, False),
+    (1, 200, 1, 32, 128, torch.bfloat16, False, False, False),
+    (1, 33, 2, 128, 48, torch.float32, True, True, True),
+]
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,dtype,state,final,vstar", FZ_BWD_CASES)
+def test_bwd_frozen_matches_oracle(B, T, H, dk, dv, dtype, state, final, vstar):
+    w = workloads.WORKLOADS[0].with_(B=B, H=H, dk=dk, dv=dv, dtype=dtype, A_mode="logspace16")
+    _announce("bwd frozen", B=B, T=T, H=H, dk=dk, dv=dv, dtype=dtype, state=state, final=final, vstar=vstar)
+    inp = workloads.make_inputs(w, T=T, seed=T + 2 * dk + dv)
+    mu0 = workloads.random_state(B, H, dv, dk, inp["I_prior"], seed=T + 5)[0] if state else None
+    gr = workloads.upstream_grads(B, T, H, dv, dk, dtype, seed=T + dv, final=final)
+    got = _run_bwd_frozen(inp, gr, mu0=mu0, vstar=vstar)
+    _compare_bwd_frozen(got, _bwd_frozen_ref(inp, gr, mu0=mu0, vstar=vstar), vstar)
+
+
+def test_bwd_frozen_empty_sequence():
+    w = workloads.WORKLOADS[0].with_(B=2, H=3, dk=64, dv=32)
+    _announce("bwd frozen T=0", B=2, H=3, dk=64, dv=32)
+    inp = workloads.make_inputs(w, T=0)
+    mu0 = workloads.random_state(2, 3, 32, 64, inp["I_prior"], seed=6)[0]
+    gr = workloads.upstream_grads(2, 0, 3, 32, 64, torch.float32, seed=6)
+    got = _run_bwd_frozen(inp, gr, mu0=mu0)
+    assert torch.equal(got["gmu0"].cpu(), gr["gmuT"])
+    assert float(got["gA"].abs().max()) == 0.0 and float(got["gIp"].abs().max()) == 0.0
+
+
+def test_bwd_frozen_mqar_workload_full():
+    w = workloads.WORKLOADS[1]
+    _announce("bwd frozen MQAR workload", B=w.B, H=w.H, T=w.T, dk=w.dk, dv=w.dv)
+    inp = workloads.make_inputs(w)
+    gr = workloads.upstream_grads(w.B, w.T, w.H, w.dv, w.dk, w.dtype, seed=8)
+    _compare_bwd_frozen(_run_bwd_frozen(inp, gr), _bwd_frozen_ref(inp, gr), False)
+
+
+def test_bwd_frozen_layer760m_sampled_head():
+    """Full 760M-layer frozen backward; the oracle runs head h of every
+    sequence, so gA[h] and gIp[h] (sums over b) compare exactly."""
+    w = workloads.WORKLOADS[2]
+    h = 5
+    _announce("bwd frozen 760M layer bf16", B=w.B, H=w.H, T=w.T, d=w.dk, sampled_head=h)
+    inp = workloads.make_inputs(w)
+    gr = workloads.upstream_grads(w.B, w.T, w.H, w.dv, w.dk, w.dtype, seed=3)
+    got = _run_bwd_frozen(inp, gr)
+    sub = oracle.select_heads(inp, [(b, h) for b in range(w.B)])
+    gy_s = to_np(gr["gy"])[:, :, h, :].transpose(1, 0, 2)[None]
+    gm_s = to_np(gr["gmuT"])[:, h][None]
+    ref = _bwd_frozen_ref(sub, {"gy": gy_s, "gmuT": gm_s})
+    bs = list(range(w.B))
+    for n in ("gq", "gk", "gv", "gbeta"):
+        assert_close(n + " (head %d)" % h, to_np(got[n])[bs, :, h, :].transpose(1, 0, 2)[None], ref[n], TOL_BWD)
+    assert_close("gdt (head %d)" % h, to_np(got["gdt"])[:, :, h].T[None], ref["gdt"], TOL_BWD)
+    assert_close("gA[h]", to_np(got["gA"])[h:h + 1], ref["gA"].sum(keepdims=True), TOL_BWD)
+    assert_close("gIp[h]", to_np(got["gIp"])[h:h + 1], ref["gIp"].sum(keepdims=True), TOL_BWD)
+    assert_close("gmu0 (head %d)" % h, to_np(got["gmu0"])[:, h][None], ref["gmu0"], TOL_BWD)
+
+
+def test_bwd_frozen_is_deterministic_and_ignores_stale_workspace():
+    w = workloads.WORKLOADS[0].with_(B=2, H=2, dk=64, dv=64)
+    _announce("bwd frozen determinism", B=2, H=2, T=77, dk=64, dv=64)
+    inp = workloads.make_inputs(w, T=77)
+    gr = workloads.upstream_grads(2, 77, 2, 64, 64, torch.float32, seed=9)
+    ws = torch.full((_pm().bwd_workspace_size(2, 77, 2, 64, 64),), 0x7F, dtype=torch.uint8, device=DEV)
+    a = _run_bwd_frozen(inp, gr, workspace=ws)
+    b = _run_bwd_frozen(inp, gr)
+    for n in FZ_BWD_NAMES:
+        assert torch.equal(a[n], b[n]), n
+
+
+# ---------------------------------------------------------------------------
 # training forward: the forward also stores the backward's checkpoints
 # ---------------------------------------------------------------------------
 
