@@ -46,6 +46,12 @@ BWD_FLOPS_PER_UPDATE = 29
 # (33 flops) plus one v_rcp_f32 (2 slots): 11.5 slots and 16.5 flops per entry.
 BD2_SLOTS_PER_ENTRY = 11.5
 BD2_FLOPS_PER_ENTRY = 16.5
+# Backward of the frozen-importance recurrence, per state entry and token:
+# replay of the content update (MUL + FMA, 3 flops) and the reverse step
+# (GM += gy q, gq, gk, gbv, da, GM *= alpha: 3 FMA + 3 MUL, 9 flops):
+# 8 issue slots, 12 flops.
+FZ_BWD_SLOTS_PER_UPDATE = 8
+FZ_BWD_FLOPS_PER_UPDATE = 12
 
 
 def alu_peak_tflops():
@@ -233,6 +239,30 @@ def frozen_extra(torch, pm, w, g, steps):
                          "algorithmic_bytes": hbm}}
 
 
+def frozen_backward_extra(torch, pm, workloads, w, g, steps):
+    """palimpsa_bwd_frozen (backward of the frozen-importance recurrence) on the
+    same workload, timed as one call (checkpoint pass, reverse walk, finishing
+    kernels)."""
+    dev = g["q"].device
+    gr = workloads.upstream_grads(w.B, w.T, w.H, w.dv, w.dk, w.dtype, seed=2)
+    gy, gmuT = gr["gy"].to(dev), gr["gmuT"].to(dev)
+    ws = torch.empty(pm.bwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device=dev)
+    args = (g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], gy)
+    out = pm.bwd_frozen(*args, gmuT=gmuT, workspace=ws)
+    fn = lambda: pm.bwd_frozen(*args, gmuT=gmuT, workspace=ws, out=out)
+    _, per = time_launches(fn, steps, 3, torch)
+    avg_s = sum(per) / len(per) / 1e3
+    updates = w.B * w.H * w.T * w.dv * w.dk
+    peak = LANE_OPS_PER_S / FZ_BWD_SLOTS_PER_UPDATE * FZ_BWD_FLOPS_PER_UPDATE / 1e12
+    achieved = updates * FZ_BWD_FLOPS_PER_UPDATE / avg_s / 1e12
+    return {"workload": w.name + ", frozen-importance backward (gq, gk, gv, gbeta, gdt, gA, gIp, gmu0)",
+            "tokens_per_s": w.B * w.T / avg_s, "ms_per_call": avg_s * 1e3,
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                         "frac": achieved / peak, "traffic": None,
+                         "scope": "whole call (5 kernels)",
+                         "per_update": "replay 2 VALU + reverse 6 VALU = 8 slots, 12 flops"}}
+
+
 def blockdiag_extra(torch, pm, w, g, steps):
     """palimpsa_fwd_blockdiag (2x2 precision blocks along the key axis) on the same workload."""
     y, muT, PT = pm.fwd_blockdiag(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], block=2)
@@ -360,6 +390,7 @@ def main():
         out["backward"] = backward_extra(torch, pm, workloads, w, g, max(5, args.steps // 5))
         out["training_step"] = training_extra(torch, pm, workloads, w, g, max(5, args.steps // 5))
         out["frozen"] = frozen_extra(torch, pm, w, g, max(20, args.steps))
+        out["frozen_backward"] = frozen_backward_extra(torch, pm, workloads, w, g, max(5, args.steps // 5))
         out["blockdiag"] = blockdiag_extra(torch, pm, w, g, max(20, args.steps // 2))
         out["recurrent_shape"] = [fig7_extra(torch, pm, workloads, dev, D, 5) for D in (512, 2048)]
     if not args.no_cpu_baseline:
