@@ -2376,6 +2376,515 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// backward of the frozen-importance recurrence on the matrix cores
+// ---------------------------------------------------------------------------
+//
+// Reverse mode of S_t = a_t S_{t-1} + w_t (x) k_t, y_t = S_t q_t (w_t = beta_t .
+// v_t / I_prior, a_t = e^{l_t}, l_t = -A dt_t), chunked over 64 tokens.  Inside
+// a chunk, with L_t the inclusive prefix sum of l and Lam = L_63, the state and
+// its adjoint G_t = dLoss/dS_t are
+//     S_t = e^{L_t} S_0 + sum_{s<=t} e^{L_t - L_s} w_s k_s^T
+//     G_t = e^{Lam - L_t} G_E + sum_{u>=t} e^{L_u - L_t} gy_u q_u^T
+// where S_0 is the state before the chunk and G_E the adjoint of the state
+// after it.  Each gradient is then one product with a boundary matrix plus one
+// causal, decay-weighted product inside the chunk:
+//     gq_t = e^{L_t} S_0^T gy_t + sum_{s<=t} e^{L_t - L_s} (gy_t . w_s) k_s
+//     gk_s = e^{Lam - L_s} G_E^T w_s + sum_{t>=s} e^{L_t - L_s} (gy_t . w_s) q_t
+//     gw_s = e^{Lam - L_s} G_E k_s + sum_{t>=s} e^{L_t - L_s} (q_t . k_s) gy_t
+// and, since every term's decay exponent is a difference of prefix sums,
+//     dLoss/dl_s = sum_{t>=s in the chunk} (q_t . gq_t - k_t . gk_t) + <G_E, S_end>,
+// which is taken in the equal form without the large cancelling pair
+// <G_E, S_end> - sum k . (G_E part of gk):
+//     dLoss/dl_s = e^{Lam} <G_E, S_0> + sum_{r<s} k_r . gkE_r
+//                  + sum_{t>=s} (q_t . gq_t - k_t . gkI_t)
+// (gkE, gkI: the G_E and the in-chunk parts of gk).
+// The chunk boundaries come from the chunks' own contributions
+//     dS_c = sum_s e^{Lam - L_s} w_s k_s^T,   dG_c = sum_t e^{L_t} gy_t q_t^T
+// by the scans S_0(c+1) = e^{Lam_c} S_0(c) + dS_c and G_E(c-1) = e^{Lam_c} G_E(c) + dG_c.
+// fzb_local_kernel forms dS_c, dG_c (all chunks at once), fzb_scan_kernel runs
+// both scans entry by entry, fzb_grad_kernel forms the gradients of every
+// chunk at once, fzb_head_kernel sums gA and gI_prior over the batch.
+//
+// Products take bf16 operands with fp32 accumulation (as the frozen forward);
+// the boundary matrices are handed from the scan to the gradient kernel in bf16.
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kFbC = 64;                  // tokens per chunk
+
+struct FzbArgs {
+    const bf16_t *q, *k, *v, *beta, *dt;  // beta NULL: v holds the write beta . v
+    const void *gy;
+    const float *A, *Ip, *mu0, *gmuT;
+    float *gq, *gk, *gv, *gbeta, *gdt, *gA, *gIp, *gmu0;
+    // workspace, per (b, h, chunk): dST / S0T [DK][DV], dG / GE [DV][DK], GT [DK][DV]
+    // (bf16), lamc, pA, pI (float), bdot [waves of the scan per head] (float)
+    bf16_t *sT, *ge, *gT;
+    float *lamc, *bdot, *pA, *pI;
+    int B, T, H, nc;
+};
+
+// Fragment of a 16x16x32 MFMA operand whose k index runs along the rows of a
+// row-major LDS array X (row stride rs): lane l gets X[k0 + 8 (l/16) + e][c0 + l%16],
+// e = 0..7, through two LDS transpose loads (within a 16-lane group, lane m
+// receives element m%4 of the 8-byte loads of lanes 4e + m/4).
+__device__ inline bf16x8_t lds_trfrag(const bf16_t *X, int rs, int k0, int c0, int lane) {
+    const int g = lane >> 4, m = lane & 15;
+    const bf16_t *p = X + (k0 + 8 * g + (m >> 2)) * rs + c0 + 4 * (m & 3);
+    typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * rs));
+    return cat8(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi));
+}
+// Fragment whose k index runs along a row: lane l gets X[r0 + l%16][k0 + 8 (l/16) + e].
+__device__ inline bf16x8_t rowfrag(const bf16_t *X, int rs, int r0, int k0, int lane) {
+    return *(const bf16x8_t *)(X + (r0 + (lane & 15)) * rs + k0 + 8 * (lane >> 4));
+}
+__device__ inline f32x4 mfma16(bf16x8_t a, bf16x8_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline uint2 pack4_bf16(f32x4 x) { return make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])); }
+
+// Widen 8 consecutive values of T at p (16-byte aligned for bf16, 32 for float).
+template <typename T> __device__ inline void load8(const T *p, float *o);
+template <> __device__ inline void load8<bf16_t>(const bf16_t *p, float *o) {
+    const u32x4 w = *(const u32x4 *)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o[2 * i] = bf_lo(w[i]); o[2 * i + 1] = bf_hi(w[i]); }
+}
+template <> __device__ inline void load8<float>(const float *p, float *o) {
+    const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o[i] = a[i]; o[4 + i] = b[i]; }
+}
+__device__ inline u32x4 pack8_bf16(const float *x) {
+    return u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
+}
+
+// Inclusive prefix sum L of l_t = -A dt_t over the chunk, lane = token
+// (l = 0 past the end of the sequence); every wave forms it.
+__device__ inline float fzb_lam(const FzbArgs &a, size_t seq, int t0, int lane, float Ah) {
+    const int t = t0 + lane;
+    const float l = t < a.T ? -Ah * (float)a.dt[seq + (size_t)t * a.H] : 0.f;
+    return wave_incl_scan(l, lane);
+}
+
+template <int DK, int DV>
+struct FzbLds {
+    static constexpr int kRK = DK + 16, kRV = DV + 16, kRP = kFbC + 16;   // row strides (bf16)
+    static constexpr int kQ = 0, kK = kQ + kFbC * kRK, kG = kK + kFbC * kRK, kW = kG + kFbC * kRV;
+    static constexpr int kP1 = kW + kFbC * kRV, kP2 = kP1 + kFbC * kRP;
+    static constexpr int kLocalHalves = kP1;              // fzb_local: Q, K, G, W only
+    static constexpr int kGradHalves = kP2 + kFbC * kRP;
+    // fzb_grad also keeps L [64], per-wave token sums (q.gq, k.gkI, k.gkE) and gw.w sums
+    static constexpr int kLocalBytes = kLocalHalves * 2;
+    static constexpr int kGradBytes = kGradHalves * 2 + (kFbC + 3 * 4 * kFbC + 4) * 4;
+};
+
+// Stage the chunk's Q and K (bf16, rows = tokens) and gy and w scaled per
+// token by sg(t) and sw(t) (as bf16); zeros past the end of the sequence.
+template <int DK, int DV, typename TG, typename SG, typename SW>
+__device__ inline void fzb_stage(const FzbArgs &a, bf16_t *hb, size_t seq, int t0, float inv_ip, int tid, SG sg, SW sw) {
+    using L = FzbLds<DK, DV>;
+    constexpr int kPk = DK / 8, kPv = DV / 8;
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    for (int p = tid; p < kFbC * kPk; p += 256) {
+        const int t = p / kPk, col = 8 * (p % kPk);
+        u32x4 qv = z, kv = z;
+        if (t0 + t < a.T) {
+            const size_t o = (seq + (size_t)(t0 + t) * a.H) * DK + col;
+            qv = *(const u32x4 *)(a.q + o);
+            kv = *(const u32x4 *)(a.k + o);
+        }
+        *(u32x4 *)(hb + L::kQ + t * L::kRK + col) = qv;
+        *(u32x4 *)(hb + L::kK + t * L::kRK + col) = kv;
+    }
+    for (int p = tid; p < kFbC * kPv; p += 256) {
+        const int t = p / kPv, col = 8 * (p % kPv);
+        float g[8], w[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { g[e] = 0.f; w[e] = 0.f; }
+        const float fg = sg(t), fw = sw(t) * inv_ip;     // (all lanes: the factors may read other lanes)
+        if (t0 + t < a.T) {
+            const size_t o = (seq + (size_t)(t0 + t) * a.H) * DV + col;
+            load8<TG>((const TG *)a.gy + o, g);
+            load8<bf16_t>(a.v + o, w);
+            if (a.beta) {
+                float bb[8];
+                load8<bf16_t>(a.beta + o, bb);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w[e] *= bb[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { g[e] *= fg; w[e] *= fw; }
+        }
+        *(u32x4 *)(hb + L::kG + t * L::kRV + col) = pack8_bf16(g);
+        *(u32x4 *)(hb + L::kW + t * L::kRV + col) = pack8_bf16(w);
+    }
+}
+
+// One workgroup per (b, h, chunk): the chunk's contributions dS_c (stored
+// transposed, [DK][DV]) and dG_c ([DV][DK]) and its decay Lam_c.
+template <int DK, int DV, typename TG>
+__global__ __launch_bounds__(256) void fzb_local_kernel(FzbArgs a) {
+    using L = FzbLds<DK, DV>;
+    extern __shared__ float lds_f[];
+    bf16_t *hb = (bf16_t *)lds_f;
+    const int bh = blockIdx.x / a.nc, c = blockIdx.x % a.nc;
+    const int b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const size_t seq = (size_t)b * a.T * a.H + h;
+    const int t0 = c * kFbC;
+    const float Ah = a.A[h], inv_ip = 1.f / a.Ip[h];
+    const float Lt = fzb_lam(a, seq, t0, lane, Ah);
+    const float Lam = wave_read(Lt, 63);
+    if (tid == 0) a.lamc[blockIdx.x] = Lam;
+    // gy scaled by e^{L_t}, w by e^{Lam - L_t} (both <= 1)
+    fzb_stage<DK, DV, TG>(a, hb, seq, t0, inv_ip, tid,
+                          [&](int t) { return __expf(__shfl(Lt, t, 64)); },
+                          [&](int t) { return __expf(Lam - __shfl(Lt, t, 64)); });
+    __syncthreads();
+    const size_t cb = (size_t)blockIdx.x;
+    // dS[i][j] = sum_s wd[s][i] k[s][j]: D rows i, columns j; stored as dS^T[j][i..i+3]
+    for (int ib = w; ib < DV / 16; ib += 4) {
+        const bf16x8_t a0 = lds_trfrag(hb + L::kW, L::kRV, 0, 16 * ib, lane);
+        const bf16x8_t a1 = lds_trfrag(hb + L::kW, L::kRV, 32, 16 * ib, lane);
+#pragma unroll 2
+        for (int jb = 0; jb < DK / 16; ++jb) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc = mfma16(a0, lds_trfrag(hb + L::kK, L::kRK, 0, 16 * jb, lane), acc);
+            acc = mfma16(a1, lds_trfrag(hb + L::kK, L::kRK, 32, 16 * jb, lane), acc);
+            const int j = 16 * jb + (lane & 15), i = 16 * ib + 4 * (lane >> 4);
+            *(uint2 *)(a.sT + (cb * DK + j) * DV + i) = pack4_bf16(acc);
+        }
+    }
+    // dG[i][j] = sum_t gd[t][i] q[t][j]: D rows j, columns i; stored as dG[i][j..j+3]
+    for (int jb = w; jb < DK / 16; jb += 4) {
+        const bf16x8_t a0 = lds_trfrag(hb + L::kQ, L::kRK, 0, 16 * jb, lane);
+        const bf16x8_t a1 = lds_trfrag(hb + L::kQ, L::kRK, 32, 16 * jb, lane);
+#pragma unroll 2
+        for (int ib = 0; ib < DV / 16; ++ib) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc = mfma16(a0, lds_trfrag(hb + L::kG, L::kRV, 0, 16 * ib, lane), acc);
+            acc = mfma16(a1, lds_trfrag(hb + L::kG, L::kRV, 32, 16 * ib, lane), acc);
+            const int i = 16 * ib + (lane & 15), j = 16 * jb + 4 * (lane >> 4);
+            *(uint2 *)(a.ge + (cb * DV + i) * DK + j) = pack4_bf16(acc);
+        }
+    }
+}
+
+// Per state entry, 4x4 entries (rows i0.., columns j0..) per thread: the
+// reverse scan of the adjoint over the chunks (G_E(c) written in place of dG_c,
+// and transposed into GT; the adjoint before the first chunk is gmu0), then the
+// forward scan of the state (S_0(c) written transposed in place of dS_c) with
+// each chunk's <G_E(c), S_0(c)>, summed per wave into bdot.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void fzb_scan_kernel(FzbArgs a) {
+    constexpr int kWgPerHead = DV * DK / 4096;     // 256 threads x 16 entries
+    constexpr int kWavesPerHead = 4 * kWgPerHead;
+    const int bh = blockIdx.x / kWgPerHead;
+    const int q = (blockIdx.x % kWgPerHead) * 256 + threadIdx.x;
+    const int i0 = 4 * (q / (DK / 4)), j0 = 4 * (q % (DK / 4));
+    const int lane = threadIdx.x & 63;
+    const int wv = (blockIdx.x % kWgPerHead) * 4 + (threadIdx.x >> 6);
+    const size_t st = (size_t)bh * DV * DK;       // this head's state in [B, H, DV, DK]
+    float g[4][4], s[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const f32x4 x = a.gmuT ? *(const f32x4 *)(a.gmuT + st + (size_t)(i0 + r) * DK + j0) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4) g[r][x4] = x[x4];
+    }
+    for (int c = a.nc - 1; c >= 0; --c) {
+        const size_t cb = (size_t)bh * a.nc + c;
+        bf16_t *gep = a.ge + cb * DV * DK;
+        bf16_t *gtp = a.gT + cb * DK * DV;
+        float d[4][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint2 u = *(const uint2 *)(gep + (size_t)(i0 + r) * DK + j0);
+            d[r][0] = bf_lo(u.x); d[r][1] = bf_hi(u.x); d[r][2] = bf_lo(u.y); d[r][3] = bf_hi(u.y);
+            *(uint2 *)(gep + (size_t)(i0 + r) * DK + j0) =
+                make_uint2(pack_bf16(g[r][0], g[r][1]), pack_bf16(g[r][2], g[r][3]));
+        }
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4)
+            *(uint2 *)(gtp + (size_t)(j0 + x4) * DV + i0) =
+                make_uint2(pack_bf16(g[0][x4], g[1][x4]), pack_bf16(g[2][x4], g[3][x4]));
+        const float e = __expf(a.lamc[cb]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int x4 = 0; x4 < 4; ++x4) g[r][x4] = fmaf(e, g[r][x4], d[r][x4]);
+    }
+    if (a.gmu0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            *(f32x4 *)(a.gmu0 + st + (size_t)(i0 + r) * DK + j0) = f32x4{g[r][0], g[r][1], g[r][2], g[r][3]};
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const f32x4 x = a.mu0 ? *(const f32x4 *)(a.mu0 + st + (size_t)(i0 + r) * DK + j0) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4) s[r][x4] = x[x4];
+    }
+    for (int c = 0; c < a.nc; ++c) {
+        const size_t cb = (size_t)bh * a.nc + c;
+        bf16_t *stp = a.sT + cb * DK * DV;
+        const bf16_t *gep = a.ge + cb * DV * DK;
+        float d[4][4];
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4) {
+            const uint2 u = *(const uint2 *)(stp + (size_t)(j0 + x4) * DV + i0);
+            d[0][x4] = bf_lo(u.x); d[1][x4] = bf_hi(u.x); d[2][x4] = bf_lo(u.y); d[3][x4] = bf_hi(u.y);
+            *(uint2 *)(stp + (size_t)(j0 + x4) * DV + i0) =
+                make_uint2(pack_bf16(s[0][x4], s[1][x4]), pack_bf16(s[2][x4], s[3][x4]));
+        }
+        const float e = __expf(a.lamc[cb]);
+        float dot = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint2 u = *(const uint2 *)(gep + (size_t)(i0 + r) * DK + j0);
+            const float gg[4] = {bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y)};
+#pragma unroll
+            for (int x4 = 0; x4 < 4; ++x4) {
+                dot = fmaf(gg[x4], s[r][x4], dot);
+                s[r][x4] = fmaf(e, s[r][x4], d[r][x4]);
+            }
+        }
+        dot = row16_sum(dot);
+        dot += __shfl_xor(dot, 16, 64);
+        dot += __shfl_xor(dot, 32, 64);
+        if (lane == 0) a.bdot[cb * kWavesPerHead + wv] = dot;
+    }
+}
+
+// One workgroup per (b, h, chunk): the gradients of the chunk's tokens, and
+// the chunk's shares of gA and of sum gw . w (for gI_prior).
+template <int DK, int DV, typename TG>
+__global__ __launch_bounds__(256) void fzb_grad_kernel(FzbArgs a) {
+    using L = FzbLds<DK, DV>;
+    constexpr int kWavesPerHead = DV * DK / 1024;       // fzb_scan_kernel's partial dots per chunk
+    extern __shared__ float lds_f[];
+    bf16_t *hb = (bf16_t *)lds_f;
+    float *lamv = (float *)(hb + L::kGradHalves);       // L_t
+    float *rq = lamv + kFbC;                             // [wave][token] sums of q . gq
+    float *rk = rq + 4 * kFbC;                           // [wave][token] sums of k . gkI
+    float *re = rk + 4 * kFbC;                           // [wave][token] sums of k . gkE
+    float *ri = re + 4 * kFbC;                           // [wave] sums of gw . w
+    const int bh = blockIdx.x / a.nc, c = blockIdx.x % a.nc;
+    const int b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const size_t seq = (size_t)b * a.T * a.H + h;
+    const int t0 = c * kFbC;
+    const float Ah = a.A[h], inv_ip = 1.f / a.Ip[h];
+    const float Lt = fzb_lam(a, seq, t0, lane, Ah);
+    const float Lam = wave_read(Lt, 63);
+    if (w == 0) lamv[lane] = Lt;
+    fzb_stage<DK, DV, TG>(a, hb, seq, t0, inv_ip, tid, [](int) { return 1.f; }, [](int) { return 1.f; });
+    __syncthreads();
+
+    // decay-masked scores, bf16 in LDS as [t][s]:
+    //   P2[t][s] = e^{L_t - L_s} q_t . k_s,  P1[t][s] = e^{L_t - L_s} gy_t . w_s  (s <= t; 0 above)
+    for (int n = w; n < 32; n += 4) {
+        const int mat = n >> 4, tb = (n >> 2) & 3, sb = n & 3;
+        bf16_t *P = hb + (mat ? L::kP1 : L::kP2);
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (sb <= tb) {
+            if (mat == 0) {
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk)
+                    acc = mfma16(rowfrag(hb + L::kQ, L::kRK, 16 * tb, 32 * kk, lane),
+                                 rowfrag(hb + L::kK, L::kRK, 16 * sb, 32 * kk, lane), acc);
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < DV / 32; ++kk)
+                    acc = mfma16(rowfrag(hb + L::kG, L::kRV, 16 * tb, 32 * kk, lane),
+                                 rowfrag(hb + L::kW, L::kRV, 16 * sb, 32 * kk, lane), acc);
+            }
+            const int s = 16 * sb + m;
+            const float ls = lamv[s];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * tb + 4 * g + r;
+                acc[r] = s <= t ? acc[r] * __expf(lamv[t] - ls) : 0.f;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) P[(16 * tb + 4 * g + r) * L::kRP + 16 * sb + m] = (bf16_t)acc[r];
+    }
+    __syncthreads();
+
+    // The lane's token in column block xb is 16 xb + m.
+    float eL[4], eR[4], pq[4], pk[4], pe[4];
+#pragma unroll
+    for (int xb = 0; xb < 4; ++xb) {
+        const float lx = lamv[16 * xb + m];
+        eL[xb] = __expf(lx);
+        eR[xb] = __expf(Lam - lx);
+        pq[xb] = 0.f;
+        pk[xb] = 0.f;
+        pe[xb] = 0.f;
+    }
+    float pw = 0.f;
+    const size_t cb = (size_t)blockIdx.x;
+    const bf16_t *s0t = a.sT + cb * DK * DV, *gtp = a.gT + cb * DK * DV, *gep = a.ge + cb * DV * DK;
+    for (int jb = w; jb < DK / 16; jb += 4) {
+        const int j = 16 * jb + 4 * g;                   // the lane's 4 key channels j..j+3
+        // gq^T[j][t] = e^{L_t} sum_i S_0^T[j][i] gy[t][i] + sum_s k[s][j] P1[t][s]
+        {
+            bf16x8_t af[DV / 32];
+#pragma unroll
+            for (int ki = 0; ki < DV / 32; ++ki) af[ki] = rowfrag(s0t, DV, 16 * jb, 32 * ki, lane);
+            const bf16x8_t k0 = lds_trfrag(hb + L::kK, L::kRK, 0, 16 * jb, lane);
+            const bf16x8_t k1 = lds_trfrag(hb + L::kK, L::kRK, 32, 16 * jb, lane);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ki = 0; ki < DV / 32; ++ki)
+                    acc = mfma16(af[ki], rowfrag(hb + L::kG, L::kRV, 16 * tb, 32 * ki, lane), acc);
+                acc *= eL[tb];
+                acc = mfma16(k0, rowfrag(hb + L::kP1, L::kRP, 16 * tb, 0, lane), acc);
+                if (tb >= 2) acc = mfma16(k1, rowfrag(hb + L::kP1, L::kRP, 16 * tb, 32, lane), acc);
+                const int t = 16 * tb + m;
+                const uint2 qq = *(const uint2 *)(hb + L::kQ + t * L::kRK + j);
+                pq[tb] += (acc[0] * bf_lo(qq.x) + acc[1] * bf_hi(qq.x)) + (acc[2] * bf_lo(qq.y) + acc[3] * bf_hi(qq.y));
+                if (t0 + t < a.T) *(f32x4 *)(a.gq + (seq + (size_t)(t0 + t) * a.H) * DK + j) = acc;
+            }
+        }
+        // gk^T[j][s] = e^{Lam - L_s} sum_i G_E^T[j][i] w[s][i] + sum_t q[t][j] P1[t][s]
+        {
+            bf16x8_t af[DV / 32];
+#pragma unroll
+            for (int ki = 0; ki < DV / 32; ++ki) af[ki] = rowfrag(gtp, DV, 16 * jb, 32 * ki, lane);
+            const bf16x8_t q0 = lds_trfrag(hb + L::kQ, L::kRK, 0, 16 * jb, lane);
+            const bf16x8_t q1 = lds_trfrag(hb + L::kQ, L::kRK, 32, 16 * jb, lane);
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, aci = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ki = 0; ki < DV / 32; ++ki)
+                    acc = mfma16(af[ki], rowfrag(hb + L::kW, L::kRV, 16 * sb, 32 * ki, lane), acc);
+                acc *= eR[sb];
+                if (sb < 2) aci = mfma16(q0, lds_trfrag(hb + L::kP1, L::kRP, 0, 16 * sb, lane), aci);
+                aci = mfma16(q1, lds_trfrag(hb + L::kP1, L::kRP, 32, 16 * sb, lane), aci);
+                const int s = 16 * sb + m;
+                const uint2 kk = *(const uint2 *)(hb + L::kK + s * L::kRK + j);
+                const float k4[4] = {bf_lo(kk.x), bf_hi(kk.x), bf_lo(kk.y), bf_hi(kk.y)};
+                pe[sb] += (acc[0] * k4[0] + acc[1] * k4[1]) + (acc[2] * k4[2] + acc[3] * k4[3]);
+                pk[sb] += (aci[0] * k4[0] + aci[1] * k4[1]) + (aci[2] * k4[2] + aci[3] * k4[3]);
+                acc += aci;
+                if (t0 + s < a.T) *(f32x4 *)(a.gk + (seq + (size_t)(t0 + s) * a.H) * DK + j) = acc;
+            }
+        }
+    }
+    // gw^T[i][s] = e^{Lam - L_s} sum_j G_E[i][j] k[s][j] + sum_t gy[t][i] P2[t][s];
+    // gv = gw beta / I_prior (v* input: gw / I_prior), gbeta = gw v / I_prior
+    for (int ib = w; ib < DV / 16; ib += 4) {
+        const int i = 16 * ib + 4 * g;                   // the lane's 4 value rows i..i+3
+        bf16x8_t af[DK / 32];
+#pragma unroll
+        for (int kj = 0; kj < DK / 32; ++kj) af[kj] = rowfrag(gep, DK, 16 * ib, 32 * kj, lane);
+        const bf16x8_t g0 = lds_trfrag(hb + L::kG, L::kRV, 0, 16 * ib, lane);
+        const bf16x8_t g1 = lds_trfrag(hb + L::kG, L::kRV, 32, 16 * ib, lane);
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kj = 0; kj < DK / 32; ++kj)
+                acc = mfma16(af[kj], rowfrag(hb + L::kK, L::kRK, 16 * sb, 32 * kj, lane), acc);
+            acc *= eR[sb];
+            if (sb < 2) acc = mfma16(g0, lds_trfrag(hb + L::kP2, L::kRP, 0, 16 * sb, lane), acc);
+            acc = mfma16(g1, lds_trfrag(hb + L::kP2, L::kRP, 32, 16 * sb, lane), acc);
+            const int s = 16 * sb + m;
+            const uint2 ww = *(const uint2 *)(hb + L::kW + s * L::kRV + i);
+            pw += (acc[0] * bf_lo(ww.x) + acc[1] * bf_hi(ww.x)) + (acc[2] * bf_lo(ww.y) + acc[3] * bf_hi(ww.y));
+            if (t0 + s < a.T) {
+                const size_t o = (seq + (size_t)(t0 + s) * a.H) * DV + i;
+                const uint2 vv = *(const uint2 *)(a.v + o);
+                const float vf[4] = {bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y)};
+                if (a.beta) {
+                    const uint2 bb = *(const uint2 *)(a.beta + o);
+                    const float bf[4] = {bf_lo(bb.x), bf_hi(bb.x), bf_lo(bb.y), bf_hi(bb.y)};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float gwi = acc[r] * inv_ip;
+                        a.gv[o + r] = gwi * bf[r];
+                        a.gbeta[o + r] = gwi * vf[r];
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) a.gv[o + r] = acc[r] * inv_ip;
+                }
+            }
+        }
+    }
+    // token sums: the 4 lane groups hold the same tokens
+#pragma unroll
+    for (int xb = 0; xb < 4; ++xb) {
+        pq[xb] += __shfl_xor(pq[xb], 16, 64);
+        pq[xb] += __shfl_xor(pq[xb], 32, 64);
+        pk[xb] += __shfl_xor(pk[xb], 16, 64);
+        pk[xb] += __shfl_xor(pk[xb], 32, 64);
+        pe[xb] += __shfl_xor(pe[xb], 16, 64);
+        pe[xb] += __shfl_xor(pe[xb], 32, 64);
+        if (g == 0) {
+            rq[w * kFbC + 16 * xb + m] = pq[xb];
+            rk[w * kFbC + 16 * xb + m] = pk[xb];
+            re[w * kFbC + 16 * xb + m] = pe[xb];
+        }
+    }
+    pw = row16_sum(pw);
+    pw += __shfl_xor(pw, 16, 64);
+    pw += __shfl_xor(pw, 32, 64);
+    if (lane == 0) ri[w] = pw;
+    __syncthreads();
+    if (w == 0) {
+        // dLoss/dl_t = e^{Lam} <G_E, S_0> + sum_{r<t} k_r . gkE_r + sum_{u>=t} (q_u . gq_u - k_u . gkI_u);
+        // lane = token
+        const float p = ((rq[lane] + rq[kFbC + lane]) + (rq[2 * kFbC + lane] + rq[3 * kFbC + lane])) -
+                        ((rk[lane] + rk[kFbC + lane]) + (rk[2 * kFbC + lane] + rk[3 * kFbC + lane]));
+        const float pe0 = (re[lane] + re[kFbC + lane]) + (re[2 * kFbC + lane] + re[3 * kFbC + lane]);
+        const float rev = wave_incl_scan(__shfl(p, 63 - lane, 64), lane);   // lane j: sum_{u >= 63 - j} p_u
+        const float pre = wave_incl_scan(pe0, lane) - pe0;                    // sum_{r < lane} pe0_r
+        float bsum = 0.f;
+#pragma unroll
+        for (int x = 0; x < kWavesPerHead; ++x) bsum += a.bdot[cb * kWavesPerHead + x];
+        const float dl = __shfl(rev, 63 - lane, 64) + pre + __expf(Lam) * bsum;
+        float ga = 0.f;
+        if (t0 + lane < a.T) {
+            const size_t o = seq + (size_t)(t0 + lane) * a.H;
+            a.gdt[o] = -Ah * dl;
+            ga = -(float)a.dt[o] * dl;
+        }
+        ga = row16_sum(ga);
+        ga += __shfl_xor(ga, 16, 64);
+        ga += __shfl_xor(ga, 32, 64);
+        if (lane == 0) {
+            a.pA[cb] = ga;
+            a.pI[cb] = (ri[0] + ri[1]) + (ri[2] + ri[3]);
+        }
+    }
+}
+
+// gA[h] and gI_prior[h] = -(1 / I_prior) sum gw . w, summed over the batch and the chunks.
+__global__ __launch_bounds__(64) void fzb_head_kernel(const float *pA, const float *pI, const float *Ip, float *gA,
+                                                      float *gIp, int B, int H, int nc) {
+    const int h = blockIdx.x * 64 + threadIdx.x;
+    if (h >= H) return;
+    float sa = 0.f, si = 0.f;
+    for (int b = 0; b < B; ++b)
+        for (int c = 0; c < nc; ++c) {
+            sa += pA[((size_t)b * H + h) * nc + c];
+            si += pI[((size_t)b * H + h) * nc + c];
+        }
+    gA[h] = sa;
+    gIp[h] = -si / Ip[h];
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 
@@ -2635,6 +3144,63 @@ palimpsa_status launch_bwd_fz_d(int dk, const FwdArgs &fa, const BwdArgs &ba, co
     }
 }
 
+// Workspace of the matrix-core frozen backward (per (b, h, chunk), 256-byte
+// aligned sections): S_0^T and G_E^T [DK][DV] and G_E [DV][DK] in bf16, and the
+// chunk's Lam, partial dots, gA and gw . w sums in float.  It is never larger
+// than plan_bwd_ws for the same sizes (checked by the caller).
+struct FzbWs {
+    bf16_t *sT, *ge, *gT;
+    float *lamc, *bdot, *pA, *pI;
+    size_t bytes;
+};
+FzbWs plan_fzb_ws(void *base, int B, int T, int H, int dk, int dv) {
+    const size_t nc = (size_t)(T + kFbC - 1) / kFbC, bhc = (size_t)B * H * nc, e = (size_t)dv * dk;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = (off + bytes + 255) / 256 * 256;
+        return o;
+    };
+    const size_t o_s = take(bhc * e * 2), o_g = take(bhc * e * 2), o_t = take(bhc * e * 2);
+    const size_t o_l = take(bhc * 4), o_d = take(bhc * (e / 1024) * 4), o_a = take(bhc * 4), o_i = take(bhc * 4);
+    char *c = (char *)base;
+    FzbWs w;
+    w.sT = (bf16_t *)(c + o_s); w.ge = (bf16_t *)(c + o_g); w.gT = (bf16_t *)(c + o_t);
+    w.lamc = (float *)(c + o_l); w.bdot = (float *)(c + o_d); w.pA = (float *)(c + o_a); w.pI = (float *)(c + o_i);
+    w.bytes = off;
+    return w;
+}
+
+template <int DK, int DV, typename TG>
+palimpsa_status launch_fzb(const FzbArgs &a, hipStream_t s) {
+    using L = FzbLds<DK, DV>;
+    static_assert(L::kGradBytes <= 160 * 1024, "frozen backward staging exceeds the CU's LDS");
+    const size_t bhc = (size_t)a.B * a.H * a.nc;
+    (void)hipGetLastError();
+    if (bhc > 0) {
+        auto k1 = fzb_local_kernel<DK, DV, TG>;
+        if (hipFuncSetAttribute((const void *)k1, hipFuncAttributeMaxDynamicSharedMemorySize, L::kLocalBytes) != hipSuccess)
+            return PALIMPSA_ERR_HIP;
+        hipLaunchKernelGGL(k1, dim3((unsigned)bhc), dim3(256), L::kLocalBytes, s, a);
+    }
+    hipLaunchKernelGGL((fzb_scan_kernel<DK, DV>), dim3((unsigned)((size_t)a.B * a.H * (DV * DK / 4096))), dim3(256), 0, s, a);
+    if (bhc > 0) {
+        auto k3 = fzb_grad_kernel<DK, DV, TG>;
+        if (hipFuncSetAttribute((const void *)k3, hipFuncAttributeMaxDynamicSharedMemorySize, L::kGradBytes) != hipSuccess)
+            return PALIMPSA_ERR_HIP;
+        hipLaunchKernelGGL(k3, dim3((unsigned)bhc), dim3(256), L::kGradBytes, s, a);
+    }
+    hipLaunchKernelGGL(fzb_head_kernel, dim3((a.H + 63) / 64), dim3(64), 0, s, (const float *)a.pA, (const float *)a.pI,
+                       a.Ip, a.gA, a.gIp, a.B, a.H, a.nc);
+    return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
+}
+
+template <typename TG>
+palimpsa_status launch_fzb_d(int dk, int dv, const FzbArgs &a, hipStream_t s) {
+    if (dk == 64) return dv == 64 ? launch_fzb<64, 64, TG>(a, s) : launch_fzb<64, 128, TG>(a, s);
+    return dv == 64 ? launch_fzb<128, 64, TG>(a, s) : launch_fzb<128, 128, TG>(a, s);
+}
+
 template <typename TIn, typename TG>
 palimpsa_status launch_bwd_d(int dk, bool ipe, const FwdArgs &fa, const BwdArgs &ba, const BwdWs &w, float *gq,
                              float *gk, float *gdt, float *gA, float *gIp, int dt_bf16, hipStream_t s) {
@@ -2806,6 +3372,22 @@ palimpsa_status palimpsa_bwd_frozen(const void *q, const void *k, const void *v,
         return PALIMPSA_ERR_UNSUPPORTED;
     const BwdWs w = plan_bwd_ws(workspace, B, T, H, dk, dv, false);
     if (workspace_bytes < w.bytes) return PALIMPSA_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    if (in_dtype == PALIMPSA_BF16 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128)) {
+        // chunked form on the matrix cores
+        const FzbWs fw = plan_fzb_ws(workspace, B, T, H, dk, dv);
+        if (fw.bytes > w.bytes) return PALIMPSA_ERR_INVALID_ARG;
+        FzbArgs fa;
+        fa.q = (const bf16_t *)q; fa.k = (const bf16_t *)k; fa.v = (const bf16_t *)v;
+        fa.beta = (const bf16_t *)beta; fa.dt = (const bf16_t *)dt; fa.gy = gy;
+        fa.A = A; fa.Ip = I_prior; fa.mu0 = mu0; fa.gmuT = gmuT;
+        fa.gq = gq; fa.gk = gk; fa.gv = gv; fa.gbeta = beta ? gbeta : nullptr; fa.gdt = gdt;
+        fa.gA = gA; fa.gIp = gIp; fa.gmu0 = gmu0;
+        fa.sT = fw.sT; fa.ge = fw.ge; fa.gT = fw.gT;
+        fa.lamc = fw.lamc; fa.bdot = fw.bdot; fa.pA = fw.pA; fa.pI = fw.pI;
+        fa.B = B; fa.T = T; fa.H = H; fa.nc = (T + kFbC - 1) / kFbC;
+        return gy_dtype == PALIMPSA_BF16 ? launch_fzb_d<bf16_t>(dk, dv, fa, s) : launch_fzb_d<float>(dk, dv, fa, s);
+    }
     // without beta the v tensor is the write itself; the beta pointer is then
     // pointed at v so that every staged load stays valid (the frozen walk
     // never reads it)
@@ -2830,7 +3412,6 @@ palimpsa_status palimpsa_bwd_frozen(const void *q, const void *k, const void *v,
     ba.B = B; ba.T = T; ba.H = H; ba.dv = dv; ba.nsb = fa.nsb;
     ba.nwg = (int)nwg; ba.xcd_remap = fa.xcd_remap;
 
-    hipStream_t s = (hipStream_t)stream;
     const bool bf_in = in_dtype == PALIMPSA_BF16, bf_gy = gy_dtype == PALIMPSA_BF16;
     const int dtb = bf_in ? 1 : 0;
     if (bf_in && bf_gy) return launch_bwd_fz_d<bf16_t, bf16_t>(dk, fa, ba, w, gq, gk, gdt, gA, gIp, dtb, s);
