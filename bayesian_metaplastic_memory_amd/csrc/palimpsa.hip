@@ -2418,10 +2418,11 @@ struct FzbArgs {
     const float *A, *Ip, *mu0, *gmuT;
     float *gq, *gk, *gv, *gbeta, *gdt, *gA, *gIp, *gmu0;
     // workspace, per (b, h, chunk): dST / S0T [DK][DV], dG / GE [DV][DK], GT [DK][DV]
-    // (bf16), lamc, pA, pI (float), bdot [waves of the scan per head] (float)
+    // (bf16), lamc, pA, pI (float)
     bf16_t *sT, *ge, *gT;
-    float *lamc, *bdot, *pA, *pI;
+    float *lamc, *pA, *pI;
     int B, T, H, nc;
+    int vec_g;                            // gv and gbeta 16-byte aligned: vector stores
 };
 
 // Fragment of a 16x16x32 MFMA operand whose k index runs along the rows of a
@@ -2478,7 +2479,7 @@ struct FzbLds {
     static constexpr int kGradHalves = kP2 + kFbC * kRP;
     // fzb_grad also keeps L [64], per-wave token sums (q.gq, k.gkI, k.gkE) and gw.w sums
     static constexpr int kLocalBytes = kLocalHalves * 2;
-    static constexpr int kGradBytes = kGradHalves * 2 + (kFbC + 3 * 4 * kFbC + 4) * 4;
+    static constexpr int kGradBytes = kGradHalves * 2 + (kFbC + 3 * 4 * kFbC + 8) * 4;
 };
 
 // Stage the chunk's Q and K (bf16, rows = tokens) and gy and w scaled per
@@ -2487,36 +2488,62 @@ template <int DK, int DV, typename TG, typename SG, typename SW>
 __device__ inline void fzb_stage(const FzbArgs &a, bf16_t *hb, size_t seq, int t0, float inv_ip, int tid, SG sg, SW sw) {
     using L = FzbLds<DK, DV>;
     constexpr int kPk = DK / 8, kPv = DV / 8;
+    constexpr int NQ = kFbC * kPk / 256, NV = kFbC * kPv / 256;   // packets per thread
+    constexpr int kGP = sizeof(TG) / 2;                             // 16-byte packets per 8 values of gy
     const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-    for (int p = tid; p < kFbC * kPk; p += 256) {
-        const int t = p / kPk, col = 8 * (p % kPk);
-        u32x4 qv = z, kv = z;
-        if (t0 + t < a.T) {
-            const size_t o = (seq + (size_t)(t0 + t) * a.H) * DK + col;
-            qv = *(const u32x4 *)(a.q + o);
-            kv = *(const u32x4 *)(a.k + o);
-        }
-        *(u32x4 *)(hb + L::kQ + t * L::kRK + col) = qv;
-        *(u32x4 *)(hb + L::kK + t * L::kRK + col) = kv;
+    // every load first (rows past the end clamped to the last token, zeroed below),
+    // so that they are all in flight together
+    const int tl = a.T - 1;
+    u32x4 qv[NQ], kv[NQ], vv[NV], bv[NV], gv[NV][kGP];
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+        const int p = tid + 256 * n, t = p / kPk, col = 8 * (p % kPk);
+        const size_t o = (seq + (size_t)min(t0 + t, tl) * a.H) * DK + col;
+        qv[n] = *(const u32x4 *)(a.q + o);
+        kv[n] = *(const u32x4 *)(a.k + o);
     }
-    for (int p = tid; p < kFbC * kPv; p += 256) {
-        const int t = p / kPv, col = 8 * (p % kPv);
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+        const int p = tid + 256 * n, t = p / kPv, col = 8 * (p % kPv);
+        const size_t o = (seq + (size_t)min(t0 + t, tl) * a.H) * DV + col;
+        vv[n] = *(const u32x4 *)(a.v + o);
+        bv[n] = a.beta ? *(const u32x4 *)(a.beta + o) : z;
+#pragma unroll
+        for (int x = 0; x < kGP; ++x) gv[n][x] = *(const u32x4 *)((const TG *)a.gy + o + 4 * x);
+    }
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+        const int p = tid + 256 * n, t = p / kPk, col = 8 * (p % kPk);
+        const bool ok = t0 + t < a.T;
+        *(u32x4 *)(hb + L::kQ + t * L::kRK + col) = ok ? qv[n] : z;
+        *(u32x4 *)(hb + L::kK + t * L::kRK + col) = ok ? kv[n] : z;
+    }
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+        const int p = tid + 256 * n, t = p / kPv, col = 8 * (p % kPv);
+        const bool ok = t0 + t < a.T;
+        const float fg = sg(t), fw = sw(t) * inv_ip;     // (every lane calls sg, sw: they may read other lanes)
         float g[8], w[8];
+        if (kGP == 1) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { g[e] = 0.f; w[e] = 0.f; }
-        const float fg = sg(t), fw = sw(t) * inv_ip;     // (all lanes: the factors may read other lanes)
-        if (t0 + t < a.T) {
-            const size_t o = (seq + (size_t)(t0 + t) * a.H) * DV + col;
-            load8<TG>((const TG *)a.gy + o, g);
-            load8<bf16_t>(a.v + o, w);
+            for (int i = 0; i < 4; ++i) { g[2 * i] = bf_lo(gv[n][0][i]); g[2 * i + 1] = bf_hi(gv[n][0][i]); }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) g[i] = __uint_as_float(gv[n][i / 4 % kGP][i % 4]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w[2 * i] = bf_lo(vv[n][i]);
+            w[2 * i + 1] = bf_hi(vv[n][i]);
             if (a.beta) {
-                float bb[8];
-                load8<bf16_t>(a.beta + o, bb);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) w[e] *= bb[e];
+                w[2 * i] *= bf_lo(bv[n][i]);
+                w[2 * i + 1] *= bf_hi(bv[n][i]);
             }
+        }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { g[e] *= fg; w[e] *= fw; }
+        for (int i = 0; i < 8; ++i) {
+            g[i] = ok ? g[i] * fg : 0.f;
+            w[i] = ok ? w[i] * fw : 0.f;
         }
         *(u32x4 *)(hb + L::kG + t * L::kRV + col) = pack8_bf16(g);
         *(u32x4 *)(hb + L::kW + t * L::kRV + col) = pack8_bf16(w);
@@ -2573,89 +2600,139 @@ __global__ __launch_bounds__(256) void fzb_local_kernel(FzbArgs a) {
     }
 }
 
-// Per state entry, 4x4 entries (rows i0.., columns j0..) per thread: the
-// reverse scan of the adjoint over the chunks (G_E(c) written in place of dG_c,
-// and transposed into GT; the adjoint before the first chunk is gmu0), then the
-// forward scan of the state (S_0(c) written transposed in place of dS_c) with
-// each chunk's <G_E(c), S_0(c)>, summed per wave into bdot.
+// The scans over the chunks, entry by entry.  A workgroup owns a 64 x 64 tile
+// of one head's state (value rows i_blk.., key channels j_blk..; 16 entries per
+// thread), so that each thread moves 32 contiguous bytes and each row of the
+// tile is 128 contiguous bytes in both the row-major and the transposed arrays.
+// The adjoint runs in reverse with each thread on 16 consecutive key channels
+// of one row: G_E(c) is written in place of dG_c and, through LDS, transposed
+// into GT; the adjoint before the first chunk is gmu0.  The state runs forward
+// with each thread on 16 consecutive rows of one key channel, so that dS_c^T is
+// read and S_0(c)^T written in place directly.  Loads run kFbPre chunks ahead
+// of the arithmetic (a ring of registers indexed at compile time).
+constexpr int kFbPre = 4;
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void fzb_scan_kernel(FzbArgs a) {
-    constexpr int kWgPerHead = DV * DK / 4096;     // 256 threads x 16 entries
-    constexpr int kWavesPerHead = 4 * kWgPerHead;
-    const int bh = blockIdx.x / kWgPerHead;
-    const int q = (blockIdx.x % kWgPerHead) * 256 + threadIdx.x;
-    const int i0 = 4 * (q / (DK / 4)), j0 = 4 * (q % (DK / 4));
-    const int lane = threadIdx.x & 63;
-    const int wv = (blockIdx.x % kWgPerHead) * 4 + (threadIdx.x >> 6);
-    const size_t st = (size_t)bh * DV * DK;       // this head's state in [B, H, DV, DK]
-    float g[4][4], s[4][4];
+    constexpr int kTiles = (DV / 64) * (DK / 64);
+    constexpr int kTS = 64 + 8, kFS = 64 + 4;          // LDS transpose tile: [64][kTS] bf16 or [64][kFS] fp32
+    __shared__ float tile_f[64 * kFS];
+    bf16_t *tile = (bf16_t *)tile_f;
+    const int bh = blockIdx.x / kTiles, tix = blockIdx.x % kTiles;
+    const int i_blk = 64 * (tix / (DK / 64)), j_blk = 64 * (tix % (DK / 64));
+    const int tid = threadIdx.x;
+    const int ra = tid >> 2, cb16 = 16 * (tid & 3);     // row ra of the tile, entries cb16..cb16+15
+    const size_t st = (size_t)bh * DV * DK;             // this head's state in [B, H, DV, DK]
+    const size_t rm = (size_t)(i_blk + ra) * DK + j_blk + cb16;   // row-major: row i, key channels
+    const size_t tm = (size_t)(j_blk + ra) * DV + i_blk + cb16;   // transposed: key channel j, rows
+    const size_t e = (size_t)DV * DK;
+    const size_t cb0 = (size_t)bh * a.nc;
+    const int nc = a.nc;
+    auto load16f = [](const float *p, float *x) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const f32x4 x = a.gmuT ? *(const f32x4 *)(a.gmuT + st + (size_t)(i0 + r) * DK + j0) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int x4 = 0; x4 < 4; ++x4) g[r][x4] = x[x4];
-    }
-    for (int c = a.nc - 1; c >= 0; --c) {
-        const size_t cb = (size_t)bh * a.nc + c;
-        bf16_t *gep = a.ge + cb * DV * DK;
-        bf16_t *gtp = a.gT + cb * DK * DV;
-        float d[4][4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint2 u = *(const uint2 *)(gep + (size_t)(i0 + r) * DK + j0);
-            d[r][0] = bf_lo(u.x); d[r][1] = bf_hi(u.x); d[r][2] = bf_lo(u.y); d[r][3] = bf_hi(u.y);
-            *(uint2 *)(gep + (size_t)(i0 + r) * DK + j0) =
-                make_uint2(pack_bf16(g[r][0], g[r][1]), pack_bf16(g[r][2], g[r][3]));
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 u = *(const f32x4 *)(p + 4 * q);
+            x[4 * q] = u[0]; x[4 * q + 1] = u[1]; x[4 * q + 2] = u[2]; x[4 * q + 3] = u[3];
         }
+    };
+    auto ld2 = [](const bf16_t *p, u32x4 *r) __attribute__((always_inline)) {
+        r[0] = *(const u32x4 *)p;
+        r[1] = *(const u32x4 *)(p + 8);
+    };
+    auto st2 = [](bf16_t *p, const float *x) __attribute__((always_inline)) {
+        *(u32x4 *)p = pack8_bf16(x);
+        *(u32x4 *)(p + 8) = pack8_bf16(x + 8);
+    };
+    auto axpy = [](float *x, float ex, const u32x4 *d) __attribute__((always_inline)) {
 #pragma unroll
-        for (int x4 = 0; x4 < 4; ++x4)
-            *(uint2 *)(gtp + (size_t)(j0 + x4) * DV + i0) =
-                make_uint2(pack_bf16(g[0][x4], g[1][x4]), pack_bf16(g[2][x4], g[3][x4]));
-        const float e = __expf(a.lamc[cb]);
+        for (int n = 0; n < 8; ++n) {
+            x[2 * n] = fmaf(ex, x[2 * n], bf_lo(d[n / 4][n % 4]));
+            x[2 * n + 1] = fmaf(ex, x[2 * n + 1], bf_hi(d[n / 4][n % 4]));
+        }
+    };
+    float g[16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+    for (int n = 0; n < 16; ++n) g[n] = 0.f;
+    if (a.gmuT) load16f(a.gmuT + st + rm, g);
+    u32x4 ring[kFbPre][2];
+    float lring[kFbPre];
 #pragma unroll
-            for (int x4 = 0; x4 < 4; ++x4) g[r][x4] = fmaf(e, g[r][x4], d[r][x4]);
+    for (int u = 0; u < kFbPre; ++u) {
+        ring[u][0] = ring[u][1] = u32x4{0u, 0u, 0u, 0u};
+        lring[u] = 0.f;
+        const int c = nc - 1 - u;
+        if (c >= 0) {
+            ld2(a.ge + (cb0 + c) * e + rm, ring[u]);
+            lring[u] = a.lamc[cb0 + c];
+        }
+    }
+    for (int c0 = nc - 1; c0 >= 0; c0 -= kFbPre) {
+#pragma unroll
+        for (int u = 0; u < kFbPre; ++u) {
+            const int c = c0 - u;
+            if (c >= 0) {
+                const u32x4 d[2] = {ring[u][0], ring[u][1]};
+                const float ex = __expf(lring[u]);
+                if (c - kFbPre >= 0) {
+                    ld2(a.ge + (cb0 + c - kFbPre) * e + rm, ring[u]);
+                    lring[u] = a.lamc[cb0 + c - kFbPre];
+                }
+                st2(a.ge + (cb0 + c) * e + rm, g);
+                // transpose through LDS: tile[j - j_blk][i - i_blk]
+#pragma unroll
+                for (int n = 0; n < 16; ++n) tile[(cb16 + n) * kTS + ra] = (bf16_t)g[n];
+                __syncthreads();
+                {
+                    bf16_t *gtp = a.gT + (cb0 + c) * e + tm;
+                    *(u32x4 *)gtp = *(const u32x4 *)(tile + ra * kTS + cb16);
+                    *(u32x4 *)(gtp + 8) = *(const u32x4 *)(tile + ra * kTS + cb16 + 8);
+                }
+                __syncthreads();
+                axpy(g, ex, d);
+            }
+        }
     }
     if (a.gmu0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            *(f32x4 *)(a.gmu0 + st + (size_t)(i0 + r) * DK + j0) = f32x4{g[r][0], g[r][1], g[r][2], g[r][3]};
+        for (int q = 0; q < 4; ++q)
+            *(f32x4 *)(a.gmu0 + st + rm + 4 * q) = f32x4{g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]};
+    }
+    // the state: mu0 (row-major) transposed through LDS (fp32) into the second mapping
+    float sv[16];
+    {
+        float x[16];
+#pragma unroll
+        for (int n = 0; n < 16; ++n) x[n] = 0.f;
+        if (a.mu0) load16f(a.mu0 + st + rm, x);
+#pragma unroll
+        for (int n = 0; n < 16; ++n) tile_f[(cb16 + n) * kFS + ra] = x[n];
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < 16; ++n) sv[n] = tile_f[ra * kFS + cb16 + n];
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const f32x4 x = a.mu0 ? *(const f32x4 *)(a.mu0 + st + (size_t)(i0 + r) * DK + j0) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int x4 = 0; x4 < 4; ++x4) s[r][x4] = x[x4];
-    }
-    for (int c = 0; c < a.nc; ++c) {
-        const size_t cb = (size_t)bh * a.nc + c;
-        bf16_t *stp = a.sT + cb * DK * DV;
-        const bf16_t *gep = a.ge + cb * DV * DK;
-        float d[4][4];
-#pragma unroll
-        for (int x4 = 0; x4 < 4; ++x4) {
-            const uint2 u = *(const uint2 *)(stp + (size_t)(j0 + x4) * DV + i0);
-            d[0][x4] = bf_lo(u.x); d[1][x4] = bf_hi(u.x); d[2][x4] = bf_lo(u.y); d[3][x4] = bf_hi(u.y);
-            *(uint2 *)(stp + (size_t)(j0 + x4) * DV + i0) =
-                make_uint2(pack_bf16(s[0][x4], s[1][x4]), pack_bf16(s[2][x4], s[3][x4]));
+    for (int u = 0; u < kFbPre; ++u) {
+        ring[u][0] = ring[u][1] = u32x4{0u, 0u, 0u, 0u};
+        lring[u] = 0.f;
+        if (u < nc) {
+            ld2(a.sT + (cb0 + u) * e + tm, ring[u]);
+            lring[u] = a.lamc[cb0 + u];
         }
-        const float e = __expf(a.lamc[cb]);
-        float dot = 0.f;
+    }
+    for (int c0 = 0; c0 < nc; c0 += kFbPre) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint2 u = *(const uint2 *)(gep + (size_t)(i0 + r) * DK + j0);
-            const float gg[4] = {bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y)};
-#pragma unroll
-            for (int x4 = 0; x4 < 4; ++x4) {
-                dot = fmaf(gg[x4], s[r][x4], dot);
-                s[r][x4] = fmaf(e, s[r][x4], d[r][x4]);
+        for (int u = 0; u < kFbPre; ++u) {
+            const int c = c0 + u;
+            if (c < nc) {
+                const u32x4 d[2] = {ring[u][0], ring[u][1]};
+                const float ex = __expf(lring[u]);
+                if (c + kFbPre < nc) {
+                    ld2(a.sT + (cb0 + c + kFbPre) * e + tm, ring[u]);
+                    lring[u] = a.lamc[cb0 + c + kFbPre];
+                }
+                st2(a.sT + (cb0 + c) * e + tm, sv);
+                axpy(sv, ex, d);
             }
         }
-        dot = row16_sum(dot);
-        dot += __shfl_xor(dot, 16, 64);
-        dot += __shfl_xor(dot, 32, 64);
-        if (lane == 0) a.bdot[cb * kWavesPerHead + wv] = dot;
     }
 }
 
@@ -2664,7 +2741,6 @@ __global__ __launch_bounds__(256) void fzb_scan_kernel(FzbArgs a) {
 template <int DK, int DV, typename TG>
 __global__ __launch_bounds__(256) void fzb_grad_kernel(FzbArgs a) {
     using L = FzbLds<DK, DV>;
-    constexpr int kWavesPerHead = DV * DK / 1024;       // fzb_scan_kernel's partial dots per chunk
     extern __shared__ float lds_f[];
     bf16_t *hb = (bf16_t *)lds_f;
     float *lamv = (float *)(hb + L::kGradHalves);       // L_t
@@ -2672,6 +2748,7 @@ __global__ __launch_bounds__(256) void fzb_grad_kernel(FzbArgs a) {
     float *rk = rq + 4 * kFbC;                           // [wave][token] sums of k . gkI
     float *re = rk + 4 * kFbC;                           // [wave][token] sums of k . gkE
     float *ri = re + 4 * kFbC;                           // [wave] sums of gw . w
+    float *rb = ri + 4;                                  // [wave] partial <G_E, S_0>
     const int bh = blockIdx.x / a.nc, c = blockIdx.x % a.nc;
     const int b = bh / a.H, h = bh % a.H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -2683,6 +2760,27 @@ __global__ __launch_bounds__(256) void fzb_grad_kernel(FzbArgs a) {
     const float Lam = wave_read(Lt, 63);
     if (w == 0) lamv[lane] = Lt;
     fzb_stage<DK, DV, TG>(a, hb, seq, t0, inv_ip, tid, [](int) { return 1.f; }, [](int) { return 1.f; });
+
+    // The output blocks of wave w: for each of its NJ key blocks jb = w + 4 x a gq
+    // and a gk block (A operands S_0^T and G_E^T rows 16 jb), then for each of
+    // its NI value blocks ib a gw block (A operand G_E rows 16 ib).  The A
+    // fragments come from HBM; each block's are loaded while the block before
+    // it computes (the first ones during the scores below).
+    constexpr int NJ = DK / 64, NI = DV / 64, NB = 2 * NJ + NI, NF = (DK > DV ? DK : DV) / 32;
+    const size_t cb = (size_t)blockIdx.x;
+    const bf16_t *s0t = a.sT + cb * DK * DV, *gtp = a.gT + cb * DK * DV, *gep = a.ge + cb * DV * DK;
+    auto load_block = [&](int n, bf16x8_t *dst) __attribute__((always_inline)) {
+        if (n < 2 * NJ) {
+            const bf16_t *base = (n & 1) ? gtp : s0t;
+#pragma unroll
+            for (int f = 0; f < DV / 32; ++f) dst[f] = rowfrag(base, DV, 16 * (w + 4 * (n >> 1)), 32 * f, lane);
+        } else {
+#pragma unroll
+            for (int f = 0; f < DK / 32; ++f) dst[f] = rowfrag(gep, DK, 16 * (w + 4 * (n - 2 * NJ)), 32 * f, lane);
+        }
+    };
+    bf16x8_t fr[2][NF];
+    load_block(0, fr[0]);
     __syncthreads();
 
     // decay-masked scores, bf16 in LDS as [t][s]:
@@ -2727,16 +2825,22 @@ __global__ __launch_bounds__(256) void fzb_grad_kernel(FzbArgs a) {
         pk[xb] = 0.f;
         pe[xb] = 0.f;
     }
-    float pw = 0.f;
-    const size_t cb = (size_t)blockIdx.x;
-    const bf16_t *s0t = a.sT + cb * DK * DV, *gtp = a.gT + cb * DK * DV, *gep = a.ge + cb * DV * DK;
-    for (int jb = w; jb < DK / 16; jb += 4) {
-        const int j = 16 * jb + 4 * g;                   // the lane's 4 key channels j..j+3
-        // gq^T[j][t] = e^{L_t} sum_i S_0^T[j][i] gy[t][i] + sum_s k[s][j] P1[t][s]
-        {
-            bf16x8_t af[DV / 32];
+    float pw = 0.f, pb = 0.f;
 #pragma unroll
-            for (int ki = 0; ki < DV / 32; ++ki) af[ki] = rowfrag(s0t, DV, 16 * jb, 32 * ki, lane);
+    for (int n = 0; n < NB; ++n) {
+        const bf16x8_t *af = fr[n & 1];
+        if (n < 2 * NJ && (n & 1)) {
+            // <G_E, S_0> over the entries of this key block (the S_0^T fragments
+            // of block n-1 and the G_E^T ones line up)
+#pragma unroll
+            for (int f = 0; f < DV / 32; ++f)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pb = fmaf((float)af[f][e], (float)fr[(n + 1) & 1][f][e], pb);
+        }
+        if (n + 1 < NB) load_block(n + 1, fr[(n + 1) & 1]);
+        if (n < 2 * NJ && !(n & 1)) {
+            // gq^T[j][t] = e^{L_t} sum_i S_0^T[j][i] gy[t][i] + sum_s k[s][j] P1[t][s]
+            const int jb = w + 4 * (n >> 1), j = 16 * jb + 4 * g;
             const bf16x8_t k0 = lds_trfrag(hb + L::kK, L::kRK, 0, 16 * jb, lane);
             const bf16x8_t k1 = lds_trfrag(hb + L::kK, L::kRK, 32, 16 * jb, lane);
 #pragma unroll
@@ -2753,12 +2857,9 @@ __global__ __launch_bounds__(256) void fzb_grad_kernel(FzbArgs a) {
                 pq[tb] += (acc[0] * bf_lo(qq.x) + acc[1] * bf_hi(qq.x)) + (acc[2] * bf_lo(qq.y) + acc[3] * bf_hi(qq.y));
                 if (t0 + t < a.T) *(f32x4 *)(a.gq + (seq + (size_t)(t0 + t) * a.H) * DK + j) = acc;
             }
-        }
-        // gk^T[j][s] = e^{Lam - L_s} sum_i G_E^T[j][i] w[s][i] + sum_t q[t][j] P1[t][s]
-        {
-            bf16x8_t af[DV / 32];
-#pragma unroll
-            for (int ki = 0; ki < DV / 32; ++ki) af[ki] = rowfrag(gtp, DV, 16 * jb, 32 * ki, lane);
+        } else if (n < 2 * NJ) {
+            // gk^T[j][s] = e^{Lam - L_s} sum_i G_E^T[j][i] w[s][i] + sum_t q[t][j] P1[t][s]
+            const int jb = w + 4 * (n >> 1), j = 16 * jb + 4 * g;
             const bf16x8_t q0 = lds_trfrag(hb + L::kQ, L::kRK, 0, 16 * jb, lane);
             const bf16x8_t q1 = lds_trfrag(hb + L::kQ, L::kRK, 32, 16 * jb, lane);
 #pragma unroll
@@ -2778,45 +2879,52 @@ __global__ __launch_bounds__(256) void fzb_grad_kernel(FzbArgs a) {
                 acc += aci;
                 if (t0 + s < a.T) *(f32x4 *)(a.gk + (seq + (size_t)(t0 + s) * a.H) * DK + j) = acc;
             }
-        }
-    }
-    // gw^T[i][s] = e^{Lam - L_s} sum_j G_E[i][j] k[s][j] + sum_t gy[t][i] P2[t][s];
-    // gv = gw beta / I_prior (v* input: gw / I_prior), gbeta = gw v / I_prior
-    for (int ib = w; ib < DV / 16; ib += 4) {
-        const int i = 16 * ib + 4 * g;                   // the lane's 4 value rows i..i+3
-        bf16x8_t af[DK / 32];
+        } else {
+            // gw^T[i][s] = e^{Lam - L_s} sum_j G_E[i][j] k[s][j] + sum_t gy[t][i] P2[t][s];
+            // gv = gw beta / I_prior (v* input: gw / I_prior), gbeta = gw v / I_prior
+            const int ib = w + 4 * (n - 2 * NJ), i = 16 * ib + 4 * g;
+            const bf16x8_t g0 = lds_trfrag(hb + L::kG, L::kRV, 0, 16 * ib, lane);
+            const bf16x8_t g1 = lds_trfrag(hb + L::kG, L::kRV, 32, 16 * ib, lane);
 #pragma unroll
-        for (int kj = 0; kj < DK / 32; ++kj) af[kj] = rowfrag(gep, DK, 16 * ib, 32 * kj, lane);
-        const bf16x8_t g0 = lds_trfrag(hb + L::kG, L::kRV, 0, 16 * ib, lane);
-        const bf16x8_t g1 = lds_trfrag(hb + L::kG, L::kRV, 32, 16 * ib, lane);
+            for (int sb = 0; sb < 4; ++sb) {
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int kj = 0; kj < DK / 32; ++kj)
+                    acc = mfma16(af[kj], rowfrag(hb + L::kK, L::kRK, 16 * sb, 32 * kj, lane), acc);
+                acc *= eR[sb];
+                if (sb < 2) acc = mfma16(g0, lds_trfrag(hb + L::kP2, L::kRP, 0, 16 * sb, lane), acc);
+                acc = mfma16(g1, lds_trfrag(hb + L::kP2, L::kRP, 32, 16 * sb, lane), acc);
+                const int s = 16 * sb + m;
+                const uint2 ww = *(const uint2 *)(hb + L::kW + s * L::kRV + i);
+                pw += (acc[0] * bf_lo(ww.x) + acc[1] * bf_hi(ww.x)) + (acc[2] * bf_lo(ww.y) + acc[3] * bf_hi(ww.y));
+                if (t0 + s < a.T) {
+                    const size_t o = (seq + (size_t)(t0 + s) * a.H) * DV + i;
+                    const uint2 vv = *(const uint2 *)(a.v + o);
+                    const float vf[4] = {bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y)};
+                    f32x4 gvv, gbb;
+                    if (a.beta) {
+                        const uint2 bb = *(const uint2 *)(a.beta + o);
+                        const float bf[4] = {bf_lo(bb.x), bf_hi(bb.x), bf_lo(bb.y), bf_hi(bb.y)};
 #pragma unroll
-            for (int kj = 0; kj < DK / 32; ++kj)
-                acc = mfma16(af[kj], rowfrag(hb + L::kK, L::kRK, 16 * sb, 32 * kj, lane), acc);
-            acc *= eR[sb];
-            if (sb < 2) acc = mfma16(g0, lds_trfrag(hb + L::kP2, L::kRP, 0, 16 * sb, lane), acc);
-            acc = mfma16(g1, lds_trfrag(hb + L::kP2, L::kRP, 32, 16 * sb, lane), acc);
-            const int s = 16 * sb + m;
-            const uint2 ww = *(const uint2 *)(hb + L::kW + s * L::kRV + i);
-            pw += (acc[0] * bf_lo(ww.x) + acc[1] * bf_hi(ww.x)) + (acc[2] * bf_lo(ww.y) + acc[3] * bf_hi(ww.y));
-            if (t0 + s < a.T) {
-                const size_t o = (seq + (size_t)(t0 + s) * a.H) * DV + i;
-                const uint2 vv = *(const uint2 *)(a.v + o);
-                const float vf[4] = {bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y)};
-                if (a.beta) {
-                    const uint2 bb = *(const uint2 *)(a.beta + o);
-                    const float bf[4] = {bf_lo(bb.x), bf_hi(bb.x), bf_lo(bb.y), bf_hi(bb.y)};
+                        for (int r = 0; r < 4; ++r) {
+                            const float gwi = acc[r] * inv_ip;
+                            gvv[r] = gwi * bf[r];
+                            gbb[r] = gwi * vf[r];
+                        }
+                    } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float gwi = acc[r] * inv_ip;
-                        a.gv[o + r] = gwi * bf[r];
-                        a.gbeta[o + r] = gwi * vf[r];
+                        for (int r = 0; r < 4; ++r) gvv[r] = acc[r] * inv_ip;
                     }
-                } else {
+                    if (a.vec_g) {
+                        *(f32x4 *)(a.gv + o) = gvv;
+                        if (a.beta) *(f32x4 *)(a.gbeta + o) = gbb;
+                    } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) a.gv[o + r] = acc[r] * inv_ip;
+                        for (int r = 0; r < 4; ++r) {
+                            a.gv[o + r] = gvv[r];
+                            if (a.beta) a.gbeta[o + r] = gbb[r];
+                        }
+                    }
                 }
             }
         }
@@ -2839,7 +2947,13 @@ __global__ __launch_bounds__(256) void fzb_grad_kernel(FzbArgs a) {
     pw = row16_sum(pw);
     pw += __shfl_xor(pw, 16, 64);
     pw += __shfl_xor(pw, 32, 64);
-    if (lane == 0) ri[w] = pw;
+    pb = row16_sum(pb);
+    pb += __shfl_xor(pb, 16, 64);
+    pb += __shfl_xor(pb, 32, 64);
+    if (lane == 0) {
+        ri[w] = pw;
+        rb[w] = pb;
+    }
     __syncthreads();
     if (w == 0) {
         // dLoss/dl_t = e^{Lam} <G_E, S_0> + sum_{r<t} k_r . gkE_r + sum_{u>=t} (q_u . gq_u - k_u . gkI_u);
@@ -2849,9 +2963,7 @@ __global__ __launch_bounds__(256) void fzb_grad_kernel(FzbArgs a) {
         const float pe0 = (re[lane] + re[kFbC + lane]) + (re[2 * kFbC + lane] + re[3 * kFbC + lane]);
         const float rev = wave_incl_scan(__shfl(p, 63 - lane, 64), lane);   // lane j: sum_{u >= 63 - j} p_u
         const float pre = wave_incl_scan(pe0, lane) - pe0;                    // sum_{r < lane} pe0_r
-        float bsum = 0.f;
-#pragma unroll
-        for (int x = 0; x < kWavesPerHead; ++x) bsum += a.bdot[cb * kWavesPerHead + x];
+        const float bsum = (rb[0] + rb[1]) + (rb[2] + rb[3]);
         const float dl = __shfl(rev, 63 - lane, 64) + pre + __expf(Lam) * bsum;
         float ga = 0.f;
         if (t0 + lane < a.T) {
@@ -2869,19 +2981,27 @@ __global__ __launch_bounds__(256) void fzb_grad_kernel(FzbArgs a) {
     }
 }
 
-// gA[h] and gI_prior[h] = -(1 / I_prior) sum gw . w, summed over the batch and the chunks.
+// gA[h] and gI_prior[h] = -(1 / I_prior) sum gw . w, summed over the batch and
+// the chunks: one wave per head.
 __global__ __launch_bounds__(64) void fzb_head_kernel(const float *pA, const float *pI, const float *Ip, float *gA,
                                                       float *gIp, int B, int H, int nc) {
-    const int h = blockIdx.x * 64 + threadIdx.x;
-    if (h >= H) return;
+    const int h = blockIdx.x, lane = threadIdx.x;
     float sa = 0.f, si = 0.f;
-    for (int b = 0; b < B; ++b)
-        for (int c = 0; c < nc; ++c) {
-            sa += pA[((size_t)b * H + h) * nc + c];
-            si += pI[((size_t)b * H + h) * nc + c];
-        }
-    gA[h] = sa;
-    gIp[h] = -si / Ip[h];
+    for (int n = lane; n < B * nc; n += 64) {
+        const size_t o = ((size_t)(n / nc) * H + h) * nc + n % nc;
+        sa += pA[o];
+        si += pI[o];
+    }
+    sa = row16_sum(sa);
+    sa += __shfl_xor(sa, 16, 64);
+    sa += __shfl_xor(sa, 32, 64);
+    si = row16_sum(si);
+    si += __shfl_xor(si, 16, 64);
+    si += __shfl_xor(si, 32, 64);
+    if (lane == 0) {
+        gA[h] = sa;
+        gIp[h] = -si / Ip[h];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -3146,11 +3266,11 @@ palimpsa_status launch_bwd_fz_d(int dk, const FwdArgs &fa, const BwdArgs &ba, co
 
 // Workspace of the matrix-core frozen backward (per (b, h, chunk), 256-byte
 // aligned sections): S_0^T and G_E^T [DK][DV] and G_E [DV][DK] in bf16, and the
-// chunk's Lam, partial dots, gA and gw . w sums in float.  It is never larger
+// chunk's Lam, gA and gw . w sums in float.  It is never larger
 // than plan_bwd_ws for the same sizes (checked by the caller).
 struct FzbWs {
     bf16_t *sT, *ge, *gT;
-    float *lamc, *bdot, *pA, *pI;
+    float *lamc, *pA, *pI;
     size_t bytes;
 };
 FzbWs plan_fzb_ws(void *base, int B, int T, int H, int dk, int dv) {
@@ -3162,11 +3282,11 @@ FzbWs plan_fzb_ws(void *base, int B, int T, int H, int dk, int dv) {
         return o;
     };
     const size_t o_s = take(bhc * e * 2), o_g = take(bhc * e * 2), o_t = take(bhc * e * 2);
-    const size_t o_l = take(bhc * 4), o_d = take(bhc * (e / 1024) * 4), o_a = take(bhc * 4), o_i = take(bhc * 4);
+    const size_t o_l = take(bhc * 4), o_a = take(bhc * 4), o_i = take(bhc * 4);
     char *c = (char *)base;
     FzbWs w;
     w.sT = (bf16_t *)(c + o_s); w.ge = (bf16_t *)(c + o_g); w.gT = (bf16_t *)(c + o_t);
-    w.lamc = (float *)(c + o_l); w.bdot = (float *)(c + o_d); w.pA = (float *)(c + o_a); w.pI = (float *)(c + o_i);
+    w.lamc = (float *)(c + o_l); w.pA = (float *)(c + o_a); w.pI = (float *)(c + o_i);
     w.bytes = off;
     return w;
 }
@@ -3183,14 +3303,15 @@ palimpsa_status launch_fzb(const FzbArgs &a, hipStream_t s) {
             return PALIMPSA_ERR_HIP;
         hipLaunchKernelGGL(k1, dim3((unsigned)bhc), dim3(256), L::kLocalBytes, s, a);
     }
-    hipLaunchKernelGGL((fzb_scan_kernel<DK, DV>), dim3((unsigned)((size_t)a.B * a.H * (DV * DK / 4096))), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fzb_scan_kernel<DK, DV>), dim3((unsigned)((size_t)a.B * a.H * (DV / 64) * (DK / 64))), dim3(256), 0,
+                       s, a);
     if (bhc > 0) {
         auto k3 = fzb_grad_kernel<DK, DV, TG>;
         if (hipFuncSetAttribute((const void *)k3, hipFuncAttributeMaxDynamicSharedMemorySize, L::kGradBytes) != hipSuccess)
             return PALIMPSA_ERR_HIP;
         hipLaunchKernelGGL(k3, dim3((unsigned)bhc), dim3(256), L::kGradBytes, s, a);
     }
-    hipLaunchKernelGGL(fzb_head_kernel, dim3((a.H + 63) / 64), dim3(64), 0, s, (const float *)a.pA, (const float *)a.pI,
+    hipLaunchKernelGGL(fzb_head_kernel, dim3(a.H), dim3(64), 0, s, (const float *)a.pA, (const float *)a.pI,
                        a.Ip, a.gA, a.gIp, a.B, a.H, a.nc);
     return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
 }
@@ -3384,8 +3505,9 @@ palimpsa_status palimpsa_bwd_frozen(const void *q, const void *k, const void *v,
         fa.gq = gq; fa.gk = gk; fa.gv = gv; fa.gbeta = beta ? gbeta : nullptr; fa.gdt = gdt;
         fa.gA = gA; fa.gIp = gIp; fa.gmu0 = gmu0;
         fa.sT = fw.sT; fa.ge = fw.ge; fa.gT = fw.gT;
-        fa.lamc = fw.lamc; fa.bdot = fw.bdot; fa.pA = fw.pA; fa.pI = fw.pI;
+        fa.lamc = fw.lamc; fa.pA = fw.pA; fa.pI = fw.pI;
         fa.B = B; fa.T = T; fa.H = H; fa.nc = (T + kFbC - 1) / kFbC;
+        fa.vec_g = aligned_to(gv, 16) && (!beta || aligned_to(gbeta, 16));
         return gy_dtype == PALIMPSA_BF16 ? launch_fzb_d<bf16_t>(dk, dv, fa, s) : launch_fzb_d<float>(dk, dv, fa, s);
     }
     // without beta the v tensor is the write itself; the beta pointer is then

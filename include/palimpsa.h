@@ -299,11 +299,16 @@ size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv, int flag
  *     mu_t = alpha_t mu_{t-1} + (w_t / I_prior[h]) (x) k_t,   y_t = mu_t q_t,
  *     w_t = beta_t . v_t (or v*_t when beta is NULL),  alpha_t = exp(-A dt_t),
  *
- * for L = sum(gy . y) + sum(gmuT . muT), computed in float32 from the forward's
- * inputs (it recomputes the states, checkpoints every 8 tokens in the
- * workspace).  It differentiates the recurrence above, not the bf16 products
- * of palimpsa_fwd_frozen: it also takes float32 inputs and any dk the exact
- * backward takes.
+ * for L = sum(gy . y) + sum(gmuT . muT), from the forward's inputs (it
+ * recomputes the states itself).  Two paths, chosen by the inputs:
+ *   - bf16 inputs with dk and dv in {64, 128}: the chunked form on the matrix
+ *     cores (64-token chunks; per chunk each gradient is one product with the
+ *     chunk's boundary state or adjoint and one causal product inside the
+ *     chunk).  Operands are bf16 as in palimpsa_fwd_frozen, accumulation fp32:
+ *     gradients carry about 2^-8 relative error, and the batch sums gA and
+ *     gIp that much of the sum of their terms' magnitudes;
+ *   - otherwise (float32 inputs, dk = 32, other dv): float32 throughout, the
+ *     states recomputed from checkpoints every 8 tokens.
  *
  * Inputs (device pointers, layouts as palimpsa_fwd_chunked):
  *   q, k      [B, T, H, dk]  in_dtype
