@@ -2472,14 +2472,18 @@ __device__ inline float fzb_lam(const FzbArgs &a, size_t seq, int t0, int lane, 
 
 template <int DK, int DV>
 struct FzbLds {
-    static constexpr int kRK = DK + 16, kRV = DV + 16, kRP = kFbC + 16;   // row strides (bf16)
+    // rows padded by 8 elements (16 bytes), so that the 16 rows a fragment read
+    // touches start in different banks
+    static constexpr int kRK = DK + 8, kRV = DV + 8, kRP = kFbC + 8;   // row strides (bf16)
     static constexpr int kQ = 0, kK = kQ + kFbC * kRK, kG = kK + kFbC * kRK, kW = kG + kFbC * kRV;
-    static constexpr int kP1 = kW + kFbC * kRV, kP2 = kP1 + kFbC * kRP;
-    static constexpr int kLocalHalves = kP1;              // fzb_local: Q, K, G, W only
-    static constexpr int kGradHalves = kP2 + kFbC * kRP;
-    // fzb_grad also keeps L [64], per-wave token sums (q.gq, k.gkI, k.gkE) and gw.w sums
+    static constexpr int kP = kW + kFbC * kRV;            // one score matrix [64][kRP]
+    static constexpr int kLocalHalves = kP;               // fzb_local: Q, K, G, W only
+    static constexpr int kGradHalves = kP + kFbC * kRP;
     static constexpr int kLocalBytes = kLocalHalves * 2;
-    static constexpr int kGradBytes = kGradHalves * 2 + (kFbC + 3 * 4 * kFbC + 8) * 4;
+    static constexpr int kGradBytes = kGradHalves * 2;
+    // fzb_grad's closing sums (per-wave token sums of q.gq, k.gkI, k.gkE, and
+    // of gw.w and <G_E, S_0>) reuse the score matrix's space
+    static_assert((3 * 4 * kFbC + 8) * 4 <= kFbC * kRP * 2, "closing sums exceed the score buffer");
 };
 
 // Stage the chunk's Q and K (bf16, rows = tokens) and gy and w scaled per
@@ -2491,17 +2495,28 @@ __device__ inline void fzb_stage(const FzbArgs &a, bf16_t *hb, size_t seq, int t
     constexpr int NQ = kFbC * kPk / 256, NV = kFbC * kPv / 256;   // packets per thread
     constexpr int kGP = sizeof(TG) / 2;                             // 16-byte packets per 8 values of gy
     const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-    // every load first (rows past the end clamped to the last token, zeroed below),
-    // so that they are all in flight together
+    // the loads of each half (q, k; then v, beta, gy) first, so that they are
+    // in flight together (rows past the end clamped to the last token, zeroed
+    // at the commit)
     const int tl = a.T - 1;
-    u32x4 qv[NQ], kv[NQ], vv[NV], bv[NV], gv[NV][kGP];
+    {
+        u32x4 qv[NQ], kv[NQ];
 #pragma unroll
-    for (int n = 0; n < NQ; ++n) {
-        const int p = tid + 256 * n, t = p / kPk, col = 8 * (p % kPk);
-        const size_t o = (seq + (size_t)min(t0 + t, tl) * a.H) * DK + col;
-        qv[n] = *(const u32x4 *)(a.q + o);
-        kv[n] = *(const u32x4 *)(a.k + o);
+        for (int n = 0; n < NQ; ++n) {
+            const int p = tid + 256 * n, t = p / kPk, col = 8 * (p % kPk);
+            const size_t o = (seq + (size_t)min(t0 + t, tl) * a.H) * DK + col;
+            qv[n] = *(const u32x4 *)(a.q + o);
+            kv[n] = *(const u32x4 *)(a.k + o);
+        }
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            const int p = tid + 256 * n, t = p / kPk, col = 8 * (p % kPk);
+            const bool ok = t0 + t < a.T;
+            *(u32x4 *)(hb + L::kQ + t * L::kRK + col) = ok ? qv[n] : z;
+            *(u32x4 *)(hb + L::kK + t * L::kRK + col) = ok ? kv[n] : z;
+        }
     }
+    u32x4 vv[NV], bv[NV], gv[NV][kGP];
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
         const int p = tid + 256 * n, t = p / kPv, col = 8 * (p % kPv);
@@ -2510,13 +2525,6 @@ __device__ inline void fzb_stage(const FzbArgs &a, bf16_t *hb, size_t seq, int t
         bv[n] = a.beta ? *(const u32x4 *)(a.beta + o) : z;
 #pragma unroll
         for (int x = 0; x < kGP; ++x) gv[n][x] = *(const u32x4 *)((const TG *)a.gy + o + 4 * x);
-    }
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) {
-        const int p = tid + 256 * n, t = p / kPk, col = 8 * (p % kPk);
-        const bool ok = t0 + t < a.T;
-        *(u32x4 *)(hb + L::kQ + t * L::kRK + col) = ok ? qv[n] : z;
-        *(u32x4 *)(hb + L::kK + t * L::kRK + col) = ok ? kv[n] : z;
     }
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
@@ -2737,18 +2745,16 @@ __global__ __launch_bounds__(256) void fzb_scan_kernel(FzbArgs a) {
 }
 
 // One workgroup per (b, h, chunk): the gradients of the chunk's tokens, and
-// the chunk's shares of gA and of sum gw . w (for gI_prior).
+// the chunk's shares of gA and of sum gw . w (for gI_prior).  Two workgroups
+// share a CU (LDS under half of it), so that one's loads overlap the other's
+// products.  Order: stage; scores q.k into P; the gw blocks; scores gy.w into
+// P; the gq and gk blocks; the closing sums.
 template <int DK, int DV, typename TG>
-__global__ __launch_bounds__(256) void fzb_grad_kernel(FzbArgs a) {
+__global__ __launch_bounds__(256, 2) void fzb_grad_kernel(FzbArgs a) {
     using L = FzbLds<DK, DV>;
     extern __shared__ float lds_f[];
     bf16_t *hb = (bf16_t *)lds_f;
-    float *lamv = (float *)(hb + L::kGradHalves);       // L_t
-    float *rq = lamv + kFbC;                             // [wave][token] sums of q . gq
-    float *rk = rq + 4 * kFbC;                           // [wave][token] sums of k . gkI
-    float *re = rk + 4 * kFbC;                           // [wave][token] sums of k . gkE
-    float *ri = re + 4 * kFbC;                           // [wave] sums of gw . w
-    float *rb = ri + 4;                                  // [wave] partial <G_E, S_0>
+    bf16_t *P = hb + L::kP;
     const int bh = blockIdx.x / a.nc, c = blockIdx.x % a.nc;
     const int b = bh / a.H, h = bh % a.H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -2756,69 +2762,64 @@ __global__ __launch_bounds__(256) void fzb_grad_kernel(FzbArgs a) {
     const size_t seq = (size_t)b * a.T * a.H + h;
     const int t0 = c * kFbC;
     const float Ah = a.A[h], inv_ip = 1.f / a.Ip[h];
-    const float Lt = fzb_lam(a, seq, t0, lane, Ah);
+    const float Lt = fzb_lam(a, seq, t0, lane, Ah);     // L of token `lane`
     const float Lam = wave_read(Lt, 63);
-    if (w == 0) lamv[lane] = Lt;
     fzb_stage<DK, DV, TG>(a, hb, seq, t0, inv_ip, tid, [](int) { return 1.f; }, [](int) { return 1.f; });
 
-    // The output blocks of wave w: for each of its NJ key blocks jb = w + 4 x a gq
-    // and a gk block (A operands S_0^T and G_E^T rows 16 jb), then for each of
-    // its NI value blocks ib a gw block (A operand G_E rows 16 ib).  The A
+    // The output blocks of wave w: first its NI value blocks ib = w + 4 x (gw;
+    // A operand G_E rows 16 ib), then for each of its NJ key blocks jb = w + 4 x
+    // a gq and a gk block (A operands S_0^T and G_E^T rows 16 jb).  The A
     // fragments come from HBM; each block's are loaded while the block before
-    // it computes (the first ones during the scores below).
-    constexpr int NJ = DK / 64, NI = DV / 64, NB = 2 * NJ + NI, NF = (DK > DV ? DK : DV) / 32;
+    // it computes (the first ones during the scores).
+    constexpr int NJ = DK / 64, NI = DV / 64, NB = NI + 2 * NJ, NF = (DK > DV ? DK : DV) / 32;
     const size_t cb = (size_t)blockIdx.x;
     const bf16_t *s0t = a.sT + cb * DK * DV, *gtp = a.gT + cb * DK * DV, *gep = a.ge + cb * DV * DK;
     auto load_block = [&](int n, bf16x8_t *dst) __attribute__((always_inline)) {
-        if (n < 2 * NJ) {
-            const bf16_t *base = (n & 1) ? gtp : s0t;
+        if (n < NI) {
 #pragma unroll
-            for (int f = 0; f < DV / 32; ++f) dst[f] = rowfrag(base, DV, 16 * (w + 4 * (n >> 1)), 32 * f, lane);
+            for (int f = 0; f < DK / 32; ++f) dst[f] = rowfrag(gep, DK, 16 * (w + 4 * n), 32 * f, lane);
         } else {
+            const int x = n - NI;
+            const bf16_t *base = (x & 1) ? gtp : s0t;
 #pragma unroll
-            for (int f = 0; f < DK / 32; ++f) dst[f] = rowfrag(gep, DK, 16 * (w + 4 * (n - 2 * NJ)), 32 * f, lane);
+            for (int f = 0; f < DV / 32; ++f) dst[f] = rowfrag(base, DV, 16 * (w + 4 * (x >> 1)), 32 * f, lane);
         }
     };
     bf16x8_t fr[2][NF];
     load_block(0, fr[0]);
     __syncthreads();
 
-    // decay-masked scores, bf16 in LDS as [t][s]:
-    //   P2[t][s] = e^{L_t - L_s} q_t . k_s,  P1[t][s] = e^{L_t - L_s} gy_t . w_s  (s <= t; 0 above)
-    for (int n = w; n < 32; n += 4) {
-        const int mat = n >> 4, tb = (n >> 2) & 3, sb = n & 3;
-        bf16_t *P = hb + (mat ? L::kP1 : L::kP2);
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (sb <= tb) {
-            if (mat == 0) {
+    // decay-masked scores into P, bf16 as [t][s]: e^{L_t - L_s} (rows(t) . cols(s))
+    // for s <= t, 0 above
+    auto scores = [&](int oa, int ob, int rs, int nk) __attribute__((always_inline)) {
+        for (int n = w; n < 16; n += 4) {
+            const int tb = n >> 2, sb = n & 3;
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (sb <= tb) {
+                for (int kk = 0; kk < nk; ++kk)
+                    acc = mfma16(rowfrag(hb + oa, rs, 16 * tb, 32 * kk, lane), rowfrag(hb + ob, rs, 16 * sb, 32 * kk, lane),
+                                 acc);
+                const int s = 16 * sb + m;
+                const float ls = __shfl(Lt, s, 64);
 #pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk)
-                    acc = mfma16(rowfrag(hb + L::kQ, L::kRK, 16 * tb, 32 * kk, lane),
-                                 rowfrag(hb + L::kK, L::kRK, 16 * sb, 32 * kk, lane), acc);
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < DV / 32; ++kk)
-                    acc = mfma16(rowfrag(hb + L::kG, L::kRV, 16 * tb, 32 * kk, lane),
-                                 rowfrag(hb + L::kW, L::kRV, 16 * sb, 32 * kk, lane), acc);
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * tb + 4 * g + r;
+                    const float lt = __shfl(Lt, t, 64);
+                    acc[r] = s <= t ? acc[r] * __expf(lt - ls) : 0.f;
+                }
             }
-            const int s = 16 * sb + m;
-            const float ls = lamv[s];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * tb + 4 * g + r;
-                acc[r] = s <= t ? acc[r] * __expf(lamv[t] - ls) : 0.f;
-            }
+            for (int r = 0; r < 4; ++r) P[(16 * tb + 4 * g + r) * L::kRP + 16 * sb + m] = (bf16_t)acc[r];
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) P[(16 * tb + 4 * g + r) * L::kRP + 16 * sb + m] = (bf16_t)acc[r];
-    }
+    };
+    scores(L::kQ, L::kK, L::kRK, DK / 32);
     __syncthreads();
 
     // The lane's token in column block xb is 16 xb + m.
     float eL[4], eR[4], pq[4], pk[4], pe[4];
 #pragma unroll
     for (int xb = 0; xb < 4; ++xb) {
-        const float lx = lamv[16 * xb + m];
+        const float lx = __shfl(Lt, 16 * xb + m, 64);
         eL[xb] = __expf(lx);
         eR[xb] = __expf(Lam - lx);
         pq[xb] = 0.f;
@@ -2828,8 +2829,15 @@ __global__ __launch_bounds__(256) void fzb_grad_kernel(FzbArgs a) {
     float pw = 0.f, pb = 0.f;
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
+        if (n == NI) {
+            // the gw blocks are done with q.k: replace it by gy.w
+            __syncthreads();
+            scores(L::kG, L::kW, L::kRV, DV / 32);
+            __syncthreads();
+        }
         const bf16x8_t *af = fr[n & 1];
-        if (n < 2 * NJ && (n & 1)) {
+        const int x = n - NI;
+        if (n >= NI && (x & 1)) {
             // <G_E, S_0> over the entries of this key block (the S_0^T fragments
             // of block n-1 and the G_E^T ones line up)
 #pragma unroll
@@ -2838,62 +2846,21 @@ __global__ __launch_bounds__(256) void fzb_grad_kernel(FzbArgs a) {
                 for (int e = 0; e < 8; ++e) pb = fmaf((float)af[f][e], (float)fr[(n + 1) & 1][f][e], pb);
         }
         if (n + 1 < NB) load_block(n + 1, fr[(n + 1) & 1]);
-        if (n < 2 * NJ && !(n & 1)) {
-            // gq^T[j][t] = e^{L_t} sum_i S_0^T[j][i] gy[t][i] + sum_s k[s][j] P1[t][s]
-            const int jb = w + 4 * (n >> 1), j = 16 * jb + 4 * g;
-            const bf16x8_t k0 = lds_trfrag(hb + L::kK, L::kRK, 0, 16 * jb, lane);
-            const bf16x8_t k1 = lds_trfrag(hb + L::kK, L::kRK, 32, 16 * jb, lane);
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ki = 0; ki < DV / 32; ++ki)
-                    acc = mfma16(af[ki], rowfrag(hb + L::kG, L::kRV, 16 * tb, 32 * ki, lane), acc);
-                acc *= eL[tb];
-                acc = mfma16(k0, rowfrag(hb + L::kP1, L::kRP, 16 * tb, 0, lane), acc);
-                if (tb >= 2) acc = mfma16(k1, rowfrag(hb + L::kP1, L::kRP, 16 * tb, 32, lane), acc);
-                const int t = 16 * tb + m;
-                const uint2 qq = *(const uint2 *)(hb + L::kQ + t * L::kRK + j);
-                pq[tb] += (acc[0] * bf_lo(qq.x) + acc[1] * bf_hi(qq.x)) + (acc[2] * bf_lo(qq.y) + acc[3] * bf_hi(qq.y));
-                if (t0 + t < a.T) *(f32x4 *)(a.gq + (seq + (size_t)(t0 + t) * a.H) * DK + j) = acc;
-            }
-        } else if (n < 2 * NJ) {
-            // gk^T[j][s] = e^{Lam - L_s} sum_i G_E^T[j][i] w[s][i] + sum_t q[t][j] P1[t][s]
-            const int jb = w + 4 * (n >> 1), j = 16 * jb + 4 * g;
-            const bf16x8_t q0 = lds_trfrag(hb + L::kQ, L::kRK, 0, 16 * jb, lane);
-            const bf16x8_t q1 = lds_trfrag(hb + L::kQ, L::kRK, 32, 16 * jb, lane);
-#pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, aci = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ki = 0; ki < DV / 32; ++ki)
-                    acc = mfma16(af[ki], rowfrag(hb + L::kW, L::kRV, 16 * sb, 32 * ki, lane), acc);
-                acc *= eR[sb];
-                if (sb < 2) aci = mfma16(q0, lds_trfrag(hb + L::kP1, L::kRP, 0, 16 * sb, lane), aci);
-                aci = mfma16(q1, lds_trfrag(hb + L::kP1, L::kRP, 32, 16 * sb, lane), aci);
-                const int s = 16 * sb + m;
-                const uint2 kk = *(const uint2 *)(hb + L::kK + s * L::kRK + j);
-                const float k4[4] = {bf_lo(kk.x), bf_hi(kk.x), bf_lo(kk.y), bf_hi(kk.y)};
-                pe[sb] += (acc[0] * k4[0] + acc[1] * k4[1]) + (acc[2] * k4[2] + acc[3] * k4[3]);
-                pk[sb] += (aci[0] * k4[0] + aci[1] * k4[1]) + (aci[2] * k4[2] + aci[3] * k4[3]);
-                acc += aci;
-                if (t0 + s < a.T) *(f32x4 *)(a.gk + (seq + (size_t)(t0 + s) * a.H) * DK + j) = acc;
-            }
-        } else {
-            // gw^T[i][s] = e^{Lam - L_s} sum_j G_E[i][j] k[s][j] + sum_t gy[t][i] P2[t][s];
+        if (n < NI) {
+            // gw^T[i][s] = e^{Lam - L_s} sum_j G_E[i][j] k[s][j] + sum_t gy[t][i] P[t][s];
             // gv = gw beta / I_prior (v* input: gw / I_prior), gbeta = gw v / I_prior
-            const int ib = w + 4 * (n - 2 * NJ), i = 16 * ib + 4 * g;
+            const int ib = w + 4 * n, i = 16 * ib + 4 * g;
             const bf16x8_t g0 = lds_trfrag(hb + L::kG, L::kRV, 0, 16 * ib, lane);
             const bf16x8_t g1 = lds_trfrag(hb + L::kG, L::kRV, 32, 16 * ib, lane);
-#pragma unroll
+#pragma unroll 1
             for (int sb = 0; sb < 4; ++sb) {
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kj = 0; kj < DK / 32; ++kj)
                     acc = mfma16(af[kj], rowfrag(hb + L::kK, L::kRK, 16 * sb, 32 * kj, lane), acc);
                 acc *= eR[sb];
-                if (sb < 2) acc = mfma16(g0, lds_trfrag(hb + L::kP2, L::kRP, 0, 16 * sb, lane), acc);
-                acc = mfma16(g1, lds_trfrag(hb + L::kP2, L::kRP, 32, 16 * sb, lane), acc);
+                if (sb < 2) acc = mfma16(g0, lds_trfrag(P, L::kRP, 0, 16 * sb, lane), acc);
+                acc = mfma16(g1, lds_trfrag(P, L::kRP, 32, 16 * sb, lane), acc);
                 const int s = 16 * sb + m;
                 const uint2 ww = *(const uint2 *)(hb + L::kW + s * L::kRV + i);
                 pw += (acc[0] * bf_lo(ww.x) + acc[1] * bf_hi(ww.x)) + (acc[2] * bf_lo(ww.y) + acc[3] * bf_hi(ww.y));
@@ -2927,9 +2894,56 @@ __global__ __launch_bounds__(256) void fzb_grad_kernel(FzbArgs a) {
                     }
                 }
             }
+        } else if (!(x & 1)) {
+            // gq^T[j][t] = e^{L_t} sum_i S_0^T[j][i] gy[t][i] + sum_s k[s][j] P[t][s]
+            const int jb = w + 4 * (x >> 1), j = 16 * jb + 4 * g;
+            const bf16x8_t k0 = lds_trfrag(hb + L::kK, L::kRK, 0, 16 * jb, lane);
+            const bf16x8_t k1 = lds_trfrag(hb + L::kK, L::kRK, 32, 16 * jb, lane);
+#pragma unroll 1
+            for (int tb = 0; tb < 4; ++tb) {
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ki = 0; ki < DV / 32; ++ki)
+                    acc = mfma16(af[ki], rowfrag(hb + L::kG, L::kRV, 16 * tb, 32 * ki, lane), acc);
+                acc *= eL[tb];
+                acc = mfma16(k0, rowfrag(P, L::kRP, 16 * tb, 0, lane), acc);
+                if (tb >= 2) acc = mfma16(k1, rowfrag(P, L::kRP, 16 * tb, 32, lane), acc);
+                const int t = 16 * tb + m;
+                const uint2 qq = *(const uint2 *)(hb + L::kQ + t * L::kRK + j);
+                pq[tb] += (acc[0] * bf_lo(qq.x) + acc[1] * bf_hi(qq.x)) + (acc[2] * bf_lo(qq.y) + acc[3] * bf_hi(qq.y));
+                if (t0 + t < a.T) *(f32x4 *)(a.gq + (seq + (size_t)(t0 + t) * a.H) * DK + j) = acc;
+            }
+        } else {
+            // gk^T[j][s] = e^{Lam - L_s} sum_i G_E^T[j][i] w[s][i] + sum_t q[t][j] P[t][s]
+            const int jb = w + 4 * (x >> 1), j = 16 * jb + 4 * g;
+            const bf16x8_t q0 = lds_trfrag(hb + L::kQ, L::kRK, 0, 16 * jb, lane);
+            const bf16x8_t q1 = lds_trfrag(hb + L::kQ, L::kRK, 32, 16 * jb, lane);
+#pragma unroll 1
+            for (int sb = 0; sb < 4; ++sb) {
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, aci = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ki = 0; ki < DV / 32; ++ki)
+                    acc = mfma16(af[ki], rowfrag(hb + L::kW, L::kRV, 16 * sb, 32 * ki, lane), acc);
+                acc *= eR[sb];
+                if (sb < 2) aci = mfma16(q0, lds_trfrag(P, L::kRP, 0, 16 * sb, lane), aci);
+                aci = mfma16(q1, lds_trfrag(P, L::kRP, 32, 16 * sb, lane), aci);
+                const int s = 16 * sb + m;
+                const uint2 kk = *(const uint2 *)(hb + L::kK + s * L::kRK + j);
+                const float k4[4] = {bf_lo(kk.x), bf_hi(kk.x), bf_lo(kk.y), bf_hi(kk.y)};
+                pe[sb] += (acc[0] * k4[0] + acc[1] * k4[1]) + (acc[2] * k4[2] + acc[3] * k4[3]);
+                pk[sb] += (aci[0] * k4[0] + aci[1] * k4[1]) + (aci[2] * k4[2] + aci[3] * k4[3]);
+                acc += aci;
+                if (t0 + s < a.T) *(f32x4 *)(a.gk + (seq + (size_t)(t0 + s) * a.H) * DK + j) = acc;
+            }
         }
     }
-    // token sums: the 4 lane groups hold the same tokens
+    // closing sums, in the score buffer's space; the 4 lane groups hold the same tokens
+    __syncthreads();
+    float *rq = (float *)P;                              // [wave][token] sums of q . gq
+    float *rk = rq + 4 * kFbC;                           // [wave][token] sums of k . gkI
+    float *re = rk + 4 * kFbC;                           // [wave][token] sums of k . gkE
+    float *ri = re + 4 * kFbC;                           // [wave] sums of gw . w
+    float *rb = ri + 4;                                  // [wave] partial <G_E, S_0>
 #pragma unroll
     for (int xb = 0; xb < 4; ++xb) {
         pq[xb] += __shfl_xor(pq[xb], 16, 64);
