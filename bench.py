@@ -46,12 +46,6 @@ BWD_FLOPS_PER_UPDATE = 29
 # (33 flops) plus one v_rcp_f32 (2 slots): 11.5 slots and 16.5 flops per entry.
 BD2_SLOTS_PER_ENTRY = 11.5
 BD2_FLOPS_PER_ENTRY = 16.5
-# Backward of the frozen-importance recurrence, per state entry and token:
-# replay of the content update (MUL + FMA, 3 flops) and the reverse step
-# (GM += gy q, gq, gk, gbv, da, GM *= alpha: 3 FMA + 3 MUL, 9 flops):
-# 8 issue slots, 12 flops.
-FZ_BWD_SLOTS_PER_UPDATE = 8
-FZ_BWD_FLOPS_PER_UPDATE = 12
 
 
 def alu_peak_tflops():
@@ -241,8 +235,11 @@ def frozen_extra(torch, pm, w, g, steps):
 
 def frozen_backward_extra(torch, pm, workloads, w, g, steps):
     """palimpsa_bwd_frozen (backward of the frozen-importance recurrence) on the
-    same workload, timed as one call (checkpoint pass, reverse walk, finishing
-    kernels)."""
+    same workload, timed as one call.  bf16 inputs with d = 64 or 128 take the
+    chunked matrix-core form (chunk contributions, scan over chunks, per-chunk
+    gradients, batch sums); its roofline is HBM, over the bytes the call must
+    move (inputs and gradients; the chunk-boundary states it passes between its
+    kernels are extra traffic)."""
     dev = g["q"].device
     gr = workloads.upstream_grads(w.B, w.T, w.H, w.dv, w.dk, w.dtype, seed=2)
     gy, gmuT = gr["gy"].to(dev), gr["gmuT"].to(dev)
@@ -252,15 +249,20 @@ def frozen_backward_extra(torch, pm, workloads, w, g, steps):
     fn = lambda: pm.bwd_frozen(*args, gmuT=gmuT, workspace=ws, out=out)
     _, per = time_launches(fn, steps, 3, torch)
     avg_s = sum(per) / len(per) / 1e3
-    updates = w.B * w.H * w.T * w.dv * w.dk
-    peak = LANE_OPS_PER_S / FZ_BWD_SLOTS_PER_UPDATE * FZ_BWD_FLOPS_PER_UPDATE / 1e12
-    achieved = updates * FZ_BWD_FLOPS_PER_UPDATE / avg_s / 1e12
+    esz = 2 if w.dtype == torch.bfloat16 else 4
+    btok = w.B * w.T * w.H
+    state = w.B * w.H * w.dv * w.dk * 4
+    # read q, k, v, beta, gy, dt and gmuT; write gq, gk, gv, gbeta, gdt (fp32) and gmu0
+    alg = btok * ((2 * w.dk + 3 * w.dv + 1) * esz + (2 * w.dk + 2 * w.dv + 1) * 4) + 2 * state
+    nc = (w.T + 63) // 64
+    boundary = 3 * w.B * w.H * nc * w.dv * w.dk * 2     # S_0^T, G_E, G_E^T per chunk, bf16
     return {"workload": w.name + ", frozen-importance backward (gq, gk, gv, gbeta, gdt, gA, gIp, gmu0)",
             "tokens_per_s": w.B * w.T / avg_s, "ms_per_call": avg_s * 1e3,
-            "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                         "frac": achieved / peak, "traffic": None,
-                         "scope": "whole call (5 kernels)",
-                         "per_update": "replay 2 VALU + reverse 6 VALU = 8 slots, 12 flops"}}
+            "roofline": {"bound": "hbm", "achieved": alg / avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": alg / avg_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                         "algorithmic_bytes": alg,
+                         "chunk_boundary_bytes": boundary,
+                         "scope": "whole call (4 kernels)"}}
 
 
 def blockdiag_extra(torch, pm, w, g, steps):
