@@ -259,7 +259,9 @@ def frozen_backward_extra(torch, pm, workloads, w, g, steps):
     return {"workload": w.name + ", frozen-importance backward (gq, gk, gv, gbeta, gdt, gA, gIp, gmu0)",
             "tokens_per_s": w.B * w.T / avg_s, "ms_per_call": avg_s * 1e3,
             "roofline": {"bound": "hbm", "achieved": alg / avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": alg / avg_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                         "frac": alg / avg_s / 1e9 / HBM_PEAK_GBS,
+                         "traffic": load_traffic("frozen_bwd_layer760m_bf16_traffic.json")
+                         if w.name.startswith("layer760m") else None,
                          "algorithmic_bytes": alg,
                          "chunk_boundary_bytes": boundary,
                          "scope": "whole call (4 kernels)"}}
