@@ -3332,8 +3332,12 @@ palimpsa_status launch_fzb(const FzbArgs &a, hipStream_t s) {
 
 template <typename TG>
 palimpsa_status launch_fzb_d(int dk, int dv, const FzbArgs &a, hipStream_t s) {
-    if (dk == 64) return dv == 64 ? launch_fzb<64, 64, TG>(a, s) : launch_fzb<64, 128, TG>(a, s);
-    return dv == 64 ? launch_fzb<128, 64, TG>(a, s) : launch_fzb<128, 128, TG>(a, s);
+    if (dk == 64) {
+        if (dv == 64) return launch_fzb<64, 64, TG>(a, s);
+        return dv == 128 ? launch_fzb<64, 128, TG>(a, s) : launch_fzb<64, 256, TG>(a, s);
+    }
+    if (dv == 64) return launch_fzb<128, 64, TG>(a, s);
+    return dv == 128 ? launch_fzb<128, 128, TG>(a, s) : launch_fzb<128, 256, TG>(a, s);
 }
 
 template <typename TIn, typename TG>
@@ -3508,7 +3512,7 @@ palimpsa_status palimpsa_bwd_frozen(const void *q, const void *k, const void *v,
     const BwdWs w = plan_bwd_ws(workspace, B, T, H, dk, dv, false);
     if (workspace_bytes < w.bytes) return PALIMPSA_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
-    if (in_dtype == PALIMPSA_BF16 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128)) {
+    if (in_dtype == PALIMPSA_BF16 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128 || dv == 256)) {
         // chunked form on the matrix cores
         const FzbWs fw = plan_fzb_ws(workspace, B, T, H, dk, dv);
         if (fw.bytes > w.bytes) return PALIMPSA_ERR_INVALID_ARG;

@@ -301,7 +301,7 @@ size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv, int flag
  *
  * for L = sum(gy . y) + sum(gmuT . muT), from the forward's inputs (it
  * recomputes the states itself).  Two paths, chosen by the inputs:
- *   - bf16 inputs with dk and dv in {64, 128}: the chunked form on the matrix
+ *   - bf16 inputs with dk in {64, 128} and dv in {64, 128, 256}: the chunked form on the matrix
  *     cores (64-token chunks; per chunk each gradient is one product with the
  *     chunk's boundary state or adjoint and one causal product inside the
  *     chunk).  Operands are bf16 as in palimpsa_fwd_frozen, accumulation fp32:

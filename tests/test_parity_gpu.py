@@ -642,9 +642,10 @@ def _bwd_frozen_ref(inp, gr, mu0=None, vstar=False):
 
 
 def _fz_mfma(dtype, dk, dv):
-    """bf16 inputs with dk, dv in {64, 128} take the matrix-core path (bf16
-    operands, the frozen forward's 2e-2 bar); the rest the float32 one."""
-    return dtype == torch.bfloat16 and dk in (64, 128) and dv in (64, 128)
+    """bf16 inputs with dk in {64, 128} and dv in {64, 128, 256} take the
+    matrix-core path (bf16 operands, the frozen forward's 2e-2 bar); the rest
+    the float32 one."""
+    return dtype == torch.bfloat16 and dk in (64, 128) and dv in (64, 128, 256)
 
 
 def _fz_tol(dtype, dk, dv):
@@ -704,6 +705,9 @@ FZ_BWD_CASES = [
     (1, 1, 2, 128, 64, torch.bfloat16, True, False, True),
     (2, 130, 2, 64, 128, torch.bfloat16, True, True, True),
     (1, 300, 1, 128, 64, torch.bfloat16, False, False, False),
+    # value expansion dv = 2 dk on the matrix cores
+    (1, 150, 2, 128, 256, torch.bfloat16, True, True, False),
+    (2, 70, 1, 64, 256, torch.bfloat16, False, True, True),
 ]
 
 
