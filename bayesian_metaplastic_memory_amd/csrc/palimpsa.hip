@@ -2398,15 +2398,16 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
 //     dLoss/dl_s = e^{Lam} <G_E, S_0> + sum_{r<s} k_r . gkE_r
 //                  + sum_{t>=s} (q_t . gq_t - k_t . gkI_t)
 // (gkE, gkI: the G_E and the in-chunk parts of gk).
-// The chunk boundaries come from the chunks' own contributions
+// The chunk boundaries follow from the chunks' own contributions
 //     dS_c = sum_s e^{Lam - L_s} w_s k_s^T,   dG_c = sum_t e^{L_t} gy_t q_t^T
-// by the scans S_0(c+1) = e^{Lam_c} S_0(c) + dS_c and G_E(c-1) = e^{Lam_c} G_E(c) + dG_c.
-// fzb_local_kernel forms dS_c, dG_c (all chunks at once), fzb_scan_kernel runs
-// both scans entry by entry, fzb_grad_kernel forms the gradients of every
-// chunk at once, fzb_head_kernel sums gA and gI_prior over the batch.
+// as S_0(c+1) = e^{Lam_c} S_0(c) + dS_c and G_E(c-1) = e^{Lam_c} G_E(c) + dG_c.
+// fzb_state_kernel walks the chunks in order for both (the state forward, the
+// adjoint backward, side by side), fzb_grad_kernel forms the gradients of
+// every chunk at once, fzb_head_kernel sums gA and gI_prior over the batch.
 //
 // Products take bf16 operands with fp32 accumulation (as the frozen forward);
-// the boundary matrices are handed from the scan to the gradient kernel in bf16.
+// the boundary matrices are handed from the state walk to the gradient kernel
+// in bf16.
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
@@ -2417,10 +2418,10 @@ struct FzbArgs {
     const void *gy;
     const float *A, *Ip, *mu0, *gmuT;
     float *gq, *gk, *gv, *gbeta, *gdt, *gA, *gIp, *gmu0;
-    // workspace, per (b, h, chunk): dST / S0T [DK][DV], dG / GE [DV][DK], GT [DK][DV]
-    // (bf16), lamc, pA, pI (float)
+    // workspace, per (b, h, chunk): S0T [DK][DV], GE [DV][DK], GT [DK][DV] (bf16),
+    // pA, pI (float)
     bf16_t *sT, *ge, *gT;
-    float *lamc, *pA, *pI;
+    float *pA, *pI;
     int B, T, H, nc;
     int vec_g;                            // gv and gbeta 16-byte aligned: vector stores
 };
@@ -2462,11 +2463,15 @@ __device__ inline u32x4 pack8_bf16(const float *x) {
     return u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
 }
 
-// Inclusive prefix sum L of l_t = -A dt_t over the chunk, lane = token
-// (l = 0 past the end of the sequence); every wave forms it.
-__device__ inline float fzb_lam(const FzbArgs &a, size_t seq, int t0, int lane, float Ah) {
-    const int t = t0 + lane;
-    const float l = t < a.T ? -Ah * (float)a.dt[seq + (size_t)t * a.H] : 0.f;
+// Inclusive prefix sum L of l_t = -A dt_t over the chunk, lane = token (l = 0
+// past the end of the sequence; every wave forms it), in two steps so that the
+// load can be issued early: the raw bits of dt for token t0 + lane (clamped to
+// the last token), then the scan.
+__device__ inline uint32_t fzb_dt_bits(const FzbArgs &a, size_t seq, int t0, int lane) {
+    return __builtin_bit_cast(uint16_t, a.dt[seq + (size_t)min(t0 + lane, a.T - 1) * a.H]);
+}
+__device__ inline float fzb_lam_bits(const FzbArgs &a, uint32_t bits, int t0, int lane, float Ah) {
+    const float l = t0 + lane < a.T ? -Ah * __uint_as_float(bits << 16) : 0.f;
     return wave_incl_scan(l, lane);
 }
 
@@ -2477,19 +2482,17 @@ struct FzbLds {
     static constexpr int kRK = DK + 8, kRV = DV + 8, kRP = kFbC + 8;   // row strides (bf16)
     static constexpr int kQ = 0, kK = kQ + kFbC * kRK, kG = kK + kFbC * kRK, kW = kG + kFbC * kRV;
     static constexpr int kP = kW + kFbC * kRV;            // one score matrix [64][kRP]
-    static constexpr int kLocalHalves = kP;               // fzb_local: Q, K, G, W only
     static constexpr int kGradHalves = kP + kFbC * kRP;
-    static constexpr int kLocalBytes = kLocalHalves * 2;
     static constexpr int kGradBytes = kGradHalves * 2;
     // fzb_grad's closing sums (per-wave token sums of q.gq, k.gkI, k.gkE, and
     // of gw.w and <G_E, S_0>) reuse the score matrix's space
     static_assert((3 * 4 * kFbC + 8) * 4 <= kFbC * kRP * 2, "closing sums exceed the score buffer");
 };
 
-// Stage the chunk's Q and K (bf16, rows = tokens) and gy and w scaled per
-// token by sg(t) and sw(t) (as bf16); zeros past the end of the sequence.
-template <int DK, int DV, typename TG, typename SG, typename SW>
-__device__ inline void fzb_stage(const FzbArgs &a, bf16_t *hb, size_t seq, int t0, float inv_ip, int tid, SG sg, SW sw) {
+// Stage the chunk's Q, K, gy and w = beta v / I_prior (bf16, rows = tokens);
+// zeros past the end of the sequence.
+template <int DK, int DV, typename TG>
+__device__ inline void fzb_stage(const FzbArgs &a, bf16_t *hb, size_t seq, int t0, float inv_ip, int tid) {
     using L = FzbLds<DK, DV>;
     constexpr int kPk = DK / 8, kPv = DV / 8;
     constexpr int NQ = kFbC * kPk / 256, NV = kFbC * kPv / 256;   // packets per thread
@@ -2530,7 +2533,6 @@ __device__ inline void fzb_stage(const FzbArgs &a, bf16_t *hb, size_t seq, int t
     for (int n = 0; n < NV; ++n) {
         const int p = tid + 256 * n, t = p / kPv, col = 8 * (p % kPv);
         const bool ok = t0 + t < a.T;
-        const float fg = sg(t), fw = sw(t) * inv_ip;     // (every lane calls sg, sw: they may read other lanes)
         float g[8], w[8];
         if (kGP == 1) {
 #pragma unroll
@@ -2550,197 +2552,187 @@ __device__ inline void fzb_stage(const FzbArgs &a, bf16_t *hb, size_t seq, int t
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            g[i] = ok ? g[i] * fg : 0.f;
-            w[i] = ok ? w[i] * fw : 0.f;
+            g[i] = ok ? g[i] : 0.f;
+            w[i] = ok ? w[i] * inv_ip : 0.f;
         }
         *(u32x4 *)(hb + L::kG + t * L::kRV + col) = pack8_bf16(g);
         *(u32x4 *)(hb + L::kW + t * L::kRV + col) = pack8_bf16(w);
     }
 }
 
-// One workgroup per (b, h, chunk): the chunk's contributions dS_c (stored
-// transposed, [DK][DV]) and dG_c ([DV][DK]) and its decay Lam_c.
+// The chunk-boundary states and adjoints, one workgroup per (b, h, 64 value
+// rows) and direction, walking the chunks in order: the first half of the grid
+// runs the state forward, S_0(c+1) = e^{Lam_c} S_0(c) + sum_s e^{Lam_c - L_s} w_s k_s^T
+// from mu0, writing S_0(c)^T; the second half runs the adjoint backward,
+// G_E(c-1) = e^{Lam_c} G_E(c) + sum_t e^{L_t} gy_t q_t^T from gmuT, writing G_E(c)^T
+// and (through LDS) G_E(c), and finally gmu0 = G_E(-1).  The running matrix stays
+// in fp32 MFMA accumulators: wave w owns rows 16 w.. of the workgroup's 64 and
+// all DK key channels.  Each chunk's inputs are loaded into registers while the
+// chunk before it computes.
+template <int DK, int DV>
+struct FzsLds {
+    static constexpr int kRK = DK + 8, kRW = 64 + 8;     // row strides (bf16)
+    static constexpr int kK = 0;                          // K or Q [64 tokens][DK]
+    static constexpr int kW = kK + kFbC * kRK;            // w or gy, the workgroup's rows [64 tokens][64]
+    static constexpr int kT = kW + kFbC * kRW;            // G_E transpose tile [64 rows][DK]
+    static constexpr int kBytes = (kT + 64 * kRK) * 2;
+};
+
 template <int DK, int DV, typename TG>
-__global__ __launch_bounds__(256) void fzb_local_kernel(FzbArgs a) {
-    using L = FzbLds<DK, DV>;
+__global__ __launch_bounds__(256) void fzb_state_kernel(FzbArgs a) {
+    using L = FzsLds<DK, DV>;
+    constexpr int RBH = DV / 64;                          // row blocks per head
+    constexpr int NQ = kFbC * DK / 8 / 256;               // 16-byte packets of K or Q per thread
+    constexpr int kGP = sizeof(TG) / 2;                   // 16-byte packets per 8 values of gy
     extern __shared__ float lds_f[];
     bf16_t *hb = (bf16_t *)lds_f;
-    const int bh = blockIdx.x / a.nc, c = blockIdx.x % a.nc;
+    const int n_half = a.B * a.H * RBH;
+    int wg = blockIdx.x;
+    const bool adj = wg >= n_half;                        // second half of the grid: the adjoint
+    if (adj) wg -= n_half;
+    // the row blocks of a head read the same keys or queries: keep them on one XCD
+    if (n_half % 8 == 0) wg = (wg % 8) * (n_half / 8) + wg / 8;
+    const int bh = wg / RBH, i0 = 64 * (wg % RBH);
     const int b = bh / a.H, h = bh % a.H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int m = lane & 15, g = lane >> 4;
     const size_t seq = (size_t)b * a.T * a.H + h;
-    const int t0 = c * kFbC;
     const float Ah = a.A[h], inv_ip = 1.f / a.Ip[h];
-    const float Lt = fzb_lam(a, seq, t0, lane, Ah);
-    const float Lam = wave_read(Lt, 63);
-    if (tid == 0) a.lamc[blockIdx.x] = Lam;
-    // gy scaled by e^{L_t}, w by e^{Lam - L_t} (both <= 1)
-    fzb_stage<DK, DV, TG>(a, hb, seq, t0, inv_ip, tid,
-                          [&](int t) { return __expf(__shfl(Lt, t, 64)); },
-                          [&](int t) { return __expf(Lam - __shfl(Lt, t, 64)); });
-    __syncthreads();
-    const size_t cb = (size_t)blockIdx.x;
-    // dS[i][j] = sum_s wd[s][i] k[s][j]: D rows i, columns j; stored as dS^T[j][i..i+3]
-    for (int ib = w; ib < DV / 16; ib += 4) {
-        const bf16x8_t a0 = lds_trfrag(hb + L::kW, L::kRV, 0, 16 * ib, lane);
-        const bf16x8_t a1 = lds_trfrag(hb + L::kW, L::kRV, 32, 16 * ib, lane);
-#pragma unroll 2
-        for (int jb = 0; jb < DK / 16; ++jb) {
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-            acc = mfma16(a0, lds_trfrag(hb + L::kK, L::kRK, 0, 16 * jb, lane), acc);
-            acc = mfma16(a1, lds_trfrag(hb + L::kK, L::kRK, 32, 16 * jb, lane), acc);
-            const int j = 16 * jb + (lane & 15), i = 16 * ib + 4 * (lane >> 4);
-            *(uint2 *)(a.sT + (cb * DK + j) * DV + i) = pack4_bf16(acc);
-        }
-    }
-    // dG[i][j] = sum_t gd[t][i] q[t][j]: D rows j, columns i; stored as dG[i][j..j+3]
-    for (int jb = w; jb < DK / 16; jb += 4) {
-        const bf16x8_t a0 = lds_trfrag(hb + L::kQ, L::kRK, 0, 16 * jb, lane);
-        const bf16x8_t a1 = lds_trfrag(hb + L::kQ, L::kRK, 32, 16 * jb, lane);
-#pragma unroll 2
-        for (int ib = 0; ib < DV / 16; ++ib) {
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-            acc = mfma16(a0, lds_trfrag(hb + L::kG, L::kRV, 0, 16 * ib, lane), acc);
-            acc = mfma16(a1, lds_trfrag(hb + L::kG, L::kRV, 32, 16 * ib, lane), acc);
-            const int i = 16 * ib + (lane & 15), j = 16 * jb + 4 * (lane >> 4);
-            *(uint2 *)(a.ge + (cb * DV + i) * DK + j) = pack4_bf16(acc);
-        }
-    }
-}
-
-// The scans over the chunks, entry by entry.  A workgroup owns a 64 x 64 tile
-// of one head's state (value rows i_blk.., key channels j_blk..; 16 entries per
-// thread), so that each thread moves 32 contiguous bytes and each row of the
-// tile is 128 contiguous bytes in both the row-major and the transposed arrays.
-// The adjoint runs in reverse with each thread on 16 consecutive key channels
-// of one row: G_E(c) is written in place of dG_c and, through LDS, transposed
-// into GT; the adjoint before the first chunk is gmu0.  The state runs forward
-// with each thread on 16 consecutive rows of one key channel, so that dS_c^T is
-// read and S_0(c)^T written in place directly.  Loads run kFbPre chunks ahead
-// of the arithmetic (a ring of registers indexed at compile time).
-constexpr int kFbPre = 4;
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void fzb_scan_kernel(FzbArgs a) {
-    constexpr int kTiles = (DV / 64) * (DK / 64);
-    constexpr int kTS = 64 + 8, kFS = 64 + 4;          // LDS transpose tile: [64][kTS] bf16 or [64][kFS] fp32
-    __shared__ float tile_f[64 * kFS];
-    bf16_t *tile = (bf16_t *)tile_f;
-    const int bh = blockIdx.x / kTiles, tix = blockIdx.x % kTiles;
-    const int i_blk = 64 * (tix / (DK / 64)), j_blk = 64 * (tix % (DK / 64));
-    const int tid = threadIdx.x;
-    const int ra = tid >> 2, cb16 = 16 * (tid & 3);     // row ra of the tile, entries cb16..cb16+15
-    const size_t st = (size_t)bh * DV * DK;             // this head's state in [B, H, DV, DK]
-    const size_t rm = (size_t)(i_blk + ra) * DK + j_blk + cb16;   // row-major: row i, key channels
-    const size_t tm = (size_t)(j_blk + ra) * DV + i_blk + cb16;   // transposed: key channel j, rows
-    const size_t e = (size_t)DV * DK;
-    const size_t cb0 = (size_t)bh * a.nc;
-    const int nc = a.nc;
-    auto load16f = [](const float *p, float *x) __attribute__((always_inline)) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f32x4 u = *(const f32x4 *)(p + 4 * q);
-            x[4 * q] = u[0]; x[4 * q + 1] = u[1]; x[4 * q + 2] = u[2]; x[4 * q + 3] = u[3];
-        }
-    };
-    auto ld2 = [](const bf16_t *p, u32x4 *r) __attribute__((always_inline)) {
-        r[0] = *(const u32x4 *)p;
-        r[1] = *(const u32x4 *)(p + 8);
-    };
-    auto st2 = [](bf16_t *p, const float *x) __attribute__((always_inline)) {
-        *(u32x4 *)p = pack8_bf16(x);
-        *(u32x4 *)(p + 8) = pack8_bf16(x + 8);
-    };
-    auto axpy = [](float *x, float ex, const u32x4 *d) __attribute__((always_inline)) {
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-            x[2 * n] = fmaf(ex, x[2 * n], bf_lo(d[n / 4][n % 4]));
-            x[2 * n + 1] = fmaf(ex, x[2 * n + 1], bf_hi(d[n / 4][n % 4]));
-        }
-    };
-    float g[16];
-#pragma unroll
-    for (int n = 0; n < 16; ++n) g[n] = 0.f;
-    if (a.gmuT) load16f(a.gmuT + st + rm, g);
-    u32x4 ring[kFbPre][2];
-    float lring[kFbPre];
-#pragma unroll
-    for (int u = 0; u < kFbPre; ++u) {
-        ring[u][0] = ring[u][1] = u32x4{0u, 0u, 0u, 0u};
-        lring[u] = 0.f;
-        const int c = nc - 1 - u;
-        if (c >= 0) {
-            ld2(a.ge + (cb0 + c) * e + rm, ring[u]);
-            lring[u] = a.lamc[cb0 + c];
-        }
-    }
-    for (int c0 = nc - 1; c0 >= 0; c0 -= kFbPre) {
-#pragma unroll
-        for (int u = 0; u < kFbPre; ++u) {
-            const int c = c0 - u;
-            if (c >= 0) {
-                const u32x4 d[2] = {ring[u][0], ring[u][1]};
-                const float ex = __expf(lring[u]);
-                if (c - kFbPre >= 0) {
-                    ld2(a.ge + (cb0 + c - kFbPre) * e + rm, ring[u]);
-                    lring[u] = a.lamc[cb0 + c - kFbPre];
-                }
-                st2(a.ge + (cb0 + c) * e + rm, g);
-                // transpose through LDS: tile[j - j_blk][i - i_blk]
-#pragma unroll
-                for (int n = 0; n < 16; ++n) tile[(cb16 + n) * kTS + ra] = (bf16_t)g[n];
-                __syncthreads();
-                {
-                    bf16_t *gtp = a.gT + (cb0 + c) * e + tm;
-                    *(u32x4 *)gtp = *(const u32x4 *)(tile + ra * kTS + cb16);
-                    *(u32x4 *)(gtp + 8) = *(const u32x4 *)(tile + ra * kTS + cb16 + 8);
-                }
-                __syncthreads();
-                axpy(g, ex, d);
-            }
-        }
-    }
-    if (a.gmu0) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            *(f32x4 *)(a.gmu0 + st + rm + 4 * q) = f32x4{g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]};
-    }
-    // the state: mu0 (row-major) transposed through LDS (fp32) into the second mapping
-    float sv[16];
+    const int nc = a.nc, tl = a.T - 1;
+    const size_t st = (size_t)bh * DV * DK;
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    // the running matrix, D layout: lane holds rows i0 + 16 w + 4 g + r of key channel 16 jb + m
+    f32x4 S[DK / 16];
     {
-        float x[16];
+        const float *init = adj ? a.gmuT : a.mu0;
 #pragma unroll
-        for (int n = 0; n < 16; ++n) x[n] = 0.f;
-        if (a.mu0) load16f(a.mu0 + st + rm, x);
+        for (int jb = 0; jb < DK / 16; ++jb)
 #pragma unroll
-        for (int n = 0; n < 16; ++n) tile_f[(cb16 + n) * kFS + ra] = x[n];
-        __syncthreads();
-#pragma unroll
-        for (int n = 0; n < 16; ++n) sv[n] = tile_f[ra * kFS + cb16 + n];
+            for (int r = 0; r < 4; ++r)
+                S[jb][r] = init ? init[st + (size_t)(i0 + 16 * w + 4 * g + r) * DK + 16 * jb + m] : 0.f;
     }
+    // prefetch registers, two chunks' worth: K or Q packets, and per row packet
+    // two 16-byte words, (v, beta) for the state or gy (bf16: one word, fp32: two)
+    u32x4 pk0[NQ], px0[2][2], pk1[NQ], px1[2][2];
+    uint32_t pd0 = 0, pd1 = 0;                            // dt bits of the lane's token
+    auto load = [&](int c, u32x4 (&pk)[NQ], u32x4 (&px)[2][2], uint32_t &pd) __attribute__((always_inline)) {
+        const int t0 = c * kFbC;
+        pd = fzb_dt_bits(a, seq, t0, lane);
 #pragma unroll
-    for (int u = 0; u < kFbPre; ++u) {
-        ring[u][0] = ring[u][1] = u32x4{0u, 0u, 0u, 0u};
-        lring[u] = 0.f;
-        if (u < nc) {
-            ld2(a.sT + (cb0 + u) * e + tm, ring[u]);
-            lring[u] = a.lamc[cb0 + u];
+        for (int n = 0; n < NQ; ++n) {
+            const int p = tid + 256 * n, t = p / (DK / 8), col = 8 * (p % (DK / 8));
+            const size_t o = (seq + (size_t)min(t0 + t, tl) * a.H) * DK + col;
+            pk[n] = *(const u32x4 *)((adj ? a.q : a.k) + o);
         }
-    }
-    for (int c0 = 0; c0 < nc; c0 += kFbPre) {
 #pragma unroll
-        for (int u = 0; u < kFbPre; ++u) {
-            const int c = c0 + u;
-            if (c < nc) {
-                const u32x4 d[2] = {ring[u][0], ring[u][1]};
-                const float ex = __expf(lring[u]);
-                if (c + kFbPre < nc) {
-                    ld2(a.sT + (cb0 + c + kFbPre) * e + tm, ring[u]);
-                    lring[u] = a.lamc[cb0 + c + kFbPre];
-                }
-                st2(a.sT + (cb0 + c) * e + tm, sv);
-                axpy(sv, ex, d);
+        for (int n = 0; n < 2; ++n) {
+            const int p = tid + 256 * n, t = p / 8, col = 8 * (p % 8);
+            const size_t o = (seq + (size_t)min(t0 + t, tl) * a.H) * DV + i0 + col;
+            if (adj) {
+                px[n][0] = *(const u32x4 *)((const TG *)a.gy + o);
+                px[n][1] = kGP == 2 ? *(const u32x4 *)((const TG *)a.gy + o + 4) : z;
+            } else {
+                px[n][0] = *(const u32x4 *)(a.v + o);
+                px[n][1] = a.beta ? *(const u32x4 *)(a.beta + o) : z;
             }
         }
+    };
+    auto commit = [&](int c, float Lt, float Lam, const u32x4 (&pk)[NQ], const u32x4 (&px)[2][2])
+                      __attribute__((always_inline)) {
+        const int t0 = c * kFbC;
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            const int p = tid + 256 * n, t = p / (DK / 8), col = 8 * (p % (DK / 8));
+            *(u32x4 *)(hb + L::kK + t * L::kRK + col) = (t0 + t < a.T) ? pk[n] : z;
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int p = tid + 256 * n, t = p / 8, col = 8 * (p % 8);
+            const bool ok = t0 + t < a.T;
+            const float lt = __shfl(Lt, t, 64);
+            float x[8];
+            if (adj) {
+                const float f = __expf(lt);                       // gy scaled by e^{L_t}
+                if (kGP == 1) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) { x[2 * i] = bf_lo(px[n][0][i]); x[2 * i + 1] = bf_hi(px[n][0][i]); }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        x[i] = __uint_as_float(px[n][0][i]);
+                        x[4 + i] = __uint_as_float(px[n][1][i]);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[i] = ok ? x[i] * f : 0.f;
+            } else {
+                const float f = __expf(Lam - lt) * inv_ip;        // w = beta v / I_prior scaled by e^{Lam - L_t}
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v0 = bf_lo(px[n][0][i]), v1 = bf_hi(px[n][0][i]);
+                    if (a.beta) { v0 *= bf_lo(px[n][1][i]); v1 *= bf_hi(px[n][1][i]); }
+                    x[2 * i] = ok ? v0 * f : 0.f;
+                    x[2 * i + 1] = ok ? v1 * f : 0.f;
+                }
+            }
+            *(u32x4 *)(hb + L::kW + t * L::kRW + col) = pack8_bf16(x);
+        }
+    };
+    auto step = [&](int n, u32x4 (&pk)[NQ], u32x4 (&px)[2][2], uint32_t &pd) __attribute__((always_inline)) {
+        const int c = adj ? nc - 1 - n : n;
+        const size_t cb = (size_t)bh * nc + c;
+        const float Lt = fzb_lam_bits(a, pd, c * kFbC, lane, Ah);
+        const float Lam = wave_read(Lt, 63);
+        __syncthreads();                                  // the previous chunk's reads of LDS are done
+        commit(c, Lt, Lam, pk, px);
+        __syncthreads();
+        if (n + 2 < nc) load(adj ? c - 2 : c + 2, pk, px, pd);   // two chunks ahead
+        // the boundary matrix of chunk c, before this chunk's update: S_0(c)^T or G_E(c)^T
+        {
+            bf16_t *dst = (adj ? a.gT : a.sT) + cb * DK * DV;
+            const int i = i0 + 16 * w + 4 * g;
+#pragma unroll
+            for (int jb = 0; jb < DK / 16; ++jb)
+                *(uint2 *)(dst + (size_t)(16 * jb + m) * DV + i) = pack4_bf16(S[jb]);
+            if (adj) {
+                // G_E(c) row-major: through LDS, rows of the workgroup's 64
+#pragma unroll
+                for (int jb = 0; jb < DK / 16; ++jb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        hb[L::kT + (16 * w + 4 * g + r) * L::kRK + 16 * jb + m] = (bf16_t)S[jb][r];
+            }
+        }
+        // update: S = e^{Lam} S + (rows of W or G)^T (K or Q), k = tokens
+        const float e = __expf(Lam);
+        const bf16x8_t a0 = lds_trfrag(hb + L::kW, L::kRW, 0, 16 * w, lane);
+        const bf16x8_t a1 = lds_trfrag(hb + L::kW, L::kRW, 32, 16 * w, lane);
+#pragma unroll
+        for (int jb = 0; jb < DK / 16; ++jb) {
+            f32x4 x = S[jb] * e;
+            x = mfma16(a0, lds_trfrag(hb + L::kK, L::kRK, 0, 16 * jb, lane), x);
+            S[jb] = mfma16(a1, lds_trfrag(hb + L::kK, L::kRK, 32, 16 * jb, lane), x);
+        }
+        if (adj) {
+            __syncthreads();
+            bf16_t *gep = a.ge + cb * DV * DK;
+            for (int p = tid; p < 64 * DK / 8; p += 256) {
+                const int r = p / (DK / 8), col = 8 * (p % (DK / 8));
+                *(u32x4 *)(gep + (size_t)(i0 + r) * DK + col) = *(const u32x4 *)(hb + L::kT + r * L::kRK + col);
+            }
+        }
+    };
+    if (nc > 0) load(adj ? nc - 1 : 0, pk0, px0, pd0);
+    if (nc > 1) load(adj ? nc - 2 : 1, pk1, px1, pd1);
+    for (int n = 0; n < nc; n += 2) {
+        step(n, pk0, px0, pd0);
+        if (n + 1 < nc) step(n + 1, pk1, px1, pd1);
+    }
+    if (adj && a.gmu0) {
+#pragma unroll
+        for (int jb = 0; jb < DK / 16; ++jb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a.gmu0[st + (size_t)(i0 + 16 * w + 4 * g + r) * DK + 16 * jb + m] = S[jb][r];
     }
 }
 
@@ -2762,9 +2754,10 @@ __global__ __launch_bounds__(256, 2) void fzb_grad_kernel(FzbArgs a) {
     const size_t seq = (size_t)b * a.T * a.H + h;
     const int t0 = c * kFbC;
     const float Ah = a.A[h], inv_ip = 1.f / a.Ip[h];
-    const float Lt = fzb_lam(a, seq, t0, lane, Ah);     // L of token `lane`
+    const uint32_t dtb = fzb_dt_bits(a, seq, t0, lane);   // issued before the staging loads
+    fzb_stage<DK, DV, TG>(a, hb, seq, t0, inv_ip, tid);
+    const float Lt = fzb_lam_bits(a, dtb, t0, lane, Ah);  // L of token `lane`
     const float Lam = wave_read(Lt, 63);
-    fzb_stage<DK, DV, TG>(a, hb, seq, t0, inv_ip, tid, [](int) { return 1.f; }, [](int) { return 1.f; });
 
     // The output blocks of wave w: first its NI value blocks ib = w + 4 x (gw;
     // A operand G_E rows 16 ib), then for each of its NJ key blocks jb = w + 4 x
@@ -3280,11 +3273,11 @@ palimpsa_status launch_bwd_fz_d(int dk, const FwdArgs &fa, const BwdArgs &ba, co
 
 // Workspace of the matrix-core frozen backward (per (b, h, chunk), 256-byte
 // aligned sections): S_0^T and G_E^T [DK][DV] and G_E [DV][DK] in bf16, and the
-// chunk's Lam, gA and gw . w sums in float.  It is never larger
+// chunk's gA and gw . w sums in float.  It is never larger
 // than plan_bwd_ws for the same sizes (checked by the caller).
 struct FzbWs {
     bf16_t *sT, *ge, *gT;
-    float *lamc, *pA, *pI;
+    float *pA, *pI;
     size_t bytes;
 };
 FzbWs plan_fzb_ws(void *base, int B, int T, int H, int dk, int dv) {
@@ -3296,11 +3289,11 @@ FzbWs plan_fzb_ws(void *base, int B, int T, int H, int dk, int dv) {
         return o;
     };
     const size_t o_s = take(bhc * e * 2), o_g = take(bhc * e * 2), o_t = take(bhc * e * 2);
-    const size_t o_l = take(bhc * 4), o_a = take(bhc * 4), o_i = take(bhc * 4);
+    const size_t o_a = take(bhc * 4), o_i = take(bhc * 4);
     char *c = (char *)base;
     FzbWs w;
     w.sT = (bf16_t *)(c + o_s); w.ge = (bf16_t *)(c + o_g); w.gT = (bf16_t *)(c + o_t);
-    w.lamc = (float *)(c + o_l); w.pA = (float *)(c + o_a); w.pI = (float *)(c + o_i);
+    w.pA = (float *)(c + o_a); w.pI = (float *)(c + o_i);
     w.bytes = off;
     return w;
 }
@@ -3311,14 +3304,11 @@ palimpsa_status launch_fzb(const FzbArgs &a, hipStream_t s) {
     static_assert(L::kGradBytes <= 160 * 1024, "frozen backward staging exceeds the CU's LDS");
     const size_t bhc = (size_t)a.B * a.H * a.nc;
     (void)hipGetLastError();
-    if (bhc > 0) {
-        auto k1 = fzb_local_kernel<DK, DV, TG>;
-        if (hipFuncSetAttribute((const void *)k1, hipFuncAttributeMaxDynamicSharedMemorySize, L::kLocalBytes) != hipSuccess)
-            return PALIMPSA_ERR_HIP;
-        hipLaunchKernelGGL(k1, dim3((unsigned)bhc), dim3(256), L::kLocalBytes, s, a);
+    {
+        using LS = FzsLds<DK, DV>;
+        hipLaunchKernelGGL((fzb_state_kernel<DK, DV, TG>), dim3((unsigned)(2 * (size_t)a.B * a.H * (DV / 64))), dim3(256),
+                           LS::kBytes, s, a);
     }
-    hipLaunchKernelGGL((fzb_scan_kernel<DK, DV>), dim3((unsigned)((size_t)a.B * a.H * (DV / 64) * (DK / 64))), dim3(256), 0,
-                       s, a);
     if (bhc > 0) {
         auto k3 = fzb_grad_kernel<DK, DV, TG>;
         if (hipFuncSetAttribute((const void *)k3, hipFuncAttributeMaxDynamicSharedMemorySize, L::kGradBytes) != hipSuccess)
@@ -3523,7 +3513,7 @@ palimpsa_status palimpsa_bwd_frozen(const void *q, const void *k, const void *v,
         fa.gq = gq; fa.gk = gk; fa.gv = gv; fa.gbeta = beta ? gbeta : nullptr; fa.gdt = gdt;
         fa.gA = gA; fa.gIp = gIp; fa.gmu0 = gmu0;
         fa.sT = fw.sT; fa.ge = fw.ge; fa.gT = fw.gT;
-        fa.lamc = fw.lamc; fa.pA = fw.pA; fa.pI = fw.pI;
+        fa.pA = fw.pA; fa.pI = fw.pI;
         fa.B = B; fa.T = T; fa.H = H; fa.nc = (T + kFbC - 1) / kFbC;
         fa.vec_g = aligned_to(gv, 16) && (!beta || aligned_to(gbeta, 16));
         return gy_dtype == PALIMPSA_BF16 ? launch_fzb_d<bf16_t>(dk, dv, fa, s) : launch_fzb_d<float>(dk, dv, fa, s);
