@@ -236,7 +236,7 @@ def frozen_extra(torch, pm, w, g, steps):
 def frozen_backward_extra(torch, pm, workloads, w, g, steps):
     """palimpsa_bwd_frozen (backward of the frozen-importance recurrence) on the
     same workload, timed as one call.  bf16 inputs with d = 64 or 128 take the
-    chunked matrix-core form (chunk contributions, scan over chunks, per-chunk
+    chunked matrix-core form (state and adjoint walk over the chunks, per-chunk
     gradients, batch sums); its roofline is HBM, over the bytes the call must
     move (inputs and gradients; the chunk-boundary states it passes between its
     kernels are extra traffic)."""
@@ -264,7 +264,7 @@ def frozen_backward_extra(torch, pm, workloads, w, g, steps):
                          if w.name.startswith("layer760m") else None,
                          "algorithmic_bytes": alg,
                          "chunk_boundary_bytes": boundary,
-                         "scope": "whole call (4 kernels)"}}
+                         "scope": "whole call (3 kernels)"}}
 
 
 def blockdiag_extra(torch, pm, w, g, steps):
