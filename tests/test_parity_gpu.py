@@ -734,6 +734,49 @@ def test_bwd_frozen_bf16_inputs_fp32_upstream_gradient():
     _compare_bwd_frozen(got, _bwd_frozen_ref(inp, gr, mu0=mu0), False, 2e-2, inp)
 
 
+def test_bwd_frozen_unaligned_value_gradients_and_mixed_dtypes():
+    """gv and gbeta only 4-byte aligned (the matrix-core path's scalar stores),
+    and float32 inputs with a bf16 upstream gradient (the float32 walk)."""
+    w = workloads.WORKLOADS[0].with_(B=1, H=2, dk=128, dv=128, dtype=torch.bfloat16, A_mode="logspace16")
+    T = 90
+    _announce("bwd frozen unaligned gv/gbeta", T=T)
+    inp = workloads.make_inputs(w, T=T, seed=41)
+    gr = workloads.upstream_grads(1, T, 2, 128, 128, torch.bfloat16, seed=41)
+    n = T * 2 * 128
+    out = {name: torch.empty(n + 1, dtype=torch.float32, device=DEV)[1:].view(1, T, 2, 128) for name in ("gv", "gbeta")}
+    assert out["gv"].data_ptr() % 16 != 0
+    g = to_device(inp, DEV)
+    got = _pm().bwd_frozen(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"],
+                           gr["gy"].to(DEV), gmuT=gr["gmuT"].to(DEV), out=out)
+    torch.cuda.synchronize()
+    _compare_bwd_frozen(got, _bwd_frozen_ref(inp, gr), False, 2e-2, inp)
+    # float32 inputs, bf16 gy: the float32 walk
+    w32 = w.with_(dtype=torch.float32, dk=64, dv=64)
+    inp32 = workloads.make_inputs(w32, T=T, seed=42)
+    gr16 = workloads.upstream_grads(1, T, 2, 64, 64, torch.bfloat16, seed=42)
+    _announce("bwd frozen fp32 in, bf16 gy", T=T)
+    _compare_bwd_frozen(_run_bwd_frozen(inp32, gr16), _bwd_frozen_ref(inp32, gr16), False, TOL_BWD)
+
+
+def test_bwd_frozen_matrix_core_agrees_with_float32_walk():
+    """The same bf16-representable inputs through both paths (bf16 tensors take
+    the matrix cores, their float32 copies the float32 walk): the two agree to
+    the matrix-core path's bar."""
+    w = workloads.WORKLOADS[0].with_(B=2, H=2, dk=64, dv=128, dtype=torch.bfloat16, A_mode="logspace16")
+    T = 100
+    _announce("bwd frozen: matrix cores vs float32 walk", T=T)
+    inp = workloads.make_inputs(w, T=T, seed=43)
+    mu0 = workloads.random_state(2, 2, 128, 64, inp["I_prior"], seed=43)[0]
+    gr = workloads.upstream_grads(2, T, 2, 128, 64, torch.bfloat16, seed=43)
+    inp32 = {k_: (x.float() if isinstance(x, torch.Tensor) and x.dtype == torch.bfloat16 else x) for k_, x in inp.items()}
+    gr32 = {k_: (x.float() if isinstance(x, torch.Tensor) else x) for k_, x in gr.items()}
+    a16 = _run_bwd_frozen(inp, gr, mu0=mu0)
+    a32 = _run_bwd_frozen(inp32, gr32, mu0=mu0)
+    for n_ in FZ_BWD_NAMES:
+        if n_ not in ("gA", "gIp"):
+            assert_close("bf16 path vs fp32 " + n_, a16[n_], a32[n_], 2e-2)
+
+
 def test_bwd_frozen_matrix_core_empty_sequence():
     w = workloads.WORKLOADS[0].with_(B=2, H=3, dk=128, dv=64, dtype=torch.bfloat16)
     _announce("bwd frozen bf16 T=0", B=2, H=3, dk=128, dv=64)
