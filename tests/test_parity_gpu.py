@@ -931,7 +931,9 @@ def test_training_forward_layer760m_matches_plain_forward_and_backward():
 # ---------------------------------------------------------------------------
 
 DV_SHAPES = [(128, 256, torch.float32), (128, 256, torch.bfloat16), (64, 48, torch.float32),
-             (32, 16, torch.float32), (128, 512, torch.bfloat16), (64, 176, torch.float32)]
+             (32, 16, torch.float32), (128, 512, torch.bfloat16), (64, 176, torch.float32),
+             # the widest value dimension the path takes
+             (128, 1024, torch.bfloat16), (32, 1024, torch.float32)]
 
 
 @pytest.mark.parametrize("dk,dv,dtype", DV_SHAPES)
@@ -1016,7 +1018,7 @@ def test_per_entry_prior_forward_step_backward(dk, dv, state):
     _compare_bwd(got, _bwd_ref(inp, gr), TOL_BWD)
 
 
-@pytest.mark.parametrize("dv", [256, 192])
+@pytest.mark.parametrize("dv", [256, 192, 1024])
 def test_frozen_value_expansion(dv):
     w = workloads.WORKLOADS[0].with_(B=1, H=3, dk=128, dv=dv, dtype=torch.bfloat16, A_mode="logspace16")
     _announce("frozen dv", B=1, H=3, T=130, dk=128, dv=dv)
@@ -1101,6 +1103,10 @@ WIDE_CASES = [
     (1, 2, 66, 1024, 80, torch.bfloat16, False),   # ten 8-row workgroups, 33 chunks
     (1, 1, 0, 512, 16, torch.float32, True),       # empty sequence: the state is copied through
     (2, 1, 0, 2048, 32, torch.float32, False),     # empty sequence from the default state
+    # the widest value dimensions the wide path takes
+    (1, 1, 12, 256, 1024, torch.float32, True),
+    (1, 1, 6, 512, 4096, torch.bfloat16, False),
+    (1, 1, 4, 2048, 4096, torch.float32, True),
 ]
 
 
