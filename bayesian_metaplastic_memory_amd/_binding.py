@@ -59,6 +59,8 @@ def load_library() -> ctypes.CDLL:
             lib.palimpsa_bwd_workspace_size.restype = sz
             lib.palimpsa_fwd_blockdiag.argtypes = [vp] * 5 + [fp] * 4 + [vp, fp, fp] + [i] * 8 + [vp]
             lib.palimpsa_fwd_blockdiag.restype = i
+            lib.palimpsa_step_blockdiag.argtypes = [vp] * 5 + [fp] * 4 + [vp] + [i] * 7 + [vp]
+            lib.palimpsa_step_blockdiag.restype = i
             lib.palimpsa_status_string.argtypes = [i]
             lib.palimpsa_status_string.restype = ctypes.c_char_p
             lib.palimpsa_version.argtypes = []
@@ -463,3 +465,41 @@ def fwd_blockdiag(q, k, v, beta, dt, A, I_prior, block: int = 2, mu0=None, P0=No
     if st != OK:
         raise PalimpsaError(st, "palimpsa_fwd_blockdiag")
     return y, muT, PT
+
+
+def step_blockdiag(q, k, v, beta, dt, A, I_prior, mu, P, block: int = 2, out_dtype=None, y=None):
+    """One decode token of the block-diagonal-precision path; updates ``mu``
+    ``[B, H, dv, dk]`` and ``P`` ``[B, H, dv, dk/2, 2, 2]`` in place and returns
+    ``y`` ``[B, H, dv]``."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, dk]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    in_dtype = q.dtype
+    if in_dtype not in _DTYPES:
+        raise ValueError("unsupported input dtype %s" % in_dtype)
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    if out_dtype not in _DTYPES:
+        raise ValueError("unsupported output dtype %s" % out_dtype)
+    for t, name, shape in ((k, "k", (B, H, dk)), (v, "v", (B, H, dv)), (beta, "beta", (B, H, dv)), (dt, "dt", (B, H))):
+        _check(t, name, shape, in_dtype, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(I_prior, "I_prior", (H,), torch.float32, dev)
+    nb = dk // block if block > 0 else 0
+    _check(mu, "mu", (B, H, dv, dk), torch.float32, dev)
+    _check(P, "P", (B, H, dv, nb, block, block), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _check(y, "y", (B, H, dv), out_dtype, dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.palimpsa_step_blockdiag(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(dt), _ptr(A), _ptr(I_prior),
+                                         _ptr(mu), _ptr(P), _ptr(y), B, H, dk, dv, int(block),
+                                         _DTYPES[in_dtype], _DTYPES[out_dtype], _stream_handle(dev))
+    if st != OK:
+        raise PalimpsaError(st, "palimpsa_step_blockdiag")
+    return y

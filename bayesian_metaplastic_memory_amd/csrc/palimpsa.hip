@@ -3011,6 +3011,76 @@ __global__ __launch_bounds__(64) void fzb_head_kernel(const float *pA, const flo
     }
 }
 
+// One decode token of the block-diagonal-precision recurrence (2x2 blocks along
+// the key axis), in place on the state (mu, P), as the block-diagonal forward
+// runs it for one token: per block of key channels (2j, 2j+1) of value row i,
+//     h   = P mu                               (the natural parameter before the token)
+//     P'  = alpha P + (1 - alpha) I_prior Id + beta_i k k^T   (on the block)
+//     h'  = alpha h + beta_i v_i k,   mu' = P'^{-1} h',   y_i = sum mu' . q
+// Each thread owns 4 key channels (two blocks) of one row; a row's threads sum
+// its readout.
+struct Bd2StepArgs {
+    const void *q, *k, *v, *beta, *dt;
+    const float *A, *Ip;
+    float *mu, *P;      // mu [B, H, dv, dk]; P [B, H, dv, dk/2, 2, 2]
+    void *y;
+    int H, dv;
+    long long rows;     // B * H * dv
+};
+
+template <int DK, typename TIn, typename TOut>
+__global__ __launch_bounds__(kStepThreads) void bd2_step_kernel(Bd2StepArgs a) {
+    constexpr int kTPR = DK / 4;                           // threads per value row
+    constexpr int kRowsPerBlock = kStepThreads / kTPR;
+    const int tid = threadIdx.x;
+    const long long row = (long long)blockIdx.x * kRowsPerBlock + tid / kTPR;
+    const int j0 = (tid % kTPR) * 4;
+    // rows past the end are clamped (and not stored): every lane of a row group
+    // takes part in the reduction
+    const bool valid = row < a.rows;
+    const long long r = valid ? row : a.rows - 1;
+    const long long bh = r / a.dv;
+    const int i = (int)(r % a.dv);
+    const int h = (int)(bh % a.H);
+    const TIn *qp = (const TIn *)a.q + bh * DK + j0;
+    const TIn *kp = (const TIn *)a.k + bh * DK + j0;
+    const float bt = io<TIn>::to_f32(((const TIn *)a.beta)[bh * a.dv + i]);
+    const float bv = bt * io<TIn>::to_f32(((const TIn *)a.v)[bh * a.dv + i]);
+    const float2 gc = gate(a.A[h], io<TIn>::to_f32(((const TIn *)a.dt)[bh]), a.Ip[h]);   // alpha, (1 - alpha) I_prior
+    float qq[4], kk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { qq[e] = io<TIn>::to_f32(qp[e]); kk[e] = io<TIn>::to_f32(kp[e]); }
+    f32x4 *mup = (f32x4 *)(a.mu + r * DK + j0);
+    f32x4 *Pp = (f32x4 *)(a.P + (r * DK + j0) * 2);        // two blocks of (p00, p01, p10, p11)
+    const f32x4 mu4 = __builtin_nontemporal_load(mup);
+    const f32x4 Pa = __builtin_nontemporal_load(Pp), Pb = __builtin_nontemporal_load(Pp + 1);
+    float mun[4], Pn[8], acc = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const f32x4 Pq = blk ? Pb : Pa;
+        const float p00 = Pq[0], p01 = Pq[1], p11 = Pq[3];
+        const float m0 = mu4[2 * blk], m1 = mu4[2 * blk + 1], k0 = kk[2 * blk], k1 = kk[2 * blk + 1];
+        const float h0 = fmaf(p00, m0, p01 * m1), h1 = fmaf(p01, m0, p11 * m1);
+        const float n00 = fmaf(gc.x, p00, fmaf(bt, k0 * k0, gc.y));
+        const float n11 = fmaf(gc.x, p11, fmaf(bt, k1 * k1, gc.y));
+        const float n01 = fmaf(gc.x, p01, bt * (k0 * k1));
+        const float g0 = fmaf(gc.x, h0, bv * k0), g1 = fmaf(gc.x, h1, bv * k1);
+        const float inv = 1.f / fmaf(n00, n11, -n01 * n01);
+        mun[2 * blk] = fmaf(n11, g0, -n01 * g1) * inv;
+        mun[2 * blk + 1] = fmaf(n00, g1, -n01 * g0) * inv;
+        acc = fmaf(mun[2 * blk], qq[2 * blk], fmaf(mun[2 * blk + 1], qq[2 * blk + 1], acc));
+        Pn[4 * blk] = n00; Pn[4 * blk + 1] = n01; Pn[4 * blk + 2] = n01; Pn[4 * blk + 3] = n11;
+    }
+    if (valid) {
+        __builtin_nontemporal_store(f32x4{mun[0], mun[1], mun[2], mun[3]}, mup);
+        __builtin_nontemporal_store(f32x4{Pn[0], Pn[1], Pn[2], Pn[3]}, Pp);
+        __builtin_nontemporal_store(f32x4{Pn[4], Pn[5], Pn[6], Pn[7]}, Pp + 1);
+    }
+    const float yv = group_sum<kTPR>(acc);
+    if (valid && tid % kTPR == 0)
+        ((TOut *)a.y)[r] = io<TOut>::from_f32(yv);
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -3401,6 +3471,55 @@ palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void 
     if (bf_in) return launch_bd2_d<bf16_t, float>(a, dk, s);
     if (bf_out) return launch_bd2_d<float, bf16_t>(a, dk, s);
     return launch_bd2_d<float, float>(a, dk, s);
+}
+
+palimpsa_status palimpsa_step_blockdiag(const void *q, const void *k, const void *v, const void *beta,
+                                        const void *dt, const float *A, const float *I_prior, float *mu, float *P,
+                                        void *y, int B, int H, int dk, int dv, int block,
+                                        palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, void *stream) {
+    if (!q || !k || !v || !beta || !dt || !A || !I_prior || !mu || !P || !y)
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || dk <= 0 || dv <= 0 || block <= 0 || !dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (block != 2 || !head_ok(dk) || !dv_ok(dv))
+        return PALIMPSA_ERR_UNSUPPORTED;
+    if (!aligned_to(mu, 16) || !aligned_to(P, 16))
+        return PALIMPSA_ERR_ALIGNMENT;
+    const size_t in_sz = in_dtype == PALIMPSA_BF16 ? 2 : 4, out_sz = out_dtype == PALIMPSA_BF16 ? 2 : 4;
+    const void *in_ptrs[] = {q, k, v, beta, dt};
+    for (const void *p : in_ptrs)
+        if (!aligned_to(p, in_sz)) return PALIMPSA_ERR_ALIGNMENT;
+    if (!aligned_to(A, 4) || !aligned_to(I_prior, 4) || !aligned_to(y, out_sz)) return PALIMPSA_ERR_ALIGNMENT;
+    const long long rows = (long long)B * H * dv;
+    if (rows * dk > (1LL << 46))
+        return PALIMPSA_ERR_UNSUPPORTED;
+    Bd2StepArgs a;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.dt = dt;
+    a.A = A; a.Ip = I_prior; a.mu = mu; a.P = P; a.y = y;
+    a.H = H; a.dv = dv; a.rows = rows;
+    const int rows_per_block = kStepThreads / (dk / 4);
+    const long long blocks = (rows + rows_per_block - 1) / rows_per_block;
+    if (blocks > 0x7fffffffLL) return PALIMPSA_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf_in = in_dtype == PALIMPSA_BF16, bf_out = out_dtype == PALIMPSA_BF16;
+    (void)hipGetLastError();
+#define PALIMPSA_BD2_STEP_LAUNCH(DK_, TI, TO) \
+    hipLaunchKernelGGL((bd2_step_kernel<DK_, TI, TO>), dim3((unsigned)blocks), dim3(kStepThreads), 0, s, a)
+#define PALIMPSA_BD2_STEP_TYPES(DK_)                                          \
+    do {                                                                      \
+        if (bf_in && bf_out) PALIMPSA_BD2_STEP_LAUNCH(DK_, bf16_t, bf16_t);   \
+        else if (bf_in) PALIMPSA_BD2_STEP_LAUNCH(DK_, bf16_t, float);         \
+        else if (bf_out) PALIMPSA_BD2_STEP_LAUNCH(DK_, float, bf16_t);        \
+        else PALIMPSA_BD2_STEP_LAUNCH(DK_, float, float);                     \
+    } while (0)
+    switch (dk) {
+    case 32: PALIMPSA_BD2_STEP_TYPES(32); break;
+    case 64: PALIMPSA_BD2_STEP_TYPES(64); break;
+    default: PALIMPSA_BD2_STEP_TYPES(128); break;
+    }
+#undef PALIMPSA_BD2_STEP_TYPES
+#undef PALIMPSA_BD2_STEP_LAUNCH
+    return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
 }
 
 size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv, int flags) {

@@ -150,6 +150,36 @@ def decode_extra(torch, pm, workloads, steps):
                          "traffic": load_traffic("step_kernel_decode_B64_H32_d128_traffic.json")}}
 
 
+def blockdiag_decode_extra(torch, pm, workloads, steps):
+    """Decode step of the 2x2 block-diagonal path at B=64, H=32, d=128: mu and
+    the precision blocks (12 bytes per state entry) read and written per step."""
+    w = workloads.WORKLOADS[3]
+    dev = torch.device("cuda:0")
+    A, Ip = (x.to(dev) for x in workloads.head_constants(w))
+    mu0, P0 = workloads.random_block_state(w.B, w.H, w.dv, w.dk, 2, Ip.cpu(), seed=7)
+    mu, P = mu0.to(dev), P0.to(dev)
+    d = {n: x.to(dev) for n, x in workloads.decode_inputs(w, 0).items()}
+    y = torch.empty(w.B, w.H, w.dv, dtype=w.dtype, device=dev)
+    fn = lambda: pm.step_blockdiag(d["q"], d["k"], d["v"], d["beta"], d["dt"], A, Ip, mu, P, y=y)
+    per_graph = 16                       # as decode_extra: a captured graph of 16 steps, replayed
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            fn()
+    _, per = time_launches(graph.replay, max(2, steps // per_graph), 3, torch)
+    avg_s = sum(per) / len(per) / 1e3 / per_graph
+    state_bytes = 2 * 12 * w.B * w.H * w.dv * w.dk
+    in_bytes = 2 * w.B * w.H * (2 * w.dk + 2 * w.dv + 1) + 2 * w.B * w.H * w.dv
+    return {"workload": "2x2 block-diagonal decode B=64 H=32 d_k=d_v=128, bf16 inputs, fp32 state",
+            "tokens_per_s": w.B / avg_s, "us_per_step": avg_s * 1e6,
+            "timing": "HIP graph of 16 steps, replayed",
+            "roofline": {"bound": "hbm", "achieved": (state_bytes + in_bytes) / avg_s / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": (state_bytes + in_bytes) / avg_s / 1e9 / HBM_PEAK_GBS, "traffic": None}}
+
+
 def backward_extra(torch, pm, workloads, w, g, steps):
     """palimpsa_bwd on the same workload: checkpoint pass, backward kernel and
     the three finishing kernels, timed as one call."""
@@ -396,6 +426,7 @@ def main():
         out["frozen"] = frozen_extra(torch, pm, w, g, max(20, args.steps))
         out["frozen_backward"] = frozen_backward_extra(torch, pm, workloads, w, g, max(5, args.steps // 5))
         out["blockdiag"] = blockdiag_extra(torch, pm, w, g, max(20, args.steps // 2))
+        out["blockdiag_decode"] = blockdiag_decode_extra(torch, pm, workloads, max(64, args.steps))
         out["recurrent_shape"] = [fig7_extra(torch, pm, workloads, dev, D, 5) for D in (512, 2048)]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads or w.B * w.H)

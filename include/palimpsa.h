@@ -371,6 +371,34 @@ palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void 
                                        int B, int T, int H, int dk, int dv, int block,
                                        palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, void *stream);
 
+/*
+ * One decode token of the block-diagonal-precision recurrence (2x2 blocks),
+ * in place on the state (recurrent inference for the path above): per value
+ * row i and key block (2j, 2j+1), the block's natural parameter h = P mu is
+ * carried through the token as palimpsa_fwd_blockdiag carries it,
+ *
+ *     P'  = alpha P + (1 - alpha) I_prior[h] Id + beta[i] k k^T,
+ *     h'  = alpha P mu + beta[i] v[i] k,   mu' = P'^{-1} h',   y[i] = sum_j mu' . q
+ *
+ *   q, k      [B, H, dk]     in_dtype
+ *   v, beta   [B, H, dv]     in_dtype
+ *   dt        [B, H]         in_dtype
+ *   A, I_prior [H]           float32
+ *   mu        [B, H, dv, dk] float32, read and overwritten
+ *   P         [B, H, dv, dk/2, 2, 2] float32 precision blocks, read and
+ *             overwritten (entry [1][0] is not read; it is written equal to [0][1])
+ *   y         [B, H, dv]     out_dtype
+ *
+ * dk in {32, 64, 128}, dv a multiple of 16 up to 1024, block == 2 (else
+ * PALIMPSA_ERR_UNSUPPORTED).  mu and P must be 16-byte aligned.  Each block is
+ * solved with a float32 division by its determinant, so the step's results
+ * match palimpsa_fwd_blockdiag over the same token up to float32 rounding.
+ */
+palimpsa_status palimpsa_step_blockdiag(const void *q, const void *k, const void *v, const void *beta,
+                                        const void *dt, const float *A, const float *I_prior, float *mu, float *P,
+                                        void *y, int B, int H, int dk, int dv, int block,
+                                        palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *palimpsa_status_string(int status);
 

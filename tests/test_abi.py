@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("palimpsa_fwd_chunked", "palimpsa_fwd_workspace_size", "palimpsa_fwd_frozen",
               "palimpsa_step", "palimpsa_bwd", "palimpsa_bwd_workspace_size", "palimpsa_bwd_frozen",
-              "palimpsa_fwd_blockdiag",
+              "palimpsa_fwd_blockdiag", "palimpsa_step_blockdiag",
               "palimpsa_status_string", "palimpsa_version"):
         assert n in names
 
@@ -302,3 +302,26 @@ BD_CASES = [
 @pytest.mark.parametrize("over,status", BD_CASES)
 def test_blockdiag_rejects_invalid_calls(lib, over, status):
     assert lib.palimpsa_fwd_blockdiag(*_bd_args(**over)) == status
+
+
+def _bd_step_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dt=FAKE, A=FAKE, Ip=FAKE, mu=FAKE, P=FAKE, y=FAKE,
+             B=2, H=3, dk=64, dv=64, block=2, ind=1, outd=1, stream=None)
+    a.update(over)
+    return [a[n] for n in ("q", "k", "v", "beta", "dt", "A", "Ip", "mu", "P", "y",
+                           "B", "H", "dk", "dv", "block", "ind", "outd", "stream")]
+
+
+BD_STEP_CASES = [
+    (dict(q=None), 1), (dict(mu=None), 1), (dict(P=None), 1), (dict(y=None), 1), (dict(beta=None), 1),
+    (dict(A=None), 1), (dict(B=0), 1), (dict(H=-1), 1), (dict(block=0), 1), (dict(ind=3), 1), (dict(outd=7), 1),
+    (dict(block=1), 2), (dict(block=4), 2), (dict(dk=48), 2), (dict(dk=256), 2), (dict(dv=24), 2),
+    (dict(mu=FAKE + 4), 3), (dict(P=FAKE + 8), 3), (dict(dt=FAKE + 1), 3), (dict(y=FAKE + 1), 3),
+    (dict(ind=0, q=FAKE + 2), 3), (dict(A=FAKE + 2), 3),
+]
+
+
+@invalid_calls
+@pytest.mark.parametrize("over,status", BD_STEP_CASES)
+def test_blockdiag_step_rejects_invalid_calls(lib, over, status):
+    assert lib.palimpsa_step_blockdiag(*_bd_step_args(**over)) == status

@@ -1086,6 +1086,51 @@ def test_blockdiag_layer760m_sampled():
     assert_close("blockdiag PT (sampled)", to_np(PT)[bs, hs][None], P_ref, TOL_F32)
 
 
+@pytest.mark.parametrize("dk,dv,dtype", [(32, 32, torch.float32), (64, 48, torch.bfloat16), (128, 128, torch.float32),
+                                         (128, 1024, torch.bfloat16)])
+def test_blockdiag_step_matches_oracle(dk, dv, dtype):
+    """One decode token from a random SPD block state against the oracle's
+    block-diagonal forward over that one token."""
+    w = workloads.WORKLOADS[0].with_(B=2, H=3, dk=dk, dv=dv, dtype=dtype, A_mode="logspace16")
+    _announce("blockdiag step", B=w.B, H=w.H, dk=dk, dv=dv, dtype=dtype)
+    inp = workloads.make_inputs(w, T=1, seed=dk + dv)
+    mu0, P0 = workloads.random_block_state(w.B, w.H, dv, dk, 2, inp["I_prior"], seed=dv)
+    d = {n: inp[n][:, 0].contiguous().to(DEV) for n in ("q", "k", "v", "beta", "dt")}
+    mu, P = mu0.to(DEV), P0.to(DEV)
+    y = _pm().step_blockdiag(d["q"], d["k"], d["v"], d["beta"], d["dt"], inp["A"].to(DEV), inp["I_prior"].to(DEV),
+                             mu, P)
+    torch.cuda.synchronize()
+    y_ref, mu_ref, P_ref = oracle.fwd_blockdiag(**{n: inp[n] for n in ("q", "k", "v", "beta", "dt", "A", "I_prior")},
+                                                block=2, mu0=mu0, P0=P0)
+    assert_close("bd step y", y, y_ref[:, 0], tol_for(dtype))
+    assert_close("bd step mu", mu, mu_ref, TOL_F32)
+    assert_close("bd step P", P, P_ref, TOL_F32)
+
+
+def test_blockdiag_steps_follow_the_forward():
+    """T decode steps from the default state reproduce the block-diagonal
+    forward's readouts and final state (up to float32 rounding: the step
+    re-forms P mu each token, the forward carries it)."""
+    w = workloads.WORKLOADS[0].with_(B=2, H=2, dk=64, dv=64, dtype=torch.float32, A_mode="logspace16")
+    T = 40
+    _announce("blockdiag steps vs forward", T=T)
+    inp = workloads.make_inputs(w, T=T, seed=77)
+    g = to_device(inp, DEV)
+    y_f, mu_f, P_f = _pm().fwd_blockdiag(*gpu_args(g), block=2)
+    mu = torch.zeros(w.B, w.H, w.dv, w.dk, device=DEV)
+    P = (g["I_prior"].view(1, w.H, 1, 1, 1, 1) * torch.eye(2, device=DEV)).expand(w.B, w.H, w.dv, w.dk // 2, 2, 2)
+    P = P.contiguous()
+    ys = []
+    for t in range(T):
+        ys.append(_pm().step_blockdiag(g["q"][:, t].contiguous(), g["k"][:, t].contiguous(), g["v"][:, t].contiguous(),
+                                       g["beta"][:, t].contiguous(), g["dt"][:, t].contiguous(), g["A"], g["I_prior"],
+                                       mu, P))
+    torch.cuda.synchronize()
+    assert_close("bd steps y", torch.stack(ys, 1), y_f, 1e-5)
+    assert_close("bd steps mu", mu, mu_f, 1e-5)
+    assert_close("bd steps P", P[..., 0, 1], P_f[..., 0, 1], 1e-5)
+
+
 # ---------------------------------------------------------------------------
 # heads as wide as the model (the pages' recurrent-kernel measurement, Fig. 7):
 # dk in {256, 512, 1024, 2048}
