@@ -177,7 +177,8 @@ def blockdiag_decode_extra(torch, pm, workloads, steps):
             "timing": "HIP graph of 16 steps, replayed",
             "roofline": {"bound": "hbm", "achieved": (state_bytes + in_bytes) / avg_s / 1e9,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": (state_bytes + in_bytes) / avg_s / 1e9 / HBM_PEAK_GBS, "traffic": None}}
+                         "frac": (state_bytes + in_bytes) / avg_s / 1e9 / HBM_PEAK_GBS,
+                         "traffic": load_traffic("bd2_step_decode_B64_H32_d128_traffic.json")}}
 
 
 def backward_extra(torch, pm, workloads, w, g, steps):
