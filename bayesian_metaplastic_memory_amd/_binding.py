@@ -422,8 +422,9 @@ def bwd_frozen(q, k, v, beta, dt, A, I_prior, gy, mu0=None, gmuT=None, want_stat
 def fwd_blockdiag(q, k, v, beta, dt, A, I_prior, block: int = 2, mu0=None, P0=None, out_dtype=None,
                   y=None, muT=None, PT=None, write_state: bool = True):
     """Forward with the precision kept block-diagonal along the key axis
-    (``block`` = 2).  Returns ``(y, muT, PT)`` with ``PT`` ``[B, H, dv, dk/2,
-    2, 2]``; ``mu0``/``P0`` likewise (both or neither)."""
+    (``block`` = 2, or 4 with d_k of 64 or 128).  Returns ``(y, muT, PT)`` with
+    ``PT`` ``[B, H, dv, dk/block, block, block]``; ``mu0``/``P0`` likewise
+    (both or neither)."""
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
     B, T, H, dk = q.shape
@@ -469,8 +470,8 @@ def fwd_blockdiag(q, k, v, beta, dt, A, I_prior, block: int = 2, mu0=None, P0=No
 
 def step_blockdiag(q, k, v, beta, dt, A, I_prior, mu, P, block: int = 2, out_dtype=None, y=None):
     """One decode token of the block-diagonal-precision path; updates ``mu``
-    ``[B, H, dv, dk]`` and ``P`` ``[B, H, dv, dk/2, 2, 2]`` in place and returns
-    ``y`` ``[B, H, dv]``."""
+    ``[B, H, dv, dk]`` and ``P`` ``[B, H, dv, dk/block, block, block]`` in place
+    and returns ``y`` ``[B, H, dv]``."""
     if q.dim() != 3:
         raise ValueError("q must be [B, H, dk]")
     B, H, dk = q.shape

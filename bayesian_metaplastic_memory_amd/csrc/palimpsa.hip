@@ -1584,6 +1584,207 @@ __global__ __launch_bounds__(kThreads) void bd2_fwd_kernel(BdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// block-diagonal precision, 4x4 blocks
+// ---------------------------------------------------------------------------
+//
+// The same update with blocks of 4 adjacent key channels (a lane's aligned
+// 4-wide column vector is one block, so d_k in {64, 128}).  A block keeps its
+// natural parameter h (4) and the upper triangle of P (10); the readout solves
+// P mu = h by Cholesky, P = L L^T, with 4 v_rsq_f32 for the diagonal of L^-1.
+// Per block and token: 34 VALU for the update, 36 VALU + 4 rsq for the solve,
+// 4 for the readout.
+
+// Solve P x = h for a symmetric positive definite 4x4 P given by its upper
+// triangle p = (p00 p01 p02 p03 p11 p12 p13 p22 p23 p33).
+__device__ inline void spd4_solve(const float *p, const float *h, float *x) {
+    const float r0 = __builtin_amdgcn_rsqf(p[0]);
+    const float l10 = p[1] * r0, l20 = p[2] * r0, l30 = p[3] * r0;
+    const float r1 = __builtin_amdgcn_rsqf(fmaf(-l10, l10, p[4]));
+    const float l21 = fmaf(-l20, l10, p[5]) * r1, l31 = fmaf(-l30, l10, p[6]) * r1;
+    const float r2 = __builtin_amdgcn_rsqf(fmaf(-l21, l21, fmaf(-l20, l20, p[7])));
+    const float l32 = fmaf(-l31, l21, fmaf(-l30, l20, p[8])) * r2;
+    const float r3 = __builtin_amdgcn_rsqf(fmaf(-l32, l32, fmaf(-l31, l31, fmaf(-l30, l30, p[9]))));
+    // L z = h, then L^T x = z
+    const float z0 = h[0] * r0;
+    const float z1 = fmaf(-l10, z0, h[1]) * r1;
+    const float z2 = fmaf(-l21, z1, fmaf(-l20, z0, h[2])) * r2;
+    const float z3 = fmaf(-l32, z2, fmaf(-l31, z1, fmaf(-l30, z0, h[3]))) * r3;
+    x[3] = z3 * r3;
+    x[2] = fmaf(-l32, x[3], z2) * r2;
+    x[1] = fmaf(-l31, x[3], fmaf(-l21, x[2], z1)) * r1;
+    x[0] = fmaf(-l30, x[3], fmaf(-l20, x[2], fmaf(-l10, x[1], z0))) * r0;
+}
+
+// One token's update of a 4-block: P = alpha P + c Id + beta k k^T, h = alpha h + (beta v) k.
+__device__ inline void bd4_update(float *p, float *hh, const float *kk, const float *k2, float alpha, float c,
+                                  float bt, float bv) {
+    p[0] = fmaf(alpha, p[0], fmaf(bt, k2[0], c));
+    p[4] = fmaf(alpha, p[4], fmaf(bt, k2[1], c));
+    p[7] = fmaf(alpha, p[7], fmaf(bt, k2[2], c));
+    p[9] = fmaf(alpha, p[9], fmaf(bt, k2[3], c));
+    p[1] = fmaf(alpha, p[1], bt * (kk[0] * kk[1]));
+    p[2] = fmaf(alpha, p[2], bt * (kk[0] * kk[2]));
+    p[3] = fmaf(alpha, p[3], bt * (kk[0] * kk[3]));
+    p[5] = fmaf(alpha, p[5], bt * (kk[1] * kk[2]));
+    p[6] = fmaf(alpha, p[6], bt * (kk[1] * kk[3]));
+    p[8] = fmaf(alpha, p[8], bt * (kk[2] * kk[3]));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hh[e] = fmaf(alpha, hh[e], bv * kk[e]);
+}
+
+template <int DK, int C, typename TOut>
+__device__ inline void bd4_chunk(const float *buf, int left, float *h, float (*P)[10], int row_local, int g,
+                                 TOut *yrow, size_t ystride) {
+    using LT = LaneTile<DK>;
+    const float *cbase = buf + LT::col(g, 0, 0);
+    const float *rbase = buf + C * Stage<DK>::kColFloats + 2 * row_local;
+    int goff = C * (Stage<DK>::kColFloats + Stage<DK>::kRowFloats);
+    asm volatile("" : "+v"(goff));
+    const float *gbase = buf + goff;
+#pragma unroll 1
+    for (int grp = 0; grp < C / kGroup; ++grp) {
+        const float *cg = cbase + grp * kGroup * Stage<DK>::kColFloats;
+        const float *rg = rbase + grp * kGroup * Stage<DK>::kRowFloats;
+        const float *gg = gbase + grp * kGroup * 2;
+        float part[kGroup];
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            const float2 gc = *(const float2 *)(gg + 2 * u);                          // alpha, c
+            const float2 rb = *(const float2 *)(rg + u * Stage<DK>::kRowFloats);      // beta, beta*v
+            const float *ct = cg + u * Stage<DK>::kColFloats;
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < LT::kNVec; ++m) {
+                float kk[4], k2[4], qq[4], mu[4];
+                const int c0 = kLanesPerRow * 4 * m;
+                vecf<4>::ld(ct + c0, kk);
+                vecf<4>::ld(ct + DK + c0, k2);
+                vecf<4>::ld(ct + 2 * DK + c0, qq);
+                bd4_update(P[m], h + 4 * m, kk, k2, gc.x, gc.y, rb.x, rb.y);
+                spd4_solve(P[m], h + 4 * m, mu);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = fmaf(mu[e], qq[e], acc);
+            }
+            part[u] = acc;
+        }
+        const float yv = row16_transpose_sum(part, g);
+        const int tt = grp * kGroup + g;
+        if (tt < left)
+            yrow[(size_t)tt * ystride] = io<TOut>::from_f32(yv);
+    }
+}
+
+// Same grid, staging and state I/O as bd2_fwd_kernel; P0 / PT are [B, H, dv, dk/4, 4, 4]
+// (the upper triangle is read; PT is written in full, symmetric).
+template <int DK, int C, typename TIn, typename TOut>
+__global__ __launch_bounds__(kThreads) void bd4_fwd_kernel(BdArgs a) {
+    using LT = LaneTile<DK>;
+    static_assert(LT::kVec == 4, "a lane's column vectors must be whole 4-blocks");
+    constexpr int NB = LT::kNVec;                        // 4-blocks per lane
+    extern __shared__ float lds[];
+    float *buf0 = lds;
+    float *buf1 = lds + C * Stage<DK>::kTokFloats;
+    const int rb_per_head = a.dv / kRowsPerWG;
+    int wg = blockIdx.x;
+    if (a.xcd_remap) {
+        const int per_xcd = a.nwg / 8;
+        wg = (wg % 8) * per_xcd + wg / 8;
+    }
+    const int bh = wg / rb_per_head;
+    const int row0 = (wg % rb_per_head) * kRowsPerWG;
+    const int b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane & (kLanesPerRow - 1);
+    const int row_local = wave * kRowsPerWave + (lane >> 4);
+    const int row = row0 + row_local;
+    const float A = a.A[h], Ip = a.Ip[h];
+    constexpr int kUp[10] = {0, 1, 2, 3, 5, 6, 7, 10, 11, 15};   // upper triangle in a row-major 4x4 block
+
+    // state: h = P mu per entry, the upper triangle of P per 4-block
+    float hv[4 * NB], P[NB][10];
+    const size_t srow = ((size_t)bh * a.dv + row) * DK;      // entry (b, h, row, 0)
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+        const int col = LT::col(g, m, 0);                     // the block's first column
+        if (a.mu0) {
+            const float *pb = a.P0 + (srow + col) * 4;          // block (col / 4): 16 floats
+            float full[16], mu[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) vecf<4>::ld(pb + 4 * q4, full + 4 * q4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mu[e] = a.mu0[srow + col + e];
+#pragma unroll
+            for (int x = 0; x < 10; ++x) P[m][x] = full[kUp[x]];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                // h = P mu with P symmetric from its upper triangle
+                float acc = 0.f;
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) acc = fmaf(full[r < cc ? 4 * r + cc : 4 * cc + r], mu[cc], acc);
+                hv[4 * m + r] = acc;
+            }
+        } else {
+#pragma unroll
+            for (int x = 0; x < 10; ++x) P[m][x] = (x == 0 || x == 4 || x == 7 || x == 9) ? Ip : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hv[4 * m + e] = 0.f;
+        }
+    }
+
+    const size_t seq = (size_t)b * a.T * a.H + h;
+    const TIn *kseq = (const TIn *)a.k + seq * DK;
+    const TIn *qseq = (const TIn *)a.q + seq * DK;
+    const TIn *vseq = (const TIn *)a.v + seq * a.dv + row0;
+    const TIn *bseq = (const TIn *)a.beta + seq * a.dv + row0;
+    const TIn *dseq = (const TIn *)a.dt + seq;
+    const size_t kq_tok = (size_t)a.H * DK, vb_tok = (size_t)a.H * a.dv;
+    const size_t ystride = (size_t)a.H * a.dv;
+    TOut *ybase = (TOut *)a.y + seq * a.dv + row;
+    const int nchunks = (a.T + C - 1) / C;
+    Stager<DK, C, TIn, true> st;
+    if (nchunks > 0) {
+        st.load(kseq, qseq, vseq, bseq, dseq, a.T, a.H, a.dv, tid);
+        st.commit(buf0, A, Ip, tid, false);
+        __syncthreads();
+    }
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * C;
+        const bool more = c + 1 < nchunks;
+        if (more) {
+            const size_t tn = (size_t)(t0 + C);
+            st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
+                    dseq + tn * a.H, a.T - (t0 + C), a.H, a.dv, tid);
+        }
+        bd4_chunk<DK, C, TOut>((c & 1) ? buf1 : buf0, a.T - t0, hv, P, row_local, g,
+                               ybase + (size_t)t0 * ystride, ystride);
+        if (more) st.commit((c & 1) ? buf0 : buf1, A, Ip, tid, false);
+        __syncthreads();
+    }
+    if (a.muT) {
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+            const int col = LT::col(g, m, 0);
+            float mu[4];
+            if (a.T == 0 && a.mu0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mu[e] = a.mu0[srow + col + e];   // copied through exactly
+            } else {
+                spd4_solve(P[m], hv + 4 * m, mu);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.muT[srow + col + e] = mu[e];
+            const float *p = P[m];
+            float *pb = a.PT + (srow + col) * 4;
+            *(float4 *)pb = make_float4(p[0], p[1], p[2], p[3]);
+            *(float4 *)(pb + 4) = make_float4(p[1], p[4], p[5], p[6]);
+            *(float4 *)(pb + 8) = make_float4(p[2], p[5], p[7], p[8]);
+            *(float4 *)(pb + 12) = make_float4(p[3], p[6], p[8], p[9]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // wide heads (d_k >= 512): one value row per wave
 // ---------------------------------------------------------------------------
 //
@@ -3081,6 +3282,62 @@ __global__ __launch_bounds__(kStepThreads) void bd2_step_kernel(Bd2StepArgs a) {
         ((TOut *)a.y)[r] = io<TOut>::from_f32(yv);
 }
 
+// The same decode token with 4x4 blocks: a thread's 4 key channels are one
+// block (P [B, H, dv, dk/4, 4, 4], upper triangle read, written in full).
+template <int DK, typename TIn, typename TOut>
+__global__ __launch_bounds__(kStepThreads) void bd4_step_kernel(Bd2StepArgs a) {
+    constexpr int kTPR = DK / 4;
+    constexpr int kRowsPerBlock = kStepThreads / kTPR;
+    const int tid = threadIdx.x;
+    const long long row = (long long)blockIdx.x * kRowsPerBlock + tid / kTPR;
+    const int j0 = (tid % kTPR) * 4;
+    const bool valid = row < a.rows;
+    const long long r = valid ? row : a.rows - 1;
+    const long long bh = r / a.dv;
+    const int i = (int)(r % a.dv);
+    const int h = (int)(bh % a.H);
+    const TIn *qp = (const TIn *)a.q + bh * DK + j0;
+    const TIn *kp = (const TIn *)a.k + bh * DK + j0;
+    const float bt = io<TIn>::to_f32(((const TIn *)a.beta)[bh * a.dv + i]);
+    const float bv = bt * io<TIn>::to_f32(((const TIn *)a.v)[bh * a.dv + i]);
+    const float2 gc = gate(a.A[h], io<TIn>::to_f32(((const TIn *)a.dt)[bh]), a.Ip[h]);
+    float qq[4], kk[4], k2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        qq[e] = io<TIn>::to_f32(qp[e]);
+        kk[e] = io<TIn>::to_f32(kp[e]);
+        k2[e] = kk[e] * kk[e];
+    }
+    f32x4 *mup = (f32x4 *)(a.mu + r * DK + j0);
+    f32x4 *Pp = (f32x4 *)(a.P + (r * DK + j0) * 4);        // the block's 16 floats
+    const f32x4 mu4 = __builtin_nontemporal_load(mup);
+    const f32x4 R0 = __builtin_nontemporal_load(Pp), R1 = __builtin_nontemporal_load(Pp + 1);
+    const f32x4 R2 = __builtin_nontemporal_load(Pp + 2), R3 = __builtin_nontemporal_load(Pp + 3);
+    float p[10] = {R0[0], R0[1], R0[2], R0[3], R1[1], R1[2], R1[3], R2[2], R2[3], R3[3]};
+    // h = P mu (P symmetric from its upper triangle)
+    float hh[4];
+    hh[0] = fmaf(p[0], mu4[0], fmaf(p[1], mu4[1], fmaf(p[2], mu4[2], p[3] * mu4[3])));
+    hh[1] = fmaf(p[1], mu4[0], fmaf(p[4], mu4[1], fmaf(p[5], mu4[2], p[6] * mu4[3])));
+    hh[2] = fmaf(p[2], mu4[0], fmaf(p[5], mu4[1], fmaf(p[7], mu4[2], p[8] * mu4[3])));
+    hh[3] = fmaf(p[3], mu4[0], fmaf(p[6], mu4[1], fmaf(p[8], mu4[2], p[9] * mu4[3])));
+    bd4_update(p, hh, kk, k2, gc.x, gc.y, bt, bv);
+    float mun[4];
+    spd4_solve(p, hh, mun);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(mun[e], qq[e], acc);
+    if (valid) {
+        __builtin_nontemporal_store(f32x4{mun[0], mun[1], mun[2], mun[3]}, mup);
+        __builtin_nontemporal_store(f32x4{p[0], p[1], p[2], p[3]}, Pp);
+        __builtin_nontemporal_store(f32x4{p[1], p[4], p[5], p[6]}, Pp + 1);
+        __builtin_nontemporal_store(f32x4{p[2], p[5], p[7], p[8]}, Pp + 2);
+        __builtin_nontemporal_store(f32x4{p[3], p[6], p[8], p[9]}, Pp + 3);
+    }
+    const float yv = group_sum<kTPR>(acc);
+    if (valid && tid % kTPR == 0)
+        ((TOut *)a.y)[r] = io<TOut>::from_f32(yv);
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -3422,6 +3679,15 @@ palimpsa_status launch_bd2(const BdArgs &a, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
 }
 
+template <int DK, typename TIn, typename TOut>
+palimpsa_status launch_bd4(const BdArgs &a, hipStream_t s) {
+    constexpr int C = 16;
+    const size_t lds = fwd_lds_bytes<DK, C>();
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((bd4_fwd_kernel<DK, C, TIn, TOut>), dim3(a.nwg), dim3(kThreads), lds, s, a);
+    return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
+}
+
 template <typename TIn, typename TOut>
 palimpsa_status launch_bd2_d(const BdArgs &a, int dk, hipStream_t s) {
     switch (dk) {
@@ -3430,6 +3696,13 @@ palimpsa_status launch_bd2_d(const BdArgs &a, int dk, hipStream_t s) {
     default: return launch_bd2<128, TIn, TOut>(a, s);
     }
 }
+
+template <typename TIn, typename TOut>
+palimpsa_status launch_bd_d(const BdArgs &a, int dk, int block, hipStream_t s) {
+    if (block == 4) return dk == 64 ? launch_bd4<64, TIn, TOut>(a, s) : launch_bd4<128, TIn, TOut>(a, s);
+    return launch_bd2_d<TIn, TOut>(a, dk, s);
+}
+
 
 }  // namespace
 
@@ -3446,7 +3719,7 @@ palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void 
         return PALIMPSA_ERR_INVALID_ARG;
     if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || block <= 0 || !dtype_ok(in_dtype) || !dtype_ok(out_dtype))
         return PALIMPSA_ERR_INVALID_ARG;
-    if (block != 2 || !head_ok(dk) || !dv_ok(dv))
+    if ((block != 2 && block != 4) || !head_ok(dk) || (block == 4 && dk == 32) || !dv_ok(dv))
         return PALIMPSA_ERR_UNSUPPORTED;
     const void *vec_ptrs[] = {q, k, v, beta, P0, PT};
     for (const void *p : vec_ptrs)
@@ -3467,10 +3740,10 @@ palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void 
     a.nwg = (int)nwg; a.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
     hipStream_t s = (hipStream_t)stream;
     const bool bf_in = in_dtype == PALIMPSA_BF16, bf_out = out_dtype == PALIMPSA_BF16;
-    if (bf_in && bf_out) return launch_bd2_d<bf16_t, bf16_t>(a, dk, s);
-    if (bf_in) return launch_bd2_d<bf16_t, float>(a, dk, s);
-    if (bf_out) return launch_bd2_d<float, bf16_t>(a, dk, s);
-    return launch_bd2_d<float, float>(a, dk, s);
+    if (bf_in && bf_out) return launch_bd_d<bf16_t, bf16_t>(a, dk, block, s);
+    if (bf_in) return launch_bd_d<bf16_t, float>(a, dk, block, s);
+    if (bf_out) return launch_bd_d<float, bf16_t>(a, dk, block, s);
+    return launch_bd_d<float, float>(a, dk, block, s);
 }
 
 palimpsa_status palimpsa_step_blockdiag(const void *q, const void *k, const void *v, const void *beta,
@@ -3481,7 +3754,7 @@ palimpsa_status palimpsa_step_blockdiag(const void *q, const void *k, const void
         return PALIMPSA_ERR_INVALID_ARG;
     if (B <= 0 || H <= 0 || dk <= 0 || dv <= 0 || block <= 0 || !dtype_ok(in_dtype) || !dtype_ok(out_dtype))
         return PALIMPSA_ERR_INVALID_ARG;
-    if (block != 2 || !head_ok(dk) || !dv_ok(dv))
+    if ((block != 2 && block != 4) || !head_ok(dk) || (block == 4 && dk == 32) || !dv_ok(dv))
         return PALIMPSA_ERR_UNSUPPORTED;
     if (!aligned_to(mu, 16) || !aligned_to(P, 16))
         return PALIMPSA_ERR_ALIGNMENT;
@@ -3503,8 +3776,14 @@ palimpsa_status palimpsa_step_blockdiag(const void *q, const void *k, const void
     hipStream_t s = (hipStream_t)stream;
     const bool bf_in = in_dtype == PALIMPSA_BF16, bf_out = out_dtype == PALIMPSA_BF16;
     (void)hipGetLastError();
-#define PALIMPSA_BD2_STEP_LAUNCH(DK_, TI, TO) \
-    hipLaunchKernelGGL((bd2_step_kernel<DK_, TI, TO>), dim3((unsigned)blocks), dim3(kStepThreads), 0, s, a)
+#define PALIMPSA_BD2_STEP_LAUNCH(DK_, TI, TO)                                                                   \
+    do {                                                                                                        \
+        if (block == 4)                                                                                         \
+            hipLaunchKernelGGL((bd4_step_kernel<DK_ == 32 ? 64 : DK_, TI, TO>), dim3((unsigned)blocks),         \
+                               dim3(kStepThreads), 0, s, a);                                                    \
+        else                                                                                                    \
+            hipLaunchKernelGGL((bd2_step_kernel<DK_, TI, TO>), dim3((unsigned)blocks), dim3(kStepThreads), 0, s, a); \
+    } while (0)
 #define PALIMPSA_BD2_STEP_TYPES(DK_)                                          \
     do {                                                                      \
         if (bf_in && bf_out) PALIMPSA_BD2_STEP_LAUNCH(DK_, bf16_t, bf16_t);   \

@@ -46,6 +46,11 @@ BWD_FLOPS_PER_UPDATE = 29
 # (33 flops) plus one v_rcp_f32 (2 slots): 11.5 slots and 16.5 flops per entry.
 BD2_SLOTS_PER_ENTRY = 11.5
 BD2_FLOPS_PER_ENTRY = 16.5
+# 4x4 blocks, per block and token: update 34 VALU (52 flops), Cholesky solve
+# 36 VALU (58 flops) plus four v_rsq_f32 (2 slots each), readout 4 FMA:
+# 82 slots and 118 flops per block, 20.5 slots and 29.5 flops per entry.
+BD4_SLOTS_PER_ENTRY = 20.5
+BD4_FLOPS_PER_ENTRY = 29.5
 
 
 def alu_peak_tflops():
@@ -316,6 +321,23 @@ def blockdiag_extra(torch, pm, w, g, steps):
                          "per_entry": "10.5 VALU + 0.5 v_rcp_f32 = 11.5 slots, 16.5 flops"}}
 
 
+def blockdiag4_extra(torch, pm, w, g, steps):
+    """palimpsa_fwd_blockdiag with 4x4 precision blocks on the same workload."""
+    y, muT, PT = pm.fwd_blockdiag(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], block=4)
+    fn = lambda: pm.fwd_blockdiag(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], block=4,
+                                  y=y, muT=muT, PT=PT)
+    _, per = time_launches(fn, steps, 5, torch)
+    avg_s = sum(per) / len(per) / 1e3
+    entries = w.B * w.H * w.T * w.dv * w.dk
+    peak = LANE_OPS_PER_S / BD4_SLOTS_PER_ENTRY * BD4_FLOPS_PER_ENTRY / 1e12
+    achieved = entries * BD4_FLOPS_PER_ENTRY / avg_s / 1e12
+    return {"workload": w.name + ", 4x4 block-diagonal precision",
+            "tokens_per_s": w.B * w.T / avg_s, "ms_per_launch": avg_s * 1e3,
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                         "frac": achieved / peak, "traffic": None,
+                         "per_entry": "18.5 VALU + 1 v_rsq_f32 = 20.5 slots, 29.5 flops"}}
+
+
 def fig7_extra(torch, pm, workloads, dev, D, steps):
     """One head as wide as the model, the shape of the pages' recurrent-kernel
     measurement (B=16, L=2048, H=1, d_k = d_v = D; bf16 inputs, fp32 state),
@@ -428,6 +450,7 @@ def main():
         out["frozen_backward"] = frozen_backward_extra(torch, pm, workloads, w, g, max(5, args.steps // 5))
         out["blockdiag"] = blockdiag_extra(torch, pm, w, g, max(20, args.steps // 2))
         out["blockdiag_decode"] = blockdiag_decode_extra(torch, pm, workloads, max(64, args.steps))
+        out["blockdiag4"] = blockdiag4_extra(torch, pm, w, g, max(10, args.steps // 5))
         out["recurrent_shape"] = [fig7_extra(torch, pm, workloads, dev, D, 5) for D in (512, 2048)]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads or w.B * w.H)

@@ -352,18 +352,21 @@ palimpsa_status palimpsa_bwd_frozen(const void *q, const void *k, const void *v,
  * with P kept block-diagonal along the key axis (blocks of `block` adjacent
  * key channels; the entries between blocks are dropped at every token, as
  * Eq. (5) drops every off-diagonal entry).  block == 1 is palimpsa_fwd_chunked;
- * this entry point implements block == 2.
+ * this entry point implements block == 2 and block == 4.
  *
  *   q, k, v, beta, dt, A, I_prior, y   as palimpsa_fwd_chunked (per-head prior)
  *   mu0       [B, H, dv, dk] float32 initial mean, and
- *   P0        [B, H, dv, dk/2, 2, 2] float32 initial precision blocks (symmetric;
- *             entry [1][0] is not read); both NULL: mu0 = 0, P0 = I_prior Id
- *   muT, PT   the final state in the same layouts, or both NULL to skip
+ *   P0        [B, H, dv, dk/block, block, block] float32 initial precision
+ *             blocks (symmetric positive definite; only the upper triangle is
+ *             read); both NULL: mu0 = 0, P0 = I_prior Id
+ *   muT, PT   the final state in the same layouts (PT written in full,
+ *             symmetric), or both NULL to skip
  *
- * dk in {32, 64, 128}, dv a multiple of 16 up to 1024, block == 2 (else
- * PALIMPSA_ERR_UNSUPPORTED).  q, k, v, beta, P0 and PT must be 16-byte
- * aligned.  Arithmetic float32 (each 2x2 block solved with a reciprocal of its
- * determinant); T == 0 copies the state through.
+ * block == 2 with dk in {32, 64, 128}, or block == 4 with dk in {64, 128}; dv a
+ * multiple of 16 up to 1024 (else PALIMPSA_ERR_UNSUPPORTED).  q, k, v, beta,
+ * P0 and PT must be 16-byte aligned.  Arithmetic float32: each 2x2 block is
+ * solved with a reciprocal of its determinant, each 4x4 block by Cholesky
+ * (v_rsq_f32 for the diagonal); T == 0 copies the state through.
  */
 palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void *v, const void *beta,
                                        const void *dt, const float *A, const float *I_prior,
@@ -372,7 +375,7 @@ palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void 
                                        palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, void *stream);
 
 /*
- * One decode token of the block-diagonal-precision recurrence (2x2 blocks),
+ * One decode token of the block-diagonal-precision recurrence (2x2 or 4x4 blocks),
  * in place on the state (recurrent inference for the path above): per value
  * row i and key block (2j, 2j+1), the block's natural parameter h = P mu is
  * carried through the token as palimpsa_fwd_blockdiag carries it,
@@ -385,14 +388,15 @@ palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void 
  *   dt        [B, H]         in_dtype
  *   A, I_prior [H]           float32
  *   mu        [B, H, dv, dk] float32, read and overwritten
- *   P         [B, H, dv, dk/2, 2, 2] float32 precision blocks, read and
- *             overwritten (entry [1][0] is not read; it is written equal to [0][1])
+ *   P         [B, H, dv, dk/block, block, block] float32 precision blocks, read
+ *             (upper triangle) and overwritten (in full, symmetric)
  *   y         [B, H, dv]     out_dtype
  *
- * dk in {32, 64, 128}, dv a multiple of 16 up to 1024, block == 2 (else
- * PALIMPSA_ERR_UNSUPPORTED).  mu and P must be 16-byte aligned.  Each block is
- * solved with a float32 division by its determinant, so the step's results
- * match palimpsa_fwd_blockdiag over the same token up to float32 rounding.
+ * block == 2 with dk in {32, 64, 128}, or block == 4 with dk in {64, 128}; dv a
+ * multiple of 16 up to 1024 (else PALIMPSA_ERR_UNSUPPORTED).  mu and P must be
+ * 16-byte aligned.  A 2x2 block is solved with a float32 division by its
+ * determinant, a 4x4 block by Cholesky, so the step's results match
+ * palimpsa_fwd_blockdiag over the same token up to float32 rounding.
  */
 palimpsa_status palimpsa_step_blockdiag(const void *q, const void *k, const void *v, const void *beta,
                                         const void *dt, const float *A, const float *I_prior, float *mu, float *P,

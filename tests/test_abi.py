@@ -293,7 +293,8 @@ def _bd_args(**over):
 BD_CASES = [
     (dict(q=None), 1), (dict(y=None), 1), (dict(A=None), 1), (dict(mu0=FAKE), 1), (dict(PT=None), 1),
     (dict(B=0), 1), (dict(T=-1), 1), (dict(block=0), 1), (dict(ind=4), 1),
-    (dict(block=1), 2), (dict(block=4), 2), (dict(dk=48), 2), (dict(dv=24), 2),
+    (dict(block=1), 2), (dict(block=3), 2), (dict(block=8), 2), (dict(block=4, dk=32), 2), (dict(dk=48), 2),
+    (dict(dv=24), 2),
     (dict(q=FAKE + 4), 3), (dict(PT=FAKE + 8), 3), (dict(mu0=FAKE + 2, P0=FAKE), 3), (dict(dt=FAKE + 1), 3),
 ]
 
@@ -315,7 +316,8 @@ def _bd_step_args(**over):
 BD_STEP_CASES = [
     (dict(q=None), 1), (dict(mu=None), 1), (dict(P=None), 1), (dict(y=None), 1), (dict(beta=None), 1),
     (dict(A=None), 1), (dict(B=0), 1), (dict(H=-1), 1), (dict(block=0), 1), (dict(ind=3), 1), (dict(outd=7), 1),
-    (dict(block=1), 2), (dict(block=4), 2), (dict(dk=48), 2), (dict(dk=256), 2), (dict(dv=24), 2),
+    (dict(block=1), 2), (dict(block=8), 2), (dict(block=4, dk=32), 2), (dict(dk=48), 2), (dict(dk=256), 2),
+    (dict(dv=24), 2),
     (dict(mu=FAKE + 4), 3), (dict(P=FAKE + 8), 3), (dict(dt=FAKE + 1), 3), (dict(y=FAKE + 1), 3),
     (dict(ind=0, q=FAKE + 2), 3), (dict(A=FAKE + 2), 3),
 ]

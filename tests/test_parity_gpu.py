@@ -1131,6 +1131,81 @@ def test_blockdiag_steps_follow_the_forward():
     assert_close("bd steps P", P[..., 0, 1], P_f[..., 0, 1], 1e-5)
 
 
+@pytest.mark.parametrize("dk,dv,dtype,state,T", [(64, 48, torch.float32, True, 37), (128, 128, torch.bfloat16, True, 70),
+                                                 (128, 64, torch.float32, False, 1), (64, 128, torch.bfloat16, False, 100),
+                                                 (128, 32, torch.float32, True, 0)])
+def test_blockdiag4_matches_oracle(dk, dv, dtype, state, T):
+    """4x4 precision blocks (Cholesky per block) against the oracle's block-diagonal forward."""
+    w = workloads.WORKLOADS[0].with_(B=2, H=2, dk=dk, dv=dv, dtype=dtype, A_mode="logspace16")
+    _announce("blockdiag4 fwd", B=w.B, H=w.H, T=T, dk=dk, dv=dv, dtype=dtype, state=state)
+    inp = workloads.make_inputs(w, T=T, seed=dk + dv + T + 4)
+    mu0 = P0 = None
+    if state:
+        mu0, P0 = workloads.random_block_state(w.B, w.H, dv, dk, 4, inp["I_prior"], seed=T + 4)
+    g = to_device(inp, DEV)
+    y, muT, PT = _pm().fwd_blockdiag(*gpu_args(g), block=4, mu0=None if mu0 is None else mu0.to(DEV),
+                                     P0=None if P0 is None else P0.to(DEV))
+    torch.cuda.synchronize()
+    y_ref, mu_ref, P_ref = oracle.fwd_blockdiag(**{n: inp[n] for n in ("q", "k", "v", "beta", "dt", "A", "I_prior")},
+                                                block=4, mu0=mu0, P0=P0)
+    if T > 0:
+        assert_close("blockdiag4 y", y, y_ref, tol_for(dtype))
+    assert_close("blockdiag4 muT", muT, mu_ref, TOL_F32)
+    assert_close("blockdiag4 PT", PT, P_ref, TOL_F32)
+
+
+def test_blockdiag4_layer760m_sampled():
+    w = workloads.WORKLOADS[2]
+    heads = [(3, 2), (6, 9)]
+    _announce("blockdiag4 760M layer", B=w.B, H=w.H, T=w.T, d=w.dk, sampled=heads)
+    inp = workloads.make_inputs(w)
+    g = to_device(inp, DEV)
+    y, muT, PT = _pm().fwd_blockdiag(*gpu_args(g), block=4)
+    torch.cuda.synchronize()
+    sub = oracle.select_heads(inp, heads)
+    y_ref, mu_ref, P_ref = oracle.fwd_blockdiag(**{n: sub[n] for n in ("q", "k", "v", "beta", "dt", "A", "I_prior")},
+                                                block=4)
+    bs = [b for b, _ in heads]
+    hs = [h for _, h in heads]
+    assert_close("blockdiag4 y (sampled)", to_np(y)[bs, :, hs, :].transpose(1, 0, 2)[None], y_ref, tol_for(w.dtype))
+    assert_close("blockdiag4 muT (sampled)", to_np(muT)[bs, hs][None], mu_ref, TOL_F32)
+    assert_close("blockdiag4 PT (sampled)", to_np(PT)[bs, hs][None], P_ref, TOL_F32)
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(64, 64, torch.float32), (128, 96, torch.bfloat16)])
+def test_blockdiag4_step_matches_oracle_and_forward(dk, dv, dtype):
+    """One 4x4-block decode token against the oracle, then steps against the forward."""
+    w = workloads.WORKLOADS[0].with_(B=2, H=2, dk=dk, dv=dv, dtype=dtype, A_mode="logspace16")
+    _announce("blockdiag4 step", B=w.B, H=w.H, dk=dk, dv=dv, dtype=dtype)
+    inp = workloads.make_inputs(w, T=1, seed=dk + dv + 5)
+    mu0, P0 = workloads.random_block_state(w.B, w.H, dv, dk, 4, inp["I_prior"], seed=dv + 5)
+    d = {n: inp[n][:, 0].contiguous().to(DEV) for n in ("q", "k", "v", "beta", "dt")}
+    mu, P = mu0.to(DEV), P0.to(DEV)
+    y = _pm().step_blockdiag(d["q"], d["k"], d["v"], d["beta"], d["dt"], inp["A"].to(DEV), inp["I_prior"].to(DEV),
+                             mu, P, block=4)
+    torch.cuda.synchronize()
+    y_ref, mu_ref, P_ref = oracle.fwd_blockdiag(**{n: inp[n] for n in ("q", "k", "v", "beta", "dt", "A", "I_prior")},
+                                                block=4, mu0=mu0, P0=P0)
+    assert_close("bd4 step y", y, y_ref[:, 0], tol_for(dtype))
+    assert_close("bd4 step mu", mu, mu_ref, TOL_F32)
+    assert_close("bd4 step P", P, P_ref, TOL_F32)
+    # 30 steps from the default state against the forward over the same tokens
+    T = 30
+    inp = workloads.make_inputs(w.with_(dtype=torch.float32), T=T, seed=88)
+    g = to_device(inp, DEV)
+    y_f, mu_f, P_f = _pm().fwd_blockdiag(*gpu_args(g), block=4)
+    mu = torch.zeros(w.B, w.H, dv, dk, device=DEV)
+    P = (g["I_prior"].view(1, w.H, 1, 1, 1, 1) * torch.eye(4, device=DEV)).expand(w.B, w.H, dv, dk // 4, 4, 4)
+    P = P.contiguous()
+    ys = [_pm().step_blockdiag(g["q"][:, t].contiguous(), g["k"][:, t].contiguous(), g["v"][:, t].contiguous(),
+                               g["beta"][:, t].contiguous(), g["dt"][:, t].contiguous(), g["A"], g["I_prior"], mu, P,
+                               block=4) for t in range(T)]
+    torch.cuda.synchronize()
+    assert_close("bd4 steps y", torch.stack(ys, 1), y_f, 1e-5)
+    assert_close("bd4 steps mu", mu, mu_f, 1e-5)
+    assert_close("bd4 steps P", P, P_f, 1e-5)
+
+
 # ---------------------------------------------------------------------------
 # heads as wide as the model (the pages' recurrent-kernel measurement, Fig. 7):
 # dk in {256, 512, 1024, 2048}
