@@ -334,7 +334,9 @@ def blockdiag4_extra(torch, pm, w, g, steps):
     return {"workload": w.name + ", 4x4 block-diagonal precision",
             "tokens_per_s": w.B * w.T / avg_s, "ms_per_launch": avg_s * 1e3,
             "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                         "frac": achieved / peak, "traffic": None,
+                         "frac": achieved / peak,
+                         "traffic": load_traffic("bd4_fwd_layer760m_bf16_traffic.json")
+                         if w.name.startswith("layer760m") else None,
                          "per_entry": "18.5 VALU + 1 v_rsq_f32 = 20.5 slots, 29.5 flops"}}
 
 
