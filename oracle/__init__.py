@@ -23,10 +23,10 @@ Contents
     an option that keeps only the diagonal of the precision at every token.
 ``bwd``
     The reverse-mode derivative of ``fwd`` (C oracle), for the training path.
-``fwd_blockdiag``
+``fwd_blockdiag`` / ``bwd_blockdiag``
     The Gaussian update with the precision kept block-diagonal along the key
     axis (limited cross-key correlations); block 1 is Eq. (5), block dk the
-    full update.
+    full update; and its reverse-mode derivative.
 ``fwd_mamba2_limit`` / ``bwd_mamba2_limit``
     The frozen-importance recurrence of the Mamba2 limit (slides, frame "The
     Mamba2 limit enables a gradual model upgrade", Secs. 2.3-2.4), and its
@@ -36,8 +36,9 @@ All arrays use the library's layouts: q, k ``[B, T, H, dk]``; v, beta
 ``[B, T, H, dv]``; dt ``[B, T, H]``; A, I_prior ``[H]``; state
 ``[B, H, dv, dk]``; y ``[B, T, H, dv]``.
 
-Every function here is pinned by ``tests/test_oracle_pins.py`` against the
-pages' worked examples, closed forms, limits and a brute-force posterior.
+Every function here is pinned (``tests/test_oracle_pins.py`` and the
+``test_oracle_*bwd_pins.py`` files) against the pages' worked examples,
+closed forms, limits, a brute-force posterior and finite differences.
 """
 from __future__ import annotations
 
@@ -458,6 +459,109 @@ def fwd_blockdiag(q, k, v, beta, dt, A, I_prior, block: int, mu0=None, P0=None):
             mu[b, h] = m.reshape(dv, dk)
             P[b, h] = Pb
     return y, mu, P
+
+
+def bwd_blockdiag(q, k, v, beta, dt, A, I_prior, block: int, gy, mu0=None, P0=None, gmuT=None, gPT=None):
+    """Reverse-mode derivative of ``fwd_blockdiag`` for
+    ``L = <gy, y> + <gmuT, muT> + <gPT, PT>``.
+
+    The forward in its natural parameters, per value row i and key block b
+    (slides, backup frame "dropping precision correlations changes the mean"):
+        P_t = a_t P_{t-1} + c_t Id + beta_i k_b k_b^T,   c_t = (1 - a_t) I_prior
+        h_t = a_t h_{t-1} + (beta_i v_i) k_b,            h_0 = P_0 mu0
+        mu_t = P_t^{-1} h_t,   y_t[i] = sum_b q_b . mu_t[i, b]
+    walked from t = T-1 down with (G_h, G_P) the adjoints of (h_t, P_t): the
+    readout adds w = P_t^{-1} gmu to G_h and -w mu_t^T to G_P (gmu = gy_i q_b);
+    then gk gets (beta v) G_h + beta (G_P + G_P^T) k, the row's write
+    gradient is G_h . k, beta's importance term k^T G_P k, the gate takes
+    <G_h, h_{t-1}> + <G_P, P_{t-1}> and trace(G_P), and both adjoints decay by
+    a_t.  P is treated as a full matrix (``gP0`` is the gradient with respect to
+    every entry of P0).  States are recomputed from checkpoints every
+    ceil(sqrt(T)) tokens.  Defaults ``mu0 = 0, P0 = I_prior Id``; the start state
+    then depends on I_prior, so ``gIp`` also collects trace(dL/dP0).  Returns
+    a dict of float64 arrays gq, gk, gv, gbeta, gdt, gA, gIp, gmu0, gP0."""
+    q, k, v, beta, dt, gy = (_f64(x) for x in (q, k, v, beta, dt, gy))
+    A, Ip = _f64(A), _f64(I_prior)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    bs = int(block)
+    if bs < 1 or dk % bs:
+        raise ValueError("block must divide dk")
+    nb = dk // bs
+    eye = np.eye(bs)
+    out = {n: np.zeros(x.shape) for n, x in (("gq", q), ("gk", k), ("gv", v), ("gbeta", v), ("gdt", dt))}
+    out["gA"], out["gIp"] = np.zeros(H), np.zeros(H)
+    out["gmu0"], out["gP0"] = np.zeros((B, H, dv, dk)), np.zeros((B, H, dv, nb, bs, bs))
+    seg = max(1, int(np.ceil(np.sqrt(max(T, 1)))))
+    solve = lambda M, x: np.linalg.solve(M, x[..., None])[..., 0]
+    for b in range(B):
+        for h in range(H):
+            if mu0 is None:
+                Pst = np.broadcast_to(Ip[h] * eye, (dv, nb, bs, bs)).copy()
+                m0 = np.zeros((dv, nb, bs))
+            else:
+                Pst = _f64(P0)[b, h].copy()
+                m0 = _f64(mu0)[b, h].reshape(dv, nb, bs)
+            hst = np.einsum("rnij,rnj->rni", Pst, m0)
+            gates = [_gate(A[h], dt[b, t, h]) for t in range(T)]
+
+            def step(hh, PP, t):
+                a, oma = gates[t]
+                kb = k[b, t, h].reshape(nb, bs)
+                bt = beta[b, t, h]
+                PP = a * PP + oma * Ip[h] * eye + bt[:, None, None, None] * (kb[:, :, None] * kb[:, None, :])[None]
+                hh = a * hh + (bt * v[b, t, h])[:, None, None] * kb[None]
+                return hh, PP
+
+            cks, hh, PP = [], hst.copy(), Pst.copy()
+            for t in range(T):
+                if t % seg == 0:
+                    cks.append((hh.copy(), PP.copy()))
+                hh, PP = step(hh, PP, t)
+            Gh, GP = np.zeros((dv, nb, bs)), np.zeros((dv, nb, bs, bs))
+            if gmuT is not None:
+                w = solve(PP, _f64(gmuT)[b, h].reshape(dv, nb, bs))
+                Gh += w
+                GP -= w[..., :, None] * solve(PP, hh)[..., None, :]
+            if gPT is not None:
+                GP += _f64(gPT)[b, h]
+            for s0 in (range(((T - 1) // seg) * seg, -1, -seg) if T else ()):
+                s1 = min(s0 + seg, T)
+                states = [cks[s0 // seg]]
+                for t in range(s0, s1):
+                    states.append(step(*states[-1], t))
+                for t in range(s1 - 1, s0 - 1, -1):
+                    (h_prev, P_prev), (h_t, P_t) = states[t - s0], states[t - s0 + 1]
+                    a, oma = gates[t]
+                    kb = k[b, t, h].reshape(nb, bs)
+                    qb = q[b, t, h].reshape(nb, bs)
+                    bt = beta[b, t, h]
+                    bvv = bt * v[b, t, h]
+                    mu_t = solve(P_t, h_t)
+                    out["gq"][b, t, h] += (gy[b, t, h][:, None, None] * mu_t).sum(0).reshape(dk)
+                    w = solve(P_t, gy[b, t, h][:, None, None] * qb[None])
+                    Gh += w
+                    GP -= w[..., :, None] * mu_t[..., None, :]
+                    g_bv = (Gh * kb[None]).sum((1, 2))
+                    GPs = GP + GP.swapaxes(-1, -2)
+                    out["gk"][b, t, h] += (bvv[:, None, None] * Gh).sum(0).reshape(dk)
+                    out["gk"][b, t, h] += (bt[:, None, None] * np.einsum("rnij,nj->rni", GPs, kb)).sum(0).reshape(dk)
+                    out["gv"][b, t, h] = g_bv * bt
+                    out["gbeta"][b, t, h] = g_bv * v[b, t, h] + np.einsum("rnij,ni,nj->r", GP, kb, kb)
+                    g_a = (Gh * h_prev).sum() + (GP * P_prev).sum()
+                    g_c = np.trace(GP, axis1=-2, axis2=-1).sum()
+                    u = Ip[h] * g_c - g_a
+                    out["gdt"][b, t, h] = A[h] * a * u
+                    out["gA"][h] += dt[b, t, h] * a * u
+                    out["gIp"][h] += oma * g_c
+                    Gh *= a
+                    GP *= a
+            # start state h_0 = P_0 mu0
+            out["gmu0"][b, h] = np.einsum("rnji,rnj->rni", Pst, Gh).reshape(dv, dk)
+            out["gP0"][b, h] = GP + Gh[..., :, None] * m0[..., None, :]
+            if mu0 is None:
+                out["gIp"][h] += np.trace(out["gP0"][b, h], axis1=-2, axis2=-1).sum()
+    return out
 
 
 # ---------------------------------------------------------------------------
