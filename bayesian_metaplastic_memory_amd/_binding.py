@@ -61,6 +61,11 @@ def load_library() -> ctypes.CDLL:
             lib.palimpsa_fwd_blockdiag.restype = i
             lib.palimpsa_step_blockdiag.argtypes = [vp] * 5 + [fp] * 4 + [vp] + [i] * 7 + [vp]
             lib.palimpsa_step_blockdiag.restype = i
+            lib.palimpsa_bwd_blockdiag_workspace_size.argtypes = [i] * 6
+            lib.palimpsa_bwd_blockdiag_workspace_size.restype = sz
+            lib.palimpsa_bwd_blockdiag.argtypes = ([vp] * 5 + [fp] * 4 + [vp, fp, fp] + [fp] * 9 + [i] * 6 +
+                                                   [i, i, vp, sz, vp])
+            lib.palimpsa_bwd_blockdiag.restype = i
             lib.palimpsa_status_string.argtypes = [i]
             lib.palimpsa_status_string.restype = ctypes.c_char_p
             lib.palimpsa_version.argtypes = []
@@ -504,3 +509,71 @@ def step_blockdiag(q, k, v, beta, dt, A, I_prior, mu, P, block: int = 2, out_dty
     if st != OK:
         raise PalimpsaError(st, "palimpsa_step_blockdiag")
     return y
+
+
+def bwd_blockdiag_workspace_size(B, T, H, dk, dv, block: int = 2) -> int:
+    """Bytes of workspace ``palimpsa_bwd_blockdiag`` needs (0 if unsupported)."""
+    return int(load_library().palimpsa_bwd_blockdiag_workspace_size(B, T, H, dk, dv, int(block)))
+
+
+def bwd_blockdiag(q, k, v, beta, dt, A, I_prior, gy, block: int = 2, mu0=None, P0=None, gmuT=None, gPT=None,
+                  want_state_grads: bool = True, workspace=None, out=None):
+    """Backward of ``fwd_blockdiag`` (2x2 blocks) for
+    ``L = <gy, y> + <gmuT, muT> + <gPT, PT>``.
+
+    Returns a dict of float32 gradients ``gq, gk, gv, gbeta, gdt, gA, gIp`` and,
+    if ``want_state_grads``, ``gmu0`` and ``gP0`` (the gradient for a
+    symmetric P0).  ``gmuT``/``gPT`` may be None (zero); ``out`` and
+    ``workspace`` as in ``bwd``."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    in_dtype = q.dtype
+    if in_dtype not in _DTYPES or gy.dtype not in _DTYPES:
+        raise ValueError("unsupported dtype")
+    for t, name, shape in ((k, "k", (B, T, H, dk)), (v, "v", (B, T, H, dv)), (beta, "beta", (B, T, H, dv)),
+                           (dt, "dt", (B, T, H))):
+        _check(t, name, shape, in_dtype, dev)
+    _check(gy, "gy", (B, T, H, dv), gy.dtype, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(I_prior, "I_prior", (H,), torch.float32, dev)
+    nb = dk // block if block > 0 else 0
+    pshape = (B, H, dv, nb, block, block)
+    for t, name, shape in ((mu0, "mu0", (B, H, dv, dk)), (P0, "P0", pshape), (gmuT, "gmuT", (B, H, dv, dk)),
+                           (gPT, "gPT", pshape)):
+        if t is not None:
+            _check(t, name, shape, torch.float32, dev)
+    shapes = {"gq": (B, T, H, dk), "gk": (B, T, H, dk), "gv": (B, T, H, dv), "gbeta": (B, T, H, dv),
+              "gdt": (B, T, H), "gA": (H,), "gIp": (H,)}
+    if want_state_grads:
+        shapes["gmu0"] = (B, H, dv, dk)
+        shapes["gP0"] = pshape
+    res = {}
+    for name, shape in shapes.items():
+        t = (out or {}).get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=torch.float32, device=dev)
+        _check(t, name, shape, torch.float32, dev)
+        res[name] = t
+    lib = load_library()
+    nbytes = bwd_blockdiag_workspace_size(B, T, H, dk, dv, block)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
+    nz = lambda t: _ptr(t) if t is not None and t.numel() else None
+    with torch.cuda.device(dev):
+        st = lib.palimpsa_bwd_blockdiag(
+            nz(q), nz(k), nz(v), nz(beta), nz(dt), _ptr(A), _ptr(I_prior), _ptr(mu0), _ptr(P0), nz(gy),
+            _ptr(gmuT), _ptr(gPT),
+            nz(res["gq"]), nz(res["gk"]), nz(res["gv"]), nz(res["gbeta"]), nz(res["gdt"]),
+            _ptr(res["gA"]), _ptr(res["gIp"]), _ptr(res.get("gmu0")), _ptr(res.get("gP0")),
+            B, T, H, dk, dv, int(block), _DTYPES[in_dtype], _DTYPES[gy.dtype],
+            _ptr(workspace), workspace.numel(), _stream_handle(dev))
+    if st != OK:
+        raise PalimpsaError(st, "palimpsa_bwd_blockdiag")
+    return res

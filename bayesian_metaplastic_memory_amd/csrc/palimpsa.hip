@@ -1584,6 +1584,467 @@ __global__ __launch_bounds__(kThreads) void bd2_fwd_kernel(BdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// block-diagonal precision (2x2 blocks): backward
+// ---------------------------------------------------------------------------
+//
+// Reverse mode through the 2x2 block update above, per value row and key
+// block, walking t = T-1 .. 0 with (G_h, G_P) the adjoints of (h_t, P_t).
+// Every use of P is a symmetric form, so only S = (G_P + G_P^T) / 2 matters
+// and a block carries it as (s00, s01, s11).  Per token and block:
+//   readout  mu = P^-1 h, w = P^-1 (gy_i q_b):  gq_b += gy_i mu,
+//            G_h += w,  S -= (w mu^T + mu w^T) / 2
+//   update   gk_b += (beta v)_i G_h + 2 beta_i S k_b,
+//            gbv_i += G_h . k_b,  gb_i += k_b^T S k_b (beta's precision term),
+//            da += G_h . h_{t-1} + <S, P_{t-1}>,  dc += tr S,
+//            then (G_h, S) *= alpha_t.
+// These are the exact backward's four row sums and two column sums, so its
+// finishing kernels (gq, gk; gdt; gA, gI_prior) serve unchanged.  The final
+// state's adjoint is G_h = P_T^-1 gmuT, S = sym(gPT) - sym(G_h mu_T^T); at the
+// start h_0 = P_0 mu_0 gives gmu0 = P_0 G_h and gP0 = S + sym(G_h mu0^T)
+// (the gradient for a symmetric P0), and the default start (mu0 = 0,
+// P_0 = I_prior Id) adds tr S to gI_prior.
+//
+// Passes: bd2_ckpt_kernel stores (h, P) before every 8th token; bd2_bwd_kernel
+// has bwd_kernel's structure (halves of 4 tokens replayed from the
+// checkpoint into registers, walked in reverse) with the step above.
+
+// A lane's 2x2 state: h for its KC columns, then (p00, p01, p11) per block;
+// a checkpoint pads it to whole float4s.
+template <int DK> struct Bd2Lane {
+    static constexpr int kKC = LaneTile<DK>::kCols;
+    static constexpr int kN = kKC + 3 * (kKC / 2);
+    static constexpr int kNP = (kN + 3) / 4 * 4;
+};
+
+// A workgroup's checkpoint block: float4 i of thread tid at blk + 4 (i kThreads + tid).
+template <int N, int NP>
+__device__ inline void bd2_ck_store(float *blk, int tid, const float *x) {
+#pragma unroll
+    for (int i = 0; i < NP; i += 4)
+        __builtin_nontemporal_store(f32x4{i < N ? x[i] : 0.f, i + 1 < N ? x[i + 1] : 0.f,
+                                          i + 2 < N ? x[i + 2] : 0.f, i + 3 < N ? x[i + 3] : 0.f},
+                                    (f32x4 *)(blk + 4 * ((i / 4) * kThreads + tid)));
+}
+template <int N, int NP>
+__device__ inline void bd2_ck_load(const float *blk, int tid, float *x) {
+#pragma unroll
+    for (int i = 0; i < NP; i += 4) {
+        const f32x4 v = __builtin_nontemporal_load((const f32x4 *)(blk + 4 * ((i / 4) * kThreads + tid)));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (i + j < N) x[i + j] = v[j];
+    }
+}
+
+// The lane's start state: from (mu0, P0) when given (P0's upper triangle),
+// else mu0 = 0 and P0 = I_prior Id.  srow: entry (b, h, row, 0).
+template <int DK>
+__device__ inline void bd2_start(const float *mu0, const float *P0, size_t srow, int g, float Ip, float *st) {
+    using LT = LaneTile<DK>;
+    constexpr int KC = LT::kCols;
+#pragma unroll
+    for (int m = 0; m < LT::kNVec; ++m)
+#pragma unroll
+        for (int e = 0; e < LT::kVec; e += 2) {
+            const int s = m * LT::kVec + e;
+            float *p = st + KC + 3 * (s / 2);
+            const int col = LT::col(g, m, e);
+            if (mu0) {
+                const float4 P = *(const float4 *)(P0 + (srow + col) * 2);
+                const float m0 = mu0[srow + col], m1 = mu0[srow + col + 1];
+                p[0] = P.x; p[1] = P.y; p[2] = P.w;
+                st[s] = fmaf(P.x, m0, P.y * m1);
+                st[s + 1] = fmaf(P.y, m0, P.w * m1);
+            } else {
+                p[0] = Ip; p[1] = 0.f; p[2] = Ip;
+                st[s] = 0.f; st[s + 1] = 0.f;
+            }
+        }
+}
+
+// One token's update of the lane's blocks (bd2_chunk's operations).  ct: the
+// token's staged k at ct[c], k^2 at ct[DK + c], from the lane's first column.
+template <int DK>
+__device__ inline void bd2_update(const float *ct, float alpha, float c, float beta, float bv, float *st) {
+    using LT = LaneTile<DK>;
+    constexpr int KC = LT::kCols;
+#pragma unroll
+    for (int m = 0; m < LT::kNVec; ++m) {
+        float kk[LT::kVec], k2[LT::kVec];
+        const int c0 = kLanesPerRow * LT::kVec * m;
+        vecf<LT::kVec>::ld(ct + c0, kk);
+        vecf<LT::kVec>::ld(ct + DK + c0, k2);
+#pragma unroll
+        for (int e = 0; e < LT::kVec; e += 2) {
+            const int s = m * LT::kVec + e;
+            float *p = st + KC + 3 * (s / 2);
+            p[0] = fmaf(alpha, p[0], fmaf(beta, k2[e], c));
+            p[2] = fmaf(alpha, p[2], fmaf(beta, k2[e + 1], c));
+            p[1] = fmaf(alpha, p[1], beta * (kk[e] * kk[e + 1]));
+            st[s] = fmaf(alpha, st[s], bv * kk[e]);
+            st[s + 1] = fmaf(alpha, st[s + 1], bv * kk[e + 1]);
+        }
+    }
+}
+
+struct BdBwdArgs {
+    const void *q, *k, *v, *beta, *dt, *gy;
+    const float *A, *Ip, *mu0, *P0, *gmuT, *gPT;    // P0, gPT: [B, H, dv, dk/2, 2, 2]
+    float *gv, *gbeta, *gmu0, *gP0;
+    float *ck;         // [B*H][T/8][dv/16][lane state]: (h, P) before every 8th token
+    float *pqk, *ps, *pI0;   // bwd_kernel's partials, same layouts
+    int B, T, H, dv, nsb, nwg, xcd_remap;
+};
+
+// Checkpoint pass: the forward's update without readout, staged like the
+// forward (no q), storing the state before tokens 0, 8, 16, ...
+template <int DK, typename TIn>
+__global__ __launch_bounds__(kThreads) void bd2_ckpt_kernel(BdBwdArgs a) {
+    using LT = LaneTile<DK>;
+    using L = Bd2Lane<DK>;
+    using SG = Stage<DK>;
+    constexpr int C = 16;
+    extern __shared__ float lds[];
+    const int rb_per_head = a.dv / kRowsPerWG;
+    int wg = blockIdx.x;
+    if (a.xcd_remap) {
+        const int per_xcd = a.nwg / 8;
+        wg = (wg % 8) * per_xcd + wg / 8;
+    }
+    const int bh = wg / rb_per_head, rb = wg % rb_per_head;
+    const int row0 = rb * kRowsPerWG;
+    const int b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane & (kLanesPerRow - 1);
+    const int row_local = wave * kRowsPerWave + (lane >> 4);
+    const float A = a.A[h], Ip = a.Ip[h];
+    float st[L::kN];
+    bd2_start<DK>(a.mu0, a.P0, ((size_t)bh * a.dv + row0 + row_local) * DK, g, Ip, st);
+    const size_t ck_stride = (size_t)rb_per_head * kThreads * L::kNP;
+    float *ckb = a.ck + ((size_t)bh * a.nsb * rb_per_head + rb) * (kThreads * L::kNP);
+
+    const size_t seq = (size_t)b * a.T * a.H + h;
+    const TIn *kseq = (const TIn *)a.k + seq * DK;
+    const TIn *vseq = (const TIn *)a.v + seq * a.dv + row0;
+    const TIn *bseq = (const TIn *)a.beta + seq * a.dv + row0;
+    const TIn *dseq = (const TIn *)a.dt + seq;
+    const size_t kq_tok = (size_t)a.H * DK, vb_tok = (size_t)a.H * a.dv;
+    const int nchunks = (a.T + C - 1) / C;
+    Stager<DK, C, TIn, false> sg;
+    sg.load(kseq, kseq, vseq, bseq, dseq, a.T, a.H, a.dv, tid);
+    sg.commit(lds, A, Ip, tid, false);
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * C;
+        const bool more = c + 1 < nchunks;
+        if (more) {
+            const size_t tn = (size_t)(t0 + C);
+            sg.load(kseq + tn * kq_tok, kseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
+                    dseq + tn * a.H, a.T - (t0 + C), a.H, a.dv, tid);
+        }
+        const float *buf = lds + (c & 1) * C * SG::kTokFloats;
+        const float *rows = buf + C * SG::kColFloats + 2 * row_local;
+        const float *gates = buf + C * (SG::kColFloats + SG::kRowFloats);
+#pragma unroll 2
+        for (int u = 0; u < C; ++u) {
+            if (u % kSB == 0 && (t0 + u) / kSB < a.nsb)
+                bd2_ck_store<L::kN, L::kNP>(ckb + (size_t)((t0 + u) / kSB) * ck_stride, tid, st);
+            const float2 gc = *(const float2 *)(gates + 2 * u);
+            const float2 rw = *(const float2 *)(rows + u * SG::kRowFloats);
+            bd2_update<DK>(buf + u * SG::kColFloats + LT::col(g, 0, 0), gc.x, gc.y, rw.x, rw.y, st);
+        }
+        if (more) sg.commit(lds + ((c + 1) & 1) * C * SG::kTokFloats, A, Ip, tid, false);
+        __syncthreads();
+    }
+}
+
+// One token of the reverse walk for the lane's blocks: St the state after the
+// token, Sp before it.  Updates (Gh, GS), returns the lane's row partials of
+// (gbv, gb, da, dc) and writes the wave's (gq, gk) column sums to red as
+// bwd_reverse_token does.
+template <int DK>
+__device__ inline void bd2_reverse_token(const float *buf, int e, const float *St, const float *Sp, float *Gh,
+                                         float *GS, int row_local, int g, int lane, float *red,
+                                         float &cbv, float &cb, float &s1, float &s2) {
+    using LT = LaneTile<DK>;
+    using S = BwdStage<DK>;
+    constexpr int KC = LT::kCols;
+    const float alpha = buf[S::kGate + 2 * e];
+    const float4 rw = *(const float4 *)(buf + S::kRows + e * S::kRowFloats + 4 * row_local);
+    const float b2 = 2.f * rw.x, bv = rw.y, gy = rw.w;
+    const float *ct = buf + e * S::kColFloats + LT::col(g, 0, 0);
+    float dq[KC], dk[KC];
+    cbv = 0.f; cb = 0.f; s1 = 0.f; s2 = 0.f;
+#pragma unroll
+    for (int m = 0; m < LT::kNVec; ++m) {
+        float kk[LT::kVec], qq[LT::kVec];
+        const int c0 = kLanesPerRow * LT::kVec * m;
+        vecf<LT::kVec>::ld(ct + c0, kk);
+        vecf<LT::kVec>::ld(ct + 2 * DK + c0, qq);
+#pragma unroll
+        for (int x = 0; x < LT::kVec; x += 2) {
+            const int s = m * LT::kVec + x;
+            const float *p = St + KC + 3 * (s / 2), *pp = Sp + KC + 3 * (s / 2);
+            float *gs = GS + 3 * (s / 2);
+            const float r = __builtin_amdgcn_rcpf(fmaf(p[0], p[2], -(p[1] * p[1])));
+            const float m0 = fmaf(p[2], St[s], -(p[1] * St[s + 1])) * r;
+            const float m1 = fmaf(p[0], St[s + 1], -(p[1] * St[s])) * r;
+            const float g0 = gy * qq[x], g1 = gy * qq[x + 1];
+            const float w0 = fmaf(p[2], g0, -(p[1] * g1)) * r;
+            const float w1 = fmaf(p[0], g1, -(p[1] * g0)) * r;
+            dq[s] = gy * m0;
+            dq[s + 1] = gy * m1;
+            Gh[s] += w0;
+            Gh[s + 1] += w1;
+            gs[0] = fmaf(-w0, m0, gs[0]);
+            gs[2] = fmaf(-w1, m1, gs[2]);
+            gs[1] = fmaf(-0.5f, fmaf(w0, m1, w1 * m0), gs[1]);
+            const float k0 = kk[x], k1 = kk[x + 1];
+            const float sk0 = fmaf(gs[0], k0, gs[1] * k1), sk1 = fmaf(gs[1], k0, gs[2] * k1);
+            dk[s] = fmaf(Gh[s], bv, b2 * sk0);
+            dk[s + 1] = fmaf(Gh[s + 1], bv, b2 * sk1);
+            cbv = fmaf(Gh[s], k0, fmaf(Gh[s + 1], k1, cbv));
+            cb = fmaf(sk0, k0, fmaf(sk1, k1, cb));
+            s1 = fmaf(Gh[s], Sp[s], fmaf(Gh[s + 1], Sp[s + 1], s1));
+            s1 = fmaf(gs[0], pp[0], fmaf(gs[2], pp[2], fmaf(2.f * gs[1], pp[1], s1)));
+            s2 += gs[0] + gs[2];
+            Gh[s] *= alpha;
+            Gh[s + 1] *= alpha;
+            gs[0] *= alpha;
+            gs[1] *= alpha;
+            gs[2] *= alpha;
+        }
+    }
+    bwd_scatter_qk<DK>(dq, dk, lane, g, red);
+}
+
+template <int DK, typename TIn, typename TG>
+__global__ __launch_bounds__(kThreads) void bd2_bwd_kernel(BdBwdArgs a) {
+    using LT = LaneTile<DK>;
+    using S = BwdStage<DK>;
+    using L = Bd2Lane<DK>;
+    constexpr int KC = LT::kCols, KB = KC / 2, N = L::kN;
+    extern __shared__ float lds[];
+    float *red = lds + S::kRed;
+    float *rs = lds + S::kRs;
+
+    const int rb_per_head = a.dv / kRowsPerWG;
+    int wg = blockIdx.x;
+    if (a.xcd_remap) {
+        const int per_xcd = a.nwg / 8;
+        wg = (wg % 8) * per_xcd + wg / 8;
+    }
+    const int bh = wg / rb_per_head;
+    const int rb = wg % rb_per_head;
+    const int row0 = rb * kRowsPerWG;
+    const int b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane & (kLanesPerRow - 1);
+    const int row_local = wave * kRowsPerWave + (lane >> 4);
+    const float A = a.A[h], Ip = a.Ip[h];
+    const size_t srow = ((size_t)bh * a.dv + row0 + row_local) * DK;
+    const size_t seq0 = (size_t)b * a.T * a.H + h;
+    const size_t bth = (size_t)a.B * a.T * a.H;
+    const size_t kq_tok = (size_t)a.H * DK, vb_tok = (size_t)a.H * a.dv;
+
+    float Gh[KC], GS[3 * KB];
+    // the final state's adjoint from (gmuT, gPT), given the final state st
+    auto final_adjoint = [&](const float *st) {
+#pragma unroll
+        for (int m = 0; m < LT::kNVec; ++m)
+#pragma unroll
+            for (int x = 0; x < LT::kVec; x += 2) {
+                const int s = m * LT::kVec + x;
+                const size_t o = srow + LT::col(g, m, x);
+                const float *p = st + KC + 3 * (s / 2);
+                const float gm0 = a.gmuT ? a.gmuT[o] : 0.f, gm1 = a.gmuT ? a.gmuT[o + 1] : 0.f;
+                const float4 gp = a.gPT ? *(const float4 *)(a.gPT + o * 2) : make_float4(0.f, 0.f, 0.f, 0.f);
+                const float det = fmaf(p[0], p[2], -(p[1] * p[1]));
+                const float mT0 = fmaf(p[2], st[s], -(p[1] * st[s + 1])) / det;
+                const float mT1 = fmaf(p[0], st[s + 1], -(p[1] * st[s])) / det;
+                const float w0 = fmaf(p[2], gm0, -(p[1] * gm1)) / det;
+                const float w1 = fmaf(p[0], gm1, -(p[1] * gm0)) / det;
+                float *gs = GS + 3 * (s / 2);
+                Gh[s] = w0;
+                Gh[s + 1] = w1;
+                gs[0] = fmaf(-w0, mT0, gp.x);
+                gs[2] = fmaf(-w1, mT1, gp.w);
+                gs[1] = 0.5f * ((gp.y + gp.z) - fmaf(w0, mT1, w1 * mT0));
+            }
+    };
+
+    if (a.nsb == 0) {
+        // T = 0: mu_T = mu_0 and P_T = P_0 are copied through, so are their gradients
+#pragma unroll
+        for (int m = 0; m < LT::kNVec; ++m)
+#pragma unroll
+            for (int x = 0; x < LT::kVec; x += 2) {
+                const int s = m * LT::kVec + x;
+                const size_t o = srow + LT::col(g, m, x);
+                const float4 gp = a.gPT ? *(const float4 *)(a.gPT + o * 2) : make_float4(0.f, 0.f, 0.f, 0.f);
+                float *gs = GS + 3 * (s / 2);
+                gs[0] = gp.x; gs[1] = 0.5f * (gp.y + gp.z); gs[2] = gp.w;
+                if (a.gmu0) {
+                    a.gmu0[o] = a.gmuT ? a.gmuT[o] : 0.f;
+                    a.gmu0[o + 1] = a.gmuT ? a.gmuT[o + 1] : 0.f;
+                }
+                if (a.gP0) *(float4 *)(a.gP0 + o * 2) = make_float4(gs[0], gs[1], gs[1], gs[2]);
+            }
+    } else {
+        const size_t ck_stride = (size_t)rb_per_head * kThreads * L::kNP;
+        const float *ckb = a.ck + ((size_t)bh * a.nsb * rb_per_head + rb) * (kThreads * L::kNP);
+        const TIn *kseq = (const TIn *)a.k + seq0 * DK;
+        const TIn *qseq = (const TIn *)a.q + seq0 * DK;
+        const TIn *vseq = (const TIn *)a.v + seq0 * a.dv + row0;
+        const TIn *bseq = (const TIn *)a.beta + seq0 * a.dv + row0;
+        const TG *gseq = (const TG *)a.gy + seq0 * a.dv + row0;
+        const TIn *dseq = (const TIn *)a.dt + seq0;
+        BwdStager<DK, TIn, TG> st;
+        {
+            const size_t tn = (size_t)(a.nsb - 1) * kSB;
+            st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
+                    gseq + tn * vb_tok, dseq + tn * a.H, a.T - (int)tn, a.H, a.dv, tid);
+            st.commit(lds + ((a.nsb - 1) & 1) * S::kFloats, A, Ip, tid, false);
+        }
+        float ckS[N];
+        bd2_ck_load<N, L::kNP>(ckb + (size_t)(a.nsb - 1) * ck_stride, tid, ckS);
+        __syncthreads();
+
+        for (int sb = a.nsb - 1; sb >= 0; --sb) {
+            const float *cur = lds + (sb & 1) * S::kFloats;
+            const int t0 = sb * kSB;
+            if (sb > 0) {
+                const size_t tn = (size_t)(t0 - kSB);
+                st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
+                        gseq + tn * vb_tok, dseq + tn * a.H, a.T - (int)tn, a.H, a.dv, tid);
+            }
+            auto replay = [&](int e, float *x) {
+                const float2 gc = *(const float2 *)(cur + S::kGate + 2 * e);
+                const float2 rw = *(const float2 *)(cur + S::kRows + e * S::kRowFloats + 4 * row_local);
+                bd2_update<DK>(cur + e * S::kColFloats + LT::col(g, 0, 0), gc.x, gc.y, rw.x, rw.y, x);
+            };
+            float xS[4][N];
+            float acc[16];      // this half's row partials: gbv, gb, da, dc of its 4 tokens
+            // upper half: tokens 4..7, replayed from the checkpoint
+            float mS[N];
+#pragma unroll
+            for (int i = 0; i < N; ++i) mS[i] = ckS[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) replay(e, mS);
+#pragma unroll
+            for (int e = 4; e < 8; ++e) {
+                const float *pv = e == 4 ? mS : xS[e > 4 ? e - 5 : 0];
+#pragma unroll
+                for (int i = 0; i < N; ++i) xS[e - 4][i] = pv[i];
+                replay(e, xS[e - 4]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (sb == a.nsb - 1) final_adjoint(xS[3]);   // tokens past T are neutral
+#pragma unroll
+            for (int e = 7; e >= 4; --e) {
+                bd2_reverse_token<DK>(cur, e, xS[e - 4], e == 4 ? mS : xS[e > 4 ? e - 5 : 0], Gh, GS, row_local,
+                                      g, lane, red + (e * kWaves + wave) * 2 * DK,
+                                      acc[e - 4], acc[e], acc[e + 4], acc[e + 8]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            bwd_row_sums(acc, g, rs + 4 * 4 * kRowsPerWG + row_local);
+            // lower half: tokens 0..3
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float *pv = e == 0 ? ckS : xS[e > 0 ? e - 1 : 0];
+#pragma unroll
+                for (int i = 0; i < N; ++i) xS[e][i] = pv[i];
+                replay(e, xS[e]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            float nS[N];
+            if (sb > 0) bd2_ck_load<N, L::kNP>(ckb + (size_t)(sb - 1) * ck_stride, tid, nS);
+#pragma unroll
+            for (int e = 3; e >= 0; --e) {
+                bd2_reverse_token<DK>(cur, e, xS[e], e == 0 ? ckS : xS[e > 0 ? e - 1 : 0], Gh, GS, row_local,
+                                      g, lane, red + (e * kWaves + wave) * 2 * DK,
+                                      acc[e], acc[e + 4], acc[e + 8], acc[e + 12]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            bwd_row_sums(acc, g, rs + row_local);
+            if (sb > 0) st.commit(lds + ((sb - 1) & 1) * S::kFloats, A, Ip, tid, false);
+            __syncthreads();
+            // sums over the 4 waves: this row block's partials of (gq, gk)
+            for (int n = 4 * tid; n < kSB * 2 * DK; n += 4 * kThreads) {
+                const int e = n / (2 * DK), c = n % (2 * DK);
+                const float *r0 = red + e * kWaves * 2 * DK + c;
+                const float4 v0 = *(const float4 *)r0, v1 = *(const float4 *)(r0 + 2 * DK);
+                const float4 v2 = *(const float4 *)(r0 + 4 * DK), v3 = *(const float4 *)(r0 + 6 * DK);
+                if (t0 + e < a.T)
+                    *(float4 *)(a.pqk + ((size_t)rb * bth + seq0 + (size_t)(t0 + e) * a.H) * 2 * DK + c) =
+                        make_float4((v0.x + v1.x) + (v2.x + v3.x), (v0.y + v1.y) + (v2.y + v3.y),
+                                    (v0.z + v1.z) + (v2.z + v3.z), (v0.w + v1.w) + (v2.w + v3.w));
+            }
+            // per (token, row): gv = gbv beta, gbeta = gbv v + gb; per token: (da, dc)
+            if (tid < kSB * kRowsPerWG) {
+                const int e = tid / kRowsPerWG, r = tid % kRowsPerWG;
+                const float gbv = rs[(e * 4 + 0) * kRowsPerWG + r], gb = rs[(e * 4 + 1) * kRowsPerWG + r];
+                const float4 rw = *(const float4 *)(cur + S::kRows + e * S::kRowFloats + 4 * r);
+                if (t0 + e < a.T) {
+                    const size_t o = (seq0 + (size_t)(t0 + e) * a.H) * a.dv + row0 + r;
+                    a.gv[o] = gbv * rw.x;
+                    a.gbeta[o] = fmaf(gbv, rw.z, gb);
+                }
+            } else if (tid < kSB * kRowsPerWG + 2 * kSB) {
+                const int u = tid - kSB * kRowsPerWG, e = u % kSB, qd = u / kSB;
+                const float *src = rs + (e * 4 + 2 + qd) * kRowsPerWG;
+                float v = 0.f;
+#pragma unroll
+                for (int r = 0; r < kRowsPerWG; ++r) v += src[r];
+                if (t0 + e < a.T) a.ps[((size_t)rb * bth + (size_t)bh * a.T + t0 + e) * 2 + qd] = v;
+            }
+            __syncthreads();
+            if (sb > 0) {
+#pragma unroll
+                for (int i = 0; i < N; ++i) ckS[i] = nS[i];
+            }
+        }
+        // the start state h_0 = P_0 mu_0
+#pragma unroll
+        for (int m = 0; m < LT::kNVec; ++m)
+#pragma unroll
+            for (int x = 0; x < LT::kVec; x += 2) {
+                const int s = m * LT::kVec + x;
+                const size_t o = srow + LT::col(g, m, x);
+                float *gs = GS + 3 * (s / 2);
+                float4 P = make_float4(Ip, 0.f, 0.f, Ip);
+                float m0 = 0.f, m1 = 0.f;
+                if (a.mu0) {
+                    P = *(const float4 *)(a.P0 + o * 2);
+                    m0 = a.mu0[o];
+                    m1 = a.mu0[o + 1];
+                }
+                if (a.gmu0) {
+                    a.gmu0[o] = fmaf(P.x, Gh[s], P.y * Gh[s + 1]);
+                    a.gmu0[o + 1] = fmaf(P.y, Gh[s], P.w * Gh[s + 1]);
+                }
+                gs[0] = fmaf(Gh[s], m0, gs[0]);
+                gs[2] = fmaf(Gh[s + 1], m1, gs[2]);
+                gs[1] = fmaf(0.5f, fmaf(Gh[s], m1, Gh[s + 1] * m0), gs[1]);
+                if (a.gP0) *(float4 *)(a.gP0 + o * 2) = make_float4(gs[0], gs[1], gs[1], gs[2]);
+            }
+    }
+    // this row block's sum of tr(gP0) (the default start P_0 = I_prior Id feeds gI_prior)
+    float gs = 0.f;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) gs += GS[3 * j] + GS[3 * j + 2];
+    gs = row16_sum(gs);
+    gs += __shfl_xor(gs, 16, 64);
+    gs += __shfl_xor(gs, 32, 64);
+    __syncthreads();
+    if (lane == 0) rs[wave] = gs;
+    __syncthreads();
+    if (tid == 0) a.pI0[(size_t)bh * rb_per_head + rb] = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+}
+
+// ---------------------------------------------------------------------------
 // block-diagonal precision, 4x4 blocks
 // ---------------------------------------------------------------------------
 //
@@ -3703,6 +4164,71 @@ palimpsa_status launch_bd_d(const BdArgs &a, int dk, int block, hipStream_t s) {
     return launch_bd2_d<TIn, TOut>(a, dk, s);
 }
 
+// Block-diagonal backward workspace: the checkpoints (lane states padded to
+// float4s), then bwd_kernel's partials in their layouts.
+struct BdBwdWs {
+    float *ck, *pqk, *ps, *gabh, *gibh, *pI0;
+    size_t bytes;
+};
+BdBwdWs plan_bd_bwd_ws(void *base, int B, int T, int H, int dk, int dv) {
+    const size_t nsb = (size_t)(T + kSB - 1) / kSB, nrb = (size_t)dv / kRowsPerWG;
+    const size_t bh = (size_t)B * H, bth = bh * T;
+    const size_t kc = (size_t)dk / kLanesPerRow, lane_np = (kc + 3 * (kc / 2) + 3) / 4 * 4;
+    size_t off = 0;
+    auto take = [&](size_t floats) {
+        const size_t o = off;
+        off = (off + floats * sizeof(float) + 255) / 256 * 256;
+        return o;
+    };
+    const size_t o_ck = take(bh * nsb * nrb * kThreads * lane_np);
+    const size_t o_pqk = take(nrb * bth * 2 * dk), o_ps = take(nrb * bth * 2);
+    const size_t o_ga = take(bh), o_gi = take(bh), o_pi = take(bh * nrb);
+    BdBwdWs w;
+    char *c = (char *)base;
+    w.ck = (float *)(c + o_ck); w.pqk = (float *)(c + o_pqk); w.ps = (float *)(c + o_ps);
+    w.gabh = (float *)(c + o_ga); w.gibh = (float *)(c + o_gi); w.pI0 = (float *)(c + o_pi);
+    w.bytes = off;
+    return w;
+}
+
+template <int DK, typename TIn, typename TG>
+palimpsa_status launch_bd2_bwd(const BdBwdArgs &a, const BdBwdWs &w, float *gq, float *gk, float *gdt, float *gA,
+                               float *gIp, int dt_bf16, hipStream_t s) {
+    (void)hipGetLastError();
+    const size_t ck_lds = fwd_lds_bytes<DK, 16>();
+    if (a.T > 0)
+        hipLaunchKernelGGL((bd2_ckpt_kernel<DK, TIn>), dim3(a.nwg), dim3(kThreads), ck_lds, s, a);
+    const size_t lds = (size_t)BwdStage<DK>::kTotal * sizeof(float);
+    auto kern = bd2_bwd_kernel<DK, TIn, TG>;
+    if (lds > 64 * 1024 &&
+        hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return PALIMPSA_ERR_HIP;
+    hipLaunchKernelGGL(kern, dim3(a.nwg), dim3(kThreads), lds, s, a);
+    const size_t bth = (size_t)a.B * a.T * a.H;
+    const int nrb = a.dv / kRowsPerWG;
+    if (bth > 0) {
+        const size_t n4 = bth * (2 * DK / 4);
+        hipLaunchKernelGGL(bwd_qk_kernel<DK>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                           (const float *)w.pqk, gq, gk, bth, nrb);
+    }
+    hipLaunchKernelGGL(bwd_gate_kernel, dim3(a.B * a.H), dim3(256), 0, s, (const float *)w.ps, a.dt, dt_bf16,
+                       a.A, a.Ip, 0, 0, gdt, w.gabh, w.gibh, a.B, a.T, a.H, nrb);
+    hipLaunchKernelGGL(bwd_head_kernel, dim3((a.H + 63) / 64), dim3(64), 0, s, (const float *)w.gabh,
+                       (const float *)w.gibh, (const float *)w.pI0, a.Ip, gA, gIp, a.B, a.H, nrb,
+                       a.mu0 ? 0 : 1, 0, 0);
+    return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
+}
+
+template <typename TIn, typename TG>
+palimpsa_status launch_bd2_bwd_d(int dk, const BdBwdArgs &a, const BdBwdWs &w, float *gq, float *gk, float *gdt,
+                                 float *gA, float *gIp, int dt_bf16, hipStream_t s) {
+    switch (dk) {
+    case 32: return launch_bd2_bwd<32, TIn, TG>(a, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    case 64: return launch_bd2_bwd<64, TIn, TG>(a, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    default: return launch_bd2_bwd<128, TIn, TG>(a, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    }
+}
+
 
 }  // namespace
 
@@ -3799,6 +4325,62 @@ palimpsa_status palimpsa_step_blockdiag(const void *q, const void *k, const void
 #undef PALIMPSA_BD2_STEP_TYPES
 #undef PALIMPSA_BD2_STEP_LAUNCH
     return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
+}
+
+size_t palimpsa_bwd_blockdiag_workspace_size(int B, int T, int H, int dk, int dv, int block) {
+    if (B <= 0 || H <= 0 || T < 0 || block != 2 || !head_ok(dk) || !dv_ok(dv)) return 0;
+    return plan_bd_bwd_ws(nullptr, B, T, H, dk, dv).bytes;
+}
+
+palimpsa_status palimpsa_bwd_blockdiag(const void *q, const void *k, const void *v, const void *beta,
+                                       const void *dt, const float *A, const float *I_prior,
+                                       const float *mu0, const float *P0,
+                                       const void *gy, const float *gmuT, const float *gPT,
+                                       float *gq, float *gk, float *gv, float *gbeta, float *gdt,
+                                       float *gA, float *gIp, float *gmu0, float *gP0,
+                                       int B, int T, int H, int dk, int dv, int block,
+                                       palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+    if (!A || !I_prior || !gA || !gIp || !workspace)
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (T > 0 && (!q || !k || !v || !beta || !dt || !gy || !gq || !gk || !gv || !gbeta || !gdt))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if ((mu0 == nullptr) != (P0 == nullptr))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || block <= 0 || !dtype_ok(in_dtype) ||
+        !dtype_ok(gy_dtype))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if (block != 2 || !head_ok(dk) || !dv_ok(dv))
+        return PALIMPSA_ERR_UNSUPPORTED;
+    const void *vec_ptrs[] = {q, k, v, beta, gy, P0, gPT, gP0, gq, gk, workspace};
+    for (const void *p : vec_ptrs)
+        if (p && !aligned_to(p, 16)) return PALIMPSA_ERR_ALIGNMENT;
+    const size_t in_sz = in_dtype == PALIMPSA_BF16 ? 2 : 4;
+    const void *f32_ptrs[] = {A, I_prior, gA, gIp, gv, gbeta, gdt, mu0, gmuT, gmu0};
+    for (const void *p : f32_ptrs)
+        if (p && !aligned_to(p, 4)) return PALIMPSA_ERR_ALIGNMENT;
+    if (dt && !aligned_to(dt, in_sz)) return PALIMPSA_ERR_ALIGNMENT;
+    const long long nwg = (long long)B * H * (dv / kRowsPerWG);
+    if (nwg > 0x7fffffffLL || (long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 46) ||
+        64LL * H * (dk > dv ? dk : dv) >= (1LL << 31) || (long long)B * H * 2 > 0x7fffffffLL)
+        return PALIMPSA_ERR_UNSUPPORTED;
+    const BdBwdWs w = plan_bd_bwd_ws(workspace, B, T, H, dk, dv);
+    if (workspace_bytes < w.bytes) return PALIMPSA_ERR_INVALID_ARG;
+
+    BdBwdArgs a = {};
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.dt = dt; a.gy = gy;
+    a.A = A; a.Ip = I_prior; a.mu0 = mu0; a.P0 = P0; a.gmuT = gmuT; a.gPT = gPT;
+    a.gv = gv; a.gbeta = gbeta; a.gmu0 = gmu0; a.gP0 = gP0;
+    a.ck = w.ck; a.pqk = w.pqk; a.ps = w.ps; a.pI0 = w.pI0;
+    a.B = B; a.T = T; a.H = H; a.dv = dv; a.nsb = (T + kSB - 1) / kSB;
+    a.nwg = (int)nwg; a.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf_in = in_dtype == PALIMPSA_BF16, bf_gy = gy_dtype == PALIMPSA_BF16;
+    const int dtb = bf_in ? 1 : 0;
+    if (bf_in && bf_gy) return launch_bd2_bwd_d<bf16_t, bf16_t>(dk, a, w, gq, gk, gdt, gA, gIp, dtb, s);
+    if (bf_in) return launch_bd2_bwd_d<bf16_t, float>(dk, a, w, gq, gk, gdt, gA, gIp, dtb, s);
+    if (bf_gy) return launch_bd2_bwd_d<float, bf16_t>(dk, a, w, gq, gk, gdt, gA, gIp, dtb, s);
+    return launch_bd2_bwd_d<float, float>(dk, a, w, gq, gk, gdt, gA, gIp, dtb, s);
 }
 
 size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv, int flags) {

@@ -51,6 +51,12 @@ BD2_FLOPS_PER_ENTRY = 16.5
 # 82 slots and 118 flops per block, 20.5 slots and 29.5 flops per entry.
 BD4_SLOTS_PER_ENTRY = 20.5
 BD4_FLOPS_PER_ENTRY = 29.5
+# Backward of the 2x2 path, per entry and token: one replay of the update
+# (11 VALU, 18 flops per block) and the reverse step per block (determinant
+# and solves 16 VALU + one v_rcp_f32, adjoint updates 19, gradient terms 15:
+# 50 VALU and 2 rcp slots, 72 flops): 31.5 slots and 45 flops per entry.
+BD2_BWD_SLOTS_PER_ENTRY = 31.5
+BD2_BWD_FLOPS_PER_ENTRY = 45
 
 
 def alu_peak_tflops():
@@ -340,6 +346,33 @@ def blockdiag4_extra(torch, pm, w, g, steps):
                          "per_entry": "18.5 VALU + 1 v_rsq_f32 = 20.5 slots, 29.5 flops"}}
 
 
+def blockdiag_backward_extra(torch, pm, workloads, w, g, steps):
+    """palimpsa_bwd_blockdiag (backward of the 2x2 block-diagonal path) on the
+    same workload, timed as one call (checkpoint pass, reverse walk, three
+    finishing kernels)."""
+    dev = g["q"].device
+    gr = workloads.upstream_grads(w.B, w.T, w.H, w.dv, w.dk, w.dtype, seed=2)
+    gy, gmuT = gr["gy"].to(dev), gr["gmuT"].to(dev)
+    ws = torch.empty(pm.bwd_blockdiag_workspace_size(w.B, w.T, w.H, w.dk, w.dv, 2), dtype=torch.uint8, device=dev)
+    args = (g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], gy)
+    out = pm.bwd_blockdiag(*args, block=2, gmuT=gmuT, workspace=ws)
+    fn = lambda: pm.bwd_blockdiag(*args, block=2, gmuT=gmuT, workspace=ws, out=out)
+    _, per = time_launches(fn, steps, 2, torch)
+    avg_s = sum(per) / len(per) / 1e3
+    entries = w.B * w.H * w.T * w.dv * w.dk
+    peak = LANE_OPS_PER_S / BD2_BWD_SLOTS_PER_ENTRY * BD2_BWD_FLOPS_PER_ENTRY / 1e12
+    achieved = entries * BD2_BWD_FLOPS_PER_ENTRY / avg_s / 1e12
+    return {"workload": w.name + ", 2x2 block-diagonal backward (gq, gk, gv, gbeta, gdt, gA, gIp, gmu0, gP0)",
+            "tokens_per_s": w.B * w.T / avg_s, "ms_per_call": avg_s * 1e3,
+            "workspace_GB": ws.numel() / 1e9,
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                         "frac": achieved / peak,
+                         "traffic": load_traffic("bd2_bwd_layer760m_bf16_traffic.json")
+                         if w.name.startswith("layer760m") else None,
+                         "scope": "whole call (5 kernels); per-kernel split in the committed trace",
+                         "per_entry": "replay 5.5 + reverse 25 VALU + 0.5 v_rcp_f32 = 31.5 slots, 45 flops"}}
+
+
 def fig7_extra(torch, pm, workloads, dev, D, steps):
     """One head as wide as the model, the shape of the pages' recurrent-kernel
     measurement (B=16, L=2048, H=1, d_k = d_v = D; bf16 inputs, fp32 state),
@@ -453,6 +486,7 @@ def main():
         out["blockdiag"] = blockdiag_extra(torch, pm, w, g, max(20, args.steps // 2))
         out["blockdiag_decode"] = blockdiag_decode_extra(torch, pm, workloads, max(64, args.steps))
         out["blockdiag4"] = blockdiag4_extra(torch, pm, w, g, max(10, args.steps // 5))
+        out["blockdiag_backward"] = blockdiag_backward_extra(torch, pm, workloads, w, g, max(5, args.steps // 5))
         out["recurrent_shape"] = [fig7_extra(torch, pm, workloads, dev, D, 5) for D in (512, 2048)]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads or w.B * w.H)

@@ -403,6 +403,58 @@ palimpsa_status palimpsa_step_blockdiag(const void *q, const void *k, const void
                                         void *y, int B, int H, int dk, int dv, int block,
                                         palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, void *stream);
 
+/*
+ * Bytes of workspace palimpsa_bwd_blockdiag needs for these sizes (0 for
+ * sizes or a block it does not support).
+ */
+size_t palimpsa_bwd_blockdiag_workspace_size(int B, int T, int H, int dk, int dv, int block);
+
+/*
+ * Reverse-mode derivative of palimpsa_fwd_blockdiag with 2x2 blocks (the
+ * block-diagonal update of the slides' backup frame "dropping precision
+ * correlations changes the mean", App. A.3-A.5) for
+ *
+ *     L = sum(gy . y) + sum(gmuT . muT) + sum(gPT . PT),
+ *
+ * from the forward's inputs (it recomputes the states from checkpoints every
+ * 8 tokens).  Per value row and key block, with h = P mu and the adjoints
+ * (G_h, G_P) walked from the last token down: the readout adds w = P^-1 gy q
+ * to G_h and -w mu^T to G_P; k gets (beta v) G_h + beta (G_P + G_P^T) k, the
+ * write beta v gets G_h . k, beta's precision term k^T G_P k, the gate
+ * <G_h, h_prev> + <G_P, P_prev> and tr G_P; both adjoints decay by alpha.
+ *
+ * Inputs (device pointers):
+ *   q, k, v, beta, dt, A, I_prior, mu0, P0   as palimpsa_fwd_blockdiag
+ *             (mu0 and P0 both given or both NULL: mu0 = 0, P0 = I_prior Id)
+ *   gy        [B, T, H, dv]  gy_dtype   dL/dy
+ *   gmuT      [B, H, dv, dk] float32    dL/dmuT, or NULL (zero)
+ *   gPT       [B, H, dv, dk/2, 2, 2]    dL/dPT (all four entries), or NULL (zero)
+ * Outputs (float32, overwritten):
+ *   gq, gk    [B, T, H, dk]     gv, gbeta [B, T, H, dv]     gdt [B, T, H]
+ *   gA, gIp   [H]   summed over the batch; with the default start state gIp
+ *             includes the start precision's share
+ *   gmu0      [B, H, dv, dk]    dL/dmu0, or NULL
+ *   gP0       [B, H, dv, dk/2, 2, 2]  the gradient for a symmetric P0 (both
+ *             off-diagonal entries hold half of dL/dp01), or NULL
+ *   workspace at least palimpsa_bwd_blockdiag_workspace_size(B, T, H, dk, dv, 2)
+ *             bytes, 16-byte aligned, caller-owned; contents on entry ignored
+ *
+ * block == 2 with dk in {32, 64, 128}, dv a multiple of 16 up to 1024 (else
+ * PALIMPSA_ERR_UNSUPPORTED).  q, k, v, beta, gy, P0, gPT, gP0, gq, gk and the
+ * workspace must be 16-byte aligned, the float32 arrays 4-byte aligned.
+ * float32 arithmetic; results are deterministic (fixed reduction order).
+ * T == 0 copies gmuT to gmu0 and the symmetric part of gPT to gP0.
+ */
+palimpsa_status palimpsa_bwd_blockdiag(const void *q, const void *k, const void *v, const void *beta,
+                                       const void *dt, const float *A, const float *I_prior,
+                                       const float *mu0, const float *P0,
+                                       const void *gy, const float *gmuT, const float *gPT,
+                                       float *gq, float *gk, float *gv, float *gbeta, float *gdt,
+                                       float *gA, float *gIp, float *gmu0, float *gP0,
+                                       int B, int T, int H, int dk, int dv, int block,
+                                       palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *palimpsa_status_string(int status);
 

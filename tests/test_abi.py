@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("palimpsa_fwd_chunked", "palimpsa_fwd_workspace_size", "palimpsa_fwd_frozen",
               "palimpsa_step", "palimpsa_bwd", "palimpsa_bwd_workspace_size", "palimpsa_bwd_frozen",
-              "palimpsa_fwd_blockdiag", "palimpsa_step_blockdiag",
+              "palimpsa_fwd_blockdiag", "palimpsa_step_blockdiag", "palimpsa_bwd_blockdiag",
+              "palimpsa_bwd_blockdiag_workspace_size",
               "palimpsa_status_string", "palimpsa_version"):
         assert n in names
 
@@ -327,3 +328,56 @@ BD_STEP_CASES = [
 @pytest.mark.parametrize("over,status", BD_STEP_CASES)
 def test_blockdiag_step_rejects_invalid_calls(lib, over, status):
     assert lib.palimpsa_step_blockdiag(*_bd_step_args(**over)) == status
+
+
+def _bd_bwd_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dt=FAKE, A=FAKE, Ip=FAKE, mu0=None, P0=None, gy=FAKE,
+             gmuT=None, gPT=None, gq=FAKE, gk=FAKE, gv=FAKE, gbeta=FAKE, gdt=FAKE, gA=FAKE, gIp=FAKE,
+             gmu0=None, gP0=None, B=2, T=8, H=3, dk=64, dv=64, block=2, ind=1, gyd=1, ws=FAKE, wsb=1 << 40,
+             stream=None)
+    a.update(over)
+    return [a[n] for n in ("q", "k", "v", "beta", "dt", "A", "Ip", "mu0", "P0", "gy", "gmuT", "gPT",
+                           "gq", "gk", "gv", "gbeta", "gdt", "gA", "gIp", "gmu0", "gP0",
+                           "B", "T", "H", "dk", "dv", "block", "ind", "gyd", "ws", "wsb", "stream")]
+
+
+# every case fails validation
+BD_BWD_CASES = [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(beta=None), 1), (dict(dt=None), 1), (dict(gy=None), 1),
+    (dict(gq=None), 1), (dict(gk=None), 1), (dict(gv=None), 1), (dict(gbeta=None), 1), (dict(gdt=None), 1),
+    (dict(gA=None), 1), (dict(gIp=None), 1), (dict(A=None), 1), (dict(Ip=None), 1), (dict(ws=None), 1),
+    (dict(mu0=FAKE), 1), (dict(P0=FAKE), 1), (dict(B=0), 1), (dict(T=-1), 1), (dict(H=0), 1), (dict(dk=0), 1),
+    (dict(block=0), 1), (dict(ind=2), 1), (dict(gyd=5), 1), (dict(wsb=64), 1),
+    (dict(q=None, T=0, A=None), 1),
+    (dict(block=1), 2), (dict(block=4), 2), (dict(block=3), 2), (dict(dk=48), 2), (dict(dv=1040), 2),
+    (dict(dv=8), 2),
+    (dict(q=FAKE + 4), 3), (dict(gy=FAKE + 8), 3), (dict(P0=FAKE + 8, mu0=FAKE), 3),
+    (dict(mu0=FAKE + 2, P0=FAKE), 3), (dict(gPT=FAKE + 4), 3), (dict(gP0=FAKE + 8), 3), (dict(gq=FAKE + 4), 3),
+    (dict(gmuT=FAKE + 1), 3), (dict(gmu0=FAKE + 2), 3), (dict(gdt=FAKE + 2), 3), (dict(dt=FAKE + 1), 3),
+    (dict(ws=FAKE + 8), 3),
+]
+
+
+@invalid_calls
+@pytest.mark.parametrize("over,status", BD_BWD_CASES)
+def test_blockdiag_bwd_rejects_invalid_calls(lib, over, status):
+    assert lib.palimpsa_bwd_blockdiag(*_bd_bwd_args(**over)) == status
+
+
+def test_bwd_blockdiag_workspace_size_host_logic(lib):
+    """Checkpoints of the lane states (h, then three entries per 2x2 block,
+    padded to float4s) every 8 tokens, then the exact backward's partials."""
+    import bayesian_metaplastic_memory_amd as pm
+    pad = lambda n: (4 * n + 255) // 256 * 256
+
+    def expect(B, T, H, dk, dv):
+        nsb, nrb, bh = (T + 7) // 8, dv // 16, B * H
+        kc = dk // 16
+        lane = (kc + 3 * (kc // 2) + 3) // 4 * 4
+        return (pad(bh * nsb * nrb * 256 * lane) + pad(nrb * bh * T * 2 * dk) + pad(nrb * bh * T * 2)
+                + 2 * pad(bh) + pad(bh * nrb))
+    for shape in [(1, 10, 2, 32, 32), (8, 4096, 12, 128, 128), (1, 0, 3, 64, 128), (2, 9, 1, 128, 64)]:
+        assert pm.bwd_blockdiag_workspace_size(*shape) == expect(*shape), shape
+    assert pm.bwd_blockdiag_workspace_size(1, 8, 2, 64, 64, block=4) == 0
+    assert pm.bwd_blockdiag_workspace_size(1, 8, 2, 48, 64) == 0
+    assert pm.bwd_blockdiag_workspace_size(0, 8, 2, 64, 64) == 0

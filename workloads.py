@@ -164,3 +164,11 @@ def random_block_state(B: int, H: int, dv: int, dk: int, block: int, I_prior: to
     L = 0.5 * torch.randn(B, H, dv, dk // block, block, block, generator=g)
     P0 = I_prior.view(1, H, 1, 1, 1, 1) * torch.eye(block) + L @ L.transpose(-1, -2)
     return mu0.float().contiguous(), P0.float().contiguous()
+
+
+def block_state_grads(B: int, H: int, dv: int, dk: int, block: int, seed: int) -> torch.Tensor:
+    """A seeded upstream gradient of the final precision blocks for the
+    block-diagonal backward, gPT ~ 0.1 N(0, 1) in every entry (not symmetric),
+    layout [B, H, dv, dk/block, block, block], float32."""
+    g = torch.Generator().manual_seed(40_000 + seed)
+    return (0.1 * torch.randn(B, H, dv, dk // block, block, block, generator=g)).contiguous()
