@@ -518,7 +518,7 @@ def bwd_blockdiag_workspace_size(B, T, H, dk, dv, block: int = 2) -> int:
 
 def bwd_blockdiag(q, k, v, beta, dt, A, I_prior, gy, block: int = 2, mu0=None, P0=None, gmuT=None, gPT=None,
                   want_state_grads: bool = True, workspace=None, out=None):
-    """Backward of ``fwd_blockdiag`` (2x2 blocks) for
+    """Backward of ``fwd_blockdiag`` (``block`` 2, or 4 with d_k of 64 or 128) for
     ``L = <gy, y> + <gmuT, muT> + <gPT, PT>``.
 
     Returns a dict of float32 gradients ``gq, gk, gv, gbeta, gdt, gA, gIp`` and,

@@ -1604,17 +1604,19 @@ __global__ __launch_bounds__(kThreads) void bd2_fwd_kernel(BdArgs a) {
 // (the gradient for a symmetric P0), and the default start (mu0 = 0,
 // P_0 = I_prior Id) adds tr S to gI_prior.
 //
-// Passes: bd2_ckpt_kernel stores (h, P) before every 8th token; bd2_bwd_kernel
+// Passes: bd_ckpt_kernel stores (h, P) before every 8th token; bd2_bwd_kernel
 // has bwd_kernel's structure (halves of 4 tokens replayed from the
 // checkpoint into registers, walked in reverse) with the step above.
 
-// A lane's 2x2 state: h for its KC columns, then (p00, p01, p11) per block;
-// a checkpoint pads it to whole float4s.
-template <int DK> struct Bd2Lane {
+// A lane's block state: h for its KC columns, then per block the upper
+// triangle of P ((p00, p01, p11) for 2x2 blocks, 10 entries for 4x4); a
+// checkpoint pads it to whole float4s.
+template <int DK, int BS> struct BdLane {
     static constexpr int kKC = LaneTile<DK>::kCols;
-    static constexpr int kN = kKC + 3 * (kKC / 2);
+    static constexpr int kN = kKC + (BS == 2 ? 3 * (kKC / 2) : 10 * (kKC / 4));
     static constexpr int kNP = (kN + 3) / 4 * 4;
 };
+template <int DK> using Bd2Lane = BdLane<DK, 2>;
 
 // A workgroup's checkpoint block: float4 i of thread tid at blk + 4 (i kThreads + tid).
 template <int N, int NP>
@@ -1696,67 +1698,52 @@ struct BdBwdArgs {
     int B, T, H, dv, nsb, nwg, xcd_remap;
 };
 
-// Checkpoint pass: the forward's update without readout, staged like the
-// forward (no q), storing the state before tokens 0, 8, 16, ...
-template <int DK, typename TIn>
-__global__ __launch_bounds__(kThreads) void bd2_ckpt_kernel(BdBwdArgs a) {
-    using LT = LaneTile<DK>;
-    using L = Bd2Lane<DK>;
-    using SG = Stage<DK>;
-    constexpr int C = 16;
-    extern __shared__ float lds[];
-    const int rb_per_head = a.dv / kRowsPerWG;
-    int wg = blockIdx.x;
-    if (a.xcd_remap) {
-        const int per_xcd = a.nwg / 8;
-        wg = (wg % 8) * per_xcd + wg / 8;
+// A sub-block's outputs once its (gq, gk) column sums are in red and its row
+// sums (gbv, gb, da, dc) in rs: the row block's (gq, gk) partials summed over
+// the 4 waves, gv = gbv beta and gbeta = gbv v + gb per (token, row), and the
+// row block's (da, dc) partials per token.
+template <int DK>
+__device__ inline void bd_bwd_epilogue(const BdBwdArgs &a, const float *cur, const float *red, const float *rs,
+                                       int tid, int t0, int rb, int bh, int row0, size_t seq0, size_t bth) {
+    using S = BwdStage<DK>;
+    for (int n = 4 * tid; n < kSB * 2 * DK; n += 4 * kThreads) {
+        const int e = n / (2 * DK), c = n % (2 * DK);
+        const float *r0 = red + e * kWaves * 2 * DK + c;
+        const float4 v0 = *(const float4 *)r0, v1 = *(const float4 *)(r0 + 2 * DK);
+        const float4 v2 = *(const float4 *)(r0 + 4 * DK), v3 = *(const float4 *)(r0 + 6 * DK);
+        if (t0 + e < a.T)
+            *(float4 *)(a.pqk + ((size_t)rb * bth + seq0 + (size_t)(t0 + e) * a.H) * 2 * DK + c) =
+                make_float4((v0.x + v1.x) + (v2.x + v3.x), (v0.y + v1.y) + (v2.y + v3.y),
+                            (v0.z + v1.z) + (v2.z + v3.z), (v0.w + v1.w) + (v2.w + v3.w));
     }
-    const int bh = wg / rb_per_head, rb = wg % rb_per_head;
-    const int row0 = rb * kRowsPerWG;
-    const int b = bh / a.H, h = bh % a.H;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int g = lane & (kLanesPerRow - 1);
-    const int row_local = wave * kRowsPerWave + (lane >> 4);
-    const float A = a.A[h], Ip = a.Ip[h];
-    float st[L::kN];
-    bd2_start<DK>(a.mu0, a.P0, ((size_t)bh * a.dv + row0 + row_local) * DK, g, Ip, st);
-    const size_t ck_stride = (size_t)rb_per_head * kThreads * L::kNP;
-    float *ckb = a.ck + ((size_t)bh * a.nsb * rb_per_head + rb) * (kThreads * L::kNP);
+    if (tid < kSB * kRowsPerWG) {
+        const int e = tid / kRowsPerWG, r = tid % kRowsPerWG;
+        const float gbv = rs[(e * 4 + 0) * kRowsPerWG + r], gb = rs[(e * 4 + 1) * kRowsPerWG + r];
+        const float4 rw = *(const float4 *)(cur + S::kRows + e * S::kRowFloats + 4 * r);
+        if (t0 + e < a.T) {
+            const size_t o = (seq0 + (size_t)(t0 + e) * a.H) * a.dv + row0 + r;
+            a.gv[o] = gbv * rw.x;
+            a.gbeta[o] = fmaf(gbv, rw.z, gb);
+        }
+    } else if (tid < kSB * kRowsPerWG + 2 * kSB) {
+        const int u = tid - kSB * kRowsPerWG, e = u % kSB, qd = u / kSB;
+        const float *src = rs + (e * 4 + 2 + qd) * kRowsPerWG;
+        float v = 0.f;
+#pragma unroll
+        for (int r = 0; r < kRowsPerWG; ++r) v += src[r];
+        if (t0 + e < a.T) a.ps[((size_t)rb * bth + (size_t)bh * a.T + t0 + e) * 2 + qd] = v;
+    }
+}
 
-    const size_t seq = (size_t)b * a.T * a.H + h;
-    const TIn *kseq = (const TIn *)a.k + seq * DK;
-    const TIn *vseq = (const TIn *)a.v + seq * a.dv + row0;
-    const TIn *bseq = (const TIn *)a.beta + seq * a.dv + row0;
-    const TIn *dseq = (const TIn *)a.dt + seq;
-    const size_t kq_tok = (size_t)a.H * DK, vb_tok = (size_t)a.H * a.dv;
-    const int nchunks = (a.T + C - 1) / C;
-    Stager<DK, C, TIn, false> sg;
-    sg.load(kseq, kseq, vseq, bseq, dseq, a.T, a.H, a.dv, tid);
-    sg.commit(lds, A, Ip, tid, false);
+// The workgroup's sum of the lanes' x into pI0[slot] (rs: 4 floats of scratch LDS).
+__device__ inline void bd_bwd_trace_partial(const BdBwdArgs &a, float x, float *rs, int tid, size_t slot) {
+    x = row16_sum(x);
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
     __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-        const int t0 = c * C;
-        const bool more = c + 1 < nchunks;
-        if (more) {
-            const size_t tn = (size_t)(t0 + C);
-            sg.load(kseq + tn * kq_tok, kseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
-                    dseq + tn * a.H, a.T - (t0 + C), a.H, a.dv, tid);
-        }
-        const float *buf = lds + (c & 1) * C * SG::kTokFloats;
-        const float *rows = buf + C * SG::kColFloats + 2 * row_local;
-        const float *gates = buf + C * (SG::kColFloats + SG::kRowFloats);
-#pragma unroll 2
-        for (int u = 0; u < C; ++u) {
-            if (u % kSB == 0 && (t0 + u) / kSB < a.nsb)
-                bd2_ck_store<L::kN, L::kNP>(ckb + (size_t)((t0 + u) / kSB) * ck_stride, tid, st);
-            const float2 gc = *(const float2 *)(gates + 2 * u);
-            const float2 rw = *(const float2 *)(rows + u * SG::kRowFloats);
-            bd2_update<DK>(buf + u * SG::kColFloats + LT::col(g, 0, 0), gc.x, gc.y, rw.x, rw.y, st);
-        }
-        if (more) sg.commit(lds + ((c + 1) & 1) * C * SG::kTokFloats, A, Ip, tid, false);
-        __syncthreads();
-    }
+    if ((tid & 63) == 0) rs[tid >> 6] = x;
+    __syncthreads();
+    if (tid == 0) a.pI0[slot] = (rs[0] + rs[1]) + (rs[2] + rs[3]);
 }
 
 // One token of the reverse walk for the lane's blocks: St the state after the
@@ -1971,35 +1958,7 @@ __global__ __launch_bounds__(kThreads) void bd2_bwd_kernel(BdBwdArgs a) {
             bwd_row_sums(acc, g, rs + row_local);
             if (sb > 0) st.commit(lds + ((sb - 1) & 1) * S::kFloats, A, Ip, tid, false);
             __syncthreads();
-            // sums over the 4 waves: this row block's partials of (gq, gk)
-            for (int n = 4 * tid; n < kSB * 2 * DK; n += 4 * kThreads) {
-                const int e = n / (2 * DK), c = n % (2 * DK);
-                const float *r0 = red + e * kWaves * 2 * DK + c;
-                const float4 v0 = *(const float4 *)r0, v1 = *(const float4 *)(r0 + 2 * DK);
-                const float4 v2 = *(const float4 *)(r0 + 4 * DK), v3 = *(const float4 *)(r0 + 6 * DK);
-                if (t0 + e < a.T)
-                    *(float4 *)(a.pqk + ((size_t)rb * bth + seq0 + (size_t)(t0 + e) * a.H) * 2 * DK + c) =
-                        make_float4((v0.x + v1.x) + (v2.x + v3.x), (v0.y + v1.y) + (v2.y + v3.y),
-                                    (v0.z + v1.z) + (v2.z + v3.z), (v0.w + v1.w) + (v2.w + v3.w));
-            }
-            // per (token, row): gv = gbv beta, gbeta = gbv v + gb; per token: (da, dc)
-            if (tid < kSB * kRowsPerWG) {
-                const int e = tid / kRowsPerWG, r = tid % kRowsPerWG;
-                const float gbv = rs[(e * 4 + 0) * kRowsPerWG + r], gb = rs[(e * 4 + 1) * kRowsPerWG + r];
-                const float4 rw = *(const float4 *)(cur + S::kRows + e * S::kRowFloats + 4 * r);
-                if (t0 + e < a.T) {
-                    const size_t o = (seq0 + (size_t)(t0 + e) * a.H) * a.dv + row0 + r;
-                    a.gv[o] = gbv * rw.x;
-                    a.gbeta[o] = fmaf(gbv, rw.z, gb);
-                }
-            } else if (tid < kSB * kRowsPerWG + 2 * kSB) {
-                const int u = tid - kSB * kRowsPerWG, e = u % kSB, qd = u / kSB;
-                const float *src = rs + (e * 4 + 2 + qd) * kRowsPerWG;
-                float v = 0.f;
-#pragma unroll
-                for (int r = 0; r < kRowsPerWG; ++r) v += src[r];
-                if (t0 + e < a.T) a.ps[((size_t)rb * bth + (size_t)bh * a.T + t0 + e) * 2 + qd] = v;
-            }
+            bd_bwd_epilogue<DK>(a, cur, red, rs, tid, t0, rb, bh, row0, seq0, bth);
             __syncthreads();
             if (sb > 0) {
 #pragma unroll
@@ -2035,13 +1994,7 @@ __global__ __launch_bounds__(kThreads) void bd2_bwd_kernel(BdBwdArgs a) {
     float gs = 0.f;
 #pragma unroll
     for (int j = 0; j < KB; ++j) gs += GS[3 * j] + GS[3 * j + 2];
-    gs = row16_sum(gs);
-    gs += __shfl_xor(gs, 16, 64);
-    gs += __shfl_xor(gs, 32, 64);
-    __syncthreads();
-    if (lane == 0) rs[wave] = gs;
-    __syncthreads();
-    if (tid == 0) a.pI0[(size_t)bh * rb_per_head + rb] = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    bd_bwd_trace_partial(a, gs, rs, tid, bh * rb_per_head + rb);
 }
 
 // ---------------------------------------------------------------------------
@@ -2057,24 +2010,34 @@ __global__ __launch_bounds__(kThreads) void bd2_bwd_kernel(BdBwdArgs a) {
 
 // Solve P x = h for a symmetric positive definite 4x4 P given by its upper
 // triangle p = (p00 p01 p02 p03 p11 p12 p13 p22 p23 p33).
-__device__ inline void spd4_solve(const float *p, const float *h, float *x) {
-    const float r0 = __builtin_amdgcn_rsqf(p[0]);
-    const float l10 = p[1] * r0, l20 = p[2] * r0, l30 = p[3] * r0;
-    const float r1 = __builtin_amdgcn_rsqf(fmaf(-l10, l10, p[4]));
-    const float l21 = fmaf(-l20, l10, p[5]) * r1, l31 = fmaf(-l30, l10, p[6]) * r1;
-    const float r2 = __builtin_amdgcn_rsqf(fmaf(-l21, l21, fmaf(-l20, l20, p[7])));
-    const float l32 = fmaf(-l31, l21, fmaf(-l30, l20, p[8])) * r2;
-    const float r3 = __builtin_amdgcn_rsqf(fmaf(-l32, l32, fmaf(-l31, l31, fmaf(-l30, l30, p[9]))));
-    // L z = h, then L^T x = z
-    const float z0 = h[0] * r0;
-    const float z1 = fmaf(-l10, z0, h[1]) * r1;
-    const float z2 = fmaf(-l21, z1, fmaf(-l20, z0, h[2])) * r2;
-    const float z3 = fmaf(-l32, z2, fmaf(-l31, z1, fmaf(-l30, z0, h[3]))) * r3;
-    x[3] = z3 * r3;
-    x[2] = fmaf(-l32, x[3], z2) * r2;
-    x[1] = fmaf(-l31, x[3], fmaf(-l21, x[2], z1)) * r1;
-    x[0] = fmaf(-l30, x[3], fmaf(-l20, x[2], fmaf(-l10, x[1], z0))) * r0;
+// The factor: r_i = 1 / L_ii and the strictly lower part of L.
+struct Chol4 {
+    float r0, r1, r2, r3, l10, l20, l30, l21, l31, l32;
+};
+__device__ inline Chol4 spd4_factor(const float *p) {
+    Chol4 f;
+    f.r0 = __builtin_amdgcn_rsqf(p[0]);
+    f.l10 = p[1] * f.r0; f.l20 = p[2] * f.r0; f.l30 = p[3] * f.r0;
+    f.r1 = __builtin_amdgcn_rsqf(fmaf(-f.l10, f.l10, p[4]));
+    f.l21 = fmaf(-f.l20, f.l10, p[5]) * f.r1;
+    f.l31 = fmaf(-f.l30, f.l10, p[6]) * f.r1;
+    f.r2 = __builtin_amdgcn_rsqf(fmaf(-f.l21, f.l21, fmaf(-f.l20, f.l20, p[7])));
+    f.l32 = fmaf(-f.l31, f.l21, fmaf(-f.l30, f.l20, p[8])) * f.r2;
+    f.r3 = __builtin_amdgcn_rsqf(fmaf(-f.l32, f.l32, fmaf(-f.l31, f.l31, fmaf(-f.l30, f.l30, p[9]))));
+    return f;
 }
+// L z = h, then L^T x = z.
+__device__ inline void spd4_apply(const Chol4 &f, const float *h, float *x) {
+    const float z0 = h[0] * f.r0;
+    const float z1 = fmaf(-f.l10, z0, h[1]) * f.r1;
+    const float z2 = fmaf(-f.l21, z1, fmaf(-f.l20, z0, h[2])) * f.r2;
+    const float z3 = fmaf(-f.l32, z2, fmaf(-f.l31, z1, fmaf(-f.l30, z0, h[3]))) * f.r3;
+    x[3] = z3 * f.r3;
+    x[2] = fmaf(-f.l32, x[3], z2) * f.r2;
+    x[1] = fmaf(-f.l31, x[3], fmaf(-f.l21, x[2], z1)) * f.r1;
+    x[0] = fmaf(-f.l30, x[3], fmaf(-f.l20, x[2], fmaf(-f.l10, x[1], z0))) * f.r0;
+}
+__device__ inline void spd4_solve(const float *p, const float *h, float *x) { spd4_apply(spd4_factor(p), h, x); }
 
 // One token's update of a 4-block: P = alpha P + c Id + beta k k^T, h = alpha h + (beta v) k.
 __device__ inline void bd4_update(float *p, float *hh, const float *kk, const float *k2, float alpha, float c,
@@ -2242,6 +2205,411 @@ __global__ __launch_bounds__(kThreads) void bd4_fwd_kernel(BdArgs a) {
             *(float4 *)(pb + 8) = make_float4(p[2], p[5], p[7], p[8]);
             *(float4 *)(pb + 12) = make_float4(p[3], p[6], p[8], p[9]);
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// block-diagonal precision, 4x4 blocks: backward
+// ---------------------------------------------------------------------------
+//
+// The 2x2 backward's reverse walk with 4x4 blocks: per token and block the
+// Cholesky factor of P_t serves both solves, mu = P^-1 h and w = P^-1 (gy_i q);
+// S = sym(G_P) is kept as its upper triangle (10 floats), and the row sums
+// weight S's off-diagonal entries twice in <S, P_prev>.  A lane state is 28
+// floats at d = 128, so the walk replays quarters of 2 tokens from the
+// checkpoint (20 replayed updates per 8 tokens) to hold two states, not four.
+
+// Index of entry (i, j) of a symmetric 4x4 block in its upper-triangle storage.
+__host__ __device__ constexpr int up4(int i, int j) {
+    return i <= j ? (i * (7 - i)) / 2 + j : (j * (7 - j)) / 2 + i;
+}
+
+// The lane's start state: from (mu0, P0) when given (P0's upper triangle),
+// else mu0 = 0 and P0 = I_prior Id.  srow: entry (b, h, row, 0).
+template <int DK>
+__device__ inline void bd4_start(const float *mu0, const float *P0, size_t srow, int g, float Ip, float *st) {
+    using LT = LaneTile<DK>;
+    constexpr int KC = LT::kCols;
+#pragma unroll
+    for (int m = 0; m < LT::kNVec; ++m) {
+        float *p = st + KC + 10 * m, *hh = st + 4 * m;
+        const int col = LT::col(g, m, 0);
+        if (mu0) {
+            const float *pb = P0 + (srow + col) * 4;
+            float mu[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mu[e] = mu0[srow + col + e];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = i; j < 4; ++j) p[up4(i, j)] = pb[4 * i + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float acc = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc = fmaf(p[up4(i, j)], mu[j], acc);
+                hh[i] = acc;
+            }
+        } else {
+#pragma unroll
+            for (int x = 0; x < 10; ++x) p[x] = (x == 0 || x == 4 || x == 7 || x == 9) ? Ip : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hh[e] = 0.f;
+        }
+    }
+}
+
+// One token's update of the lane's 4-blocks (bd4_update, as the forward runs it).
+template <int DK>
+__device__ inline void bd4_update_lane(const float *ct, float alpha, float c, float beta, float bv, float *st) {
+    using LT = LaneTile<DK>;
+    constexpr int KC = LT::kCols;
+#pragma unroll
+    for (int m = 0; m < LT::kNVec; ++m) {
+        float kk[4], k2[4];
+        const int c0 = kLanesPerRow * 4 * m;
+        vecf<4>::ld(ct + c0, kk);
+        vecf<4>::ld(ct + DK + c0, k2);
+        bd4_update(st + KC + 10 * m, st + 4 * m, kk, k2, alpha, c, beta, bv);
+    }
+}
+
+// One token of the reverse walk for the lane's 4-blocks (St after the token,
+// Sp before it); outputs as bd2_reverse_token.
+template <int DK>
+__device__ inline void bd4_reverse_token(const float *buf, int e, const float *St, const float *Sp, float *Gh,
+                                         float *GS, int row_local, int g, int lane, float *red,
+                                         float &cbv, float &cb, float &s1, float &s2) {
+    using LT = LaneTile<DK>;
+    using S = BwdStage<DK>;
+    constexpr int KC = LT::kCols;
+    const float alpha = buf[S::kGate + 2 * e];
+    const float4 rw = *(const float4 *)(buf + S::kRows + e * S::kRowFloats + 4 * row_local);
+    const float b2 = 2.f * rw.x, bv = rw.y, gy = rw.w;
+    const float *ct = buf + e * S::kColFloats + LT::col(g, 0, 0);
+    float dq[KC], dk[KC];
+    cbv = 0.f; cb = 0.f; s1 = 0.f; s2 = 0.f;
+#pragma unroll
+    for (int m = 0; m < LT::kNVec; ++m) {
+        float kk[4], qq[4];
+        const int c0 = kLanesPerRow * 4 * m;
+        vecf<4>::ld(ct + c0, kk);
+        vecf<4>::ld(ct + 2 * DK + c0, qq);
+        const float *p = St + KC + 10 * m, *pp = Sp + KC + 10 * m;
+        const float *hh = St + 4 * m, *hp = Sp + 4 * m;
+        float *gh = Gh + 4 * m, *gs = GS + 10 * m;
+        const Chol4 f = spd4_factor(p);
+        float mu[4], gq4[4], w[4], sk[4];
+        spd4_apply(f, hh, mu);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gq4[i] = gy * qq[i];
+        spd4_apply(f, gq4, w);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dq[4 * m + i] = gy * mu[i];
+            gh[i] += w[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            gs[up4(i, i)] = fmaf(-w[i], mu[i], gs[up4(i, i)]);
+#pragma unroll
+            for (int j = i + 1; j < 4; ++j)
+                gs[up4(i, j)] = fmaf(-0.5f, fmaf(w[i], mu[j], w[j] * mu[i]), gs[up4(i, j)]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float acc = gs[up4(i, 0)] * kk[0];
+#pragma unroll
+            for (int j = 1; j < 4; ++j) acc = fmaf(gs[up4(i, j)], kk[j], acc);
+            sk[i] = acc;
+            dk[4 * m + i] = fmaf(gh[i], bv, b2 * sk[i]);
+            cbv = fmaf(gh[i], kk[i], cbv);
+            cb = fmaf(sk[i], kk[i], cb);
+            s1 = fmaf(gh[i], hp[i], s1);
+            s2 += gs[up4(i, i)];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s1 = fmaf(gs[up4(i, i)], pp[up4(i, i)], s1);
+#pragma unroll
+            for (int j = i + 1; j < 4; ++j) s1 = fmaf(2.f * gs[up4(i, j)], pp[up4(i, j)], s1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gh[i] *= alpha;
+#pragma unroll
+        for (int x = 0; x < 10; ++x) gs[x] *= alpha;
+    }
+    bwd_scatter_qk<DK>(dq, dk, lane, g, red);
+}
+
+template <int DK, typename TIn, typename TG>
+__global__ __launch_bounds__(kThreads) void bd4_bwd_kernel(BdBwdArgs a) {
+    using LT = LaneTile<DK>;
+    using S = BwdStage<DK>;
+    using L = BdLane<DK, 4>;
+    static_assert(LT::kVec == 4, "a lane's column vectors must be whole 4-blocks");
+    constexpr int KC = LT::kCols, NB = KC / 4, N = L::kN;
+    extern __shared__ float lds[];
+    float *red = lds + S::kRed;
+    float *rs = lds + S::kRs;
+
+    const int rb_per_head = a.dv / kRowsPerWG;
+    int wg = blockIdx.x;
+    if (a.xcd_remap) {
+        const int per_xcd = a.nwg / 8;
+        wg = (wg % 8) * per_xcd + wg / 8;
+    }
+    const int bh = wg / rb_per_head;
+    const int rb = wg % rb_per_head;
+    const int row0 = rb * kRowsPerWG;
+    const int b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane & (kLanesPerRow - 1);
+    const int row_local = wave * kRowsPerWave + (lane >> 4);
+    const float A = a.A[h], Ip = a.Ip[h];
+    const size_t srow = ((size_t)bh * a.dv + row0 + row_local) * DK;
+    const size_t seq0 = (size_t)b * a.T * a.H + h;
+    const size_t bth = (size_t)a.B * a.T * a.H;
+    const size_t kq_tok = (size_t)a.H * DK, vb_tok = (size_t)a.H * a.dv;
+
+    float Gh[KC], GS[10 * NB];
+    // gPT's block at entry o, symmetrised into the upper triangle u
+    auto load_gpt = [&](size_t o, float *u) {
+        const float *gb = a.gPT + o * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = i; j < 4; ++j)
+                u[up4(i, j)] = a.gPT ? (i == j ? gb[5 * i] : 0.5f * (gb[4 * i + j] + gb[4 * j + i])) : 0.f;
+    };
+    auto store_gp0 = [&](size_t o, const float *u) {
+        float *gb = a.gP0 + o * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float row[4] = {u[up4(i, 0)], u[up4(i, 1)], u[up4(i, 2)], u[up4(i, 3)]};
+            vecf<4>::st(gb + 4 * i, row);
+        }
+    };
+    // the final state's adjoint from (gmuT, gPT), given the final state st
+    auto final_adjoint = [&](const float *st) {
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+            const size_t o = srow + LT::col(g, m, 0);
+            const Chol4 f = spd4_factor(st + KC + 10 * m);
+            float gm[4], muT[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gm[e] = a.gmuT ? a.gmuT[o + e] : 0.f;
+            spd4_apply(f, st + 4 * m, muT);
+            spd4_apply(f, gm, Gh + 4 * m);
+            float *gs = GS + 10 * m;
+            const float *w = Gh + 4 * m;
+            load_gpt(o, gs);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                gs[up4(i, i)] = fmaf(-w[i], muT[i], gs[up4(i, i)]);
+#pragma unroll
+                for (int j = i + 1; j < 4; ++j)
+                    gs[up4(i, j)] = fmaf(-0.5f, fmaf(w[i], muT[j], w[j] * muT[i]), gs[up4(i, j)]);
+            }
+        }
+    };
+
+    if (a.nsb == 0) {
+        // T = 0: mu_T = mu_0 and P_T = P_0 are copied through, so are their gradients
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+            const size_t o = srow + LT::col(g, m, 0);
+            load_gpt(o, GS + 10 * m);
+            if (a.gmu0)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a.gmu0[o + e] = a.gmuT ? a.gmuT[o + e] : 0.f;
+            if (a.gP0) store_gp0(o, GS + 10 * m);
+        }
+    } else {
+        const size_t ck_stride = (size_t)rb_per_head * kThreads * L::kNP;
+        const float *ckb = a.ck + ((size_t)bh * a.nsb * rb_per_head + rb) * (kThreads * L::kNP);
+        const TIn *kseq = (const TIn *)a.k + seq0 * DK;
+        const TIn *qseq = (const TIn *)a.q + seq0 * DK;
+        const TIn *vseq = (const TIn *)a.v + seq0 * a.dv + row0;
+        const TIn *bseq = (const TIn *)a.beta + seq0 * a.dv + row0;
+        const TG *gseq = (const TG *)a.gy + seq0 * a.dv + row0;
+        const TIn *dseq = (const TIn *)a.dt + seq0;
+        BwdStager<DK, TIn, TG> st;
+        {
+            const size_t tn = (size_t)(a.nsb - 1) * kSB;
+            st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
+                    gseq + tn * vb_tok, dseq + tn * a.H, a.T - (int)tn, a.H, a.dv, tid);
+            st.commit(lds + ((a.nsb - 1) & 1) * S::kFloats, A, Ip, tid, false);
+        }
+        float ckS[N];
+        bd2_ck_load<N, L::kNP>(ckb + (size_t)(a.nsb - 1) * ck_stride, tid, ckS);
+        __syncthreads();
+
+        for (int sb = a.nsb - 1; sb >= 0; --sb) {
+            const float *cur = lds + (sb & 1) * S::kFloats;
+            const int t0 = sb * kSB;
+            if (sb > 0) {
+                const size_t tn = (size_t)(t0 - kSB);
+                st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
+                        gseq + tn * vb_tok, dseq + tn * a.H, a.T - (int)tn, a.H, a.dv, tid);
+            }
+            auto replay = [&](int e, float *x) {
+                const float2 gc = *(const float2 *)(cur + S::kGate + 2 * e);
+                const float2 rw = *(const float2 *)(cur + S::kRows + e * S::kRowFloats + 4 * row_local);
+                bd4_update_lane<DK>(cur + e * S::kColFloats + LT::col(g, 0, 0), gc.x, gc.y, rw.x, rw.y, x);
+            };
+            float acc[16];      // this half's row partials: gbv, gb, da, dc of its 4 tokens
+            // tokens 2qd and 2qd + 1, replayed from the checkpoint, walked in reverse
+            auto quarter = [&](const int qd) {
+                float mS[N], x0[N], x1[N];
+#pragma unroll
+                for (int i = 0; i < N; ++i) mS[i] = ckS[i];
+                for (int e = 0; e < 2 * qd; ++e) replay(e, mS);
+#pragma unroll
+                for (int i = 0; i < N; ++i) x0[i] = mS[i];
+                replay(2 * qd, x0);
+#pragma unroll
+                for (int i = 0; i < N; ++i) x1[i] = x0[i];
+                replay(2 * qd + 1, x1);
+                if (qd == 3 && sb == a.nsb - 1) final_adjoint(x1);   // tokens past T are neutral
+                const int e1 = 2 * qd + 1, e0 = 2 * qd;
+                __builtin_amdgcn_sched_barrier(0);
+                bd4_reverse_token<DK>(cur, e1, x1, x0, Gh, GS, row_local, g, lane,
+                                      red + (e1 * kWaves + wave) * 2 * DK,
+                                      acc[e1 % 4], acc[e1 % 4 + 4], acc[e1 % 4 + 8], acc[e1 % 4 + 12]);
+                __builtin_amdgcn_sched_barrier(0);
+                bd4_reverse_token<DK>(cur, e0, x0, mS, Gh, GS, row_local, g, lane,
+                                      red + (e0 * kWaves + wave) * 2 * DK,
+                                      acc[e0 % 4], acc[e0 % 4 + 4], acc[e0 % 4 + 8], acc[e0 % 4 + 12]);
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            quarter(3);
+            quarter(2);
+            bwd_row_sums(acc, g, rs + 4 * 4 * kRowsPerWG + row_local);
+            float nS[N];
+            if (sb > 0) bd2_ck_load<N, L::kNP>(ckb + (size_t)(sb - 1) * ck_stride, tid, nS);
+            quarter(1);
+            quarter(0);
+            bwd_row_sums(acc, g, rs + row_local);
+            if (sb > 0) st.commit(lds + ((sb - 1) & 1) * S::kFloats, A, Ip, tid, false);
+            __syncthreads();
+            bd_bwd_epilogue<DK>(a, cur, red, rs, tid, t0, rb, bh, row0, seq0, bth);
+            __syncthreads();
+            if (sb > 0) {
+#pragma unroll
+                for (int i = 0; i < N; ++i) ckS[i] = nS[i];
+            }
+        }
+        // the start state h_0 = P_0 mu_0: gmu0 = P_0 G_h, gP0 = S + sym(G_h mu0^T)
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+            const size_t o = srow + LT::col(g, m, 0);
+            float p0[10], m0[4] = {0.f, 0.f, 0.f, 0.f};
+            float *gs = GS + 10 * m;
+            const float *gh = Gh + 4 * m;
+            if (a.mu0) {
+                const float *pb = a.P0 + o * 4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = i; j < 4; ++j) p0[up4(i, j)] = pb[4 * i + j];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m0[e] = a.mu0[o + e];
+            } else {
+#pragma unroll
+                for (int x = 0; x < 10; ++x) p0[x] = (x == 0 || x == 4 || x == 7 || x == 9) ? Ip : 0.f;
+            }
+            if (a.gmu0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc = fmaf(p0[up4(i, j)], gh[j], acc);
+                    a.gmu0[o + i] = acc;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                gs[up4(i, i)] = fmaf(gh[i], m0[i], gs[up4(i, i)]);
+#pragma unroll
+                for (int j = i + 1; j < 4; ++j)
+                    gs[up4(i, j)] = fmaf(0.5f, fmaf(gh[i], m0[j], gh[j] * m0[i]), gs[up4(i, j)]);
+            }
+            if (a.gP0) store_gp0(o, gs);
+        }
+    }
+    // this row block's sum of tr(gP0) (the default start P_0 = I_prior Id feeds gI_prior)
+    float gsum = 0.f;
+#pragma unroll
+    for (int m = 0; m < NB; ++m) gsum += (GS[10 * m] + GS[10 * m + 4]) + (GS[10 * m + 7] + GS[10 * m + 9]);
+    bd_bwd_trace_partial(a, gsum, rs, tid, (size_t)bh * rb_per_head + rb);
+}
+
+// Checkpoint pass of either block size: the forward's update without readout,
+// staged like the forward (no q), storing the state before tokens 0, 8, 16, ...
+template <int DK, int BS, typename TIn>
+__global__ __launch_bounds__(kThreads) void bd_ckpt_kernel(BdBwdArgs a) {
+    using LT = LaneTile<DK>;
+    using L = BdLane<DK, BS>;
+    using SG = Stage<DK>;
+    constexpr int C = 16;
+    extern __shared__ float lds[];
+    const int rb_per_head = a.dv / kRowsPerWG;
+    int wg = blockIdx.x;
+    if (a.xcd_remap) {
+        const int per_xcd = a.nwg / 8;
+        wg = (wg % 8) * per_xcd + wg / 8;
+    }
+    const int bh = wg / rb_per_head, rb = wg % rb_per_head;
+    const int row0 = rb * kRowsPerWG;
+    const int b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane & (kLanesPerRow - 1);
+    const int row_local = wave * kRowsPerWave + (lane >> 4);
+    const float A = a.A[h], Ip = a.Ip[h];
+    float st[L::kN];
+    if constexpr (BS == 2) bd2_start<DK>(a.mu0, a.P0, ((size_t)bh * a.dv + row0 + row_local) * DK, g, Ip, st);
+    else bd4_start<DK>(a.mu0, a.P0, ((size_t)bh * a.dv + row0 + row_local) * DK, g, Ip, st);
+    const size_t ck_stride = (size_t)rb_per_head * kThreads * L::kNP;
+    float *ckb = a.ck + ((size_t)bh * a.nsb * rb_per_head + rb) * (kThreads * L::kNP);
+
+    const size_t seq = (size_t)b * a.T * a.H + h;
+    const TIn *kseq = (const TIn *)a.k + seq * DK;
+    const TIn *vseq = (const TIn *)a.v + seq * a.dv + row0;
+    const TIn *bseq = (const TIn *)a.beta + seq * a.dv + row0;
+    const TIn *dseq = (const TIn *)a.dt + seq;
+    const size_t kq_tok = (size_t)a.H * DK, vb_tok = (size_t)a.H * a.dv;
+    const int nchunks = (a.T + C - 1) / C;
+    Stager<DK, C, TIn, false> sg;
+    sg.load(kseq, kseq, vseq, bseq, dseq, a.T, a.H, a.dv, tid);
+    sg.commit(lds, A, Ip, tid, false);
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * C;
+        const bool more = c + 1 < nchunks;
+        if (more) {
+            const size_t tn = (size_t)(t0 + C);
+            sg.load(kseq + tn * kq_tok, kseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
+                    dseq + tn * a.H, a.T - (t0 + C), a.H, a.dv, tid);
+        }
+        const float *buf = lds + (c & 1) * C * SG::kTokFloats;
+        const float *rows = buf + C * SG::kColFloats + 2 * row_local;
+        const float *gates = buf + C * (SG::kColFloats + SG::kRowFloats);
+#pragma unroll 2
+        for (int u = 0; u < C; ++u) {
+            if (u % kSB == 0 && (t0 + u) / kSB < a.nsb)
+                bd2_ck_store<L::kN, L::kNP>(ckb + (size_t)((t0 + u) / kSB) * ck_stride, tid, st);
+            const float2 gc = *(const float2 *)(gates + 2 * u);
+            const float2 rw = *(const float2 *)(rows + u * SG::kRowFloats);
+            if constexpr (BS == 2)
+                bd2_update<DK>(buf + u * SG::kColFloats + LT::col(g, 0, 0), gc.x, gc.y, rw.x, rw.y, st);
+            else
+                bd4_update_lane<DK>(buf + u * SG::kColFloats + LT::col(g, 0, 0), gc.x, gc.y, rw.x, rw.y, st);
+        }
+        if (more) sg.commit(lds + ((c + 1) & 1) * C * SG::kTokFloats, A, Ip, tid, false);
+        __syncthreads();
     }
 }
 
@@ -4170,10 +4538,11 @@ struct BdBwdWs {
     float *ck, *pqk, *ps, *gabh, *gibh, *pI0;
     size_t bytes;
 };
-BdBwdWs plan_bd_bwd_ws(void *base, int B, int T, int H, int dk, int dv) {
+BdBwdWs plan_bd_bwd_ws(void *base, int B, int T, int H, int dk, int dv, int block) {
     const size_t nsb = (size_t)(T + kSB - 1) / kSB, nrb = (size_t)dv / kRowsPerWG;
     const size_t bh = (size_t)B * H, bth = bh * T;
-    const size_t kc = (size_t)dk / kLanesPerRow, lane_np = (kc + 3 * (kc / 2) + 3) / 4 * 4;
+    const size_t kc = (size_t)dk / kLanesPerRow;
+    const size_t lane_np = (kc + (block == 2 ? 3 * (kc / 2) : 10 * (kc / 4)) + 3) / 4 * 4;
     size_t off = 0;
     auto take = [&](size_t floats) {
         const size_t o = off;
@@ -4191,15 +4560,17 @@ BdBwdWs plan_bd_bwd_ws(void *base, int B, int T, int H, int dk, int dv) {
     return w;
 }
 
-template <int DK, typename TIn, typename TG>
-palimpsa_status launch_bd2_bwd(const BdBwdArgs &a, const BdBwdWs &w, float *gq, float *gk, float *gdt, float *gA,
-                               float *gIp, int dt_bf16, hipStream_t s) {
+template <int DK, int BS, typename TIn, typename TG>
+palimpsa_status launch_bd_bwd(const BdBwdArgs &a, const BdBwdWs &w, float *gq, float *gk, float *gdt, float *gA,
+                              float *gIp, int dt_bf16, hipStream_t s) {
     (void)hipGetLastError();
     const size_t ck_lds = fwd_lds_bytes<DK, 16>();
     if (a.T > 0)
-        hipLaunchKernelGGL((bd2_ckpt_kernel<DK, TIn>), dim3(a.nwg), dim3(kThreads), ck_lds, s, a);
+        hipLaunchKernelGGL((bd_ckpt_kernel<DK, BS, TIn>), dim3(a.nwg), dim3(kThreads), ck_lds, s, a);
     const size_t lds = (size_t)BwdStage<DK>::kTotal * sizeof(float);
-    auto kern = bd2_bwd_kernel<DK, TIn, TG>;
+    void (*kern)(BdBwdArgs);
+    if constexpr (BS == 2) kern = bd2_bwd_kernel<DK, TIn, TG>;
+    else kern = bd4_bwd_kernel<DK, TIn, TG>;
     if (lds > 64 * 1024 &&
         hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return PALIMPSA_ERR_HIP;
@@ -4220,12 +4591,15 @@ palimpsa_status launch_bd2_bwd(const BdBwdArgs &a, const BdBwdWs &w, float *gq, 
 }
 
 template <typename TIn, typename TG>
-palimpsa_status launch_bd2_bwd_d(int dk, const BdBwdArgs &a, const BdBwdWs &w, float *gq, float *gk, float *gdt,
-                                 float *gA, float *gIp, int dt_bf16, hipStream_t s) {
+palimpsa_status launch_bd_bwd_d(int dk, int block, const BdBwdArgs &a, const BdBwdWs &w, float *gq, float *gk,
+                                float *gdt, float *gA, float *gIp, int dt_bf16, hipStream_t s) {
+    if (block == 4)
+        return dk == 64 ? launch_bd_bwd<64, 4, TIn, TG>(a, w, gq, gk, gdt, gA, gIp, dt_bf16, s)
+                        : launch_bd_bwd<128, 4, TIn, TG>(a, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
     switch (dk) {
-    case 32: return launch_bd2_bwd<32, TIn, TG>(a, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
-    case 64: return launch_bd2_bwd<64, TIn, TG>(a, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
-    default: return launch_bd2_bwd<128, TIn, TG>(a, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    case 32: return launch_bd_bwd<32, 2, TIn, TG>(a, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    case 64: return launch_bd_bwd<64, 2, TIn, TG>(a, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
+    default: return launch_bd_bwd<128, 2, TIn, TG>(a, w, gq, gk, gdt, gA, gIp, dt_bf16, s);
     }
 }
 
@@ -4328,8 +4702,10 @@ palimpsa_status palimpsa_step_blockdiag(const void *q, const void *k, const void
 }
 
 size_t palimpsa_bwd_blockdiag_workspace_size(int B, int T, int H, int dk, int dv, int block) {
-    if (B <= 0 || H <= 0 || T < 0 || block != 2 || !head_ok(dk) || !dv_ok(dv)) return 0;
-    return plan_bd_bwd_ws(nullptr, B, T, H, dk, dv).bytes;
+    if (B <= 0 || H <= 0 || T < 0 || (block != 2 && block != 4) || !head_ok(dk) || (block == 4 && dk == 32) ||
+        !dv_ok(dv))
+        return 0;
+    return plan_bd_bwd_ws(nullptr, B, T, H, dk, dv, block).bytes;
 }
 
 palimpsa_status palimpsa_bwd_blockdiag(const void *q, const void *k, const void *v, const void *beta,
@@ -4350,7 +4726,7 @@ palimpsa_status palimpsa_bwd_blockdiag(const void *q, const void *k, const void 
     if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || block <= 0 || !dtype_ok(in_dtype) ||
         !dtype_ok(gy_dtype))
         return PALIMPSA_ERR_INVALID_ARG;
-    if (block != 2 || !head_ok(dk) || !dv_ok(dv))
+    if ((block != 2 && block != 4) || !head_ok(dk) || (block == 4 && dk == 32) || !dv_ok(dv))
         return PALIMPSA_ERR_UNSUPPORTED;
     const void *vec_ptrs[] = {q, k, v, beta, gy, P0, gPT, gP0, gq, gk, workspace};
     for (const void *p : vec_ptrs)
@@ -4364,7 +4740,7 @@ palimpsa_status palimpsa_bwd_blockdiag(const void *q, const void *k, const void 
     if (nwg > 0x7fffffffLL || (long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 46) ||
         64LL * H * (dk > dv ? dk : dv) >= (1LL << 31) || (long long)B * H * 2 > 0x7fffffffLL)
         return PALIMPSA_ERR_UNSUPPORTED;
-    const BdBwdWs w = plan_bd_bwd_ws(workspace, B, T, H, dk, dv);
+    const BdBwdWs w = plan_bd_bwd_ws(workspace, B, T, H, dk, dv, block);
     if (workspace_bytes < w.bytes) return PALIMPSA_ERR_INVALID_ARG;
 
     BdBwdArgs a = {};
@@ -4377,10 +4753,10 @@ palimpsa_status palimpsa_bwd_blockdiag(const void *q, const void *k, const void 
     hipStream_t s = (hipStream_t)stream;
     const bool bf_in = in_dtype == PALIMPSA_BF16, bf_gy = gy_dtype == PALIMPSA_BF16;
     const int dtb = bf_in ? 1 : 0;
-    if (bf_in && bf_gy) return launch_bd2_bwd_d<bf16_t, bf16_t>(dk, a, w, gq, gk, gdt, gA, gIp, dtb, s);
-    if (bf_in) return launch_bd2_bwd_d<bf16_t, float>(dk, a, w, gq, gk, gdt, gA, gIp, dtb, s);
-    if (bf_gy) return launch_bd2_bwd_d<float, bf16_t>(dk, a, w, gq, gk, gdt, gA, gIp, dtb, s);
-    return launch_bd2_bwd_d<float, float>(dk, a, w, gq, gk, gdt, gA, gIp, dtb, s);
+    if (bf_in && bf_gy) return launch_bd_bwd_d<bf16_t, bf16_t>(dk, block, a, w, gq, gk, gdt, gA, gIp, dtb, s);
+    if (bf_in) return launch_bd_bwd_d<bf16_t, float>(dk, block, a, w, gq, gk, gdt, gA, gIp, dtb, s);
+    if (bf_gy) return launch_bd_bwd_d<float, bf16_t>(dk, block, a, w, gq, gk, gdt, gA, gIp, dtb, s);
+    return launch_bd_bwd_d<float, float>(dk, block, a, w, gq, gk, gdt, gA, gIp, dtb, s);
 }
 
 size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv, int flags) {

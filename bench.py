@@ -57,6 +57,12 @@ BD4_FLOPS_PER_ENTRY = 29.5
 # 50 VALU and 2 rcp slots, 72 flops): 31.5 slots and 45 flops per entry.
 BD2_BWD_SLOTS_PER_ENTRY = 31.5
 BD2_BWD_FLOPS_PER_ENTRY = 45
+# 4x4 blocks, per block and token: one replay of the update (34 VALU, 52
+# flops) and the reverse step (Cholesky factor 16 VALU + 4 v_rsq_f32, two
+# solves 40, G_h, S and the gradient terms 104: 160 VALU and 8 rsq slots,
+# 248 flops): 50.5 slots and 75 flops per entry.
+BD4_BWD_SLOTS_PER_ENTRY = 50.5
+BD4_BWD_FLOPS_PER_ENTRY = 75
 
 
 def alu_peak_tflops():
@@ -346,31 +352,37 @@ def blockdiag4_extra(torch, pm, w, g, steps):
                          "per_entry": "18.5 VALU + 1 v_rsq_f32 = 20.5 slots, 29.5 flops"}}
 
 
-def blockdiag_backward_extra(torch, pm, workloads, w, g, steps):
-    """palimpsa_bwd_blockdiag (backward of the 2x2 block-diagonal path) on the
+def blockdiag_backward_extra(torch, pm, workloads, w, g, steps, block=2):
+    """palimpsa_bwd_blockdiag (backward of the block-diagonal path) on the
     same workload, timed as one call (checkpoint pass, reverse walk, three
     finishing kernels)."""
     dev = g["q"].device
     gr = workloads.upstream_grads(w.B, w.T, w.H, w.dv, w.dk, w.dtype, seed=2)
     gy, gmuT = gr["gy"].to(dev), gr["gmuT"].to(dev)
-    ws = torch.empty(pm.bwd_blockdiag_workspace_size(w.B, w.T, w.H, w.dk, w.dv, 2), dtype=torch.uint8, device=dev)
+    ws = torch.empty(pm.bwd_blockdiag_workspace_size(w.B, w.T, w.H, w.dk, w.dv, block), dtype=torch.uint8,
+                     device=dev)
     args = (g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], gy)
-    out = pm.bwd_blockdiag(*args, block=2, gmuT=gmuT, workspace=ws)
-    fn = lambda: pm.bwd_blockdiag(*args, block=2, gmuT=gmuT, workspace=ws, out=out)
+    out = pm.bwd_blockdiag(*args, block=block, gmuT=gmuT, workspace=ws)
+    fn = lambda: pm.bwd_blockdiag(*args, block=block, gmuT=gmuT, workspace=ws, out=out)
     _, per = time_launches(fn, steps, 2, torch)
     avg_s = sum(per) / len(per) / 1e3
     entries = w.B * w.H * w.T * w.dv * w.dk
-    peak = LANE_OPS_PER_S / BD2_BWD_SLOTS_PER_ENTRY * BD2_BWD_FLOPS_PER_ENTRY / 1e12
-    achieved = entries * BD2_BWD_FLOPS_PER_ENTRY / avg_s / 1e12
-    return {"workload": w.name + ", 2x2 block-diagonal backward (gq, gk, gv, gbeta, gdt, gA, gIp, gmu0, gP0)",
+    slots, flops = ((BD2_BWD_SLOTS_PER_ENTRY, BD2_BWD_FLOPS_PER_ENTRY) if block == 2 else
+                    (BD4_BWD_SLOTS_PER_ENTRY, BD4_BWD_FLOPS_PER_ENTRY))
+    peak = LANE_OPS_PER_S / slots * flops / 1e12
+    achieved = entries * flops / avg_s / 1e12
+    per_entry = ("replay 5.5 + reverse 25 VALU + 0.5 v_rcp_f32 = 31.5 slots, 45 flops" if block == 2 else
+                 "replay 8.5 + reverse 40 VALU + 1 v_rsq_f32 = 50.5 slots, 75 flops")
+    return {"workload": w.name + ", %dx%d block-diagonal backward (gq, gk, gv, gbeta, gdt, gA, gIp, gmu0, gP0)"
+            % (block, block),
             "tokens_per_s": w.B * w.T / avg_s, "ms_per_call": avg_s * 1e3,
             "workspace_GB": ws.numel() / 1e9,
             "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                          "frac": achieved / peak,
-                         "traffic": load_traffic("bd2_bwd_layer760m_bf16_traffic.json")
+                         "traffic": load_traffic("bd%d_bwd_layer760m_bf16_traffic.json" % block)
                          if w.name.startswith("layer760m") else None,
                          "scope": "whole call (5 kernels); per-kernel split in the committed trace",
-                         "per_entry": "replay 5.5 + reverse 25 VALU + 0.5 v_rcp_f32 = 31.5 slots, 45 flops"}}
+                         "per_entry": per_entry}}
 
 
 def fig7_extra(torch, pm, workloads, dev, D, steps):
@@ -487,6 +499,8 @@ def main():
         out["blockdiag_decode"] = blockdiag_decode_extra(torch, pm, workloads, max(64, args.steps))
         out["blockdiag4"] = blockdiag4_extra(torch, pm, w, g, max(10, args.steps // 5))
         out["blockdiag_backward"] = blockdiag_backward_extra(torch, pm, workloads, w, g, max(5, args.steps // 5))
+        out["blockdiag4_backward"] = blockdiag_backward_extra(torch, pm, workloads, w, g, max(5, args.steps // 5),
+                                                              block=4)
         out["recurrent_shape"] = [fig7_extra(torch, pm, workloads, dev, D, 5) for D in (512, 2048)]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads or w.B * w.H)

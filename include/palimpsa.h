@@ -410,9 +410,9 @@ palimpsa_status palimpsa_step_blockdiag(const void *q, const void *k, const void
 size_t palimpsa_bwd_blockdiag_workspace_size(int B, int T, int H, int dk, int dv, int block);
 
 /*
- * Reverse-mode derivative of palimpsa_fwd_blockdiag with 2x2 blocks (the
- * block-diagonal update of the slides' backup frame "dropping precision
- * correlations changes the mean", App. A.3-A.5) for
+ * Reverse-mode derivative of palimpsa_fwd_blockdiag (the block-diagonal
+ * update of the slides' backup frame "dropping precision correlations changes
+ * the mean", App. A.3-A.5) for
  *
  *     L = sum(gy . y) + sum(gmuT . muT) + sum(gPT . PT),
  *
@@ -428,19 +428,22 @@ size_t palimpsa_bwd_blockdiag_workspace_size(int B, int T, int H, int dk, int dv
  *             (mu0 and P0 both given or both NULL: mu0 = 0, P0 = I_prior Id)
  *   gy        [B, T, H, dv]  gy_dtype   dL/dy
  *   gmuT      [B, H, dv, dk] float32    dL/dmuT, or NULL (zero)
- *   gPT       [B, H, dv, dk/2, 2, 2]    dL/dPT (all four entries), or NULL (zero)
+ *   gPT       [B, H, dv, dk/block, block, block]  dL/dPT (every entry), or NULL (zero)
  * Outputs (float32, overwritten):
  *   gq, gk    [B, T, H, dk]     gv, gbeta [B, T, H, dv]     gdt [B, T, H]
  *   gA, gIp   [H]   summed over the batch; with the default start state gIp
  *             includes the start precision's share
  *   gmu0      [B, H, dv, dk]    dL/dmu0, or NULL
- *   gP0       [B, H, dv, dk/2, 2, 2]  the gradient for a symmetric P0 (both
- *             off-diagonal entries hold half of dL/dp01), or NULL
- *   workspace at least palimpsa_bwd_blockdiag_workspace_size(B, T, H, dk, dv, 2)
- *             bytes, 16-byte aligned, caller-owned; contents on entry ignored
+ *   gP0       [B, H, dv, dk/block, block, block]  the gradient for a symmetric
+ *             P0 (written in full and symmetric: each off-diagonal pair holds
+ *             half of the derivative by their shared value), or NULL
+ *   workspace at least palimpsa_bwd_blockdiag_workspace_size(B, T, H, dk, dv,
+ *             block) bytes, 16-byte aligned, caller-owned; contents on entry
+ *             ignored
  *
- * block == 2 with dk in {32, 64, 128}, dv a multiple of 16 up to 1024 (else
- * PALIMPSA_ERR_UNSUPPORTED).  q, k, v, beta, gy, P0, gPT, gP0, gq, gk and the
+ * block == 2 with dk in {32, 64, 128}, or block == 4 with dk in {64, 128}; dv a
+ * multiple of 16 up to 1024 (else PALIMPSA_ERR_UNSUPPORTED).  A 4x4 block's
+ * Cholesky factor serves both of its solves per token.  q, k, v, beta, gy, P0, gPT, gP0, gq, gk and the
  * workspace must be 16-byte aligned, the float32 arrays 4-byte aligned.
  * float32 arithmetic; results are deterministic (fixed reduction order).
  * T == 0 copies gmuT to gmu0 and the symmetric part of gPT to gP0.

@@ -349,8 +349,8 @@ BD_BWD_CASES = [
     (dict(mu0=FAKE), 1), (dict(P0=FAKE), 1), (dict(B=0), 1), (dict(T=-1), 1), (dict(H=0), 1), (dict(dk=0), 1),
     (dict(block=0), 1), (dict(ind=2), 1), (dict(gyd=5), 1), (dict(wsb=64), 1),
     (dict(q=None, T=0, A=None), 1),
-    (dict(block=1), 2), (dict(block=4), 2), (dict(block=3), 2), (dict(dk=48), 2), (dict(dv=1040), 2),
-    (dict(dv=8), 2),
+    (dict(block=1), 2), (dict(block=3), 2), (dict(block=8), 2), (dict(block=4, dk=32), 2), (dict(dk=48), 2),
+    (dict(dv=1040), 2), (dict(dv=8), 2),
     (dict(q=FAKE + 4), 3), (dict(gy=FAKE + 8), 3), (dict(P0=FAKE + 8, mu0=FAKE), 3),
     (dict(mu0=FAKE + 2, P0=FAKE), 3), (dict(gPT=FAKE + 4), 3), (dict(gP0=FAKE + 8), 3), (dict(gq=FAKE + 4), 3),
     (dict(gmuT=FAKE + 1), 3), (dict(gmu0=FAKE + 2), 3), (dict(gdt=FAKE + 2), 3), (dict(dt=FAKE + 1), 3),
@@ -365,19 +365,23 @@ def test_blockdiag_bwd_rejects_invalid_calls(lib, over, status):
 
 
 def test_bwd_blockdiag_workspace_size_host_logic(lib):
-    """Checkpoints of the lane states (h, then three entries per 2x2 block,
-    padded to float4s) every 8 tokens, then the exact backward's partials."""
+    """Checkpoints of the lane states (h, then the upper triangle of each
+    block: 3 entries per 2x2 block, 10 per 4x4, padded to float4s) every 8
+    tokens, then the exact backward's partials."""
     import bayesian_metaplastic_memory_amd as pm
     pad = lambda n: (4 * n + 255) // 256 * 256
 
-    def expect(B, T, H, dk, dv):
+    def expect(B, T, H, dk, dv, block=2):
         nsb, nrb, bh = (T + 7) // 8, dv // 16, B * H
         kc = dk // 16
-        lane = (kc + 3 * (kc // 2) + 3) // 4 * 4
+        lane = (kc + (3 * (kc // 2) if block == 2 else 10 * (kc // 4)) + 3) // 4 * 4
         return (pad(bh * nsb * nrb * 256 * lane) + pad(nrb * bh * T * 2 * dk) + pad(nrb * bh * T * 2)
                 + 2 * pad(bh) + pad(bh * nrb))
     for shape in [(1, 10, 2, 32, 32), (8, 4096, 12, 128, 128), (1, 0, 3, 64, 128), (2, 9, 1, 128, 64)]:
         assert pm.bwd_blockdiag_workspace_size(*shape) == expect(*shape), shape
-    assert pm.bwd_blockdiag_workspace_size(1, 8, 2, 64, 64, block=4) == 0
+        if shape[3] > 32:
+            assert pm.bwd_blockdiag_workspace_size(*shape, block=4) == expect(*shape, block=4), shape
+    assert pm.bwd_blockdiag_workspace_size(1, 8, 2, 32, 64, block=4) == 0
+    assert pm.bwd_blockdiag_workspace_size(1, 8, 2, 64, 64, block=8) == 0
     assert pm.bwd_blockdiag_workspace_size(1, 8, 2, 48, 64) == 0
     assert pm.bwd_blockdiag_workspace_size(0, 8, 2, 64, 64) == 0

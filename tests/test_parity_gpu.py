@@ -1220,98 +1220,105 @@ def _sym_blocks(G):
     return 0.5 * (G + np.swapaxes(G, -1, -2))
 
 
-def _bd_bwd_run(inp, gy, mu0=None, P0=None, gmuT=None, gPT=None):
+def _bd_bwd_run(inp, gy, mu0=None, P0=None, gmuT=None, gPT=None, block=2):
     g = to_device(inp, DEV)
     dev = lambda t: None if t is None else t.to(DEV)
-    out = _pm().bwd_blockdiag(*gpu_args(g), dev(gy), block=2, mu0=dev(mu0), P0=dev(P0), gmuT=dev(gmuT),
+    out = _pm().bwd_blockdiag(*gpu_args(g), dev(gy), block=block, mu0=dev(mu0), P0=dev(P0), gmuT=dev(gmuT),
                               gPT=dev(gPT))
     torch.cuda.synchronize()
     return out
 
 
-def _bd_bwd_ref(inp, gy, mu0=None, P0=None, gmuT=None, gPT=None):
-    ref = oracle.bwd_blockdiag(**{n: inp[n] for n in BD_FWD_KEYS}, block=2, gy=gy, mu0=mu0, P0=P0,
+def _bd_bwd_ref(inp, gy, mu0=None, P0=None, gmuT=None, gPT=None, block=2):
+    ref = oracle.bwd_blockdiag(**{n: inp[n] for n in BD_FWD_KEYS}, block=block, gy=gy, mu0=mu0, P0=P0,
                                gmuT=gmuT, gPT=gPT)
     ref["gP0"] = _sym_blocks(ref["gP0"])
     return ref
 
 
 BD_BWD_CASES = [
-    # B, T, H, dk, dv, dtype, gy dtype, start state given, final-state gradients
-    (1, 37, 2, 32, 32, torch.float32, torch.float32, True, True),
-    (2, 64, 3, 64, 64, torch.float32, torch.float32, False, False),
-    (1, 100, 2, 128, 128, torch.bfloat16, torch.bfloat16, True, True),
-    (2, 17, 2, 64, 48, torch.float32, torch.bfloat16, True, False),
-    (1, 9, 3, 128, 64, torch.bfloat16, torch.float32, False, True),
-    (1, 1, 2, 32, 64, torch.float32, torch.float32, True, True),
-    (2, 8, 1, 128, 32, torch.float32, torch.float32, False, True),
-    (1, 150, 1, 32, 128, torch.bfloat16, torch.bfloat16, False, False),
+    # block, B, T, H, dk, dv, dtype, gy dtype, start state given, final-state gradients
+    (2, 1, 37, 2, 32, 32, torch.float32, torch.float32, True, True),
+    (2, 2, 64, 3, 64, 64, torch.float32, torch.float32, False, False),
+    (2, 1, 100, 2, 128, 128, torch.bfloat16, torch.bfloat16, True, True),
+    (2, 2, 17, 2, 64, 48, torch.float32, torch.bfloat16, True, False),
+    (2, 1, 9, 3, 128, 64, torch.bfloat16, torch.float32, False, True),
+    (2, 1, 1, 2, 32, 64, torch.float32, torch.float32, True, True),
+    (2, 2, 8, 1, 128, 32, torch.float32, torch.float32, False, True),
+    (2, 1, 150, 1, 32, 128, torch.bfloat16, torch.bfloat16, False, False),
+    (4, 1, 37, 2, 64, 32, torch.float32, torch.float32, True, True),
+    (4, 2, 64, 2, 128, 64, torch.float32, torch.float32, False, False),
+    (4, 1, 100, 2, 128, 128, torch.bfloat16, torch.bfloat16, True, True),
+    (4, 2, 17, 1, 64, 48, torch.float32, torch.bfloat16, True, False),
+    (4, 1, 1, 2, 128, 16, torch.float32, torch.float32, True, True),
+    (4, 1, 9, 3, 64, 128, torch.bfloat16, torch.float32, False, True),
 ]
 
 
-@pytest.mark.parametrize("B,T,H,dk,dv,dtype,gdtype,state,final", BD_BWD_CASES)
-def test_blockdiag_bwd_matches_oracle(B, T, H, dk, dv, dtype, gdtype, state, final):
+@pytest.mark.parametrize("block,B,T,H,dk,dv,dtype,gdtype,state,final", BD_BWD_CASES)
+def test_blockdiag_bwd_matches_oracle(block, B, T, H, dk, dv, dtype, gdtype, state, final):
     w = workloads.WORKLOADS[0].with_(B=B, H=H, dk=dk, dv=dv, dtype=dtype, A_mode="logspace16")
-    _announce("blockdiag bwd", B=B, T=T, H=H, dk=dk, dv=dv, dtype=dtype, gy=gdtype, state=state, final=final)
+    _announce("blockdiag bwd", block=block, B=B, T=T, H=H, dk=dk, dv=dv, dtype=dtype, gy=gdtype, state=state,
+              final=final)
     inp = workloads.make_inputs(w, T=T, seed=T + dk + 5 * dv)
     mu0 = P0 = None
     if state:
-        mu0, P0 = workloads.random_block_state(B, H, dv, dk, 2, inp["I_prior"], seed=T + 2)
+        mu0, P0 = workloads.random_block_state(B, H, dv, dk, block, inp["I_prior"], seed=T + 2)
     gr = workloads.upstream_grads(B, T, H, dv, dk, gdtype, seed=T + dk + 1, final=final)
-    gPT = workloads.block_state_grads(B, H, dv, dk, 2, seed=T) if final else None
-    got = _bd_bwd_run(inp, gr["gy"], mu0, P0, gr["gmuT"], gPT)
-    ref = _bd_bwd_ref(inp, gr["gy"], mu0, P0, gr["gmuT"], gPT)
+    gPT = workloads.block_state_grads(B, H, dv, dk, block, seed=T) if final else None
+    got = _bd_bwd_run(inp, gr["gy"], mu0, P0, gr["gmuT"], gPT, block=block)
+    ref = _bd_bwd_ref(inp, gr["gy"], mu0, P0, gr["gmuT"], gPT, block=block)
     for n in BD_BWD_NAMES:
-        assert_close("bd " + n, got[n], ref[n], TOL_BWD)
+        assert_close("bd%d %s" % (block, n), got[n], ref[n], TOL_BWD)
 
 
-def test_blockdiag_bwd_empty_sequence():
+@pytest.mark.parametrize("block", [2, 4])
+def test_blockdiag_bwd_empty_sequence(block):
     B, H, dk, dv = 2, 3, 64, 32
     w = workloads.WORKLOADS[0].with_(B=B, H=H, dk=dk, dv=dv)
-    _announce("blockdiag bwd T=0", B=B, H=H, dk=dk, dv=dv)
+    _announce("blockdiag bwd T=0", block=block, B=B, H=H, dk=dk, dv=dv)
     inp = workloads.make_inputs(w, T=0)
-    mu0, P0 = workloads.random_block_state(B, H, dv, dk, 2, inp["I_prior"], seed=6)
+    mu0, P0 = workloads.random_block_state(B, H, dv, dk, block, inp["I_prior"], seed=6)
     gr = workloads.upstream_grads(B, 0, H, dv, dk, torch.float32, seed=6)
-    gPT = workloads.block_state_grads(B, H, dv, dk, 2, seed=6)
-    got = _bd_bwd_run(inp, gr["gy"], mu0, P0, gr["gmuT"], gPT)
+    gPT = workloads.block_state_grads(B, H, dv, dk, block, seed=6)
+    got = _bd_bwd_run(inp, gr["gy"], mu0, P0, gr["gmuT"], gPT, block=block)
     assert torch.equal(got["gmu0"].cpu(), gr["gmuT"])
-    s01 = 0.5 * (gPT[..., 0, 1] + gPT[..., 1, 0])
-    gP0 = got["gP0"].cpu()
-    assert torch.equal(gP0[..., 0, 0], gPT[..., 0, 0]) and torch.equal(gP0[..., 1, 1], gPT[..., 1, 1])
-    assert torch.equal(gP0[..., 0, 1], s01) and torch.equal(gP0[..., 1, 0], s01)
+    assert torch.equal(got["gP0"].cpu(), 0.5 * (gPT + gPT.transpose(-1, -2)))
     assert float(got["gA"].abs().max()) == 0.0 and float(got["gIp"].abs().max()) == 0.0
     # the default start state: gI_prior collects tr(gP0) = tr(gPT)
-    got = _bd_bwd_run(inp, gr["gy"], gmuT=gr["gmuT"], gPT=gPT)
-    ref = _bd_bwd_ref(inp, gr["gy"], gmuT=gr["gmuT"], gPT=gPT)
-    assert_close("bd gIp (T=0, default start)", got["gIp"], ref["gIp"], TOL_F32)
+    got = _bd_bwd_run(inp, gr["gy"], gmuT=gr["gmuT"], gPT=gPT, block=block)
+    ref = _bd_bwd_ref(inp, gr["gy"], gmuT=gr["gmuT"], gPT=gPT, block=block)
+    assert_close("bd%d gIp (T=0, default start)" % block, got["gIp"], ref["gIp"], TOL_F32)
 
 
-def test_blockdiag_bwd_is_deterministic():
+@pytest.mark.parametrize("block", [2, 4])
+def test_blockdiag_bwd_is_deterministic(block):
     B, T, H, dk, dv = 2, 77, 2, 128, 64
     w = workloads.WORKLOADS[0].with_(B=B, H=H, dk=dk, dv=dv, dtype=torch.bfloat16, A_mode="logspace16")
-    _announce("blockdiag bwd determinism", B=B, T=T, H=H, dk=dk, dv=dv)
+    _announce("blockdiag bwd determinism", block=block, B=B, T=T, H=H, dk=dk, dv=dv)
     inp = workloads.make_inputs(w, T=T, seed=9)
     gr = workloads.upstream_grads(B, T, H, dv, dk, torch.bfloat16, seed=9)
-    a = _bd_bwd_run(inp, gr["gy"], gmuT=gr["gmuT"])
-    b = _bd_bwd_run(inp, gr["gy"], gmuT=gr["gmuT"])
+    a = _bd_bwd_run(inp, gr["gy"], gmuT=gr["gmuT"], block=block)
+    b = _bd_bwd_run(inp, gr["gy"], gmuT=gr["gmuT"], block=block)
     for n in BD_BWD_NAMES:
         assert torch.equal(a[n], b[n]), n
 
 
-def test_blockdiag_bwd_layer760m_sampled_head():
+@pytest.mark.parametrize("block", [2, 4])
+def test_blockdiag_bwd_layer760m_sampled_head(block):
     """The full 760M-layer block-diagonal backward on the GPU; the oracle runs
     one (sequence, head) pair, whose per-token and per-sequence gradients
     compare directly."""
     w = workloads.WORKLOADS[2]
-    b, h = 3, 7
-    _announce("blockdiag bwd 760M layer bf16", B=w.B, H=w.H, T=w.T, d=w.dk, sampled=(b, h))
+    b, h = (3, 7) if block == 2 else (6, 2)
+    _announce("blockdiag bwd 760M layer bf16", block=block, B=w.B, H=w.H, T=w.T, d=w.dk, sampled=(b, h))
     inp = workloads.make_inputs(w)
     gr = workloads.upstream_grads(w.B, w.T, w.H, w.dv, w.dk, w.dtype, seed=12)
-    gPT = workloads.block_state_grads(w.B, w.H, w.dv, w.dk, 2, seed=12)
-    got = _bd_bwd_run(inp, gr["gy"], gmuT=gr["gmuT"], gPT=gPT)
+    gPT = workloads.block_state_grads(w.B, w.H, w.dv, w.dk, block, seed=12)
+    got = _bd_bwd_run(inp, gr["gy"], gmuT=gr["gmuT"], gPT=gPT, block=block)
     sub = oracle.select_heads(inp, [(b, h)])
     ref = _bd_bwd_ref(sub, to_np(gr["gy"])[b:b + 1, :, h:h + 1], gmuT=to_np(gr["gmuT"])[b:b + 1, h:h + 1],
-                      gPT=to_np(gPT)[b:b + 1, h:h + 1])
+                      gPT=to_np(gPT)[b:b + 1, h:h + 1], block=block)
     for n in ("gq", "gk", "gv", "gbeta"):
         assert_close("bd %s (sampled)" % n, to_np(got[n])[b:b + 1, :, h:h + 1], ref[n], TOL_BWD)
     assert_close("bd gdt (sampled)", to_np(got["gdt"])[b:b + 1, :, h:h + 1], ref["gdt"], TOL_BWD)
