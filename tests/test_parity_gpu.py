@@ -1272,6 +1272,40 @@ def test_blockdiag_bwd_matches_oracle(block, B, T, H, dk, dv, dtype, gdtype, sta
         assert_close("bd%d %s" % (block, n), got[n], ref[n], TOL_BWD)
 
 
+@pytest.mark.parametrize("block,dk,dtype", [(2, 128, torch.bfloat16), (2, 32, torch.float32), (4, 64, torch.bfloat16)])
+def test_blockdiag_bwd_widest_value_dimension(block, dk, dtype):
+    """dv = 1024, the widest the path takes (64 row blocks per head), from a
+    random state with final-state gradients."""
+    B, T, H, dv = 1, 45, 1, 1024
+    w = workloads.WORKLOADS[0].with_(B=B, H=H, dk=dk, dv=dv, dtype=dtype, A_mode="logspace16")
+    _announce("blockdiag bwd dv=1024", block=block, B=B, T=T, H=H, dk=dk, dv=dv, dtype=dtype)
+    inp = workloads.make_inputs(w, T=T, seed=dk + block)
+    mu0, P0 = workloads.random_block_state(B, H, dv, dk, block, inp["I_prior"], seed=dk)
+    gr = workloads.upstream_grads(B, T, H, dv, dk, dtype, seed=dk + 3)
+    gPT = workloads.block_state_grads(B, H, dv, dk, block, seed=dk)
+    got = _bd_bwd_run(inp, gr["gy"], mu0, P0, gr["gmuT"], gPT, block=block)
+    ref = _bd_bwd_ref(inp, gr["gy"], mu0, P0, gr["gmuT"], gPT, block=block)
+    for n in BD_BWD_NAMES:
+        assert_close("bd%d %s (dv=1024)" % (block, n), got[n], ref[n], TOL_BWD)
+
+
+@pytest.mark.parametrize("block", [2, 4])
+def test_blockdiag_bwd_no_forgetting(block):
+    """dt = 0 everywhere: alpha = 1 and c = 0 at every token, so P only
+    accumulates evidence and gI_prior keeps only the default start's share;
+    gdt and gA are the derivatives at dt = 0."""
+    B, T, H, dk, dv = 2, 50, 2, 64, 32
+    w = workloads.WORKLOADS[0].with_(B=B, H=H, dk=dk, dv=dv)
+    _announce("blockdiag bwd alpha=1", block=block, B=B, T=T, H=H, dk=dk, dv=dv)
+    inp = workloads.make_inputs(w, T=T, seed=21)
+    inp["dt"] = torch.zeros_like(inp["dt"])
+    gr = workloads.upstream_grads(B, T, H, dv, dk, torch.float32, seed=21)
+    got = _bd_bwd_run(inp, gr["gy"], gmuT=gr["gmuT"], block=block)
+    ref = _bd_bwd_ref(inp, gr["gy"], gmuT=gr["gmuT"], block=block)
+    for n in BD_BWD_NAMES:
+        assert_close("bd%d %s (alpha=1)" % (block, n), got[n], ref[n], TOL_BWD)
+
+
 @pytest.mark.parametrize("block", [2, 4])
 def test_blockdiag_bwd_empty_sequence(block):
     B, H, dk, dv = 2, 3, 64, 32
