@@ -1037,7 +1037,8 @@ def test_frozen_value_expansion(dv):
 
 @pytest.mark.parametrize("dk,dv,dtype,state,T", [(32, 32, torch.float32, False, 37), (64, 48, torch.float32, True, 100),
                                                  (128, 128, torch.bfloat16, True, 70), (128, 64, torch.float32, False, 1),
-                                                 (64, 128, torch.bfloat16, False, 160)])
+                                                 (64, 128, torch.bfloat16, False, 160),
+                                                 (128, 1024, torch.bfloat16, True, 45), (32, 1024, torch.float32, False, 45)])
 def test_blockdiag_matches_oracle(dk, dv, dtype, state, T):
     w = workloads.WORKLOADS[0].with_(B=2, H=2, dk=dk, dv=dv, dtype=dtype, A_mode="logspace16")
     _announce("blockdiag fwd", B=w.B, H=w.H, T=T, dk=dk, dv=dv, dtype=dtype, state=state)
@@ -1133,7 +1134,8 @@ def test_blockdiag_steps_follow_the_forward():
 
 @pytest.mark.parametrize("dk,dv,dtype,state,T", [(64, 48, torch.float32, True, 37), (128, 128, torch.bfloat16, True, 70),
                                                  (128, 64, torch.float32, False, 1), (64, 128, torch.bfloat16, False, 100),
-                                                 (128, 32, torch.float32, True, 0)])
+                                                 (128, 32, torch.float32, True, 0),
+                                                 (64, 1024, torch.bfloat16, True, 45)])
 def test_blockdiag4_matches_oracle(dk, dv, dtype, state, T):
     """4x4 precision blocks (Cholesky per block) against the oracle's block-diagonal forward."""
     w = workloads.WORKLOADS[0].with_(B=2, H=2, dk=dk, dv=dv, dtype=dtype, A_mode="logspace16")
