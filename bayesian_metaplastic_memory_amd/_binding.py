@@ -90,6 +90,23 @@ def _stream_handle(device: torch.device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def check_params(A, I_prior, dt=None, beta=None, I0=None):
+    """Check the data preconditions the library does not check itself (they
+    live in device memory): A >= 0 and finite, I_prior > 0 and finite, and if
+    given dt >= 0, beta >= 0, I0 > 0, all finite.  Raises ValueError naming
+    the first violation.  Opt-in, since it reads the values back to the host
+    (one synchronisation per tensor); call it once per set of parameters, not
+    per step."""
+    def bad(t, positive):
+        x = t.detach().float()
+        lo = (x <= 0) if positive else (x < 0)
+        return bool((~torch.isfinite(x)).any().item()) or bool(lo.any().item())
+    for t, name, positive in ((A, "A", False), (I_prior, "I_prior", True), (dt, "dt", False),
+                              (beta, "beta", False), (I0, "I0", True)):
+        if t is not None and bad(t, positive):
+            raise ValueError("%s must be finite and %s" % (name, "> 0" if positive else ">= 0"))
+
+
 def _check(t, name, shape, dtype, device):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)

@@ -38,7 +38,8 @@
  *    exception crosses this interface.
  *  - Data preconditions that are NOT checked (they live in device memory):
  *    A >= 0 and finite, I_prior > 0, beta >= 0, dt >= 0, I0 > 0, all inputs
- *    finite.  Violations give unspecified values, never a fault.
+ *    finite.  Violations give unspecified values, never a fault.  (The Python
+ *    binding's check_params tests them on request.)
  *  - Supported head sizes: dk in {32, 64, 128}; dv any multiple of 16 from
  *    16 to 1024 (so the value expansion dv = 2 dk of the pages' model is
  *    covered).  The chunked forward and the decode step also take heads as

@@ -385,3 +385,21 @@ def test_bwd_blockdiag_workspace_size_host_logic(lib):
     assert pm.bwd_blockdiag_workspace_size(1, 8, 2, 64, 64, block=8) == 0
     assert pm.bwd_blockdiag_workspace_size(1, 8, 2, 48, 64) == 0
     assert pm.bwd_blockdiag_workspace_size(0, 8, 2, 64, 64) == 0
+
+
+def test_check_params_host_logic():
+    """The opt-in value check of the data preconditions (CPU tensors here)."""
+    import torch
+    import bayesian_metaplastic_memory_amd as pm
+    A, Ip = torch.tensor([0.0, 1.0, 16.0]), torch.tensor([1.0, 0.5, 2.0])
+    pm.check_params(A, Ip, dt=torch.zeros(2, 3), beta=torch.rand(2, 3), I0=torch.ones(4))
+    bad = [dict(A=torch.tensor([-1.0, 1.0, 1.0])), dict(I_prior=torch.tensor([1.0, 0.0, 1.0])),
+           dict(A=torch.tensor([float("nan"), 1.0, 1.0])), dict(I_prior=torch.tensor([1.0, float("inf"), 1.0])),
+           dict(dt=torch.tensor([-1e-3])), dict(beta=torch.tensor([-0.5])), dict(I0=torch.tensor([0.0])),
+           dict(dt=torch.tensor([1.0, float("nan")], dtype=torch.bfloat16))]
+    for over in bad:
+        kw = dict(A=A, I_prior=Ip)
+        kw.update(over)
+        name = next(iter(over))
+        with pytest.raises(ValueError, match=name):
+            pm.check_params(**kw)
