@@ -57,14 +57,14 @@ def load_library() -> ctypes.CDLL:
             lib.palimpsa_bwd_frozen.argtypes = [vp] * 5 + [fp] * 3 + [vp, fp] + [fp] * 8 + [i] * 7 + [vp, sz, vp]
             lib.palimpsa_bwd_frozen.restype = i
             lib.palimpsa_bwd_workspace_size.restype = sz
-            lib.palimpsa_fwd_blockdiag.argtypes = [vp] * 5 + [fp] * 4 + [vp, fp, fp] + [i] * 8 + [vp]
+            lib.palimpsa_fwd_blockdiag.argtypes = [vp] * 5 + [fp] * 4 + [vp, fp, fp] + [i] * 9 + [vp, sz, vp]
             lib.palimpsa_fwd_blockdiag.restype = i
             lib.palimpsa_step_blockdiag.argtypes = [vp] * 5 + [fp] * 4 + [vp] + [i] * 7 + [vp]
             lib.palimpsa_step_blockdiag.restype = i
             lib.palimpsa_bwd_blockdiag_workspace_size.argtypes = [i] * 6
             lib.palimpsa_bwd_blockdiag_workspace_size.restype = sz
             lib.palimpsa_bwd_blockdiag.argtypes = ([vp] * 5 + [fp] * 4 + [vp, fp, fp] + [fp] * 9 + [i] * 6 +
-                                                   [i, i, vp, sz, vp])
+                                                   [i, i, i, vp, sz, vp])
             lib.palimpsa_bwd_blockdiag.restype = i
             lib.palimpsa_status_string.argtypes = [i]
             lib.palimpsa_status_string.restype = ctypes.c_char_p
@@ -442,11 +442,15 @@ def bwd_frozen(q, k, v, beta, dt, A, I_prior, gy, mu0=None, gmuT=None, want_stat
 
 
 def fwd_blockdiag(q, k, v, beta, dt, A, I_prior, block: int = 2, mu0=None, P0=None, out_dtype=None,
-                  y=None, muT=None, PT=None, write_state: bool = True):
+                  y=None, muT=None, PT=None, write_state: bool = True, save_checkpoints: bool = False,
+                  workspace=None):
     """Forward with the precision kept block-diagonal along the key axis
     (``block`` = 2, or 4 with d_k of 64 or 128).  Returns ``(y, muT, PT)`` with
     ``PT`` ``[B, H, dv, dk/block, block, block]``; ``mu0``/``P0`` likewise
-    (both or neither)."""
+    (both or neither).  ``save_checkpoints`` (the training forward) also stores
+    the backward's checkpoints in ``workspace``, a contiguous uint8 device
+    tensor of ``bwd_blockdiag_workspace_size`` bytes, for a following
+    ``bwd_blockdiag(..., workspace=workspace, checkpoints_saved=True)``."""
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
     B, T, H, dk = q.shape
@@ -479,12 +483,20 @@ def fwd_blockdiag(q, k, v, beta, dt, A, I_prior, block: int = 2, mu0=None, P0=No
         _check(PT, "PT", (B, H, dv, nb, block, block), torch.float32, dev)
     else:
         muT = PT = None
+    if save_checkpoints:
+        if workspace is None:
+            raise ValueError("save_checkpoints needs a backward workspace (bwd_blockdiag_workspace_size bytes)")
+        if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
+    else:
+        workspace = None
     lib = load_library()
     with torch.cuda.device(dev):
         st = lib.palimpsa_fwd_blockdiag(
             _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(dt), _ptr(A), _ptr(I_prior), _ptr(mu0), _ptr(P0),
             _ptr(y) if y.numel() else None, _ptr(muT), _ptr(PT), B, T, H, dk, dv, int(block),
-            _DTYPES[in_dtype], _DTYPES[out_dtype], _stream_handle(dev))
+            _DTYPES[in_dtype], _DTYPES[out_dtype], SAVE_CHECKPOINTS if save_checkpoints else 0,
+            _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream_handle(dev))
     if st != OK:
         raise PalimpsaError(st, "palimpsa_fwd_blockdiag")
     return y, muT, PT
@@ -534,14 +546,16 @@ def bwd_blockdiag_workspace_size(B, T, H, dk, dv, block: int = 2) -> int:
 
 
 def bwd_blockdiag(q, k, v, beta, dt, A, I_prior, gy, block: int = 2, mu0=None, P0=None, gmuT=None, gPT=None,
-                  want_state_grads: bool = True, workspace=None, out=None):
+                  want_state_grads: bool = True, workspace=None, out=None, checkpoints_saved: bool = False):
     """Backward of ``fwd_blockdiag`` (``block`` 2, or 4 with d_k of 64 or 128) for
     ``L = <gy, y> + <gmuT, muT> + <gPT, PT>``.
 
     Returns a dict of float32 gradients ``gq, gk, gv, gbeta, gdt, gA, gIp`` and,
     if ``want_state_grads``, ``gmu0`` and ``gP0`` (the gradient for a
     symmetric P0).  ``gmuT``/``gPT`` may be None (zero); ``out`` and
-    ``workspace`` as in ``bwd``."""
+    ``workspace`` as in ``bwd``.  ``checkpoints_saved``: ``workspace`` holds the
+    checkpoints a ``fwd_blockdiag(..., save_checkpoints=True)`` call on the
+    same inputs stored, and the checkpoint pass is skipped."""
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
     B, T, H, dk = q.shape
@@ -578,6 +592,8 @@ def bwd_blockdiag(q, k, v, beta, dt, A, I_prior, gy, block: int = 2, mu0=None, P
         res[name] = t
     lib = load_library()
     nbytes = bwd_blockdiag_workspace_size(B, T, H, dk, dv, block)
+    if checkpoints_saved and workspace is None:
+        raise ValueError("checkpoints_saved needs the workspace the training forward wrote")
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
@@ -590,7 +606,7 @@ def bwd_blockdiag(q, k, v, beta, dt, A, I_prior, gy, block: int = 2, mu0=None, P
             nz(res["gq"]), nz(res["gk"]), nz(res["gv"]), nz(res["gbeta"]), nz(res["gdt"]),
             _ptr(res["gA"]), _ptr(res["gIp"]), _ptr(res.get("gmu0")), _ptr(res.get("gP0")),
             B, T, H, dk, dv, int(block), _DTYPES[in_dtype], _DTYPES[gy.dtype],
-            _ptr(workspace), workspace.numel(), _stream_handle(dev))
+            CHECKPOINTS_SAVED if checkpoints_saved else 0, _ptr(workspace), workspace.numel(), _stream_handle(dev))
     if st != OK:
         raise PalimpsaError(st, "palimpsa_bwd_blockdiag")
     return res

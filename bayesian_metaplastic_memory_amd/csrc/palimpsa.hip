@@ -1432,13 +1432,53 @@ struct BdArgs {
     const float *A, *Ip, *mu0, *P0;   // P0 / PT: [B, H, dv, dk/2, 2, 2]
     void *y;
     float *muT, *PT;
-    int B, T, H, dv, nwg, xcd_remap;
+    float *ck;         // the training forward: the backward's checkpoints (else NULL)
+    float *ck_sink;    // ... and one workgroup block that takes the stores past the sequence
+    int B, T, H, dv, nwg, xcd_remap, nsb;
 };
 
-template <int DK, int C, typename TOut>
+// A lane's block state: h for its KC columns, then per block the upper
+// triangle of P ((p00, p01, p11) for 2x2 blocks, 10 entries for 4x4); a
+// checkpoint pads it to whole float4s.
+template <int DK, int BS> struct BdLane {
+    static constexpr int kKC = LaneTile<DK>::kCols;
+    static constexpr int kN = kKC + (BS == 2 ? 3 * (kKC / 2) : 10 * (kKC / 4));
+    static constexpr int kNP = (kN + 3) / 4 * 4;
+};
+template <int DK> using Bd2Lane = BdLane<DK, 2>;
+
+// A workgroup's checkpoint block: float4 i of thread tid at blk + 4 (i kThreads + tid).
+template <int N, int NP>
+__device__ inline void bd2_ck_store(float *blk, int tid, const float *x) {
+#pragma unroll
+    for (int i = 0; i < NP; i += 4)
+        __builtin_nontemporal_store(f32x4{i < N ? x[i] : 0.f, i + 1 < N ? x[i + 1] : 0.f,
+                                          i + 2 < N ? x[i + 2] : 0.f, i + 3 < N ? x[i + 3] : 0.f},
+                                    (f32x4 *)(blk + 4 * ((i / 4) * kThreads + tid)));
+}
+template <int N, int NP>
+__device__ inline void bd2_ck_load(const float *blk, int tid, float *x) {
+#pragma unroll
+    for (int i = 0; i < NP; i += 4) {
+        const f32x4 v = __builtin_nontemporal_load((const f32x4 *)(blk + 4 * ((i / 4) * kThreads + tid)));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (i + j < N) x[i + j] = v[j];
+    }
+}
+
+
+// CKPT (the training forward): the lane's state before the chunk's tokens 0
+// and 8 is stored as the backward's checkpoint at ck_a and ck_b (a discard
+// block where the sequence has no such sub-block), unconditionally, so the
+// token loop stays one straight-line block.
+template <int DK, int C, typename TOut, bool CKPT = false>
 __device__ inline void bd2_chunk(const float *buf, int left, float *h, float *p00, float *p01, float *p11,
-                                 int row_local, int g, TOut *yrow, size_t ystride) {
+                                 int row_local, int g, TOut *yrow, size_t ystride,
+                                 float *ck_a = nullptr, float *ck_b = nullptr) {
     using LT = LaneTile<DK>;
+    using L = BdLane<DK, 2>;
+    static_assert(!CKPT || (C == 16 && kGroup == 2 * kSB), "the checkpointing forward runs chunk 16");
     const float *cbase = buf + LT::col(g, 0, 0);
     const float *rbase = buf + C * Stage<DK>::kColFloats + 2 * row_local;
     int goff = C * (Stage<DK>::kColFloats + Stage<DK>::kRowFloats);
@@ -1452,6 +1492,18 @@ __device__ inline void bd2_chunk(const float *buf, int left, float *h, float *p0
         float part[kGroup];
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) {
+            if (CKPT && u % kSB == 0) {
+                float st[L::kN];
+#pragma unroll
+                for (int x = 0; x < LT::kCols; ++x) st[x] = h[x];
+#pragma unroll
+                for (int pb = 0; pb < LT::kCols / 2; ++pb) {
+                    st[LT::kCols + 3 * pb] = p00[pb];
+                    st[LT::kCols + 3 * pb + 1] = p01[pb];
+                    st[LT::kCols + 3 * pb + 2] = p11[pb];
+                }
+                bd2_ck_store<L::kN, L::kNP>(u == 0 ? ck_a : ck_b, threadIdx.x, st);
+            }
             const float2 gc = *(const float2 *)(gg + 2 * u);                          // alpha, c
             const float2 rb = *(const float2 *)(rg + u * Stage<DK>::kRowFloats);      // beta, beta*v
             const float *ct = cg + u * Stage<DK>::kColFloats;
@@ -1487,7 +1539,7 @@ __device__ inline void bd2_chunk(const float *buf, int left, float *h, float *p0
     }
 }
 
-template <int DK, int C, typename TIn, typename TOut>
+template <int DK, int C, typename TIn, typename TOut, bool CKPT = false>
 __global__ __launch_bounds__(kThreads) void bd2_fwd_kernel(BdArgs a) {
     using LT = LaneTile<DK>;
     static_assert(LT::kVec % 2 == 0, "a lane's columns must hold whole 2-blocks");
@@ -1541,6 +1593,12 @@ __global__ __launch_bounds__(kThreads) void bd2_fwd_kernel(BdArgs a) {
     const size_t kq_tok = (size_t)a.H * DK, vb_tok = (size_t)a.H * a.dv;
     const size_t ystride = (size_t)a.H * a.dv;
     TOut *ybase = (TOut *)a.y + seq * a.dv + row;
+    const size_t ck_stride = CKPT ? (size_t)rb_per_head * kThreads * BdLane<DK, 2>::kNP : 0;
+    float *ckb = CKPT ? a.ck + ((size_t)bh * a.nsb * rb_per_head + wg % rb_per_head) *
+                                   (kThreads * BdLane<DK, 2>::kNP)
+                      : nullptr;
+    // sub-block sb's checkpoint block, or the discard block past the sequence
+    auto ck_at = [&](int sb) { return !CKPT ? nullptr : sb < a.nsb ? ckb + (size_t)sb * ck_stride : a.ck_sink; };
     const int nchunks = (a.T + C - 1) / C;
     Stager<DK, C, TIn, true> st;
     if (nchunks > 0) {
@@ -1556,8 +1614,8 @@ __global__ __launch_bounds__(kThreads) void bd2_fwd_kernel(BdArgs a) {
             st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
                     dseq + tn * a.H, a.T - (t0 + C), a.H, a.dv, tid);
         }
-        bd2_chunk<DK, C, TOut>((c & 1) ? buf1 : buf0, a.T - t0, hv, p00, p01, p11, row_local, g,
-                               ybase + (size_t)t0 * ystride, ystride);
+        bd2_chunk<DK, C, TOut, CKPT>((c & 1) ? buf1 : buf0, a.T - t0, hv, p00, p01, p11, row_local, g,
+                                     ybase + (size_t)t0 * ystride, ystride, ck_at(t0 / kSB), ck_at(t0 / kSB + 1));
         if (more) st.commit((c & 1) ? buf0 : buf1, A, Ip, tid, false);
         __syncthreads();
     }
@@ -1608,35 +1666,6 @@ __global__ __launch_bounds__(kThreads) void bd2_fwd_kernel(BdArgs a) {
 // has bwd_kernel's structure (halves of 4 tokens replayed from the
 // checkpoint into registers, walked in reverse) with the step above.
 
-// A lane's block state: h for its KC columns, then per block the upper
-// triangle of P ((p00, p01, p11) for 2x2 blocks, 10 entries for 4x4); a
-// checkpoint pads it to whole float4s.
-template <int DK, int BS> struct BdLane {
-    static constexpr int kKC = LaneTile<DK>::kCols;
-    static constexpr int kN = kKC + (BS == 2 ? 3 * (kKC / 2) : 10 * (kKC / 4));
-    static constexpr int kNP = (kN + 3) / 4 * 4;
-};
-template <int DK> using Bd2Lane = BdLane<DK, 2>;
-
-// A workgroup's checkpoint block: float4 i of thread tid at blk + 4 (i kThreads + tid).
-template <int N, int NP>
-__device__ inline void bd2_ck_store(float *blk, int tid, const float *x) {
-#pragma unroll
-    for (int i = 0; i < NP; i += 4)
-        __builtin_nontemporal_store(f32x4{i < N ? x[i] : 0.f, i + 1 < N ? x[i + 1] : 0.f,
-                                          i + 2 < N ? x[i + 2] : 0.f, i + 3 < N ? x[i + 3] : 0.f},
-                                    (f32x4 *)(blk + 4 * ((i / 4) * kThreads + tid)));
-}
-template <int N, int NP>
-__device__ inline void bd2_ck_load(const float *blk, int tid, float *x) {
-#pragma unroll
-    for (int i = 0; i < NP; i += 4) {
-        const f32x4 v = __builtin_nontemporal_load((const f32x4 *)(blk + 4 * ((i / 4) * kThreads + tid)));
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (i + j < N) x[i + j] = v[j];
-    }
-}
 
 // The lane's start state: from (mu0, P0) when given (P0's upper triangle),
 // else mu0 = 0 and P0 = I_prior Id.  srow: entry (b, h, row, 0).
@@ -1696,6 +1725,7 @@ struct BdBwdArgs {
     float *ck;         // [B*H][T/8][dv/16][lane state]: (h, P) before every 8th token
     float *pqk, *ps, *pI0;   // bwd_kernel's partials, same layouts
     int B, T, H, dv, nsb, nwg, xcd_remap;
+    int ck_saved;      // the training forward stored the checkpoints already
 };
 
 // A sub-block's outputs once its (gq, gk) column sums are in red and its row
@@ -2056,10 +2086,12 @@ __device__ inline void bd4_update(float *p, float *hh, const float *kk, const fl
     for (int e = 0; e < 4; ++e) hh[e] = fmaf(alpha, hh[e], bv * kk[e]);
 }
 
-template <int DK, int C, typename TOut>
+template <int DK, int C, typename TOut, bool CKPT = false>
 __device__ inline void bd4_chunk(const float *buf, int left, float *h, float (*P)[10], int row_local, int g,
-                                 TOut *yrow, size_t ystride) {
+                                 TOut *yrow, size_t ystride, float *ck_a = nullptr, float *ck_b = nullptr) {
     using LT = LaneTile<DK>;
+    using L = BdLane<DK, 4>;
+    static_assert(!CKPT || (C == 16 && kGroup == 2 * kSB), "the checkpointing forward runs chunk 16");
     const float *cbase = buf + LT::col(g, 0, 0);
     const float *rbase = buf + C * Stage<DK>::kColFloats + 2 * row_local;
     int goff = C * (Stage<DK>::kColFloats + Stage<DK>::kRowFloats);
@@ -2073,6 +2105,16 @@ __device__ inline void bd4_chunk(const float *buf, int left, float *h, float (*P
         float part[kGroup];
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) {
+            if (CKPT && u % kSB == 0) {
+                float st[L::kN];
+#pragma unroll
+                for (int x = 0; x < LT::kCols; ++x) st[x] = h[x];
+#pragma unroll
+                for (int mb = 0; mb < LT::kNVec; ++mb)
+#pragma unroll
+                    for (int x = 0; x < 10; ++x) st[LT::kCols + 10 * mb + x] = P[mb][x];
+                bd2_ck_store<L::kN, L::kNP>(u == 0 ? ck_a : ck_b, threadIdx.x, st);
+            }
             const float2 gc = *(const float2 *)(gg + 2 * u);                          // alpha, c
             const float2 rb = *(const float2 *)(rg + u * Stage<DK>::kRowFloats);      // beta, beta*v
             const float *ct = cg + u * Stage<DK>::kColFloats;
@@ -2100,7 +2142,7 @@ __device__ inline void bd4_chunk(const float *buf, int left, float *h, float (*P
 
 // Same grid, staging and state I/O as bd2_fwd_kernel; P0 / PT are [B, H, dv, dk/4, 4, 4]
 // (the upper triangle is read; PT is written in full, symmetric).
-template <int DK, int C, typename TIn, typename TOut>
+template <int DK, int C, typename TIn, typename TOut, bool CKPT = false>
 __global__ __launch_bounds__(kThreads) void bd4_fwd_kernel(BdArgs a) {
     using LT = LaneTile<DK>;
     static_assert(LT::kVec == 4, "a lane's column vectors must be whole 4-blocks");
@@ -2165,6 +2207,12 @@ __global__ __launch_bounds__(kThreads) void bd4_fwd_kernel(BdArgs a) {
     const size_t kq_tok = (size_t)a.H * DK, vb_tok = (size_t)a.H * a.dv;
     const size_t ystride = (size_t)a.H * a.dv;
     TOut *ybase = (TOut *)a.y + seq * a.dv + row;
+    const size_t ck_stride = CKPT ? (size_t)rb_per_head * kThreads * BdLane<DK, 4>::kNP : 0;
+    float *ckb = CKPT ? a.ck + ((size_t)bh * a.nsb * rb_per_head + wg % rb_per_head) *
+                                   (kThreads * BdLane<DK, 4>::kNP)
+                      : nullptr;
+    // sub-block sb's checkpoint block, or the discard block past the sequence
+    auto ck_at = [&](int sb) { return !CKPT ? nullptr : sb < a.nsb ? ckb + (size_t)sb * ck_stride : a.ck_sink; };
     const int nchunks = (a.T + C - 1) / C;
     Stager<DK, C, TIn, true> st;
     if (nchunks > 0) {
@@ -2180,8 +2228,8 @@ __global__ __launch_bounds__(kThreads) void bd4_fwd_kernel(BdArgs a) {
             st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
                     dseq + tn * a.H, a.T - (t0 + C), a.H, a.dv, tid);
         }
-        bd4_chunk<DK, C, TOut>((c & 1) ? buf1 : buf0, a.T - t0, hv, P, row_local, g,
-                               ybase + (size_t)t0 * ystride, ystride);
+        bd4_chunk<DK, C, TOut, CKPT>((c & 1) ? buf1 : buf0, a.T - t0, hv, P, row_local, g,
+                                     ybase + (size_t)t0 * ystride, ystride, ck_at(t0 / kSB), ck_at(t0 / kSB + 1));
         if (more) st.commit((c & 1) ? buf0 : buf1, A, Ip, tid, false);
         __syncthreads();
     }
@@ -4504,7 +4552,8 @@ palimpsa_status launch_bd2(const BdArgs &a, hipStream_t s) {
     constexpr int C = 16;
     const size_t lds = fwd_lds_bytes<DK, C>();
     (void)hipGetLastError();
-    hipLaunchKernelGGL((bd2_fwd_kernel<DK, C, TIn, TOut>), dim3(a.nwg), dim3(kThreads), lds, s, a);
+    if (a.ck) hipLaunchKernelGGL((bd2_fwd_kernel<DK, C, TIn, TOut, true>), dim3(a.nwg), dim3(kThreads), lds, s, a);
+    else hipLaunchKernelGGL((bd2_fwd_kernel<DK, C, TIn, TOut>), dim3(a.nwg), dim3(kThreads), lds, s, a);
     return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
 }
 
@@ -4513,7 +4562,8 @@ palimpsa_status launch_bd4(const BdArgs &a, hipStream_t s) {
     constexpr int C = 16;
     const size_t lds = fwd_lds_bytes<DK, C>();
     (void)hipGetLastError();
-    hipLaunchKernelGGL((bd4_fwd_kernel<DK, C, TIn, TOut>), dim3(a.nwg), dim3(kThreads), lds, s, a);
+    if (a.ck) hipLaunchKernelGGL((bd4_fwd_kernel<DK, C, TIn, TOut, true>), dim3(a.nwg), dim3(kThreads), lds, s, a);
+    else hipLaunchKernelGGL((bd4_fwd_kernel<DK, C, TIn, TOut>), dim3(a.nwg), dim3(kThreads), lds, s, a);
     return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
 }
 
@@ -4535,7 +4585,7 @@ palimpsa_status launch_bd_d(const BdArgs &a, int dk, int block, hipStream_t s) {
 // Block-diagonal backward workspace: the checkpoints (lane states padded to
 // float4s), then bwd_kernel's partials in their layouts.
 struct BdBwdWs {
-    float *ck, *pqk, *ps, *gabh, *gibh, *pI0;
+    float *ck, *pqk, *ps, *gabh, *gibh, *pI0, *sink;
     size_t bytes;
 };
 BdBwdWs plan_bd_bwd_ws(void *base, int B, int T, int H, int dk, int dv, int block) {
@@ -4552,10 +4602,13 @@ BdBwdWs plan_bd_bwd_ws(void *base, int B, int T, int H, int dk, int dv, int bloc
     const size_t o_ck = take(bh * nsb * nrb * kThreads * lane_np);
     const size_t o_pqk = take(nrb * bth * 2 * dk), o_ps = take(nrb * bth * 2);
     const size_t o_ga = take(bh), o_gi = take(bh), o_pi = take(bh * nrb);
+    // the training forward's discarded checkpoint stores (one workgroup block)
+    const size_t o_sink = take((size_t)kThreads * lane_np);
     BdBwdWs w;
     char *c = (char *)base;
     w.ck = (float *)(c + o_ck); w.pqk = (float *)(c + o_pqk); w.ps = (float *)(c + o_ps);
     w.gabh = (float *)(c + o_ga); w.gibh = (float *)(c + o_gi); w.pI0 = (float *)(c + o_pi);
+    w.sink = (float *)(c + o_sink);
     w.bytes = off;
     return w;
 }
@@ -4565,7 +4618,7 @@ palimpsa_status launch_bd_bwd(const BdBwdArgs &a, const BdBwdWs &w, float *gq, f
                               float *gIp, int dt_bf16, hipStream_t s) {
     (void)hipGetLastError();
     const size_t ck_lds = fwd_lds_bytes<DK, 16>();
-    if (a.T > 0)
+    if (a.T > 0 && !a.ck_saved)
         hipLaunchKernelGGL((bd_ckpt_kernel<DK, BS, TIn>), dim3(a.nwg), dim3(kThreads), ck_lds, s, a);
     const size_t lds = (size_t)BwdStage<DK>::kTotal * sizeof(float);
     void (*kern)(BdBwdArgs);
@@ -4612,8 +4665,11 @@ palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void 
                                        const void *dt, const float *A, const float *I_prior,
                                        const float *mu0, const float *P0, void *y, float *muT, float *PT,
                                        int B, int T, int H, int dk, int dv, int block,
-                                       palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, void *stream) {
+                                       palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
     if (!A || !I_prior || (T > 0 && (!q || !k || !v || !beta || !dt || !y)))
+        return PALIMPSA_ERR_INVALID_ARG;
+    if ((flags & ~PALIMPSA_SAVE_CHECKPOINTS) || ((flags & PALIMPSA_SAVE_CHECKPOINTS) && !workspace))
         return PALIMPSA_ERR_INVALID_ARG;
     if ((mu0 == nullptr) != (P0 == nullptr) || (muT == nullptr) != (PT == nullptr))
         return PALIMPSA_ERR_INVALID_ARG;
@@ -4621,7 +4677,8 @@ palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void 
         return PALIMPSA_ERR_INVALID_ARG;
     if ((block != 2 && block != 4) || !head_ok(dk) || (block == 4 && dk == 32) || !dv_ok(dv))
         return PALIMPSA_ERR_UNSUPPORTED;
-    const void *vec_ptrs[] = {q, k, v, beta, P0, PT};
+    const bool save = (flags & PALIMPSA_SAVE_CHECKPOINTS) != 0;
+    const void *vec_ptrs[] = {q, k, v, beta, P0, PT, save ? workspace : nullptr};
     for (const void *p : vec_ptrs)
         if (p && !aligned_to(p, 16)) return PALIMPSA_ERR_ALIGNMENT;
     const size_t in_sz = in_dtype == PALIMPSA_BF16 ? 2 : 4, out_sz = out_dtype == PALIMPSA_BF16 ? 2 : 4;
@@ -4632,12 +4689,21 @@ palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void 
     if (nwg > 0x7fffffffLL || (long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 46) ||
         64LL * H * (dk > dv ? dk : dv) >= (1LL << 31))
         return PALIMPSA_ERR_UNSUPPORTED;
+    if (save && workspace_bytes < plan_bd_bwd_ws(nullptr, B, T, H, dk, dv, block).bytes)
+        return PALIMPSA_ERR_INVALID_ARG;
     if (T == 0 && !muT) return PALIMPSA_OK;
     BdArgs a;
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.dt = dt;
     a.A = A; a.Ip = I_prior; a.mu0 = mu0; a.P0 = P0; a.y = y; a.muT = muT; a.PT = PT;
     a.B = B; a.T = T; a.H = H; a.dv = dv;
     a.nwg = (int)nwg; a.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
+    a.nsb = (T + kSB - 1) / kSB;
+    a.ck = a.ck_sink = nullptr;
+    if (save && T > 0) {
+        const BdBwdWs w = plan_bd_bwd_ws(workspace, B, T, H, dk, dv, block);
+        a.ck = w.ck;
+        a.ck_sink = w.sink;
+    }
     hipStream_t s = (hipStream_t)stream;
     const bool bf_in = in_dtype == PALIMPSA_BF16, bf_out = out_dtype == PALIMPSA_BF16;
     if (bf_in && bf_out) return launch_bd_d<bf16_t, bf16_t>(a, dk, block, s);
@@ -4715,9 +4781,9 @@ palimpsa_status palimpsa_bwd_blockdiag(const void *q, const void *k, const void 
                                        float *gq, float *gk, float *gv, float *gbeta, float *gdt,
                                        float *gA, float *gIp, float *gmu0, float *gP0,
                                        int B, int T, int H, int dk, int dv, int block,
-                                       palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype,
+                                       palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype, int flags,
                                        void *workspace, size_t workspace_bytes, void *stream) {
-    if (!A || !I_prior || !gA || !gIp || !workspace)
+    if (!A || !I_prior || !gA || !gIp || !workspace || (flags & ~PALIMPSA_CHECKPOINTS_SAVED))
         return PALIMPSA_ERR_INVALID_ARG;
     if (T > 0 && (!q || !k || !v || !beta || !dt || !gy || !gq || !gk || !gv || !gbeta || !gdt))
         return PALIMPSA_ERR_INVALID_ARG;
@@ -4749,6 +4815,7 @@ palimpsa_status palimpsa_bwd_blockdiag(const void *q, const void *k, const void 
     a.gv = gv; a.gbeta = gbeta; a.gmu0 = gmu0; a.gP0 = gP0;
     a.ck = w.ck; a.pqk = w.pqk; a.ps = w.ps; a.pI0 = w.pI0;
     a.B = B; a.T = T; a.H = H; a.dv = dv; a.nsb = (T + kSB - 1) / kSB;
+    a.ck_saved = (flags & PALIMPSA_CHECKPOINTS_SAVED) ? 1 : 0;
     a.nwg = (int)nwg; a.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
     hipStream_t s = (hipStream_t)stream;
     const bool bf_in = in_dtype == PALIMPSA_BF16, bf_gy = gy_dtype == PALIMPSA_BF16;

@@ -373,10 +373,28 @@ def blockdiag_backward_extra(torch, pm, workloads, w, g, steps, block=2):
     achieved = entries * flops / avg_s / 1e12
     per_entry = ("replay 5.5 + reverse 25 VALU + 0.5 v_rcp_f32 = 31.5 slots, 45 flops" if block == 2 else
                  "replay 8.5 + reverse 40 VALU + 1 v_rsq_f32 = 50.5 slots, 75 flops")
+    # one training step: the forward that stores the checkpoints, then the
+    # backward that reuses them; beside it the plain forward and a backward
+    # that recomputes them
+    fargs = args[:7]
+    y, muT, PT = pm.fwd_blockdiag(*fargs, block=block)
+
+    def fused():
+        pm.fwd_blockdiag(*fargs, block=block, y=y, muT=muT, PT=PT, save_checkpoints=True, workspace=ws)
+        pm.bwd_blockdiag(*args, block=block, gmuT=gmuT, workspace=ws, out=out, checkpoints_saved=True)
+
+    def recompute():
+        pm.fwd_blockdiag(*fargs, block=block, y=y, muT=muT, PT=PT)
+        fn()
+
+    _, per_f = time_launches(fused, steps, 2, torch)
+    _, per_r = time_launches(recompute, steps, 2, torch)
+    f_s, r_s = sum(per_f) / len(per_f) / 1e3, sum(per_r) / len(per_r) / 1e3
     return {"workload": w.name + ", %dx%d block-diagonal backward (gq, gk, gv, gbeta, gdt, gA, gIp, gmu0, gP0)"
             % (block, block),
             "tokens_per_s": w.B * w.T / avg_s, "ms_per_call": avg_s * 1e3,
             "workspace_GB": ws.numel() / 1e9,
+            "training_step_ms": f_s * 1e3, "recompute_training_step_ms": r_s * 1e3,
             "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                          "frac": achieved / peak,
                          "traffic": load_traffic("bd%d_bwd_layer760m_bf16_traffic.json" % block)

@@ -362,6 +362,12 @@ palimpsa_status palimpsa_bwd_frozen(const void *q, const void *k, const void *v,
  *             read); both NULL: mu0 = 0, P0 = I_prior Id
  *   muT, PT   the final state in the same layouts (PT written in full,
  *             symmetric), or both NULL to skip
+ *   flags     0, or PALIMPSA_SAVE_CHECKPOINTS (the training forward): also
+ *             store the backward's checkpoints in workspace, which must then
+ *             be the workspace of a following palimpsa_bwd_blockdiag call
+ *             (palimpsa_bwd_blockdiag_workspace_size(B, T, H, dk, dv, block)
+ *             bytes, 16-byte aligned) that passes PALIMPSA_CHECKPOINTS_SAVED;
+ *             without the flag workspace is not read and may be NULL
  *
  * block == 2 with dk in {32, 64, 128}, or block == 4 with dk in {64, 128}; dv a
  * multiple of 16 up to 1024 (else PALIMPSA_ERR_UNSUPPORTED).  q, k, v, beta,
@@ -373,7 +379,8 @@ palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void 
                                        const void *dt, const float *A, const float *I_prior,
                                        const float *mu0, const float *P0, void *y, float *muT, float *PT,
                                        int B, int T, int H, int dk, int dv, int block,
-                                       palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, void *stream);
+                                       palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
+                                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One decode token of the block-diagonal-precision recurrence (2x2 or 4x4 blocks),
@@ -438,9 +445,13 @@ size_t palimpsa_bwd_blockdiag_workspace_size(int B, int T, int H, int dk, int dv
  *   gP0       [B, H, dv, dk/block, block, block]  the gradient for a symmetric
  *             P0 (written in full and symmetric: each off-diagonal pair holds
  *             half of the derivative by their shared value), or NULL
+ *   flags     0, or PALIMPSA_CHECKPOINTS_SAVED: the workspace holds the
+ *             checkpoints a palimpsa_fwd_blockdiag call with
+ *             PALIMPSA_SAVE_CHECKPOINTS stored for the same inputs, and the
+ *             checkpoint pass is skipped (the results are bitwise the same)
  *   workspace at least palimpsa_bwd_blockdiag_workspace_size(B, T, H, dk, dv,
  *             block) bytes, 16-byte aligned, caller-owned; contents on entry
- *             ignored
+ *             ignored unless PALIMPSA_CHECKPOINTS_SAVED
  *
  * block == 2 with dk in {32, 64, 128}, or block == 4 with dk in {64, 128}; dv a
  * multiple of 16 up to 1024 (else PALIMPSA_ERR_UNSUPPORTED).  A 4x4 block's
@@ -456,7 +467,7 @@ palimpsa_status palimpsa_bwd_blockdiag(const void *q, const void *k, const void 
                                        float *gq, float *gk, float *gv, float *gbeta, float *gdt,
                                        float *gA, float *gIp, float *gmu0, float *gP0,
                                        int B, int T, int H, int dk, int dv, int block,
-                                       palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype,
+                                       palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype, int flags,
                                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */

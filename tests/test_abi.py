@@ -285,10 +285,11 @@ def test_bwd_workspace_size_host_logic(lib):
 
 def _bd_args(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dt=FAKE, A=FAKE, Ip=FAKE, mu0=None, P0=None, y=FAKE,
-             muT=FAKE, PT=FAKE, B=2, T=8, H=3, dk=64, dv=64, block=2, ind=1, outd=1, stream=None)
+             muT=FAKE, PT=FAKE, B=2, T=8, H=3, dk=64, dv=64, block=2, ind=1, outd=1, flags=0, ws=None, wsb=0,
+             stream=None)
     a.update(over)
     return [a[n] for n in ("q", "k", "v", "beta", "dt", "A", "Ip", "mu0", "P0", "y", "muT", "PT",
-                           "B", "T", "H", "dk", "dv", "block", "ind", "outd", "stream")]
+                           "B", "T", "H", "dk", "dv", "block", "ind", "outd", "flags", "ws", "wsb", "stream")]
 
 
 BD_CASES = [
@@ -297,6 +298,10 @@ BD_CASES = [
     (dict(block=1), 2), (dict(block=3), 2), (dict(block=8), 2), (dict(block=4, dk=32), 2), (dict(dk=48), 2),
     (dict(dv=24), 2),
     (dict(q=FAKE + 4), 3), (dict(PT=FAKE + 8), 3), (dict(mu0=FAKE + 2, P0=FAKE), 3), (dict(dt=FAKE + 1), 3),
+    # the training forward: a backward workspace of the right size
+    (dict(flags=4), 1), (dict(flags=8, ws=FAKE, wsb=1 << 40), 1), (dict(flags=1), 1),
+    (dict(flags=4, ws=FAKE, wsb=64), 1), (dict(flags=4, ws=FAKE + 8, wsb=1 << 40), 3),
+    (dict(flags=4, ws=FAKE, wsb=1 << 40, block=3), 2),
 ]
 
 
@@ -333,12 +338,12 @@ def test_blockdiag_step_rejects_invalid_calls(lib, over, status):
 def _bd_bwd_args(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dt=FAKE, A=FAKE, Ip=FAKE, mu0=None, P0=None, gy=FAKE,
              gmuT=None, gPT=None, gq=FAKE, gk=FAKE, gv=FAKE, gbeta=FAKE, gdt=FAKE, gA=FAKE, gIp=FAKE,
-             gmu0=None, gP0=None, B=2, T=8, H=3, dk=64, dv=64, block=2, ind=1, gyd=1, ws=FAKE, wsb=1 << 40,
-             stream=None)
+             gmu0=None, gP0=None, B=2, T=8, H=3, dk=64, dv=64, block=2, ind=1, gyd=1, flags=0, ws=FAKE,
+             wsb=1 << 40, stream=None)
     a.update(over)
     return [a[n] for n in ("q", "k", "v", "beta", "dt", "A", "Ip", "mu0", "P0", "gy", "gmuT", "gPT",
                            "gq", "gk", "gv", "gbeta", "gdt", "gA", "gIp", "gmu0", "gP0",
-                           "B", "T", "H", "dk", "dv", "block", "ind", "gyd", "ws", "wsb", "stream")]
+                           "B", "T", "H", "dk", "dv", "block", "ind", "gyd", "flags", "ws", "wsb", "stream")]
 
 
 # every case fails validation
@@ -354,7 +359,7 @@ BD_BWD_CASES = [
     (dict(q=FAKE + 4), 3), (dict(gy=FAKE + 8), 3), (dict(P0=FAKE + 8, mu0=FAKE), 3),
     (dict(mu0=FAKE + 2, P0=FAKE), 3), (dict(gPT=FAKE + 4), 3), (dict(gP0=FAKE + 8), 3), (dict(gq=FAKE + 4), 3),
     (dict(gmuT=FAKE + 1), 3), (dict(gmu0=FAKE + 2), 3), (dict(gdt=FAKE + 2), 3), (dict(dt=FAKE + 1), 3),
-    (dict(ws=FAKE + 8), 3),
+    (dict(ws=FAKE + 8), 3), (dict(flags=4), 1), (dict(flags=9), 1), (dict(flags=8, wsb=64), 1),
 ]
 
 
@@ -367,7 +372,8 @@ def test_blockdiag_bwd_rejects_invalid_calls(lib, over, status):
 def test_bwd_blockdiag_workspace_size_host_logic(lib):
     """Checkpoints of the lane states (h, then the upper triangle of each
     block: 3 entries per 2x2 block, 10 per 4x4, padded to float4s) every 8
-    tokens, then the exact backward's partials."""
+    tokens, then the exact backward's partials, then one workgroup block for
+    the training forward's stores past the sequence."""
     import bayesian_metaplastic_memory_amd as pm
     pad = lambda n: (4 * n + 255) // 256 * 256
 
@@ -376,7 +382,8 @@ def test_bwd_blockdiag_workspace_size_host_logic(lib):
         kc = dk // 16
         lane = (kc + (3 * (kc // 2) if block == 2 else 10 * (kc // 4)) + 3) // 4 * 4
         return (pad(bh * nsb * nrb * 256 * lane) + pad(nrb * bh * T * 2 * dk) + pad(nrb * bh * T * 2)
-                + 2 * pad(bh) + pad(bh * nrb))
+                + 2 * pad(bh) + pad(bh * nrb)
+                + pad(256 * lane))    # the training forward's discard block
     for shape in [(1, 10, 2, 32, 32), (8, 4096, 12, 128, 128), (1, 0, 3, 64, 128), (2, 9, 1, 128, 64)]:
         assert pm.bwd_blockdiag_workspace_size(*shape) == expect(*shape), shape
         if shape[3] > 32:

@@ -1308,6 +1308,37 @@ def test_blockdiag_bwd_no_forgetting(block):
         assert_close("bd%d %s (alpha=1)" % (block, n), got[n], ref[n], TOL_BWD)
 
 
+@pytest.mark.parametrize("block,T,dk,dtype", [(2, 37, 128, torch.bfloat16), (2, 64, 32, torch.float32),
+                                              (4, 41, 64, torch.float32), (4, 16, 128, torch.bfloat16),
+                                              (2, 0, 64, torch.float32)])
+def test_blockdiag_training_forward_saves_the_checkpoints(block, T, dk, dtype):
+    """The forward with save_checkpoints writes the backward's checkpoints as
+    the backward's own pass would: its outputs equal the plain forward's and
+    the backward that reuses them equals the one that recomputes them, bitwise
+    (T = 37 and 41 end mid-chunk, so the discard block takes a store)."""
+    B, H, dv = 2, 2, 48
+    w = workloads.WORKLOADS[0].with_(B=B, H=H, dk=dk, dv=dv, dtype=dtype, A_mode="logspace16")
+    _announce("blockdiag training forward", block=block, B=B, T=T, H=H, dk=dk, dv=dv, dtype=dtype)
+    inp = workloads.make_inputs(w, T=T, seed=T + block)
+    mu0, P0 = workloads.random_block_state(B, H, dv, dk, block, inp["I_prior"], seed=T)
+    gr = workloads.upstream_grads(B, T, H, dv, dk, dtype, seed=T + 1)
+    g = to_device(inp, DEV)
+    mu0, P0, gy, gmuT = mu0.to(DEV), P0.to(DEV), gr["gy"].to(DEV), gr["gmuT"].to(DEV)
+    pm = _pm()
+    ws = torch.empty(pm.bwd_blockdiag_workspace_size(B, T, H, dk, dv, block), dtype=torch.uint8, device=DEV)
+    ref_fwd = pm.fwd_blockdiag(*gpu_args(g), block=block, mu0=mu0, P0=P0)
+    ref_bwd = pm.bwd_blockdiag(*gpu_args(g), gy, block=block, mu0=mu0, P0=P0, gmuT=gmuT)
+    ws.fill_(0xFF)          # any stale contents must be overwritten
+    got_fwd = pm.fwd_blockdiag(*gpu_args(g), block=block, mu0=mu0, P0=P0, save_checkpoints=True, workspace=ws)
+    got_bwd = pm.bwd_blockdiag(*gpu_args(g), gy, block=block, mu0=mu0, P0=P0, gmuT=gmuT, workspace=ws,
+                               checkpoints_saved=True)
+    torch.cuda.synchronize()
+    for name, x, y in zip(("y", "muT", "PT"), got_fwd, ref_fwd):
+        assert torch.equal(x, y), name
+    for n in BD_BWD_NAMES:
+        assert torch.equal(got_bwd[n], ref_bwd[n]), n
+
+
 @pytest.mark.parametrize("block", [2, 4])
 def test_blockdiag_bwd_empty_sequence(block):
     B, H, dk, dv = 2, 3, 64, 32
