@@ -425,6 +425,64 @@ def test_decode_steps_replay_in_a_hip_graph():
         assert torch.equal(mu_g, mu_e) and torch.equal(I_g, I_e)
 
 
+@pytest.mark.parametrize("path", ["exact", "blockdiag2", "blockdiag4"])
+def test_training_step_replays_in_a_hip_graph(path):
+    """A captured training step (the forward that stores the checkpoints, then
+    the backward that reuses them; no memsets or allocations inside) replays
+    to the eager results, bitwise, every replay, with eager work and
+    synchronisations in between."""
+    pm = _pm()
+    B, T, H, dk, dv = 2, 100, 2, 64, 48
+    w = workloads.WORKLOADS[0].with_(B=B, H=H, dk=dk, dv=dv, dtype=torch.bfloat16, A_mode="logspace16")
+    _announce("training step graph replay", path=path, B=B, T=T, H=H, dk=dk, dv=dv, replays=3)
+    inp = workloads.make_inputs(w, T=T, seed=77)
+    g = to_device(inp, DEV)
+    args = gpu_args(g)
+    gr = workloads.upstream_grads(B, T, H, dv, dk, torch.bfloat16, seed=77)
+    gy, gmuT = gr["gy"].to(DEV), gr["gmuT"].to(DEV)
+    if path == "exact":
+        ws = torch.empty(pm.bwd_workspace_size(B, T, H, dk, dv), dtype=torch.uint8, device=DEV)
+        fo = [torch.empty(B, T, H, dv, dtype=torch.bfloat16, device=DEV),
+              torch.empty(B, H, dv, dk, device=DEV), torch.empty(B, H, dv, dk, device=DEV)]
+        out = pm.bwd(*args, gy, gmuT=gmuT, workspace=ws)
+
+        def step(fo, out):
+            pm.fwd_chunked(*args, y=fo[0], muT=fo[1], IT=fo[2], workspace=ws, save_checkpoints=True)
+            pm.bwd(*args, gy, gmuT=gmuT, workspace=ws, out=out, checkpoints_saved=True)
+    else:
+        block = 2 if path == "blockdiag2" else 4
+        ws = torch.empty(pm.bwd_blockdiag_workspace_size(B, T, H, dk, dv, block), dtype=torch.uint8, device=DEV)
+        fo = list(pm.fwd_blockdiag(*args, block=block))
+        out = pm.bwd_blockdiag(*args, gy, block=block, gmuT=gmuT, workspace=ws)
+
+        def step(fo, out):
+            pm.fwd_blockdiag(*args, block=block, y=fo[0], muT=fo[1], PT=fo[2], save_checkpoints=True,
+                             workspace=ws)
+            pm.bwd_blockdiag(*args, gy, block=block, gmuT=gmuT, workspace=ws, out=out, checkpoints_saved=True)
+    step(fo, out)                                   # warm the binding and the kernels
+    torch.cuda.synchronize()
+    ref_fo = [x.clone() for x in fo]
+    ref_out = {n: x.clone() for n, x in out.items() if x is not None}
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(fo, out)
+    for r in range(3):
+        for x in fo:
+            x.zero_()
+        for x in out.values():
+            if x is not None:
+                x.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(fo, ref_fo):
+            assert torch.equal(a, b), "forward output, replay %d" % r
+        for n, x in ref_out.items():
+            assert torch.equal(out[n], x), "%s, replay %d" % (n, r)
+        step([torch.empty_like(x) for x in fo], {n: torch.empty_like(x) for n, x in ref_out.items()})
+        torch.cuda.synchronize()                    # eager work between the replays
+
+
 # ---------------------------------------------------------------------------
 # frozen-importance (Mamba2-limit) forward on the matrix cores
 # ---------------------------------------------------------------------------
