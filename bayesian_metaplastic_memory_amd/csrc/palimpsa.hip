@@ -2424,12 +2424,16 @@ __global__ __launch_bounds__(kThreads) void bd4_bwd_kernel(BdBwdArgs a) {
     float Gh[KC], GS[10 * NB];
     // gPT's block at entry o, symmetrised into the upper triangle u
     auto load_gpt = [&](size_t o, float *u) {
+        if (!a.gPT) {
+#pragma unroll
+            for (int x = 0; x < 10; ++x) u[x] = 0.f;
+            return;
+        }
         const float *gb = a.gPT + o * 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = i; j < 4; ++j)
-                u[up4(i, j)] = a.gPT ? (i == j ? gb[5 * i] : 0.5f * (gb[4 * i + j] + gb[4 * j + i])) : 0.f;
+            for (int j = i; j < 4; ++j) u[up4(i, j)] = i == j ? gb[5 * i] : 0.5f * (gb[4 * i + j] + gb[4 * j + i]);
     };
     auto store_gp0 = [&](size_t o, const float *u) {
         float *gb = a.gP0 + o * 4;
