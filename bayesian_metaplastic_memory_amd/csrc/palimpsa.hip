@@ -1837,7 +1837,10 @@ __device__ inline void bd2_reverse_token(const float *buf, int e, const float *S
 }
 
 template <int DK, typename TIn, typename TG>
-__global__ __launch_bounds__(kThreads) void bd2_bwd_kernel(BdBwdArgs a) {
+// Two workgroups per CU (two waves per SIMD, 256 registers per lane at most):
+// the next checkpoint is loaded into ckS once ckS is dead rather than into a
+// prefetch copy, which is what keeps the lane within that budget.
+__global__ __launch_bounds__(kThreads, 2) void bd2_bwd_kernel(BdBwdArgs a) {
     using LT = LaneTile<DK>;
     using S = BwdStage<DK>;
     using L = Bd2Lane<DK>;
@@ -1976,8 +1979,6 @@ __global__ __launch_bounds__(kThreads) void bd2_bwd_kernel(BdBwdArgs a) {
                 replay(e, xS[e]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            float nS[N];
-            if (sb > 0) bd2_ck_load<N, L::kNP>(ckb + (size_t)(sb - 1) * ck_stride, tid, nS);
 #pragma unroll
             for (int e = 3; e >= 0; --e) {
                 bd2_reverse_token<DK>(cur, e, xS[e], e == 0 ? ckS : xS[e > 0 ? e - 1 : 0], Gh, GS, row_local,
@@ -1986,14 +1987,12 @@ __global__ __launch_bounds__(kThreads) void bd2_bwd_kernel(BdBwdArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             bwd_row_sums(acc, g, rs + row_local);
+            // the next checkpoint, into ckS now that token 0's reverse step has used it
+            if (sb > 0) bd2_ck_load<N, L::kNP>(ckb + (size_t)(sb - 1) * ck_stride, tid, ckS);
             if (sb > 0) st.commit(lds + ((sb - 1) & 1) * S::kFloats, A, Ip, tid, false);
             __syncthreads();
             bd_bwd_epilogue<DK>(a, cur, red, rs, tid, t0, rb, bh, row0, seq0, bth);
             __syncthreads();
-            if (sb > 0) {
-#pragma unroll
-                for (int i = 0; i < N; ++i) ckS[i] = nS[i];
-            }
         }
         // the start state h_0 = P_0 mu_0
 #pragma unroll
@@ -2391,7 +2390,8 @@ __device__ inline void bd4_reverse_token(const float *buf, int e, const float *S
 }
 
 template <int DK, typename TIn, typename TG>
-__global__ __launch_bounds__(kThreads) void bd4_bwd_kernel(BdBwdArgs a) {
+// Two workgroups per CU, as bd2_bwd_kernel (at d = 128 a few values spill).
+__global__ __launch_bounds__(kThreads, 2) void bd4_bwd_kernel(BdBwdArgs a) {
     using LT = LaneTile<DK>;
     using S = BwdStage<DK>;
     using L = BdLane<DK, 4>;
@@ -2517,6 +2517,8 @@ __global__ __launch_bounds__(kThreads) void bd4_bwd_kernel(BdBwdArgs a) {
                 float mS[N], x0[N], x1[N];
 #pragma unroll
                 for (int i = 0; i < N; ++i) mS[i] = ckS[i];
+                // ckS is dead after the last quarter's copy: the next checkpoint goes there
+                if (qd == 0 && sb > 0) bd2_ck_load<N, L::kNP>(ckb + (size_t)(sb - 1) * ck_stride, tid, ckS);
                 for (int e = 0; e < 2 * qd; ++e) replay(e, mS);
 #pragma unroll
                 for (int i = 0; i < N; ++i) x0[i] = mS[i];
@@ -2539,8 +2541,6 @@ __global__ __launch_bounds__(kThreads) void bd4_bwd_kernel(BdBwdArgs a) {
             quarter(3);
             quarter(2);
             bwd_row_sums(acc, g, rs + 4 * 4 * kRowsPerWG + row_local);
-            float nS[N];
-            if (sb > 0) bd2_ck_load<N, L::kNP>(ckb + (size_t)(sb - 1) * ck_stride, tid, nS);
             quarter(1);
             quarter(0);
             bwd_row_sums(acc, g, rs + row_local);
@@ -2548,10 +2548,6 @@ __global__ __launch_bounds__(kThreads) void bd4_bwd_kernel(BdBwdArgs a) {
             __syncthreads();
             bd_bwd_epilogue<DK>(a, cur, red, rs, tid, t0, rb, bh, row0, seq0, bth);
             __syncthreads();
-            if (sb > 0) {
-#pragma unroll
-                for (int i = 0; i < N; ++i) ckS[i] = nS[i];
-            }
         }
         // the start state h_0 = P_0 mu_0: gmu0 = P_0 G_h, gP0 = S + sym(G_h mu0^T)
 #pragma unroll
