@@ -4109,7 +4109,7 @@ struct Bd2StepArgs {
     long long rows;     // B * H * dv
 };
 
-template <int DK, typename TIn, typename TOut>
+template <int DK, typename TIn, typename TOut, bool I32 = false>
 __global__ __launch_bounds__(kStepThreads) void bd2_step_kernel(Bd2StepArgs a) {
     constexpr int kTPR = DK / 4;                           // threads per value row
     constexpr int kRowsPerBlock = kStepThreads / kTPR;
@@ -4120,9 +4120,20 @@ __global__ __launch_bounds__(kStepThreads) void bd2_step_kernel(Bd2StepArgs a) {
     // takes part in the reduction
     const bool valid = row < a.rows;
     const long long r = valid ? row : a.rows - 1;
-    const long long bh = r / a.dv;
-    const int i = (int)(r % a.dv);
-    const int h = (int)(bh % a.H);
+    long long bh;
+    int i, h;
+    if (I32) {
+        // rows < 2^32: 32-bit division (a 64-bit one is a long software
+        // sequence; 5% of the 2x2 block-diagonal step's time at B64 H32 d128)
+        const unsigned r32 = (unsigned)r, dv32 = (unsigned)a.dv;
+        bh = (long long)(r32 / dv32);
+        i = (int)(r32 % dv32);
+        h = (int)((unsigned)bh % (unsigned)a.H);
+    } else {
+        bh = r / a.dv;
+        i = (int)(r % a.dv);
+        h = (int)(bh % a.H);
+    }
     const TIn *qp = (const TIn *)a.q + bh * DK + j0;
     const TIn *kp = (const TIn *)a.k + bh * DK + j0;
     const float bt = io<TIn>::to_f32(((const TIn *)a.beta)[bh * a.dv + i]);
@@ -4164,7 +4175,7 @@ __global__ __launch_bounds__(kStepThreads) void bd2_step_kernel(Bd2StepArgs a) {
 
 // The same decode token with 4x4 blocks: a thread's 4 key channels are one
 // block (P [B, H, dv, dk/4, 4, 4], upper triangle read, written in full).
-template <int DK, typename TIn, typename TOut>
+template <int DK, typename TIn, typename TOut, bool I32 = false>
 __global__ __launch_bounds__(kStepThreads) void bd4_step_kernel(Bd2StepArgs a) {
     constexpr int kTPR = DK / 4;
     constexpr int kRowsPerBlock = kStepThreads / kTPR;
@@ -4173,9 +4184,20 @@ __global__ __launch_bounds__(kStepThreads) void bd4_step_kernel(Bd2StepArgs a) {
     const int j0 = (tid % kTPR) * 4;
     const bool valid = row < a.rows;
     const long long r = valid ? row : a.rows - 1;
-    const long long bh = r / a.dv;
-    const int i = (int)(r % a.dv);
-    const int h = (int)(bh % a.H);
+    long long bh;
+    int i, h;
+    if (I32) {
+        // rows < 2^32: 32-bit division (a 64-bit one is a long software
+        // sequence; 5% of the 2x2 block-diagonal step's time at B64 H32 d128)
+        const unsigned r32 = (unsigned)r, dv32 = (unsigned)a.dv;
+        bh = (long long)(r32 / dv32);
+        i = (int)(r32 % dv32);
+        h = (int)((unsigned)bh % (unsigned)a.H);
+    } else {
+        bh = r / a.dv;
+        i = (int)(r % a.dv);
+        h = (int)(bh % a.H);
+    }
     const TIn *qp = (const TIn *)a.q + bh * DK + j0;
     const TIn *kp = (const TIn *)a.k + bh * DK + j0;
     const float bt = io<TIn>::to_f32(((const TIn *)a.beta)[bh * a.dv + i]);
@@ -4744,12 +4766,19 @@ palimpsa_status palimpsa_step_blockdiag(const void *q, const void *k, const void
     if (blocks > 0x7fffffffLL) return PALIMPSA_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     const bool bf_in = in_dtype == PALIMPSA_BF16, bf_out = out_dtype == PALIMPSA_BF16;
+    const bool i32 = rows <= 0xffffffffLL;
     (void)hipGetLastError();
 #define PALIMPSA_BD2_STEP_LAUNCH(DK_, TI, TO)                                                                   \
     do {                                                                                                        \
-        if (block == 4)                                                                                         \
+        if (block == 4 && i32)                                                                                  \
+            hipLaunchKernelGGL((bd4_step_kernel<DK_ == 32 ? 64 : DK_, TI, TO, true>), dim3((unsigned)blocks),   \
+                               dim3(kStepThreads), 0, s, a);                                                    \
+        else if (block == 4)                                                                                    \
             hipLaunchKernelGGL((bd4_step_kernel<DK_ == 32 ? 64 : DK_, TI, TO>), dim3((unsigned)blocks),         \
                                dim3(kStepThreads), 0, s, a);                                                    \
+        else if (i32)                                                                                           \
+            hipLaunchKernelGGL((bd2_step_kernel<DK_, TI, TO, true>), dim3((unsigned)blocks), dim3(kStepThreads), \
+                               0, s, a);                                                                        \
         else                                                                                                    \
             hipLaunchKernelGGL((bd2_step_kernel<DK_, TI, TO>), dim3((unsigned)blocks), dim3(kStepThreads), 0, s, a); \
     } while (0)
