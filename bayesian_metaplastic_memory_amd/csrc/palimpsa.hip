@@ -146,15 +146,21 @@ struct FwdArgs {
 
 // Workspace of a time-split forward: for each of the first nseg-1 segments,
 // its affine summary from a zero state, laid out as M_loc [nseg-1][B*H][dv][dk],
-// then Ibar_loc (same shape), then the decay product P [nseg-1][B*H].
+// then Ibar_loc (same shape); then a copy of the caller's start state
+// (mu0, I0), [B*H][dv][dk] each; then the decay product P [nseg-1][B*H].
+// The replay pass starts every segment from the copy, never from mu0/I0
+// themselves: its last segment may overwrite those (muT aliasing mu0, IT
+// aliasing I0) while other segments of the same rows have not started yet.
 struct SegWs {
-    float *M, *Ib, *P;
+    float *M, *Ib, *mu0, *I0, *P;
     size_t per_seg;    // B * H * dv * dk
     __device__ SegWs(float *ws, int nseg, size_t bh, int dv, int dk)
         : per_seg(bh * dv * dk) {
         M = ws;
         Ib = ws + (size_t)(nseg - 1) * per_seg;
-        P = Ib + (size_t)(nseg - 1) * per_seg;
+        mu0 = Ib + (size_t)(nseg - 1) * per_seg;
+        I0 = mu0 + per_seg;
+        P = I0 + per_seg;
     }
 };
 
@@ -587,17 +593,35 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
     if (MODE == kSummary) {
 #pragma unroll
         for (int s = 0; s < LT::kCols; ++s) { I[s] = 0.f; M[s] = 0.f; }   // I holds Ibar here
-    } else {
-        if (a.mu0) {
+        if (seg == 0 && a.mu0) {   // the replay pass's copy of the start state
+            const SegWs w(a.ws, a.nseg, (size_t)a.B * a.H, a.dv, DK);
 #pragma unroll
             for (int m = 0; m < LT::kNVec; ++m) {
                 float mu[LT::kVec], ii[LT::kVec];
                 vecf<LT::kVec>::ld(a.mu0 + srow + LT::col(g, m, 0), mu);
+                vecf<LT::kVec>::ld(a.I0 + srow + LT::col(g, m, 0), ii);
+                vecf<LT::kVec>::st(w.mu0 + srow + LT::col(g, m, 0), mu);
+                vecf<LT::kVec>::st(w.I0 + srow + LT::col(g, m, 0), ii);
+            }
+        }
+    } else {
+        if (a.mu0) {
+            // a split replay reads the summary pass's copy (see SegWs)
+            const float *mu0 = a.mu0, *I0 = a.I0;
+            if (MODE == kReplay && a.nseg > 1) {
+                const SegWs w(a.ws, a.nseg, (size_t)a.B * a.H, a.dv, DK);
+                mu0 = w.mu0;
+                I0 = w.I0;
+            }
+#pragma unroll
+            for (int m = 0; m < LT::kNVec; ++m) {
+                float mu[LT::kVec], ii[LT::kVec];
+                vecf<LT::kVec>::ld(mu0 + srow + LT::col(g, m, 0), mu);
                 if (a.frozen) {
 #pragma unroll
                     for (int e = 0; e < LT::kVec; ++e) ii[e] = Ip;
                 } else {
-                    vecf<LT::kVec>::ld(a.I0 + srow + LT::col(g, m, 0), ii);
+                    vecf<LT::kVec>::ld(I0 + srow + LT::col(g, m, 0), ii);
                 }
 #pragma unroll
                 for (int e = 0; e < LT::kVec; ++e) {
@@ -4245,6 +4269,7 @@ __global__ __launch_bounds__(kStepThreads) void bd4_step_kernel(Bd2StepArgs a) {
 // ---------------------------------------------------------------------------
 
 inline bool aligned_to(const void *p, size_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
+
 inline bool head_ok(int d) { return d == 32 || d == 64 || d == 128; }
 // key widths of the exact forward and the decode step: up to a head as wide as
 // the model (the pages' recurrent-kernel measurement goes to 2048)
@@ -4344,18 +4369,20 @@ palimpsa_status launch_fwd_d(const FwdArgs &a, int dk, int C, bool ipe, hipStrea
 
 size_t lds_bytes_for(int dk, int C) { return (size_t)2 * C * (3 * dk + 2 * kRowsPerWG + 2) * sizeof(float); }
 
-// Chunk actually used: the request if given (8 is raised to 16, the
-// reduction group; larger requests shrink until the buffers fit the device's
-// LDS), else the largest that lets three workgroups share a CU when there are
-// enough workgroups to need it.
+// Chunk actually used: the library's choice is the largest chunk (16 to 64)
+// whose double-buffered staging lets three workgroups share a CU when there
+// are enough workgroups to need it, else the largest that fits the device's
+// LDS.  A request caps that choice (8 is raised to 16, the reduction group):
+// a larger chunk than the choice would only cost occupancy, and the results
+// are the same bits for every chunk.
 int pick_chunk(int requested, int dk, long long nwg, size_t lds_max) {
-    int C = requested < 16 ? (requested == 0 ? 0 : 16) : requested;
-    if (C == 0) {
-        const size_t budget = nwg > 256 ? 54 * 1024 : lds_max;
-        C = 64;
-        while (C > 16 && lds_bytes_for(dk, C) > budget) C /= 2;
+    const size_t budget = nwg > 256 ? 54 * 1024 : lds_max;
+    int C = 64;
+    while (C > 16 && lds_bytes_for(dk, C) > budget) C /= 2;
+    if (requested > 0) {
+        const int cap = requested < 16 ? 16 : requested;
+        while (C > 16 && C > cap) C /= 2;
     }
-    while (C > 16 && lds_bytes_for(dk, C) > lds_max) C /= 2;
     return C;
 }
 
@@ -4395,7 +4422,8 @@ SegPlan plan_segments(int B, int T, int H, int dk, int dv, int segments, int cus
     if (p.seg_len == 0) p.seg_len = 64;
     p.nseg = (int)((T + p.seg_len - 1) / p.seg_len);
     if (p.nseg < 1) p.nseg = 1;
-    p.ws_bytes = p.nseg > 1 ? ((size_t)(p.nseg - 1) * ((size_t)2 * B * H * dv * dk + (size_t)B * H) * sizeof(float))
+    // (nseg - 1) summaries (M_loc, Ibar_loc, P), the start-state copy (mu0, I0)
+    p.ws_bytes = p.nseg > 1 ? (((size_t)p.nseg * 2 * B * H * dv * dk + (size_t)(p.nseg - 1) * B * H) * sizeof(float))
                             : 0;
     return p;
 }
@@ -5043,23 +5071,29 @@ size_t palimpsa_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segm
     return plan_segments(B, T, H, dk, dv, segments, device_cus()).ws_bytes;
 }
 
-palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v,
-                                     const void *beta, const void *dt,
-                                     const float *A, const float *I_prior,
-                                     const float *mu0, const float *I0,
-                                     void *y, float *muT, float *IT,
-                                     int B, int T, int H, int dk, int dv, int chunk, int segments,
-                                     palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
-                                     void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The chunked forward (palimpsa_fwd_chunked).
+palimpsa_status fwd_chunked_impl(const void *q, const void *k, const void *v,
+                                 const void *beta, const void *dt,
+                                 const float *A, const float *I_prior,
+                                 const float *mu0, const float *I0,
+                                 void *y, float *muT, float *IT,
+                                 int B, int T, int H, int dk, int dv, int chunk, int segments,
+                                 palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
     if (!A || !I_prior || (T > 0 && (!q || !k || !v || !beta || !dt || !y)) || (flags & ~kFlagsFwd))
         return PALIMPSA_ERR_INVALID_ARG;
+
     if ((mu0 == nullptr) != (I0 == nullptr) || (muT == nullptr) != (IT == nullptr))
         return PALIMPSA_ERR_INVALID_ARG;
     if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0)
         return PALIMPSA_ERR_INVALID_ARG;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
         return PALIMPSA_ERR_INVALID_ARG;
-    if (chunk != 0 && chunk != 8 && chunk != 16 && chunk != 32 && chunk != 64)
+    if (chunk != 0 && chunk != 8 && chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128)
         return PALIMPSA_ERR_INVALID_ARG;
     if (segments < 0 || segments > 64 || (workspace_bytes > 0 && !workspace))
         return PALIMPSA_ERR_INVALID_ARG;
@@ -5135,6 +5169,23 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
     if (bf_out) return launch_fwd_d<float, bf16_t>(a, dk, C, ipe, s);
     return launch_fwd_d<float, float>(a, dk, C, ipe, s);
 }
+
+}  // namespace
+
+extern "C" {
+
+palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v,
+                                     const void *beta, const void *dt,
+                                     const float *A, const float *I_prior,
+                                     const float *mu0, const float *I0,
+                                     void *y, float *muT, float *IT,
+                                     int B, int T, int H, int dk, int dv, int chunk, int segments,
+                                     palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+    return fwd_chunked_impl(q, k, v, beta, dt, A, I_prior, mu0, I0, y, muT, IT, B, T, H, dk, dv, chunk,
+                            segments, in_dtype, out_dtype, flags, workspace, workspace_bytes, stream);
+}
+
 
 palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
                               const void *beta, const void *dt,

@@ -7,11 +7,17 @@ inputs resident in HBM.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
-The roofline object reports the chunked-forward kernel against the FP32
-vector-ALU issue roof (the binding one: the readout divides by a per-token,
-per-entry precision, so there is no dense contraction for the matrix cores,
-and the kernel needs only a few hundred GB/s of HBM).  Per state-entry update
-the method needs 4 FMA + 2 MUL + 1 reciprocal = 10 flops + 1 rcp.
+Every roofline object reports its kernel (or call) against MI355X's published
+peaks: FP32 vector 157.3 TFLOP/s, HBM3E 8 TB/s, dense bf16 matrix cores
+2.5 PFLOP/s.  `frac` is achieved / peak for the roof named in `bound`, and
+`valu_frac`, `hbm_frac` and `mfma_frac` give all three.  The exact forward is
+bound by the FP32 vector ALU (the readout divides by a per-token, per-entry
+precision, so there is no dense contraction for the matrix cores, and the
+kernel needs only a few hundred GB/s of HBM); per state-entry update the
+method needs 4 FMA + 2 MUL + 1 reciprocal = 10 flops.  A secondary
+`issue_model` states the same time against this build's own instruction-issue
+bound (no packed FP32: one wave64 FP32 VALU instruction per SIMD every 4
+clocks, transcendentals not counted), which no kernel can exceed.
 """
 from __future__ import annotations
 
@@ -26,48 +32,69 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-# Chip constants used by the ALU roof (MI355X: 256 CUs x 4 SIMDs, each SIMD
-# issuing one wave64 FP32 VALU instruction every 4 clocks = 16 lane-ops/clk,
-# at the 2.4 GHz peak engine clock).  Packed FP32 is not used by this build,
-# so one FMA is one lane-op.
+# Published MI355X peaks.  The FP32 vector figure counts a packed FMA
+# (2 lanes x 2 flops) on every lane and clock: 256 CUs x 4 SIMDs x 16 lanes x
+# 2 x 2 flops x 2.4 GHz.
+FP32_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+# Instruction-issue bound of this build (secondary): each SIMD issues one
+# wave64 FP32 VALU instruction every 4 clocks (16 lane-ops per clock; packed
+# FP32 is switched off in the build), 256 CUs x 4 SIMDs at 2.4 GHz.
 CUS, SIMDS, LANES_PER_CLK, CLOCK_HZ = 256, 4, 16, 2.4e9
 LANE_OPS_PER_S = CUS * SIMDS * LANES_PER_CLK * CLOCK_HZ       # 3.93e13
-VALU_PER_UPDATE = 6          # 4 FMA + 2 MUL
-RCP_SLOTS = 2                # v_rcp_f32 issue cost in FMA slots: half rate on gfx950
-FLOPS_PER_UPDATE = 10        # FMA = 2 flops, MUL = 1; the reciprocal is not counted
-HBM_PEAK_GBS = 8000.0
-# Backward per state entry and token: replay of the update (2 FMA + MUL + FMA
-# = 4 VALU, 7 flops) and the reverse step (16 VALU = 22 flops, plus one
-# v_rcp_f32 = 2 slots): 22 issue slots, 29 flops.
-BWD_SLOTS_PER_UPDATE = 22
-BWD_FLOPS_PER_UPDATE = 29
-# 2x2 block-diagonal precision, per block of two entries and token: precision
-# 2 + 2 + 3 VALU, content 4, determinant 2, solve 6, readout 2 = 21 VALU
-# (33 flops) plus one v_rcp_f32 (2 slots): 11.5 slots and 16.5 flops per entry.
-BD2_SLOTS_PER_ENTRY = 11.5
-BD2_FLOPS_PER_ENTRY = 16.5
-# 4x4 blocks, per block and token: update 34 VALU (52 flops), Cholesky solve
-# 36 VALU (58 flops) plus four v_rsq_f32 (2 slots each), readout 4 FMA:
-# 82 slots and 118 flops per block, 20.5 slots and 29.5 flops per entry.
-BD4_SLOTS_PER_ENTRY = 20.5
-BD4_FLOPS_PER_ENTRY = 29.5
-# Backward of the 2x2 path, per entry and token: one replay of the update
-# (11 VALU, 18 flops per block) and the reverse step per block (determinant
-# and solves 16 VALU + one v_rcp_f32, adjoint updates 19, gradient terms 15:
-# 50 VALU and 2 rcp slots, 72 flops): 31.5 slots and 45 flops per entry.
-BD2_BWD_SLOTS_PER_ENTRY = 31.5
-BD2_BWD_FLOPS_PER_ENTRY = 45
-# 4x4 blocks, per block and token: one replay of the update (34 VALU, 52
-# flops) and the reverse step (Cholesky factor 16 VALU + 4 v_rsq_f32, two
-# solves 40, G_h, S and the gradient terms 104: 160 VALU and 8 rsq slots,
-# 248 flops): 50.5 slots and 75 flops per entry.
-BD4_BWD_SLOTS_PER_ENTRY = 50.5
-BD4_BWD_FLOPS_PER_ENTRY = 75
+# Per state-entry update and token, VALU instructions other than
+# transcendentals (v_rcp_f32, v_rsq_f32), and algorithmic flops (FMA = 2,
+# MUL/ADD = 1, transcendentals not counted):
+#  forward: w = fma(beta, k2, c), I = fma(a, I, w), t = bv k, M = fma(a, M, t),
+#           u = M r, acc = fma(u, q, acc)                       6 VALU, 10 flops
+#  backward: replay of the update 4 VALU (7 flops) + reverse step 16 VALU
+#           (22 flops)                                           20 VALU, 29 flops
+#  2x2 block-diagonal forward, per entry: 10.5 VALU, 16.5 flops
+#  4x4 block-diagonal forward, per entry: 18.5 VALU, 29.5 flops
+#  2x2 backward, per entry: replay 5.5 + reverse 25 VALU, 45 flops
+#  4x4 backward, per entry: replay 8.5 + reverse 40 VALU, 75 flops
+FWD = dict(valu=6, flops=10)
+BWD = dict(valu=20, flops=29)
+BD2 = dict(valu=10.5, flops=16.5)
+BD4 = dict(valu=18.5, flops=29.5)
+BD2_BWD = dict(valu=30.5, flops=45)
+BD4_BWD = dict(valu=48.5, flops=75)
 
 
-def alu_peak_tflops():
-    updates_per_s = LANE_OPS_PER_S / (VALU_PER_UPDATE + RCP_SLOTS)
-    return updates_per_s * FLOPS_PER_UPDATE / 1e12
+def roofline(bound, seconds, flops=0.0, nbytes=0.0, mfma_flops=0.0, traffic=None, mix=None, **extra):
+    """A roofline object for `seconds` of work that must do `flops` FP32
+    vector flops, move `nbytes` of HBM bytes and do `mfma_flops` of matrix-core
+    flops (all algorithmic).  `mix` (per-unit VALU count and flops) adds the
+    instruction-issue model."""
+    valu = flops / seconds / 1e12
+    hbm = nbytes / seconds / 1e9
+    mfma = mfma_flops / seconds / 1e12
+    if bound == "alu":
+        achieved, peak, unit = valu, FP32_PEAK_TFLOPS, "TFLOP/s"
+    elif bound == "hbm":
+        achieved, peak, unit = hbm, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = mfma, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    out = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+           "traffic": traffic, "valu_frac": valu / FP32_PEAK_TFLOPS, "hbm_frac": hbm / HBM_PEAK_GBS,
+           "mfma_frac": mfma / MFMA_BF16_PEAK_TFLOPS, "algorithmic_bytes": nbytes}
+    if mix is not None:
+        model = LANE_OPS_PER_S / mix["valu"] * mix["flops"] / 1e12
+        out["issue_model"] = {"peak": model, "unit": "TFLOP/s", "frac": valu / model,
+                              "per_unit": "%g VALU (transcendentals not counted), %g flops"
+                                          % (mix["valu"], mix["flops"])}
+    out.update(extra)
+    return out
+
+
+def fwd_bytes(w, esz_in, esz_out, state_in=False):
+    """Algorithmic HBM bytes of one chunked forward: the per-token inputs and y,
+    the final state written (and the start state read when given)."""
+    per_tok = w.B * w.T * w.H
+    state = w.B * w.H * w.dv * w.dk * 4
+    return (per_tok * ((2 * w.dk + 2 * w.dv + 1) * esz_in + w.dv * esz_out)
+            + 2 * state * (2 if state_in else 1))
 
 
 def kernel_source_hash():
@@ -86,14 +113,6 @@ def load_traffic(name):
     if d.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return d.get("hbm_bytes_per_launch")
-
-
-def bwd_peak_tflops():
-    return LANE_OPS_PER_S / BWD_SLOTS_PER_UPDATE * BWD_FLOPS_PER_UPDATE / 1e12
-
-
-def bd2_peak_tflops():
-    return LANE_OPS_PER_S / BD2_SLOTS_PER_ENTRY * BD2_FLOPS_PER_ENTRY / 1e12
 
 
 def time_launches(fn, steps, warmup, torch):
@@ -118,8 +137,20 @@ def time_launches(fn, steps, warmup, torch):
     return outer0.elapsed_time(outer1), per
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, w, max_heads):
-    import numpy as np
+    """The float64 oracle (plain sequential Eq. (5) in C, OpenMP over heads)
+    on the host cores: once with every thread the runtime offers, once with
+    one thread, on the same sample of heads at full length."""
     import oracle
     heads = [(b, h) for b in range(w.B) for h in range(w.H)][:max_heads]
     sub = oracle.select_heads(inp, heads)
@@ -127,11 +158,29 @@ def cpu_baseline(inp, w, max_heads):
     t0 = time.perf_counter()
     oracle.fwd(**sub, nthreads=threads)
     wall = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.fwd(**sub, nthreads=1)
+    wall1 = time.perf_counter() - t0
     layer_seqs = len(heads) / w.H                # sampled heads as a fraction of B sequences
     return {"value": layer_seqs * w.T / wall, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "wall_s": wall,
+            "one_thread": {"value": layer_seqs * w.T / wall1, "unit": "tokens/s", "wall_s": wall1},
             "sample": "%d of %d heads (b,h) at full T=%d, float64 sequential Eq. (5), "
-                      "OpenMP over heads; %.1f s wall" % (len(heads), w.B * w.H, w.T, wall)}
+                      "OpenMP over heads: %.1f s wall on %d threads, %.1f s on 1"
+                      % (len(heads), w.B * w.H, w.T, wall, threads, wall1)}
+
+
+def graph_step_time(torch, fn, steps, per_graph=16):
+    """Per-call time of a short kernel: a captured HIP graph of `per_graph`
+    calls (they record no memsets or allocations), replayed and timed."""
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            fn()
+    _, per = time_launches(graph.replay, max(2, steps // per_graph), 3, torch)
+    return sum(per) / len(per) / 1e3 / per_graph
 
 
 def decode_extra(torch, pm, workloads, steps):
@@ -144,27 +193,17 @@ def decode_extra(torch, pm, workloads, steps):
     d = {n: x.to(dev) for n, x in workloads.decode_inputs(w, 0).items()}
     y = torch.empty(w.B, w.H, w.dv, dtype=w.dtype, device=dev)
     fn = lambda: pm.step(d["q"], d["k"], d["v"], d["beta"], d["dt"], A, Ip, mu, I, y=y)
-    # A decode kernel takes ~85 us, less than the Python binding needs to
-    # submit it, so the timed loop replays a captured graph of 16 steps (the
-    # launches contain no memsets or allocations) and reports per-step time.
-    per_graph = 16
-    fn()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for _ in range(per_graph):
-            fn()
-    total_ms, per = time_launches(graph.replay, max(2, steps // per_graph), 3, torch)
-    avg_s = sum(per) / len(per) / 1e3 / per_graph
-    state_bytes = 16 * w.B * w.H * w.dv * w.dk
-    in_bytes = 2 * w.B * w.H * (2 * w.dk + 2 * w.dv + 1) + 2 * w.B * w.H * w.dv
+    # A decode kernel takes under 90 us, less than the Python binding needs to
+    # submit it, so the timed loop replays a captured graph of 16 steps.
+    avg_s = graph_step_time(torch, fn, steps)
+    updates = w.B * w.H * w.dv * w.dk
+    nbytes = 16 * updates + 2 * w.B * w.H * (2 * w.dk + 2 * w.dv + 1) + 2 * w.B * w.H * w.dv
     return {"workload": "decode B=64 H=32 d_k=d_v=128, bf16 inputs, fp32 state",
             "tokens_per_s": w.B / avg_s, "us_per_step": avg_s * 1e6,
             "timing": "HIP graph of 16 steps, replayed",
-            "roofline": {"bound": "hbm", "achieved": (state_bytes + in_bytes) / avg_s / 1e9,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": (state_bytes + in_bytes) / avg_s / 1e9 / HBM_PEAK_GBS,
-                         "traffic": load_traffic("step_kernel_decode_B64_H32_d128_traffic.json")}}
+            "roofline": roofline("hbm", avg_s, flops=updates * FWD["flops"], nbytes=nbytes,
+                                 traffic=load_traffic("step_kernel_decode_B64_H32_d128_traffic.json"),
+                                 kernel="step_kernel<128, bf16, bf16>")}
 
 
 def blockdiag_decode_extra(torch, pm, workloads, steps):
@@ -178,29 +217,29 @@ def blockdiag_decode_extra(torch, pm, workloads, steps):
     d = {n: x.to(dev) for n, x in workloads.decode_inputs(w, 0).items()}
     y = torch.empty(w.B, w.H, w.dv, dtype=w.dtype, device=dev)
     fn = lambda: pm.step_blockdiag(d["q"], d["k"], d["v"], d["beta"], d["dt"], A, Ip, mu, P, y=y)
-    per_graph = 16                       # as decode_extra: a captured graph of 16 steps, replayed
-    fn()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for _ in range(per_graph):
-            fn()
-    _, per = time_launches(graph.replay, max(2, steps // per_graph), 3, torch)
-    avg_s = sum(per) / len(per) / 1e3 / per_graph
-    state_bytes = 2 * 12 * w.B * w.H * w.dv * w.dk
-    in_bytes = 2 * w.B * w.H * (2 * w.dk + 2 * w.dv + 1) + 2 * w.B * w.H * w.dv
+    avg_s = graph_step_time(torch, fn, steps)
+    entries = w.B * w.H * w.dv * w.dk
+    nbytes = 2 * 12 * entries + 2 * w.B * w.H * (2 * w.dk + 2 * w.dv + 1) + 2 * w.B * w.H * w.dv
     return {"workload": "2x2 block-diagonal decode B=64 H=32 d_k=d_v=128, bf16 inputs, fp32 state",
             "tokens_per_s": w.B / avg_s, "us_per_step": avg_s * 1e6,
             "timing": "HIP graph of 16 steps, replayed",
-            "roofline": {"bound": "hbm", "achieved": (state_bytes + in_bytes) / avg_s / 1e9,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": (state_bytes + in_bytes) / avg_s / 1e9 / HBM_PEAK_GBS,
-                         "traffic": load_traffic("bd2_step_decode_B64_H32_d128_traffic.json")}}
+            "roofline": roofline("hbm", avg_s, flops=entries * BD2["flops"], nbytes=nbytes,
+                                 traffic=load_traffic("bd2_step_decode_B64_H32_d128_traffic.json"),
+                                 kernel="bd2_step_kernel<128, bf16, bf16>")}
+
+
+def grad_bytes(w, esz):
+    """Algorithmic HBM bytes of a backward call: read q, k, v, beta, dt, gy and
+    the final-state gradients; write the float32 per-token gradients and the
+    start-state gradients."""
+    btok = w.B * w.T * w.H
+    state = w.B * w.H * w.dv * w.dk * 4
+    return btok * ((2 * w.dk + 3 * w.dv + 1) * esz + (2 * w.dk + 2 * w.dv + 1) * 4) + 4 * state
 
 
 def backward_extra(torch, pm, workloads, w, g, steps):
     """palimpsa_bwd on the same workload: checkpoint pass, backward kernel and
-    the three finishing kernels, timed as one call."""
+    the finishing kernels, timed as one call."""
     dev = g["q"].device
     gr = {n: (x.to(dev) if x is not None else None)
           for n, x in workloads.upstream_grads(w.B, w.T, w.H, w.dv, w.dk, w.dtype, seed=2).items()}
@@ -211,15 +250,16 @@ def backward_extra(torch, pm, workloads, w, g, steps):
     _, per = time_launches(fn, steps, 3, torch)
     avg_s = sum(per) / len(per) / 1e3
     updates = w.B * w.H * w.T * w.dv * w.dk
-    achieved = updates * BWD_FLOPS_PER_UPDATE / avg_s / 1e12
+    esz = 2 if w.dtype == torch.bfloat16 else 4
     return {"workload": w.name + ", backward (gq, gk, gv, gbeta, gdt, gA, gIp, gmu0, gI0)",
             "tokens_per_s": w.B * w.T / avg_s, "ms_per_call": avg_s * 1e3,
             "workspace_GB": ws.numel() / 1e9,
-            "roofline": {"bound": "alu", "achieved": achieved, "peak": bwd_peak_tflops(), "unit": "TFLOP/s",
-                         "frac": achieved / bwd_peak_tflops(),
-                         "traffic": load_traffic("bwd_layer760m_bf16_traffic.json") if w.name.startswith("layer760m") else None,
-                         "scope": "whole call (5 kernels); per-kernel split in the committed trace",
-                         "per_update": "replay 4 VALU + reverse 16 VALU + 1 v_rcp_f32 = 22 slots, 29 flops"}}
+            "roofline": roofline("alu", avg_s, flops=updates * BWD["flops"], nbytes=grad_bytes(w, esz) + 8 *
+                                 w.B * w.H * w.dv * w.dk, mix=BWD,
+                                 traffic=load_traffic("bwd_layer760m_bf16_traffic.json")
+                                 if w.name.startswith("layer760m") else None,
+                                 scope="whole call (checkpoint pass, reverse walk, finishing kernels); "
+                                       "per-kernel split in the committed trace")}
 
 
 def training_extra(torch, pm, workloads, w, g, steps):
@@ -252,9 +292,13 @@ def training_extra(torch, pm, workloads, w, g, steps):
     mean_s = lambda per: sum(per) / len(per) / 1e3
     s_s, f_s, r_s = mean_s(per_s), mean_s(per_f), mean_s(per_r)
     ck_bytes = w.B * w.H * ((w.T + 7) // 8) * 2 * w.dv * w.dk * 4
+    updates = w.B * w.H * w.T * w.dv * w.dk
     return {"workload": w.name + ", training step (forward with y and final state, then the full backward)",
             "tokens_per_s": w.B * w.T / f_s, "ms_per_step": f_s * 1e3,
             "recompute_ms_per_step": r_s * 1e3,
+            "roofline": roofline("alu", f_s, flops=updates * (FWD["flops"] + BWD["flops"]),
+                                 mix=dict(valu=FWD["valu"] + BWD["valu"], flops=FWD["flops"] + BWD["flops"]),
+                                 scope="whole step (checkpointing forward + backward)"),
             "checkpointing_forward": {
                 "ms_per_launch": s_s * 1e3, "checkpoint_GB": ck_bytes / 1e9,
                 "checkpoint_write_GBs": ck_bytes / s_s / 1e9,
@@ -262,6 +306,14 @@ def training_extra(torch, pm, workloads, w, g, steps):
                 if w.name.startswith("layer760m") else None},
             "note": "checkpointing forward + backward reusing its checkpoints; "
                     "recompute_ms_per_step is plain forward + backward with its own checkpoint pass"}
+
+
+def frozen_mfma_flops(w):
+    """Matrix-core flops of the chunked frozen forward (64-token chunks): per
+    chunk Q S^T, the masked scores Q K^T, their product with W, and the state
+    update W^T K."""
+    per_chunk = 2 * 64 * (2 * w.dv * w.dk + 64 * w.dk + 64 * w.dv)
+    return w.B * w.H * ((w.T + 63) // 64) * per_chunk
 
 
 def frozen_extra(torch, pm, w, g, steps):
@@ -275,10 +327,10 @@ def frozen_extra(torch, pm, w, g, steps):
     hbm = w.B * w.T * w.H * (2 * w.dk + 2 * w.dv + 1 + w.dv) * esz + 4 * w.B * w.H * w.dv * w.dk
     return {"workload": w.name + ", frozen importance (Mamba2 limit) on MFMA",
             "tokens_per_s": w.B * w.T / avg_s, "ms_per_launch": avg_s * 1e3,
-            "roofline": {"bound": "hbm", "achieved": hbm / avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": hbm / avg_s / 1e9 / HBM_PEAK_GBS,
-                         "traffic": load_traffic("frozen_fwd_layer760m_bf16_traffic.json") if w.name.startswith("layer760m") else None,
-                         "algorithmic_bytes": hbm}}
+            "roofline": roofline("hbm", avg_s, nbytes=hbm, mfma_flops=frozen_mfma_flops(w),
+                                 traffic=load_traffic("frozen_fwd_layer760m_bf16_traffic.json")
+                                 if w.name.startswith("layer760m") else None,
+                                 kernel="frozen_fwd_kernel<%d>" % w.dk)}
 
 
 def frozen_backward_extra(torch, pm, workloads, w, g, steps):
@@ -298,58 +350,36 @@ def frozen_backward_extra(torch, pm, workloads, w, g, steps):
     _, per = time_launches(fn, steps, 3, torch)
     avg_s = sum(per) / len(per) / 1e3
     esz = 2 if w.dtype == torch.bfloat16 else 4
-    btok = w.B * w.T * w.H
-    state = w.B * w.H * w.dv * w.dk * 4
-    # read q, k, v, beta, gy, dt and gmuT; write gq, gk, gv, gbeta, gdt (fp32) and gmu0
-    alg = btok * ((2 * w.dk + 3 * w.dv + 1) * esz + (2 * w.dk + 2 * w.dv + 1) * 4) + 2 * state
+    alg = grad_bytes(w, esz) - 2 * w.B * w.H * w.dv * w.dk * 4     # no gIT read, no gI0 written
     nc = (w.T + 63) // 64
     boundary = 3 * w.B * w.H * nc * w.dv * w.dk * 2     # S_0^T, G_E, G_E^T per chunk, bf16
     return {"workload": w.name + ", frozen-importance backward (gq, gk, gv, gbeta, gdt, gA, gIp, gmu0)",
             "tokens_per_s": w.B * w.T / avg_s, "ms_per_call": avg_s * 1e3,
-            "roofline": {"bound": "hbm", "achieved": alg / avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": alg / avg_s / 1e9 / HBM_PEAK_GBS,
-                         "traffic": load_traffic("frozen_bwd_layer760m_bf16_traffic.json")
-                         if w.name.startswith("layer760m") else None,
-                         "algorithmic_bytes": alg,
-                         "chunk_boundary_bytes": boundary,
-                         "scope": "whole call (3 kernels)"}}
+            "roofline": roofline("hbm", avg_s, nbytes=alg, mfma_flops=3 * frozen_mfma_flops(w),
+                                 traffic=load_traffic("frozen_bwd_layer760m_bf16_traffic.json")
+                                 if w.name.startswith("layer760m") else None,
+                                 chunk_boundary_bytes=boundary, scope="whole call (3 kernels)")}
 
 
-def blockdiag_extra(torch, pm, w, g, steps):
-    """palimpsa_fwd_blockdiag (2x2 precision blocks along the key axis) on the same workload."""
-    y, muT, PT = pm.fwd_blockdiag(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], block=2)
-    fn = lambda: pm.fwd_blockdiag(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], block=2,
-                                  y=y, muT=muT, PT=PT)
-    _, per = time_launches(fn, steps, 10, torch)
-    avg_s = sum(per) / len(per) / 1e3
-    entries = w.B * w.H * w.T * w.dv * w.dk
-    achieved = entries * BD2_FLOPS_PER_ENTRY / avg_s / 1e12
-    return {"workload": w.name + ", 2x2 block-diagonal precision",
-            "tokens_per_s": w.B * w.T / avg_s, "ms_per_launch": avg_s * 1e3,
-            "roofline": {"bound": "alu", "achieved": achieved, "peak": bd2_peak_tflops(), "unit": "TFLOP/s",
-                         "frac": achieved / bd2_peak_tflops(),
-                         "traffic": load_traffic("bd2_fwd_layer760m_bf16_traffic.json")
-                         if w.name.startswith("layer760m") else None,
-                         "per_entry": "10.5 VALU + 0.5 v_rcp_f32 = 11.5 slots, 16.5 flops"}}
-
-
-def blockdiag4_extra(torch, pm, w, g, steps):
-    """palimpsa_fwd_blockdiag with 4x4 precision blocks on the same workload."""
-    y, muT, PT = pm.fwd_blockdiag(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], block=4)
-    fn = lambda: pm.fwd_blockdiag(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], block=4,
+def blockdiag_extra(torch, pm, w, g, steps, block=2):
+    """palimpsa_fwd_blockdiag (2x2 or 4x4 precision blocks along the key axis)
+    on the same workload."""
+    y, muT, PT = pm.fwd_blockdiag(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], block=block)
+    fn = lambda: pm.fwd_blockdiag(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], block=block,
                                   y=y, muT=muT, PT=PT)
     _, per = time_launches(fn, steps, 5, torch)
     avg_s = sum(per) / len(per) / 1e3
     entries = w.B * w.H * w.T * w.dv * w.dk
-    peak = LANE_OPS_PER_S / BD4_SLOTS_PER_ENTRY * BD4_FLOPS_PER_ENTRY / 1e12
-    achieved = entries * BD4_FLOPS_PER_ENTRY / avg_s / 1e12
-    return {"workload": w.name + ", 4x4 block-diagonal precision",
+    mix = BD2 if block == 2 else BD4
+    esz = 2 if w.dtype == torch.bfloat16 else 4
+    state = w.B * w.H * w.dv * w.dk * 4 * (1 + (block + 1) / 2)     # mu + upper triangle of P
+    return {"workload": w.name + ", %dx%d block-diagonal precision" % (block, block),
             "tokens_per_s": w.B * w.T / avg_s, "ms_per_launch": avg_s * 1e3,
-            "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                         "frac": achieved / peak,
-                         "traffic": load_traffic("bd4_fwd_layer760m_bf16_traffic.json")
-                         if w.name.startswith("layer760m") else None,
-                         "per_entry": "18.5 VALU + 1 v_rsq_f32 = 20.5 slots, 29.5 flops"}}
+            "roofline": roofline("alu", avg_s, flops=entries * mix["flops"],
+                                 nbytes=w.B * w.T * w.H * (2 * w.dk + 3 * w.dv + 1) * esz + state, mix=mix,
+                                 traffic=load_traffic("bd%d_fwd_layer760m_bf16_traffic.json" % block)
+                                 if w.name.startswith("layer760m") else None,
+                                 kernel="bd%d_fwd_kernel<%d, C, bf16, bf16>" % (block, w.dk))}
 
 
 def blockdiag_backward_extra(torch, pm, workloads, w, g, steps, block=2):
@@ -367,12 +397,7 @@ def blockdiag_backward_extra(torch, pm, workloads, w, g, steps, block=2):
     _, per = time_launches(fn, steps, 2, torch)
     avg_s = sum(per) / len(per) / 1e3
     entries = w.B * w.H * w.T * w.dv * w.dk
-    slots, flops = ((BD2_BWD_SLOTS_PER_ENTRY, BD2_BWD_FLOPS_PER_ENTRY) if block == 2 else
-                    (BD4_BWD_SLOTS_PER_ENTRY, BD4_BWD_FLOPS_PER_ENTRY))
-    peak = LANE_OPS_PER_S / slots * flops / 1e12
-    achieved = entries * flops / avg_s / 1e12
-    per_entry = ("replay 5.5 + reverse 25 VALU + 0.5 v_rcp_f32 = 31.5 slots, 45 flops" if block == 2 else
-                 "replay 8.5 + reverse 40 VALU + 1 v_rsq_f32 = 50.5 slots, 75 flops")
+    mix = BD2_BWD if block == 2 else BD4_BWD
     # one training step: the forward that stores the checkpoints, then the
     # backward that reuses them; beside it the plain forward and a backward
     # that recomputes them
@@ -395,12 +420,41 @@ def blockdiag_backward_extra(torch, pm, workloads, w, g, steps, block=2):
             "tokens_per_s": w.B * w.T / avg_s, "ms_per_call": avg_s * 1e3,
             "workspace_GB": ws.numel() / 1e9,
             "training_step_ms": f_s * 1e3, "recompute_training_step_ms": r_s * 1e3,
-            "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                         "frac": achieved / peak,
-                         "traffic": load_traffic("bd%d_bwd_layer760m_bf16_traffic.json" % block)
-                         if w.name.startswith("layer760m") else None,
-                         "scope": "whole call (5 kernels); per-kernel split in the committed trace",
-                         "per_entry": per_entry}}
+            "roofline": roofline("alu", avg_s, flops=entries * mix["flops"], mix=mix,
+                                 traffic=load_traffic("bd%d_bwd_layer760m_bf16_traffic.json" % block)
+                                 if w.name.startswith("layer760m") else None,
+                                 scope="whole call (5 kernels); per-kernel split in the committed trace")}
+
+
+def forward_config_extra(torch, pm, workloads, key, steps):
+    """The chunked forward on another of the workloads (the MQAR-scale fp32
+    layer, the 32k-token context and its beta = 1e-6 variant), in the launch
+    configuration the library picks for it (a time split where B*H is small),
+    timed as one call."""
+    w = workloads.WORKLOADS[key]
+    dev = torch.device("cuda:0")
+    inp = workloads.make_inputs(w)
+    g = {n: (x.to(dev) if isinstance(x, torch.Tensor) else x) for n, x in inp.items()}
+    y = torch.empty(w.B, w.T, w.H, w.dv, dtype=w.dtype, device=dev)
+    muT = torch.empty(w.B, w.H, w.dv, w.dk, device=dev)
+    IT = torch.empty_like(muT)
+    nws = pm.workspace_size(w.B, w.T, w.H, w.dk, w.dv, 0)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    fn = lambda: pm.fwd_chunked(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"],
+                                chunk=w.chunk, y=y, muT=muT, IT=IT, workspace=ws if nws else None)
+    _, per = time_launches(fn, steps, 3, torch)
+    avg_s = sum(per) / len(per) / 1e3
+    updates = w.B * w.H * w.T * w.dv * w.dk
+    esz = 2 if w.dtype == torch.bfloat16 else 4
+    # workspace floats: (nseg - 1) summaries of 2 bh dv dk + bh, a start-state copy of 2 bh dv dk
+    bh = w.B * w.H
+    nseg = (nws // 4 + bh) // (2 * bh * w.dv * w.dk + bh) if nws else 1
+    del g, inp
+    return {"workload": w.name + ", chunked forward", "tokens_per_s": w.B * w.T / avg_s,
+            "ms_per_call": avg_s * 1e3, "segments": nseg, "chunk": w.chunk,
+            "roofline": roofline("alu", avg_s, flops=updates * FWD["flops"], nbytes=fwd_bytes(w, esz, esz),
+                                 mix=FWD, traffic=None,
+                                 scope="whole call" + (" (summary pass + replay pass)" if nseg > 1 else ""))}
 
 
 def fig7_extra(torch, pm, workloads, dev, D, steps):
@@ -418,11 +472,14 @@ def fig7_extra(torch, pm, workloads, dev, D, steps):
     _, per = time_launches(fn, steps, 2, torch)
     avg_s = sum(per) / len(per) / 1e3
     updates = w.B * w.H * w.T * w.dv * w.dk
-    achieved = updates * FLOPS_PER_UPDATE / avg_s / 1e12
     return {"workload": w.name, "tokens_per_s": w.B * w.T / avg_s, "ms_per_launch": avg_s * 1e3,
             "state_updates_per_s": updates / avg_s,
-            "roofline": {"bound": "alu", "achieved": achieved, "peak": alu_peak_tflops(), "unit": "TFLOP/s",
-                         "frac": achieved / alu_peak_tflops(), "traffic": None}}
+            "roofline": roofline("alu", avg_s, flops=updates * FWD["flops"], nbytes=fwd_bytes(w, 2, 2), mix=FWD,
+                                 kernel="wide_fwd_kernel<%d, bf16, bf16>" % D)}
+
+
+EXTRAS = ("decode", "backward", "training_step", "frozen", "frozen_backward", "blockdiag", "blockdiag_decode",
+          "blockdiag4", "blockdiag_backward", "blockdiag4_backward", "recurrent_shape", "configs")
 
 
 def main():
@@ -434,7 +491,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads in the oracle sample (0: all heads of the workload)")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the backward and frozen-path timings")
+    ap.add_argument("--no-extras", action="store_true", help="skip every object beside the headline forward")
+    ap.add_argument("--only", default="",
+                    help="comma-separated subset of the extra objects to run (%s)" % ", ".join(EXTRAS))
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--workload", default="2",
                     help="forward workload to time: 2 (760M layer, default), 0, 1, 4 or 4b")
@@ -476,12 +535,9 @@ def main():
     avg_launch_s = sum(per) / len(per) / 1e3
     tokens = w.B * w.T
     updates = w.B * w.H * w.T * w.dv * w.dk
-    achieved = updates * FLOPS_PER_UPDATE / avg_launch_s / 1e12
-    peak = alu_peak_tflops()
     traffic = load_traffic("fwd_chunked_layer760m_bf16_traffic.json") if args.workload == "2" else None
     esz = 2 if w.dtype == torch.bfloat16 else 4
-    hbm_alg = (w.B * w.T * w.H * (2 * w.dk + 2 * w.dv + 1 + w.dv) * esz
-               + 8 * w.B * w.H * w.dv * w.dk)
+    tname = str(w.dtype).replace("torch.", "").replace("bfloat16", "bf16")
     out = {
         "metric": "tokens/s of Palimpsa chunked forward (B*T/s) and % of HBM/MFMA roofline",
         "value": tokens * args.steps / (total_ms / 1e3),
@@ -499,27 +555,46 @@ def main():
                    "T": w.T, "d_k": w.dk, "d_v": w.dv, "chunk": args.chunk or "auto",
                    "inputs": str(w.dtype).replace("torch.", ""), "state": "fp32",
                    "global_batch": w.B, "seq_len": w.T},
-        "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic,
-                     "kernel": "fwd_chunked_kernel<%d, C, %s, %s>" % (w.dk, *(2 * [str(w.dtype)[6:]])),
-                     "avg_launch_ms": avg_launch_s * 1e3,
-                     "per_update": "4 FMA + 2 MUL (10 flops) + 1 v_rcp_f32 (2 FMA slots)",
-                     "hbm_algorithmic_GBs": hbm_alg / avg_launch_s / 1e9},
+        "roofline": roofline("alu", avg_launch_s, flops=updates * FWD["flops"], nbytes=fwd_bytes(w, esz, esz),
+                             mix=FWD, traffic=traffic,
+                             kernel="fwd_chunked_kernel<%d, C, %s, %s>" % (w.dk, tname, tname),
+                             avg_launch_ms=avg_launch_s * 1e3,
+                             per_update="4 FMA + 2 MUL (10 flops) + 1 v_rcp_f32"),
     }
-    if not args.no_decode:
+    want = set(EXTRAS) if not args.only else set(args.only.split(","))
+    if args.no_extras:
+        want = set()
+    if args.no_decode:
+        want.discard("decode")
+    if "decode" in want:
         out["decode"] = decode_extra(torch, pm, workloads, max(64, args.steps))
-    if not args.no_extras and w.dtype == torch.bfloat16:
-        out["backward"] = backward_extra(torch, pm, workloads, w, g, max(5, args.steps // 5))
-        out["training_step"] = training_extra(torch, pm, workloads, w, g, max(5, args.steps // 5))
-        out["frozen"] = frozen_extra(torch, pm, w, g, max(20, args.steps))
-        out["frozen_backward"] = frozen_backward_extra(torch, pm, workloads, w, g, max(5, args.steps // 5))
-        out["blockdiag"] = blockdiag_extra(torch, pm, w, g, max(20, args.steps // 2))
-        out["blockdiag_decode"] = blockdiag_decode_extra(torch, pm, workloads, max(64, args.steps))
-        out["blockdiag4"] = blockdiag4_extra(torch, pm, w, g, max(10, args.steps // 5))
-        out["blockdiag_backward"] = blockdiag_backward_extra(torch, pm, workloads, w, g, max(5, args.steps // 5))
-        out["blockdiag4_backward"] = blockdiag_backward_extra(torch, pm, workloads, w, g, max(5, args.steps // 5),
-                                                              block=4)
-        out["recurrent_shape"] = [fig7_extra(torch, pm, workloads, dev, D, 5) for D in (512, 2048)]
+    if w.dtype == torch.bfloat16:
+        few = max(5, args.steps // 5)
+        if "backward" in want:
+            out["backward"] = backward_extra(torch, pm, workloads, w, g, few)
+        if "training_step" in want:
+            out["training_step"] = training_extra(torch, pm, workloads, w, g, few)
+        if "frozen" in want:
+            out["frozen"] = frozen_extra(torch, pm, w, g, max(20, args.steps))
+        if "frozen_backward" in want:
+            out["frozen_backward"] = frozen_backward_extra(torch, pm, workloads, w, g, few)
+        if "blockdiag" in want:
+            out["blockdiag"] = blockdiag_extra(torch, pm, w, g, max(20, args.steps // 2))
+        if "blockdiag_decode" in want:
+            out["blockdiag_decode"] = blockdiag_decode_extra(torch, pm, workloads, max(64, args.steps))
+        if "blockdiag4" in want:
+            out["blockdiag4"] = blockdiag_extra(torch, pm, w, g, max(10, args.steps // 5), block=4)
+        if "blockdiag_backward" in want:
+            out["blockdiag_backward"] = blockdiag_backward_extra(torch, pm, workloads, w, g, few)
+        if "blockdiag4_backward" in want:
+            out["blockdiag4_backward"] = blockdiag_backward_extra(torch, pm, workloads, w, g, few, block=4)
+        if "recurrent_shape" in want:
+            out["recurrent_shape"] = [fig7_extra(torch, pm, workloads, dev, D, 5) for D in (512, 2048)]
+    if "configs" in want:
+        del g
+        torch.cuda.empty_cache()
+        out["configs"] = {str(key): forward_config_extra(torch, pm, workloads, key, max(10, args.steps // 2))
+                          for key in (1, 4, "4b") if str(key) != args.workload}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads or w.B * w.H)
     print(json.dumps(out), flush=True)

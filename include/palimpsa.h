@@ -116,11 +116,13 @@ typedef enum {
  *   muT, IT   [B, H, dv, dk] float32 final state; both NULL skips writing it
  *                            (one NULL alone is an error).  muT may alias mu0
  *                            and IT may alias I0 (in-place resume).
- *   chunk     tokens staged per step through on-chip memory, one of
- *             {8, 16, 32, 64}, or 0 for the library's choice (8 is run as 16;
- *             a chunk whose staging buffers exceed the device's LDS is
- *             halved until they fit).  A performance hint only: the results
- *             are bit-identical for every chunk.
+ *   chunk     the most tokens to stage per step through on-chip memory, one
+ *             of {8, 16, 32, 64, 128}, or 0 for the library's choice (the
+ *             largest of 16, 32, 64 whose staging buffers let three
+ *             workgroups share a CU when the grid is large enough to need it,
+ *             else the largest that fits the device's LDS).  A nonzero chunk
+ *             caps that choice (8 is run as 16).  A performance hint only: the
+ *             results are bit-identical for every chunk.
  *   segments  time segments (0..64).  1: one pass over the sequence.  >= 2:
  *             cut T into that many segments (lengths rounded up to multiples
  *             of 64 tokens, so fewer may result) that run side by side: a
@@ -133,8 +135,10 @@ typedef enum {
  *             workgroups would leave the GPU under-filled).  Results of a split
  *             match the single pass up to float32 rounding.
  *   workspace, workspace_bytes
- *             device scratch for the segment summaries, owned by the caller,
- *             16-byte aligned; palimpsa_fwd_workspace_size() gives the size.
+ *             device scratch for the segment summaries and a copy of the
+ *             start state (so that an in-place resume stays correct under a
+ *             split), owned by the caller, 16-byte aligned;
+ *             palimpsa_fwd_workspace_size() gives the size.
  *             NULL / 0 is valid: with segments == 0 the forward then runs in
  *             one pass; an explicit segments >= 2 without enough workspace is
  *             PALIMPSA_ERR_INVALID_ARG.  Contents are overwritten; calls that

@@ -88,11 +88,16 @@ static void oracle_token(int dk, int dv,
     }
 }
 
+/* Threads of the OpenMP runtime's own default, taken before any call sets
+ * them; nthreads <= 0 means that default, whatever an earlier call asked for. */
+static int default_threads = 0;
+
 static void set_threads(int nthreads)
 {
 #ifdef _OPENMP
-    if (nthreads > 0)
-        omp_set_num_threads(nthreads);
+    if (default_threads == 0)
+        default_threads = omp_get_max_threads();
+    omp_set_num_threads(nthreads > 0 ? nthreads : default_threads);
 #else
     (void)nthreads;
 #endif
@@ -101,7 +106,9 @@ static void set_threads(int nthreads)
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP
-    return omp_get_max_threads();
+    if (default_threads == 0)
+        default_threads = omp_get_max_threads();
+    return default_threads;
 #else
     return 1;
 #endif

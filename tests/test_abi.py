@@ -85,7 +85,7 @@ FWD_CASES = [
     (dict(Ip=None), 1), (dict(y=None), 1), (dict(mu0=FAKE), 1), (dict(I0=FAKE), 1),
     (dict(muT=None), 1), (dict(IT=None), 1), (dict(B=0), 1), (dict(H=0), 1), (dict(T=-1), 1),
     (dict(dk=0), 1), (dict(ind=2), 1), (dict(outd=-1), 1), (dict(chunk=12), 1),
-    (dict(chunk=128), 1), (dict(dk=48), 2), (dict(dv=4104), 2), (dict(dv=24), 2), (dict(dk=16), 2),
+    (dict(chunk=256), 1), (dict(chunk=96), 1), (dict(dk=48), 2), (dict(dv=4104), 2), (dict(dv=24), 2), (dict(dk=16), 2),
     (dict(flags=16), 1), (dict(flags=-1), 1), (dict(flags=2, Ip=FAKE + 4), 3),
     # the training forward: a backward workspace, one pass at chunk 16, dk <= 128
     (dict(flags=8), 1), (dict(flags=4), 1), (dict(flags=4, ws=FAKE, wsb=64), 1),
@@ -107,11 +107,14 @@ def test_workspace_size_host_logic(lib):
     import bayesian_metaplastic_memory_amd as pm
     # 760M layer (768 workgroups): no split
     assert pm.workspace_size(8, 4096, 12, 128, 128, 0) == 0
-    # long context, 32 heads (256 workgroups): 3 segments -> 2 summaries
-    assert pm.workspace_size(1, 32768, 32, 128, 128, 0) == 2 * (2 * 32 * 128 * 128 + 32) * 4
+    # long context, 32 heads (256 workgroups): 3 segments -> 2 summaries (M_loc,
+    # Ibar_loc, decay product) plus one copy of the start state (mu0, I0)
+    def split_bytes(nseg, bh, dv, dk):
+        return ((nseg - 1) * (2 * bh * dv * dk + bh) + 2 * bh * dv * dk) * 4
+    assert pm.workspace_size(1, 32768, 32, 128, 128, 0) == split_bytes(3, 32, 128, 128)
     # explicit requests; rounding to 64-token segments caps the count
-    assert pm.workspace_size(1, 1000, 2, 64, 64, 4) == 3 * (2 * 2 * 64 * 64 + 2) * 4
-    assert pm.workspace_size(1, 100, 2, 64, 64, 8) == 1 * (2 * 2 * 64 * 64 + 2) * 4
+    assert pm.workspace_size(1, 1000, 2, 64, 64, 4) == split_bytes(4, 2, 64, 64)
+    assert pm.workspace_size(1, 100, 2, 64, 64, 8) == split_bytes(2, 2, 64, 64)
     assert pm.workspace_size(1, 64, 2, 64, 64, 8) == 0
     assert pm.workspace_size(1, 4096, 2, 64, 64, 1) == 0
     assert pm.workspace_size(1, 0, 2, 64, 64, 4) == 0

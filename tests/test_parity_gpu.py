@@ -11,7 +11,8 @@ import torch
 
 import oracle
 import workloads
-from parity_utils import TOL_BWD, TOL_F32, assert_close, gpu_args, rel_err, to_device, to_np, tol_for
+from parity_utils import (TOL_BWD, TOL_F32, assert_close, gpu_args, rel_err, report_per_head, to_device, to_np,
+                          tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,11 +36,16 @@ def _run_fwd(inp, chunk=0, out_dtype=None):
     return y, muT, IT
 
 
-def _compare_full(inp, y, muT, IT, tol, log=None):
-    y_ref, mu_ref, I_ref = oracle.fwd(**inp)
+def _compare_full(inp, y, muT, IT, tol, log=None, per_head=False, ref=None):
+    y_ref, mu_ref, I_ref = oracle.fwd(**inp) if ref is None else ref
     assert_close("y", y, y_ref, tol, log)
     assert_close("muT", muT, mu_ref, tol, log)
     assert_close("IT", IT, I_ref, tol, log)
+    if per_head:
+        report_per_head("y", y, y_ref, (0, 2), tol)
+        report_per_head("muT", muT, mu_ref, (0, 1), tol)
+        report_per_head("IT", IT, I_ref, (0, 1), tol)
+    return y_ref, mu_ref, I_ref
 
 
 def _compare_sampled(inp, heads, y, muT, IT, tol):
@@ -90,15 +96,19 @@ def test_mqar_fp32_full():
     _compare_full(inp, y, muT, IT, tol_for(w.dtype))
 
 
-LAYER_HEADS = [(0, 0), (3, 5), (7, 11), (5, 2)]
-
-
-def test_layer760m_bf16_sampled():
+def test_layer760m_bf16_every_head():
+    """The 760M layer at full size, every (b, h) against the oracle: y in
+    bf16 (the bf16 bar), then y in float32, where only the kernels' float32
+    arithmetic separates the two (held to the float32 bar, as the state)."""
     w = workloads.WORKLOADS[2]
-    _announce("fwd 760M-layer bf16", B=w.B, H=w.H, T=w.T, d=w.dk, chunk=w.chunk)
+    _announce("fwd 760M-layer bf16, every head", B=w.B, H=w.H, T=w.T, d=w.dk, chunk=w.chunk)
     inp = workloads.make_inputs(w)
     y, muT, IT = _run_fwd(inp, chunk=w.chunk)
-    _compare_sampled(inp, LAYER_HEADS, y, muT, IT, tol_for(w.dtype))
+    ref = _compare_full(inp, y, muT, IT, tol_for(w.dtype), per_head=True)
+    _announce("fwd 760M-layer bf16 inputs, fp32 y, every head", B=w.B, H=w.H, T=w.T, d=w.dk)
+    y32, muT32, IT32 = _run_fwd(inp, chunk=0, out_dtype=torch.float32)
+    assert torch.equal(muT32, muT) and torch.equal(IT32, IT)
+    _compare_full(inp, y32, muT32, IT32, TOL_F32, per_head=True, ref=ref)
 
 
 def test_layer760m_bf16_default_chunk_bitwise_equal():
@@ -113,15 +123,21 @@ def test_layer760m_bf16_default_chunk_bitwise_equal():
 
 
 @pytest.mark.parametrize("variant", [4, "4b"])
-def test_long_context_bf16_sampled(variant):
+def test_long_context_bf16_every_head(variant):
+    """32k tokens, every head (the launch the library chooses: a time split),
+    with y in bf16 and in float32."""
     w = workloads.WORKLOADS[variant]
-    _announce("fwd long-context bf16 " + str(variant), B=w.B, H=w.H, T=w.T, d=w.dk)
+    _announce("fwd long-context bf16 %s, every head" % variant, B=w.B, H=w.H, T=w.T, d=w.dk)
     inp = workloads.make_inputs(w)
     y, muT, IT = _run_fwd(inp, chunk=w.chunk)
-    heads = [(0, 0), (0, 31)]
-    _compare_sampled(inp, heads, y, muT, IT, tol_for(w.dtype))
+    ref = _compare_full(inp, y, muT, IT, tol_for(w.dtype), per_head=True)
+    _announce("fwd long-context %s, fp32 y" % variant, B=w.B, H=w.H, T=w.T, d=w.dk)
+    y32, muT32, IT32 = _run_fwd(inp, out_dtype=torch.float32)
+    _compare_full(inp, y32, muT32, IT32, TOL_F32, per_head=True, ref=ref)
+    del y32, ref
     if variant == "4b":
         # importance stays at I_prior: the Mamba2-form recurrence gives the same readout
+        heads = [(0, 0), (0, 31)]
         sub = oracle.select_heads(inp, heads)
         y_lim, _ = oracle.fwd_mamba2_limit(**{n: sub[n] for n in
                                               ("q", "k", "v", "beta", "dt", "A", "I_prior")})
@@ -141,7 +157,8 @@ def test_decode_bf16_after_prefill():
     inp = workloads.make_inputs(w, device=DEV)          # drawn on the GPU (2.1 GB per array)
     y_pre, mu, I = _pm().fwd_chunked(*gpu_args(inp), chunk=w.chunk)
     torch.cuda.synchronize()
-    heads = [(0, 0), (17, 9), (63, 31)]
+    # 64 (b, h) pairs: every sequence once and every head twice
+    heads = [(b, (5 * b + 3) % w.H) for b in range(w.B)]
     bs = [b for b, _ in heads]
     hs = [h for _, h in heads]
     sub_in = {}
@@ -150,7 +167,7 @@ def test_decode_bf16_after_prefill():
     sub_in["dt"] = inp["dt"][bs, :, hs].transpose(0, 1).unsqueeze(0).cpu()
     sub_in["A"] = inp["A"][hs].cpu()
     sub_in["I_prior"] = inp["I_prior"][hs].cpu()
-    y_ref, m_ref, P_ref = oracle.fwd(**sub_in, nthreads=len(heads))
+    y_ref, m_ref, P_ref = oracle.fwd(**sub_in)
     tol = tol_for(w.dtype)
     y_s = to_np(y_pre[bs, :, hs, :].transpose(0, 1).unsqueeze(0))
     assert_close("prefill y (sampled)", y_s, y_ref, tol)
@@ -194,7 +211,7 @@ def test_chunk_size_is_bitwise_invariant():
     inp = workloads.make_inputs(w, T=300)
     mu0, I0 = workloads.random_state(w.B, w.H, w.dv, w.dk, inp["I_prior"], seed=5)
     inp["mu0"], inp["I0"] = mu0, I0
-    outs = [_run_fwd(inp, chunk=c) for c in (8, 16, 32, 64, 0)]
+    outs = [_run_fwd(inp, chunk=c) for c in (8, 16, 32, 64, 128, 0)]
     for o in outs[1:]:
         for x, z in zip(outs[0], o):
             assert torch.equal(x, z)
@@ -219,6 +236,33 @@ def test_split_and_resume_matches_one_pass():
     assert rel_err(torch.cat([y1, y2], dim=1), y) <= 1e-5
     assert rel_err(mu2, muT) <= 1e-5 and rel_err(I2, IT) <= 1e-6
     _compare_full(inp, torch.cat([y1, y2], dim=1), mu2, I2, tol=1e-4)
+
+
+@pytest.mark.parametrize("segments", [3, 4])
+def test_split_resume_in_place_matches_out_of_place(segments):
+    """A time-split forward whose final state overwrites its start state
+    (muT aliasing mu0, IT aliasing I0) on a grid of several thousand
+    workgroups, far more than the GPU holds at once: the last segment's rows
+    finish while other segments of the same rows have not started, and the
+    result must still be bitwise that of the out-of-place call."""
+    w = workloads.WORKLOADS[2].with_(B=4, H=32)
+    T = 1024
+    _announce("split resume in place", B=w.B, H=w.H, T=T, d=w.dk, segments=segments)
+    inp = workloads.make_inputs(w, T=T)
+    mu0, I0 = workloads.random_state(w.B, w.H, w.dv, w.dk, inp["I_prior"], seed=11)
+    g = to_device(inp, DEV)
+    pm = _pm()
+    nwg = w.B * w.H * (w.dv // 16) * segments
+    print("  workgroups per pass: %d" % nwg, flush=True)
+    y_a, mu_a, I_a = pm.fwd_chunked(*gpu_args(g), mu0=mu0.to(DEV), I0=I0.to(DEV), segments=segments)
+    mu, I = mu0.to(DEV), I0.to(DEV)
+    y_b, mu_b, I_b = pm.fwd_chunked(*gpu_args(g), mu0=mu, I0=I, muT=mu, IT=I, segments=segments)
+    torch.cuda.synchronize()
+    assert mu_b.data_ptr() == mu.data_ptr() and I_b.data_ptr() == I.data_ptr()
+    assert torch.equal(y_a, y_b)
+    assert torch.equal(mu_a, mu_b) and torch.equal(I_a, I_b)
+    inp["mu0"], inp["I0"] = mu0, I0
+    _compare_sampled(inp, [(0, 0), (3, 31), (2, 17)], y_b, mu_b, I_b, tol_for(w.dtype))
 
 
 def test_step_sequence_matches_chunked():
