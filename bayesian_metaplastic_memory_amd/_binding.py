@@ -45,6 +45,10 @@ def load_library() -> ctypes.CDLL:
             lib.palimpsa_fwd_chunked.argtypes = ([vp] * 5 + [fp] * 4 + [vp, fp, fp] + [i] * 10 +
                                                  [vp, sz, vp])
             lib.palimpsa_fwd_chunked.restype = i
+            lib.palimpsa_fwd_chunked_noalloc.argtypes = ([vp] * 5 + [fp] * 4 + [vp, fp, fp] + [i] * 10 + [vp])
+            lib.palimpsa_fwd_chunked_noalloc.restype = i
+            lib.palimpsa_noalloc_scratch_bytes.argtypes = []
+            lib.palimpsa_noalloc_scratch_bytes.restype = sz
             lib.palimpsa_fwd_workspace_size.argtypes = [i] * 6
             lib.palimpsa_fwd_workspace_size.restype = sz
             lib.palimpsa_fwd_frozen.argtypes = [vp] * 5 + [fp] * 3 + [vp, fp] + [i] * 7 + [vp]
@@ -140,10 +144,27 @@ def workspace_size(B, T, H, dk, dv, segments: int = 0) -> int:
     return int(load_library().palimpsa_fwd_workspace_size(B, T, H, dk, dv, int(segments)))
 
 
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the fixed per-GPU scratch array of ``fwd_chunked_noalloc``."""
+    return int(load_library().palimpsa_noalloc_scratch_bytes())
+
+
+def fwd_chunked_noalloc(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None, chunk: int = 0,
+                        out_dtype=None, y=None, muT=None, IT=None, write_state: bool = True,
+                        segments: int = 0, vstar: bool = False):
+    """``fwd_chunked`` through ``palimpsa_fwd_chunked_noalloc``: no workspace;
+    a time split uses the library's fixed scratch array on the device.  The C
+    call allocates nothing (outputs not passed in are allocated here, by
+    torch, before it)."""
+    return fwd_chunked(q, k, v, beta, dt, A, I_prior, mu0=mu0, I0=I0, chunk=chunk, out_dtype=out_dtype,
+                       y=y, muT=muT, IT=IT, write_state=write_state, segments=segments, vstar=vstar,
+                       _noalloc=True)
+
+
 def fwd_chunked(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None, chunk: int = 0,
                 out_dtype=None, y=None, muT=None, IT=None, write_state: bool = True,
                 segments: int = 0, workspace=None, vstar: bool = False,
-                save_checkpoints: bool = False):
+                save_checkpoints: bool = False, _noalloc: bool = False):
     """Chunked forward.  Returns ``(y, muT, IT)``; ``muT``/``IT`` are None when
     ``write_state`` is False.  Outputs are allocated unless passed in (they may
     alias ``mu0``/``I0`` for an in-place resume).  ``segments`` (0 = library's
@@ -199,6 +220,16 @@ def fwd_chunked(q, k, v, beta, dt, A, I_prior, mu0=None, I0=None, chunk: int = 0
     else:
         muT = IT = None
     lib = load_library()
+    if _noalloc:
+        with torch.cuda.device(dev):
+            st = lib.palimpsa_fwd_chunked_noalloc(
+                _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(dt), _ptr(A), _ptr(I_prior),
+                _ptr(mu0), _ptr(I0), _ptr(y) if y.numel() else None,
+                _ptr(muT), _ptr(IT), B, T, H, dk, dv, int(chunk), int(segments),
+                _DTYPES[in_dtype], _DTYPES[out_dtype], flags, _stream_handle(dev))
+        if st != OK:
+            raise PalimpsaError(st, "palimpsa_fwd_chunked_noalloc")
+        return y, muT, IT
     if workspace is None:
         nbytes = workspace_size(B, T, H, dk, dv, segments)
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None

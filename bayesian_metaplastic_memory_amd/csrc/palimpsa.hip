@@ -51,9 +51,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "palimpsa.h"
 
 #define PALIMPSA_VERSION 100  // 0.1.0
+
+// The no-allocation forward's scratch (see device_scratch below): 64 MiB per
+// GPU, enough for every time split the library chooses by itself on MI355X.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -4270,6 +4277,36 @@ __global__ __launch_bounds__(kStepThreads) void bd4_step_kernel(Bd2StepArgs a) {
 
 inline bool aligned_to(const void *p, size_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
 
+// Scratch of palimpsa_fwd_chunked_noalloc: a fixed device array that each GPU
+// the library runs on holds until the process ends (callers that cannot
+// allocate pass no workspace).  Host code never uses the array's name as an
+// address (on the host it is only a stand-in for the symbol); it uses the
+// device address that hipGetSymbolAddress returns, looked up once per device
+// with that device current.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of this device's scratch (NULL and an error on failure).
+void *device_scratch(palimpsa_status *st) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *st = PALIMPSA_ERR_HIP;
+        return nullptr;
+    }
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *ptr = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) {
+        *st = PALIMPSA_ERR_HIP;
+        return nullptr;
+    }
+    *st = PALIMPSA_OK;
+    return g_scratch_ptr[dev];
+}
 inline bool head_ok(int d) { return d == 32 || d == 64 || d == 128; }
 // key widths of the exact forward and the decode step: up to a head as wide as
 // the model (the pages' recurrent-kernel measurement goes to 2048)
@@ -5075,7 +5112,9 @@ size_t palimpsa_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segm
 
 namespace {
 
-// The chunked forward (palimpsa_fwd_chunked).
+// The chunked forward behind both entry points.  noalloc: the caller passes
+// no workspace; a split runs in this device's fixed scratch array instead,
+// and a call whose split would need more than that array holds is refused.
 palimpsa_status fwd_chunked_impl(const void *q, const void *k, const void *v,
                                  const void *beta, const void *dt,
                                  const float *A, const float *I_prior,
@@ -5083,10 +5122,11 @@ palimpsa_status fwd_chunked_impl(const void *q, const void *k, const void *v,
                                  void *y, float *muT, float *IT,
                                  int B, int T, int H, int dk, int dv, int chunk, int segments,
                                  palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
-                                 void *workspace, size_t workspace_bytes, void *stream) {
+                                 void *workspace, size_t workspace_bytes, void *stream, bool noalloc) {
     if (!A || !I_prior || (T > 0 && (!q || !k || !v || !beta || !dt || !y)) || (flags & ~kFlagsFwd))
         return PALIMPSA_ERR_INVALID_ARG;
-
+    if (noalloc && (flags & PALIMPSA_SAVE_CHECKPOINTS))   // that workspace is a backward's, gigabytes
+        return PALIMPSA_ERR_INVALID_ARG;
     if ((mu0 == nullptr) != (I0 == nullptr) || (muT == nullptr) != (IT == nullptr))
         return PALIMPSA_ERR_INVALID_ARG;
     if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0)
@@ -5153,6 +5193,13 @@ palimpsa_status fwd_chunked_impl(const void *q, const void *k, const void *v,
 
     if (T == 0 && !muT) return PALIMPSA_OK;   // nothing to compute or write
     SegPlan plan = plan_segments(B, T, H, dk, dv, segments, device_cus());
+    if (noalloc && plan.nseg > 1) {
+        if (plan.ws_bytes > kNoAllocScratchBytes) return PALIMPSA_ERR_SCRATCH_LIMIT;
+        palimpsa_status st;
+        workspace = device_scratch(&st);
+        if (st != PALIMPSA_OK) return st;
+        workspace_bytes = kNoAllocScratchBytes;
+    }
     if (plan.nseg > 1 && (!workspace || workspace_bytes < plan.ws_bytes)) {
         if (segments >= 2) return PALIMPSA_ERR_INVALID_ARG;     // a split was asked for explicitly
         plan = plan_segments(B, T, H, dk, dv, 1, 256);          // auto: run unsplit
@@ -5183,9 +5230,22 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
                                      palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
                                      void *workspace, size_t workspace_bytes, void *stream) {
     return fwd_chunked_impl(q, k, v, beta, dt, A, I_prior, mu0, I0, y, muT, IT, B, T, H, dk, dv, chunk,
-                            segments, in_dtype, out_dtype, flags, workspace, workspace_bytes, stream);
+                            segments, in_dtype, out_dtype, flags, workspace, workspace_bytes, stream, false);
 }
 
+palimpsa_status palimpsa_fwd_chunked_noalloc(const void *q, const void *k, const void *v,
+                                             const void *beta, const void *dt,
+                                             const float *A, const float *I_prior,
+                                             const float *mu0, const float *I0,
+                                             void *y, float *muT, float *IT,
+                                             int B, int T, int H, int dk, int dv, int chunk, int segments,
+                                             palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
+                                             void *stream) {
+    return fwd_chunked_impl(q, k, v, beta, dt, A, I_prior, mu0, I0, y, muT, IT, B, T, H, dk, dv, chunk,
+                            segments, in_dtype, out_dtype, flags, nullptr, 0, stream, true);
+}
+
+size_t palimpsa_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
                               const void *beta, const void *dt,
@@ -5257,6 +5317,8 @@ const char *palimpsa_status_string(int status) {
     case PALIMPSA_ERR_UNSUPPORTED: return "unsupported configuration (head size must be 32, 64 or 128)";
     case PALIMPSA_ERR_ALIGNMENT: return "tensor pointer misaligned (see palimpsa.h)";
     case PALIMPSA_ERR_HIP: return "HIP runtime error at launch";
+    case PALIMPSA_ERR_SCRATCH_LIMIT:
+        return "the call needs more scratch than the no-allocation entry point's fixed buffer holds";
     default: return "unknown status";
     }
 }

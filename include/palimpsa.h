@@ -86,7 +86,9 @@ typedef enum {
     PALIMPSA_ERR_INVALID_ARG = 1,  /* null pointer, negative or zero size, bad enum */
     PALIMPSA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head size, dtype pair) */
     PALIMPSA_ERR_ALIGNMENT = 3,    /* a tensor pointer breaks the alignment rule above */
-    PALIMPSA_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
+    PALIMPSA_ERR_HIP = 4,          /* the HIP runtime reported an error at launch */
+    PALIMPSA_ERR_SCRATCH_LIMIT = 5 /* palimpsa_fwd_chunked_noalloc: the call would need more
+                                      scratch than the library's fixed buffer holds */
 } palimpsa_status;
 
 typedef enum {
@@ -168,6 +170,40 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
                                      int segments, palimpsa_dtype in_dtype,
                                      palimpsa_dtype out_dtype, int flags, void *workspace,
                                      size_t workspace_bytes, void *stream);
+
+/*
+ * palimpsa_fwd_chunked for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same operation, arguments and results as
+ * palimpsa_fwd_chunked with a large enough workspace, but it takes none.  A
+ * time split keeps its segment summaries and its copy of the start state in a
+ * fixed scratch array inside the library instead, palimpsa_noalloc_scratch_bytes()
+ * bytes (64 MiB) on each GPU the library runs on, held until the process ends.
+ * The call allocates nothing.
+ *
+ *   flags     as palimpsa_fwd_chunked, except PALIMPSA_SAVE_CHECKPOINTS
+ *             (whose workspace is a backward's): PALIMPSA_ERR_INVALID_ARG
+ *
+ * A call whose split (the library's own choice with segments == 0, or the
+ * one asked for) would need more scratch than that returns
+ * PALIMPSA_ERR_SCRATCH_LIMIT and launches nothing; every split the library
+ * chooses by itself on MI355X fits (at most about 38 MB, at dk = 256).
+ * Calls on one GPU share its scratch array: calls that can overlap on one GPU
+ * (other streams, other threads) race and must be ordered by the caller.
+ * The first call on a device looks the array's address up (with that device
+ * current); later calls reuse it.
+ */
+palimpsa_status palimpsa_fwd_chunked_noalloc(const void *q, const void *k, const void *v,
+                                             const void *beta, const void *dt,
+                                             const float *A, const float *I_prior,
+                                             const float *mu0, const float *I0,
+                                             void *y, float *muT, float *IT,
+                                             int B, int T, int H, int dk, int dv, int chunk,
+                                             int segments, palimpsa_dtype in_dtype,
+                                             palimpsa_dtype out_dtype, int flags, void *stream);
+
+/* Bytes of the fixed scratch array palimpsa_fwd_chunked_noalloc uses per GPU. */
+size_t palimpsa_noalloc_scratch_bytes(void);
 
 /*
  * Bytes of workspace palimpsa_fwd_chunked needs for the split it would choose

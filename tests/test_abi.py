@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     import bayesian_metaplastic_memory_amd as pm
-    for s in range(5):
+    for s in range(6):
         assert pm.status_string(s)
     assert pm.status_string(99) == "unknown status"
     assert pm.version() >= 100
@@ -125,6 +125,23 @@ def test_workspace_size_host_logic(lib):
 @pytest.mark.parametrize("over,status", FWD_CASES)
 def test_fwd_rejects_invalid_calls(lib, over, status):
     assert lib.palimpsa_fwd_chunked(*_fwd_args(**over)) == status
+
+
+def _noalloc_args(**over):
+    a = _fwd_args(**over)
+    return a[:22] + [a[24]]      # no workspace, no workspace bytes
+
+
+NOALLOC_CASES = [
+    (dict(q=None), 1), (dict(flags=4), 1), (dict(flags=8), 1), (dict(chunk=12), 1), (dict(B=0), 1),
+    (dict(dk=48), 2), (dict(q=FAKE + 4), 3), (dict(segments=65), 1),
+]
+
+
+@invalid_calls
+@pytest.mark.parametrize("over,status", NOALLOC_CASES)
+def test_noalloc_fwd_rejects_invalid_calls(lib, over, status):
+    assert lib.palimpsa_fwd_chunked_noalloc(*_noalloc_args(**over)) == status
 
 
 def _step_args(**over):
