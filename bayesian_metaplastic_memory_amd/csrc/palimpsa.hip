@@ -4512,11 +4512,13 @@ BwdWs plan_bwd_ws(void *base, int B, int T, int H, int dk, int dv, bool ipe) {
     // the training forward's discarded checkpoint stores (one workgroup block)
     const size_t o_sink = take((size_t)kThreads * 2 * (dk / kLanesPerRow));
     BwdWs w;
+    // section pointers only exist for a real base (a size query passes none)
     char *c = (char *)base;
-    w.ck = (float *)(c + o_ck); w.pqk = (float *)(c + o_pqk); w.ps = (float *)(c + o_ps);
-    w.gabh = (float *)(c + o_ga); w.gibh = (float *)(c + o_gi); w.pI0 = (float *)(c + o_pi);
-    w.pip = ipe ? (float *)(c + o_pip) : nullptr;
-    w.sink = (float *)(c + o_sink);
+    auto at = [c](size_t o) { return c ? c + o : nullptr; };
+    w.ck = (float *)at(o_ck); w.pqk = (float *)at(o_pqk); w.ps = (float *)at(o_ps);
+    w.gabh = (float *)at(o_ga); w.gibh = (float *)at(o_gi); w.pI0 = (float *)at(o_pi);
+    w.pip = ipe ? (float *)at(o_pip) : nullptr;
+    w.sink = (float *)at(o_sink);
     w.bytes = off;
     return w;
 }
@@ -4584,10 +4586,12 @@ FzbWs plan_fzb_ws(void *base, int B, int T, int H, int dk, int dv) {
     };
     const size_t o_s = take(bhc * e * 2), o_g = take(bhc * e * 2), o_t = take(bhc * e * 2);
     const size_t o_a = take(bhc * 4), o_i = take(bhc * 4);
+    // section pointers only exist for a real base (a size query passes none)
     char *c = (char *)base;
+    auto at = [c](size_t o) { return c ? c + o : nullptr; };
     FzbWs w;
-    w.sT = (bf16_t *)(c + o_s); w.ge = (bf16_t *)(c + o_g); w.gT = (bf16_t *)(c + o_t);
-    w.pA = (float *)(c + o_a); w.pI = (float *)(c + o_i);
+    w.sT = (bf16_t *)at(o_s); w.ge = (bf16_t *)at(o_g); w.gT = (bf16_t *)at(o_t);
+    w.pA = (float *)at(o_a); w.pI = (float *)at(o_i);
     w.bytes = off;
     return w;
 }
@@ -4695,10 +4699,12 @@ BdBwdWs plan_bd_bwd_ws(void *base, int B, int T, int H, int dk, int dv, int bloc
     // the training forward's discarded checkpoint stores (one workgroup block)
     const size_t o_sink = take((size_t)kThreads * lane_np);
     BdBwdWs w;
+    // section pointers only exist for a real base (a size query passes none)
     char *c = (char *)base;
-    w.ck = (float *)(c + o_ck); w.pqk = (float *)(c + o_pqk); w.ps = (float *)(c + o_ps);
-    w.gabh = (float *)(c + o_ga); w.gibh = (float *)(c + o_gi); w.pI0 = (float *)(c + o_pi);
-    w.sink = (float *)(c + o_sink);
+    auto at = [c](size_t o) { return c ? c + o : nullptr; };
+    w.ck = (float *)at(o_ck); w.pqk = (float *)at(o_pqk); w.ps = (float *)at(o_ps);
+    w.gabh = (float *)at(o_ga); w.gibh = (float *)at(o_gi); w.pI0 = (float *)at(o_pi);
+    w.sink = (float *)at(o_sink);
     w.bytes = off;
     return w;
 }
@@ -4755,7 +4761,7 @@ palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void 
                                        const void *dt, const float *A, const float *I_prior,
                                        const float *mu0, const float *P0, void *y, float *muT, float *PT,
                                        int B, int T, int H, int dk, int dv, int block,
-                                       palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
+                                       int in_dtype, int out_dtype, int flags,
                                        void *workspace, size_t workspace_bytes, void *stream) {
     if (!A || !I_prior || (T > 0 && (!q || !k || !v || !beta || !dt || !y)))
         return PALIMPSA_ERR_INVALID_ARG;
@@ -4805,7 +4811,7 @@ palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void 
 palimpsa_status palimpsa_step_blockdiag(const void *q, const void *k, const void *v, const void *beta,
                                         const void *dt, const float *A, const float *I_prior, float *mu, float *P,
                                         void *y, int B, int H, int dk, int dv, int block,
-                                        palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, void *stream) {
+                                        int in_dtype, int out_dtype, void *stream) {
     if (!q || !k || !v || !beta || !dt || !A || !I_prior || !mu || !P || !y)
         return PALIMPSA_ERR_INVALID_ARG;
     if (B <= 0 || H <= 0 || dk <= 0 || dv <= 0 || block <= 0 || !dtype_ok(in_dtype) || !dtype_ok(out_dtype))
@@ -4878,7 +4884,7 @@ palimpsa_status palimpsa_bwd_blockdiag(const void *q, const void *k, const void 
                                        float *gq, float *gk, float *gv, float *gbeta, float *gdt,
                                        float *gA, float *gIp, float *gmu0, float *gP0,
                                        int B, int T, int H, int dk, int dv, int block,
-                                       palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype, int flags,
+                                       int in_dtype, int gy_dtype, int flags,
                                        void *workspace, size_t workspace_bytes, void *stream) {
     if (!A || !I_prior || !gA || !gIp || !workspace || (flags & ~PALIMPSA_CHECKPOINTS_SAVED))
         return PALIMPSA_ERR_INVALID_ARG;
@@ -4934,7 +4940,7 @@ palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const 
                              float *gq, float *gk, float *gv, float *gbeta, float *gdt,
                              float *gA, float *gIp, float *gmu0, float *gI0,
                              int B, int T, int H, int dk, int dv,
-                             palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype, int flags,
+                             int in_dtype, int gy_dtype, int flags,
                              void *workspace, size_t workspace_bytes, void *stream) {
     if (!A || !I_prior || !gA || !gIp || !workspace || (flags & ~kFlagsBwd))
         return PALIMPSA_ERR_INVALID_ARG;
@@ -4997,7 +5003,7 @@ palimpsa_status palimpsa_bwd_frozen(const void *q, const void *k, const void *v,
                                     float *gq, float *gk, float *gv, float *gbeta, float *gdt,
                                     float *gA, float *gIp, float *gmu0,
                                     int B, int T, int H, int dk, int dv,
-                                    palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype,
+                                    int in_dtype, int gy_dtype,
                                     void *workspace, size_t workspace_bytes, void *stream) {
     if (!A || !I_prior || !gA || !gIp || !workspace)
         return PALIMPSA_ERR_INVALID_ARG;
@@ -5074,7 +5080,7 @@ palimpsa_status palimpsa_fwd_frozen(const void *q, const void *k, const void *v,
                                     const void *beta, const void *dt,
                                     const float *A, const float *I_prior, const float *mu0,
                                     void *y, float *muT, int B, int T, int H, int dk, int dv,
-                                    palimpsa_dtype in_dtype, palimpsa_dtype out_dtype,
+                                    int in_dtype, int out_dtype,
                                     void *stream) {
     if (!A || !I_prior || (T > 0 && (!q || !k || !v || !dt || !y)))
         return PALIMPSA_ERR_INVALID_ARG;
@@ -5121,7 +5127,7 @@ palimpsa_status fwd_chunked_impl(const void *q, const void *k, const void *v,
                                  const float *mu0, const float *I0,
                                  void *y, float *muT, float *IT,
                                  int B, int T, int H, int dk, int dv, int chunk, int segments,
-                                 palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
+                                 int in_dtype, int out_dtype, int flags,
                                  void *workspace, size_t workspace_bytes, void *stream, bool noalloc) {
     if (!A || !I_prior || (T > 0 && (!q || !k || !v || !beta || !dt || !y)) || (flags & ~kFlagsFwd))
         return PALIMPSA_ERR_INVALID_ARG;
@@ -5227,7 +5233,7 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
                                      const float *mu0, const float *I0,
                                      void *y, float *muT, float *IT,
                                      int B, int T, int H, int dk, int dv, int chunk, int segments,
-                                     palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
+                                     int in_dtype, int out_dtype, int flags,
                                      void *workspace, size_t workspace_bytes, void *stream) {
     return fwd_chunked_impl(q, k, v, beta, dt, A, I_prior, mu0, I0, y, muT, IT, B, T, H, dk, dv, chunk,
                             segments, in_dtype, out_dtype, flags, workspace, workspace_bytes, stream, false);
@@ -5239,7 +5245,7 @@ palimpsa_status palimpsa_fwd_chunked_noalloc(const void *q, const void *k, const
                                              const float *mu0, const float *I0,
                                              void *y, float *muT, float *IT,
                                              int B, int T, int H, int dk, int dv, int chunk, int segments,
-                                             palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
+                                             int in_dtype, int out_dtype, int flags,
                                              void *stream) {
     return fwd_chunked_impl(q, k, v, beta, dt, A, I_prior, mu0, I0, y, muT, IT, B, T, H, dk, dv, chunk,
                             segments, in_dtype, out_dtype, flags, nullptr, 0, stream, true);
@@ -5252,7 +5258,7 @@ palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
                               const float *A, const float *I_prior,
                               float *mu, float *I, void *y,
                               int B, int H, int dk, int dv,
-                              palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
+                              int in_dtype, int out_dtype, int flags,
                               void *stream) {
     if (!q || !k || !v || !beta || !dt || !A || !I_prior || !mu || !I || !y || (flags & ~kFlagsOptions))
         return PALIMPSA_ERR_INVALID_ARG;

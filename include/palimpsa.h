@@ -27,8 +27,11 @@
  *    or write with 128-bit accesses must be 16-byte aligned: q, k, v, beta and
  *    the state arrays of palimpsa_fwd_chunked, and mu, I of palimpsa_step.
  *    Every other pointer needs the natural alignment of its element type.
- *  - in_dtype applies to q, k, v, beta and dt; out_dtype to y.  A, I_prior and
- *    every state array are float32.
+ *  - in_dtype applies to q, k, v, beta and dt; out_dtype to y (gy_dtype to the
+ *    backward's gy).  They are int parameters holding a palimpsa_dtype value,
+ *    so that any int, valid or not, reaches the validation (which rejects
+ *    the others) as a defined value.  A, I_prior and every state array are
+ *    float32.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL means the default
  *    stream) and runs asynchronously; the caller synchronises.
  *  - The library allocates no device memory and keeps no per-call state;
@@ -167,8 +170,8 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
                                      const float *mu0, const float *I0,
                                      void *y, float *muT, float *IT,
                                      int B, int T, int H, int dk, int dv, int chunk,
-                                     int segments, palimpsa_dtype in_dtype,
-                                     palimpsa_dtype out_dtype, int flags, void *workspace,
+                                     int segments, int in_dtype,
+                                     int out_dtype, int flags, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
 /*
@@ -199,8 +202,8 @@ palimpsa_status palimpsa_fwd_chunked_noalloc(const void *q, const void *k, const
                                              const float *mu0, const float *I0,
                                              void *y, float *muT, float *IT,
                                              int B, int T, int H, int dk, int dv, int chunk,
-                                             int segments, palimpsa_dtype in_dtype,
-                                             palimpsa_dtype out_dtype, int flags, void *stream);
+                                             int segments, int in_dtype,
+                                             int out_dtype, int flags, void *stream);
 
 /* Bytes of the fixed scratch array palimpsa_fwd_chunked_noalloc uses per GPU. */
 size_t palimpsa_noalloc_scratch_bytes(void);
@@ -244,7 +247,7 @@ palimpsa_status palimpsa_fwd_frozen(const void *q, const void *k, const void *v,
                                     const void *beta, const void *dt,
                                     const float *A, const float *I_prior, const float *mu0,
                                     void *y, float *muT, int B, int T, int H, int dk, int dv,
-                                    palimpsa_dtype in_dtype, palimpsa_dtype out_dtype,
+                                    int in_dtype, int out_dtype,
                                     void *stream);
 
 /*
@@ -264,7 +267,7 @@ palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
                               const float *A, const float *I_prior,
                               float *mu, float *I, void *y,
                               int B, int H, int dk, int dv,
-                              palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
+                              int in_dtype, int out_dtype, int flags,
                               void *stream);
 
 /*
@@ -319,7 +322,7 @@ palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const 
                              float *gq, float *gk, float *gv, float *gbeta, float *gdt,
                              float *gA, float *gIp, float *gmu0, float *gI0,
                              int B, int T, int H, int dk, int dv,
-                             palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype, int flags,
+                             int in_dtype, int gy_dtype, int flags,
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -378,7 +381,7 @@ palimpsa_status palimpsa_bwd_frozen(const void *q, const void *k, const void *v,
                                     float *gq, float *gk, float *gv, float *gbeta, float *gdt,
                                     float *gA, float *gIp, float *gmu0,
                                     int B, int T, int H, int dk, int dv,
-                                    palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype,
+                                    int in_dtype, int gy_dtype,
                                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -419,7 +422,7 @@ palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void 
                                        const void *dt, const float *A, const float *I_prior,
                                        const float *mu0, const float *P0, void *y, float *muT, float *PT,
                                        int B, int T, int H, int dk, int dv, int block,
-                                       palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, int flags,
+                                       int in_dtype, int out_dtype, int flags,
                                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -449,7 +452,7 @@ palimpsa_status palimpsa_fwd_blockdiag(const void *q, const void *k, const void 
 palimpsa_status palimpsa_step_blockdiag(const void *q, const void *k, const void *v, const void *beta,
                                         const void *dt, const float *A, const float *I_prior, float *mu, float *P,
                                         void *y, int B, int H, int dk, int dv, int block,
-                                        palimpsa_dtype in_dtype, palimpsa_dtype out_dtype, void *stream);
+                                        int in_dtype, int out_dtype, void *stream);
 
 /*
  * Bytes of workspace palimpsa_bwd_blockdiag needs for these sizes (0 for
@@ -507,7 +510,7 @@ palimpsa_status palimpsa_bwd_blockdiag(const void *q, const void *k, const void 
                                        float *gq, float *gk, float *gv, float *gbeta, float *gdt,
                                        float *gA, float *gIp, float *gmu0, float *gP0,
                                        int B, int T, int H, int dk, int dv, int block,
-                                       palimpsa_dtype in_dtype, palimpsa_dtype gy_dtype, int flags,
+                                       int in_dtype, int gy_dtype, int flags,
                                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
