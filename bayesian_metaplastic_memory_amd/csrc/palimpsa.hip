@@ -70,6 +70,7 @@ namespace {
 
 typedef __bf16 bf16_t;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 template <typename T> struct io;
 // bits()/from_bits(): a scalar kept in its raw bits between a prefetch and its
@@ -214,7 +215,7 @@ struct Stager {
 
     uint4 kq[kKQPerThread];
     uint4 vv, bb;
-    uint32_t dtv, dtc;     // raw bits (io<TIn>::bits) until the commit
+    uint32_t dtv = 0, dtc = 0;   // raw bits (io<TIn>::bits) until the commit
 
     __device__ static inline int vb_slot(int tid) { return (tid + kThreads - 64) % kThreads; }
     __device__ static inline int gate_slot(int tid) { return (tid + kThreads - 128) % kThreads; }
@@ -460,41 +461,6 @@ __device__ inline void compute_chunk(const float *buf, int left, float *M, float
     }
 }
 
-// Summary pass of a time-split forward over one staged chunk: the affine map
-// of the chunk applied to a zero start, Ibar = alpha Ibar + beta k^2 and
-// M = alpha M + (beta v) k (natural parameters, App. A.12), plus the running
-// decay product P.  4 VALU ops per entry and token, no reciprocal, no readout.
-template <int DK, int C>
-__device__ inline void summary_chunk(const float *buf, float *M, float *Ib, float &P,
-                                     int row_local, int g) {
-    using LT = LaneTile<DK>;
-    const float *cbase = buf + LT::col(g, 0, 0);
-    const float *rbase = buf + C * Stage<DK>::kColFloats + 2 * row_local;
-    int goff = C * (Stage<DK>::kColFloats + Stage<DK>::kRowFloats);
-    asm volatile("" : "+v"(goff));
-    const float *gbase = buf + goff;
-#pragma unroll 4
-    for (int u = 0; u < C; ++u) {
-        const float alpha = gbase[2 * u];
-        const float2 rb = *(const float2 *)(rbase + u * Stage<DK>::kRowFloats);     // beta, beta*v
-        const float *ct = cbase + u * Stage<DK>::kColFloats;
-        P *= alpha;
-#pragma unroll
-        for (int m = 0; m < LT::kNVec; ++m) {
-            float kk[LT::kVec], k2[LT::kVec];
-            const int c0 = kLanesPerRow * LT::kVec * m;
-            vecf<LT::kVec>::ld(ct + c0, kk);
-            vecf<LT::kVec>::ld(ct + DK + c0, k2);
-#pragma unroll
-            for (int e = 0; e < LT::kVec; ++e) {
-                const int s = m * LT::kVec + e;
-                Ib[s] = fmaf(alpha, Ib[s], rb.x * k2[e]);
-                M[s] = fmaf(alpha, M[s], rb.y * kk[e]);
-            }
-        }
-    }
-}
-
 // Checkpoint pass of the backward over one staged chunk: the forward update
 // without readout (the same 4 VALU ops per entry and token as the replay,
 // so the states are bit-identical to the forward's), storing (M, I) before
@@ -539,7 +505,7 @@ __device__ inline void ckpt_chunk(const float *buf, float *M, float *I, int row_
     }
 }
 
-enum FwdMode { kReplay = 0, kSummary = 1, kCheckpoint = 2 };
+enum FwdMode { kReplay = 0, kCheckpoint = 2 };
 
 // One launch of the chunked forward.
 //
@@ -552,8 +518,7 @@ enum FwdMode { kReplay = 0, kSummary = 1, kCheckpoint = 2 };
 // kCheckpoint (the backward's first pass; nseg = 1): the sequence from
 // (mu0, I0) without readout, storing (M, I) before every kSB-th token.
 //
-// kSummary: segment s < nseg-1 runs from a zero state without readout and
-// writes its (M_loc, Ibar_loc, P) to the workspace.
+// (The summaries of a split come from summary_mfma_kernel.)
 template <int DK, int C, typename TIn, typename TOut, int MODE, bool IPE, bool CKPT = false>
 __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
     using LT = LaneTile<DK>;
@@ -587,8 +552,8 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
     const int t_begin = seg * a.seg_len;
     const int t_end = min(a.T, t_begin + a.seg_len);
 
-    // start state.  Replay: M = I0 . mu0, I = I0 (or M = 0, I = I_prior), then
-    // the earlier segments' summaries folded in.  Summary: M = Ibar = 0.
+    // start state: M = I0 . mu0, I = I0 (or M = 0, I = I_prior), then the
+    // earlier segments' summaries folded in
     float M[LT::kCols], I[LT::kCols];
     const size_t srow = ((size_t)bh * a.dv + row) * DK;
     float ipe[IPE ? LT::kCols : 1];
@@ -597,21 +562,7 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
 #pragma unroll
         for (int m = 0; m < LT::kNVec; ++m) vecf<LT::kVec>::ld(ip + LT::col(g, m, 0), ipe + m * LT::kVec);
     }
-    if (MODE == kSummary) {
-#pragma unroll
-        for (int s = 0; s < LT::kCols; ++s) { I[s] = 0.f; M[s] = 0.f; }   // I holds Ibar here
-        if (seg == 0 && a.mu0) {   // the replay pass's copy of the start state
-            const SegWs w(a.ws, a.nseg, (size_t)a.B * a.H, a.dv, DK);
-#pragma unroll
-            for (int m = 0; m < LT::kNVec; ++m) {
-                float mu[LT::kVec], ii[LT::kVec];
-                vecf<LT::kVec>::ld(a.mu0 + srow + LT::col(g, m, 0), mu);
-                vecf<LT::kVec>::ld(a.I0 + srow + LT::col(g, m, 0), ii);
-                vecf<LT::kVec>::st(w.mu0 + srow + LT::col(g, m, 0), mu);
-                vecf<LT::kVec>::st(w.I0 + srow + LT::col(g, m, 0), ii);
-            }
-        }
-    } else {
+    {
         if (a.mu0) {
             // a split replay reads the summary pass's copy (see SegWs)
             const float *mu0 = a.mu0, *I0 = a.I0;
@@ -676,7 +627,6 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
 
     const int ntok = t_end - t_begin;
     const int nchunks = (ntok + C - 1) / C;
-    float P = 1.f;
     // checkpoints: [B*H][nsb][row block][thread][2 DK/16] floats
     const size_t ck_stride = (size_t)rb_per_head * kThreads * 2 * LT::kCols;
     float *ckp = (MODE == kCheckpoint || CKPT)
@@ -702,8 +652,6 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
                 cur, ntok - t0, M, I, row_local, g, ybase + (size_t)t0 * ystride, ystride, ipe,
                 CKPT ? ckp + (size_t)(t0 / kSB) * ck_stride : nullptr,
                 CKPT ? (ntok - t0 > kSB ? ckp + (size_t)(t0 / kSB + 1) * ck_stride : a.ck_sink) : nullptr);
-        else if (MODE == kSummary)
-            summary_chunk<DK, C>(cur, M, I, P, row_local, g);
         else
             ckpt_chunk<DK, C, IPE>(cur, M, I, row_local, g, ckp, ck_stride, t0, ntok, ipe);
         if (more) st.commit((c & 1) ? buf0 : buf1, A, Ip, tid, a.vstar);
@@ -711,17 +659,6 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
     }
 
     if (MODE == kCheckpoint) return;
-    if (MODE == kSummary) {
-        const SegWs w(a.ws, a.nseg, (size_t)a.B * a.H, a.dv, DK);
-#pragma unroll
-        for (int m = 0; m < LT::kNVec; ++m) {
-            vecf<LT::kVec>::st(w.M + seg * w.per_seg + srow + LT::col(g, m, 0), M + m * LT::kVec);
-            vecf<LT::kVec>::st(w.Ib + seg * w.per_seg + srow + LT::col(g, m, 0), I + m * LT::kVec);
-        }
-        if (row0 == 0 && tid == 0)
-            w.P[(size_t)seg * a.B * a.H + bh] = P;
-        return;
-    }
 
     // final state (last segment only): mu = M / I (correctly rounded division), I
     if (a.muT && seg == a.nseg - 1) {
@@ -740,6 +677,287 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
             vecf<LT::kVec>::st(a.IT + srow + LT::col(g, m, 0), ii);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// time-split summary pass on the matrix cores
+// ---------------------------------------------------------------------------
+//
+// A segment's affine summary from a zero state is a sum of decayed outer
+// products (the natural-parameter scans of slides frame "Natural parameters
+// expose two affine scans", App. A.12, unrolled over the segment):
+//
+//     M_loc    = sum_s w_s (beta_s . v_s) (x) k_s,     w_s = prod_{r > s} alpha_r
+//     Ibar_loc = sum_s w_s  beta_s         (x) k_s^2,   P   = prod_s alpha_s
+//
+// a dense contraction over the segment's tokens, so it runs on
+// v_mfma_f32_16x16x4_f32 (float32 operands and accumulation) instead of the
+// recurrence's 4 VALU ops per entry and token.  Per chunk of 64 staged tokens
+// the accumulators are first scaled by the chunk's decay P_c and then take
+// the chunk's 64 outer products weighted by w within the chunk,
+// w_t = exp(sum_{r > t} -A dt_r) (a suffix sum over at most 63 tokens, so no
+// long products).
+//
+// One workgroup per (segment, head, 16 value rows, 64 key columns); wave w
+// owns the 16-column tiles w, w + 4, ... of its slice of M_loc and of Ibar_loc.  Operand
+// layout of v_mfma_f32_16x16x4_f32 (A 16x4, B 4x16, C 16x16): lane l gives
+// A[l % 16][l / 16] and B[l / 16][l % 16] and holds C[4 (l / 16) + r][l % 16],
+// r = 0..3; here the 4-wide inner dimension is 4 tokens, A's rows are value
+// rows and B's columns are key columns.
+// DPP moves for a wave scan: lanes whose source is out of range read 0
+// (dpp_zero), or only the rows in ROWS take part and the others add 0.
+template <int CTRL>
+__device__ inline float dpp_zero(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL, int ROWS>
+__device__ inline float dpp_rows(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+
+// Staging of the summary pass: chunks of 64 tokens kept in LDS in the input
+// type and in the input's layout (k as [token][column], v and beta as
+// [token][row]), written with 16-byte stores, plus the chunk-local weights
+// w_t and the chunk's decay.  The matrix-core operands need one column (or
+// row) per lane and successive tokens per step, so bf16 inputs are read back
+// with gfx950's transposing LDS read (ds_read_b64_tr_b16: four tokens of the
+// lane's column per read) and float32 inputs one value at a time.  k rows are
+// 80 elements apart (a 64-column slice plus padding), so that the 16 lanes of
+// a transposing read (4 rows x 4 column quads) hit 32 distinct banks.  The
+// global loads of chunk c+1 are in flight while chunk c is on the matrix
+// cores.
+template <int DK, typename TIn>
+struct SumStage {
+    static constexpr int C = 64;
+    static constexpr int kPer = 16 / (int)sizeof(TIn);         // elements per 16-byte packet
+    static constexpr int kRS = DK <= 64 ? 80 : DK + 16;         // k row stride (elements)
+    static constexpr int kColPkts = DK / kPer;
+    static constexpr int kRowPkts = kRowsPerWG / kPer;         // packets per token of v (or beta)
+    static constexpr int kKP = C * kColPkts;
+    static constexpr int kKPT = kKP / kThreads;
+    static constexpr int kVP = C * kRowPkts;
+    static constexpr int kVPT = (2 * kVP + kThreads - 1) / kThreads;
+    static constexpr size_t kKBytes = (size_t)C * kRS * sizeof(TIn);
+    static constexpr size_t kVBytes = (size_t)C * kRowsPerWG * sizeof(TIn);
+    static constexpr size_t kBuf = kKBytes + 2 * kVBytes + (size_t)(C + 4) * sizeof(float);
+    static_assert(kKP % kThreads == 0 && C <= kThreads, "whole packets per thread");
+
+    uint4 kp[kKPT], vp[kVPT];
+    uint32_t dtv = 0;
+
+    // k rows are DK wide here but ktok elements apart in memory (a slice of a
+    // wider head when the key columns are split over workgroups)
+    __device__ inline void load(const TIn *kb, const TIn *vb, const TIn *bb, const TIn *db, int left, int H,
+                                int dv, uint32_t ktok, int tid) {
+#pragma unroll
+        for (int u = 0; u < kKPT; ++u) {
+            const int p = tid + u * kThreads;
+            const int tt = p / kColPkts;
+            kp[u] = make_uint4(0, 0, 0, 0);
+            if (tt < left) kp[u] = *(const uint4 *)(kb + (uint32_t)tt * ktok + (p % kColPkts) * kPer);
+        }
+#pragma unroll
+        for (int u = 0; u < kVPT; ++u) {
+            const int q = tid + u * kThreads;
+            if (q < 2 * kVP) {
+                const bool isb = q >= kVP;
+                const int pp = isb ? q - kVP : q;
+                const int tt = pp / kRowPkts;
+                vp[u] = make_uint4(0, 0, 0, 0);
+                if (tt < left)
+                    vp[u] = *(const uint4 *)((isb ? bb : vb) + (uint32_t)tt * (uint32_t)(H * dv) + (pp % kRowPkts) * kPer);
+            }
+        }
+        if (tid < C) {
+            dtv = 0;
+            if (tid < left) dtv = io<TIn>::bits(db[(uint32_t)tid * (uint32_t)H]);
+        }
+    }
+
+    // Packets to LDS; wave 0 forms the chunk's weights: with l_t = -A dt_t,
+    // w_t = exp(sum_{r > t} l_r) (an exclusive suffix sum over the 64 lanes)
+    // and the chunk's decay P_c = w_0 exp(l_0).
+    __device__ inline void commit(char *buf, float A, int tid) const {
+        TIn *kl = (TIn *)buf;
+        TIn *vl = (TIn *)(buf + kKBytes);
+        TIn *bl = (TIn *)(buf + kKBytes + kVBytes);
+        float *gl = (float *)(buf + kKBytes + 2 * kVBytes);
+#pragma unroll
+        for (int u = 0; u < kKPT; ++u) {
+            const int p = tid + u * kThreads;
+            *(uint4 *)(kl + (p / kColPkts) * kRS + (p % kColPkts) * kPer) = kp[u];
+        }
+#pragma unroll
+        for (int u = 0; u < kVPT; ++u) {
+            const int q = tid + u * kThreads;
+            if (q < 2 * kVP) {
+                const bool isb = q >= kVP;
+                const int pp = isb ? q - kVP : q;
+                *(uint4 *)((isb ? bl : vl) + (pp / kRowPkts) * kRowsPerWG + (pp % kRowPkts) * kPer) = vp[u];
+            }
+        }
+        if (tid < 64) {
+            // token t sits in lane 63 - t, so a prefix scan over the lanes is a
+            // suffix sum over the tokens; shifting by one lane first makes it
+            // exclusive (a lane's own token is not in its sum)
+            const float l = -A * io<TIn>::from_bits(dtv);
+            const float x = __shfl(l, 63 - tid, 64);
+            float e = dpp_zero<0x138>(x);                    // wave_shr:1
+            e += dpp_zero<0x111>(e);                         // row_shr:1
+            e += dpp_zero<0x112>(e);                         // row_shr:2
+            e += dpp_zero<0x114>(e);                         // row_shr:4
+            e += dpp_zero<0x118>(e);                         // row_shr:8
+            e += dpp_rows<0x142, 0xA>(e);                    // row_bcast:15 into rows 1, 3
+            e += dpp_rows<0x143, 0xC>(e);                    // row_bcast:31 into rows 2, 3
+            const float et = __shfl(e, 63 - tid, 64);        // back to token order
+            const float wt = expf(et);
+            gl[tid] = wt;
+            if (tid == 0) gl[C] = wt * expf(l);
+        }
+    }
+
+    // Lane (g, m) = (lane / 16, lane % 16): X[r0 + 8 g + e][c0 + m], e = 0..3,
+    // widened (rows of rs elements).
+    __device__ static inline void read4(const TIn *X, int rs, int r0, int c0, int lane, float *o) {
+        const int g = lane >> 4, m = lane & 15;
+        if constexpr (sizeof(TIn) == 2) {
+            typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+            const TIn *p = X + (r0 + 8 * g + (m >> 2)) * rs + c0 + 4 * (m & 3);
+            const i16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = __uint_as_float((uint32_t)(uint16_t)x[e] << 16);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = io<TIn>::to_f32(X[(r0 + 8 * g + e) * rs + c0 + m]);
+        }
+    }
+};
+
+template <int DK, typename TIn>
+__global__ __launch_bounds__(kThreads) void summary_mfma_kernel(FwdArgs a) {
+    // each workgroup owns 16 value rows and a slice of DKC key columns
+    constexpr int kCS = DK >= 64 ? DK / 64 : 1;
+    constexpr int DKC = DK / kCS;
+    using SS = SumStage<DKC, TIn>;
+    constexpr int C = SS::C;
+    constexpr int kTiles = DKC / 16;
+    constexpr int kTPW = (kTiles + kWaves - 1) / kWaves;   // tiles per wave (at most)
+    extern __shared__ float lds[];
+    char *buf0 = (char *)lds;
+    char *buf1 = buf0 + SS::kBuf;
+
+    const int rb_per_head = a.dv / kRowsPerWG;
+    int wg = blockIdx.x;
+    if (a.xcd_remap) {
+        const int per_xcd = a.nwg / 8;
+        wg = (wg % 8) * per_xcd + wg / 8;
+    }
+    const int cs = wg % kCS;
+    wg /= kCS;
+    const int seg = wg / a.nwg_seg;
+    wg -= seg * a.nwg_seg;
+    const int bh = wg / rb_per_head;
+    const int row0 = (wg % rb_per_head) * kRowsPerWG;
+    const int col0 = cs * DKC;
+    const int b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar tile tests
+    const SegWs w(a.ws, a.nseg, (size_t)a.B * a.H, a.dv, DK);
+
+    if (seg == 0 && cs == 0 && a.mu0) {   // the replay pass's copy of the start state (see SegWs)
+        const size_t base = ((size_t)bh * a.dv + row0) * DK;
+        for (int n = 4 * tid; n < kRowsPerWG * DK; n += 4 * kThreads) {
+            *(float4 *)(w.mu0 + base + n) = *(const float4 *)(a.mu0 + base + n);
+            *(float4 *)(w.I0 + base + n) = *(const float4 *)(a.I0 + base + n);
+        }
+    }
+
+    const int t_begin = seg * a.seg_len;
+    const int ntok = min(a.T, t_begin + a.seg_len) - t_begin;
+    const int nchunks = (ntok + C - 1) / C;
+    const size_t seq = ((size_t)b * a.T + t_begin) * a.H + h;
+    const TIn *kseq = (const TIn *)a.k + seq * DK + col0;
+    const TIn *vseq = (const TIn *)a.v + seq * a.dv + row0;
+    const TIn *bseq = (const TIn *)a.beta + seq * a.dv + row0;
+    const TIn *dseq = (const TIn *)a.dt + seq;
+    const size_t kq_tok = (size_t)a.H * DK, vb_tok = (size_t)a.H * a.dv;
+    const float A = a.A[h];
+    const bool vstar = a.vstar != 0;
+
+    f32x4 accM[kTPW], accI[kTPW];
+#pragma unroll
+    for (int t = 0; t < kTPW; ++t) { accM[t] = f32x4{0.f, 0.f, 0.f, 0.f}; accI[t] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    float P = 1.f;
+    const int m = lane & 15, kq = lane >> 4;     // A row / B column; token within the 4-token step
+
+    SS st;
+    if (nchunks > 0) {
+        st.load(kseq, vseq, bseq, dseq, ntok, a.H, a.dv, (uint32_t)kq_tok, tid);
+        st.commit(buf0, A, tid);
+        __syncthreads();
+    }
+    for (int c = 0; c < nchunks; ++c) {
+        const bool more = c + 1 < nchunks;
+        if (more) {
+            const size_t tn = (size_t)((c + 1) * C);
+            st.load(kseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok, dseq + tn * a.H,
+                    ntok - (c + 1) * C, a.H, a.dv, (uint32_t)kq_tok, tid);
+        }
+        const char *cur = (c & 1) ? buf1 : buf0;
+        const TIn *kl = (const TIn *)cur;
+        const TIn *vl = (const TIn *)(cur + SS::kKBytes);
+        const TIn *bl = (const TIn *)(cur + SS::kKBytes + SS::kVBytes);
+        const float *gl = (const float *)(cur + SS::kKBytes + 2 * SS::kVBytes);
+        // decay of the whole chunk applied to what came before it
+        const float Pc = gl[C];
+        P *= Pc;
+#pragma unroll
+        for (int t = 0; t < kTPW; ++t) { accM[t] *= Pc; accI[t] *= Pc; }
+        // steps of 4 tokens: lane group g feeds token r0 + 8 g + e at step (r0, e),
+        // r0 in {0, 4, 32, 36}, so the 16 steps cover the 64 tokens once
+#pragma unroll
+        for (int r0i = 0; r0i < 4; ++r0i) {
+            const int r0 = (r0i >> 1) * 32 + (r0i & 1) * 4;
+            const float4 w4 = *(const float4 *)(gl + r0 + 8 * kq);
+            const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+            float v4[4], b4[4];
+            SS::read4(vl, kRowsPerWG, r0, 0, lane, v4);
+            SS::read4(bl, kRowsPerWG, r0, 0, lane, b4);
+#pragma unroll
+            for (int t = 0; t < kTPW; ++t) {
+                const int tile = wave + kWaves * t;
+                if (kTiles % kWaves == 0 || tile < kTiles) {
+                    float k4[4];
+                    SS::read4(kl, SS::kRS, r0, tile * 16, lane, k4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float aI = wv[e] * b4[e];
+                        const float aM = vstar ? wv[e] * v4[e] : aI * v4[e];   // w beta v, or w v*
+                        accM[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aM, k4[e], accM[t], 0, 0, 0);
+                        accI[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aI, k4[e] * k4[e], accI[t], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        if (more) st.commit((c & 1) ? buf0 : buf1, A, tid);
+        __syncthreads();
+    }
+
+    // lane l holds rows 4 (l / 16) + r, column l % 16 of each of its tiles
+#pragma unroll
+    for (int t = 0; t < kTPW; ++t) {
+        const int tile = wave + kWaves * t;
+        if (kTiles % kWaves == 0 || tile < kTiles) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const size_t o = ((size_t)bh * a.dv + row0 + 4 * kq + r) * DK + col0 + tile * 16 + m;
+                w.M[seg * w.per_seg + o] = accM[t][r];
+                w.Ib[seg * w.per_seg + o] = accI[t][r];
+            }
+        }
+    }
+    if (row0 == 0 && cs == 0 && tid == 0) w.P[(size_t)seg * a.B * a.H + bh] = P;
 }
 
 // ---------------------------------------------------------------------------
@@ -3521,7 +3739,6 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
 // the boundary matrices are handed from the state walk to the gradient kernel
 // in bf16.
 
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kFbC = 64;                  // tokens per chunk
 
@@ -4336,12 +4553,29 @@ palimpsa_status launch_pass(FwdArgs a, int nseg_launched, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
 }
 
+// The time split's summary pass on the matrix cores (segments 0..nseg-2).
+template <int DK, typename TIn>
+palimpsa_status launch_summary(FwdArgs a, hipStream_t s) {
+    constexpr int kCS = DK >= 64 ? DK / 64 : 1;   // key-column slices per (segment, head, row block)
+    a.nwg = a.nwg_seg * (a.nseg - 1) * kCS;
+    a.xcd_remap = (a.nwg % 8 == 0) ? 1 : 0;
+    const size_t lds = 2 * SumStage<DK / kCS, TIn>::kBuf;
+    auto kern = summary_mfma_kernel<DK, TIn>;
+    if (lds > 64 * 1024) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return PALIMPSA_ERR_HIP;
+    }
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(kern, dim3(a.nwg), dim3(kThreads), lds, s, a);
+    return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
+}
+
 // Summary pass (segments 0..nseg-2) then the replay pass (all segments).
 // (the summary pass does not read the prior, so it has no IPE variant)
 template <int DK, int C, typename TIn, typename TOut, bool IPE>
 palimpsa_status launch_fwd_t(const FwdArgs &a, hipStream_t s) {
     if (a.nseg > 1) {
-        const palimpsa_status st = launch_pass<DK, C, TIn, TOut, kSummary, false>(a, a.nseg - 1, s);
+        const palimpsa_status st = launch_summary<DK, TIn>(a, s);
         if (st != PALIMPSA_OK) return st;
     }
     return launch_pass<DK, C, TIn, TOut, kReplay, IPE>(a, a.nseg, s);
@@ -5210,7 +5444,7 @@ palimpsa_status fwd_chunked_impl(const void *q, const void *k, const void *v,
         if (segments >= 2) return PALIMPSA_ERR_INVALID_ARG;     // a split was asked for explicitly
         plan = plan_segments(B, T, H, dk, dv, 1, 256);          // auto: run unsplit
     }
-    if (nwg * plan.nseg > 0x7fffffffLL) return PALIMPSA_ERR_UNSUPPORTED;
+    if (nwg * plan.nseg * 4 > 0x7fffffffLL) return PALIMPSA_ERR_UNSUPPORTED;   // (summary: up to 4 column slices)
     a.nseg = plan.nseg;
     a.seg_len = plan.seg_len;
     a.ws = (float *)workspace;
