@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import workloads
-from parity_utils import (TOL_BWD, TOL_F32, assert_close, gpu_args, rel_err, report_per_head, to_device, to_np,
+from parity_utils import (TOL_BF16, TOL_BWD, TOL_F32, assert_close, gpu_args, rel_err, report_per_head, to_device, to_np,
                           tol_for)
 
 pytestmark = pytest.mark.gpu
@@ -767,13 +767,17 @@ def _sum_terms(inp, ref, vstar):
 
 def assert_sum_close(name, x, ref, terms, tol):
     """A batch sum against the oracle, relative to the sum of its terms'
-    magnitudes: a sum of terms that each carry relative error e is off by at
-    most e times that, whatever the cancellation between them."""
+    magnitudes (a sum of terms that each carry relative error e is off by at
+    most e times that, whatever the cancellation between them), and also
+    normwise, relative to the sum itself, against the bf16 bar."""
     x, ref = to_np(x), to_np(ref)
     den = float(np.max(terms))
     e = float(np.abs(x - ref).max() / (den if den > 0 else 1.0))
-    print("  %-22s max componentwise err %.3e (bar %.0e)" % (name, e, tol), flush=True)
+    en = rel_err(x, ref)
+    print("  %-22s max componentwise err %.3e (bar %.0e); normwise %.3e (bar %.0e)" % (name, e, tol, en, TOL_BF16),
+          flush=True)
     assert np.isfinite(x).all() and e <= tol, "%s: err %.3e > %.1e" % (name, e, tol)
+    assert en <= TOL_BF16, "%s: normwise err %.3e > %.1e" % (name, en, TOL_BF16)
 
 
 def _compare_bwd_frozen(got, ref, vstar, tol=TOL_BWD, inp=None):
