@@ -3170,6 +3170,271 @@ __global__ __launch_bounds__(kThreads) void wide_fwd_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// wide heads, row-parallel form (d_k >= 512 with a workspace)
+// ---------------------------------------------------------------------------
+//
+// At d_k = d_v = 2048 one head's state is 32 MB, far more than a workgroup can
+// stage per token, and the column-parallel layout above spends LDS reads and a
+// whole-wave reduction on every token.  Here lanes run along value rows: a
+// wave owns 64 rows of one head and KCL consecutive key columns of each (2 KCL
+// VGPRs of state per lane).  The column operands k_j, k_j^2, q_j of a token are
+// then the same for all 64 lanes, so they come in by scalar loads and feed the
+// FMAs as SGPR operands: the token loop is the update's 6 VALU + 1 v_rcp_f32
+// per entry with no LDS traffic and no cross-lane reduction, and each lane
+// sums its own KCL columns of the readout.
+//
+// A workgroup is kWrNW such waves on the same 64 rows and kWrNW * KCL adjacent
+// columns (a column slice).  The waves' partial readouts meet in LDS every
+// 8 or 16 tokens and are added in wave order; the NQ slices of a row block
+// leave their sums in a workspace, and a last pass adds them in slice order
+// and rounds to the output type.  A first pass writes k^2 (float32) and the
+// gates (alpha, c) once per token, so the scalar operands need no ALU work
+// beyond widening bf16 (two SALU bit operations per pair of columns).
+//
+// The loop-carried FMAs are written so that the new I and M land in the
+// registers of the old ones (in_place_fma): left to itself the register
+// allocator rotates the 2 KCL state registers through the temporaries and
+// pays a copy per entry and token.
+
+constexpr int kWrNW = 16;   // waves per workgroup (one column slice)
+// tokens per LDS reduction block: 16 (128 KB) where the registers allow one
+// workgroup per CU anyway, 8 (64 KB) at 16 columns per lane
+template <int KCL> constexpr int wr_tok() { return KCL >= 32 ? 16 : 8; }
+
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// A load the compiler may issue as a scalar (SMEM) load: the address is
+// uniform over the wave and the memory is not written by the kernel.
+template <typename T>
+__device__ inline T scalar_load(const void *p) {
+    return *(const __attribute__((address_space(4))) T *)p;
+}
+
+// x = s * x + w with x's register as the destination (v_fma_f32, s an SGPR)
+__device__ inline void in_place_fma(float &x, float s, float w) {
+    asm("v_fma_f32 %0, %1, %0, %2" : "+v"(x) : "s"(s), "v"(w));
+}
+
+// A group of a wave's columns for one token as the prep pass lays it out and
+// as it sits in SGPRs: k^2 in float32, k and q as raw 32-bit words of the
+// input type (16 bf16 columns or 8 float32 ones), the token's gate (alpha,
+// c), padded to a multiple of 16 bytes.  One record per (token, group): the
+// kernel reads each with four scalar loads off one address.
+template <typename TIn> struct ColGroup;
+template <> struct ColGroup<bf16_t> {
+    static constexpr int kCols = 16, kWords = 36;
+    f32x16 k2;
+    u32x8 k, q;
+    f32x2 g;
+    __device__ static inline float widen(uint32_t w, int j) {
+        return __uint_as_float(j & 1 ? w & 0xffff0000u : w << 16);
+    }
+    __device__ inline float kc(int j) const { return widen(k[j / 2], j); }
+    __device__ inline float qc(int j) const { return widen(q[j / 2], j); }
+    __device__ inline void load(const uint32_t *r) {
+        k2 = scalar_load<f32x16>(r);
+        k = scalar_load<u32x8>(r + 16);
+        q = scalar_load<u32x8>(r + 24);
+        g = scalar_load<f32x2>(r + 32);
+    }
+};
+template <> struct ColGroup<float> {
+    static constexpr int kCols = 8, kWords = 28;
+    f32x8 k2;
+    u32x8 k, q;
+    f32x2 g;
+    __device__ inline float kc(int j) const { return __uint_as_float(k[j]); }
+    __device__ inline float qc(int j) const { return __uint_as_float(q[j]); }
+    __device__ inline void load(const uint32_t *r) {
+        k2 = scalar_load<f32x8>(r);
+        k = scalar_load<u32x8>(r + 8);
+        q = scalar_load<u32x8>(r + 16);
+        g = scalar_load<f32x2>(r + 24);
+    }
+};
+
+struct WideRowsArgs {
+    const void *v, *beta;
+    const uint32_t *rec;   // [B, T, H, D / kCols] column-group records
+    const float *Ip, *mu0, *I0;
+    float *muT, *IT;
+    float *part;           // [nq, B, T, H, dv]: each column slice's readout
+    int B, T, H, D, dv, nq, nwg, xcd_remap;
+};
+
+// One column-group record per thread: k^2, the raw k and q words, the gate.
+template <typename TIn>
+__global__ __launch_bounds__(256) void wide_prep_kernel(const TIn *q, const TIn *k, const TIn *dt, const float *A,
+                                                        const float *Ip, uint32_t *rec, size_t ntok, int H, int D) {
+    using CG = ColGroup<TIn>;
+    constexpr int G = CG::kCols, W = CG::kWords;
+    constexpr int kWordsKQ = G * (int)sizeof(TIn) / 4;   // words of k (and of q) in a group
+    const int per_tok = D / G;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t tok = i / per_tok;
+    if (tok >= ntok) return;
+    const int c = (int)(i % per_tok) * G;
+    uint32_t *r = rec + i * W;
+    const uint4 *kp = (const uint4 *)(k + tok * D + c), *qp = (const uint4 *)(q + tok * D + c);
+#pragma unroll
+    for (int p = 0; p < kWordsKQ / 4; ++p) {
+        const uint4 kw = kp[p];
+        float x[packet<TIn>::kN];
+        packet<TIn>::widen(kw, x);
+#pragma unroll
+        for (int e = 0; e < packet<TIn>::kN; e += 4)
+            *(float4 *)(r + p * packet<TIn>::kN + e) = make_float4(x[e] * x[e], x[e + 1] * x[e + 1],
+                                                                   x[e + 2] * x[e + 2], x[e + 3] * x[e + 3]);
+        *(uint4 *)(r + G + 4 * p) = kw;
+        *(uint4 *)(r + G + kWordsKQ + 4 * p) = qp[p];
+    }
+    const int h = (int)(tok % H);
+    const float2 gt = gate(A[h], io<TIn>::to_f32(dt[tok]), Ip[h]);
+    *(uint4 *)(r + G + 2 * kWordsKQ) = make_uint4(__float_as_uint(gt.x), __float_as_uint(gt.y), 0u, 0u);
+}
+
+template <int KCL, typename TIn>
+__global__ __launch_bounds__(kWrNW * 64) void wide_rows_kernel(WideRowsArgs a) {
+    using CG = ColGroup<TIn>;
+    constexpr int NW = kWrNW, CB = wr_tok<KCL>(), G = CG::kCols, NG = KCL / G, W = CG::kWords;
+    static_assert(KCL % G == 0, "columns per lane come in whole groups");
+    extern __shared__ float red[];   // [2][CB][NW][64] partial readouts
+    int wg = blockIdx.x;
+    if (a.xcd_remap) {
+        const int per_xcd = a.nwg / 8;
+        wg = (wg % 8) * per_xcd + wg / 8;
+    }
+    // row block fastest, then column slice, then head: the row blocks of one
+    // slice share its records through an XCD's L2
+    const int rbs = a.dv / 64;
+    const int rb = wg % rbs;
+    const int qs = (wg / rbs) % a.nq;
+    const int bh = wg / rbs / a.nq;
+    const int b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int D = a.D, T = a.T;
+    const int row = rb * 64 + lane;
+    const int col0 = (qs * NW + wave) * KCL;
+
+    float M[KCL], I[KCL];
+    const size_t srow = ((size_t)bh * a.dv + row) * D + col0;
+    if (a.mu0) {
+#pragma unroll
+        for (int m = 0; m < KCL; m += 4) {
+            float mu[4], ii[4];
+            vecf<4>::ld(a.mu0 + srow + m, mu);
+            vecf<4>::ld(a.I0 + srow + m, ii);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { I[m + e] = ii[e]; M[m + e] = ii[e] * mu[e]; }
+        }
+    } else {
+        const float Ip = a.Ip[h];
+#pragma unroll
+        for (int s = 0; s < KCL; ++s) { I[s] = Ip; M[s] = 0.f; }
+    }
+
+    const size_t seq = (size_t)b * T * a.H + h;   // token index of (b, t = 0, h)
+    const size_t H = (size_t)a.H;
+    const uint32_t *rp = a.rec + (seq * (D / G) + col0 / G) * W;   // the wave's first record
+    const size_t tstep = H * (D / G) * W;                          // words between tokens
+    const TIn *vp = (const TIn *)a.v + seq * a.dv + row;
+    const TIn *bp = (const TIn *)a.beta + seq * a.dv + row;
+    const size_t rstep = H * a.dv;
+    const size_t slice = (size_t)a.B * T * H * a.dv;
+    float *part = a.part + (size_t)qs * slice + seq * a.dv + rb * 64;
+
+    // the lane's (beta, v), one token ahead, as raw bits
+    uint32_t bn = io<TIn>::bits(bp[0]), vn = io<TIn>::bits(vp[0]);
+    // Records are software-pipelined: group (t, gi) is in SGPRs before it is
+    // used, and the loads of the group after it are issued as soon as it has
+    // arrived.  Scalar loads complete out of order, so every wait is a wait
+    // for all of them; the empty asm makes the next loads' address depend on
+    // the current group, which places that one wait before they are issued,
+    // and the group's arithmetic then hides their latency.
+    CG nx;
+    nx.load(rp);
+    const int nblk = (T + CB - 1) / CB;
+#pragma unroll 1
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int t0 = blk * CB;
+        const int nt = T - t0 < CB ? T - t0 : CB;
+        float *buf = red + (blk & 1) * (CB * NW * 64);
+#pragma unroll 1
+        for (int u = 0; u < nt; ++u) {
+            const size_t t = (size_t)(t0 + u);
+            const bool last = t0 + u + 1 >= T;
+            const float bt = io<TIn>::from_bits(bn), bv = bt * io<TIn>::from_bits(vn);
+            if (!last) {
+                bn = io<TIn>::bits(bp[(t + 1) * rstep]);
+                vn = io<TIn>::bits(vp[(t + 1) * rstep]);
+            }
+            float acc = 0.f;
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const CG cur = nx;
+                // the next record: (t, gi + 1), else (t + 1, 0); the last
+                // token's last group reloads itself (an in-bounds address)
+                size_t off = gi + 1 < NG ? t * tstep + (gi + 1) * W : (last ? t * tstep + gi * W : (t + 1) * tstep);
+                const uint32_t w0 = cur.k[0];
+                asm volatile("" : "+s"(off) : "s"(w0));
+                nx.load(rp + off);
+                __builtin_amdgcn_sched_barrier(0);   // issue them before this group's arithmetic
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    const int s = gi * G + j;
+                    in_place_fma(I[s], cur.g.x, fmaf(bt, cur.k2[j], cur.g.y));
+                    in_place_fma(M[s], cur.g.x, bv * cur.kc(j));
+                    const float y = M[s] * __builtin_amdgcn_rcpf(I[s]);
+                    acc = s == 0 ? y * cur.qc(j) : fmaf(y, cur.qc(j), acc);
+                }
+            }
+            buf[(u * NW + wave) * 64 + lane] = acc;
+        }
+        // the slice's readout of these tokens: waves added in order (the
+        // other buffer is written next, and the block after that only once
+        // every wave has passed the next barrier, i.e. finished this sum)
+        __syncthreads();
+        if (tid < nt * 64) {
+            const int u = tid >> 6, r = tid & 63;
+            float s = buf[u * NW * 64 + r];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) s += buf[(u * NW + w) * 64 + r];
+            part[(size_t)(t0 + u) * rstep + r] = s;
+        }
+    }
+    if (a.muT) {
+#pragma unroll
+        for (int m = 0; m < KCL; m += 4) {
+            float mu[4], ii[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { mu[e] = M[m + e] / I[m + e]; ii[e] = I[m + e]; }
+            vecf<4>::st(a.muT + srow + m, mu);
+            vecf<4>::st(a.IT + srow + m, ii);
+        }
+    }
+}
+
+// y = the column slices' readouts added in slice order, rounded to TOut
+template <typename TOut>
+__global__ __launch_bounds__(256) void wide_sum_kernel(const float *part, TOut *y, size_t n, int nq) {
+    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    float4 s = *(const float4 *)(part + i);
+    for (int q = 1; q < nq; ++q) {
+        const float4 x = *(const float4 *)(part + (size_t)q * n + i);
+        s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
+    }
+    y[i] = io<TOut>::from_f32(s.x);
+    y[i + 1] = io<TOut>::from_f32(s.y);
+    y[i + 2] = io<TOut>::from_f32(s.z);
+    y[i + 3] = io<TOut>::from_f32(s.w);
+}
+
+// ---------------------------------------------------------------------------
 // frozen-importance forward (the Mamba2 limit) on the matrix cores
 // ---------------------------------------------------------------------------
 //
@@ -4605,6 +4870,65 @@ palimpsa_status launch_wide(FwdArgs a, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
 }
 
+// Row-parallel wide-head forward: columns per lane and column slices, the
+// workspace layout [column-group records][slice readouts] (256-byte aligned;
+// the records are sized for float32 inputs, 14 bytes per token and column,
+// bf16 ones use 9).  Taken for d_k >= 512 when d_v is a multiple of 64,
+// T >= 1 and the grid covers every CU at least once; otherwise the
+// column-parallel kernel runs.
+struct WideRowsPlan {
+    int kcl, nq;
+    long long nwg;
+    size_t part_off, bytes;
+};
+bool plan_wide_rows(int B, int T, int H, int dk, int dv, int cus, WideRowsPlan *p) {
+    if (dk < 512 || T <= 0 || dv % 64 != 0) return false;
+    p->kcl = dk >= 1024 ? 32 : 16;
+    p->nq = dk / (p->kcl * kWrNW);
+    p->nwg = (long long)B * H * (dv / 64) * p->nq;
+    if (p->nwg < cus || p->nwg > 0x7fffffffLL) return false;
+    const size_t ntok = (size_t)B * T * H;
+    static_assert(ColGroup<float>::kWords * 4 == 14 * ColGroup<float>::kCols, "float32 records: 14 B per column");
+    static_assert(ColGroup<bf16_t>::kWords * 4 <= 14 * ColGroup<bf16_t>::kCols, "bf16 records fit that size");
+    p->part_off = (ntok * dk * 14 + 255) / 256 * 256;
+    p->bytes = p->part_off + (size_t)p->nq * ntok * dv * sizeof(float);
+    return true;
+}
+
+template <int KCL, typename TIn, typename TOut>
+palimpsa_status launch_wide_rows(const FwdArgs &f, int dk, const WideRowsPlan &p, void *ws, hipStream_t s) {
+    WideRowsArgs a;
+    a.v = f.v; a.beta = f.beta;
+    a.rec = (const uint32_t *)ws;
+    a.Ip = f.Ip; a.mu0 = f.mu0; a.I0 = f.I0; a.muT = f.muT; a.IT = f.IT;
+    a.part = (float *)((char *)ws + p.part_off);
+    a.B = f.B; a.T = f.T; a.H = f.H; a.D = dk; a.dv = f.dv; a.nq = p.nq;
+    a.nwg = (int)p.nwg;
+    a.xcd_remap = (a.nwg % 8 == 0) ? 1 : 0;
+    const size_t ntok = (size_t)f.B * f.T * f.H;
+    const size_t prep_threads = ntok * (dk / ColGroup<TIn>::kCols);
+    const size_t n = ntok * f.dv;
+    const size_t lds = (size_t)2 * wr_tok<KCL>() * kWrNW * 64 * sizeof(float);
+    auto kern = wide_rows_kernel<KCL, TIn>;
+    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return PALIMPSA_ERR_HIP;
+    if ((prep_threads + 255) / 256 > 0x7fffffffULL || (n / 4 + 255) / 256 > 0x7fffffffULL)
+        return PALIMPSA_ERR_UNSUPPORTED;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(wide_prep_kernel<TIn>, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, s,
+                       (const TIn *)f.q, (const TIn *)f.k, (const TIn *)f.dt, f.A, f.Ip, (uint32_t *)ws, ntok, f.H, dk);
+    hipLaunchKernelGGL(kern, dim3(a.nwg), dim3(kWrNW * 64), lds, s, a);
+    hipLaunchKernelGGL(wide_sum_kernel<TOut>, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
+                       (const float *)a.part, (TOut *)f.y, n, p.nq);
+    return hipGetLastError() == hipSuccess ? PALIMPSA_OK : PALIMPSA_ERR_HIP;
+}
+
+template <typename TIn, typename TOut>
+palimpsa_status launch_wide_rows_d(const FwdArgs &f, int dk, const WideRowsPlan &p, void *ws, hipStream_t s) {
+    return p.kcl == 32 ? launch_wide_rows<32, TIn, TOut>(f, dk, p, ws, s)
+                       : launch_wide_rows<16, TIn, TOut>(f, dk, p, ws, s);
+}
+
 // Training forward: the forward that also stores the backward's checkpoints
 // (one pass, chunk 16 as the checkpoint pass, so the states are the same bits).
 template <typename TIn, typename TOut>
@@ -5344,7 +5668,11 @@ palimpsa_status palimpsa_fwd_frozen(const void *q, const void *k, const void *v,
 
 
 size_t palimpsa_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segments) {
-    if (B <= 0 || H <= 0 || T < 0 || !fwd_dk_ok(dk) || !fwd_dv_ok(dv) || segments < 0 || dk > 256) return 0;
+    if (B <= 0 || H <= 0 || T < 0 || !fwd_dk_ok(dk) || !fwd_dv_ok(dv) || segments < 0) return 0;
+    if (dk > 256) {
+        WideRowsPlan p;
+        return plan_wide_rows(B, T, H, dk, dv, device_cus(), &p) ? p.bytes : 0;
+    }
     return plan_segments(B, T, H, dk, dv, segments, device_cus()).ws_bytes;
 }
 
@@ -5432,6 +5760,15 @@ palimpsa_status fwd_chunked_impl(const void *q, const void *k, const void *v,
     }
 
     if (T == 0 && !muT) return PALIMPSA_OK;   // nothing to compute or write
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf_in = in_dtype == PALIMPSA_BF16, bf_out = out_dtype == PALIMPSA_BF16;
+    WideRowsPlan wp;
+    if (!noalloc && workspace && plan_wide_rows(B, T, H, dk, dv, device_cus(), &wp) && workspace_bytes >= wp.bytes) {
+        if (bf_in && bf_out) return launch_wide_rows_d<bf16_t, bf16_t>(a, dk, wp, workspace, s);
+        if (bf_in) return launch_wide_rows_d<bf16_t, float>(a, dk, wp, workspace, s);
+        if (bf_out) return launch_wide_rows_d<float, bf16_t>(a, dk, wp, workspace, s);
+        return launch_wide_rows_d<float, float>(a, dk, wp, workspace, s);
+    }
     SegPlan plan = plan_segments(B, T, H, dk, dv, segments, device_cus());
     if (noalloc && plan.nseg > 1) {
         if (plan.ws_bytes > kNoAllocScratchBytes) return PALIMPSA_ERR_SCRATCH_LIMIT;
@@ -5449,8 +5786,6 @@ palimpsa_status fwd_chunked_impl(const void *q, const void *k, const void *v,
     a.seg_len = plan.seg_len;
     a.ws = (float *)workspace;
     const int C = pick_chunk(chunk, dk, nwg * plan.nseg, device_lds_max());
-    hipStream_t s = (hipStream_t)stream;
-    const bool bf_in = in_dtype == PALIMPSA_BF16, bf_out = out_dtype == PALIMPSA_BF16;
     if (bf_in && bf_out) return launch_fwd_d<bf16_t, bf16_t>(a, dk, C, ipe, s);
     if (bf_in) return launch_fwd_d<bf16_t, float>(a, dk, C, ipe, s);
     if (bf_out) return launch_fwd_d<float, bf16_t>(a, dk, C, ipe, s);

@@ -460,22 +460,28 @@ def forward_config_extra(torch, pm, workloads, key, steps):
 def fig7_extra(torch, pm, workloads, dev, D, steps):
     """One head as wide as the model, the shape of the pages' recurrent-kernel
     measurement (B=16, L=2048, H=1, d_k = d_v = D; bf16 inputs, fp32 state),
-    through the chunked forward (the state stays on chip for the whole
-    sequence, as in a recurrent kernel)."""
+    through the chunked forward with its workspace: the row-parallel form (a
+    prep pass of column records, the recurrence with the state in registers for
+    the whole sequence, and the sum over column slices)."""
     w = workloads.WORKLOADS[2].with_(name="recurrent-shape B16 L2048 H1 D%d" % D, B=16, T=2048, H=1, dk=D, dv=D)
     inp = workloads.make_inputs(w, seed=70 + D // 512)
     g = {n: (x.to(dev) if isinstance(x, torch.Tensor) else x) for n, x in inp.items()}
     y = torch.empty(w.B, w.T, w.H, w.dv, dtype=w.dtype, device=dev)
     muT = torch.empty(w.B, w.H, w.dv, w.dk, device=dev)
     IT = torch.empty_like(muT)
-    fn = lambda: pm.fwd_chunked(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], y=y, muT=muT, IT=IT)
+    nws = pm.workspace_size(w.B, w.T, w.H, w.dk, w.dv)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    fn = lambda: pm.fwd_chunked(g["q"], g["k"], g["v"], g["beta"], g["dt"], g["A"], g["I_prior"], y=y, muT=muT, IT=IT,
+                                workspace=ws)
     _, per = time_launches(fn, steps, 2, torch)
     avg_s = sum(per) / len(per) / 1e3
     updates = w.B * w.H * w.T * w.dv * w.dk
+    kcl = 32 if D >= 1024 else 16
     return {"workload": w.name, "tokens_per_s": w.B * w.T / avg_s, "ms_per_launch": avg_s * 1e3,
-            "state_updates_per_s": updates / avg_s,
+            "state_updates_per_s": updates / avg_s, "workspace_bytes": nws,
             "roofline": roofline("alu", avg_s, flops=updates * FWD["flops"], nbytes=fwd_bytes(w, 2, 2), mix=FWD,
-                                 kernel="wide_fwd_kernel<%d, bf16, bf16>" % D)}
+                                 kernel="wide_prep_kernel<bf16> + wide_rows_kernel<%d, bf16> + wide_sum_kernel<bf16>"
+                                        % kcl, scope="whole call")}
 
 
 EXTRAS = ("decode", "backward", "training_step", "frozen", "frozen_backward", "blockdiag", "blockdiag_decode",

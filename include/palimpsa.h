@@ -148,6 +148,15 @@ typedef enum {
  *             one pass; an explicit segments >= 2 without enough workspace is
  *             PALIMPSA_ERR_INVALID_ARG.  Contents are overwritten; calls that
  *             share a workspace must not overlap.
+ *             Heads of dk >= 512 (dv a multiple of 64, T >= 1, and at least
+ *             one workgroup of 64 value rows x one column slice per CU) use
+ *             it for the row-parallel form: per-token records of the column
+ *             operands (14 bytes per token and key column) and each column
+ *             slice's partial readout (4 bytes per output element and slice;
+ *             2 slices at dk = 512 and 1024, 4 at 2048);
+ *             palimpsa_fwd_workspace_size() reports that size.  Without it (NULL, or fewer bytes) such heads run the
+ *             column-parallel kernel: the final state is the same bits and y
+ *             differs only in the float32 order of its sum over key columns.
  *   flags     palimpsa_flags bits (see above), or 0.
  *
  * With PALIMPSA_SAVE_CHECKPOINTS (the training forward) the workspace is a
@@ -191,6 +200,9 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
  * one asked for) would need more scratch than that returns
  * PALIMPSA_ERR_SCRATCH_LIMIT and launches nothing; every split the library
  * chooses by itself on MI355X fits (at most about 38 MB, at dk = 256).
+ * Heads of dk >= 512 run the column-parallel kernel here (the row-parallel
+ * form's workspace is gigabytes): results as palimpsa_fwd_chunked without a
+ * workspace.
  * Calls on one GPU share its scratch array: calls that can overlap on one GPU
  * (other streams, other threads) race and must be ordered by the caller.
  * The first call on a device looks the array's address up (with that device
@@ -211,7 +223,9 @@ size_t palimpsa_noalloc_scratch_bytes(void);
 /*
  * Bytes of workspace palimpsa_fwd_chunked needs for the split it would choose
  * for these sizes and `segments` on the current device (0: no split, no
- * workspace).  Returns 0 for sizes the forward would reject.
+ * workspace), or, for dk >= 512, for the row-parallel form (0 where that
+ * form is not taken; `segments` is then not used).  Returns 0 for sizes the
+ * forward would reject.
  */
 size_t palimpsa_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segments);
 

@@ -121,6 +121,29 @@ def test_workspace_size_host_logic(lib):
     assert pm.workspace_size(1, 64, 2, 48, 64, 0) == 0
 
 
+def test_wide_rows_workspace_size_host_logic(lib):
+    """Heads of 512 keys and wider: the row-parallel form's workspace is the
+    column-group records (14 bytes per token and key column, padded to 256
+    bytes) plus 4 bytes per output element and column slice (2 slices at
+    d_k = 512 and 1024, 4 at 2048); it is offered only when d_v is a multiple
+    of 64, T >= 1 and the 64-row x slice grid has a workgroup for each of the
+    device's CUs (256 without a device).  The split request is not used."""
+    import bayesian_metaplastic_memory_amd as pm
+
+    def expect(B, T, H, dk, dv):
+        nq = 2 if dk <= 1024 else 4
+        ntok = B * T * H
+        return (ntok * dk * 14 + 255) // 256 * 256 + nq * ntok * dv * 4
+    for shape in [(16, 2048, 1, 2048, 2048), (16, 2048, 1, 512, 512), (2, 9, 2, 1024, 2048), (1, 3, 1, 2048, 4096),
+                  (4, 21, 1, 512, 2048)]:
+        assert pm.workspace_size(*shape) == expect(*shape), shape
+        assert pm.workspace_size(*shape, 3) == expect(*shape), shape
+    assert pm.workspace_size(1, 9, 1, 2048, 2048) == 0      # 128 workgroups
+    assert pm.workspace_size(16, 9, 1, 2048, 2016) == 0     # d_v not a multiple of 64
+    assert pm.workspace_size(16, 0, 1, 2048, 2048) == 0     # empty sequence
+    assert pm.workspace_size(16, 9, 1, 256, 256) == 0       # d_k = 256: the column-parallel kernel
+
+
 @invalid_calls
 @pytest.mark.parametrize("over,status", FWD_CASES)
 def test_fwd_rejects_invalid_calls(lib, over, status):

@@ -1541,6 +1541,86 @@ def test_wide_heads_forward_and_step(B, H, T, dk, dv, dtype, state):
     assert_close("wide step I", IT, ref[2], TOL_F32)
 
 
+# Heads of 512 keys and wider run row-parallel (lanes on value rows, the
+# column operands k, k^2, q as scalar operands, partial readouts of column
+# slices added in a last pass) when the call has the workspace that
+# workspace_size() reports; that is nonzero when d_v is a multiple of 64 and
+# the grid of 64-row blocks x column slices covers every CU.
+ROWS_CASES = [
+    # B, H, T, dk, dv, dtype, start state
+    (4, 1, 21, 512, 2048, torch.bfloat16, True),    # 16 columns per lane, 2 slices, ragged last 8-token block
+    (2, 2, 9, 1024, 2048, torch.float32, False),    # 32 columns per lane, 2 slices
+    (1, 2, 11, 2048, 2048, torch.bfloat16, True),   # 4 slices
+    (1, 1, 3, 2048, 4096, torch.float32, True),     # the widest value dimension
+    (2, 4, 17, 512, 1024, torch.float32, False),
+]
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv,dtype,state", ROWS_CASES)
+def test_wide_heads_row_parallel(B, H, T, dk, dv, dtype, state):
+    """Every output against the oracle; against the column-parallel kernel
+    (no workspace) the final state is the same bits (the same update, in the
+    same order, per entry) and y differs only in the order of its sum."""
+    pm = _pm()
+    assert pm.workspace_size(B, T, H, dk, dv) > 0
+    w = workloads.WORKLOADS[0].with_(B=B, H=H, dk=dk, dv=dv, dtype=dtype, A_mode="logspace16")
+    _announce("wide head row-parallel fwd", B=B, H=H, T=T, dk=dk, dv=dv, dtype=dtype, state=state)
+    inp = workloads.make_inputs(w, T=T, seed=3 * dk + dv + T)
+    if state:
+        inp["mu0"], inp["I0"] = workloads.random_state(B, H, dv, dk, inp["I_prior"], seed=dk + 1)
+    y, muT, IT = _run_fwd(inp)
+    _compare_full(inp, y, muT, IT, tol_for(dtype))
+    g = to_device(inp, DEV)
+    none = torch.empty(0, dtype=torch.uint8, device=DEV)
+    y_c, mu_c, I_c = pm.fwd_chunked(*gpu_args(g), mu0=g.get("mu0"), I0=g.get("I0"), workspace=none,
+                                    out_dtype=torch.float32)
+    y_r, _, _ = pm.fwd_chunked(*gpu_args(g), mu0=g.get("mu0"), I0=g.get("I0"), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(mu_c, muT) and torch.equal(I_c, IT)
+    assert rel_err(y_r, y_c) <= 1e-5
+
+
+def test_wide_heads_row_parallel_resume_in_place():
+    """muT/IT aliasing mu0/I0: each lane reads its entries before the first
+    token and writes the same entries after the last, so in place equals out
+    of place bit for bit."""
+    B, H, T, dk, dv = 1, 2, 13, 2048, 2048
+    w = workloads.WORKLOADS[0].with_(B=B, H=H, dk=dk, dv=dv, dtype=torch.bfloat16, A_mode="logspace16")
+    _announce("wide head row-parallel in-place resume", B=B, H=H, T=T, dk=dk, dv=dv)
+    inp = workloads.make_inputs(w, T=T, seed=91)
+    inp["mu0"], inp["I0"] = workloads.random_state(B, H, dv, dk, inp["I_prior"], seed=92)
+    g = to_device(inp, DEV)
+    pm = _pm()
+    y1, mu1, I1 = pm.fwd_chunked(*gpu_args(g), mu0=g["mu0"], I0=g["I0"])
+    mu, I = g["mu0"].clone(), g["I0"].clone()
+    y2, mu2, I2 = pm.fwd_chunked(*gpu_args(g), mu0=mu, I0=I, muT=mu, IT=I)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(mu1, mu2) and torch.equal(I1, I2)
+    assert mu2.data_ptr() == mu.data_ptr()
+
+
+@pytest.mark.parametrize("D", [512, 2048])
+def test_recurrent_shape_full_size_sampled_rows(D):
+    """The recurrent-kernel shape the bench times (B=16, T=2048, H=1,
+    d_k = d_v = D, bf16), through the same launch; the oracle runs on sampled
+    value rows of sampled sequences (rows are independent: row i's state and
+    y_i depend only on beta_i, v_i and the shared k, q, dt), every key column."""
+    w = workloads.WORKLOADS[2].with_(B=16, T=2048, H=1, dk=D, dv=D)
+    _announce("recurrent shape full size, sampled rows", B=16, T=2048, H=1, D=D)
+    inp = workloads.make_inputs(w, seed=70 + D // 512)
+    assert _pm().workspace_size(w.B, w.T, w.H, D, D) > 0
+    y, muT, IT = _run_fwd(inp)
+    bs = [0, 7, 15]
+    rows = [0, 1, 63, 64, 255, 256, D // 2 + 5, D - 1]
+    sub = {n: (x[bs] if n in ("q", "k", "dt") else x) for n, x in inp.items()}
+    sub["v"] = inp["v"][bs][..., rows]
+    sub["beta"] = inp["beta"][bs][..., rows]
+    y_ref, mu_ref, I_ref = oracle.fwd(**sub, nthreads=len(bs))
+    assert_close("y (sampled rows)", to_np(y)[bs][..., rows], y_ref, TOL_BF16)
+    assert_close("muT (sampled rows)", to_np(muT)[bs][:, :, rows, :], mu_ref, TOL_F32)
+    assert_close("IT (sampled rows)", to_np(IT)[bs][:, :, rows, :], I_ref, TOL_F32)
+
+
 def test_wide_head_256_time_split_matches_single_pass():
     w = workloads.WORKLOADS[0].with_(B=1, H=1, dk=256, dv=64, A_mode="logspace16")
     _announce("dk=256 time split", T=700, dk=256, dv=64)
