@@ -4991,10 +4991,16 @@ int device_cus() {
 
 // Time segments of the forward.  With few (head, row block) workgroups the
 // GPU is under-filled, so the sequence is cut into segments that run side by
-// side (a summary pass, then a replay pass).  Auto: aim at three workgroups
-// per CU when fewer than two would run, at most 8 segments and at least 256
-// tokens per segment.  Segment lengths are multiples of 64 tokens, so the
-// chunk choice never moves a segment boundary.
+// side (a summary pass, then a replay pass).  Auto, when fewer than two
+// workgroups per CU would run: R segments fill the GPU once at three
+// workgroups per CU; take the largest multiple of R up to 12 (R itself when
+// R > 12), so that the replay runs as whole rounds of workgroups, and a few
+// of them where R is small (several rounds even out the CUs' pace: on the
+// 32-head, 32k-token layer 12 segments take 4.33 ms where 3, one round,
+// take 4.60).  At most 32 segments, at least 256 tokens each, and a
+// workspace that fits the no-allocation entry's scratch.  Segment lengths
+// are multiples of 64 tokens, so the chunk choice never moves a segment
+// boundary.
 struct SegPlan {
     int nseg, seg_len;
     size_t ws_bytes;
@@ -5005,9 +5011,14 @@ SegPlan plan_segments(int B, int T, int H, int dk, int dv, int segments, int cus
     if (T > 0 && segments >= 2) {
         S = segments;
     } else if (T > 0 && segments == 0 && nwg_seg < 2LL * cus) {
-        S = (3LL * cus) / nwg_seg;
-        S = S > 8 ? 8 : S;
-        S = S > T / 256 ? T / 256 : S;
+        const long long R = (3LL * cus) / nwg_seg;
+        S = R >= 12 ? R : R * (12 / R);
+        if (S > 32) S = 32;
+        if (S > T / 256) S = T / 256;
+        // floats per segment, an upper bound of the workspace's share
+        const long long per = 2LL * B * H * dv * dk + (long long)B * H;
+        const long long cap = (long long)(kNoAllocScratchBytes / sizeof(float)) / per;
+        if (S > cap) S = cap;
     }
     const long long units = (T + 63) / 64;
     if (S > units) S = units;

@@ -136,9 +136,11 @@ typedef enum {
  *             form of the natural-parameter scans, slides frame "Natural
  *             parameters expose two affine scans"), then a replay pass starts
  *             every segment from the composition of the earlier maps and reads
- *             out.  0: the library decides (it splits only when B*H*dv/16
- *             workgroups would leave the GPU under-filled).  Results of a split
- *             match the single pass up to float32 rounding.
+ *             out.  0: the library decides (it splits only when the B*H*dv/16
+ *             workgroups would be fewer than two per CU, into whole rounds of
+ *             three workgroups per CU, up to 32 segments of at least 256
+ *             tokens, within the no-allocation scratch size).  Results of a
+ *             split match the single pass up to float32 rounding.
  *   workspace, workspace_bytes
  *             device scratch for the segment summaries and a copy of the
  *             start state (so that an in-place resume stays correct under a
@@ -199,7 +201,7 @@ palimpsa_status palimpsa_fwd_chunked(const void *q, const void *k, const void *v
  * A call whose split (the library's own choice with segments == 0, or the
  * one asked for) would need more scratch than that returns
  * PALIMPSA_ERR_SCRATCH_LIMIT and launches nothing; every split the library
- * chooses by itself on MI355X fits (at most about 38 MB, at dk = 256).
+ * chooses by itself fits (its choice is capped to this size).
  * Heads of dk >= 512 run the column-parallel kernel here (the row-parallel
  * form's workspace is gigabytes): results as palimpsa_fwd_chunked without a
  * workspace.

@@ -107,11 +107,22 @@ def test_workspace_size_host_logic(lib):
     import bayesian_metaplastic_memory_amd as pm
     # 760M layer (768 workgroups): no split
     assert pm.workspace_size(8, 4096, 12, 128, 128, 0) == 0
-    # long context, 32 heads (256 workgroups): 3 segments -> 2 summaries (M_loc,
+    # long context, 32 heads (256 workgroups; 3 segments fill 256 CUs at three
+    # workgroups each): 4 rounds = 12 segments -> 11 summaries (M_loc,
     # Ibar_loc, decay product) plus one copy of the start state (mu0, I0)
     def split_bytes(nseg, bh, dv, dk):
         return ((nseg - 1) * (2 * bh * dv * dk + bh) + 2 * bh * dv * dk) * 4
-    assert pm.workspace_size(1, 32768, 32, 128, 128, 0) == split_bytes(3, 32, 128, 128)
+    assert pm.workspace_size(1, 32768, 32, 128, 128, 0) == split_bytes(12, 32, 128, 128)
+    # MQAR layer (128 workgroups, 6 per round -> 12): at least 256 tokens per segment -> 8
+    assert pm.workspace_size(4, 2048, 8, 64, 64, 0) == split_bytes(8, 32, 64, 64)
+    # 96 workgroups: one round of 8 segments
+    assert pm.workspace_size(1, 4096, 12, 128, 128, 0) == split_bytes(8, 12, 128, 128)
+    # 32 workgroups: one round of 24 segments
+    assert pm.workspace_size(1, 65536, 8, 64, 64, 0) == split_bytes(24, 8, 64, 64)
+    # the choice is capped to the no-allocation scratch (64 MiB): 8 MiB per
+    # segment here, so 7 segments rather than 12
+    assert pm.workspace_size(1, 32768, 4, 256, 1024, 0) == split_bytes(7, 4, 1024, 256)
+    assert split_bytes(7, 4, 1024, 256) <= pm.noalloc_scratch_bytes() < split_bytes(8, 4, 1024, 256)
     # explicit requests; rounding to 64-token segments caps the count
     assert pm.workspace_size(1, 1000, 2, 64, 64, 4) == split_bytes(4, 2, 64, 64)
     assert pm.workspace_size(1, 100, 2, 64, 64, 8) == split_bytes(2, 2, 64, 64)
