@@ -4209,6 +4209,17 @@ __global__ __launch_bounds__(256) void fzb_state_kernel(FzbArgs a) {
     // two 16-byte words, (v, beta) for the state or gy (bf16: one word, fp32: two)
     u32x4 pk0[NQ], px0[2][2], pk1[NQ], px1[2][2];
     uint32_t pd0 = 0, pd1 = 0;                            // dt bits of the lane's token
+    // Every prefetch is one unconditional load from an address chosen by
+    // pointer selects: a load under a branch, or a select between a loaded
+    // value and a constant, makes the compiler wait for it at once (to copy
+    // it into the merged register), which would undo the two-chunk lead.
+    // Packets that the commit does not use (beta absent, bf16 gy) repeat the
+    // first one.
+    const char *kq_base = adj ? (const char *)a.q : (const char *)a.k;
+    const char *x0_base = adj ? (const char *)a.gy : (const char *)a.v;
+    const size_t x0_esz = adj ? sizeof(TG) : sizeof(bf16_t);
+    const char *x1_base = adj ? (kGP == 2 ? x0_base + 4 * sizeof(TG) : x0_base)
+                              : (a.beta ? (const char *)a.beta : x0_base);
     auto load = [&](int c, u32x4 (&pk)[NQ], u32x4 (&px)[2][2], uint32_t &pd) __attribute__((always_inline)) {
         const int t0 = c * kFbC;
         pd = fzb_dt_bits(a, seq, t0, lane);
@@ -4216,19 +4227,14 @@ __global__ __launch_bounds__(256) void fzb_state_kernel(FzbArgs a) {
         for (int n = 0; n < NQ; ++n) {
             const int p = tid + 256 * n, t = p / (DK / 8), col = 8 * (p % (DK / 8));
             const size_t o = (seq + (size_t)min(t0 + t, tl) * a.H) * DK + col;
-            pk[n] = *(const u32x4 *)((adj ? a.q : a.k) + o);
+            pk[n] = *(const u32x4 *)(kq_base + o * sizeof(bf16_t));
         }
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             const int p = tid + 256 * n, t = p / 8, col = 8 * (p % 8);
             const size_t o = (seq + (size_t)min(t0 + t, tl) * a.H) * DV + i0 + col;
-            if (adj) {
-                px[n][0] = *(const u32x4 *)((const TG *)a.gy + o);
-                px[n][1] = kGP == 2 ? *(const u32x4 *)((const TG *)a.gy + o + 4) : z;
-            } else {
-                px[n][0] = *(const u32x4 *)(a.v + o);
-                px[n][1] = a.beta ? *(const u32x4 *)(a.beta + o) : z;
-            }
+            px[n][0] = *(const u32x4 *)(x0_base + o * x0_esz);
+            px[n][1] = *(const u32x4 *)(x1_base + o * x0_esz);
         }
     };
     auto commit = [&](int c, float Lt, float Lam, const u32x4 (&pk)[NQ], const u32x4 (&px)[2][2])
