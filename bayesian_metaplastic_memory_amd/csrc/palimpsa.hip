@@ -4040,6 +4040,13 @@ __device__ inline f32x4 mfma16(bf16x8_t a, bf16x8_t b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ inline uint2 pack4_bf16(f32x4 x) { return make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])); }
+// Fragment-major layout of a [DK][DV] boundary matrix (S_0^T, G_E^T): the A
+// operand of rows 16 jb and columns 32 f (lane l: row 16 jb + l % 16, columns
+// 32 f + 8 (l / 16) .. + 7) is 64 lanes x 16 bytes, contiguous, so that the
+// state walk's stores and the gradient kernel's loads are whole 512-byte runs.
+__device__ inline size_t fragidx(int dv, int jb, int f, int lane) {
+    return ((size_t)(jb * (dv / 32) + f) * 64 + lane) * 8;
+}
 
 // Widen 8 consecutive values of T at p (16-byte aligned for bf16, 32 for float).
 template <typename T> __device__ inline void load8(const T *p, float *o);
@@ -4287,13 +4294,21 @@ __global__ __launch_bounds__(256) void fzb_state_kernel(FzbArgs a) {
         commit(c, Lt, Lam, pk, px);
         __syncthreads();
         if (n + 2 < nc) load(adj ? c - 2 : c + 2, pk, px, pd);   // two chunks ahead
-        // the boundary matrix of chunk c, before this chunk's update: S_0(c)^T or G_E(c)^T
+        // the boundary matrix of chunk c, before this chunk's update: S_0(c)^T or
+        // G_E(c)^T, fragment-major.  Lane (g, m) holds rows 4 g .. 4 g + 3 (of the
+        // wave's 16) of key columns 16 jb + m; a swap with lane (g ^ 1, m) over
+        // two key blocks leaves 8 consecutive rows of one key column in each
+        // lane: block jb in the even-g lane, jb + 1 in the odd one.
         {
             bf16_t *dst = (adj ? a.gT : a.sT) + cb * DK * DV;
-            const int i = i0 + 16 * w + 4 * g;
+            const int f = i0 / 32 + (w >> 1), fl = 16 * (2 * (w & 1) + (g >> 1)) + m;
 #pragma unroll
-            for (int jb = 0; jb < DK / 16; ++jb)
-                *(uint2 *)(dst + (size_t)(16 * jb + m) * DV + i) = pack4_bf16(S[jb]);
+            for (int jb = 0; jb < DK / 16; jb += 2) {
+                const uint2 p0 = pack4_bf16(S[jb]), p1 = pack4_bf16(S[jb + 1]);
+                const auto x = __builtin_amdgcn_permlane16_swap(p0.x, p1.x, false, false);
+                const auto y = __builtin_amdgcn_permlane16_swap(p0.y, p1.y, false, false);
+                *(uint4 *)(dst + fragidx(DV, jb + (g & 1), f, fl)) = make_uint4(x[0], y[0], x[1], y[1]);
+            }
             if (adj) {
                 // G_E(c) row-major: through LDS, rows of the workgroup's 64
 #pragma unroll
@@ -4375,7 +4390,8 @@ __global__ __launch_bounds__(256, 2) void fzb_grad_kernel(FzbArgs a) {
             const int x = n - NI;
             const bf16_t *base = (x & 1) ? gtp : s0t;
 #pragma unroll
-            for (int f = 0; f < DV / 32; ++f) dst[f] = rowfrag(base, DV, 16 * (w + 4 * (x >> 1)), 32 * f, lane);
+            for (int f = 0; f < DV / 32; ++f)
+                dst[f] = *(const bf16x8_t *)(base + fragidx(DV, w + 4 * (x >> 1), f, lane));
         }
     };
     bf16x8_t fr[2][NF];
