@@ -4293,7 +4293,6 @@ __global__ __launch_bounds__(256) void fzb_state_kernel(FzbArgs a) {
         __syncthreads();                                  // the previous chunk's reads of LDS are done
         commit(c, Lt, Lam, pk, px);
         __syncthreads();
-        if (n + 2 < nc) load(adj ? c - 2 : c + 2, pk, px, pd);   // two chunks ahead
         // the boundary matrix of chunk c, before this chunk's update: S_0(c)^T or
         // G_E(c)^T, fragment-major.  Lane (g, m) holds rows 4 g .. 4 g + 3 (of the
         // wave's 16) of key columns 16 jb + m; a swap with lane (g ^ 1, m) over
@@ -4328,6 +4327,10 @@ __global__ __launch_bounds__(256) void fzb_state_kernel(FzbArgs a) {
             x = mfma16(a0, lds_trfrag(hb + L::kK, L::kRK, 0, 16 * jb, lane), x);
             S[jb] = mfma16(a1, lds_trfrag(hb + L::kK, L::kRK, 32, 16 * jb, lane), x);
         }
+        // the loads two chunks ahead, issued after the boundary stores and the
+        // products: right after the barrier every wave of the CU would queue
+        // its loads and stores at once and wait for the address units
+        if (n + 2 < nc) load(adj ? c - 2 : c + 2, pk, px, pd);
         if (adj) {
             __syncthreads();
             bf16_t *gep = a.ge + cb * DV * DK;
