@@ -567,6 +567,12 @@ def main():
                              avg_launch_ms=avg_launch_s * 1e3,
                              per_update="4 FMA + 2 MUL (10 flops) + 1 v_rcp_f32"),
     }
+    t_start = time.time()
+
+    def progress(name):
+        print("[bench] %s done, %.1f s" % (name, time.time() - t_start), file=sys.stderr, flush=True)
+
+    progress("forward")
     want = set(EXTRAS) if not args.only else set(args.only.split(","))
     if args.no_extras:
         want = set()
@@ -574,35 +580,48 @@ def main():
         want.discard("decode")
     if "decode" in want:
         out["decode"] = decode_extra(torch, pm, workloads, max(64, args.steps))
+        progress("decode")
     if w.dtype == torch.bfloat16:
         few = max(5, args.steps // 5)
         if "backward" in want:
             out["backward"] = backward_extra(torch, pm, workloads, w, g, few)
+            progress("backward")
         if "training_step" in want:
             out["training_step"] = training_extra(torch, pm, workloads, w, g, few)
+            progress("training_step")
         if "frozen" in want:
             out["frozen"] = frozen_extra(torch, pm, w, g, max(20, args.steps))
+            progress("frozen")
         if "frozen_backward" in want:
             out["frozen_backward"] = frozen_backward_extra(torch, pm, workloads, w, g, few)
+            progress("frozen_backward")
         if "blockdiag" in want:
             out["blockdiag"] = blockdiag_extra(torch, pm, w, g, max(20, args.steps // 2))
+            progress("blockdiag")
         if "blockdiag_decode" in want:
             out["blockdiag_decode"] = blockdiag_decode_extra(torch, pm, workloads, max(64, args.steps))
+            progress("blockdiag_decode")
         if "blockdiag4" in want:
             out["blockdiag4"] = blockdiag_extra(torch, pm, w, g, max(10, args.steps // 5), block=4)
+            progress("blockdiag4")
         if "blockdiag_backward" in want:
             out["blockdiag_backward"] = blockdiag_backward_extra(torch, pm, workloads, w, g, few)
+            progress("blockdiag_backward")
         if "blockdiag4_backward" in want:
             out["blockdiag4_backward"] = blockdiag_backward_extra(torch, pm, workloads, w, g, few, block=4)
+            progress("blockdiag4_backward")
         if "recurrent_shape" in want:
             out["recurrent_shape"] = [fig7_extra(torch, pm, workloads, dev, D, 5) for D in (512, 2048)]
+            progress("recurrent_shape")
     if "configs" in want:
         del g
         torch.cuda.empty_cache()
         out["configs"] = {str(key): forward_config_extra(torch, pm, workloads, key, max(10, args.steps // 2))
                           for key in (1, 4, "4b") if str(key) != args.workload}
+        progress("configs")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads or w.B * w.H)
+        progress("cpu_baseline")
     print(json.dumps(out), flush=True)
 
 
