@@ -480,6 +480,8 @@ def fig7_extra(torch, pm, workloads, dev, D, steps):
     return {"workload": w.name, "tokens_per_s": w.B * w.T / avg_s, "ms_per_launch": avg_s * 1e3,
             "state_updates_per_s": updates / avg_s, "workspace_bytes": nws,
             "roofline": roofline("alu", avg_s, flops=updates * FWD["flops"], nbytes=fwd_bytes(w, 2, 2), mix=FWD,
+                                 traffic=load_traffic("wide_rows_recurrent_shape_D2048_bf16_traffic.json")
+                                 if D == 2048 else None,
                                  kernel="wide_prep_kernel<bf16> + wide_rows_kernel<%d, bf16> + wide_sum_kernel<bf16>"
                                         % kcl, scope="whole call")}
 
@@ -528,6 +530,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_each_way": 4 * n, "launches": 3}))
         return
+    t_start = time.time()
     w = workloads.WORKLOADS[int(args.workload) if args.workload.isdigit() else args.workload]
     inp = workloads.make_inputs(w)
     g = {n: (x.to(dev) if isinstance(x, torch.Tensor) else x) for n, x in inp.items()}
@@ -567,8 +570,6 @@ def main():
                              avg_launch_ms=avg_launch_s * 1e3,
                              per_update="4 FMA + 2 MUL (10 flops) + 1 v_rcp_f32"),
     }
-    t_start = time.time()
-
     def progress(name):
         print("[bench] %s done, %.1f s" % (name, time.time() - t_start), file=sys.stderr, flush=True)
 
