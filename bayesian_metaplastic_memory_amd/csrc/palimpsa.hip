@@ -3266,34 +3266,52 @@ struct WideRowsArgs {
 };
 
 // One column-group record per thread: k^2, the raw k and q words, the gate.
+// The records are built in LDS and leave as whole 16-byte columns of the
+// workgroup's block (256 records, contiguous in the output): written record
+// by record, each store instruction would cover 64 separate 16-byte pieces
+// 144 bytes apart, and the partial lines cost about three times the bytes.
 template <typename TIn>
 __global__ __launch_bounds__(256) void wide_prep_kernel(const TIn *q, const TIn *k, const TIn *dt, const float *A,
                                                         const float *Ip, uint32_t *rec, size_t ntok, int H, int D) {
     using CG = ColGroup<TIn>;
-    constexpr int G = CG::kCols, W = CG::kWords;
+    constexpr int G = CG::kCols, W = CG::kWords, W4 = W / 4;
+    static_assert(W % 4 == 0, "records are whole 16-byte packets");
     constexpr int kWordsKQ = G * (int)sizeof(TIn) / 4;   // words of k (and of q) in a group
+    __shared__ uint4 blk[256 * W4];
     const int per_tok = D / G;
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    const size_t tok = i / per_tok;
-    if (tok >= ntok) return;
-    const int c = (int)(i % per_tok) * G;
-    uint32_t *r = rec + i * W;
-    const uint4 *kp = (const uint4 *)(k + tok * D + c), *qp = (const uint4 *)(q + tok * D + c);
+    const size_t i0 = (size_t)blockIdx.x * 256;
+    const size_t nrec = ntok * per_tok;
+    const size_t i = i0 + threadIdx.x;
+    if (i < nrec) {
+        const size_t tok = i / per_tok;
+        const int c = (int)(i % per_tok) * G;
+        uint4 *r = blk + threadIdx.x * W4;
+        const uint4 *kp = (const uint4 *)(k + tok * D + c), *qp = (const uint4 *)(q + tok * D + c);
 #pragma unroll
-    for (int p = 0; p < kWordsKQ / 4; ++p) {
-        const uint4 kw = kp[p];
-        float x[packet<TIn>::kN];
-        packet<TIn>::widen(kw, x);
+        for (int p = 0; p < kWordsKQ / 4; ++p) {
+            const uint4 kw = kp[p];
+            float x[packet<TIn>::kN];
+            packet<TIn>::widen(kw, x);
 #pragma unroll
-        for (int e = 0; e < packet<TIn>::kN; e += 4)
-            *(float4 *)(r + p * packet<TIn>::kN + e) = make_float4(x[e] * x[e], x[e + 1] * x[e + 1],
-                                                                   x[e + 2] * x[e + 2], x[e + 3] * x[e + 3]);
-        *(uint4 *)(r + G + 4 * p) = kw;
-        *(uint4 *)(r + G + kWordsKQ + 4 * p) = qp[p];
+            for (int e = 0; e < packet<TIn>::kN; e += 4)
+                r[(p * packet<TIn>::kN + e) / 4] = make_uint4(__float_as_uint(x[e] * x[e]), __float_as_uint(x[e + 1] * x[e + 1]),
+                                                              __float_as_uint(x[e + 2] * x[e + 2]),
+                                                              __float_as_uint(x[e + 3] * x[e + 3]));
+            r[G / 4 + p] = kw;
+            r[(G + kWordsKQ) / 4 + p] = qp[p];
+        }
+        const int h = (int)(tok % H);
+        const float2 gt = gate(A[h], io<TIn>::to_f32(dt[tok]), Ip[h]);
+        r[(G + 2 * kWordsKQ) / 4] = make_uint4(__float_as_uint(gt.x), __float_as_uint(gt.y), 0u, 0u);
     }
-    const int h = (int)(tok % H);
-    const float2 gt = gate(A[h], io<TIn>::to_f32(dt[tok]), Ip[h]);
-    *(uint4 *)(r + G + 2 * kWordsKQ) = make_uint4(__float_as_uint(gt.x), __float_as_uint(gt.y), 0u, 0u);
+    __syncthreads();
+    const size_t valid = (nrec - i0 < 256 ? nrec - i0 : 256) * W4;   // packets of this block's records
+    uint4 *out = (uint4 *)rec + i0 * W4;
+#pragma unroll
+    for (int n = 0; n < W4; ++n) {
+        const int pkt = threadIdx.x + 256 * n;
+        if ((size_t)pkt < valid) out[pkt] = blk[pkt];
+    }
 }
 
 template <int KCL, typename TIn>
