@@ -1553,6 +1553,8 @@ ROWS_CASES = [
     (1, 2, 11, 2048, 2048, torch.bfloat16, True),   # 4 slices
     (1, 1, 3, 2048, 4096, torch.float32, True),     # the widest value dimension
     (2, 4, 17, 512, 1024, torch.float32, False),
+    (4, 1, 1, 512, 2048, torch.bfloat16, True),     # one token: a single, partial reduction block
+    (5, 13, 5, 2048, 64, torch.float32, True),      # one row block per head; 260 workgroups (no XCD remap)
 ]
 
 
