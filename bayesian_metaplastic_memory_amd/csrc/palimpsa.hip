@@ -1578,10 +1578,22 @@ template <int DK>
 __global__ __launch_bounds__(256) void bwd_qk_kernel(const float *pqk, float *gq, float *gk, size_t bth, int nrb) {
     const size_t n4 = (size_t)blockIdx.x * 256 + threadIdx.x;          // float4 index
     if (n4 >= bth * (2 * DK / 4)) return;
+    // the row blocks' partials in order, 8 loads in flight at a time (a
+    // rolled loop waited for each load before issuing the next); blocks
+    // past nrb reload the last one and are not added
+    constexpr int kU = 8;
+    const size_t rs = bth * 2 * DK;
     float4 acc = *(const float4 *)(pqk + 4 * n4);
-    for (int r = 1; r < nrb; ++r) {
-        const float4 x = *(const float4 *)(pqk + (size_t)r * bth * 2 * DK + 4 * n4);
-        acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+    for (int r0 = 1; r0 < nrb; r0 += kU) {
+        float4 x[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int r = r0 + u < nrb ? r0 + u : nrb - 1;
+            x[u] = *(const float4 *)(pqk + (size_t)r * rs + 4 * n4);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            if (r0 + u < nrb) { acc.x += x[u].x; acc.y += x[u].y; acc.z += x[u].z; acc.w += x[u].w; }
     }
     const size_t tok = (4 * n4) / (2 * DK);
     const int c = (int)((4 * n4) % (2 * DK));
@@ -1604,11 +1616,18 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const float *ps, const vo
     float accA = 0.f, accI = 0.f;
     for (int t = threadIdx.x; t < T; t += 256) {
         const size_t row = ((size_t)b * T + t) * H + h;
+        // the row blocks' partials in order, 8 loads in flight at a time
         float da = 0.f, dc = 0.f;
-        for (int r = 0; r < nrb; ++r) {
-            const float2 x = *(const float2 *)(ps + ((size_t)r * bth + (size_t)bh * T + t) * 2);
-            da += x.x;
-            dc += x.y;
+        for (int r0 = 0; r0 < nrb; r0 += 8) {
+            float2 x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int r = r0 + u < nrb ? r0 + u : nrb - 1;
+                x[u] = *(const float2 *)(ps + ((size_t)r * bth + (size_t)bh * T + t) * 2);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (r0 + u < nrb) { da += x[u].x; dc += x[u].y; }
         }
         const float d = dt_bf16 ? (float)((const bf16_t *)dt)[row] : ((const float *)dt)[row];
         const float x = -Ah * d;
@@ -3441,11 +3460,15 @@ template <typename TOut>
 __global__ __launch_bounds__(256) void wide_sum_kernel(const float *part, TOut *y, size_t n, int nq) {
     const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= n) return;
-    float4 s = *(const float4 *)(part + i);
-    for (int q = 1; q < nq; ++q) {
-        const float4 x = *(const float4 *)(part + (size_t)q * n + i);
-        s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
-    }
+    // all slices' loads in flight before the in-order sum (nq <= 4; slices past
+    // nq reload the last one and are not added)
+    float4 x[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q] = *(const float4 *)(part + (size_t)(q < nq ? q : nq - 1) * n + i);
+    float4 s = x[0];
+#pragma unroll
+    for (int q = 1; q < 4; ++q)
+        if (q < nq) { s.x += x[q].x; s.y += x[q].y; s.z += x[q].z; s.w += x[q].w; }
     y[i] = io<TOut>::from_f32(s.x);
     y[i + 1] = io<TOut>::from_f32(s.y);
     y[i + 2] = io<TOut>::from_f32(s.z);
@@ -4928,6 +4951,7 @@ bool plan_wide_rows(int B, int T, int H, int dk, int dv, int cus, WideRowsPlan *
     if (dk < 512 || T <= 0 || dv % 64 != 0) return false;
     p->kcl = dk >= 1024 ? 32 : 16;
     p->nq = dk / (p->kcl * kWrNW);
+    if (p->nq > 4) return false;   // wide_sum_kernel adds at most 4 slices
     p->nwg = (long long)B * H * (dv / 64) * p->nq;
     if (p->nwg < cus || p->nwg > 0x7fffffffLL) return false;
     const size_t ntok = (size_t)B * T * H;
