@@ -293,12 +293,15 @@ def training_extra(torch, pm, workloads, w, g, steps):
     s_s, f_s, r_s = mean_s(per_s), mean_s(per_f), mean_s(per_r)
     ck_bytes = w.B * w.H * ((w.T + 7) // 8) * 2 * w.dv * w.dk * 4
     updates = w.B * w.H * w.T * w.dv * w.dk
+    esz = 2 if w.dtype == torch.bfloat16 else 4
     return {"workload": w.name + ", training step (forward with y and final state, then the full backward)",
             "tokens_per_s": w.B * w.T / f_s, "ms_per_step": f_s * 1e3,
             "recompute_ms_per_step": r_s * 1e3,
             "roofline": roofline("alu", f_s, flops=updates * (FWD["flops"] + BWD["flops"]),
+                                 nbytes=fwd_bytes(w, esz, esz) + grad_bytes(w, esz),
                                  mix=dict(valu=FWD["valu"] + BWD["valu"], flops=FWD["flops"] + BWD["flops"]),
-                                 scope="whole step (checkpointing forward + backward)"),
+                                 scope="whole step (checkpointing forward + backward); algorithmic bytes of the "
+                                       "forward and of the backward's inputs and gradients"),
             "checkpointing_forward": {
                 "ms_per_launch": s_s * 1e3, "checkpoint_GB": ck_bytes / 1e9,
                 "checkpoint_write_GBs": ck_bytes / s_s / 1e9,
