@@ -3206,9 +3206,11 @@ __global__ __launch_bounds__(kThreads) void wide_fwd_kernel(FwdArgs a) {
 // columns (a column slice).  The waves' partial readouts meet in LDS every
 // 8 or 16 tokens and are added in wave order; the NQ slices of a row block
 // leave their sums in a workspace, and a last pass adds them in slice order
-// and rounds to the output type.  A first pass writes k^2 (float32) and the
-// gates (alpha, c) once per token, so the scalar operands need no ALU work
-// beyond widening bf16 (two SALU bit operations per pair of columns).
+// and rounds to the output type.  A first pass lays each token's columns out
+// as records (k^2 in float32, the raw k and q words, the gate (alpha, c)), so
+// the scalar operands need no ALU work beyond widening bf16 (two SALU bit
+// operations per pair of columns) and a group of columns arrives with four
+// scalar loads off one address.
 //
 // The loop-carried FMAs are written so that the new I and M land in the
 // registers of the old ones (in_place_fma): left to itself the register
