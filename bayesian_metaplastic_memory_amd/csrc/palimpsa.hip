@@ -146,8 +146,7 @@ struct FwdArgs {
     int nseg;          // time segments (1: no split)
     float *ws;         // segment summaries, see SegWs
     float *ck;         // backward checkpoints (kCheckpoint mode, training forward), see bwd_kernel
-    float *ck_sink;    // training forward: one block's worth of discarded stores
-    int nsb;           // checkpoints per sequence: ceil(T / kSB)
+    int nck;           // checkpoints per sequence: ceil(T / kCkI)
     int vstar;         // 1: v holds beta . v (the write itself)
     int frozen;        // checkpoint pass of the frozen-importance backward: M_0 = I_prior mu0
 };
@@ -178,7 +177,8 @@ constexpr int kRowsPerWave = 4;
 constexpr int kRowsPerWG = kRowsPerWave * kWaves;   // 16 value rows per workgroup
 constexpr int kLanesPerRow = 16;
 constexpr int kGroup = 16;                // tokens per transposing reduction (= lanes per row)
-constexpr int kSB = 8;                    // tokens between backward checkpoints
+constexpr int kSB = 8;                    // tokens per backward sub-block (staging and reverse walk)
+constexpr int kCkI = 2 * kSB;             // tokens between checkpoints of the diagonal backward
 
 // LDS floats per staged token: k, k^2, q columns + (beta, beta*v) per row + gate.
 template <int DK> struct Stage {
@@ -392,6 +392,36 @@ __device__ inline void load_pair(const float *blk, int tid, float *M, float *I) 
     for (int i = 0; i < N; ++i) { M[i] = v[i]; I[i] = v[N + i]; }
 }
 
+// Marks N values as used at this point (see BwdStager::ready).
+template <int N>
+__device__ inline void regs_ready(const float *x) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" ::"v"(x[i]));
+}
+
+// The same layout in LDS (a thread's private slots; every access instruction
+// covers 1 KiB of consecutive banks).
+template <int N>
+__device__ inline void lds_store_pair(float *blk, int tid, const float *M, const float *I) {
+    float v[2 * N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) { v[i] = M[i]; v[N + i] = I[i]; }
+#pragma unroll
+    for (int i = 0; i < 2 * N; i += 4)
+        *(float4 *)(blk + 4 * ((i / 4) * kThreads + tid)) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+}
+template <int N>
+__device__ inline void lds_load_pair(const float *blk, int tid, float *M, float *I) {
+    float v[2 * N];
+#pragma unroll
+    for (int i = 0; i < 2 * N; i += 4) {
+        const float4 x = *(const float4 *)(blk + 4 * ((i / 4) * kThreads + tid));
+        v[i] = x.x; v[i + 1] = x.y; v[i + 2] = x.z; v[i + 3] = x.w;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) { M[i] = v[i]; I[i] = v[N + i]; }
+}
+
 // The per-token hot loop over one staged chunk.  Per token and lane: for each
 // of the lane's DK/16 state entries 6 VALU ops and one v_rcp_f32; the lane's
 // partial of y_t goes to a register.  Every 16 tokens one transposing
@@ -401,18 +431,16 @@ __device__ inline void load_pair(const float *blk, int tid, float *M, float *I) 
 // With a prior per state entry (IPE) the gate's c is staged as 1 - alpha and
 // scaled by the lane's prior ipe[s]: one more VALU op per entry and token.
 //
-// With CKPT (the training forward, C = 16) the states before the chunk's
-// tokens 0 and kSB are also stored, as the backward's checkpoint pass would
-// store them, at the blocks ck_a and ck_b.  The caller points ck_b at a sink
-// when the sequence ends within the chunk's first kSB tokens: a data-dependent
-// branch or select in here costs the loop twice its registers.
+// With CKPT (the training forward, C = kCkI = 16) the state before the
+// chunk's first token is also stored at the block ck, as the backward's
+// checkpoint pass would store it.
 template <int DK, int C, typename TOut, bool IPE, bool CKPT>
 __device__ inline void compute_chunk(const float *buf, int left, float *M, float *I,
                                      int row_local, int g, TOut *yrow, size_t ystride, const float *ipe,
-                                     float *ck_a = nullptr, float *ck_b = nullptr) {
+                                     float *ck = nullptr) {
     using LT = LaneTile<DK>;
     static_assert(C % kGroup == 0, "chunk must be a multiple of 16 tokens");
-    static_assert(!CKPT || (C == 16 && kGroup == 2 * kSB), "checkpointing forward runs chunk 16");
+    static_assert(!CKPT || (C == kCkI && kGroup == kCkI), "checkpointing forward runs chunk 16");
     const float *cbase = buf + LT::col(g, 0, 0);
     const float *rbase = buf + C * Stage<DK>::kColFloats + 2 * row_local;
     // The gate address is the same in every lane; holding it in a VGPR (the
@@ -429,8 +457,7 @@ __device__ inline void compute_chunk(const float *buf, int left, float *M, float
         float part[kGroup];
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) {
-            if (CKPT && u == 0) store_pair<LT::kCols>(ck_a, threadIdx.x, M, I);
-            if (CKPT && u == kSB) store_pair<LT::kCols>(ck_b, threadIdx.x, M, I);
+            if (CKPT && u == 0) store_pair<LT::kCols>(ck, threadIdx.x, M, I);
             const float2 gc = *(const float2 *)(gg + 2 * u);                          // alpha, c
             const float2 rb = *(const float2 *)(rg + u * Stage<DK>::kRowFloats);      // beta, beta*v
             const float *ct = cg + u * Stage<DK>::kColFloats;
@@ -464,22 +491,24 @@ __device__ inline void compute_chunk(const float *buf, int left, float *M, float
 // Checkpoint pass of the backward over one staged chunk: the forward update
 // without readout (the same 4 VALU ops per entry and token as the replay,
 // so the states are bit-identical to the forward's), storing (M, I) before
-// every kSB-th token of the sequence: the workgroup's block for the
-// checkpoint before token kSB s is at ckp + s * ck_stride.
+// every kCkI-th token of the sequence: the workgroup's block for the
+// checkpoint before token kCkI s is at ckp + s * ck_stride.
 template <int DK, int C, bool IPE>
 __device__ inline void ckpt_chunk(const float *buf, float *M, float *I, int row_local, int g,
                                   float *ckp, size_t ck_stride, int t0, int ntok, const float *ipe) {
     using LT = LaneTile<DK>;
-    static_assert(C % kSB == 0, "chunk must hold whole checkpoint intervals");
+    static_assert(C % kCkI == 0, "chunk must hold whole checkpoint intervals");
     const float *cbase = buf + LT::col(g, 0, 0);
     const float *rbase = buf + C * Stage<DK>::kColFloats + 2 * row_local;
     int goff = C * (Stage<DK>::kColFloats + Stage<DK>::kRowFloats);
     asm volatile("" : "+v"(goff));
     const float *gbase = buf + goff;
+    // rolled over 8-token halves: unrolling a whole interval raises the
+    // register count (and lowers the occupancy) without saving any work
 #pragma unroll 1
     for (int sb = 0; sb < C / kSB; ++sb) {
-        if (t0 + sb * kSB < ntok) {
-            store_pair<LT::kCols>(ckp + (size_t)((t0 / kSB) + sb) * ck_stride, threadIdx.x, M, I);
+        if (sb % 2 == 0 && t0 + sb * kSB < ntok) {
+            store_pair<LT::kCols>(ckp + (size_t)((t0 + sb * kSB) / kCkI) * ck_stride, threadIdx.x, M, I);
         }
 #pragma unroll
         for (int u0 = 0; u0 < kSB; ++u0) {
@@ -516,7 +545,7 @@ enum FwdMode { kReplay = 0, kCheckpoint = 2 };
 // Without a split (nseg = 1) this is the whole sequence in one pass.
 //
 // kCheckpoint (the backward's first pass; nseg = 1): the sequence from
-// (mu0, I0) without readout, storing (M, I) before every kSB-th token.
+// (mu0, I0) without readout, storing (M, I) before every kCkI-th token.
 //
 // (The summaries of a split come from summary_mfma_kernel.)
 template <int DK, int C, typename TIn, typename TOut, int MODE, bool IPE, bool CKPT = false>
@@ -627,10 +656,10 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
 
     const int ntok = t_end - t_begin;
     const int nchunks = (ntok + C - 1) / C;
-    // checkpoints: [B*H][nsb][row block][thread][2 DK/16] floats
+    // checkpoints: [B*H][nck][row block][thread][2 DK/16] floats
     const size_t ck_stride = (size_t)rb_per_head * kThreads * 2 * LT::kCols;
     float *ckp = (MODE == kCheckpoint || CKPT)
-                     ? a.ck + ((size_t)bh * a.nsb * rb_per_head + row0 / kRowsPerWG) * (kThreads * 2 * LT::kCols)
+                     ? a.ck + ((size_t)bh * a.nck * rb_per_head + row0 / kRowsPerWG) * (kThreads * 2 * LT::kCols)
                      : nullptr;
     Stager<DK, C, TIn, MODE == kReplay> st;
     if (nchunks > 0) {
@@ -650,8 +679,7 @@ __global__ __launch_bounds__(kThreads) void fwd_chunked_kernel(FwdArgs a) {
         if (MODE == kReplay)
             compute_chunk<DK, C, TOut, IPE, CKPT>(
                 cur, ntok - t0, M, I, row_local, g, ybase + (size_t)t0 * ystride, ystride, ipe,
-                CKPT ? ckp + (size_t)(t0 / kSB) * ck_stride : nullptr,
-                CKPT ? (ntok - t0 > kSB ? ckp + (size_t)(t0 / kSB + 1) * ck_stride : a.ck_sink) : nullptr);
+                CKPT ? ckp + (size_t)(t0 / kCkI) * ck_stride : nullptr);
         else
             ckpt_chunk<DK, C, IPE>(cur, M, I, row_local, g, ckp, ck_stride, t0, ntok, ipe);
         if (more) st.commit((c & 1) ? buf0 : buf1, A, Ip, tid, a.vstar);
@@ -984,11 +1012,17 @@ __global__ __launch_bounds__(kThreads) void summary_mfma_kernel(FwdArgs a) {
 //
 // Passes (one stream):
 //  1. checkpoint: the forward kernel in kCheckpoint mode stores (M, I)
-//     before every 8th token (4 VALU ops per entry and token, no readout).
+//     before every 16th token (4 VALU ops per entry and token, no readout).
 //  2. bwd_kernel: one workgroup per (head, 16 value rows), the forward's
-//     lane layout.  Sub-blocks of 8 tokens are taken newest first; each half
-//     of 4 tokens is replayed from the checkpoint into registers and walked
-//     in reverse.  Row sums (gbv, gb, da, dc) use the forward's transposing
+//     lane layout.  Sub-blocks of 8 tokens are taken newest first, each
+//     16-token checkpoint interval as its newer sub-block, then its older one.
+//     The newer one first replays the older one from the checkpoint to reach
+//     its own start state, leaving the state at the older one's token 4 in a
+//     per-thread LDS snapshot.  In each sub-block each half of 4 tokens is
+//     replayed into registers (from the sub-block's start state, or from the
+//     snapshot for the older sub-block's upper half) and walked in reverse:
+//     28 replayed tokens per interval, against 24 with a checkpoint every 8
+//     tokens, for half the checkpoint bytes.  Row sums (gbv, gb, da, dc) use the forward's transposing
 //     DPP reduction; column sums (gq, gk) are reduce-scattered across the
 //     4 rows of a wave, summed over the 4 waves in LDS and written as this
 //     row block's partial.
@@ -1004,7 +1038,10 @@ template <int DK> struct BwdStage {
     static constexpr int kFloats = kGate + 2 * kSB;
     static constexpr int kRed = 2 * kFloats;                  // gq | gk per token and wave
     static constexpr int kRs = kRed + kSB * kWaves * 2 * DK;   // row sums [token][4][16 rows]
-    static constexpr int kTotal = kRs + kSB * 4 * kRowsPerWG;
+    // per-thread snapshot of (M, I) at an older sub-block's token 4: float4 i
+    // of thread tid at kSnap + 4 (i kThreads + tid)
+    static constexpr int kSnap = kRs + kSB * 4 * kRowsPerWG;
+    static constexpr int kTotal = kSnap + kThreads * 2 * (DK / kLanesPerRow);
 };
 
 struct BwdArgs {
@@ -1016,7 +1053,9 @@ struct BwdArgs {
     float *ps;         // [row block][B*H][T][2]: (da, dc) partials
     float *pI0;        // [B*H][row block]: sum of gI0 (default start state)
     float *pip;        // per-entry prior: [B*H][dv][dk] per-sequence gradient of I_prior
-    int B, T, H, dv, nsb, nwg, xcd_remap;
+    int B, T, H, dv, nwg, xcd_remap;
+    int nsb;           // sub-blocks per sequence: ceil(T / kSB)
+    int nck;           // checkpoints per sequence: ceil(T / kCkI)
     int vstar;         // 1: v holds beta . v
 };
 
@@ -1038,6 +1077,18 @@ struct BwdStager {
     uint4 kq[kKQPer];
     uint4 vv, bb, gg;
     uint32_t dtv;          // raw bits (io<TIn>::bits) until the commit
+
+    // Makes the loaded packets count as used here, so the wait for them lands
+    // here.  The loads sit under per-lane branches, so the compiler cannot
+    // count them: left to itself it waits for every outstanding memory
+    // operation at the first use (vmcnt(0)), which after the walk's stores
+    // includes those stores.
+    __device__ inline void ready() const {
+#pragma unroll
+        for (int u = 0; u < kKQPer; ++u) asm volatile("" ::"v"(kq[u].x), "v"(kq[u].y), "v"(kq[u].z), "v"(kq[u].w));
+        asm volatile("" ::"v"(vv.x), "v"(vv.y), "v"(vv.z), "v"(vv.w), "v"(bb.x), "v"(bb.y), "v"(bb.z), "v"(bb.w));
+        asm volatile("" ::"v"(gg.x), "v"(gg.y), "v"(gg.z), "v"(gg.w), "v"(dtv));
+    }
 
     __device__ static inline int vb_slot(int tid) { return (tid + kThreads - 64) % kThreads; }
     __device__ static inline int gy_slot(int tid) { return (tid + kThreads - 128) % kThreads; }
@@ -1376,40 +1427,69 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(BwdArgs a) {
             }
     } else {
         const size_t ck_stride = (size_t)rb_per_head * kThreads * 2 * KC;
-        const float *ckb = a.ck + ((size_t)bh * a.nsb * rb_per_head + rb) * (kThreads * 2 * KC);
+        const float *ckb = a.ck + ((size_t)bh * a.nck * rb_per_head + rb) * (kThreads * 2 * KC);
         const TIn *kseq = (const TIn *)a.k + seq0 * DK;
         const TIn *qseq = (const TIn *)a.q + seq0 * DK;
         const TIn *vseq = (const TIn *)a.v + seq0 * a.dv + row0;
         const TIn *bseq = (const TIn *)a.beta + seq0 * a.dv + row0;
         const TG *gseq = (const TG *)a.gy + seq0 * a.dv + row0;
         const TIn *dseq = (const TIn *)a.dt + seq0;
+        float *snap = lds + S::kSnap;
+        // Sub-block sb is staged in buffer sb & 1.  When sub-block sb starts,
+        // sb and sb - 1 are both staged (a newer sub-block replays the older
+        // one); sb - 2 is loaded during sb and committed into sb's buffer
+        // after it.
         BwdStager<DK, TIn, TG> st;
-        {
-            const size_t tn = (size_t)(a.nsb - 1) * kSB;
+        auto stage = [&](int sbl) __attribute__((always_inline)) {
+            const size_t tn = (size_t)sbl * kSB;
             st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
                     gseq + tn * vb_tok, dseq + tn * a.H, a.T - (int)tn, a.H, a.dv, tid);
-            st.commit(lds + ((a.nsb - 1) & 1) * S::kFloats, A, Ip, tid, a.vstar);
+        };
+        stage(a.nsb - 1);
+        st.commit(lds + ((a.nsb - 1) & 1) * S::kFloats, A, Ip, tid, a.vstar);
+        if (a.nsb > 1) {
+            stage(a.nsb - 2);
+            st.commit(lds + ((a.nsb - 2) & 1) * S::kFloats, A, Ip, tid, a.vstar);
         }
+        // the start state of the current checkpoint interval (sub-blocks 2n, 2n + 1)
         float ckM[KC], ckI[KC];
-        load_pair<KC>(ckb + (size_t)(a.nsb - 1) * ck_stride, tid, ckM, ckI);
+        load_pair<KC>(ckb + (size_t)((a.nsb - 1) / 2) * ck_stride, tid, ckM, ckI);
+        regs_ready<KC>(ckM);
+        regs_ready<KC>(ckI);
         __syncthreads();
 
         for (int sb = a.nsb - 1; sb >= 0; --sb) {
             const float *cur = lds + (sb & 1) * S::kFloats;
             const int t0 = sb * kSB;
-            if (sb > 0) {
-                const size_t tn = (size_t)(t0 - kSB);
-                st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
-                        gseq + tn * vb_tok, dseq + tn * a.H, a.T - (int)tn, a.H, a.dv, tid);
+            const bool newer = sb & 1;      // the newer sub-block of its checkpoint interval
+            if (sb > 1) stage(sb - 2);
+            float nM[KC], nI[KC];           // the start state of the next sub-block taken
+            if (newer) {
+                // this sub-block's start state: the older sub-block (staged in
+                // the other buffer) replayed from the interval's checkpoint,
+                // which the older sub-block then starts from
+                const float *older = lds + ((sb - 1) & 1) * S::kFloats;
+#pragma unroll
+                for (int s = 0; s < KC; ++s) { nM[s] = ckM[s]; nI[s] = ckI[s]; }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bwd_replay_token<DK, IPE, FZ>(older, e, ckM, ckI, row_local, g, ipe);
+                lds_store_pair<KC>(snap, tid, ckM, ckI);
+#pragma unroll
+                for (int e = 4; e < 8; ++e) bwd_replay_token<DK, IPE, FZ>(older, e, ckM, ckI, row_local, g, ipe);
             }
             float xM[4][KC], xI[4][KC];
             float acc[16];      // this half's row partials: gbv, gb, da, dc of its 4 tokens
-            // upper half: tokens 4..7, replayed from the checkpoint
+            // upper half: tokens 4..7, replayed from the state before token 4:
+            // an older sub-block's snapshot, else the start state replayed
             float mM[KC], mI[KC];
+            if (!newer && sb + 1 < a.nsb) {
+                lds_load_pair<KC>(snap, tid, mM, mI);
+            } else {
 #pragma unroll
-            for (int s = 0; s < KC; ++s) { mM[s] = ckM[s]; mI[s] = ckI[s]; }
+                for (int s = 0; s < KC; ++s) { mM[s] = ckM[s]; mI[s] = ckI[s]; }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) bwd_replay_token<DK, IPE, FZ>(cur, e, mM, mI, row_local, g, ipe);
+                for (int e = 0; e < 4; ++e) bwd_replay_token<DK, IPE, FZ>(cur, e, mM, mI, row_local, g, ipe);
+            }
 #pragma unroll
             for (int e = 4; e < 8; ++e) {
                 const float *pm = e == 4 ? mM : xM[e > 4 ? e - 5 : 0];
@@ -1463,8 +1543,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(BwdArgs a) {
                 bwd_replay_token<DK, IPE, FZ>(cur, e, xM[e], xI[e], row_local, g, ipe);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            float nM[KC], nI[KC];
-            if (sb > 0) load_pair<KC>(ckb + (size_t)(sb - 1) * ck_stride, tid, nM, nI);
+            // an older sub-block hands over to the previous interval's newer one
+            if (!newer && sb > 0) load_pair<KC>(ckb + (size_t)(sb / 2 - 1) * ck_stride, tid, nM, nI);
 #pragma unroll
             for (int e = 3; e >= 0; --e) {
                 if (FZ) {
@@ -1481,7 +1561,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(BwdArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             bwd_row_sums(acc, g, rs + row_local);
-            if (sb > 0) st.commit(lds + ((sb - 1) & 1) * S::kFloats, A, Ip, tid, a.vstar);
+            // the next sub-block's packets and start state, waited for while
+            // only loads are outstanding (not after this sub-block's stores)
+            if (sb > 1) st.ready();
+            regs_ready<KC>(nM);
+            regs_ready<KC>(nI);
             __syncthreads();
             // sums over the 4 waves: this row block's partials of (gq, gk) and (da, dc)
             for (int n = 4 * tid; n < kSB * 2 * DK; n += 4 * kThreads) {
@@ -1525,6 +1609,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(BwdArgs a) {
                 if (t0 + e < a.T) a.ps[((size_t)rb * bth + (size_t)bh * a.T + t0 + e) * 2 + qd] = v;
             }
             __syncthreads();
+            if (sb > 1) {
+                st.commit(lds + (sb & 1) * S::kFloats, A, Ip, tid, a.vstar);
+                if (!newer) __syncthreads();    // sub-block sb - 1 replays sb - 2 at once
+            }
             if (sb > 0) {
 #pragma unroll
                 for (int s = 0; s < KC; ++s) { ckM[s] = nM[s]; ckI[s] = nI[s]; }
@@ -5125,18 +5213,18 @@ palimpsa_status launch_frozen(const FrozenArgs &a, hipStream_t s) {
 }
 
 // Workspace of the backward, in 256-byte aligned sections (float counts):
-//   ck    [B*H][nsb][dv/16][dk/32][256][4]  checkpoints, nsb = ceil(T / 8)
+//   ck    [B*H][nck][dv/16][dk/32][256][4]  checkpoints, nck = ceil(T / 16)
 //   pqk   [dv/16][B*T*H][2 dk]              row-block partials of gq | gk
 //   ps    [dv/16][B*H][T][2]                row-block partials of (da, dc)
 //   gabh, gibh [B*H]                        per-sequence gate gradient sums
 //   pI0   [B*H][dv/16]                      row-block sums of gI0
 //   pip   [B*H][dv][dk]                     per-entry prior only: per-sequence gI_prior
 struct BwdWs {
-    float *ck, *pqk, *ps, *gabh, *gibh, *pI0, *pip, *sink;
+    float *ck, *pqk, *ps, *gabh, *gibh, *pI0, *pip;
     size_t bytes;
 };
 BwdWs plan_bwd_ws(void *base, int B, int T, int H, int dk, int dv, bool ipe) {
-    const size_t nsb = (size_t)(T + kSB - 1) / kSB, nrb = (size_t)dv / kRowsPerWG;
+    const size_t nck = (size_t)(T + kCkI - 1) / kCkI, nrb = (size_t)dv / kRowsPerWG;
     const size_t bh = (size_t)B * H, bth = bh * T;
     size_t off = 0;
     auto take = [&](size_t floats) {
@@ -5144,11 +5232,9 @@ BwdWs plan_bwd_ws(void *base, int B, int T, int H, int dk, int dv, bool ipe) {
         off = (off + floats * sizeof(float) + 255) / 256 * 256;
         return o;
     };
-    const size_t o_ck = take(bh * nsb * 2 * dv * dk), o_pqk = take(nrb * bth * 2 * dk), o_ps = take(nrb * bth * 2);
+    const size_t o_ck = take(bh * nck * 2 * dv * dk), o_pqk = take(nrb * bth * 2 * dk), o_ps = take(nrb * bth * 2);
     const size_t o_ga = take(bh), o_gi = take(bh), o_pi = take(bh * nrb);
     const size_t o_pip = ipe ? take(bh * dv * dk) : off;
-    // the training forward's discarded checkpoint stores (one workgroup block)
-    const size_t o_sink = take((size_t)kThreads * 2 * (dk / kLanesPerRow));
     BwdWs w;
     // section pointers only exist for a real base (a size query passes none)
     char *c = (char *)base;
@@ -5156,7 +5242,6 @@ BwdWs plan_bwd_ws(void *base, int B, int T, int H, int dk, int dv, bool ipe) {
     w.ck = (float *)at(o_ck); w.pqk = (float *)at(o_pqk); w.ps = (float *)at(o_ps);
     w.gabh = (float *)at(o_ga); w.gibh = (float *)at(o_gi); w.pI0 = (float *)at(o_pi);
     w.pip = ipe ? (float *)at(o_pip) : nullptr;
-    w.sink = (float *)at(o_sink);
     w.bytes = off;
     return w;
 }
@@ -5614,7 +5699,7 @@ palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const 
     fa.nwg = (int)nwg; fa.xcd_remap = (nwg % 8 == 0) ? 1 : 0; fa.nwg_seg = (int)nwg;
     fa.seg_len = T > 0 ? T : 1; fa.nseg = 1;
     fa.ck = (flags & PALIMPSA_CHECKPOINTS_SAVED) ? nullptr : w.ck;
-    fa.nsb = (T + kSB - 1) / kSB;
+    fa.nck = (T + kCkI - 1) / kCkI;
     fa.vstar = (flags & PALIMPSA_VSTAR) ? 1 : 0;
 
     BwdArgs ba = {};
@@ -5623,7 +5708,7 @@ palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const 
     ba.gv = gv; ba.gbeta = gbeta; ba.gmu0 = gmu0; ba.gI0 = gI0;
     ba.ck = w.ck; ba.pqk = w.pqk; ba.ps = w.ps; ba.pI0 = w.pI0; ba.pip = w.pip;
     ba.vstar = fa.vstar;
-    ba.B = B; ba.T = T; ba.H = H; ba.dv = dv; ba.nsb = fa.nsb;
+    ba.B = B; ba.T = T; ba.H = H; ba.dv = dv; ba.nsb = (T + kSB - 1) / kSB; ba.nck = fa.nck;
     ba.nwg = (int)nwg; ba.xcd_remap = fa.xcd_remap;
 
     hipStream_t s = (hipStream_t)stream;
@@ -5693,7 +5778,7 @@ palimpsa_status palimpsa_bwd_frozen(const void *q, const void *k, const void *v,
     fa.B = B; fa.T = T; fa.H = H; fa.dv = dv;
     fa.nwg = (int)nwg; fa.xcd_remap = (nwg % 8 == 0) ? 1 : 0; fa.nwg_seg = (int)nwg;
     fa.seg_len = T > 0 ? T : 1; fa.nseg = 1;
-    fa.ck = w.ck; fa.nsb = (T + kSB - 1) / kSB;
+    fa.ck = w.ck; fa.nck = (T + kCkI - 1) / kCkI;
     fa.vstar = beta ? 0 : 1;
     fa.frozen = 1;
 
@@ -5703,7 +5788,7 @@ palimpsa_status palimpsa_bwd_frozen(const void *q, const void *k, const void *v,
     ba.gv = gv; ba.gbeta = beta ? gbeta : nullptr; ba.gmu0 = gmu0; ba.gI0 = nullptr;
     ba.ck = w.ck; ba.pqk = w.pqk; ba.ps = w.ps; ba.pI0 = w.pI0; ba.pip = nullptr;
     ba.vstar = fa.vstar;
-    ba.B = B; ba.T = T; ba.H = H; ba.dv = dv; ba.nsb = fa.nsb;
+    ba.B = B; ba.T = T; ba.H = H; ba.dv = dv; ba.nsb = (T + kSB - 1) / kSB; ba.nck = fa.nck;
     ba.nwg = (int)nwg; ba.xcd_remap = fa.xcd_remap;
 
     const bool bf_in = in_dtype == PALIMPSA_BF16, bf_gy = gy_dtype == PALIMPSA_BF16;
@@ -5823,13 +5908,13 @@ palimpsa_status fwd_chunked_impl(const void *q, const void *k, const void *v,
     a.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
     a.nwg_seg = (int)nwg;
     a.vstar = (flags & PALIMPSA_VSTAR) ? 1 : 0;
-    a.ck = nullptr; a.ck_sink = nullptr; a.nsb = 0; a.frozen = 0;
+    a.ck = nullptr; a.nck = 0; a.frozen = 0;
     if (save_ck) {
         if ((long long)B * H * 2 > 0x7fffffffLL) return PALIMPSA_ERR_UNSUPPORTED;
         const BwdWs w = plan_bwd_ws(workspace, B, T, H, dk, dv, ipe);
         if (workspace_bytes < w.bytes) return PALIMPSA_ERR_INVALID_ARG;
         if (T == 0 && !muT) return PALIMPSA_OK;
-        a.ck = w.ck; a.ck_sink = w.sink; a.nsb = (T + kSB - 1) / kSB;
+        a.ck = w.ck; a.nck = (T + kCkI - 1) / kCkI;
         a.nseg = 1; a.seg_len = T > 0 ? T : 1; a.ws = nullptr;
         hipStream_t s = (hipStream_t)stream;
         const bool bf_in = in_dtype == PALIMPSA_BF16, bf_out = out_dtype == PALIMPSA_BF16;

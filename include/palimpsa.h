@@ -165,7 +165,7 @@ typedef enum {
  * backward workspace of at least palimpsa_bwd_workspace_size(B, T, H, dk, dv,
  * flags) bytes (else PALIMPSA_ERR_INVALID_ARG); the forward runs in one pass
  * (segments must be 0 or 1, chunk 0 or 16, dk <= 128, dv <= 1024, else
- * PALIMPSA_ERR_UNSUPPORTED) and also stores the state before every 8th token
+ * PALIMPSA_ERR_UNSUPPORTED) and also stores the state before every 16th token
  * there, bit-identical to what palimpsa_bwd would recompute.  A backward called
  * on the same inputs, flags (PALIMPSA_CHECKPOINTS_SAVED in place of
  * PALIMPSA_SAVE_CHECKPOINTS) and workspace then reuses them.
@@ -296,7 +296,7 @@ palimpsa_status palimpsa_step(const void *q, const void *k, const void *v,
  * taken through the natural-parameter scans of the slides' frame "Natural
  * parameters expose two affine scans" (App. A.12) and the gate of Eq. (9)
  * (alpha = exp(-A dt), c = (1 - alpha) I_prior).  It recomputes the forward
- * states itself (checkpoints every 8 tokens in the workspace), so it takes
+ * states itself (checkpoints every 16 tokens in the workspace), so it takes
  * the forward's inputs, not its outputs.
  *
  * Inputs (device pointers, layouts and dtypes as palimpsa_fwd_chunked):
@@ -343,7 +343,7 @@ palimpsa_status palimpsa_bwd(const void *q, const void *k, const void *v, const 
 
 /*
  * Bytes of workspace palimpsa_bwd needs: the checkpoints (8 B per state
- * entry every 8 tokens: B H ceil(T/8) dv dk 8 bytes) plus the per-row-block
+ * entry every 16 tokens: B H ceil(T/16) dv dk 8 bytes) plus the per-row-block
  * partials of gq, gk (dv/16 x B T H x 2 dk x 4 bytes) and small sums; with
  * PALIMPSA_PRIOR_PER_ENTRY also each sequence's gIp (B H dv dk x 4 bytes).
  * Returns 0 for sizes or flags palimpsa_bwd would reject.  flags may carry
@@ -368,7 +368,7 @@ size_t palimpsa_bwd_workspace_size(int B, int T, int H, int dk, int dv, int flag
  *     gradients carry about 2^-8 relative error, and the batch sums gA and
  *     gIp that much of the sum of their terms' magnitudes;
  *   - otherwise (float32 inputs, dk = 32, other dv): float32 throughout, the
- *     states recomputed from checkpoints every 8 tokens.
+ *     states recomputed from checkpoints every 16 tokens.
  *
  * Inputs (device pointers, layouts as palimpsa_fwd_chunked):
  *   q, k      [B, T, H, dk]  in_dtype

@@ -313,16 +313,15 @@ def test_bwd_frozen_rejects_invalid_calls(lib, over, status):
 
 
 def test_bwd_workspace_size_host_logic(lib):
-    """Checkpoints every 8 tokens plus the row-block partials, each section
+    """Checkpoints every 16 tokens plus the row-block partials, each section
     padded to 256 bytes."""
     import bayesian_metaplastic_memory_amd as pm
     pad = lambda n: (4 * n + 255) // 256 * 256
 
     def expect(B, T, H, dk, dv, per_entry=False):
-        nsb, nrb, bh = (T + 7) // 8, dv // 16, B * H
-        return (pad(bh * nsb * 2 * dv * dk) + pad(nrb * bh * T * 2 * dk) + pad(nrb * bh * T * 2)
-                + 2 * pad(bh) + pad(bh * nrb) + (pad(bh * dv * dk) if per_entry else 0)
-                + pad(256 * 2 * dk // 16))    # the training forward's sink block
+        nck, nrb, bh = (T + 15) // 16, dv // 16, B * H
+        return (pad(bh * nck * 2 * dv * dk) + pad(nrb * bh * T * 2 * dk) + pad(nrb * bh * T * 2)
+                + 2 * pad(bh) + pad(bh * nrb) + (pad(bh * dv * dk) if per_entry else 0))
     for shape in [(1, 10, 2, 32, 32), (8, 4096, 12, 128, 128), (1, 0, 3, 64, 128), (2, 9, 1, 128, 64),
                   (1, 33, 2, 128, 256), (2, 5, 3, 64, 48)]:
         assert pm.bwd_workspace_size(*shape) == expect(*shape), shape
