@@ -1077,12 +1077,10 @@ struct BwdStager {
     uint4 kq[kKQPer];
     uint4 vv, bb, gg;
     uint32_t dtv;          // raw bits (io<TIn>::bits) until the commit
+    int left_;             // tokens of the sequence from the sub-block's start
 
     // Makes the loaded packets count as used here, so the wait for them lands
-    // here.  The loads sit under per-lane branches, so the compiler cannot
-    // count them: left to itself it waits for every outstanding memory
-    // operation at the first use (vmcnt(0)), which after the walk's stores
-    // includes those stores.
+    // here rather than at the commit, after the walk's stores.
     __device__ inline void ready() const {
 #pragma unroll
         for (int u = 0; u < kKQPer; ++u) asm volatile("" ::"v"(kq[u].x), "v"(kq[u].y), "v"(kq[u].z), "v"(kq[u].w));
@@ -1095,43 +1093,41 @@ struct BwdStager {
     __device__ static inline int dt_slot(int tid) { return (tid + kThreads - 192) % kThreads; }
 
     // Bases point at token t0 of this (b, h) (v, beta, gy at the workgroup's
-    // first row); `left` = T - t0.  Token tt is at offset tt H d.
+    // first row); `left` = T - t0 >= 1.  Token tt is at offset tt H d.
+    // Branch-free: every thread issues every load, tokens past the end read
+    // token left - 1 (the commit stages zeros for them) and threads without a
+    // packet read packet 0.  Loads under per-lane branches are not counted by
+    // the compiler, which then makes the next wait for an earlier load (a
+    // checkpoint) wait for all of these as well.
     __device__ inline void load(const TIn *kb, const TIn *qb, const TIn *vb, const TIn *bb_, const TG *gb,
                                 const TIn *db, int left, int H, int dv, int tid) {
+        left_ = left;
 #pragma unroll
         for (int u = 0; u < kKQPer; ++u) {
-            const int p = tid + u * kThreads;
-            if ((2 * kHalf) % kThreads == 0 || p < 2 * kHalf) {
-                const bool isq = p >= kHalf;
-                const int pp = isq ? p - kHalf : p;
-                const int tt = pp / kColPkts;
-                const uint32_t off = (uint32_t)tt * (uint32_t)(H * DK) + (pp % kColPkts) * kPer;
-                kq[u] = make_uint4(0, 0, 0, 0);
-                if (tt < left) kq[u] = *(const uint4 *)((isq ? qb : kb) + off);
-            }
+            int p = tid + u * kThreads;
+            if ((2 * kHalf) % kThreads != 0 && p >= 2 * kHalf) p = 0;
+            const bool isq = p >= kHalf;
+            const int pp = isq ? p - kHalf : p;
+            const int tt = min(pp / kColPkts, left - 1);
+            const uint32_t off = (uint32_t)tt * (uint32_t)(H * DK) + (pp % kColPkts) * kPer;
+            kq[u] = *(const uint4 *)((isq ? qb : kb) + off);
         }
-        const int pv = vb_slot(tid);
-        if (pv < kVB) {
-            const int tt = pv / kRowPkts;
+        {
+            const int pv = vb_slot(tid) < kVB ? vb_slot(tid) : 0;
+            const int tt = min(pv / kRowPkts, left - 1);
             const uint32_t off = (uint32_t)tt * (uint32_t)(H * dv) + (pv % kRowPkts) * kPer;
-            vv = make_uint4(0, 0, 0, 0);
-            bb = make_uint4(0, 0, 0, 0);
-            if (tt < left) {
-                vv = *(const uint4 *)(vb + off);
-                bb = *(const uint4 *)(bb_ + off);
-            }
+            vv = *(const uint4 *)(vb + off);
+            bb = *(const uint4 *)(bb_ + off);
         }
-        const int pg = gy_slot(tid);
-        if (pg < kGY) {
-            const int tt = pg / kRowPktsG;
+        {
+            const int pg = gy_slot(tid) < kGY ? gy_slot(tid) : 0;
+            const int tt = min(pg / kRowPktsG, left - 1);
             const uint32_t off = (uint32_t)tt * (uint32_t)(H * dv) + (pg % kRowPktsG) * kPerG;
-            gg = make_uint4(0, 0, 0, 0);
-            if (tt < left) gg = *(const uint4 *)(gb + off);
+            gg = *(const uint4 *)(gb + off);
         }
-        const int pd = dt_slot(tid);
-        if (pd < kSB) {
-            dtv = 0;
-            if (pd < left) dtv = io<TIn>::bits(db[(uint32_t)pd * (uint32_t)H]);
+        {
+            const int pd = dt_slot(tid) < kSB ? dt_slot(tid) : 0;
+            dtv = io<TIn>::bits(db[(uint32_t)min(pd, left - 1) * (uint32_t)H]);
         }
     }
 
@@ -1147,7 +1143,7 @@ struct BwdStager {
                 const int tt = pp / kColPkts;
                 const int off = (pp % kColPkts) * kPer;
                 float x[kPer];
-                packet<TIn>::widen(kq[u], x);
+                packet<TIn>::widen(tt < left_ ? kq[u] : make_uint4(0, 0, 0, 0), x);   // past the end: k = q = 0
                 float *dst = buf + tt * S::kColFloats + off;
 #pragma unroll
                 for (int e = 0; e < kPer; e += 4) {
@@ -1165,9 +1161,10 @@ struct BwdStager {
         if (pv < kVB) {
             const int tt = pv / kRowPkts;
             const int r0 = (pv % kRowPkts) * kPer;
+            const bool in = tt < left_;       // past the end: v = beta = 0
             float xv[kPer], xb[kPer];
-            packet<TIn>::widen(vv, xv);
-            packet<TIn>::widen(bb, xb);
+            packet<TIn>::widen(in ? vv : make_uint4(0, 0, 0, 0), xv);
+            packet<TIn>::widen(in ? bb : make_uint4(0, 0, 0, 0), xb);
             float *dst = rows + tt * S::kRowFloats + 4 * r0;
 #pragma unroll
             for (int e = 0; e < kPer; ++e) {
@@ -1180,14 +1177,15 @@ struct BwdStager {
             const int tt = pg / kRowPktsG;
             const int r0 = (pg % kRowPktsG) * kPerG;
             float xg[kPerG];
-            packet<TG>::widen(gg, xg);
+            packet<TG>::widen(tt < left_ ? gg : make_uint4(0, 0, 0, 0), xg);
             float *dst = rows + tt * S::kRowFloats + 4 * r0 + 3;
 #pragma unroll
             for (int e = 0; e < kPerG; ++e) dst[4 * e] = xg[e];
         }
         const int pd = dt_slot(tid);
         if (pd < kSB) {
-            const float2 gc = gate(A, io<TIn>::from_bits(dtv), Ip);
+            // past the end: dt = 0, so alpha = 1 and c = 0
+            const float2 gc = gate(A, io<TIn>::from_bits(pd < left_ ? dtv : 0u), Ip);
             *(float2 *)(buf + S::kGate + 2 * pd) = gc;
         }
     }
@@ -2294,6 +2292,9 @@ __global__ __launch_bounds__(kThreads, 2) void bd2_bwd_kernel(BdBwdArgs a) {
         for (int sb = a.nsb - 1; sb >= 0; --sb) {
             const float *cur = lds + (sb & 1) * S::kFloats;
             const int t0 = sb * kSB;
+            // the checkpoint (loaded at the end of the previous sub-block) is
+            // waited for before the next loads go out, not behind them
+            regs_ready<N>(ckS);
             if (sb > 0) {
                 const size_t tn = (size_t)(t0 - kSB);
                 st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
@@ -2329,6 +2330,7 @@ __global__ __launch_bounds__(kThreads, 2) void bd2_bwd_kernel(BdBwdArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             bwd_row_sums(acc, g, rs + 4 * 4 * kRowsPerWG + row_local);
+            if (sb > 0) st.ready();    // half a sub-block after the loads, before any store
             // lower half: tokens 0..3
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -2860,6 +2862,9 @@ __global__ __launch_bounds__(kThreads, 2) void bd4_bwd_kernel(BdBwdArgs a) {
         for (int sb = a.nsb - 1; sb >= 0; --sb) {
             const float *cur = lds + (sb & 1) * S::kFloats;
             const int t0 = sb * kSB;
+            // the checkpoint (loaded at the end of the previous sub-block) is
+            // waited for before the next loads go out, not behind them
+            regs_ready<N>(ckS);
             if (sb > 0) {
                 const size_t tn = (size_t)(t0 - kSB);
                 st.load(kseq + tn * kq_tok, qseq + tn * kq_tok, vseq + tn * vb_tok, bseq + tn * vb_tok,
@@ -2900,6 +2905,7 @@ __global__ __launch_bounds__(kThreads, 2) void bd4_bwd_kernel(BdBwdArgs a) {
             quarter(3);
             quarter(2);
             bwd_row_sums(acc, g, rs + 4 * 4 * kRowsPerWG + row_local);
+            if (sb > 0) st.ready();    // half a sub-block after the loads, before any store
             quarter(1);
             quarter(0);
             bwd_row_sums(acc, g, rs + row_local);
