@@ -291,7 +291,7 @@ def training_extra(torch, pm, workloads, w, g, steps):
     _, per_r = time_launches(recompute, steps, 3, torch)
     mean_s = lambda per: sum(per) / len(per) / 1e3
     s_s, f_s, r_s = mean_s(per_s), mean_s(per_f), mean_s(per_r)
-    ck_bytes = w.B * w.H * ((w.T + 7) // 8) * 2 * w.dv * w.dk * 4
+    ck_bytes = w.B * w.H * ((w.T + 15) // 16) * 2 * w.dv * w.dk * 4
     updates = w.B * w.H * w.T * w.dv * w.dk
     esz = 2 if w.dtype == torch.bfloat16 else 4
     return {"workload": w.name + ", training step (forward with y and final state, then the full backward)",
