@@ -3611,19 +3611,22 @@ struct FrozenArgs {
 
 template <int DK>
 struct FzLds {
-    // One staging buffer (bf16 unless noted); two are used alternately.  Rows
-    // are padded by 8 elements (16 bytes) so that the 16 rows a fragment read
-    // touches fall in distinct LDS banks.  K is also swizzled: the 16-byte
-    // column block cb of row r sits at block cb ^ ((r / 8) % 8), which keeps
-    // the stagers' row writes (8 tokens apart) in distinct banks too.
+    // One staging buffer (bf16 unless noted); two are used alternately.  All
+    // arrays are token-major, as the inputs are; the operands that need the
+    // token index along k (K^T, W^T) are read with gfx950's transposing LDS
+    // read.  Q and K rows are padded by 8 elements (16 bytes) so that the 16
+    // rows a fragment read touches fall in distinct LDS banks.  K is also
+    // swizzled: the 16-byte column block cb of row r sits at block
+    // cb ^ ((r / 8) % 8), which keeps the stagers' row writes (8 tokens apart)
+    // in distinct banks too.  W rows are 80 elements apart (40 banks), so the
+    // 8 token rows of a half-wave's transposing read hit distinct banks.
     static constexpr int kQS = DK + 8;                   // row stride of Q and K
-    static constexpr int kTS = kFzC + 8;                 // row stride of the token-minor arrays
+    static constexpr int kWS = kFzRows + 16;             // row stride of W and diag(d) W
     static constexpr int kQ = 0;                         // Q  [C][DK]
     static constexpr int kK = kQ + kFzC * kQS;           // K  [C][DK]
-    static constexpr int kKt = kK + kFzC * kQS;          // K^T [DK][C]
-    static constexpr int kWt = kKt + DK * kTS;           // W^T [64][C]
-    static constexpr int kWdt = kWt + kFzRows * kTS;     // (diag(d) W)^T [64][C]
-    static constexpr int kP = kWdt + kFzRows * kTS;      // P^T tiles [10][64 lanes][4], D-fragment order
+    static constexpr int kW = kK + kFzC * kQS;           // W  [C][64]
+    static constexpr int kWd = kW + kFzC * kWS;          // diag(d) W [C][64]
+    static constexpr int kP = kWd + kFzC * kWS;          // P^T tiles [10][64 lanes][4], D-fragment order
     static constexpr int kBufHalves = kP + 10 * 256;
     static constexpr int kLamBytes = kFzC * 4;           // Lam [C] float, after the halves
     static constexpr int kBufBytes = kBufHalves * 2 + kLamBytes;
@@ -3634,7 +3637,6 @@ struct FzLds {
 // (Indexing a register packet through a pointer would push it to scratch.)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ inline uint32_t u4get(const u32x4 &p, int i) { return p[i]; }
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Value of x in lane `src` (wave-uniform source lane).
 __device__ inline float wave_read(float x, int src) {
@@ -3670,6 +3672,15 @@ __device__ inline bf16x4_t lds_b64(const bf16_t *p) { return *(const bf16x4_t *)
 __device__ inline bf16x8_t cat8(bf16x4_t x, bf16x4_t y) {
     return bf16x8_t{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 }
+// Four consecutive rows of one column through gfx950's transposing LDS read
+// (ds_read_b64_tr_b16): lane m of each 16-lane group supplies the address of
+// X[r + m / 4][c0 + 4 (m % 4)] (8 bytes) and receives X[r + e][c0 + m],
+// e = 0..3, where r may differ between the four groups.  The pointer is the
+// lane's own 8-byte source.
+__device__ inline bf16x4_t lds_tr4(const bf16_t *src) {
+    typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+    return __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)src));
+}
 // index of the lower-triangle score tile (s block sb <= query block tb)
 __device__ constexpr int tri(int sb, int tb) { return tb * (tb + 1) / 2 + sb; }
 
@@ -3702,16 +3713,14 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
 
     // ---- staging waves (threads 256..511, index u = tid - 256).  Roles:
     //   u in [0, DK):        one 8x8 block of K (tokens 8 (u % 8).., columns
-    //                        8 (u / 8)..), written as K rows and, transposed in
-    //                        registers, as K^T rows; and 8 packets of Q (packet
-    //                        e DK + u in row-major order: consecutive threads
-    //                        cover a token row)
+    //                        8 (u / 8)..), written as K rows; and 8 packets of
+    //                        Q (packet e DK + u in row-major order: consecutive
+    //                        threads cover a token row)
     //   u in [DK, DK+128):   x = u - DK; two whole waves.  Each thread stages one
     //                        4-token x 8-row block of W = beta . v / I_prior
-    //                        (tokens 4 (x%16).., rows 8 (x/16)..), written
-    //                        transposed as W^T and (diag(d) W)^T; both waves
-    //                        scan the gate (one token per lane) and the first
-    //                        writes Lam
+    //                        (tokens 4 (x/8).., rows 8 (x%8)..), written as W
+    //                        and diag(d) W rows; both waves scan the gate (one
+    //                        token per lane) and the first writes Lam
     // The block assignments put the 16 lanes of one LDS write pass on rows or
     // tokens that fall in distinct banks.
     //   u >= DK+128:         idle (d_k = 64)
@@ -3741,7 +3750,7 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
             for (int e = 0; e < 8; ++e)
                 pr[8 + e] = *(const u32x4 *)(a.q + row(t0 + e * (DK / kQPk) + tq0) * DK + qcol);
         } else if (u < DK + 128) {
-            const int x = u - DK, tok0 = 4 * (x % 16), i0 = ib0 + 8 * (x / 16);
+            const int x = u - DK, tok0 = 4 * (x / 8), i0 = ib0 + 8 * (x % 8);
             const bf16_t *bsrc = a.beta ? a.beta : a.v;    // no beta: replaced by 1.0 at the commit
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -3752,44 +3761,16 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
             pdt = __builtin_bit_cast(uint16_t, a.dt[row(t0 + lane)]);
         }
     };
-    // 8x8 transpose of bf16: out[c] holds element c of in[0..7]
-    auto transpose8 = [](const u32x4 (&in)[8], u32x4 (&out)[8]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int wd = c / 2;
-            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
-            out[c] = u32x4{__builtin_amdgcn_perm(u4get(in[1], wd), u4get(in[0], wd), sel),
-                                __builtin_amdgcn_perm(u4get(in[3], wd), u4get(in[2], wd), sel),
-                                __builtin_amdgcn_perm(u4get(in[5], wd), u4get(in[4], wd), sel),
-                                __builtin_amdgcn_perm(u4get(in[7], wd), u4get(in[6], wd), sel)};
-        }
-    };
-    // 4x8 -> 8x4 transpose of bf16: out[c] (two dwords) holds element c of in[0..3]
-    auto transpose4x8 = [](const u32x4 (&in)[4], u32x2 (&out)[8]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int wd = c / 2;
-            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-            out[c] = u32x2{__builtin_amdgcn_perm(u4get(in[1], wd), u4get(in[0], wd), sel),
-                           __builtin_amdgcn_perm(u4get(in[3], wd), u4get(in[2], wd), sel)};
-        }
-    };
     auto commit = [&](char *buf, int t0, const u32x4 *pr, uint32_t pdt) __attribute__((always_inline)) {
         bf16_t *hb = (bf16_t *)buf;
         float *lam = (float *)(buf + L::kBufHalves * 2);
         const u32x4 z = u32x4{0u, 0u, 0u, 0u};
         if (u < DK) {
-            const int tok0 = 8 * (u % 8), col = 8 * (u / 8);
+            const int tok0 = 8 * (u % 8);
             const int pcol = 8 * ((u / 8) ^ (u % 8));     // swizzled column block (rows tok0.. share r / 8)
-            u32x4 kin[8], kt[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                kin[e] = (t0 + tok0 + e < a.T) ? pr[e] : z;
-                *(u32x4 *)(hb + L::kK + (tok0 + e) * L::kQS + pcol) = kin[e];
-            }
-            transpose8(kin, kt);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) *(u32x4 *)(hb + L::kKt + (col + c) * L::kTS + tok0) = kt[c];
+            for (int e = 0; e < 8; ++e)
+                *(u32x4 *)(hb + L::kK + (tok0 + e) * L::kQS + pcol) = (t0 + tok0 + e < a.T) ? pr[e] : z;
             const int tq0 = u / kQPk, qcol = 8 * (u % kQPk);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -3802,8 +3783,7 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
             const float lam_l = wave_incl_scan((t0 + lane < a.T) ? -Ah * __uint_as_float(pdt << 16) : 0.f, lane);
             if (x < 64) lam[lane] = lam_l;
             const float dl = __expf(wave_read(lam_l, 63) - lam_l);   // e^(Lam_end - Lam_s)
-            const int tok0 = 4 * (x % 16), il0 = 8 * (x / 16);
-            u32x4 win[4], wdn[4];
+            const int tok0 = 4 * (x / 8), il0 = 8 * (x % 8);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float de = __shfl(dl, tok0 + e, 64);
@@ -3817,16 +3797,9 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
                     ww[pp] = pack_bf16(w0, w1);
                     wd[pp] = pack_bf16(w0 * de, w1 * de);
                 }
-                win[e] = u32x4{ww[0], ww[1], ww[2], ww[3]};
-                wdn[e] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+                *(u32x4 *)(hb + L::kW + (tok0 + e) * L::kWS + il0) = u32x4{ww[0], ww[1], ww[2], ww[3]};
+                *(u32x4 *)(hb + L::kWd + (tok0 + e) * L::kWS + il0) = u32x4{wd[0], wd[1], wd[2], wd[3]};
             }
-            u32x2 wt[8];
-            transpose4x8(win, wt);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) *(u32x2 *)(hb + L::kWt + (il0 + c) * L::kTS + tok0) = wt[c];
-            transpose4x8(wdn, wt);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) *(u32x2 *)(hb + L::kWdt + (il0 + c) * L::kTS + tok0) = wt[c];
         }
     };
 
@@ -3952,16 +3925,28 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
             }
             // (e) state: S^T = e^Lam_end S^T + K^T diag(d) W
             const float e_end = __expf(lam[kFzC - 1]);
+            // Operands with the token index along k, read transposed from the
+            // token-major arrays: lane (lg, lr) supplies row 8 lg + lr / 4 (+4)
+            // of its 32-token slice and columns 4 (lr % 4).. of its 16-column
+            // block, and receives 8 consecutive tokens of one column.
+            const int trow = 8 * lg + (lr >> 2), tcol = 4 * (lr & 3);
             bf16x8_t wd[2];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) wd[ks] = lds_b128(hb + L::kWdt + (16 * w + lr) * L::kTS + 32 * ks + 8 * lg);
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16_t *p = hb + L::kWd + (32 * ks + trow) * L::kWS + 16 * w + tcol;
+                wd[ks] = cat8(lds_tr4(p), lds_tr4(p + 4 * L::kWS));
+            }
 #pragma unroll
             for (int jb = 0; jb < DK / 16; ++jb) {
                 f32x4 acc = St[jb] * e_end;
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        lds_b128(hb + L::kKt + (16 * jb + lr) * L::kTS + 32 * ks + 8 * lg), wd[ks], acc, 0, 0, 0);
+                for (int ks = 0; ks < 2; ++ks) {
+                    // K^T fragment from the swizzled K rows (the 8 rows share r / 8)
+                    const int r = 32 * ks + trow, c = 16 * jb + tcol;
+                    const bf16_t *p = hb + L::kK + r * L::kQS + 8 * ((c >> 3) ^ ((r >> 3) & 7)) + (c & 7);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat8(lds_tr4(p), lds_tr4(p + 4 * L::kQS)), wd[ks],
+                                                                 acc, 0, 0, 0);
+                }
                 St[jb] = acc;
             }
         }
@@ -3976,14 +3961,17 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
             // (c) Y^T for value rows of wave w: intra-chunk W^T P^T + inter-chunk S Q^T e^Lam_t.
             // The k index (token s) of the intra product follows the P^T
             // fragments: slots 0-3 = s 4lg..4lg+3 of s block 2ks, slots 4-7 of block 2ks+1.
-            const bf16_t *wrow = hb + L::kWt + (16 * w + lr) * L::kTS + 4 * lg;
+            // W^T fragments, read transposed from the token-major W: lane (lg, lr)
+            // supplies token row 4 lg + lr / 4 (and 16 more) and value rows
+            // 16 w + 4 (lr % 4).., and receives tokens 4 lg.. of value row 16 w + lr
+            const bf16_t *wtr = hb + L::kW + (4 * lg + (lr >> 2)) * L::kWS + 16 * w + 4 * (lr & 3);
             const bf16x4_t zero4 = {(bf16_t)0.f, (bf16_t)0.f, (bf16_t)0.f, (bf16_t)0.f};
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
                 f32x4 yi = {0.f, 0.f, 0.f, 0.f}, ye = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks <= tb / 2; ++ks) {
-                    const bf16x8_t av = cat8(lds_b64(wrow + 32 * ks), lds_b64(wrow + 32 * ks + 16));
+                    const bf16x8_t av = cat8(lds_tr4(wtr + 32 * ks * L::kWS), lds_tr4(wtr + (32 * ks + 16) * L::kWS));
                     const bf16x8_t bv = cat8(ptile(tri(2 * ks, tb)), 2 * ks + 1 <= tb ? ptile(tri(2 * ks + 1 <= tb ? 2 * ks + 1 : 0, tb)) : zero4);
                     yi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, yi, 0, 0, 0);
                 }
