@@ -3662,10 +3662,13 @@ __device__ inline float wave_incl_scan(float x, int lane) {
 }
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Two floats to packed bf16 (round to nearest even) in one v_cvt_pk_bf16_f32;
+// converting them one at a time and merging the halves takes four instructions.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (bf16_t)lo) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (bf16_t)hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2_t));
 }
+__device__ inline bf16x4_t cvt4_bf16(f32x4 x) { return __builtin_convertvector(x, bf16x4_t); }
 
 __device__ inline bf16x8_t lds_b128(const bf16_t *p) { return *(const bf16x8_t *)p; }
 __device__ inline bf16x4_t lds_b64(const bf16_t *p) { return *(const bf16x4_t *)p; }
@@ -3738,96 +3741,100 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
     // past the end are clamped to T-1.  Every load takes the same branch-free
     // address form: per-load branches would split the loads into blocks whose
     // register reuse makes the wave wait for earlier loads.
-    auto load = [&](int t0, u32x4 *pr, uint32_t &pdt) __attribute__((always_inline)) {
-        const int tl = a.T - 1;
-        auto row = [&](int t) { return seq + (size_t)min(t, tl) * a.H; };
-        if (u < DK) {
-            const int tok0 = 8 * (u % 8), col = 8 * (u / 8);
+    // One lambda per role and no role test inside: each role's loop then has
+    // straight-line loads, which the compiler counts, so a commit waits only
+    // for the packets it uses.
+    auto row = [&](int t) { return seq + (size_t)min(t, a.T - 1) * a.H; };
+    auto load_k = [&](int t0) __attribute__((always_inline)) {
+        const int tok0 = 8 * (u % 8), col = 8 * (u / 8);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pr[e] = *(const u32x4 *)(a.k + row(t0 + tok0 + e) * DK + col);
-            const int tq0 = u / kQPk, qcol = 8 * (u % kQPk);
+        for (int e = 0; e < 8; ++e) pr[e] = *(const u32x4 *)(a.k + row(t0 + tok0 + e) * DK + col);
+        const int tq0 = u / kQPk, qcol = 8 * (u % kQPk);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                pr[8 + e] = *(const u32x4 *)(a.q + row(t0 + e * (DK / kQPk) + tq0) * DK + qcol);
-        } else if (u < DK + 128) {
-            const int x = u - DK, tok0 = 4 * (x / 8), i0 = ib0 + 8 * (x % 8);
-            const bf16_t *bsrc = a.beta ? a.beta : a.v;    // no beta: replaced by 1.0 at the commit
+        for (int e = 0; e < 8; ++e)
+            pr[8 + e] = *(const u32x4 *)(a.q + row(t0 + e * (DK / kQPk) + tq0) * DK + qcol);
+    };
+    // W role: x = u - DK; with d_k = 64 the role's third wave (x >= 128) loads
+    // the first wave's packets and stores nothing
+    const int wx = u - DK, wxl = wx & 127;
+    auto load_w = [&](int t0, u32x4 *p, uint32_t &d) __attribute__((always_inline)) {
+        const int tok0 = 4 * (wxl / 8), i0 = ib0 + 8 * (wxl % 8);
+        const bf16_t *bsrc = a.beta ? a.beta : a.v;    // no beta: replaced by 1.0 at the commit
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const size_t o = row(t0 + tok0 + e) * a.dv + i0;
-                pr[e] = *(const u32x4 *)(a.v + o);
-                pr[4 + e] = *(const u32x4 *)(bsrc + o);
-            }
-            pdt = __builtin_bit_cast(uint16_t, a.dt[row(t0 + lane)]);
+        for (int e = 0; e < 4; ++e) {
+            const size_t o = row(t0 + tok0 + e) * a.dv + i0;
+            p[e] = *(const u32x4 *)(a.v + o);
+            p[4 + e] = *(const u32x4 *)(bsrc + o);
+        }
+        d = __builtin_bit_cast(uint16_t, a.dt[row(t0 + lane)]);
+    };
+    auto commit_k = [&](char *buf, int t0) __attribute__((always_inline)) {
+        bf16_t *hb = (bf16_t *)buf;
+        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+        const int tok0 = 8 * (u % 8);
+        const int pcol = 8 * ((u / 8) ^ (u % 8));     // swizzled column block (rows tok0.. share r / 8)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            *(u32x4 *)(hb + L::kK + (tok0 + e) * L::kQS + pcol) = (t0 + tok0 + e < a.T) ? pr[e] : z;
+        const int tq0 = u / kQPk, qcol = 8 * (u % kQPk);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int tq = e * (DK / kQPk) + tq0;
+            *(u32x4 *)(hb + L::kQ + tq * L::kQS + qcol) = (t0 + tq < a.T) ? pr[8 + e] : z;
         }
     };
-    auto commit = [&](char *buf, int t0, const u32x4 *pr, uint32_t pdt) __attribute__((always_inline)) {
+    auto commit_w = [&](char *buf, int t0, const u32x4 *p, uint32_t d) __attribute__((always_inline)) {
         bf16_t *hb = (bf16_t *)buf;
         float *lam = (float *)(buf + L::kBufHalves * 2);
-        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-        if (u < DK) {
-            const int tok0 = 8 * (u % 8);
-            const int pcol = 8 * ((u / 8) ^ (u % 8));     // swizzled column block (rows tok0.. share r / 8)
+        // gate: Lam = inclusive prefix sum of -A dt over the chunk, lane = token
+        const float lam_l = wave_incl_scan((t0 + lane < a.T) ? -Ah * __uint_as_float(d << 16) : 0.f, lane);
+        if (wx < 64) lam[lane] = lam_l;
+        const float dl = __expf(wave_read(lam_l, 63) - lam_l);   // e^(Lam_end - Lam_s)
+        const int tok0 = 4 * (wxl / 8), il0 = 8 * (wxl % 8);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                *(u32x4 *)(hb + L::kK + (tok0 + e) * L::kQS + pcol) = (t0 + tok0 + e < a.T) ? pr[e] : z;
-            const int tq0 = u / kQPk, qcol = 8 * (u % kQPk);
+        for (int e = 0; e < 4; ++e) {
+            const float de = __shfl(dl, tok0 + e, 64);
+            const bool ok = t0 + tok0 + e < a.T;
+            uint32_t ww[4], wd[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int tq = e * (DK / kQPk) + tq0;
-                *(u32x4 *)(hb + L::kQ + tq * L::kQS + qcol) = (t0 + tq < a.T) ? pr[8 + e] : z;
+            for (int pp = 0; pp < 4; ++pp) {
+                const uint32_t vw = u4get(p[e], pp), bw = a.beta ? u4get(p[4 + e], pp) : 0x3f803f80u;
+                const float w0 = ok ? bf_lo(bw) * bf_lo(vw) * inv_ip : 0.f;
+                const float w1 = ok ? bf_hi(bw) * bf_hi(vw) * inv_ip : 0.f;
+                ww[pp] = pack_bf16(w0, w1);
+                wd[pp] = pack_bf16(w0 * de, w1 * de);
             }
-        } else if (u < DK + 128) {
-            const int x = u - DK;
-            // gate: Lam = inclusive prefix sum of -A dt over the chunk, lane = token
-            const float lam_l = wave_incl_scan((t0 + lane < a.T) ? -Ah * __uint_as_float(pdt << 16) : 0.f, lane);
-            if (x < 64) lam[lane] = lam_l;
-            const float dl = __expf(wave_read(lam_l, 63) - lam_l);   // e^(Lam_end - Lam_s)
-            const int tok0 = 4 * (x / 8), il0 = 8 * (x % 8);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float de = __shfl(dl, tok0 + e, 64);
-                const bool ok = t0 + tok0 + e < a.T;
-                uint32_t ww[4], wd[4];
-#pragma unroll
-                for (int pp = 0; pp < 4; ++pp) {
-                    const uint32_t vw = u4get(pr[e], pp), bw = a.beta ? u4get(pr[4 + e], pp) : 0x3f803f80u;
-                    const float w0 = ok ? bf_lo(bw) * bf_lo(vw) * inv_ip : 0.f;
-                    const float w1 = ok ? bf_hi(bw) * bf_hi(vw) * inv_ip : 0.f;
-                    ww[pp] = pack_bf16(w0, w1);
-                    wd[pp] = pack_bf16(w0 * de, w1 * de);
-                }
+            if (wx < 128) {
                 *(u32x4 *)(hb + L::kW + (tok0 + e) * L::kWS + il0) = u32x4{ww[0], ww[1], ww[2], ww[3]};
                 *(u32x4 *)(hb + L::kWd + (tok0 + e) * L::kWS + il0) = u32x4{wd[0], wd[1], wd[2], wd[3]};
             }
         }
     };
 
-    // Two phases per chunk, each closed by a barrier.  Phase A: the compute
-    // waves form the chunk's 10 decay-masked score tiles, 2-3 per wave, and
-    // share them through LDS, while the stagers stage chunk c+1 into buffer
-    // (c+1)&1 (not read during chunk c) and issue the loads of chunk c+2, which
-    // then have a whole chunk to arrive; the compute waves also update the
-    // state, keeping the previous one in bf16 for phase B.  Phase B: the
-    // compute waves form Y.  The two roles run separate loops with the same
-    // barriers, so that neither's registers stay reserved in the other's code.
-    // The K role loads chunk c+2 in phase A, right after staging c+1.  The
-    // W role stages chunk c+1 in phase A and loads chunk c+3 in phase B (its
-    // loads would otherwise queue behind the K role's and hold phase A up),
-    // alternating between two register sets.
     auto buf_of = [&](int c) { return lds + (c & 1) * L::kBufBytes; };
+    // The W role's packets of one register set, marked used before the other
+    // set's loads go out, so that the wait for them (loads two phases old)
+    // lands here and a commit never waits for loads issued a phase earlier.
+    auto w_ready = [&](const u32x4 *p, uint32_t d) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) asm volatile("" ::"v"(p[e].x), "v"(p[e].y), "v"(p[e].z), "v"(p[e].w));
+        asm volatile("" ::"v"(d));
+    };
+    // Every load batch is issued, for chunk min(c, nchunks - 1) (the surplus
+    // ones near the end reload the last chunk and are never committed): a
+    // batch under a branch is one the compiler cannot count, and it then waits
+    // for all outstanding loads at the next commit.
+    auto clampc = [&](int c) { return min(c, nchunks - 1) * kFzC; };
     if (stager && u < DK) {
         if (nchunks > 0) {
-            load(0, pr, pdt);
-            commit(lds, 0, pr, pdt);
-            if (nchunks > 1) load(kFzC, pr, pdt);
+            load_k(0);
+            commit_k(lds, 0);
+            load_k(clampc(1));
         }
         __syncthreads();
         for (int c = 0; c < nchunks; ++c) {
-            if (c + 1 < nchunks) {
-                commit(buf_of(c + 1), (c + 1) * kFzC, pr, pdt);
-                if (c + 2 < nchunks) load((c + 2) * kFzC, pr, pdt);
-            }
+            if (c + 1 < nchunks) commit_k(buf_of(c + 1), (c + 1) * kFzC);
+            load_k(clampc(c + 2));
             __syncthreads();
             __syncthreads();
         }
@@ -3835,21 +3842,24 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
     }
     if (stager) {
         if (nchunks > 0) {
-            load(0, pr, pdt);
-            commit(lds, 0, pr, pdt);
-            if (nchunks > 1) load(kFzC, pr2, pdt2);
-            if (nchunks > 2) load(2 * kFzC, pr, pdt);
+            load_w(0, pr, pdt);
+            commit_w(lds, 0, pr, pdt);
+            load_w(clampc(1), pr2, pdt2);
+            w_ready(pr2, pdt2);    // as in the loop: the loop head then never waits for pr
+            load_w(clampc(2), pr, pdt);
         }
         __syncthreads();
         for (int c = 0; c < nchunks; c += 2) {
-            if (c + 1 < nchunks) commit(buf_of(c + 1), (c + 1) * kFzC, pr2, pdt2);
+            if (c + 1 < nchunks) commit_w(buf_of(c + 1), (c + 1) * kFzC, pr2, pdt2);
             __syncthreads();
-            if (c + 3 < nchunks) load((c + 3) * kFzC, pr2, pdt2);
+            w_ready(pr, pdt);
+            load_w(clampc(c + 3), pr2, pdt2);
             __syncthreads();
             if (c + 1 >= nchunks) break;
-            if (c + 2 < nchunks) commit(buf_of(c + 2), (c + 2) * kFzC, pr, pdt);
+            if (c + 2 < nchunks) commit_w(buf_of(c + 2), (c + 2) * kFzC, pr, pdt);
             __syncthreads();
-            if (c + 4 < nchunks) load((c + 4) * kFzC, pr, pdt);
+            w_ready(pr2, pdt2);
+            load_w(clampc(c + 4), pr, pdt);
             __syncthreads();
         }
         return;
@@ -3906,23 +3916,17 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
             for (int n = 0; n < 3; ++n) {
                 const float lt = lam[16 * ttb[n] + lr];
                 const f32x4 ls = *(const f32x4 *)(lam + 16 * tsb[n] + 4 * lg);
-                bf16x4_t pt;
+                f32x4 pt;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const bool keep = tsb[n] < ttb[n] || 4 * lg + r <= lr;
-                    pt[r] = (bf16_t)(keep ? g3[n][r] * __expf(lt - ls[r]) : 0.f);
+                    pt[r] = keep ? g3[n][r] * __expf(lt - ls[r]) : 0.f;
                 }
-                *(bf16x4_t *)(pw + 256 * ti[n]) = pt;
+                *(bf16x4_t *)(pw + 256 * ti[n]) = cvt4_bf16(pt);
             }
             // the state before this chunk, as the bf16 A operand of S Q^T in phase B
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    sa[kk][r] = (bf16_t)St[2 * kk][r];
-                    sa[kk][4 + r] = (bf16_t)St[2 * kk + 1][r];
-                }
-            }
+            for (int kk = 0; kk < DK / 32; ++kk) sa[kk] = cat8(cvt4_bf16(St[2 * kk]), cvt4_bf16(St[2 * kk + 1]));
             // (e) state: S^T = e^Lam_end S^T + K^T diag(d) W
             const float e_end = __expf(lam[kFzC - 1]);
             // Operands with the token index along k, read transposed from the
@@ -3988,8 +3992,7 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) o[r] = fmaf(et, ye[r], yi[r]);
                     if (a.y_bf16) {
-                        const bf16x4_t ob = {(bf16_t)o[0], (bf16_t)o[1], (bf16_t)o[2], (bf16_t)o[3]};
-                        *(bf16x4_t *)((bf16_t *)a.y + yo) = ob;
+                        *(bf16x4_t *)((bf16_t *)a.y + yo) = cvt4_bf16(f32x4{o[0], o[1], o[2], o[3]});
                     } else {
                         *(f32x4 *)((float *)a.y + yo) = f32x4{o[0], o[1], o[2], o[3]};
                     }
