@@ -3811,6 +3811,19 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
         }
     };
 
+    // Two phases per chunk, each closed by a barrier.  Phase A: the compute
+    // waves form the chunk's 10 decay-masked score tiles, 2-3 per wave, and
+    // share them through LDS, while the stagers stage chunk c+1 into buffer
+    // (c+1)&1 (not read during chunk c); the compute waves also update the
+    // state, keeping the previous one in bf16 for phase B.  Phase B: the
+    // compute waves form Y.  The roles run separate loops with the same
+    // barriers, so that no role's registers stay reserved in another's code.
+    // The K role loads chunk c+2 in phase A, right after staging c+1.  The
+    // W role stages chunk c+1 in phase A and loads chunk c+3 in phase B (its
+    // loads would otherwise queue behind the K role's and hold phase A up),
+    // alternating between two register sets.  (Spreading both roles' work
+    // over all four staging waves was slower: the compute waves are the
+    // critical path, and two of them then share a SIMD with more staging.)
     auto buf_of = [&](int c) { return lds + (c & 1) * L::kBufBytes; };
     // The W role's packets of one register set, marked used before the other
     // set's loads go out, so that the wait for them (loads two phases old)
