@@ -539,8 +539,10 @@ def _frozen_ref(inp, mu0=None, vstar=False):
     return oracle.fwd_mamba2_limit(**args, mu0=mu0)
 
 
+# T = 200, 100, 64, 63, 1: 4 (ragged), 2 (ragged), 1, 1 (ragged) chunks of 64 and a single token;
+# the staging alternates two register sets per pair of chunks
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
-@pytest.mark.parametrize("T", [200, 64, 1])
+@pytest.mark.parametrize("T", [200, 100, 64, 63, 1])
 def test_frozen_matches_mamba2_limit_oracle(dk, dv, T):
     w = workloads.WORKLOADS[2].with_(B=2, H=3, dk=dk, dv=dv)
     _announce("frozen fwd", T=T, dk=dk, dv=dv)
