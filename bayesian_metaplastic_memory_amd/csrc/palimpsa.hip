@@ -77,14 +77,12 @@ template <typename T> struct io;
 // use, so that the widening (and the wait for the load) happens at the use
 // and not where the load is issued; bits 0 is 0.0 in both types.
 template <> struct io<float> {
-    static constexpr int kBytes = 4;
     __device__ static inline float to_f32(float x) { return x; }
     __device__ static inline float from_f32(float x) { return x; }
     __device__ static inline uint32_t bits(float x) { return __float_as_uint(x); }
     __device__ static inline float from_bits(uint32_t b) { return __uint_as_float(b); }
 };
 template <> struct io<bf16_t> {
-    static constexpr int kBytes = 2;
     __device__ static inline float to_f32(bf16_t x) { return (float)x; }
     __device__ static inline bf16_t from_f32(float x) { return (bf16_t)x; }  // RNE
     __device__ static inline uint32_t bits(bf16_t x) { return __builtin_bit_cast(uint16_t, x); }
@@ -1617,7 +1615,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(BwdArgs a) {
             }
         }
         // gradients of the start state: M_0 = I_0 mu_0
-        float gi_sum = 0.f;
 #pragma unroll
         for (int m = 0; m < LT::kNVec; ++m)
 #pragma unroll
@@ -4189,18 +4186,6 @@ __device__ inline size_t fragidx(int dv, int jb, int f, int lane) {
     return ((size_t)(jb * (dv / 32) + f) * 64 + lane) * 8;
 }
 
-// Widen 8 consecutive values of T at p (16-byte aligned for bf16, 32 for float).
-template <typename T> __device__ inline void load8(const T *p, float *o);
-template <> __device__ inline void load8<bf16_t>(const bf16_t *p, float *o) {
-    const u32x4 w = *(const u32x4 *)p;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { o[2 * i] = bf_lo(w[i]); o[2 * i + 1] = bf_hi(w[i]); }
-}
-template <> __device__ inline void load8<float>(const float *p, float *o) {
-    const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { o[i] = a[i]; o[4 + i] = b[i]; }
-}
 __device__ inline u32x4 pack8_bf16(const float *x) {
     return u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
 }

@@ -1,7 +1,6 @@
 """Host-side checks of the C ABI: the library loads, exports every declared
 symbol, and rejects invalid calls with the documented status codes before
 launching anything (no GPU needed: every call here fails validation)."""
-import ctypes
 import os
 import re
 import subprocess
