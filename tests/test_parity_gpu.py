@@ -556,6 +556,22 @@ def test_frozen_matches_mamba2_limit_oracle(dk, dv, T):
     assert_close("frozen muT", muT, mu_ref, 2e-2)
 
 
+def test_frozen_empty_sequence_copies_state_through():
+    """T = 0: no chunk runs; muT is mu0 bit for bit (zero without mu0)."""
+    w = workloads.WORKLOADS[2].with_(B=2, H=3)
+    _announce("frozen fwd T=0", B=2, H=3)
+    inp = workloads.make_inputs(w, T=0)
+    mu0, _ = workloads.random_state(2, 3, w.dv, w.dk, inp["I_prior"], seed=5)
+    g = to_device(inp, DEV)
+    y, muT = _pm().fwd_frozen(*gpu_args(g), mu0=mu0.to(DEV))
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (2, 0, 3, w.dv)
+    assert torch.equal(muT.cpu(), mu0)
+    y, muT = _pm().fwd_frozen(*gpu_args(g))
+    torch.cuda.synchronize()
+    assert torch.equal(muT.cpu(), torch.zeros_like(mu0))
+
+
 def test_frozen_vstar_input_and_bf16_output():
     w = workloads.WORKLOADS[2].with_(B=1, H=4)
     T = 300
