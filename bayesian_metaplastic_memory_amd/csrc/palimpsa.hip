@@ -3684,6 +3684,54 @@ __device__ inline bf16x4_t lds_tr4(const bf16_t *src) {
 // index of the lower-triangle score tile (s block sb <= query block tb)
 __device__ constexpr int tri(int sb, int tb) { return tb * (tb + 1) / 2 + sb; }
 
+// Score tiles of compute wave CW (s block, t block) as compile-time lists, so
+// that the wave loads each distinct Q and K fragment once per k step: waves 0
+// and 1 take three tiles, 2 and 3 two (4, 4, 3, 3 fragment reads per step).
+// The tiles go to LDS as the decay-masked P^T = G^T e^(Lam_t - Lam_s) / I_prior
+// (s <= t) in bf16, D-fragment order; the 1 / I_prior of w = beta v / I_prior
+// is applied here (as -ln I_prior in the exponent) rather than to every
+// element of W.
+template <int DK, int CW>
+__device__ inline void fz_scores(const bf16_t *hb, const float *lam, bf16_t *pw, int lane, float ln_inv_ip) {
+    using L = FzLds<DK>;
+    constexpr int NT = CW < 2 ? 3 : 2;
+    constexpr int kSb[4][3] = {{0, 0, 1}, {0, 1, 2}, {0, 1, 0}, {2, 3, 0}};
+    constexpr int kTb[4][3] = {{0, 1, 1}, {2, 2, 2}, {3, 3, 0}, {3, 3, 0}};
+    const int lr = lane & 15, lg = lane >> 4;
+    f32x4 g[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) g[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < DK / 32; ++kk) {
+        bf16x8_t qf[4], kf[4];
+#pragma unroll
+        for (int bl = 0; bl < 4; ++bl) {
+            bool uq = false, uk = false;
+#pragma unroll
+            for (int n = 0; n < NT; ++n) { uq |= kTb[CW][n] == bl; uk |= kSb[CW][n] == bl; }
+            if (uq) qf[bl] = lds_b128(hb + L::kQ + (16 * bl + lr) * L::kQS + 32 * kk + 8 * lg);
+            const int kr = 16 * bl + lr;
+            if (uk) kf[bl] = lds_b128(hb + L::kK + kr * L::kQS + 8 * ((4 * kk + lg) ^ ((kr >> 3) & 7)));
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+            g[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kSb[CW][n]], qf[kTb[CW][n]], g[n], 0, 0, 0);
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const int sb = kSb[CW][n], tb = kTb[CW][n];
+        const float lt = lam[16 * tb + lr] + ln_inv_ip;
+        const f32x4 ls = *(const f32x4 *)(lam + 16 * sb + 4 * lg);
+        f32x4 pt;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool keep = sb < tb || 4 * lg + r <= lr;
+            pt[r] = keep ? g[n][r] * __expf(lt - ls[r]) : 0.f;
+        }
+        *(bf16x4_t *)(pw + 256 * tri(sb, tb)) = cvt4_bf16(pt);
+    }
+}
+
 // Warp-specialised: waves 0-3 compute chunk c while waves 4-7 widen and
 // stage chunk c+1 into the other LDS buffer and load chunk c+2 from HBM; two
 // barriers per chunk.  The compute waves first form the 10 lower-triangle
@@ -3707,7 +3755,7 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
     const bool stager = wv >= 4;
     const int w = wv & 3;
     const int lr = lane & 15, lg = lane >> 4;                 // fragment row/col and lane group
-    const float Ah = a.A[h], inv_ip = 1.f / a.Ip[h];
+    const float Ah = a.A[h], inv_ip = 1.f / a.Ip[h], ln_inv_ip = -__logf(a.Ip[h]);
     const size_t seq = (size_t)b * a.T * a.H + h;            // [B, T, H] row of (b, 0, h)
     const int nchunks = (a.T + kFzC - 1) / kFzC;
 
@@ -3717,10 +3765,10 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
     //                        Q (packet e DK + u in row-major order: consecutive
     //                        threads cover a token row)
     //   u in [DK, DK+128):   x = u - DK; two whole waves.  Each thread stages one
-    //                        4-token x 8-row block of W = beta . v / I_prior
-    //                        (tokens 4 (x/8).., rows 8 (x%8)..), written as W
-    //                        and diag(d) W rows; both waves scan the gate (one
-    //                        token per lane) and the first writes Lam
+    //                        4-token x 8-row block of beta . v (tokens 4 (x/8)..,
+    //                        rows 8 (x%8)..), written as W = beta . v and as
+    //                        diag(d) W / I_prior rows; both waves scan the gate
+    //                        (one token per lane) and the first writes Lam
     // The block assignments put the 16 lanes of one LDS write pass on rows or
     // tokens that fall in distinct banks.
     //   u >= DK+128:         idle (d_k = 64)
@@ -3786,7 +3834,9 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
         // gate: Lam = inclusive prefix sum of -A dt over the chunk, lane = token
         const float lam_l = wave_incl_scan((t0 + lane < a.T) ? -Ah * __uint_as_float(d << 16) : 0.f, lane);
         if (wx < 64) lam[lane] = lam_l;
-        const float dl = __expf(wave_read(lam_l, 63) - lam_l);   // e^(Lam_end - Lam_s)
+        // e^(Lam_end - Lam_s) / I_prior: W is staged as beta . v, its 1 / I_prior
+        // applied here for diag(d) W and in the score tiles for the readout
+        const float dl = __expf(wave_read(lam_l, 63) - lam_l) * inv_ip;
         const int tok0 = 4 * (wxl / 8), il0 = 8 * (wxl % 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -3795,9 +3845,9 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
             uint32_t ww[4], wd[4];
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
-                const uint32_t vw = u4get(p[e], pp), bw = a.beta ? u4get(p[4 + e], pp) : 0x3f803f80u;
-                const float w0 = ok ? bf_lo(bw) * bf_lo(vw) * inv_ip : 0.f;
-                const float w1 = ok ? bf_hi(bw) * bf_hi(vw) * inv_ip : 0.f;
+                const uint32_t vw = ok ? u4get(p[e], pp) : 0u;     // past the end: w = 0
+                const uint32_t bw = a.beta ? u4get(p[4 + e], pp) : 0x3f803f80u;
+                const float w0 = bf_lo(bw) * bf_lo(vw), w1 = bf_hi(bw) * bf_hi(vw);
                 ww[pp] = pack_bf16(w0, w1);
                 wd[pp] = pack_bf16(w0 * de, w1 * de);
             }
@@ -3896,43 +3946,13 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
         const bf16_t *hb = (const bf16_t *)buf;
         const float *lam = (const float *)(buf + L::kBufHalves * 2);
         {
-            // (a) scores G^T[s][t] = k_s . q_t of this wave's tiles (tri index
-            // 0-2, 3-5, 6-7, 8-9 for waves 0-3; waves 2 and 3 form their last
-            // tile twice so that all four run the same straight-line code)
-            const int i0 = w < 2 ? 3 * w : 2 * w + 2;
-            int ti[3], tsb[3], ttb[3];
-#pragma unroll
-            for (int n = 0; n < 3; ++n) {
-                ti[n] = i0 + (n < 2 || w < 2 ? n : 1);
-                ttb[n] = ti[n] >= 6 ? 3 : ti[n] >= 3 ? 2 : ti[n] >= 1 ? 1 : 0;
-                tsb[n] = ti[n] - ttb[n] * (ttb[n] + 1) / 2;
-            }
-            f32x4 g3[3];
-#pragma unroll
-            for (int n = 0; n < 3; ++n) g3[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-#pragma unroll
-                for (int n = 0; n < 3; ++n) {
-                    const int kr = 16 * tsb[n] + lr;
-                    const bf16x8_t qf = lds_b128(hb + L::kQ + (16 * ttb[n] + lr) * L::kQS + 32 * kk + 8 * lg);
-                    const bf16x8_t kf = lds_b128(hb + L::kK + kr * L::kQS + 8 * ((4 * kk + lg) ^ ((kr >> 3) & 7)));
-                    g3[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf, g3[n], 0, 0, 0);
-                }
-            }
-            // decay and causal mask: P^T[s][t] = G^T[s][t] e^(Lam_t - Lam_s) for s <= t, as bf16
-            bf16_t *pw = (bf16_t *)bufw + L::kP + 4 * lane;
-#pragma unroll
-            for (int n = 0; n < 3; ++n) {
-                const float lt = lam[16 * ttb[n] + lr];
-                const f32x4 ls = *(const f32x4 *)(lam + 16 * tsb[n] + 4 * lg);
-                f32x4 pt;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool keep = tsb[n] < ttb[n] || 4 * lg + r <= lr;
-                    pt[r] = keep ? g3[n][r] * __expf(lt - ls[r]) : 0.f;
-                }
-                *(bf16x4_t *)(pw + 256 * ti[n]) = cvt4_bf16(pt);
+            // (a) scores G^T[s][t] = k_s . q_t of this wave's tiles, decay-masked, to LDS
+            bf16_t *pw_ = (bf16_t *)bufw + L::kP + 4 * lane;
+            switch (w) {
+            case 0: fz_scores<DK, 0>(hb, lam, pw_, lane, ln_inv_ip); break;
+            case 1: fz_scores<DK, 1>(hb, lam, pw_, lane, ln_inv_ip); break;
+            case 2: fz_scores<DK, 2>(hb, lam, pw_, lane, ln_inv_ip); break;
+            default: fz_scores<DK, 3>(hb, lam, pw_, lane, ln_inv_ip); break;
             }
             // the state before this chunk, as the bf16 A operand of S Q^T in phase B
 #pragma unroll
