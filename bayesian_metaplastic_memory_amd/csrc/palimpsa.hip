@@ -3970,19 +3970,20 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
                 const bf16_t *p = hb + L::kWd + (32 * ks + trow) * L::kWS + 16 * w + tcol;
                 wd[ks] = cat8(lds_tr4(p), lds_tr4(p + 4 * L::kWS));
             }
+            // k step outer: the DK/16 key blocks' products are independent, so
+            // that many are in flight between the two dependent steps
 #pragma unroll
-            for (int jb = 0; jb < DK / 16; ++jb) {
-                f32x4 acc = St[jb] * e_end;
+            for (int jb = 0; jb < DK / 16; ++jb) St[jb] = St[jb] * e_end;
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int jb = 0; jb < DK / 16; ++jb) {
                     // K^T fragment from the swizzled K rows (the 8 rows share r / 8)
                     const int r = 32 * ks + trow, c = 16 * jb + tcol;
                     const bf16_t *p = hb + L::kK + r * L::kQS + 8 * ((c >> 3) ^ ((r >> 3) & 7)) + (c & 7);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat8(lds_tr4(p), lds_tr4(p + 4 * L::kQS)), wd[ks],
-                                                                 acc, 0, 0, 0);
+                    St[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat8(lds_tr4(p), lds_tr4(p + 4 * L::kQS)), wd[ks],
+                                                                    St[jb], 0, 0, 0);
                 }
-                St[jb] = acc;
-            }
         }
         __syncthreads();
         {
@@ -4000,27 +4001,41 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
             // 16 w + 4 (lr % 4).., and receives tokens 4 lg.. of value row 16 w + lr
             const bf16_t *wtr = hb + L::kW + (4 * lg + (lr >> 2)) * L::kWS + 16 * w + 4 * (lr & 3);
             const bf16x4_t zero4 = {(bf16_t)0.f, (bf16_t)0.f, (bf16_t)0.f, (bf16_t)0.f};
+            // The two W^T fragments serve every query block; the four blocks'
+            // inter-chunk chains run interleaved (k step outer), so that four
+            // independent products are in flight instead of one chain of four.
+            bf16x8_t av[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                av[ks] = cat8(lds_tr4(wtr + 32 * ks * L::kWS), lds_tr4(wtr + (32 * ks + 16) * L::kWS));
+            f32x4 yi[4], ye[4];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                f32x4 yi = {0.f, 0.f, 0.f, 0.f}, ye = {0.f, 0.f, 0.f, 0.f};
+                yi[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                ye[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks <= tb / 2; ++ks) {
-                    const bf16x8_t av = cat8(lds_tr4(wtr + 32 * ks * L::kWS), lds_tr4(wtr + (32 * ks + 16) * L::kWS));
                     const bf16x8_t bv = cat8(ptile(tri(2 * ks, tb)), 2 * ks + 1 <= tb ? ptile(tri(2 * ks + 1 <= tb ? 2 * ks + 1 : 0, tb)) : zero4);
-                    yi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, yi, 0, 0, 0);
+                    yi[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], bv, yi[tb], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk)
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const bf16_t *qrow = hb + L::kQ + (16 * tb + lr) * L::kQS + 32 * kk + 4 * lg;
+                    ye[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[kk], cat8(lds_b64(qrow), lds_b64(qrow + 16)),
+                                                                    ye[tb], 0, 0, 0);
                 }
 #pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk) {
-                    const bf16_t *qrow = hb + L::kQ + (16 * tb + lr) * L::kQS + 32 * kk + 4 * lg;
-                    ye = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[kk], cat8(lds_b64(qrow), lds_b64(qrow + 16)), ye, 0, 0, 0);
-                }
+            for (int tb = 0; tb < 4; ++tb) {
                 const int t = 16 * tb + lr;
                 const float et = __expf(lam_t[tb]);
                 if (t0 + t < a.T) {
                     const size_t yo = (seq + (size_t)(t0 + t) * a.H) * a.dv + ib0 + 16 * w + 4 * lg;
                     float o[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) o[r] = fmaf(et, ye[r], yi[r]);
+                    for (int r = 0; r < 4; ++r) o[r] = fmaf(et, ye[tb][r], yi[tb][r]);
                     if (a.y_bf16) {
                         *(bf16x4_t *)((bf16_t *)a.y + yo) = cvt4_bf16(f32x4{o[0], o[1], o[2], o[3]});
                     } else {
