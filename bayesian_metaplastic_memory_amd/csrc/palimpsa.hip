@@ -3627,7 +3627,12 @@ struct FzLds {
     static constexpr int kBufHalves = kP + 10 * 256;
     static constexpr int kLamBytes = kFzC * 4;           // Lam [C] float, after the halves
     static constexpr int kBufBytes = kBufHalves * 2 + kLamBytes;
-    static constexpr int kTotal = 2 * kBufBytes;
+    // Two y tiles (chunk c in tile c&1), [C tokens][64 rows] in the output
+    // type, rows 16 bytes longer than the data (144 or 272 bytes) so that the
+    // 16 tokens of a compute wave's fragment write fall in distinct banks.
+    static constexpr int kY = 2 * kBufBytes;
+    static constexpr int kYTile = kFzC * (kFzRows * 4 + 16);
+    static constexpr int kTotal = kY + 2 * kYTile;
 };
 
 // Dword i of a 16-byte packet, and the bf16 in its low / high half as float.
@@ -3758,6 +3763,7 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
     const float Ah = a.A[h], inv_ip = 1.f / a.Ip[h], ln_inv_ip = -__logf(a.Ip[h]);
     const size_t seq = (size_t)b * a.T * a.H + h;            // [B, T, H] row of (b, 0, h)
     const int nchunks = (a.T + kFzC - 1) / kFzC;
+    const int yesz = a.y_bf16 ? 2 : 4, yrow = 64 * yesz + 16;  // y element and LDS row bytes
 
     // ---- staging waves (threads 256..511, index u = tid - 256).  Roles:
     //   u in [0, DK):        one 8x8 block of K (tokens 8 (u % 8).., columns
@@ -3886,6 +3892,18 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
     // for all outstanding loads at the next commit.
     auto clampc = [&](int c) { return min(c, nchunks - 1) * kFzC; };
     if (stager && u < DK) {
+        // y of chunk c (complete after chunk c's phase B) from its LDS tile to
+        // HBM in 16-byte packets, whole output rows per group of threads
+        auto write_y = [&](int c) __attribute__((always_inline)) {
+            const int t0 = c * kFzC, ppr = 64 * yesz / 16;           // packets per token row
+            const char *yt = lds + L::kY + (c & 1) * L::kYTile;
+            for (int p = u; p < kFzC * ppr; p += DK) {
+                const int t = p / ppr, col = 16 * (p % ppr);
+                if (t0 + t < a.T)
+                    *(u32x4 *)((char *)a.y + ((seq + (size_t)(t0 + t) * a.H) * a.dv + ib0) * yesz + col) =
+                        *(const u32x4 *)(yt + t * yrow + col);
+            }
+        };
         if (nchunks > 0) {
             load_k(0);
             commit_k(lds, 0);
@@ -3896,8 +3914,10 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
             if (c + 1 < nchunks) commit_k(buf_of(c + 1), (c + 1) * kFzC);
             load_k(clampc(c + 2));
             __syncthreads();
+            if (c > 0) write_y(c - 1);      // phase B: the compute waves fill the other tile
             __syncthreads();
         }
+        if (nchunks > 0) write_y(nchunks - 1);
         return;
     }
     if (stager) {
@@ -4027,21 +4047,18 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
                     ye[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[kk], cat8(lds_b64(qrow), lds_b64(qrow + 16)),
                                                                     ye[tb], 0, 0, 0);
                 }
+            // y of the wave's rows into the chunk's LDS tile; the K-role stagers
+            // write it out during the next chunk's phase B as whole rows (a
+            // fragment store scatters 8 or 16 bytes per lane over 16 token rows)
+            char *yt = lds + L::kY + (c & 1) * L::kYTile + (4 * lg + 16 * w) * yesz;
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
                 const int t = 16 * tb + lr;
                 const float et = __expf(lam_t[tb]);
-                if (t0 + t < a.T) {
-                    const size_t yo = (seq + (size_t)(t0 + t) * a.H) * a.dv + ib0 + 16 * w + 4 * lg;
-                    float o[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) o[r] = fmaf(et, ye[tb][r], yi[tb][r]);
-                    if (a.y_bf16) {
-                        *(bf16x4_t *)((bf16_t *)a.y + yo) = cvt4_bf16(f32x4{o[0], o[1], o[2], o[3]});
-                    } else {
-                        *(f32x4 *)((float *)a.y + yo) = f32x4{o[0], o[1], o[2], o[3]};
-                    }
-                }
+                const f32x4 o = {fmaf(et, ye[tb][0], yi[tb][0]), fmaf(et, ye[tb][1], yi[tb][1]),
+                                 fmaf(et, ye[tb][2], yi[tb][2]), fmaf(et, ye[tb][3], yi[tb][3])};
+                if (a.y_bf16) *(bf16x4_t *)(yt + t * yrow) = cvt4_bf16(o);
+                else *(f32x4 *)(yt + t * yrow) = o;
             }
         }
         __syncthreads();
