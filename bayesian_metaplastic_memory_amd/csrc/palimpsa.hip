@@ -4340,38 +4340,45 @@ __device__ inline void fzb_stage(const FzbArgs &a, bf16_t *hb, size_t seq, int t
 }
 
 // The chunk-boundary states and adjoints, one workgroup per (b, h, 64 value
-// rows) and direction, walking the chunks in order: the first half of the grid
+// rows, half of the key channels) and direction, walking the chunks in order
+// (the chain of a chunk step is short, so more and smaller walks overlap
+// better on a CU; the key halves of a row block read the same w or gy, from
+// L2): the first half of the grid
 // runs the state forward, S_0(c+1) = e^{Lam_c} S_0(c) + sum_s e^{Lam_c - L_s} w_s k_s^T
 // from mu0, writing S_0(c)^T; the second half runs the adjoint backward,
 // G_E(c-1) = e^{Lam_c} G_E(c) + sum_t e^{L_t} gy_t q_t^T from gmuT, writing G_E(c)^T
 // and (through LDS) G_E(c), and finally gmu0 = G_E(-1).  The running matrix stays
 // in fp32 MFMA accumulators: wave w owns rows 16 w.. of the workgroup's 64 and
-// all DK key channels.  Each chunk's inputs are loaded into registers while the
+// its KJ key channels.  Each chunk's inputs are loaded into registers while the
 // chunk before it computes.
+constexpr int kFzsKS = 2;                                 // key-channel splits of the state walk
 template <int DK, int DV>
 struct FzsLds {
-    static constexpr int kRK = DK + 8, kRW = 64 + 8;     // row strides (bf16)
-    static constexpr int kK = 0;                          // K or Q [64 tokens][DK]
+    static constexpr int KJ = DK / kFzsKS;                // key channels per workgroup
+    static constexpr int kRK = KJ + 8, kRW = 64 + 8;     // row strides (bf16)
+    static constexpr int kK = 0;                          // K or Q, the workgroup's channels [64 tokens][KJ]
     static constexpr int kW = kK + kFbC * kRK;            // w or gy, the workgroup's rows [64 tokens][64]
-    static constexpr int kT = kW + kFbC * kRW;            // G_E transpose tile [64 rows][DK]
+    static constexpr int kT = kW + kFbC * kRW;            // G_E transpose tile [64 rows][KJ]
     static constexpr int kBytes = (kT + 64 * kRK) * 2;
 };
 
 template <int DK, int DV, typename TG>
 __global__ __launch_bounds__(256) void fzb_state_kernel(FzbArgs a) {
     using L = FzsLds<DK, DV>;
+    constexpr int KJ = L::KJ;
+    static_assert(KJ % 32 == 0 && kFbC * KJ / 8 % 256 == 0, "key channels per state walk");
     constexpr int RBH = DV / 64;                          // row blocks per head
-    constexpr int NQ = kFbC * DK / 8 / 256;               // 16-byte packets of K or Q per thread
+    constexpr int NQ = kFbC * KJ / 8 / 256;               // 16-byte packets of K or Q per thread
     constexpr int kGP = sizeof(TG) / 2;                   // 16-byte packets per 8 values of gy
     extern __shared__ float lds_f[];
     bf16_t *hb = (bf16_t *)lds_f;
-    const int n_half = a.B * a.H * RBH;
+    const int n_half = a.B * a.H * RBH * kFzsKS;
     int wg = blockIdx.x;
     const bool adj = wg >= n_half;                        // second half of the grid: the adjoint
     if (adj) wg -= n_half;
-    // the row blocks of a head read the same keys or queries: keep them on one XCD
+    // the blocks of a head read the same keys or queries and rows: keep them on one XCD
     if (n_half % 8 == 0) wg = (wg % 8) * (n_half / 8) + wg / 8;
-    const int bh = wg / RBH, i0 = 64 * (wg % RBH);
+    const int bh = wg / (RBH * kFzsKS), i0 = 64 * (wg / kFzsKS % RBH), j0 = KJ * (wg % kFzsKS);
     const int b = bh / a.H, h = bh % a.H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int m = lane & 15, g = lane >> 4;
@@ -4380,15 +4387,15 @@ __global__ __launch_bounds__(256) void fzb_state_kernel(FzbArgs a) {
     const int nc = a.nc, tl = a.T - 1;
     const size_t st = (size_t)bh * DV * DK;
     const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-    // the running matrix, D layout: lane holds rows i0 + 16 w + 4 g + r of key channel 16 jb + m
-    f32x4 S[DK / 16];
+    // the running matrix, D layout: lane holds rows i0 + 16 w + 4 g + r of key channel j0 + 16 jb + m
+    f32x4 S[KJ / 16];
     {
         const float *init = adj ? a.gmuT : a.mu0;
 #pragma unroll
-        for (int jb = 0; jb < DK / 16; ++jb)
+        for (int jb = 0; jb < KJ / 16; ++jb)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                S[jb][r] = init ? init[st + (size_t)(i0 + 16 * w + 4 * g + r) * DK + 16 * jb + m] : 0.f;
+                S[jb][r] = init ? init[st + (size_t)(i0 + 16 * w + 4 * g + r) * DK + j0 + 16 * jb + m] : 0.f;
     }
     // prefetch registers, two chunks' worth: K or Q packets, and per row packet
     // two 16-byte words, (v, beta) for the state or gy (bf16: one word, fp32: two)
@@ -4410,8 +4417,8 @@ __global__ __launch_bounds__(256) void fzb_state_kernel(FzbArgs a) {
         pd = fzb_dt_bits(a, seq, t0, lane);
 #pragma unroll
         for (int n = 0; n < NQ; ++n) {
-            const int p = tid + 256 * n, t = p / (DK / 8), col = 8 * (p % (DK / 8));
-            const size_t o = (seq + (size_t)min(t0 + t, tl) * a.H) * DK + col;
+            const int p = tid + 256 * n, t = p / (KJ / 8), col = 8 * (p % (KJ / 8));
+            const size_t o = (seq + (size_t)min(t0 + t, tl) * a.H) * DK + j0 + col;
             pk[n] = *(const u32x4 *)(kq_base + o * sizeof(bf16_t));
         }
 #pragma unroll
@@ -4427,7 +4434,7 @@ __global__ __launch_bounds__(256) void fzb_state_kernel(FzbArgs a) {
         const int t0 = c * kFbC;
 #pragma unroll
         for (int n = 0; n < NQ; ++n) {
-            const int p = tid + 256 * n, t = p / (DK / 8), col = 8 * (p % (DK / 8));
+            const int p = tid + 256 * n, t = p / (KJ / 8), col = 8 * (p % (KJ / 8));
             *(u32x4 *)(hb + L::kK + t * L::kRK + col) = (t0 + t < a.T) ? pk[n] : z;
         }
 #pragma unroll
@@ -4480,16 +4487,16 @@ __global__ __launch_bounds__(256) void fzb_state_kernel(FzbArgs a) {
             bf16_t *dst = (adj ? a.gT : a.sT) + cb * DK * DV;
             const int f = i0 / 32 + (w >> 1), fl = 16 * (2 * (w & 1) + (g >> 1)) + m;
 #pragma unroll
-            for (int jb = 0; jb < DK / 16; jb += 2) {
+            for (int jb = 0; jb < KJ / 16; jb += 2) {
                 const uint2 p0 = pack4_bf16(S[jb]), p1 = pack4_bf16(S[jb + 1]);
                 const auto x = __builtin_amdgcn_permlane16_swap(p0.x, p1.x, false, false);
                 const auto y = __builtin_amdgcn_permlane16_swap(p0.y, p1.y, false, false);
-                *(uint4 *)(dst + fragidx(DV, jb + (g & 1), f, fl)) = make_uint4(x[0], y[0], x[1], y[1]);
+                *(uint4 *)(dst + fragidx(DV, j0 / 16 + jb + (g & 1), f, fl)) = make_uint4(x[0], y[0], x[1], y[1]);
             }
             if (adj) {
                 // G_E(c) row-major: through LDS, rows of the workgroup's 64
 #pragma unroll
-                for (int jb = 0; jb < DK / 16; ++jb)
+                for (int jb = 0; jb < KJ / 16; ++jb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         hb[L::kT + (16 * w + 4 * g + r) * L::kRK + 16 * jb + m] = (bf16_t)S[jb][r];
@@ -4500,7 +4507,7 @@ __global__ __launch_bounds__(256) void fzb_state_kernel(FzbArgs a) {
         const bf16x8_t a0 = lds_trfrag(hb + L::kW, L::kRW, 0, 16 * w, lane);
         const bf16x8_t a1 = lds_trfrag(hb + L::kW, L::kRW, 32, 16 * w, lane);
 #pragma unroll
-        for (int jb = 0; jb < DK / 16; ++jb) {
+        for (int jb = 0; jb < KJ / 16; ++jb) {
             f32x4 x = S[jb] * e;
             x = mfma16(a0, lds_trfrag(hb + L::kK, L::kRK, 0, 16 * jb, lane), x);
             S[jb] = mfma16(a1, lds_trfrag(hb + L::kK, L::kRK, 32, 16 * jb, lane), x);
@@ -4512,9 +4519,9 @@ __global__ __launch_bounds__(256) void fzb_state_kernel(FzbArgs a) {
         if (adj) {
             __syncthreads();
             bf16_t *gep = a.ge + cb * DV * DK;
-            for (int p = tid; p < 64 * DK / 8; p += 256) {
-                const int r = p / (DK / 8), col = 8 * (p % (DK / 8));
-                *(u32x4 *)(gep + (size_t)(i0 + r) * DK + col) = *(const u32x4 *)(hb + L::kT + r * L::kRK + col);
+            for (int p = tid; p < 64 * KJ / 8; p += 256) {
+                const int r = p / (KJ / 8), col = 8 * (p % (KJ / 8));
+                *(u32x4 *)(gep + (size_t)(i0 + r) * DK + j0 + col) = *(const u32x4 *)(hb + L::kT + r * L::kRK + col);
             }
         }
     };
@@ -4526,9 +4533,9 @@ __global__ __launch_bounds__(256) void fzb_state_kernel(FzbArgs a) {
     }
     if (adj && a.gmu0) {
 #pragma unroll
-        for (int jb = 0; jb < DK / 16; ++jb)
+        for (int jb = 0; jb < KJ / 16; ++jb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) a.gmu0[st + (size_t)(i0 + 16 * w + 4 * g + r) * DK + 16 * jb + m] = S[jb][r];
+            for (int r = 0; r < 4; ++r) a.gmu0[st + (size_t)(i0 + 16 * w + 4 * g + r) * DK + j0 + 16 * jb + m] = S[jb][r];
     }
 }
 
@@ -5374,7 +5381,7 @@ palimpsa_status launch_fzb(const FzbArgs &a, hipStream_t s) {
     (void)hipGetLastError();
     {
         using LS = FzsLds<DK, DV>;
-        hipLaunchKernelGGL((fzb_state_kernel<DK, DV, TG>), dim3((unsigned)(2 * (size_t)a.B * a.H * (DV / 64))), dim3(256),
+        hipLaunchKernelGGL((fzb_state_kernel<DK, DV, TG>), dim3((unsigned)(2 * (size_t)a.B * a.H * (DV / 64) * kFzsKS)), dim3(256),
                            LS::kBytes, s, a);
     }
     if (bhc > 0) {
