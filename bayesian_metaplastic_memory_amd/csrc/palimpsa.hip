@@ -3866,17 +3866,20 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
 
     // Two phases per chunk, each closed by a barrier.  Phase A: the compute
     // waves form the chunk's 10 decay-masked score tiles, 2-3 per wave, and
-    // share them through LDS, while the stagers stage chunk c+1 into buffer
-    // (c+1)&1 (not read during chunk c); the compute waves also update the
-    // state, keeping the previous one in bf16 for phase B.  Phase B: the
-    // compute waves form Y.  The roles run separate loops with the same
-    // barriers, so that no role's registers stay reserved in another's code.
-    // The K role loads chunk c+2 in phase A, right after staging c+1.  The
-    // W role stages chunk c+1 in phase A and loads chunk c+3 in phase B (its
-    // loads would otherwise queue behind the K role's and hold phase A up),
-    // alternating between two register sets.  (Spreading both roles' work
-    // over all four staging waves was slower: the compute waves are the
-    // critical path, and two of them then share a SIMD with more staging.)
+    // share them through LDS; they also update the state, keeping the
+    // previous one in bf16 for phase B.  Phase B: the compute waves form Y.
+    // The stagers fill buffer (c+1)&1 (not read during chunk c) with chunk
+    // c+1: the W role in phase A, the K role in phase B, so that each phase
+    // carries about half of the chunk's LDS traffic (phase A's score and K^T
+    // reads are the larger share; the K and Q writes are twice the W ones).
+    // The roles run separate loops with the same barriers, so that no role's
+    // registers stay reserved in another's code.  The K role copies y of
+    // chunk c-1 out in phase A, then stages c+1 and loads c+2 in phase B
+    // (loading c+2 in phase A instead, from a second register set, measured
+    // no faster).  The W role loads chunk c+3 in phase B, alternating between
+    // two register sets.  (Spreading both roles' work over all four staging
+    // waves was slower: the compute waves are the critical path, and two of
+    // them then share a SIMD with more staging.)
     auto buf_of = [&](int c) { return lds + (c & 1) * L::kBufBytes; };
     // The W role's packets of one register set, marked used before the other
     // set's loads go out, so that the wait for them (loads two phases old)
@@ -3911,10 +3914,12 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
         }
         __syncthreads();
         for (int c = 0; c < nchunks; ++c) {
+            // phase A: y of chunk c-1 out (its tile is next written in phase B of c+1)
+            if (c > 0) write_y(c - 1);
+            __syncthreads();
+            // phase B: chunk c+1 into the other buffer, whose last reads were in chunk c-1
             if (c + 1 < nchunks) commit_k(buf_of(c + 1), (c + 1) * kFzC);
             load_k(clampc(c + 2));
-            __syncthreads();
-            if (c > 0) write_y(c - 1);      // phase B: the compute waves fill the other tile
             __syncthreads();
         }
         if (nchunks > 0) write_y(nchunks - 1);
@@ -4048,7 +4053,7 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
                                                                     ye[tb], 0, 0, 0);
                 }
             // y of the wave's rows into the chunk's LDS tile; the K-role stagers
-            // write it out during the next chunk's phase B as whole rows (a
+            // write it out during the next chunk's phase A as whole rows (a
             // fragment store scatters 8 or 16 bytes per lane over 16 token rows)
             char *yt = lds + L::kY + (c & 1) * L::kYTile + (4 * lg + 16 * w) * yesz;
 #pragma unroll
