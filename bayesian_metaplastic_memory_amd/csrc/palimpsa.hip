@@ -3778,8 +3778,9 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
     // The block assignments put the 16 lanes of one LDS write pass on rows or
     // tokens that fall in distinct banks.
     //   u >= DK+128:         idle (d_k = 64)
-    // Loads read a valid row (clamped to T-1); tokens past the end are zeroed
-    // when written (q = k = w = 0, dt = 0: no effect on y or the state).
+    // Loads read a valid row (clamped to T-1); past the end of the sequence
+    // q = k = 0, dt = 0 and diag(d) W = 0 are staged (no effect on y or the
+    // state; W keeps the last token's values, which meet only masked scores).
     const int u = tid - 256;
     constexpr int kQPk = DK / 8;            // 16-byte packets per Q row
     // 16-byte packets of this thread's role: the K role stages one chunk
@@ -3841,17 +3842,19 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
         const float lam_l = wave_incl_scan((t0 + lane < a.T) ? -Ah * __uint_as_float(d << 16) : 0.f, lane);
         if (wx < 64) lam[lane] = lam_l;
         // e^(Lam_end - Lam_s) / I_prior: W is staged as beta . v, its 1 / I_prior
-        // applied here for diag(d) W and in the score tiles for the readout
-        const float dl = __expf(wave_read(lam_l, 63) - lam_l) * inv_ip;
+        // applied here for diag(d) W and in the score tiles for the readout.
+        // Past the end of the sequence the weight is 0, so diag(d) W is 0
+        // there; W itself keeps the (finite) values of the clamped last token,
+        // which only meet score entries of token pairs s > t, masked to 0.
+        const float dl = (t0 + lane < a.T) ? __expf(wave_read(lam_l, 63) - lam_l) * inv_ip : 0.f;
         const int tok0 = 4 * (wxl / 8), il0 = 8 * (wxl % 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float de = __shfl(dl, tok0 + e, 64);
-            const bool ok = t0 + tok0 + e < a.T;
             uint32_t ww[4], wd[4];
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
-                const uint32_t vw = ok ? u4get(p[e], pp) : 0u;     // past the end: w = 0
+                const uint32_t vw = u4get(p[e], pp);
                 const uint32_t bw = a.beta ? u4get(p[4 + e], pp) : 0x3f803f80u;
                 const float w0 = bf_lo(bw) * bf_lo(vw), w1 = bf_hi(bw) * bf_hi(vw);
                 ww[pp] = pack_bf16(w0, w1);
