@@ -3699,9 +3699,12 @@ __device__ constexpr int tri(int sb, int tb) { return tb * (tb + 1) / 2 + sb; }
 template <int DK, int CW>
 __device__ inline void fz_scores(const bf16_t *hb, const float *lam, bf16_t *pw, int lane, float ln_inv_ip) {
     using L = FzLds<DK>;
-    constexpr int NT = CW < 2 ? 3 : 2;
-    constexpr int kSb[4][3] = {{0, 0, 1}, {0, 1, 2}, {0, 1, 0}, {2, 3, 0}};
-    constexpr int kTb[4][3] = {{0, 1, 1}, {2, 2, 2}, {3, 3, 0}, {3, 3, 0}};
+    // 4, 3, 2, 1 tiles: waves 0 and 1 share their SIMDs with the K role,
+    // whose phase A work (the y copy) is light, waves 2 and 3 with the W role's
+    // commit; Q and K fragments read per k step: 4, 4, 3, 2
+    constexpr int NT = 4 - CW;
+    constexpr int kSb[4][4] = {{0, 1, 0, 1}, {0, 0, 1, 0}, {2, 2, 0, 0}, {3, 0, 0, 0}};
+    constexpr int kTb[4][4] = {{2, 2, 3, 3}, {0, 1, 1, 0}, {2, 3, 0, 0}, {3, 0, 0, 0}};
     const int lr = lane & 15, lg = lane >> 4;
     f32x4 g[NT];
 #pragma unroll
@@ -3868,7 +3871,7 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
     };
 
     // Two phases per chunk, each closed by a barrier.  Phase A: the compute
-    // waves form the chunk's 10 decay-masked score tiles, 2-3 per wave, and
+    // waves form the chunk's 10 decay-masked score tiles, 1-4 per wave, and
     // share them through LDS; they also update the state, keeping the
     // previous one in bf16 for phase B.  Phase B: the compute waves form Y.
     // The stagers fill buffer (c+1)&1 (not read during chunk c) with chunk
