@@ -4569,6 +4569,24 @@ __global__ __launch_bounds__(256, 2) void fzb_grad_kernel(FzbArgs a) {
     const int t0 = c * kFbC;
     const float Ah = a.A[h], inv_ip = 1.f / a.Ip[h];
     const uint32_t dtb = fzb_dt_bits(a, seq, t0, lane);   // issued before the staging loads
+    // v and beta as the gw blocks use them (block x: rows 16 (w + 4 x) + 4 g..,
+    // the lane's token 16 sb + m), loaded with the staging loads of the same
+    // lines, which bring them into L2 (loaded at the gw blocks they came from
+    // HBM a second time); kept in registers where that leaves room
+    constexpr bool kPre = DV <= 128;
+    constexpr int NIP = kPre ? DV / 64 : 1;
+    uint2 vq[NIP][4], bq[NIP][4];
+    if constexpr (kPre) {
+        const bf16_t *bsrc = a.beta ? a.beta : a.v;           // no beta: not read
+#pragma unroll
+        for (int x = 0; x < NIP; ++x)
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                const size_t o = (seq + (size_t)min(t0 + 16 * sb + m, a.T - 1) * a.H) * DV + 16 * (w + 4 * x) + 4 * g;
+                vq[x][sb] = *(const uint2 *)(a.v + o);
+                bq[x][sb] = *(const uint2 *)(bsrc + o);
+            }
+    }
     fzb_stage<DK, DV, TG>(a, hb, seq, t0, inv_ip, tid);
     const float Lt = fzb_lam_bits(a, dtb, t0, lane, Ah);  // L of token `lane`
     const float Lam = wave_read(Lt, 63);
@@ -4660,7 +4678,8 @@ __global__ __launch_bounds__(256, 2) void fzb_grad_kernel(FzbArgs a) {
             const int ib = w + 4 * n, i = 16 * ib + 4 * g;
             const bf16x8_t g0 = lds_trfrag(hb + L::kG, L::kRV, 0, 16 * ib, lane);
             const bf16x8_t g1 = lds_trfrag(hb + L::kG, L::kRV, 32, 16 * ib, lane);
-#pragma unroll 1
+            constexpr int kSbU = kPre ? 4 : 1;             // rolled where the registers are short
+#pragma unroll kSbU
             for (int sb = 0; sb < 4; ++sb) {
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -4674,11 +4693,11 @@ __global__ __launch_bounds__(256, 2) void fzb_grad_kernel(FzbArgs a) {
                 pw += (acc[0] * bf_lo(ww.x) + acc[1] * bf_hi(ww.x)) + (acc[2] * bf_lo(ww.y) + acc[3] * bf_hi(ww.y));
                 if (t0 + s < a.T) {
                     const size_t o = (seq + (size_t)(t0 + s) * a.H) * DV + i;
-                    const uint2 vv = *(const uint2 *)(a.v + o);
+                    const uint2 vv = kPre ? vq[n < NIP ? n : 0][sb] : *(const uint2 *)(a.v + o);
                     const float vf[4] = {bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y)};
                     f32x4 gvv, gbb;
                     if (a.beta) {
-                        const uint2 bb = *(const uint2 *)(a.beta + o);
+                        const uint2 bb = kPre ? bq[n < NIP ? n : 0][sb] : *(const uint2 *)(a.beta + o);
                         const float bf[4] = {bf_lo(bb.x), bf_hi(bb.x), bf_lo(bb.y), bf_hi(bb.y)};
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
