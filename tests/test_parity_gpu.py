@@ -931,11 +931,12 @@ def test_bwd_frozen_mqar_workload_full():
     _compare_bwd_frozen(_run_bwd_frozen(inp, gr), _bwd_frozen_ref(inp, gr), False)
 
 
-def test_bwd_frozen_layer760m_sampled_head():
+# heads 0, 5, 11: A = 1, about 3.5 and 16 (the slowest and the fastest decay)
+@pytest.mark.parametrize("h", [0, 5, 11])
+def test_bwd_frozen_layer760m_sampled_head(h):
     """Full 760M-layer frozen backward; the oracle runs head h of every
     sequence, so gA[h] and gIp[h] (sums over b) compare exactly."""
     w = workloads.WORKLOADS[2]
-    h = 5
     _announce("bwd frozen 760M layer bf16", B=w.B, H=w.H, T=w.T, d=w.dk, sampled_head=h)
     inp = workloads.make_inputs(w)
     gr = workloads.upstream_grads(w.B, w.T, w.H, w.dv, w.dk, w.dtype, seed=3)
