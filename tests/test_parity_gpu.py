@@ -699,29 +699,19 @@ def test_bwd_mqar_workload_full():
     _compare_bwd(_run_bwd(inp, gr), _bwd_ref(inp, gr), TOL_BWD)
 
 
-def test_bwd_layer760m_sampled_head():
-    """Full 760M-layer backward on the GPU; the oracle runs one head index h
-    for every sequence b, so gA[h] and gIp[h] (sums over b) compare exactly."""
+def test_bwd_layer760m_every_head():
+    """Full 760M-layer backward on the GPU (the launch the bench times)
+    against the oracle on every (b, h): each gradient normwise at the float32
+    bar, the per-token ones also per (b, h)."""
     w = workloads.WORKLOADS[2]
-    h = 7
-    _announce("bwd 760M layer bf16", B=w.B, H=w.H, T=w.T, d=w.dk, sampled_head=h)
+    _announce("bwd 760M layer bf16, every head", B=w.B, H=w.H, T=w.T, d=w.dk)
     inp = workloads.make_inputs(w)
     gr = workloads.upstream_grads(w.B, w.T, w.H, w.dv, w.dk, w.dtype, seed=2)
     got = _run_bwd(inp, gr)
-    heads = [(b, h) for b in range(w.B)]
-    sub = oracle.select_heads(inp, heads)
-    gy_s = to_np(gr["gy"])[:, :, h, :].transpose(1, 0, 2)[None]
-    gm_s = to_np(gr["gmuT"])[:, h][None]
-    gi_s = to_np(gr["gIT"])[:, h][None]
-    ref = oracle.bwd(**sub, gy=gy_s, gmuT=gm_s, gIT=gi_s, nthreads=len(heads))
-    bs = list(range(w.B))
-    for n in ("gq", "gk", "gv", "gbeta"):
-        assert_close(n + " (head %d)" % h, to_np(got[n])[bs, :, h, :].transpose(1, 0, 2)[None], ref[n], TOL_BWD)
-    assert_close("gdt (head %d)" % h, to_np(got["gdt"])[:, :, h].T[None], ref["gdt"], TOL_BWD)
-    assert_close("gA[h]", to_np(got["gA"])[h:h + 1], ref["gA"].sum(keepdims=True), TOL_BWD)
-    assert_close("gIp[h]", to_np(got["gIp"])[h:h + 1], ref["gIp"].sum(keepdims=True), TOL_BWD)
-    assert_close("gmu0 (head %d)" % h, to_np(got["gmu0"])[:, h][None], ref["gmu0"], TOL_BWD)
-    assert_close("gI0 (head %d)" % h, to_np(got["gI0"])[:, h][None], ref["gI0"], TOL_BWD)
+    ref = _bwd_ref(inp, gr, nthreads=16)
+    _compare_bwd(got, ref, TOL_BWD)
+    for n in ("gq", "gk", "gv", "gbeta", "gdt"):
+        report_per_head(n, got[n], ref[n], (0, 2), TOL_BWD)
 
 
 def test_bwd_is_deterministic_and_ignores_stale_workspace():
