@@ -4570,9 +4570,9 @@ __global__ __launch_bounds__(256, 2) void fzb_grad_kernel(FzbArgs a) {
     const float Ah = a.A[h], inv_ip = 1.f / a.Ip[h];
     const uint32_t dtb = fzb_dt_bits(a, seq, t0, lane);   // issued before the staging loads
     // v and beta as the gw blocks use them (block x: rows 16 (w + 4 x) + 4 g..,
-    // the lane's token 16 sb + m), loaded with the staging loads of the same
-    // lines, which bring them into L2 (loaded at the gw blocks they came from
-    // HBM a second time); kept in registers where that leaves room
+    // the lane's token 16 sb + m), loaded with the staging loads and kept in
+    // registers where that leaves room, so that the gw blocks wait for no load
+    // (loaded there, each 16-token block waited for its own)
     constexpr bool kPre = DV <= 128;
     constexpr int NIP = kPre ? DV / 64 : 1;
     uint2 vq[NIP][4], bq[NIP][4];
