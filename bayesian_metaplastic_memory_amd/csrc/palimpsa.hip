@@ -3970,7 +3970,6 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
     }
     __syncthreads();
     for (int c = 0; c < nchunks; ++c) {
-        const int t0 = c * kFzC;
         bf16x8_t sa[DK / 32];
         char *bufw = lds + (c & 1) * L::kBufBytes;
         const char *buf = bufw;
