@@ -3632,7 +3632,9 @@ struct FzLds {
     // 16 tokens of a compute wave's fragment write fall in distinct banks.
     static constexpr int kY = 2 * kBufBytes;
     static constexpr int kYTile = kFzC * (kFzRows * 4 + 16);
-    static constexpr int kTotal = kY + 2 * kYTile;
+    // the W role's per-wave copy of the chunk's state weights [wave][64 tokens]
+    static constexpr int kDl = kY + 2 * kYTile;
+    static constexpr int kTotal = kDl + 4 * kFzC * 4;
 };
 
 // Dword i of a 16-byte packet, and the bf16 in its low / high half as float.
@@ -3851,9 +3853,14 @@ __global__ __launch_bounds__(512) void frozen_fwd_kernel(FrozenArgs a) {
         // which only meet score entries of token pairs s > t, masked to 0.
         const float dl = (t0 + lane < a.T) ? __expf(wave_read(lam_l, 63) - lam_l) * inv_ip : 0.f;
         const int tok0 = 4 * (wxl / 8), il0 = 8 * (wxl % 8);
+        // the thread's four tokens' weights through the wave's own LDS slot
+        // (one write and one 16-byte read instead of four lane shuffles)
+        float *dls = (float *)(lds + L::kDl) + kFzC * (wx >> 6);
+        dls[lane] = dl;
+        const f32x4 d4 = *(const f32x4 *)(dls + tok0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float de = __shfl(dl, tok0 + e, 64);
+            const float de = d4[e];
             uint32_t ww[4], wd[4];
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
