@@ -4279,7 +4279,8 @@ struct FzbLds {
     static constexpr int kQ = 0, kK = kQ + kFbC * kRK, kG = kK + kFbC * kRK, kW = kG + kFbC * kRV;
     static constexpr int kP = kW + kFbC * kRV;            // one score matrix [64][kRP]
     static constexpr int kGradHalves = kP + kFbC * kRP;
-    static constexpr int kGradBytes = kGradHalves * 2;
+    static constexpr int kL = kGradHalves * 2;            // L of the chunk's tokens [64] (float)
+    static constexpr int kGradBytes = kL + kFbC * 4;
     // fzb_grad's closing sums (per-wave token sums of q.gq, k.gkI, k.gkE, and
     // of gw.w and <G_E, S_0>) reuse the score matrix's space
     static_assert((3 * 4 * kFbC + 8) * 4 <= kFbC * kRP * 2, "closing sums exceed the score buffer");
@@ -4596,6 +4597,10 @@ __global__ __launch_bounds__(256, 2) void fzb_grad_kernel(FzbArgs a) {
     fzb_stage<DK, DV, TG>(a, hb, seq, t0, inv_ip, tid);
     const float Lt = fzb_lam_bits(a, dtb, t0, lane, Ah);  // L of token `lane`
     const float Lam = wave_read(Lt, 63);
+    // L in LDS as well (read after the first barrier): a token's L is then one
+    // read, four consecutive tokens' one 16-byte read, not lane shuffles
+    const float *Ls = (const float *)((const char *)hb + L::kL);
+    if (w == 0) ((float *)Ls)[lane] = Lt;
 
     // The output blocks of wave w: first its NI value blocks ib = w + 4 x (gw;
     // A operand G_E rows 16 ib), then for each of its NJ key blocks jb = w + 4 x
@@ -4632,12 +4637,12 @@ __global__ __launch_bounds__(256, 2) void fzb_grad_kernel(FzbArgs a) {
                     acc = mfma16(rowfrag(hb + oa, rs, 16 * tb, 32 * kk, lane), rowfrag(hb + ob, rs, 16 * sb, 32 * kk, lane),
                                  acc);
                 const int s = 16 * sb + m;
-                const float ls = __shfl(Lt, s, 64);
+                const float ls = Ls[s];
+                const f32x4 lt4 = *(const f32x4 *)(Ls + 16 * tb + 4 * g);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = 16 * tb + 4 * g + r;
-                    const float lt = __shfl(Lt, t, 64);
-                    acc[r] = s <= t ? acc[r] * __expf(lt - ls) : 0.f;
+                    acc[r] = s <= t ? acc[r] * __expf(lt4[r] - ls) : 0.f;
                 }
             }
 #pragma unroll
@@ -4651,7 +4656,7 @@ __global__ __launch_bounds__(256, 2) void fzb_grad_kernel(FzbArgs a) {
     float eL[4], eR[4], pq[4], pk[4], pe[4];
 #pragma unroll
     for (int xb = 0; xb < 4; ++xb) {
-        const float lx = __shfl(Lt, 16 * xb + m, 64);
+        const float lx = Ls[16 * xb + m];
         eL[xb] = __expf(lx);
         eR[xb] = __expf(Lam - lx);
         pq[xb] = 0.f;
